@@ -1,0 +1,210 @@
+/*
+ * qmoe.h -- C ABI of an MI355X (gfx950) library that computes one quantized
+ * Mixture-of-Experts layer on a slice [slice_lo, slice_hi) of the expert intermediate
+ * dimension I: top-k routing, token->expert alignment, the gate_up grouped GEMM with a
+ * SwiGLU epilogue, the down projection to hidden-width partial sums, and the
+ * routing-weighted combine with the shared expert.
+ *
+ * Source of the operation: the FreeToken pages (issue #520 "[TP=2] Quantized MoE expert
+ * parallelism ...", issue #62 "Offloaded MoE ignores tensor parallelism ...", PR #637
+ * "tensor-parallel weight sharding", PR #70 "tensor-parallel DeepSeek-V4 runtime").
+ *
+ * Conventions for every call
+ *   - All array arguments are DEVICE pointers, except the two descriptor structs
+ *     (moe_bank, moe_align_out), which live in host memory and hold device pointers.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every call only
+ *     enqueues work on that stream and returns; nothing synchronises with the host, no
+ *     device memory is allocated or freed, and grid sizes depend on host arguments only
+ *     (never on device-side counts), so a sequence of calls can be captured in a HIP graph.
+ *     The expert-layer calls are dense in and dense out with static shapes, as the pages'
+ *     fused kernels are (issue #62, second comment; issue #62 "Why not expert parallelism").
+ *   - The caller owns every buffer.  The library keeps no pointer after a call returns and
+ *     never aliases one argument through another (the pages clone every shard so that no
+ *     view pins its parent: issue #520 section 4 ".clone()", PR #70 "Checkpoint loading").
+ *   - Return value: MOE_OK (0) or a negative MOE_ERR_* code.  All argument checks run on
+ *     the host before anything is enqueued ("fail with a targeted configuration error
+ *     before any layer is built", PR #70 "Checkpoint loading"; "does not silently pad",
+ *     PR #70 "Scope and non-goals").  moe_last_error() returns this thread's detail text.
+ *   - T == 0 (no tokens) is a successful no-op once the other arguments check out; arrays
+ *     whose size is proportional to T may then be NULL.
+ *   - The library runs on gfx950 only; any other device gives MOE_ERR_UNSUPPORTED.
+ */
+#ifndef QMOE_H
+#define QMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ status codes */
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG (-1) /* null required pointer, T < 0, k < 1, k > E, bad sizes   */
+#define MOE_ERR_ALIGNMENT (-2)   /* slice not on the format's block boundary, or !(0<=lo<hi<=I) */
+#define MOE_ERR_UNSUPPORTED (-3) /* shape the kernels do not cover, or device not gfx950     */
+#define MOE_ERR_WORKSPACE (-4)   /* workspace smaller than the *_workspace_bytes() figure    */
+#define MOE_ERR_HIP (-5)         /* a HIP runtime call or launch failed                      */
+
+/* ------------------------------------------------------------------ expert banks */
+
+/* Weight formats.
+ *   MOE_FMT_NVFP4: packed e2m1 codes, one e4m3fn scale per 16 consecutive K elements, and
+ *     an fp32 global per output row; W = e2m1 * e4m3(scale) * global, computed as W4A16
+ *     (weights dequantized, multiplied against bf16 activations: issue #520 section 2).
+ *   MOE_FMT_FP8_BLOCK128: e4m3fn codes with an fp32 weight_scale_inv per 128x128 block;
+ *     W = e4m3 * scale_inv (PR #637 "Implementation notes"; PR #70 "Checkpoint loading").
+ *   MOE_FMT_MXFP4_E8M0: packed e2m1 codes with an e8m0 scale per 32 consecutive K
+ *     elements; W = e2m1 * 2^(e8m0 - 127) (the DeepSeek-V4 routed FP4 experts' 32-element
+ *     scale blocks, PR #70 "Checkpoint loading"; issue #62 "What it touches" item 2).
+ * Packed FP4 stores two codes per byte, the even K index in the low nibble. */
+typedef enum {
+  MOE_FMT_NVFP4 = 1,
+  MOE_FMT_FP8_BLOCK128 = 2,
+  MOE_FMT_MXFP4_E8M0 = 3
+} moe_format;
+
+/* One bank of E experts, full-I layout, expert-major and row-major per matrix
+ * (issue #520 patch, nvfp4.py layout()/pack(); issue #62 "What it touches" item 1):
+ *   gate_up        [E, 2I, H] weights: gate rows [0, I), up rows [I, 2I); K = H.
+ *                  NVFP4/MXFP4: u8 [E, 2I, H/2]; FP8_BLOCK128: u8 e4m3 [E, 2I, H].
+ *   gate_up_scale  NVFP4: u8 e4m3 [E, 2I, H/16]; FP8_BLOCK128: f32 [E, 2I/128, H/128];
+ *                  MXFP4: u8 e8m0 [E, 2I, H/32].
+ *   gate_up_global NVFP4 only: f32 [E, 2I] (per output row); NULL otherwise.
+ *   down           [E, H, I] weights; K = I.  NVFP4/MXFP4: u8 [E, H, I/2];
+ *                  FP8_BLOCK128: u8 e4m3 [E, H, I].
+ *   down_scale     NVFP4: u8 e4m3 [E, H, I/16]; FP8_BLOCK128: f32 [E, H/128, I/128];
+ *                  MXFP4: u8 e8m0 [E, H, I/32].
+ *   down_global    NVFP4 only: f32 [E, H]; NULL otherwise.
+ * A rank that stores only its own slice passes that storage as a bank with I = hi - lo
+ * and the slice [0, I) (PR #70: TP=1 is the identity layout). */
+typedef struct {
+  int32_t fmt; /* moe_format */
+  int32_t E, H, I;
+  const void *gate_up;
+  const void *gate_up_scale;
+  const float *gate_up_global;
+  const void *down;
+  const void *down_scale;
+  const float *down_global;
+} moe_bank;
+
+/* ------------------------------------------------------------------ routing */
+
+/* moe_route -- replicated router and top-k selection (issue #62 second comment:
+ * norm_topk_prob defaults to True and the router is replicated; PR #70 ownership table:
+ * every rank must make the same expert selection).
+ *   x_bf16        [T, H] bf16 tokens.
+ *   w_router_bf16 [E, H] bf16 router weight.
+ *   bias          [E] f32 added to every token's logits, or NULL.
+ *   logits        [T, E] f32 output: logits[t,e] = sum_h x[t,h] W[e,h] + bias[e]
+ *                 (fp32 accumulation of exact bf16 products).
+ *   topk_ids      [T, k] int32 output: the k experts ranking first under
+ *                 (logit descending, expert index ascending), in that order.
+ *   topk_w        [T, k] f32 output: softmax over the k selected logits when renormalize
+ *                 != 0, else the full softmax probability of each selected expert.
+ * Requires 1 <= k <= E <= 1024 and H % 128 == 0. */
+int moe_route(const void *x_bf16, int T, int H, const void *w_router_bf16, int E,
+              const float *bias, int k, int renormalize, float *logits, int32_t *topk_ids,
+              float *topk_w, void *stream);
+
+/* moe_route_from_logits -- the selection step of moe_route on caller-supplied f32 logits
+ * [T, E] (plus bias[e] if non-NULL, added in f32 before selection).  Same outputs and
+ * rules as moe_route. */
+int moe_route_from_logits(const float *logits, int T, int E, const float *bias, int k,
+                          int renormalize, int32_t *topk_ids, float *topk_w, void *stream);
+
+/* ------------------------------------------------------------------ alignment */
+
+/* Output of moe_align: the T*k flat pairs f = t*k + j stably sorted by expert, every
+ * expert's run padded to a multiple of block_m with the sentinel T*k.  The pages name this
+ * step (moe_align, PR #637 "Notes") without defining it; this is the definition.
+ *   sorted_ids   [capacity] int32: pair indices, ascending f within each expert; sentinel
+ *                T*k in padding slots and from total_padded to capacity.
+ *   block_expert [capacity / block_m] int32: expert of each block_m-row block; -1 past
+ *                total_padded.
+ *   counts       [E] int32: pairs routed to each expert.
+ *   offsets      [E + 1] int32: start of each expert's run; offsets[E] = total_padded.
+ *   total_padded [1] int32.
+ *   block_m      rows per block: a multiple of 16 in [16, 256].
+ *   capacity     must be >= moe_align_capacity(T, k, E, block_m). */
+typedef struct {
+  int32_t *sorted_ids;
+  int32_t *block_expert;
+  int32_t *counts;
+  int32_t *offsets;
+  int32_t *total_padded;
+  int32_t block_m;
+  int32_t capacity;
+} moe_align_out;
+
+/* Rows needed for any routing: T*k + E*(block_m - 1), rounded up to block_m. */
+int32_t moe_align_capacity(int T, int k, int E, int block_m);
+
+/* Device workspace moe_align needs (per-chunk expert histograms). */
+size_t moe_align_workspace_bytes(int T, int k, int E);
+
+/* moe_align -- stable counting sort of topk_ids [T, k] (int32 in [0, E)).  Every output
+ * array in *out is fully written.  Deterministic: the result does not depend on
+ * scheduling.  Requires E <= 1024.  An id outside [0, E) is a caller error whose pairs
+ * are dropped (they appear nowhere in sorted_ids). */
+int moe_align(const int32_t *topk_ids, int T, int k, int E, const moe_align_out *out,
+              void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------ expert layer */
+
+/* Device workspace moe_expert_forward needs for (routed, shared, T, k, block_m, slice). */
+size_t moe_workspace_bytes(const moe_bank *routed, const moe_bank *shared, int T, int k,
+                           int block_m, int slice_lo, int slice_hi);
+
+#define MOE_OUT_F32 0
+#define MOE_OUT_BF16 1
+
+/* moe_expert_forward -- the quantized expert layer on the slice [slice_lo, slice_hi) of I,
+ * producing this rank's hidden-width partial sum (issue #520 section 4 "Expert sharding":
+ * the MoE output is sum_i silu(gate_i) up_i down_i, linear in the intermediate index).
+ *   For every pair f = t*k + j routed to expert e = topk_ids[t, j] (given through `al`):
+ *     g_i = x_t . Wg_e[i],  u_i = x_t . Wu_e[I + i]    for i in [lo, hi)  (gate rows
+ *       [lo, hi), up rows [I+lo, I+hi): issue #62 "What it touches" item 1)
+ *     a_i = silu(g_i) * u_i, rounded to bf16 (the A16 activation of the down GEMM)
+ *     y_n = sum_{i in [lo,hi)} a_i Wd_e[n, i]       for n in [0, H)  (down columns)
+ *   out[t, :] = sum_j topk_w[t, j] * y(pair t*k+j)  +  shared(x_t)
+ *   where the shared expert (weight 1, same slice) is added to the routed partial before
+ *   any reduction across ranks (PR #70 ownership table and the paragraph after it).
+ * Companion scales are sliced with their weight's axis; the NVFP4 per-row globals of
+ * gate_up follow its rows and down_global is used whole (PR #637 "Implementation notes").
+ *   routed      E-expert bank; shared: NULL or a 1-expert bank of the same format, H and I.
+ *   x_bf16      [T, H] bf16; topk_w [T, k] f32; al: the moe_align output for these ids.
+ *   slice_lo/hi multiples of the format block (NVFP4 16, MXFP4 32, FP8_BLOCK128 128), with
+ *               0 <= lo < hi <= I (issue #62 "What it touches" item 2; PR #70 div_tp(...,
+ *               multiple_of=128)).  The kernels additionally need (hi - lo) % 32 == 0.
+ *   out         [T, H] f32 (out_dtype MOE_OUT_F32) or bf16 (MOE_OUT_BF16), overwritten.
+ *   workspace   >= moe_workspace_bytes(...) bytes of device memory.
+ * Experts that received no tokens are never read. */
+int moe_expert_forward(const moe_bank *routed, const moe_bank *shared, const void *x_bf16,
+                       int T, int k, const float *topk_w, const moe_align_out *al,
+                       int slice_lo, int slice_hi, void *out, int out_dtype, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/* The two halves of moe_expert_forward, for callers that time or schedule them apart.
+ * Both take the same arguments and the same workspace; moe_expert_down reads what
+ * moe_expert_gate_up left in the workspace for the same (routed, shared, x, al, slice). */
+int moe_expert_gate_up(const moe_bank *routed, const moe_bank *shared, const void *x_bf16,
+                       int T, int k, const moe_align_out *al, int slice_lo, int slice_hi,
+                       void *workspace, size_t workspace_bytes, void *stream);
+int moe_expert_down(const moe_bank *routed, const moe_bank *shared, int T, int k,
+                    const float *topk_w, const moe_align_out *al, int slice_lo, int slice_hi,
+                    void *out, int out_dtype, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/* ------------------------------------------------------------------ diagnostics */
+
+const char *moe_status_string(int status); /* static text for a status code */
+const char *moe_last_error(void);          /* this thread's detail text for the last error */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMOE_H */

@@ -1,0 +1,384 @@
+// abi.cpp -- host side of the C ABI declared in include/qmoe.h: argument and layout checks
+// (all before anything is enqueued), workspace sizing, and kernel dispatch on the
+// caller's stream.  No call allocates device memory or synchronises with the host.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "launch.h"
+#include "qmoe.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+// Per-device "is this a gfx950" cache: 0 unknown, 1 yes, 2 no.
+std::atomic<int> g_arch_ok[64];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= 64) return fail(MOE_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  int st = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+      return fail(MOE_ERR_HIP, "hipGetDeviceProperties failed");
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_ok[dev].store(st, std::memory_order_relaxed);
+  }
+  if (st != 1) return fail(MOE_ERR_UNSUPPORTED, "this library runs on gfx950 (MI355X) only");
+  return MOE_OK;
+}
+
+int hip_status(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int format_block(int fmt) {
+  switch (fmt) {
+    case MOE_FMT_NVFP4: return 16;
+    case MOE_FMT_FP8_BLOCK128: return 128;
+    case MOE_FMT_MXFP4_E8M0: return 32;
+    default: return 0;
+  }
+}
+
+const char *format_name(int fmt) {
+  switch (fmt) {
+    case MOE_FMT_NVFP4: return "NVFP4";
+    case MOE_FMT_FP8_BLOCK128: return "FP8_BLOCK128";
+    case MOE_FMT_MXFP4_E8M0: return "MXFP4_E8M0";
+    default: return "unknown";
+  }
+}
+
+int check_bank(const moe_bank *b, const char *name) {
+  if (!b) return fail(MOE_ERR_INVALID_ARG, "%s bank is NULL", name);
+  const int blk = format_block(b->fmt);
+  if (!blk) return fail(MOE_ERR_INVALID_ARG, "%s bank: unknown format %d", name, b->fmt);
+  if (b->E < 1 || b->H < 1 || b->I < 1)
+    return fail(MOE_ERR_INVALID_ARG, "%s bank: E=%d H=%d I=%d must be positive", name, b->E, b->H, b->I);
+  if (b->E > 1024) return fail(MOE_ERR_UNSUPPORTED, "%s bank: E=%d > 1024", name, b->E);
+  if (!b->gate_up || !b->gate_up_scale || !b->down || !b->down_scale)
+    return fail(MOE_ERR_INVALID_ARG, "%s bank: NULL weight or scale pointer", name);
+  if (b->fmt == MOE_FMT_NVFP4 && (!b->gate_up_global || !b->down_global))
+    return fail(MOE_ERR_INVALID_ARG, "%s bank: NVFP4 needs gate_up_global and down_global", name);
+  if (b->I % blk)
+    return fail(MOE_ERR_ALIGNMENT, "%s bank: I=%d is not a multiple of the %s block %d", name, b->I,
+                format_name(b->fmt), blk);
+  if (b->H % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "%s bank: H=%d must be a multiple of 128 (K tile)", name, b->H);
+  if (b->I % 32)
+    return fail(MOE_ERR_UNSUPPORTED, "%s bank: I=%d must be a multiple of 32 (row pitch of 16-byte loads)",
+                name, b->I);
+  return MOE_OK;
+}
+
+int check_slice(const moe_bank *b, int lo, int hi) {
+  const int blk = format_block(b->fmt);
+  if (!(0 <= lo && lo < hi && hi <= b->I))
+    return fail(MOE_ERR_ALIGNMENT, "slice [%d, %d) is not a non-empty range inside [0, I=%d)", lo, hi, b->I);
+  if (lo % blk || hi % blk)
+    return fail(MOE_ERR_ALIGNMENT, "slice [%d, %d) is not on the %s block boundary (%d)", lo, hi,
+                format_name(b->fmt), blk);
+  if (lo % 32 || hi % 32)
+    return fail(MOE_ERR_UNSUPPORTED, "slice [%d, %d): the kernels need lo and hi multiples of 32", lo, hi);
+  return MOE_OK;
+}
+
+int check_align_out(const moe_align_out *al, int T, int k, int E) {
+  if (!al) return fail(MOE_ERR_INVALID_ARG, "align descriptor is NULL");
+  if (al->block_m < 16 || al->block_m > 256 || al->block_m % 16)
+    return fail(MOE_ERR_UNSUPPORTED, "block_m=%d must be a multiple of 16 in [16, 256]", al->block_m);
+  const int32_t need = moe_align_capacity(T, k, E, al->block_m);
+  if (need < 0) return fail(MOE_ERR_INVALID_ARG, "bad sizes for the alignment capacity");
+  if (al->capacity < need || al->capacity % al->block_m)
+    return fail(MOE_ERR_INVALID_ARG, "capacity=%d must be a multiple of block_m and >= %d", al->capacity, need);
+  if (!al->sorted_ids || !al->block_expert || !al->counts || !al->offsets || !al->total_padded)
+    return fail(MOE_ERR_INVALID_ARG, "align descriptor has a NULL array");
+  return MOE_OK;
+}
+
+struct FwdPlan {
+  int Il, n_routed_sub, n_shared_sub, shared_rows, P, Psh;
+  size_t h_bytes, y_off, y_bytes, total;
+};
+
+FwdPlan plan_forward(const moe_bank *routed, const moe_bank *shared, int T, int k, int cap, int lo, int hi) {
+  FwdPlan p;
+  p.Il = hi - lo;
+  p.n_routed_sub = cap / 16;
+  p.n_shared_sub = shared ? (T + 15) / 16 : 0;
+  p.shared_rows = p.n_shared_sub * 16;
+  p.P = T * k;
+  p.Psh = shared ? T : 0;
+  p.h_bytes = align_up((size_t)(cap + p.shared_rows) * p.Il * 2, 256);
+  p.y_off = p.h_bytes;
+  p.y_bytes = align_up((size_t)(p.P + p.Psh) * routed->H * 4, 256);
+  p.total = p.h_bytes + p.y_bytes;
+  return p;
+}
+
+// Checks shared by the forward entry points; fills *plan.
+int check_forward(const moe_bank *routed, const moe_bank *shared, int T, int k, const moe_align_out *al,
+                  int lo, int hi, size_t workspace_bytes, const void *workspace, FwdPlan *plan) {
+  int rc = check_bank(routed, "routed");
+  if (rc) return rc;
+  if (shared) {
+    rc = check_bank(shared, "shared");
+    if (rc) return rc;
+    if (shared->E != 1 || shared->fmt != routed->fmt || shared->H != routed->H || shared->I != routed->I)
+      return fail(MOE_ERR_INVALID_ARG,
+                  "shared bank must be one expert of the routed bank's format, H and I (E=%d fmt=%d H=%d I=%d)",
+                  shared->E, shared->fmt, shared->H, shared->I);
+  }
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T=%d < 0", T);
+  if (k < 1 || k > routed->E) return fail(MOE_ERR_INVALID_ARG, "k=%d must be in [1, E=%d]", k, routed->E);
+  rc = check_slice(routed, lo, hi);
+  if (rc) return rc;
+  rc = check_align_out(al, T, k, routed->E);
+  if (rc) return rc;
+  if ((long long)T * k > (1LL << 30)) return fail(MOE_ERR_UNSUPPORTED, "T*k too large");
+  *plan = plan_forward(routed, shared, T, k, al->capacity, lo, hi);
+  if (workspace_bytes < plan->total)
+    return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, plan->total);
+  if (!workspace && plan->total) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
+  return MOE_OK;
+}
+
+qmoe::GateUpArgs gate_up_args(const moe_bank *routed, const moe_bank *shared, const void *x, int T, int k,
+                              const moe_align_out *al, int lo, const FwdPlan &p, void *workspace) {
+  qmoe::GateUpArgs a;
+  a.x = static_cast<const uint16_t *>(x);
+  a.T = T;
+  a.H = routed->H;
+  a.k = k;
+  a.gu = static_cast<const uint8_t *>(routed->gate_up);
+  a.gus = static_cast<const uint8_t *>(routed->gate_up_scale);
+  a.gug = routed->gate_up_global;
+  a.sgu = shared ? static_cast<const uint8_t *>(shared->gate_up) : nullptr;
+  a.sgus = shared ? static_cast<const uint8_t *>(shared->gate_up_scale) : nullptr;
+  a.sgug = shared ? shared->gate_up_global : nullptr;
+  a.E = routed->E;
+  a.I = routed->I;
+  a.sorted_ids = al->sorted_ids;
+  a.block_expert = al->block_expert;
+  a.total_padded = al->total_padded;
+  a.block_m = al->block_m;
+  a.cap = al->capacity;
+  a.n_routed_sub = p.n_routed_sub;
+  a.lo = lo;
+  a.Il = p.Il;
+  a.h = static_cast<uint16_t *>(workspace);
+  return a;
+}
+
+qmoe::DownArgs down_args(const moe_bank *routed, const moe_bank *shared, int T, int k, const float *topk_w,
+                         const moe_align_out *al, int lo, const FwdPlan &p, void *workspace) {
+  qmoe::DownArgs a;
+  a.h = static_cast<const uint16_t *>(workspace);
+  a.T = T;
+  a.H = routed->H;
+  a.k = k;
+  a.dn = static_cast<const uint8_t *>(routed->down);
+  a.dns = static_cast<const uint8_t *>(routed->down_scale);
+  a.dng = routed->down_global;
+  a.sdn = shared ? static_cast<const uint8_t *>(shared->down) : nullptr;
+  a.sdns = shared ? static_cast<const uint8_t *>(shared->down_scale) : nullptr;
+  a.sdng = shared ? shared->down_global : nullptr;
+  a.E = routed->E;
+  a.I = routed->I;
+  a.sorted_ids = al->sorted_ids;
+  a.block_expert = al->block_expert;
+  a.total_padded = al->total_padded;
+  a.block_m = al->block_m;
+  a.cap = al->capacity;
+  a.n_routed_sub = p.n_routed_sub;
+  a.lo = lo;
+  a.Il = p.Il;
+  a.topk_w = topk_w;
+  a.Y = reinterpret_cast<float *>(static_cast<char *>(workspace) + p.y_off);
+  return a;
+}
+
+int run_gate_up(const moe_bank *routed, const moe_bank *shared, const void *x, int T, int k,
+                const moe_align_out *al, int lo, const FwdPlan &p, void *workspace, hipStream_t s) {
+  qmoe::GateUpArgs a = gate_up_args(routed, shared, x, T, k, al, lo, p, workspace);
+  return hip_status(qmoe::launch_gate_up(routed->fmt, a, p.n_shared_sub, s), "gate_up launch");
+}
+
+int run_down(const moe_bank *routed, const moe_bank *shared, int T, int k, const float *topk_w,
+             const moe_align_out *al, int lo, const FwdPlan &p, void *out, int out_dtype, void *workspace,
+             hipStream_t s) {
+  qmoe::DownArgs a = down_args(routed, shared, T, k, topk_w, al, lo, p, workspace);
+  int rc = hip_status(qmoe::launch_down(routed->fmt, a, p.n_shared_sub, s), "down launch");
+  if (rc) return rc;
+  return hip_status(qmoe::launch_combine(a.Y, T, k, routed->H, shared != nullptr, out, out_dtype == MOE_OUT_BF16, s),
+                    "combine launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_ALIGNMENT: return "slice not aligned to the format block";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or device";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char *moe_last_error(void) { return g_last_error.c_str(); }
+
+int32_t moe_align_capacity(int T, int k, int E, int block_m) {
+  if (T < 0 || k < 1 || E < 1 || block_m < 1) return -1;
+  const long long need = (long long)T * k + (long long)E * (block_m - 1);
+  const long long cap = (need + block_m - 1) / block_m * block_m;
+  return cap > 0x7fffffffLL ? -1 : (int32_t)cap;
+}
+
+size_t moe_align_workspace_bytes(int T, int k, int E) {
+  if (T <= 0 || k < 1 || E < 1) return 0;
+  const long long P = (long long)T * k;
+  return (size_t)((P + 1023) / 1024) * (size_t)E * sizeof(int32_t);
+}
+
+size_t moe_workspace_bytes(const moe_bank *routed, const moe_bank *shared, int T, int k, int block_m,
+                           int slice_lo, int slice_hi) {
+  if (!routed || T < 0 || k < 1 || slice_hi <= slice_lo || block_m < 16) return 0;
+  const int32_t cap = moe_align_capacity(T, k, routed->E, block_m);
+  if (cap < 0) return 0;
+  return plan_forward(routed, shared, T, k, cap, slice_lo, slice_hi).total;
+}
+
+int moe_route(const void *x_bf16, int T, int H, const void *w_router_bf16, int E, const float *bias, int k,
+              int renormalize, float *logits, int32_t *topk_ids, float *topk_w, void *stream) {
+  if (!w_router_bf16 || (T > 0 && (!x_bf16 || !logits || !topk_ids || !topk_w)))
+    return fail(MOE_ERR_INVALID_ARG, "moe_route: NULL required pointer");
+  if (T < 0 || H < 1 || E < 1) return fail(MOE_ERR_INVALID_ARG, "moe_route: T=%d H=%d E=%d", T, H, E);
+  if (k < 1 || k > E) return fail(MOE_ERR_INVALID_ARG, "moe_route: k=%d must be in [1, E=%d]", k, E);
+  if (E > 1024 || k > 64) return fail(MOE_ERR_UNSUPPORTED, "moe_route: needs E <= 1024 and k <= 64");
+  if (H % 128) return fail(MOE_ERR_UNSUPPORTED, "moe_route: H=%d must be a multiple of 128", H);
+  if (T > 16 * 65535) return fail(MOE_ERR_UNSUPPORTED, "moe_route: T=%d too large", T);
+  int rc = check_device();
+  if (rc) return rc;
+  if (T == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = hip_status(qmoe::launch_router_logits(static_cast<const uint16_t *>(x_bf16), T, H,
+                                             static_cast<const uint16_t *>(w_router_bf16), E, bias, logits, s),
+                  "router launch");
+  if (rc) return rc;
+  return hip_status(qmoe::launch_topk(logits, T, E, nullptr, k, renormalize, topk_ids, topk_w, s), "topk launch");
+}
+
+int moe_route_from_logits(const float *logits, int T, int E, const float *bias, int k, int renormalize,
+                          int32_t *topk_ids, float *topk_w, void *stream) {
+  if (T > 0 && (!logits || !topk_ids || !topk_w))
+    return fail(MOE_ERR_INVALID_ARG, "moe_route_from_logits: NULL pointer");
+  if (T < 0 || E < 1) return fail(MOE_ERR_INVALID_ARG, "moe_route_from_logits: T=%d E=%d", T, E);
+  if (k < 1 || k > E) return fail(MOE_ERR_INVALID_ARG, "moe_route_from_logits: k=%d must be in [1, E=%d]", k, E);
+  if (E > 1024 || k > 64) return fail(MOE_ERR_UNSUPPORTED, "moe_route_from_logits: needs E <= 1024 and k <= 64");
+  int rc = check_device();
+  if (rc) return rc;
+  if (T == 0) return ok();
+  return hip_status(qmoe::launch_topk(logits, T, E, bias, k, renormalize, topk_ids, topk_w,
+                                      static_cast<hipStream_t>(stream)),
+                    "topk launch");
+}
+
+int moe_align(const int32_t *topk_ids, int T, int k, int E, const moe_align_out *out, void *workspace,
+              size_t workspace_bytes, void *stream) {
+  if (!topk_ids && T > 0) return fail(MOE_ERR_INVALID_ARG, "moe_align: topk_ids is NULL");
+  if (T < 0 || k < 1 || E < 1) return fail(MOE_ERR_INVALID_ARG, "moe_align: T=%d k=%d E=%d", T, k, E);
+  if (E > 1024) return fail(MOE_ERR_UNSUPPORTED, "moe_align: E=%d > 1024", E);
+  if ((long long)T * k > (1LL << 30)) return fail(MOE_ERR_UNSUPPORTED, "moe_align: T*k too large");
+  int rc = check_align_out(out, T, k, E);
+  if (rc) return rc;
+  const size_t need = moe_align_workspace_bytes(T, k, E);
+  if (workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "moe_align: workspace %zu < %zu", workspace_bytes, need);
+  if (need && !workspace) return fail(MOE_ERR_INVALID_ARG, "moe_align: workspace is NULL");
+  rc = check_device();
+  if (rc) return rc;
+  if (T == 0) return ok();
+  return hip_status(qmoe::launch_align(topk_ids, T, k, E, out->block_m, out->capacity, out->sorted_ids,
+                                       out->block_expert, out->counts, out->offsets, out->total_padded,
+                                       static_cast<int32_t *>(workspace), static_cast<hipStream_t>(stream)),
+                    "align launch");
+}
+
+int moe_expert_gate_up(const moe_bank *routed, const moe_bank *shared, const void *x_bf16, int T, int k,
+                       const moe_align_out *al, int slice_lo, int slice_hi, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+  FwdPlan p;
+  int rc = check_forward(routed, shared, T, k, al, slice_lo, slice_hi, workspace_bytes, workspace, &p);
+  if (rc) return rc;
+  if (!x_bf16 && T > 0) return fail(MOE_ERR_INVALID_ARG, "x is NULL");
+  rc = check_device();
+  if (rc) return rc;
+  if (T == 0) return ok();
+  return run_gate_up(routed, shared, x_bf16, T, k, al, slice_lo, p, workspace, static_cast<hipStream_t>(stream));
+}
+
+int moe_expert_down(const moe_bank *routed, const moe_bank *shared, int T, int k, const float *topk_w,
+                    const moe_align_out *al, int slice_lo, int slice_hi, void *out, int out_dtype, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+  FwdPlan p;
+  int rc = check_forward(routed, shared, T, k, al, slice_lo, slice_hi, workspace_bytes, workspace, &p);
+  if (rc) return rc;
+  if (T > 0 && (!topk_w || !out)) return fail(MOE_ERR_INVALID_ARG, "topk_w or out is NULL");
+  if (out_dtype != MOE_OUT_F32 && out_dtype != MOE_OUT_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "out_dtype=%d", out_dtype);
+  rc = check_device();
+  if (rc) return rc;
+  if (T == 0) return ok();
+  return run_down(routed, shared, T, k, topk_w, al, slice_lo, p, out, out_dtype, workspace,
+                  static_cast<hipStream_t>(stream));
+}
+
+int moe_expert_forward(const moe_bank *routed, const moe_bank *shared, const void *x_bf16, int T, int k,
+                       const float *topk_w, const moe_align_out *al, int slice_lo, int slice_hi, void *out,
+                       int out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+  FwdPlan p;
+  int rc = check_forward(routed, shared, T, k, al, slice_lo, slice_hi, workspace_bytes, workspace, &p);
+  if (rc) return rc;
+  if (T > 0 && (!x_bf16 || !topk_w || !out)) return fail(MOE_ERR_INVALID_ARG, "x, topk_w or out is NULL");
+  if (out_dtype != MOE_OUT_F32 && out_dtype != MOE_OUT_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "out_dtype=%d", out_dtype);
+  rc = check_device();
+  if (rc) return rc;
+  if (T == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = run_gate_up(routed, shared, x_bf16, T, k, al, slice_lo, p, workspace, s);
+  if (rc) return rc;
+  return run_down(routed, shared, T, k, topk_w, al, slice_lo, p, out, out_dtype, workspace, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,156 @@
+// align.hip -- moe_align for gfx950: a stable counting sort of the T*k flat (token, slot)
+// pairs by expert, each expert's run padded to a multiple of block_m.  The FreeToken pages
+// name this step (PR #637 "Notes": the moe_align fallback on ROCm) without defining it;
+// the definition implemented here is the one stated in include/qmoe.h.
+//
+// Three passes over chunks of 1024 pairs, none of them ordered by atomics, so the result
+// is deterministic:
+//   1. k_align_hist    per-chunk expert histograms            -> hist[chunk][E]
+//   2. k_align_scan    per-expert exclusive prefix over chunks (in place), counts, padded
+//                      offsets, block_expert, and the sentinel in every padding slot
+//   3. k_align_scatter stable rank of each pair inside its chunk (ballot match masks per
+//                      64-pair row, prefix over the 16 rows of the chunk) -> sorted_ids
+#include "device_common.h"
+#include "launch.h"
+
+namespace qmoe {
+
+constexpr int kChunk = 1024;  // pairs per chunk = 16 rows of 64
+
+__global__ __launch_bounds__(256) void k_align_hist(const int32_t *__restrict__ ids, int P, int E,
+                                                    int32_t *__restrict__ hist) {
+  extern __shared__ int32_t cnt[];  // [E]
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+  __syncthreads();
+  const int base = blockIdx.x * kChunk;
+  for (int i = threadIdx.x; i < kChunk; i += blockDim.x) {
+    const int f = base + i;
+    if (f < P) {
+      const int e = ids[f];
+      if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);  // a count does not depend on the order
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(size_t)blockIdx.x * E + e] = cnt[e];
+}
+
+// One workgroup of 1024 threads.  Thread e owns expert e (E <= 1024).
+__global__ __launch_bounds__(1024) void k_align_scan(int32_t *__restrict__ hist, int nchunk, int E, int BM,
+                                                     int P, int cap, int32_t *__restrict__ sorted_ids,
+                                                     int32_t *__restrict__ block_expert,
+                                                     int32_t *__restrict__ counts,
+                                                     int32_t *__restrict__ offsets,
+                                                     int32_t *__restrict__ total_padded) {
+  __shared__ int32_t scan[1024];
+  __shared__ int32_t wsum[16];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E) {
+    for (int c = 0; c < nchunk; c++) {
+      const int v = hist[(size_t)c * E + e];
+      hist[(size_t)c * E + e] = run;  // exclusive prefix: where chunk c's pairs of e start
+      run += v;
+    }
+    counts[e] = run;
+  }
+  const int padded = e < E ? (run + BM - 1) / BM * BM : 0;
+  // block-wide exclusive scan of padded (wave scan, then scan of the 16 wave totals)
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  int inc = padded;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(inc, off);
+    if (lane >= off) inc += o;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  int wbase = 0;
+  for (int w = 0; w < wave; w++) wbase += wsum[w];
+  const int start = wbase + inc - padded;
+  scan[threadIdx.x] = start;
+  __syncthreads();
+  int total = 0;
+  for (int w = 0; w < 16; w++) total += wsum[w];
+  if (e < E) {
+    offsets[e] = start;
+    for (int b = start / BM; b < (start + padded) / BM; b++) block_expert[b] = e;
+    for (int p = start + run; p < start + padded; p++) sorted_ids[p] = P;  // padding slots
+  }
+  if (e == 0) {
+    offsets[E] = total;
+    total_padded[0] = total;
+  }
+  for (int b = total / BM + threadIdx.x; b < cap / BM; b += blockDim.x) block_expert[b] = -1;
+  for (int p = total + threadIdx.x; p < cap; p += blockDim.x) sorted_ids[p] = P;
+}
+
+// One workgroup (256 threads = 4 waves) per chunk; wave w handles rows 4w..4w+3 of 64 pairs.
+__global__ __launch_bounds__(256) void k_align_scatter(const int32_t *__restrict__ ids, int P, int E,
+                                                       const int32_t *__restrict__ hist,
+                                                       const int32_t *__restrict__ offsets,
+                                                       int32_t *__restrict__ sorted_ids) {
+  extern __shared__ int32_t rowcnt[];  // [16][E]: pairs of expert e in row r of this chunk
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < 16 * E; i += blockDim.x) rowcnt[i] = 0;
+  __syncthreads();
+  int nbits = 0;
+  while ((1 << nbits) < E) nbits++;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int myexp[4], myrank[4];
+  const int base = blockIdx.x * kChunk;
+#pragma unroll
+  for (int rr = 0; rr < 4; rr++) {
+    const int row = wave * 4 + rr;
+    const int f = base + row * 64 + lane;
+    int e = f < P ? ids[f] : -1;
+    if (e < 0 || e >= E) e = -1;
+    uint64_t peers = __ballot(e >= 0);
+    for (int bit = 0; bit < nbits; bit++) {
+      const uint64_t m = __ballot(e >= 0 && ((e >> bit) & 1));
+      peers &= ((e >> bit) & 1) ? m : ~m;
+    }
+    myexp[rr] = e;
+    myrank[rr] = __popcll(peers & below);
+    if (e >= 0 && myrank[rr] == 0) rowcnt[row * E + e] = __popcll(peers);  // row leader
+  }
+  __syncthreads();
+  // exclusive prefix over the 16 rows, per expert
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int run = 0;
+    for (int r = 0; r < 16; r++) {
+      const int v = rowcnt[r * E + e];
+      rowcnt[r * E + e] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int rr = 0; rr < 4; rr++) {
+    const int row = wave * 4 + rr;
+    const int e = myexp[rr];
+    if (e >= 0) {
+      const int f = base + row * 64 + lane;
+      const int pos = offsets[e] + hist[(size_t)blockIdx.x * E + e] + rowcnt[row * E + e] + myrank[rr];
+      sorted_ids[pos] = f;
+    }
+  }
+}
+
+hipError_t launch_align(const int32_t *ids, int T, int k, int E, int BM, int cap, int32_t *sorted_ids,
+                        int32_t *block_expert, int32_t *counts, int32_t *offsets, int32_t *total_padded,
+                        int32_t *hist, hipStream_t s) {
+  const int P = T * k;
+  const int nchunk = (P + kChunk - 1) / kChunk;
+  if (nchunk > 0) {
+    hipLaunchKernelGGL(k_align_hist, dim3(nchunk), dim3(256), E * sizeof(int32_t), s, ids, P, E, hist);
+  }
+  hipLaunchKernelGGL(k_align_scan, dim3(1), dim3(1024), 0, s, hist, nchunk, E, BM, P, cap, sorted_ids,
+                     block_expert, counts, offsets, total_padded);
+  if (nchunk > 0) {
+    hipLaunchKernelGGL(k_align_scatter, dim3(nchunk), dim3(256), 16 * E * sizeof(int32_t), s, ids, P, E,
+                       hist, offsets, sorted_ids);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qmoe

@@ -1,0 +1,90 @@
+// device_common.h -- gfx950 building blocks shared by the routing, alignment and expert
+// kernels: vector types, the bf16 MFMA, and in-register weight decoders.
+//
+// MFMA v_mfma_f32_16x16x32_bf16 operand layout (wave64, lane l, i = 0..7, j = 0..3):
+//   A (16x32, M x K): lane l holds A[l % 16][8 * (l / 16) + i]
+//   B (32x16, K x N): lane l holds B[8 * (l / 16) + i][l % 16]
+//   D (16x16, M x N): lane l holds D[4 * (l / 16) + j][l % 16]
+// A contraction does not care which K index a (lane group, i) slot carries as long as A
+// and B agree, so the kernels hand each lane group a contiguous run of K and load it with
+// wide vector loads.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+
+union frag8 {  // 8 bf16 = 4 dwords = one MFMA operand slot of one lane
+  bf16x8_t v;
+  bf16x2_t h[4];
+  uint32_t u[4];
+  uint4 q;
+};
+
+__device__ __forceinline__ f32x4_t mfma_bf16(const frag8 &a, const frag8 &b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+
+__device__ __forceinline__ bf16x2_t pack_bf16(float a, float b) {  // round to nearest even
+  bf16x2_t r;
+  r[0] = (__bf16)a;
+  r[1] = (__bf16)b;
+  return r;
+}
+
+__device__ __forceinline__ uint16_t bf16_bits(float a) {
+  __bf16 h = (__bf16)a;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+// e4m3fn byte -> f32 (gfx950 decodes the OCP E4M3 encoding natively).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)(byte & 0xFFu), 0);
+}
+
+// e8m0 byte (1..254) -> the f32 2^(b-127); the conversion instructions use only the
+// exponent field of their f32 scale operand.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t byte) { return __uint_as_float((byte & 0xFFu) << 23); }
+
+// 8 e2m1 codes (dword; element i in nibble i, low nibble first) -> 8 bf16 of code * s.
+// The e2m1 -> f32 conversion is exact; e2m1 * e4m3 has at most 6 significant bits, so the
+// product and its bf16 rounding are exact.
+__device__ __forceinline__ void fp4x8_mul_to_bf16(uint32_t codes, float s, frag8 &out) {
+  f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+  f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+  f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+  f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+  out.h[0] = pack_bf16(p0[0] * s, p0[1] * s);
+  out.h[1] = pack_bf16(p1[0] * s, p1[1] * s);
+  out.h[2] = pack_bf16(p2[0] * s, p2[1] * s);
+  out.h[3] = pack_bf16(p3[0] * s, p3[1] * s);
+}
+
+// 8 e2m1 codes -> 8 bf16 of code * 2^x, where pow2 is the f32 2^x (MXFP4 e8m0 scale).
+__device__ __forceinline__ void fp4x8_pow2_to_bf16(uint32_t codes, float pow2, frag8 &out) {
+  out.h[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, pow2, 0);
+  out.h[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, pow2, 1);
+  out.h[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, pow2, 2);
+  out.h[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, pow2, 3);
+}
+
+// 8 e4m3 codes (two dwords, element i in byte i) -> 8 bf16 (exact).
+__device__ __forceinline__ void fp8x8_to_bf16(uint32_t lo, uint32_t hi, frag8 &out) {
+  out.h[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  out.h[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  out.h[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  out.h[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+}
+
+// Wave-wide helpers (wave64).
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63u); }

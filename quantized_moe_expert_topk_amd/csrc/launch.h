@@ -1,0 +1,53 @@
+// launch.h -- internal interface between the host-side ABI (abi.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qmoe.h"
+
+namespace qmoe {
+
+struct GateUpArgs {
+  const uint16_t *x;  // [T, H] bf16
+  int T, H, k;
+  const uint8_t *gu;  // routed bank gate_up codes (all experts)
+  const uint8_t *gus; // routed gate_up scales
+  const float *gug;   // routed gate_up globals (NVFP4) or null
+  const uint8_t *sgu, *sgus;  // shared bank (1 expert) or null
+  const float *sgug;
+  int E, I;
+  const int32_t *sorted_ids, *block_expert, *total_padded;
+  int block_m, cap, n_routed_sub;  // n_routed_sub = cap / 16
+  int lo, Il;
+  uint16_t *h;  // [cap + 16 * n_shared_sub, Il] bf16
+};
+
+struct DownArgs {
+  const uint16_t *h;
+  int T, H, k;
+  const uint8_t *dn, *dns;
+  const float *dng;
+  const uint8_t *sdn, *sdns;
+  const float *sdng;
+  int E, I;
+  const int32_t *sorted_ids, *block_expert, *total_padded;
+  int block_m, cap, n_routed_sub;
+  int lo, Il;
+  const float *topk_w;  // [T * k]
+  float *Y;             // [T * k + T_shared, H]
+};
+
+hipError_t launch_router_logits(const uint16_t *x, int T, int H, const uint16_t *w, int E,
+                                const float *bias, float *logits, hipStream_t s);
+hipError_t launch_topk(const float *logits, int T, int E, const float *bias, int k, int renormalize,
+                       int32_t *ids, float *wts, hipStream_t s);
+hipError_t launch_align(const int32_t *ids, int T, int k, int E, int BM, int cap, int32_t *sorted_ids,
+                        int32_t *block_expert, int32_t *counts, int32_t *offsets, int32_t *total_padded,
+                        int32_t *hist, hipStream_t s);
+hipError_t launch_gate_up(int fmt, const GateUpArgs &a, int n_shared_sub, hipStream_t s);
+hipError_t launch_down(int fmt, const DownArgs &a, int n_shared_sub, hipStream_t s);
+hipError_t launch_combine(const float *Y, int T, int k, int H, int has_shared, void *out, int out_bf16,
+                          hipStream_t s);
+
+}  // namespace qmoe

@@ -1,0 +1,42 @@
+"""Helpers of the GPU parity tests: upload synthetic inputs, run the HIP path through the
+binding, and compare with the oracle at the stated tolerance."""
+import numpy as np
+import torch
+
+import quantized_moe_expert_topk_amd as qm
+
+
+def tol(ref: np.ndarray) -> float:
+    """Output acceptance: max|delta| <= 1e-2 * max|ref| + 1e-3."""
+    return 1e-2 * float(np.abs(ref).max()) + 1e-3
+
+
+def to_dev(a: np.ndarray | None, dev="cuda"):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def device_bank(b, dev="cuda") -> qm.DeviceBank:
+    return qm.DeviceBank(b.fmt, b.E, b.H, b.I, to_dev(b.gate_up, dev), to_dev(b.gate_up_scale, dev),
+                         to_dev(b.down, dev), to_dev(b.down_scale, dev), to_dev(b.gate_up_global, dev),
+                         to_dev(b.down_global, dev))
+
+
+def bf16_dev(bits: np.ndarray, dev="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits)).view(torch.bfloat16).to(dev)
+
+
+def check_close(name, got: np.ndarray, ref: np.ndarray, report=None):
+    err = float(np.abs(got.astype(np.float64) - ref).max())
+    t = tol(ref)
+    print(f"[parity] {name}: max|d|={err:.3e} tol={t:.3e} max|ref|={np.abs(ref).max():.3e} ratio={err / t:.3f}",
+          flush=True)
+    if report is not None:
+        report[name] = dict(err=err, tol=t)
+    assert err <= t, f"{name}: max|delta| {err:.3e} > tol {t:.3e}"
+    return err
+
+
+def align_np(al: qm.AlignOut) -> dict:
+    return dict(sorted_ids=al.sorted_ids.cpu().numpy(), block_expert=al.block_expert.cpu().numpy(),
+                counts=al.counts.cpu().numpy(), offsets=al.offsets.cpu().numpy(),
+                total_padded=al.total_padded.cpu().numpy())

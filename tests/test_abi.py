@@ -1,0 +1,118 @@
+"""Host-side checks of the C ABI (CPU only): the library loads, exports every entry point
+include/qmoe.h declares, and rejects bad arguments with the documented codes before it
+touches a device.  No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_moe_expert_topk_amd as qm
+from quantized_moe_expert_topk_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # a non-NULL pointer value; validation never dereferences it
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "qmoe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_entry_point():
+    names = _header_functions()
+    assert set(names) == set(L.EXPORTS), names
+    lib = L.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = L.lib()
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.moe_status_string(code)
+    assert lib.moe_status_string(-99) == b"unknown status"
+
+
+def test_align_capacity_and_workspace_sizes():
+    assert qm.moe_align_capacity(16, 2, 8, 16) == 32 + 8 * 15 + 8  # 160 rounded up to 16 -> 160
+    for T, k, E, bm in [(1, 8, 256, 16), (64, 8, 256, 16), (8192, 8, 256, 64), (0, 8, 256, 16)]:
+        c = qm.moe_align_capacity(T, k, E, bm)
+        assert c % bm == 0 and c >= T * k + E * (bm - 1) and c - (T * k + E * (bm - 1)) < bm
+    assert qm.moe_align_capacity(-1, 8, 256, 16) == -1
+    assert qm.moe_align_workspace_bytes(8192, 8, 256) == 64 * 256 * 4
+    assert qm.moe_align_workspace_bytes(0, 8, 256) == 0
+
+
+def _bank(fmt=1, E=8, H=256, I=128, glob=True):
+    return L.MoeBankStruct(fmt, E, H, I, FAKE, FAKE, FAKE if glob else None, FAKE, FAKE, FAKE if glob else None)
+
+
+def _align(bm=16, cap=None, T=16, k=2, E=8):
+    cap = qm.moe_align_capacity(T, k, E, bm) if cap is None else cap
+    return L.MoeAlignOutStruct(FAKE, FAKE, FAKE, FAKE, FAKE, bm, cap)
+
+
+def _fwd(bank=None, shared=None, T=16, k=2, lo=0, hi=128, al=None, ws=1 << 30, out_dtype=0, x=FAKE):
+    lib = L.lib()
+    bank = bank or _bank()
+    al = al or _align(T=T, k=k, E=bank.E)
+    rc = lib.moe_expert_forward(ctypes.byref(bank), ctypes.byref(shared) if shared else None, x, T, k, FAKE,
+                                ctypes.byref(al), lo, hi, FAKE, out_dtype, FAKE, ws, None)
+    return rc, lib.moe_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lo=8, hi=128), L.MOE_ERR_ALIGNMENT),                 # NVFP4 block is 16
+    (dict(lo=64, hi=64), L.MOE_ERR_ALIGNMENT),                 # empty slice
+    (dict(lo=0, hi=144), L.MOE_ERR_ALIGNMENT),                 # past I
+    (dict(lo=-16, hi=64), L.MOE_ERR_ALIGNMENT),
+    (dict(lo=16, hi=128), L.MOE_ERR_UNSUPPORTED),              # 16-aligned but the kernels need 32
+    (dict(k=0), L.MOE_ERR_INVALID_ARG),
+    (dict(k=9), L.MOE_ERR_INVALID_ARG),                        # k > E
+    (dict(T=-1), L.MOE_ERR_INVALID_ARG),
+    (dict(ws=100), L.MOE_ERR_WORKSPACE),
+    (dict(bank=_bank(fmt=7)), L.MOE_ERR_INVALID_ARG),
+    (dict(bank=_bank(glob=False)), L.MOE_ERR_INVALID_ARG),     # NVFP4 needs globals
+    (dict(bank=_bank(H=200)), L.MOE_ERR_UNSUPPORTED),
+    (dict(bank=_bank(fmt=2, I=192), hi=128), L.MOE_ERR_ALIGNMENT),  # fp8-block I % 128
+    (dict(bank=_bank(fmt=2, I=256), lo=64, hi=192), L.MOE_ERR_ALIGNMENT),  # fp8-block slice % 128
+    (dict(bank=_bank(fmt=3), lo=16, hi=128), L.MOE_ERR_ALIGNMENT),  # MXFP4 block is 32
+    (dict(al=_align(bm=8)), L.MOE_ERR_UNSUPPORTED),
+    (dict(al=_align(cap=32)), L.MOE_ERR_INVALID_ARG),
+    (dict(shared=_bank(E=2)), L.MOE_ERR_INVALID_ARG),          # shared must be one expert
+    (dict(shared=_bank(E=1, I=64)), L.MOE_ERR_INVALID_ARG),    # and the same I
+    (dict(out_dtype=5), L.MOE_ERR_INVALID_ARG),
+    (dict(x=None), L.MOE_ERR_INVALID_ARG),
+])
+def test_forward_rejects_bad_arguments_before_any_launch(kw, code):
+    rc, msg = _fwd(**kw)
+    assert rc == code, (rc, msg)
+    assert msg
+
+
+def test_route_and_align_reject_bad_arguments():
+    lib = L.lib()
+    assert lib.moe_route(None, 4, 256, FAKE, 8, None, 2, 1, FAKE, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(FAKE, 4, 256, FAKE, 8, None, 9, 1, FAKE, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(FAKE, 4, 200, FAKE, 8, None, 2, 1, FAKE, FAKE, FAKE, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route(FAKE, 4, 256, FAKE, 2048, None, 2, 1, FAKE, FAKE, FAKE, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route_from_logits(FAKE, 4, 8, None, 0, 1, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    al = _align(T=16, k=2, E=8)
+    assert lib.moe_align(FAKE, 16, 2, 8, ctypes.byref(al), FAKE, 0, None) == L.MOE_ERR_WORKSPACE
+    assert lib.moe_align(None, 16, 2, 8, ctypes.byref(al), FAKE, 1 << 20, None) == L.MOE_ERR_INVALID_ARG
+    small = _align(cap=16)
+    assert lib.moe_align(FAKE, 16, 2, 8, ctypes.byref(small), FAKE, 1 << 20, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_align(FAKE, 16, 2, 2048, ctypes.byref(al), FAKE, 1 << 20, None) == L.MOE_ERR_UNSUPPORTED
+
+
+def test_workspace_bytes_formula():
+    b = _bank(E=8, H=256, I=128)
+    s = _bank(E=1, H=256, I=128)
+    lib = L.lib()
+    T, k, bm = 16, 2, 16
+    cap = qm.moe_align_capacity(T, k, 8, bm)
+    h = -(-((cap + 16) * 64 * 2) // 256) * 256
+    y = -(-((T * k + T) * 256 * 4) // 256) * 256
+    assert lib.moe_workspace_bytes(ctypes.byref(b), ctypes.byref(s), T, k, bm, 0, 64) == h + y

@@ -1,0 +1,242 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Routing selection and alignment are compared bit for bit; expert outputs must meet
+max|delta| <= 1e-2 * max|ref| + 1e-3.  Inputs come from the seeded generator or from the
+oracle, never from the GPU path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import quantized_moe_expert_topk_amd as qm
+from oracle import oracle as O
+from synth import synth as S
+from tests.gpu_util import align_np, bf16_dev, check_close, device_bank, to_dev
+
+pytestmark = pytest.mark.gpu
+
+NEAR_TIE = 1e-5  # fp32 logit gap below which the k-th/(k+1)-th choice is not pinned
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    qm.lib()
+    yield
+
+
+_cache = {}
+
+
+def inputs_for(cid, T, batch=0, experts="routed"):
+    """Layer inputs of config `cid` for T tokens with only the experts the oracle routes to
+    materialised (plus the oracle routing).  Cached per (cid, T, batch)."""
+    key = (cid, T, batch)
+    if key not in _cache:
+        cfg = S.CONFIGS[cid]
+        base = S.layer_inputs(cfg, T, batch=batch, experts=[])
+        lg, ids, w, gap = O.route(base.x, base.router, base.bias, cfg.k, cfg.renormalize)
+        inp = S.layer_inputs(cfg, T, batch=batch, experts=np.unique(ids))
+        _cache[key] = (inp, dict(logits=lg, ids=ids, w=w, gap=gap))
+    return _cache[key]
+
+
+def dev_banks(inp):
+    key = ("dev", id(inp))
+    if key not in _cache:
+        _cache[key] = (device_bank(inp.routed), device_bank(inp.shared) if inp.shared is not None else None)
+    return _cache[key]
+
+
+# ----------------------------------------------------------------------------- routing
+
+@pytest.mark.parametrize("T,E,k,renorm,with_bias", [
+    (1, 256, 8, True, False), (16, 8, 2, True, False), (300, 256, 8, True, True), (77, 1000, 64, True, False),
+    (33, 64, 6, False, False), (5, 3, 3, True, False),
+])
+def test_route_from_logits_selection_is_bit_exact(T, E, k, renorm, with_bias):
+    lg = S.logits_f32(7, E + k, T, E)
+    lg[:, E // 2] = lg[:, 1]                      # exact ties: index 1 must rank first
+    if T > 3:
+        lg[3, :] = np.float32(0.25)               # a row of all-equal logits
+    bias = S.zipf_bias(8, E, 1.1) if with_bias else None
+    eff = lg + bias if with_bias else lg          # the fp32 add the kernel does
+    ids_ref, w_ref, _ = O.topk(eff.astype(np.float64), k, renorm)
+    ids, w = qm.moe_route_from_logits(to_dev(lg), k, to_dev(bias), renorm)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ids_ref)
+    assert np.abs(w.cpu().numpy() - w_ref).max() <= 2e-6
+
+
+@pytest.mark.parametrize("cid,T", [(1, 16), (2, 1), (2, 64), (4, 64), (5, 16), (3, 8192)])
+def test_route_matches_oracle(cid, T):
+    cfg = S.CONFIGS[cid]
+    x = S.tokens(cfg.seed, T, cfg.H)
+    wr = S.router_weight(cfg.seed, cfg.E, cfg.H)
+    bias = S.zipf_bias(cfg.seed, cfg.E, cfg.zipf_s) if cfg.zipf_s else None
+    lg_ref, ids_ref, w_ref, gap = O.route(x, wr, bias, cfg.k, cfg.renormalize)
+    lg, ids, w = qm.moe_route(bf16_dev(x), bf16_dev(wr), to_dev(bias), cfg.k, cfg.renormalize)
+    lerr = np.abs(lg.cpu().numpy() - lg_ref).max()
+    assert lerr <= 5e-6, lerr
+    sure = gap > NEAR_TIE
+    print(f"[route] cfg{cid} T={T}: max logit err {lerr:.2e}, near-tie tokens {int((~sure).sum())}", flush=True)
+    ids_g = ids.cpu().numpy()
+    np.testing.assert_array_equal(ids_g[sure], ids_ref[sure])
+    assert np.abs(w.cpu().numpy()[sure] - w_ref[sure]).max() <= 1e-5
+    # near-tie tokens: the picks must still be a valid top-k within the tie window
+    for t in np.nonzero(~sure)[0]:
+        kth = np.sort(lg_ref[t])[::-1][cfg.k - 1]
+        assert (lg_ref[t][ids_g[t]] >= kth - 2 * NEAR_TIE).all()
+
+
+def test_route_is_deterministic():
+    cfg = S.CONFIGS[3]
+    x = bf16_dev(S.tokens(cfg.seed, 4096, cfg.H))
+    wr = bf16_dev(S.router_weight(cfg.seed, cfg.E, cfg.H))
+    a = qm.moe_route(x, wr, None, 8)
+    b = qm.moe_route(x, wr, None, 8)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+# ----------------------------------------------------------------------------- alignment
+
+@pytest.mark.parametrize("T,k,E,bm,kind", [
+    (16, 2, 8, 16, "rand"), (1, 8, 256, 16, "rand"), (64, 8, 256, 16, "rand"), (8192, 8, 256, 64, "rand"),
+    (4096, 8, 256, 32, "rand"), (130, 8, 1000, 16, "rand"), (3000, 4, 7, 128, "rand"), (1, 1, 1, 16, "rand"),
+    (500, 8, 256, 16, "one_expert"), (257, 3, 256, 256, "two_experts"), (8192, 8, 256, 16, "zipf"),
+])
+def test_align_is_bit_exact(T, k, E, bm, kind):
+    if kind == "rand":
+        ids = S.randint(13, T * 31 + E, T * k, E).reshape(T, k)
+    elif kind == "one_expert":
+        ids = np.full((T, k), E // 3, np.int32)
+    elif kind == "two_experts":
+        ids = np.where(np.arange(T * k) % 5 == 0, 0, E - 1).astype(np.int32).reshape(T, k)
+    else:
+        cfg = S.CONFIGS[3]
+        x = S.tokens(cfg.seed, T, cfg.H)
+        _, ids, _, _ = O.route(x, S.router_weight(cfg.seed, E, cfg.H), S.zipf_bias(cfg.seed, E, 1.1), k)
+    ref = O.align(ids, E, bm)
+    out = qm.moe_align(to_dev(ids), E, bm)
+    got = align_np(out)
+    for key in ref:
+        np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
+    again = align_np(qm.moe_align(to_dev(ids), E, bm))
+    for key in ref:
+        np.testing.assert_array_equal(again[key], got[key], err_msg=key)
+
+
+# ----------------------------------------------------------------------------- expert layer
+
+def _forward_gpu(inp, ids, w, lo, hi, bm=None, out_dtype=torch.float32, banks=None):
+    cfg = inp.cfg
+    T = ids.shape[0]
+    bm = bm or qm.choose_block_m(T, cfg.k, cfg.E)
+    rb, sb = banks or dev_banks(inp)
+    al = qm.moe_align(to_dev(ids), cfg.E, bm)
+    out = qm.moe_expert_forward(rb, sb, bf16_dev(inp.x), to_dev(w.astype(np.float32)), al, lo, hi,
+                                out_dtype=out_dtype)
+    return out.float().cpu().numpy()
+
+
+FORWARD_CASES = [(1, 16, (0, 128)), (1, 16, (0, 64)), (1, 16, (64, 128)),
+                 (2, 1, (0, 256)), (2, 8, (0, 256)), (2, 32, (0, 256)), (2, 64, (0, 256)), (2, 64, (0, 512)),
+                 (2, 1, (0, 512)),
+                 (4, 1, (0, 256)), (4, 64, (0, 256)), (4, 64, (0, 512)),
+                 (5, 1, (0, 1024)), (5, 16, (0, 1024)), (5, 16, (1024, 2048))]
+
+
+@pytest.mark.parametrize("cid,T,sl", FORWARD_CASES)
+def test_expert_forward_matches_oracle(cid, T, sl):
+    """Oracle routing fed to both sides; GPU align + gate_up + down + combine vs oracle."""
+    inp, r = inputs_for(cid, T)
+    lo, hi = sl
+    ref = O.expert_forward(inp.routed, inp.shared, inp.x, r["ids"], r["w"], lo, hi)
+    got = _forward_gpu(inp, r["ids"], r["w"], lo, hi)
+    check_close(f"cfg{cid} T={T} slice=[{lo},{hi})", got, ref)
+
+
+@pytest.mark.parametrize("bm", [16, 32, 64, 128])
+def test_expert_forward_any_block_m(bm):
+    inp, r = inputs_for(2, 64)
+    ref = O.expert_forward(inp.routed, inp.shared, inp.x, r["ids"], r["w"], 0, 256)
+    check_close(f"cfg2 T=64 bm={bm}", _forward_gpu(inp, r["ids"], r["w"], 0, 256, bm=bm), ref)
+
+
+@pytest.mark.parametrize("cid,T,sl", [(1, 16, (0, 128)), (2, 64, (0, 256)), (5, 16, (0, 1024))])
+def test_full_layer_matches_oracle(cid, T, sl):
+    """The whole GPU path (route -> align -> forward) against the whole oracle layer,
+    excluding tokens whose k-th/(k+1)-th logit gap is inside the near-tie window."""
+    inp, r = inputs_for(cid, T)
+    cfg = inp.cfg
+    lo, hi = sl
+    rb, sb = dev_banks(inp)
+    bias = to_dev(inp.bias) if inp.bias is not None else None
+    layer = qm.MoeLayer(rb, sb, bf16_dev(inp.router), bias, T, cfg.k, lo, hi, cfg.renormalize)
+    got = layer(bf16_dev(inp.x)).cpu().numpy()
+    sure = r["gap"] > NEAR_TIE
+    np.testing.assert_array_equal(layer.ids.cpu().numpy()[sure], r["ids"][sure])
+    ref = O.expert_forward(inp.routed, inp.shared, inp.x, r["ids"], r["w"], lo, hi)
+    check_close(f"full layer cfg{cid} T={T} [{lo},{hi})", got[sure], ref[sure])
+
+
+@pytest.mark.parametrize("cid,T,cuts", [(1, 16, (0, 64, 128)), (2, 64, (0, 256, 512)), (4, 64, (0, 256, 512)),
+                                        (2, 8, (0, 128, 384, 512))])
+def test_gpu_slices_sum_to_gpu_full(cid, T, cuts):
+    """Linearity in the intermediate index on the GPU: disjoint slices tiling [0, I) sum to
+    the unsliced GPU result (issue #520 section 4)."""
+    inp, r = inputs_for(cid, T)
+    full = _forward_gpu(inp, r["ids"], r["w"], 0, inp.cfg.I)
+    parts = sum(_forward_gpu(inp, r["ids"], r["w"], lo, hi) for lo, hi in zip(cuts[:-1], cuts[1:]))
+    check_close(f"slice sum cfg{cid} T={T} cuts={cuts}", parts, full.astype(np.float64))
+
+
+def test_pre_sliced_bank_equals_slice_of_full_bank():
+    """A rank's own storage [0, Il) gives bit-identical results to [lo, hi) of the full bank."""
+    inp, r = inputs_for(2, 32)
+    for lo, hi in ((0, 256), (256, 512), (128, 384)):
+        full = _forward_gpu(inp, r["ids"], r["w"], lo, hi)
+        own = (device_bank(S.slice_bank(inp.routed, lo, hi)), device_bank(S.slice_bank(inp.shared, lo, hi)))
+        mine = _forward_gpu(inp, r["ids"], r["w"], 0, hi - lo, banks=own)
+        np.testing.assert_array_equal(mine, full)
+
+
+def test_negative_control_mis_sliced_up_rows_fails_parity():
+    """Up rows taken at Il+lo instead of I+lo (a mis-sliced bank handed to the GPU) must be
+    caught by the parity check: the check is sensitive (issue #520 section 5)."""
+    inp, r = inputs_for(2, 32)
+    lo, hi = 0, 256
+    ref = O.expert_forward(inp.routed, inp.shared, inp.x, r["ids"], r["w"], lo, hi)
+    bad = S.slice_bank(inp.routed, lo, hi)
+    bad.gate_up[:, 256:] = inp.routed.gate_up[:, 256:512]
+    bad.gate_up_scale[:, 256:] = inp.routed.gate_up_scale[:, 256:512]
+    bad.gate_up_global[:, 256:] = inp.routed.gate_up_global[:, 256:512]
+    got = _forward_gpu(inp, r["ids"], r["w"], 0, hi - lo,
+                       banks=(device_bank(bad), device_bank(S.slice_bank(inp.shared, lo, hi))))
+    err = np.abs(got - ref).max()
+    tol = 1e-2 * np.abs(ref).max() + 1e-3
+    print(f"[negative control] max|d|={err:.3e} vs tol {tol:.3e}", flush=True)
+    assert err > tol
+
+
+def test_forward_is_deterministic_and_bf16_output_matches():
+    inp, r = inputs_for(2, 64)
+    a = _forward_gpu(inp, r["ids"], r["w"], 0, 256)
+    b = _forward_gpu(inp, r["ids"], r["w"], 0, 256)
+    np.testing.assert_array_equal(a, b)
+    c = _forward_gpu(inp, r["ids"], r["w"], 0, 256, out_dtype=torch.bfloat16)
+    ref = O.expert_forward(inp.routed, inp.shared, inp.x, r["ids"], r["w"], 0, 256)
+    check_close("cfg2 T=64 bf16 out", c, ref)
+    np.testing.assert_array_equal(c, torch.from_numpy(a).to(torch.bfloat16).float().numpy())
+
+
+def test_zero_tokens_is_a_no_op():
+    inp, r = inputs_for(1, 16)
+    rb, sb = dev_banks(inp)
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((0, 2), dtype=torch.int32, device="cuda")
+    al = qm.moe_align(ids, 8, 16)
+    out = qm.moe_expert_forward(rb, None, x, torch.empty((0, 2), device="cuda"), al, 0, 128)
+    assert out.shape == (0, 256)
+    lg, i2, w2 = qm.moe_route(x, bf16_dev(inp.router), None, 2)
+    assert i2.shape == (0, 2)
