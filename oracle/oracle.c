@@ -331,3 +331,11 @@ void oracle_dequant_down(const oracle_bank *b, int e, double *out) {
   for (int n = 0; n < b->H; n++)
     for (int i = 0; i < b->I; i++) out[(size_t)n * b->I + i] = oracle_weight_down(b, e, n, i);
 }
+
+/* Threads the OpenMP loops above use (1 when built without OpenMP). */
+#ifdef _OPENMP
+#include <omp.h>
+int oracle_num_threads(void) { return omp_get_max_threads(); }
+#else
+int oracle_num_threads(void) { return 1; }
+#endif

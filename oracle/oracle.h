@@ -46,5 +46,6 @@ int oracle_expert_forward(const oracle_bank *routed, const oracle_bank *shared, 
                           double *out);
 void oracle_dequant_gate_up(const oracle_bank *b, int e, double *out);
 void oracle_dequant_down(const oracle_bank *b, int e, double *out);
+int oracle_num_threads(void);
 
 #endif

@@ -63,6 +63,8 @@ def lib():
         L.oracle_expert_forward.argtypes = [pb, pb, vp, i32, i32, vp, vp, i32, i32, vp]
         L.oracle_dequant_gate_up.argtypes = [pb, i32, vp]
         L.oracle_dequant_down.argtypes = [pb, i32, vp]
+        L.oracle_num_threads.restype = i32
+        L.oracle_num_threads.argtypes = []
         _lib = L
     return _lib
 
@@ -83,6 +85,10 @@ def bank_struct(bank) -> _Bank:
 
 
 # ----------------------------------------------------------------------------- scalars
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())
+
 
 def e2m1(code: int) -> float:
     return lib().oracle_e2m1(code)

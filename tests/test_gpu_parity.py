@@ -240,3 +240,28 @@ def test_zero_tokens_is_a_no_op():
     assert out.shape == (0, 256)
     lg, i2, w2 = qm.moe_route(x, bf16_dev(inp.router), None, 2)
     assert i2.shape == (0, 2)
+
+
+def test_graph_replays_match_eager():
+    """The three calls captured in a HIP graph: every replay (with eager work and
+    synchronisations in between) reproduces the eager result bit for bit."""
+    inp, r = inputs_for(2, 32)
+    cfg = inp.cfg
+    rb, sb = dev_banks(inp)
+    layer = qm.MoeLayer(rb, sb, bf16_dev(inp.router), None, 32, cfg.k, 0, 256)
+    x = bf16_dev(inp.x)
+    eager = layer(x).clone()
+    ids_eager = layer.ids.clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer(x)
+    other = qm.MoeLayer(rb, sb, bf16_dev(inp.router), None, 32, cfg.k, 256, 512)
+    for _ in range(3):
+        layer.out.zero_()
+        layer.ids.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(layer.out, eager) and torch.equal(layer.ids, ids_eager)
+        other(x)  # eager work between replays
+        torch.cuda.synchronize()
