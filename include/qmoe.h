@@ -99,15 +99,18 @@ typedef struct {
  *   w_router_bf16 [E, H] bf16 router weight.
  *   bias          [E] f32 added to every token's logits, or NULL.
  *   logits        [T, E] f32 output: logits[t,e] = sum_h x[t,h] W[e,h] + bias[e]
- *                 (fp32 accumulation of exact bf16 products).
+ *                 (fp32 accumulation of exact bf16 products, summed in a fixed order).
  *   topk_ids      [T, k] int32 output: the k experts ranking first under
  *                 (logit descending, expert index ascending), in that order.
  *   topk_w        [T, k] f32 output: softmax over the k selected logits when renormalize
  *                 != 0, else the full softmax probability of each selected expert.
- * Requires 1 <= k <= E <= 1024 and H % 128 == 0. */
+ *   workspace     >= moe_route_workspace_bytes(T, H, E) bytes (split-K partial logits of
+ *                 small batches; 0 bytes, and NULL allowed, for large ones).
+ * Requires 1 <= k <= min(E, 64), E <= 1024 and H % 128 == 0.  Deterministic. */
+size_t moe_route_workspace_bytes(int T, int H, int E);
 int moe_route(const void *x_bf16, int T, int H, const void *w_router_bf16, int E,
               const float *bias, int k, int renormalize, float *logits, int32_t *topk_ids,
-              float *topk_w, void *stream);
+              float *topk_w, void *workspace, size_t workspace_bytes, void *stream);
 
 /* moe_route_from_logits -- the selection step of moe_route on caller-supplied f32 logits
  * [T, E] (plus bias[e] if non-NULL, added in f32 before selection).  Same outputs and

@@ -6,4 +6,5 @@ The compute lives in ``libqmoe.so`` (hand-written HIP kernels behind the C ABI o
 from ._lib import EXPORTS, LIB_PATH, MoeError, lib  # noqa: F401
 from .api import (AlignOut, DeviceBank, MoeLayer, alloc_align, choose_block_m, moe_align,  # noqa: F401
                   moe_align_capacity, moe_align_workspace_bytes, moe_expert_down, moe_expert_forward,
-                  moe_expert_gate_up, moe_route, moe_route_from_logits, moe_workspace_bytes)
+                  moe_expert_gate_up, moe_route, moe_route_from_logits, moe_route_workspace_bytes,
+                  moe_workspace_bytes)

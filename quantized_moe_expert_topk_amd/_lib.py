@@ -19,7 +19,7 @@ MOE_FMT = {"nvfp4": 1, "fp8blk": 2, "mxfp4": 3}
 MOE_OUT_F32, MOE_OUT_BF16 = 0, 1
 
 # every entry point include/qmoe.h declares
-EXPORTS = ("moe_route", "moe_route_from_logits", "moe_align_capacity", "moe_align_workspace_bytes", "moe_align",
+EXPORTS = ("moe_route", "moe_route_workspace_bytes", "moe_route_from_logits", "moe_align_capacity", "moe_align_workspace_bytes", "moe_align",
            "moe_workspace_bytes", "moe_expert_forward", "moe_expert_gate_up", "moe_expert_down",
            "moe_status_string", "moe_last_error")
 
@@ -59,7 +59,9 @@ def lib() -> ctypes.CDLL:
         i32, vp, sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
         pb = ctypes.POINTER(MoeBankStruct)
         pa = ctypes.POINTER(MoeAlignOutStruct)
-        L.moe_route.argtypes = [vp, i32, i32, vp, i32, vp, i32, i32, vp, vp, vp, vp]
+        L.moe_route.argtypes = [vp, i32, i32, vp, i32, vp, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.moe_route_workspace_bytes.argtypes = [i32, i32, i32]
+        L.moe_route_workspace_bytes.restype = sz
         L.moe_route_from_logits.argtypes = [vp, i32, i32, vp, i32, i32, vp, vp, vp]
         L.moe_align_capacity.argtypes = [i32, i32, i32, i32]
         L.moe_align_capacity.restype = ctypes.c_int32

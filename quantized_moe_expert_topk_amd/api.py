@@ -74,8 +74,12 @@ class AlignOut:
 
 # ----------------------------------------------------------------------------- routing
 
+def moe_route_workspace_bytes(T: int, H: int, E: int) -> int:
+    return int(lib().moe_route_workspace_bytes(T, H, E))
+
+
 def moe_route(x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor | None, k: int, renormalize: bool = True,
-              logits=None, topk_ids=None, topk_w=None, stream=None):
+              logits=None, topk_ids=None, topk_w=None, workspace=None, stream=None):
     """Router logits, top-k ids and weights.  x [T,H] bf16, w_router [E,H] bf16, bias [E] f32."""
     T, H = x.shape
     E = w_router.shape[0]
@@ -90,8 +94,13 @@ def moe_route(x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor | None
     _need(logits, torch.float32, (T, E), "logits")
     _need(topk_ids, torch.int32, (T, k), "topk_ids")
     _need(topk_w, torch.float32, (T, k), "topk_w")
+    need = moe_route_workspace_bytes(T, H, E)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     check("moe_route", lib().moe_route(_ptr(x), T, H, _ptr(w_router), E, _ptr(bias), k, int(renormalize),
-                                       _ptr(logits), _ptr(topk_ids), _ptr(topk_w), _stream(stream)))
+                                       _ptr(logits), _ptr(topk_ids), _ptr(topk_w), _ptr(workspace), ws_bytes,
+                                       _stream(stream)))
     return logits, topk_ids, topk_w
 
 
@@ -228,12 +237,14 @@ class MoeLayer:
         self.w = torch.empty((T, k), dtype=torch.float32, device=dev)
         self.align = alloc_align(T, k, E, self.block_m, dev)
         self.align_ws = torch.empty(max(moe_align_workspace_bytes(T, k, E), 1), dtype=torch.uint8, device=dev)
+        self.route_ws = torch.empty(max(moe_route_workspace_bytes(T, routed.H, E), 1), dtype=torch.uint8, device=dev)
         self.ws = torch.empty(max(moe_workspace_bytes(routed, shared, T, k, self.block_m, slice_lo, slice_hi), 1),
                               dtype=torch.uint8, device=dev)
         self.out = torch.empty((T, routed.H), dtype=out_dtype, device=dev)
 
     def __call__(self, x: torch.Tensor, stream=None) -> torch.Tensor:
-        moe_route(x, self.w_router, self.bias, self.k, self.renormalize, self.logits, self.ids, self.w, stream)
+        moe_route(x, self.w_router, self.bias, self.k, self.renormalize, self.logits, self.ids, self.w,
+                  self.route_ws, stream)
         moe_align(self.ids, self.routed.E, self.block_m, self.align, self.align_ws, stream)
         moe_expert_forward(self.routed, self.shared, x, self.w, self.align, self.lo, self.hi, self.out,
                            self.out.dtype, self.ws, stream)

@@ -75,6 +75,19 @@ const char *format_name(int fmt) {
   }
 }
 
+// gate_up K split: H = 128 * kwaves * ksteps with kwaves <= 4 and ksteps <= 8 (kwaves as
+// large as possible).  Returns false if H has no such factorisation.
+bool gate_up_ksplit(int H, int *kwaves, int *ksteps) {
+  const int n = H / 128;
+  for (int w = 4; w >= 1; w--)
+    if (n % w == 0 && n / w <= 8) {
+      *kwaves = w;
+      *ksteps = n / w;
+      return true;
+    }
+  return false;
+}
+
 int check_bank(const moe_bank *b, const char *name) {
   if (!b) return fail(MOE_ERR_INVALID_ARG, "%s bank is NULL", name);
   const int blk = format_block(b->fmt);
@@ -89,8 +102,9 @@ int check_bank(const moe_bank *b, const char *name) {
   if (b->I % blk)
     return fail(MOE_ERR_ALIGNMENT, "%s bank: I=%d is not a multiple of the %s block %d", name, b->I,
                 format_name(b->fmt), blk);
-  if (b->H % 128)
-    return fail(MOE_ERR_UNSUPPORTED, "%s bank: H=%d must be a multiple of 128 (K tile)", name, b->H);
+  int kw, ks;
+  if (b->H % 128 || !gate_up_ksplit(b->H, &kw, &ks))
+    return fail(MOE_ERR_UNSUPPORTED, "%s bank: H=%d must be 128 * w * s with w <= 4 and s <= 8", name, b->H);
   if (b->I % 32)
     return fail(MOE_ERR_UNSUPPORTED, "%s bank: I=%d must be a multiple of 32 (row pitch of 16-byte loads)",
                 name, b->I);
@@ -192,6 +206,7 @@ qmoe::GateUpArgs gate_up_args(const moe_bank *routed, const moe_bank *shared, co
   a.n_routed_sub = p.n_routed_sub;
   a.lo = lo;
   a.Il = p.Il;
+  gate_up_ksplit(routed->H, &a.kwaves, &a.ksteps);
   a.h = static_cast<uint16_t *>(workspace);
   return a;
 }
@@ -200,6 +215,7 @@ qmoe::DownArgs down_args(const moe_bank *routed, const moe_bank *shared, int T, 
                          const moe_align_out *al, int lo, const FwdPlan &p, void *workspace) {
   qmoe::DownArgs a;
   a.h = static_cast<const uint16_t *>(workspace);
+  a.h_rows = al->capacity + p.shared_rows;
   a.T = T;
   a.H = routed->H;
   a.k = k;
@@ -279,8 +295,14 @@ size_t moe_workspace_bytes(const moe_bank *routed, const moe_bank *shared, int T
   return plan_forward(routed, shared, T, k, cap, slice_lo, slice_hi).total;
 }
 
+size_t moe_route_workspace_bytes(int T, int H, int E) {
+  if (T <= 0 || H < 128 || E < 1) return 0;
+  return qmoe::router_workspace_bytes(T, E, H);
+}
+
 int moe_route(const void *x_bf16, int T, int H, const void *w_router_bf16, int E, const float *bias, int k,
-              int renormalize, float *logits, int32_t *topk_ids, float *topk_w, void *stream) {
+              int renormalize, float *logits, int32_t *topk_ids, float *topk_w, void *workspace,
+              size_t workspace_bytes, void *stream) {
   if (!w_router_bf16 || (T > 0 && (!x_bf16 || !logits || !topk_ids || !topk_w)))
     return fail(MOE_ERR_INVALID_ARG, "moe_route: NULL required pointer");
   if (T < 0 || H < 1 || E < 1) return fail(MOE_ERR_INVALID_ARG, "moe_route: T=%d H=%d E=%d", T, H, E);
@@ -288,15 +310,17 @@ int moe_route(const void *x_bf16, int T, int H, const void *w_router_bf16, int E
   if (E > 1024 || k > 64) return fail(MOE_ERR_UNSUPPORTED, "moe_route: needs E <= 1024 and k <= 64");
   if (H % 128) return fail(MOE_ERR_UNSUPPORTED, "moe_route: H=%d must be a multiple of 128", H);
   if (T > 16 * 65535) return fail(MOE_ERR_UNSUPPORTED, "moe_route: T=%d too large", T);
+  const size_t need = moe_route_workspace_bytes(T, H, E);
+  if (workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "moe_route: workspace %zu < %zu", workspace_bytes, need);
+  if (need && !workspace) return fail(MOE_ERR_INVALID_ARG, "moe_route: workspace is NULL");
   int rc = check_device();
   if (rc) return rc;
   if (T == 0) return ok();
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  rc = hip_status(qmoe::launch_router_logits(static_cast<const uint16_t *>(x_bf16), T, H,
-                                             static_cast<const uint16_t *>(w_router_bf16), E, bias, logits, s),
-                  "router launch");
-  if (rc) return rc;
-  return hip_status(qmoe::launch_topk(logits, T, E, nullptr, k, renormalize, topk_ids, topk_w, s), "topk launch");
+  return hip_status(qmoe::launch_route(static_cast<const uint16_t *>(x_bf16), T, H,
+                                       static_cast<const uint16_t *>(w_router_bf16), E, bias, k, renormalize, logits,
+                                       topk_ids, topk_w, static_cast<float *>(workspace),
+                                       static_cast<hipStream_t>(stream)),
+                    "route launch");
 }
 
 int moe_route_from_logits(const float *logits, int T, int E, const float *bias, int k, int renormalize,

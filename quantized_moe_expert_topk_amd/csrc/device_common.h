@@ -86,5 +86,35 @@ __device__ __forceinline__ void fp8x8_to_bf16(uint32_t lo, uint32_t hi, frag8 &o
   out.h[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
 }
 
+// Buffer resources (wave-uniform, in SGPRs): loads take a 32-bit byte offset, fold
+// constant offsets into the instruction, and return 0 past `bytes` (hardware range check).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Callers pass values that are the same in every lane; readfirstlane states that to the
+// compiler so the descriptor is built in SGPRs.
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t v = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  void *p = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+__device__ __forceinline__ uint32_t buf_load2(rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t buf_load1(rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
 // Wave-wide helpers (wave64).
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63u); }

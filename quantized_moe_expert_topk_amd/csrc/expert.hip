@@ -16,10 +16,13 @@
 //   FP8_BLOCK  e4m3 -> bf16 exact; the fp32 128x128 block scale multiplies each 128-wide
 //              K chunk's partial sum.
 //
-// Tiling: a workgroup is 4 waves and covers 16 rows of the pair list x 64 output columns;
-// wave w owns columns [16w, 16w+16) and runs the whole K loop.  K advances 128 per step;
-// lane group g = l/16 reads the contiguous K run [kc+32g, kc+32g+32) of its row of both
-// operands (the MFMA slots of A and B carry the same K indices).
+// Tiling: a workgroup is 4 waves over 16 rows of the pair list (one aligned sub-block of a
+// single expert).  gate_up: 32 slice columns of gate and of up (4 MFMA tiles), K split over
+// the 4 waves and reduced through LDS.  down: each wave owns 4 x 16 hidden columns over the
+// whole slice.  K advances in 128-wide chunks: lane group g = l/16 reads the contiguous
+// run [kc+32g, kc+32g+32) of its row of both operands (the MFMA slots of A and B carry the
+// same K indices).  A wave issues the loads of 2 chunks before decoding either of them,
+// so the weight bytes are in flight while the VALU dequantizes.
 #include "device_common.h"
 #include "launch.h"
 
@@ -27,52 +30,208 @@ namespace qmoe {
 
 // ---------------------------------------------------------------------------- B operand
 
-// Load + dequantize the 32-element K run [k0, k0+32) of one weight row into 4 fragments
-// (fragment s = K [k0+8s, k0+8s+8)).  `row` is the row index inside the expert's matrix,
-// `K` the matrix width (elements).  For FP8_BLOCK the block scale is applied by the caller.
+// One expert's weight matrix [rows, K] (K = row width in elements) as buffer resources.
 template <int FMT>
-__device__ __forceinline__ void load_b(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
-                                       size_t row, int K, int k0, frag8 (&b)[4]) {
+struct WMat {
+  rsrc_t codes, scales;
+  int K;
+};
+
+template <int FMT>
+__device__ __forceinline__ WMat<FMT> weight_matrix(const uint8_t *codes, const uint8_t *scales, int e, int rows,
+                                                   int K) {
+  WMat<FMT> m;
+  m.K = K;
   if constexpr (FMT == MOE_FMT_NVFP4) {
-    const uint4 c = *reinterpret_cast<const uint4 *>(codes + row * (size_t)(K / 2) + k0 / 2);
-    const uint8_t *sp = scales + row * (size_t)(K / 16) + k0 / 16;
-    const float s0 = e4m3_to_f32(sp[0]), s1 = e4m3_to_f32(sp[1]);
-    fp4x8_mul_to_bf16(c.x, s0, b[0]);
-    fp4x8_mul_to_bf16(c.y, s0, b[1]);
-    fp4x8_mul_to_bf16(c.z, s1, b[2]);
-    fp4x8_mul_to_bf16(c.w, s1, b[3]);
+    m.codes = make_rsrc(codes + (size_t)e * rows * (K / 2), (uint32_t)rows * (K / 2));
+    m.scales = make_rsrc(scales + (size_t)e * rows * (K / 16), (uint32_t)rows * (K / 16));
   } else if constexpr (FMT == MOE_FMT_MXFP4_E8M0) {
-    const uint4 c = *reinterpret_cast<const uint4 *>(codes + row * (size_t)(K / 2) + k0 / 2);
-    const float p = e8m0_to_f32(scales[row * (size_t)(K / 32) + k0 / 32]);
-    fp4x8_pow2_to_bf16(c.x, p, b[0]);
-    fp4x8_pow2_to_bf16(c.y, p, b[1]);
-    fp4x8_pow2_to_bf16(c.z, p, b[2]);
-    fp4x8_pow2_to_bf16(c.w, p, b[3]);
+    m.codes = make_rsrc(codes + (size_t)e * rows * (K / 2), (uint32_t)rows * (K / 2));
+    m.scales = make_rsrc(scales + (size_t)e * rows * (K / 32), (uint32_t)rows * (K / 32));
   } else {
-    const uint4 *cp = reinterpret_cast<const uint4 *>(codes + row * (size_t)K + k0);
-    const uint4 c0 = cp[0], c1 = cp[1];
-    fp8x8_to_bf16(c0.x, c0.y, b[0]);
-    fp8x8_to_bf16(c0.z, c0.w, b[1]);
-    fp8x8_to_bf16(c1.x, c1.y, b[2]);
-    fp8x8_to_bf16(c1.z, c1.w, b[3]);
+    m.codes = make_rsrc(codes + (size_t)e * rows * K, (uint32_t)rows * K);
+    m.scales = make_rsrc(scales + (size_t)e * (rows / 128) * (K / 128) * 4, (uint32_t)(rows / 128) * (K / 128) * 4);
+  }
+  return m;
+}
+
+// Scale run of one lane: NB consecutive scale bytes starting at byte `off` (any
+// alignment), gathered with dword loads and funnel shifts.  Bytes past the resource read
+// as 0 (buffer range check).
+template <int NB>
+struct ScaleRun {
+  uint32_t w[(NB + 3) / 4];
+};
+
+template <int NB>
+__device__ __forceinline__ void load_scale_run(rsrc_t r, uint32_t off, ScaleRun<NB> &s) {
+  if constexpr (NB == 1) {
+    s.w[0] = buf_load1(r, off);
+  } else if constexpr (NB == 2) {
+    s.w[0] = buf_load2(r, off);  // NVFP4 runs start at even bytes
+  } else {
+    constexpr int ND = NB / 4 + 1;  // dwords covering NB bytes at any alignment
+    const uint32_t base = off & ~3u, sh = (off & 3u) * 8;
+    uint32_t d[ND + (ND & 1)];
+    if constexpr (ND == 2) {
+      const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)base, 0, 0));
+      d[0] = v.x;
+      d[1] = v.y;
+    } else {
+#pragma unroll
+      for (int q = 0; q < ND; q += 4) {
+        const uint4 v = buf_load16(r, base + 4 * q);
+        d[q] = v.x;
+        if (q + 1 < ND) d[q + 1] = v.y;
+        if (q + 2 < ND) d[q + 2] = v.z;
+        if (q + 3 < ND) d[q + 3] = v.w;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < NB / 4; q++) s.w[q] = __builtin_amdgcn_alignbit(d[q + 1], d[q], sh);
   }
 }
 
-__device__ __forceinline__ void load_a(const uint16_t *__restrict__ rowp, int k0, bool valid, frag8 (&a)[4]) {
-  const uint4 *p = reinterpret_cast<const uint4 *>(rowp + k0);
+template <int NB>
+__device__ __forceinline__ uint32_t run_byte(const ScaleRun<NB> &s, int i) {  // i: compile-time after unrolling
+  return (s.w[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+}
+
+struct ARaw {
+  uint4 q[4];  // 32 bf16 = one 32-wide K piece of one activation row
+};
+
+// Dequantize a 32-wide piece to 4 bf16 fragments (fragment s = K [8s, 8s+8) of the piece).
+//   NVFP4: codes c (32 nibbles), e4m3 scales s0 (first 16) and s1 (last 16)
+__device__ __forceinline__ void decode_nvfp4(const uint4 &c, uint32_t s0, uint32_t s1, frag8 (&b)[4]) {
+  const float f0 = e4m3_to_f32(s0), f1 = e4m3_to_f32(s1);
+  fp4x8_mul_to_bf16(c.x, f0, b[0]);
+  fp4x8_mul_to_bf16(c.y, f0, b[1]);
+  fp4x8_mul_to_bf16(c.z, f1, b[2]);
+  fp4x8_mul_to_bf16(c.w, f1, b[3]);
+}
+
+__device__ __forceinline__ void decode_mxfp4(const uint4 &c, uint32_t e8, frag8 (&b)[4]) {
+  const float p = e8m0_to_f32(e8);
+  fp4x8_pow2_to_bf16(c.x, p, b[0]);
+  fp4x8_pow2_to_bf16(c.y, p, b[1]);
+  fp4x8_pow2_to_bf16(c.z, p, b[2]);
+  fp4x8_pow2_to_bf16(c.w, p, b[3]);
+}
+
+__device__ __forceinline__ void zero_frags(frag8 (&b)[4]) {
 #pragma unroll
-  for (int s = 0; s < 4; s++) a[s].q = valid ? p[s] : make_uint4(0, 0, 0, 0);
+  for (int q = 0; q < 4; q++) b[q].q = make_uint4(0, 0, 0, 0);
+}
+
+// Multiply-accumulate a wave's K range [kw0, kw0 + 128*COUNT) of one 16-row A block against
+// NT weight tiles; positions at or past kvalid (relative to kw0) contribute zero and load
+// from clamped in-bounds offsets.
+//   FP4 formats: lane group g owns the contiguous run [32*COUNT*g, 32*COUNT*(g+1)) and step
+//     i reads its 32-wide piece i, so a lane's scales for the whole run are one load per tile.
+//   FP8_BLOCK: step i is the 128-wide chunk [128 i, 128 i + 128) and lane group g reads its
+//     piece [32 g, 32 g + 32), so every MFMA stays inside one 128x128 scale block.
+// NPF steps (2 for FP4, 1 for FP8) are loaded before any of them is decoded.
+//   ra, a_row: activation buffer and the byte offset of this lane's row (K index 0)
+//   m, rows:   weight matrix and this lane's row of each tile;  b_k0: K offset in the row
+template <int FMT, int NT, int COUNT>
+__device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FMT> &m, const uint32_t (&rows)[NT],
+                                        int b_k0, int kw0, int kvalid, int g, f32x4_t (&acc)[NT]) {
+  constexpr bool FP4 = FMT != MOE_FMT_FP8_BLOCK128;
+  constexpr int NPF = FP4 ? 2 : 1;  // steps loaded before decoding (FP8 steps carry twice the bytes)
+  const uint32_t K = (uint32_t)m.K;
+  // scale runs (FP4): NVFP4 2 bytes per step, MXFP4 1 byte per step
+  constexpr int SNB = FMT == MOE_FMT_NVFP4 ? 2 * COUNT : COUNT;
+  ScaleRun<FP4 ? SNB : 1> srun[NT];
+  const int grun = 32 * COUNT * g;  // FP4: start of lane group g's run
+  if constexpr (FP4) {
+    const int k = kw0 + (grun < kvalid ? grun : 0);
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+      const uint32_t off = FMT == MOE_FMT_NVFP4 ? rows[t] * (K / 16) + (b_k0 + k) / 16 : rows[t] * (K / 32) + (b_k0 + k) / 32;
+      load_scale_run(m.scales, off, srun[t]);
+    }
+  }
+#pragma unroll
+  for (int i0 = 0; i0 < COUNT; i0 += NPF) {
+    ARaw ar[NPF];
+    uint4 c0[NPF][NT], c1[NPF][NT];
+    float bs[NPF][NT];
+#pragma unroll
+    for (int ii = 0; ii < NPF; ii++) {
+      const int i = i0 + ii;
+      if (i >= COUNT) break;
+      const int kr = FP4 ? grun + 32 * i : 128 * i + 32 * g;  // position relative to kw0
+      const int k = kw0 + (kr < kvalid ? kr : 0);
+#pragma unroll
+      for (int q = 0; q < 4; q++) ar[ii].q[q] = buf_load16(ra, a_row + k * 2 + 16 * q);
+#pragma unroll
+      for (int t = 0; t < NT; t++) {
+        if constexpr (FP4) {
+          c0[ii][t] = buf_load16(m.codes, rows[t] * (K / 2) + (b_k0 + k) / 2);
+        } else {
+          const uint32_t o = rows[t] * K + b_k0 + k;
+          c0[ii][t] = buf_load16(m.codes, o);
+          c1[ii][t] = buf_load16(m.codes, o + 16);
+          bs[ii][t] = buf_load_f32(m.scales, ((rows[t] / 128) * (K / 128) + (b_k0 + kw0 + 128 * i) / 128) * 4);
+        }
+      }
+    }
+#pragma unroll
+    for (int ii = 0; ii < NPF; ii++) {
+      const int i = i0 + ii;
+      if (i >= COUNT) break;
+      const int kr = FP4 ? grun + 32 * i : 128 * i + 32 * g;
+      const bool v = kr < kvalid;
+      frag8 av[4];
+#pragma unroll
+      for (int q = 0; q < 4; q++) av[q].q = ar[ii].q[q];
+#pragma unroll
+      for (int t = 0; t < NT; t++) {
+        frag8 bv[4];
+        if constexpr (FMT == MOE_FMT_NVFP4) {
+          decode_nvfp4(c0[ii][t], run_byte(srun[t], 2 * i), run_byte(srun[t], 2 * i + 1), bv);
+        } else if constexpr (FMT == MOE_FMT_MXFP4_E8M0) {
+          decode_mxfp4(c0[ii][t], run_byte(srun[t], i), bv);
+        } else {
+          fp8x8_to_bf16(c0[ii][t].x, c0[ii][t].y, bv[0]);
+          fp8x8_to_bf16(c0[ii][t].z, c0[ii][t].w, bv[1]);
+          fp8x8_to_bf16(c1[ii][t].x, c1[ii][t].y, bv[2]);
+          fp8x8_to_bf16(c1[ii][t].z, c1[ii][t].w, bv[3]);
+        }
+        if (!v) zero_frags(bv);
+        if constexpr (FMT == MOE_FMT_FP8_BLOCK128) {
+          f32x4_t tmp = zero4();
+#pragma unroll
+          for (int q = 0; q < 4; q++) tmp = mfma_bf16(av[q], bv[q], tmp);
+#pragma unroll
+          for (int j = 0; j < 4; j++) acc[t][j] += bs[ii][t] * tmp[j];
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; q++) acc[t] = mfma_bf16(av[q], bv[q], acc[t]);
+        }
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------- gate_up
 
-template <int FMT>
-__global__ __launch_bounds__(256) void k_gate_up(GateUpArgs a) {
+// Workgroup = 4 waves on one 16-row block and GCOLS slice columns [c0, c0+GCOLS): tiles
+// 0..GT-1 are gate rows lo+c0+16t+[0,16), tiles GT..2GT-1 the matching up rows I+....  The
+// first kwaves waves split K into contiguous ranges; their partial sums are added in wave
+// order through LDS, then wave t < GT applies the SwiGLU epilogue of tile t.
+constexpr int GCOLS = 32;
+constexpr int GT = GCOLS / 16;
+constexpr int kMinWaves = 3;  // waves per SIMD the expert kernels are compiled for
+
+template <int FMT, int COUNT>
+__global__ __launch_bounds__(256, kMinWaves) void k_gate_up(GateUpArgs a) {
+  __shared__ float red[4][2 * GT][4][64];  // [wave][tile][j][lane]
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int sb = blockIdx.x;
-  const int c0 = blockIdx.y * 64 + wave * 16;  // first slice column of this wave
-  if (c0 >= a.Il) return;
+  const int c0 = blockIdx.y * GCOLS;
   const bool is_shared = sb >= a.n_routed_sub;
   int p0, e, tok;
   const uint8_t *codes;
@@ -80,8 +239,8 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpArgs a) {
   const float *glob;
   if (!is_shared) {
     p0 = sb * 16;
-    if (p0 >= a.total_padded[0]) return;
-    e = a.block_expert[p0 / a.block_m];
+    if (p0 >= __builtin_amdgcn_readfirstlane(a.total_padded[0])) return;  // uniform over the workgroup
+    e = __builtin_amdgcn_readfirstlane(a.block_expert[p0 / a.block_m]);
     if (e < 0) return;
     const int f = a.sorted_ids[p0 + r];
     tok = f < a.T * a.k ? f / a.k : -1;
@@ -98,61 +257,65 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpArgs a) {
     glob = a.sgug;
   }
   const int H = a.H, I = a.I;
-  const size_t gate_row = (size_t)e * 2 * I + a.lo + c0 + r;  // row inside the bank's [E*2I] rows
-  const size_t up_row = gate_row + I;
-  const uint16_t *xrow = a.x + (size_t)(tok >= 0 ? tok : 0) * H;
-  f32x4_t accg = zero4(), accu = zero4();
-  for (int kc = 0; kc < H; kc += 128) {
-    const int k0 = kc + 32 * g;
-    frag8 av[4], bg[4], bu[4];
-    load_a(xrow, k0, tok >= 0, av);
-    load_b<FMT>(codes, scales, gate_row, H, k0, bg);
-    load_b<FMT>(codes, scales, up_row, H, k0, bu);
-    if constexpr (FMT == MOE_FMT_FP8_BLOCK128) {
-      // block scale of rows [row/128] and K block kc/128 (uniform over the wave)
-      const float *si = reinterpret_cast<const float *>(scales);
-      const float sg = si[(gate_row / 128) * (size_t)(H / 128) + kc / 128];
-      const float su = si[(up_row / 128) * (size_t)(H / 128) + kc / 128];
-      f32x4_t tg = zero4(), tu = zero4();
+  const int ntile = min(GT, (a.Il - c0) / 16);  // gate tiles inside the slice (Il % 32 == 0)
+  const WMat<FMT> m = weight_matrix<FMT>(codes, scales, e, 2 * I, H);
+  uint32_t rows[2 * GT];  // rows inside this expert's [2I, H] matrix
 #pragma unroll
-      for (int s = 0; s < 4; s++) {
-        tg = mfma_bf16(av[s], bg[s], tg);
-        tu = mfma_bf16(av[s], bu[s], tu);
-      }
+  for (int t = 0; t < GT; t++) {
+    rows[t] = a.lo + c0 + 16 * (t < ntile ? t : 0) + r;
+    rows[GT + t] = rows[t] + I;
+  }
+  // padding rows read token 0: finite values in rows nobody consumes
+  const rsrc_t ra = make_rsrc(a.x, (uint32_t)a.T * H * 2);
+  const uint32_t a_row = (uint32_t)(tok >= 0 ? tok : 0) * H * 2;
+  f32x4_t acc[2 * GT];
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        accg[j] += sg * tg[j];
-        accu[j] += su * tu[j];
-      }
-    } else {
+  for (int t = 0; t < 2 * GT; t++) acc[t] = zero4();
+  // K split: wave w < a.kwaves takes [w*kw, (w+1)*kw), kw = 128 * a.ksteps
+  if (wave < a.kwaves) {  // COUNT >= ksteps; steps past ksteps are masked
+    const int kw = 128 * a.ksteps;
+    mma_run<FMT, 2 * GT, COUNT>(ra, a_row, m, rows, 0, wave * kw, kw, g, acc);
+  }
 #pragma unroll
-      for (int s = 0; s < 4; s++) {
-        accg = mfma_bf16(av[s], bg[s], accg);
-        accu = mfma_bf16(av[s], bu[s], accu);
-      }
+  for (int t = 0; t < 2 * GT; t++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) red[wave][t][j][lane] = acc[t][j];
+  __syncthreads();
+  if (wave < ntile) {
+    const int t = wave;  // gate tile t, up tile GT + t
+    float gsc = 1.f, usc = 1.f;
+    if constexpr (FMT == MOE_FMT_NVFP4) {
+      gsc = glob[(size_t)e * 2 * I + rows[t]];
+      usc = glob[(size_t)e * 2 * I + rows[GT + t]];
     }
-  }
-  float gsc = 1.f, usc = 1.f;
-  if constexpr (FMT == MOE_FMT_NVFP4) {
-    gsc = glob[gate_row];
-    usc = glob[up_row];
-  }
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const float gv = accg[j] * gsc, uv = accu[j] * usc;
-    const float hv = gv / (1.f + __expf(-gv)) * uv;
-    a.h[(size_t)(p0 + 4 * g + j) * a.Il + c0 + r] = bf16_bits(hv);
+    for (int j = 0; j < 4; j++) {
+      float gv = 0.f, uv = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; w++) {
+        gv += red[w][t][j][lane];
+        uv += red[w][GT + t][j][lane];
+      }
+      gv *= gsc;
+      uv *= usc;
+      const float hv = gv / (1.f + __expf(-gv)) * uv;
+      a.h[(size_t)(p0 + 4 * g + j) * a.Il + c0 + 16 * t + r] = bf16_bits(hv);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------- down
 
-template <int FMT>
-__global__ __launch_bounds__(256) void k_down(DownArgs a) {
+// Wave w owns hidden columns [n0, n0 + 16*DNT), n0 = blockIdx.y*64*DNT + 16*DNT*w: DNT MFMA
+// tiles sharing one A fragment (a row block of h); K = the slice width Il.
+constexpr int DNT = 4;
+
+template <int FMT, int COUNT>
+__global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int sb = blockIdx.x;
-  const int n0 = blockIdx.y * 64 + wave * 16;  // first output column (hidden index)
+  const int n0 = blockIdx.y * 64 * DNT + wave * 16 * DNT;  // first output column (hidden index)
   if (n0 >= a.H) return;
   const bool is_shared = sb >= a.n_routed_sub;
   int p0, e;
@@ -161,8 +324,8 @@ __global__ __launch_bounds__(256) void k_down(DownArgs a) {
   const float *glob;
   if (!is_shared) {
     p0 = sb * 16;
-    if (p0 >= a.total_padded[0]) return;
-    e = a.block_expert[p0 / a.block_m];
+    if (p0 >= __builtin_amdgcn_readfirstlane(a.total_padded[0])) return;
+    e = __builtin_amdgcn_readfirstlane(a.block_expert[p0 / a.block_m]);
     if (e < 0) return;
     codes = a.dn;
     scales = a.dns;
@@ -175,46 +338,39 @@ __global__ __launch_bounds__(256) void k_down(DownArgs a) {
     glob = a.sdng;
   }
   const int H = a.H, I = a.I, Il = a.Il;
-  const size_t drow = (size_t)e * H + n0 + r;  // down row of output column n0 + r
-  const uint16_t *hrow = a.h + (size_t)(p0 + r) * Il;
-  f32x4_t acc = zero4();
-  for (int kc = 0; kc < Il; kc += 128) {
-    const int k0 = kc + 32 * g;
-    const bool valid = k0 < Il;  // Il % 32 == 0: a lane group's run is all in or all out
-    frag8 av[4], bv[4];
-    load_a(hrow, k0, valid, av);
-    if (valid) {
-      load_b<FMT>(codes, scales, drow, I, a.lo + k0, bv);
-    } else {
+  const int ntile = min(DNT, (H - n0) / 16);
+  const WMat<FMT> m = weight_matrix<FMT>(codes, scales, e, H, I);
+  uint32_t rows[DNT];  // rows inside this expert's [H, I] matrix
 #pragma unroll
-      for (int s = 0; s < 4; s++) bv[s].q = make_uint4(0, 0, 0, 0);
-    }
-    if constexpr (FMT == MOE_FMT_FP8_BLOCK128) {
-      const float *si = reinterpret_cast<const float *>(scales);
-      const float sc = si[(drow / 128) * (size_t)(I / 128) + (a.lo + kc) / 128];
-      f32x4_t t = zero4();
+  for (int t = 0; t < DNT; t++) rows[t] = n0 + 16 * (t < ntile ? t : 0) + r;
+  f32x4_t acc[DNT];
 #pragma unroll
-      for (int s = 0; s < 4; s++) t = mfma_bf16(av[s], bv[s], t);
-#pragma unroll
-      for (int j = 0; j < 4; j++) acc[j] += sc * t[j];
-    } else {
-#pragma unroll
-      for (int s = 0; s < 4; s++) acc = mfma_bf16(av[s], bv[s], acc);
-    }
-  }
-  float dsc = 1.f;
-  if constexpr (FMT == MOE_FMT_NVFP4) dsc = glob[drow];
+  for (int t = 0; t < DNT; t++) acc[t] = zero4();
+  const rsrc_t ra = make_rsrc(a.h, (uint32_t)a.h_rows * Il * 2);
+  const uint32_t a_row = (uint32_t)(p0 + r) * Il * 2;
+  for (int kw0 = 0; kw0 < Il; kw0 += 128 * COUNT)  // runs of COUNT steps; the tail is masked
+    mma_run<FMT, DNT, COUNT>(ra, a_row, m, rows, a.lo, kw0, Il - kw0, g, acc);
   const int P = a.T * a.k;
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const int p = p0 + 4 * g + j;
-    const float y = acc[j] * dsc;
+    int dst;
+    float wgt = 1.f;
     if (!is_shared) {
       const int f = a.sorted_ids[p];
-      if (f < P) a.Y[(size_t)f * H + n0 + r] = a.topk_w[f] * y;
+      dst = f < P ? f : -1;
+      if (dst >= 0) wgt = a.topk_w[f];
     } else {
       const int t = p - a.cap;
-      if (t < a.T) a.Y[(size_t)(P + t) * H + n0 + r] = y;
+      dst = t < a.T ? P + t : -1;
+    }
+    if (dst < 0) continue;
+#pragma unroll
+    for (int t = 0; t < DNT; t++) {
+      if (t >= ntile) break;
+      float y = acc[t][j];
+      if constexpr (FMT == MOE_FMT_NVFP4) y *= glob[(size_t)e * H + rows[t]];
+      a.Y[(size_t)dst * H + n0 + 16 * t + r] = wgt * y;
     }
   }
 }
@@ -254,22 +410,45 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ Y, in
 
 // ---------------------------------------------------------------------------- launchers
 
+// Step count of a K run as a template argument: 1, 2, 4 or 8 (runs are masked past K).
+static int count_class(int steps) { return steps <= 1 ? 1 : steps <= 2 ? 2 : steps <= 4 ? 4 : 8; }
+
+template <int FMT>
+static void launch_gate_up_fmt(const GateUpArgs &a, dim3 grid, hipStream_t s) {
+  switch (count_class(a.ksteps)) {
+    case 1: hipLaunchKernelGGL((k_gate_up<FMT, 1>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_gate_up<FMT, 2>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_gate_up<FMT, 4>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_gate_up<FMT, 8>), grid, dim3(256), 0, s, a); break;
+  }
+}
+
 hipError_t launch_gate_up(int fmt, const GateUpArgs &a, int n_shared_sub, hipStream_t s) {
-  dim3 grid(a.n_routed_sub + n_shared_sub, (a.Il + 63) / 64);
+  dim3 grid(a.n_routed_sub + n_shared_sub, (a.Il + GCOLS - 1) / GCOLS);
   switch (fmt) {
-    case MOE_FMT_NVFP4: hipLaunchKernelGGL(k_gate_up<MOE_FMT_NVFP4>, grid, dim3(256), 0, s, a); break;
-    case MOE_FMT_MXFP4_E8M0: hipLaunchKernelGGL(k_gate_up<MOE_FMT_MXFP4_E8M0>, grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL(k_gate_up<MOE_FMT_FP8_BLOCK128>, grid, dim3(256), 0, s, a); break;
+    case MOE_FMT_NVFP4: launch_gate_up_fmt<MOE_FMT_NVFP4>(a, grid, s); break;
+    case MOE_FMT_MXFP4_E8M0: launch_gate_up_fmt<MOE_FMT_MXFP4_E8M0>(a, grid, s); break;
+    default: launch_gate_up_fmt<MOE_FMT_FP8_BLOCK128>(a, grid, s); break;
   }
   return hipGetLastError();
 }
 
+template <int FMT>
+static void launch_down_fmt(const DownArgs &a, dim3 grid, hipStream_t s) {
+  switch (count_class((a.Il + 127) / 128)) {
+    case 1: hipLaunchKernelGGL((k_down<FMT, 1>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_down<FMT, 2>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_down<FMT, 4>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_down<FMT, 8>), grid, dim3(256), 0, s, a); break;
+  }
+}
+
 hipError_t launch_down(int fmt, const DownArgs &a, int n_shared_sub, hipStream_t s) {
-  dim3 grid(a.n_routed_sub + n_shared_sub, (a.H + 63) / 64);
+  dim3 grid(a.n_routed_sub + n_shared_sub, (a.H + 64 * DNT - 1) / (64 * DNT));
   switch (fmt) {
-    case MOE_FMT_NVFP4: hipLaunchKernelGGL(k_down<MOE_FMT_NVFP4>, grid, dim3(256), 0, s, a); break;
-    case MOE_FMT_MXFP4_E8M0: hipLaunchKernelGGL(k_down<MOE_FMT_MXFP4_E8M0>, grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL(k_down<MOE_FMT_FP8_BLOCK128>, grid, dim3(256), 0, s, a); break;
+    case MOE_FMT_NVFP4: launch_down_fmt<MOE_FMT_NVFP4>(a, grid, s); break;
+    case MOE_FMT_MXFP4_E8M0: launch_down_fmt<MOE_FMT_MXFP4_E8M0>(a, grid, s); break;
+    default: launch_down_fmt<MOE_FMT_FP8_BLOCK128>(a, grid, s); break;
   }
   return hipGetLastError();
 }

@@ -20,11 +20,13 @@ struct GateUpArgs {
   const int32_t *sorted_ids, *block_expert, *total_padded;
   int block_m, cap, n_routed_sub;  // n_routed_sub = cap / 16
   int lo, Il;
+  int kwaves, ksteps;  // K split of gate_up: kwaves waves x ksteps steps of 128 (H = 128*kwaves*ksteps)
   uint16_t *h;  // [cap + 16 * n_shared_sub, Il] bf16
 };
 
 struct DownArgs {
   const uint16_t *h;
+  int h_rows;  // rows of h (cap + shared rows)
   int T, H, k;
   const uint8_t *dn, *dns;
   const float *dng;
@@ -38,8 +40,11 @@ struct DownArgs {
   float *Y;             // [T * k + T_shared, H]
 };
 
-hipError_t launch_router_logits(const uint16_t *x, int T, int H, const uint16_t *w, int E,
-                                const float *bias, float *logits, hipStream_t s);
+int router_ksplit(int T, int E, int H);
+size_t router_workspace_bytes(int T, int E, int H);
+hipError_t launch_route(const uint16_t *x, int T, int H, const uint16_t *w, int E, const float *bias, int k,
+                        int renormalize, float *logits, int32_t *ids, float *wts, float *partial,
+                        hipStream_t s);
 hipError_t launch_topk(const float *logits, int T, int E, const float *bias, int k, int renormalize,
                        int32_t *ids, float *wts, hipStream_t s);
 hipError_t launch_align(const int32_t *ids, int T, int k, int E, int BM, int cap, int32_t *sorted_ids,

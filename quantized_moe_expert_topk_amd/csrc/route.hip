@@ -4,28 +4,38 @@
 // then per token the k experts ranking first under (logit descending, index ascending)
 // and their softmax weights (renormalised over the k picks when norm_topk_prob is set:
 // FreeToken issue #62, second comment; PR #70 ownership table, "Router ... Replicated").
+//
+// Two kernels:
+//   k_router_partial  split-K GEMM: KS workgroup layers each reduce H/KS of K and write
+//                     their own partial [KS][T][E] (no atomics), so decode-sized batches
+//                     still spread the router weight over the whole chip.
+//   k_topk            sums the KS partials in a fixed order (plus bias), writes the
+//                     logits, then one wave per token selects k experts by k rounds of a
+//                     wave-wide (value, lower index) maximum built from DPP row steps.
 #include "device_common.h"
 #include "launch.h"
 
 namespace qmoe {
 
-// One workgroup = 4 waves = 16 tokens x 64 experts; wave w owns experts [16w, 16w+16).
-// K advances 128 per step: lane group g = l/16 loads the contiguous 32-element run
-// [kc + 32g, kc + 32g + 32) of its row for both operands (64 B per lane per operand).
-__global__ __launch_bounds__(256) void k_router_logits(const uint16_t *__restrict__ x, int T, int H,
-                                                       const uint16_t *__restrict__ w, int E,
-                                                       const float *__restrict__ bias,
-                                                       float *__restrict__ logits) {
+// One workgroup = 4 waves = 16 tokens x 64 experts x one K split; wave w owns experts
+// [16w, 16w+16).  K advances 128 per step: lane group g = l/16 loads the contiguous
+// 32-element run [kc + 32g, kc + 32g + 32) of its row for both operands.
+__global__ __launch_bounds__(256) void k_router_partial(const uint16_t *__restrict__ x, int T, int H,
+                                                        const uint16_t *__restrict__ w, int E,
+                                                        const float *__restrict__ bias, int kchunk,
+                                                        float *__restrict__ part) {
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int t0 = blockIdx.y * 16, e0 = blockIdx.x * 64 + wave * 16;
   if (e0 >= E) return;
+  const int ks = blockIdx.z;
+  const int kbeg = ks * kchunk, kend = kbeg + kchunk;
   const int ta = t0 + r, eb = e0 + r;
   const bool va = ta < T, vb = eb < E;
   const uint4 *xa = reinterpret_cast<const uint4 *>(x + (size_t)(va ? ta : 0) * H);
   const uint4 *wb = reinterpret_cast<const uint4 *>(w + (size_t)(vb ? eb : 0) * H);
   f32x4_t acc = zero4();
-  for (int kc = 0; kc < H; kc += 128) {
+  for (int kc = kbeg; kc < kend; kc += 128) {
     const int q = (kc + 32 * g) >> 3;  // uint4 index (8 bf16 each)
     frag8 a[4], b[4];
 #pragma unroll
@@ -37,61 +47,120 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t *__restric
     for (int s = 0; s < 4; s++) acc = mfma_bf16(a[s], b[s], acc);
   }
   if (vb) {
-    const float bv = bias ? bias[eb] : 0.f;
+    const float bv = (bias && ks == 0 && gridDim.z == 1) ? bias[eb] : 0.f;
+    float *dst = part + (size_t)ks * T * E;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const int t = t0 + 4 * g + j;
-      if (t < T) logits[(size_t)t * E + eb] = acc[j] + bv;
+      if (t < T) dst[(size_t)t * E + eb] = acc[j] + bv;
     }
   }
 }
 
-// Top-k: one wave per token.  Lane l holds experts e = l + 64 q.  Each of the k rounds
-// takes the wave-wide best (value, then lower index) among the not-yet-taken experts.
-constexpr int kMaxSlots = 16;  // E <= 1024
+// ---------------------------------------------------------------------------- top-k
 
-__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
+// Ordered 64-bit key: larger logit first, then lower index.  Float bits are mapped to an
+// unsigned order (sign flip) in the upper half; the lower half is ~index.
+__device__ __forceinline__ uint64_t rank_key(float v, int idx) {
+  uint32_t u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)(~(uint32_t)idx);
 }
 
-__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, int T, int E,
+__device__ __forceinline__ int key_index(uint64_t key) { return (int)(~(uint32_t)key); }
+
+__device__ __forceinline__ float key_value(uint64_t key) {
+  uint32_t u = (uint32_t)(key >> 32);
+  u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
+  return __uint_as_float(u);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max(uint64_t k) {
+  const uint32_t lo = (uint32_t)k, hi = (uint32_t)(k >> 32);
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, 0xF, 0xF, false);
+  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, 0xF, 0xF, false);
+  const uint64_t o = ((uint64_t)ohi << 32) | olo;
+  return o > k ? o : k;
+}
+
+// Wave-wide maximum of the 64-bit key, returned to every lane (uniform).
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+  k = dpp_max<0xB1>(k);   // quad_perm [1,0,3,2]
+  k = dpp_max<0x4E>(k);   // quad_perm [2,3,0,1]
+  k = dpp_max<0x141>(k);  // row_half_mirror
+  k = dpp_max<0x140>(k);  // row_mirror: every lane now holds its 16-lane row's maximum
+  uint64_t best = 0;
+#pragma unroll
+  for (int row = 0; row < 4; row++) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, 16 * row);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 16 * row);
+    const uint64_t rk = ((uint64_t)hi << 32) | lo;
+    best = rk > best ? rk : best;
+  }
+  return best;
+}
+
+// Four tokens per workgroup.  Phase 1: all threads sum the KS partials of the 4 tokens'
+// logits (fixed order, independent loads), add the bias, write the logits and stage them
+// in LDS.  Phase 2: wave w selects for token w.  Each lane sorts its NS keys (experts
+// l + 64q) descending; each round takes the wave-wide maximum of the lanes' heads and the
+// winning lane shifts its keys.
+template <int NS>
+__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, int KS, int T, int E,
                                               const float *__restrict__ bias, int k, int renormalize,
-                                              int32_t *__restrict__ ids, float *__restrict__ wts) {
-  const int lane = lane_id();
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const int nslot = (E + 63) >> 6;
-  float v[kMaxSlots];
+                                              float *__restrict__ logits_out, int32_t *__restrict__ ids,
+                                              float *__restrict__ wts) {
+  __shared__ float lg[4][NS * 64];
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * 4;
+  for (int i = threadIdx.x; i < 4 * E; i += 256) {
+    const int tt = i / E, e = i - tt * E, t = t0 + tt;
+    if (t >= T) continue;
+    float s = 0.f;
+    for (int k0 = 0; k0 < KS; k0 += 4) {
+      float v[4];
 #pragma unroll
-  for (int q = 0; q < kMaxSlots; q++) {
-    const int e = lane + 64 * q;
-    v[q] = (q < nslot && e < E) ? logits[(size_t)t * E + e] + (bias ? bias[e] : 0.f) : -INFINITY;
-    if (v[q] != v[q]) v[q] = -INFINITY;  // a NaN logit ranks last (selection stays in range)
+      for (int q = 0; q < 4; q++) v[q] = part[((size_t)min(k0 + q, KS - 1) * T + t) * E + e];
+#pragma unroll
+      for (int q = 0; q < 4; q++)
+        if (k0 + q < KS) s += v[q];
+    }
+    if (bias) s += bias[e];
+    if (logits_out) logits_out[(size_t)t * E + e] = s;
+    lg[tt][e] = s;
   }
-  uint32_t taken = 0;
-  float mine = 0.f;  // lane j < k keeps the j-th selected logit
-  float top = 0.f;
+  __syncthreads();
+  const int t = t0 + wave;
+  if (t >= T) return;
+  uint64_t key[NS];
+  float vals[NS];
+#pragma unroll
+  for (int q = 0; q < NS; q++) {
+    const int e = lane + 64 * q;
+    vals[q] = e < E ? lg[wave][e] : -INFINITY;
+    key[q] = e < E ? rank_key(vals[q] != vals[q] ? -INFINITY : vals[q], e) : 0;  // NaN ranks last
+  }
+  // descending sort of the lane's keys (odd-even transposition network)
+#pragma unroll
+  for (int pass = 0; pass < NS; pass++)
+#pragma unroll
+    for (int q = pass & 1; q + 1 < NS; q += 2)
+      if (key[q] < key[q + 1]) {
+        const uint64_t tmp = key[q];
+        key[q] = key[q + 1];
+        key[q + 1] = tmp;
+      }
+  float mine = 0.f, top = 0.f;
   for (int j = 0; j < k; j++) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+    const uint64_t best = wave_max_key(key[0]);
+    const int bi = key_index(best);
+    const float bv = key_value(best);
+    if (key[0] == best) {  // keys are unique (index in the low half): exactly one lane
 #pragma unroll
-    for (int q = 0; q < kMaxSlots; q++) {
-      const int e = lane + 64 * q;
-      if (q < nslot && e < E && !(taken >> q & 1u) && better(v[q], e, bv, bi)) {
-        bv = v[q];
-        bi = e;
-      }
+      for (int q = 0; q + 1 < NS; q++) key[q] = key[q + 1];
+      key[NS - 1] = 0;
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
     if (lane == j) mine = bv;
     if (j == 0) top = bv;
     if (lane == 0) ids[(size_t)t * k + j] = bi;
@@ -103,26 +172,61 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
   } else {
     z = 0.f;
 #pragma unroll
-    for (int q = 0; q < kMaxSlots; q++)
-      if (q < nslot && lane + 64 * q < E) z += expf(v[q] - top);
+    for (int q = 0; q < NS; q++)
+      if (lane + 64 * q < E) z += expf(vals[q] - top);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
   if (lane < k) wts[(size_t)t * k + lane] = expf(mine - top) / z;
 }
 
-hipError_t launch_router_logits(const uint16_t *x, int T, int H, const uint16_t *w, int E,
-                                const float *bias, float *logits, hipStream_t s) {
-  dim3 grid((E + 63) / 64, (T + 15) / 16);
-  hipLaunchKernelGGL(k_router_logits, grid, dim3(256), 0, s, x, T, H, w, E, bias, logits);
+static hipError_t launch_topk_ns(const float *part, int KS, int T, int E, const float *bias, int k, int renormalize,
+                                 float *logits_out, int32_t *ids, float *wts, hipStream_t s) {
+  const dim3 grid((T + 3) / 4), block(256);
+  const int slots = (E + 63) / 64;
+  if (slots <= 1)
+    hipLaunchKernelGGL(k_topk<1>, grid, block, 0, s, part, KS, T, E, bias, k, renormalize, logits_out, ids, wts);
+  else if (slots <= 2)
+    hipLaunchKernelGGL(k_topk<2>, grid, block, 0, s, part, KS, T, E, bias, k, renormalize, logits_out, ids, wts);
+  else if (slots <= 4)
+    hipLaunchKernelGGL(k_topk<4>, grid, block, 0, s, part, KS, T, E, bias, k, renormalize, logits_out, ids, wts);
+  else if (slots <= 8)
+    hipLaunchKernelGGL(k_topk<8>, grid, block, 0, s, part, KS, T, E, bias, k, renormalize, logits_out, ids, wts);
+  else
+    hipLaunchKernelGGL(k_topk<16>, grid, block, 0, s, part, KS, T, E, bias, k, renormalize, logits_out, ids, wts);
   return hipGetLastError();
+}
+
+// K splits for the router GEMM: enough workgroups to cover the chip at small T.
+int router_ksplit(int T, int E, int H) {
+  const int base = ((E + 63) / 64) * ((T + 15) / 16);
+  int ks = 1;
+  while (base * ks < 256 && ks < 16 && ks * 2 <= H / 128 && (H / 128) % (ks * 2) == 0) ks *= 2;
+  return ks;
+}
+
+size_t router_workspace_bytes(int T, int E, int H) {
+  const int ks = router_ksplit(T, E, H);
+  return ks > 1 ? (size_t)ks * T * E * sizeof(float) : 0;
+}
+
+hipError_t launch_route(const uint16_t *x, int T, int H, const uint16_t *w, int E, const float *bias, int k,
+                        int renormalize, float *logits, int32_t *ids, float *wts, float *partial,
+                        hipStream_t s) {
+  const int ks = router_ksplit(T, E, H);
+  float *part = ks > 1 ? partial : logits;
+  dim3 grid((E + 63) / 64, (T + 15) / 16, ks);
+  hipLaunchKernelGGL(k_router_partial, grid, dim3(256), 0, s, x, T, H, w, E, bias, H / ks, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // with one split the GEMM already added the bias and wrote the logits in place
+  return launch_topk_ns(part, ks, T, E, ks > 1 ? bias : nullptr, k, renormalize, ks > 1 ? logits : nullptr, ids, wts,
+                        s);
 }
 
 hipError_t launch_topk(const float *logits, int T, int E, const float *bias, int k, int renormalize,
                        int32_t *ids, float *wts, hipStream_t s) {
-  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, bias, k, renormalize,
-                     ids, wts);
-  return hipGetLastError();
+  return launch_topk_ns(logits, 1, T, E, bias, k, renormalize, nullptr, ids, wts, s);
 }
 
 }  // namespace qmoe

@@ -94,10 +94,13 @@ def test_forward_rejects_bad_arguments_before_any_launch(kw, code):
 
 def test_route_and_align_reject_bad_arguments():
     lib = L.lib()
-    assert lib.moe_route(None, 4, 256, FAKE, 8, None, 2, 1, FAKE, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
-    assert lib.moe_route(FAKE, 4, 256, FAKE, 8, None, 9, 1, FAKE, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
-    assert lib.moe_route(FAKE, 4, 200, FAKE, 8, None, 2, 1, FAKE, FAKE, FAKE, None) == L.MOE_ERR_UNSUPPORTED
-    assert lib.moe_route(FAKE, 4, 256, FAKE, 2048, None, 2, 1, FAKE, FAKE, FAKE, None) == L.MOE_ERR_UNSUPPORTED
+    W = 1 << 30
+    assert lib.moe_route(None, 4, 256, FAKE, 8, None, 2, 1, FAKE, FAKE, FAKE, FAKE, W, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(FAKE, 4, 256, FAKE, 8, None, 9, 1, FAKE, FAKE, FAKE, FAKE, W, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(FAKE, 4, 200, FAKE, 8, None, 2, 1, FAKE, FAKE, FAKE, FAKE, W, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route(FAKE, 4, 256, FAKE, 2048, None, 2, 1, FAKE, FAKE, FAKE, FAKE, W, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route_workspace_bytes(64, 2048, 256) > 0
+    assert lib.moe_route(FAKE, 64, 2048, FAKE, 256, None, 8, 1, FAKE, FAKE, FAKE, FAKE, 0, None) == L.MOE_ERR_WORKSPACE
     assert lib.moe_route_from_logits(FAKE, 4, 8, None, 0, 1, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
     al = _align(T=16, k=2, E=8)
     assert lib.moe_align(FAKE, 16, 2, 8, ctypes.byref(al), FAKE, 0, None) == L.MOE_ERR_WORKSPACE
