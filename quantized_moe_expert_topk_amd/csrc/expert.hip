@@ -124,44 +124,70 @@ __device__ __forceinline__ void zero_frags(frag8 (&b)[4]) {
   for (int q = 0; q < 4; q++) b[q].q = make_uint4(0, 0, 0, 0);
 }
 
+// Scale bytes of one tile row for a group of 2 K steps (chunk mapping): NVFP4 16 bytes
+// (2 steps x 4 lane groups x 2 groups of 16), MXFP4 8 bytes (2 x 4 x 1).  All four lane
+// groups of a row load the same span; each lane then selects its own bytes.
+template <int FMT>
+__device__ __forceinline__ uint4 load_scale_span(rsrc_t r, uint32_t off, bool aligned) {
+  constexpr int NB = FMT == MOE_FMT_NVFP4 ? 16 : 8;
+  if (aligned) {  // uniform: a dword-aligned start for every lane
+    if constexpr (NB == 16) return buf_load16(r, off);
+    const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+    return make_uint4(v.x, v.y, 0, 0);
+  }
+  ScaleRun<NB> run;
+  load_scale_run(r, off, run);
+  if constexpr (NB == 16) return make_uint4(run.w[0], run.w[1], run.w[2], run.w[3]);
+  return make_uint4(run.w[0], run.w[1], 0, 0);
+}
+
+// This lane's scale bytes of step s (0/1) of a span (lane group g).
+//   NVFP4: the two e4m3 bytes at 8s + 2g, 8s + 2g + 1 (low 16 bits of the result)
+//   MXFP4: the e8m0 byte at 4s + g
+template <int FMT>
+__device__ __forceinline__ uint32_t span_scales(const uint4 &sp, int s, int g) {
+  if constexpr (FMT == MOE_FMT_NVFP4) {
+    const uint32_t lo = s ? sp.z : sp.x, hi = s ? sp.w : sp.y;
+    return ((g & 2) ? hi : lo) >> (16 * (g & 1));
+  } else {
+    return (s ? sp.y : sp.x) >> (8 * g);
+  }
+}
+
 // Multiply-accumulate a wave's K range [kw0, kw0 + 128*COUNT) of one 16-row A block against
-// NT weight tiles; positions at or past kvalid (relative to kw0) contribute zero and load
-// from clamped in-bounds offsets.
-//   FP4 formats: lane group g owns the contiguous run [32*COUNT*g, 32*COUNT*(g+1)) and step
-//     i reads its 32-wide piece i, so a lane's scales for the whole run are one load per tile.
-//   FP8_BLOCK: step i is the 128-wide chunk [128 i, 128 i + 128) and lane group g reads its
-//     piece [32 g, 32 g + 32), so every MFMA stays inside one 128x128 scale block.
-// NPF steps (2 for FP4, 1 for FP8) are loaded before any of them is decoded.
-//   ra, a_row: activation buffer and the byte offset of this lane's row (K index 0)
+// NT weight tiles.  Step i is the 128-wide chunk [kw0 + 128 i, +128); lane group g reads
+// its 32-wide piece [32 g, 32 g + 32) (one contiguous 64 B run of each of 16 rows per code
+// load), so every MFMA stays inside one 128x128 FP8 scale block.  Positions at or past
+// kvalid (relative to kw0) contribute zero and load from clamped in-bounds offsets.  Steps
+// are taken in groups of 2 (FP4) or 1 (FP8) whose loads are all issued before decoding.
+//   ra, a_row: activation buffer and the byte offset of this lane's row; a row past the
+//              buffer end reads as zeros without a memory request (padding rows)
 //   m, rows:   weight matrix and this lane's row of each tile;  b_k0: K offset in the row
 template <int FMT, int NT, int COUNT>
 __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FMT> &m, const uint32_t (&rows)[NT],
                                         int b_k0, int kw0, int kvalid, int g, f32x4_t (&acc)[NT]) {
   constexpr bool FP4 = FMT != MOE_FMT_FP8_BLOCK128;
-  constexpr int NPF = FP4 ? 2 : 1;  // steps loaded before decoding (FP8 steps carry twice the bytes)
+  constexpr int NPF = FP4 ? 2 : 1;
   const uint32_t K = (uint32_t)m.K;
-  // scale runs (FP4): NVFP4 2 bytes per step, MXFP4 1 byte per step
-  constexpr int SNB = FMT == MOE_FMT_NVFP4 ? 2 * COUNT : COUNT;
-  ScaleRun<FP4 ? SNB : 1> srun[NT];
-  const int grun = 32 * COUNT * g;  // FP4: start of lane group g's run
-  if constexpr (FP4) {
-    const int k = kw0 + (grun < kvalid ? grun : 0);
-#pragma unroll
-    for (int t = 0; t < NT; t++) {
-      const uint32_t off = FMT == MOE_FMT_NVFP4 ? rows[t] * (K / 16) + (b_k0 + k) / 16 : rows[t] * (K / 32) + (b_k0 + k) / 32;
-      load_scale_run(m.scales, off, srun[t]);
-    }
-  }
+  const int sdiv = FMT == MOE_FMT_NVFP4 ? 16 : 32;
+  // spans are dword aligned when the row pitch and the run start are (uniform)
+  const bool sal = ((K / sdiv) % 4 == 0) && (((b_k0 + kw0) / sdiv) % 4 == 0);
 #pragma unroll
   for (int i0 = 0; i0 < COUNT; i0 += NPF) {
     ARaw ar[NPF];
     uint4 c0[NPF][NT], c1[NPF][NT];
+    uint4 sp[NT];
     float bs[NPF][NT];
+    if constexpr (FP4) {
+      const int kg = kw0 + (128 * i0 < kvalid ? 128 * i0 : 0);
+#pragma unroll
+      for (int t = 0; t < NT; t++) sp[t] = load_scale_span<FMT>(m.scales, rows[t] * (K / sdiv) + (b_k0 + kg) / sdiv, sal);
+    }
 #pragma unroll
     for (int ii = 0; ii < NPF; ii++) {
       const int i = i0 + ii;
       if (i >= COUNT) break;
-      const int kr = FP4 ? grun + 32 * i : 128 * i + 32 * g;  // position relative to kw0
+      const int kr = 128 * i + 32 * g;  // position relative to kw0
       const int k = kw0 + (kr < kvalid ? kr : 0);
 #pragma unroll
       for (int q = 0; q < 4; q++) ar[ii].q[q] = buf_load16(ra, a_row + k * 2 + 16 * q);
@@ -181,8 +207,7 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
     for (int ii = 0; ii < NPF; ii++) {
       const int i = i0 + ii;
       if (i >= COUNT) break;
-      const int kr = FP4 ? grun + 32 * i : 128 * i + 32 * g;
-      const bool v = kr < kvalid;
+      const bool v = 128 * i + 32 * g < kvalid;
       frag8 av[4];
 #pragma unroll
       for (int q = 0; q < 4; q++) av[q].q = ar[ii].q[q];
@@ -190,9 +215,10 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
       for (int t = 0; t < NT; t++) {
         frag8 bv[4];
         if constexpr (FMT == MOE_FMT_NVFP4) {
-          decode_nvfp4(c0[ii][t], run_byte(srun[t], 2 * i), run_byte(srun[t], 2 * i + 1), bv);
+          const uint32_t sc = span_scales<FMT>(sp[t], ii, g);
+          decode_nvfp4(c0[ii][t], sc & 0xFFu, (sc >> 8) & 0xFFu, bv);
         } else if constexpr (FMT == MOE_FMT_MXFP4_E8M0) {
-          decode_mxfp4(c0[ii][t], run_byte(srun[t], i), bv);
+          decode_mxfp4(c0[ii][t], span_scales<FMT>(sp[t], ii, g) & 0xFFu, bv);
         } else {
           fp8x8_to_bf16(c0[ii][t].x, c0[ii][t].y, bv[0]);
           fp8x8_to_bf16(c0[ii][t].z, c0[ii][t].w, bv[1]);
@@ -265,9 +291,15 @@ __global__ __launch_bounds__(256, kMinWaves) void k_gate_up(GateUpArgs a) {
     rows[t] = a.lo + c0 + 16 * (t < ntile ? t : 0) + r;
     rows[GT + t] = rows[t] + I;
   }
-  // padding rows read token 0: finite values in rows nobody consumes
+  float gsc[GT], usc[GT];  // per-row globals, loaded early
+#pragma unroll
+  for (int t = 0; t < GT; t++) {
+    gsc[t] = FMT == MOE_FMT_NVFP4 ? glob[(size_t)e * 2 * I + rows[t]] : 1.f;
+    usc[t] = FMT == MOE_FMT_NVFP4 ? glob[(size_t)e * 2 * I + rows[GT + t]] : 1.f;
+  }
+  // padding rows point past the activation buffer: they read zeros without a memory request
   const rsrc_t ra = make_rsrc(a.x, (uint32_t)a.T * H * 2);
-  const uint32_t a_row = (uint32_t)(tok >= 0 ? tok : 0) * H * 2;
+  const uint32_t a_row = tok >= 0 ? (uint32_t)tok * H * 2 : 0x80000000u;
   f32x4_t acc[2 * GT];
 #pragma unroll
   for (int t = 0; t < 2 * GT; t++) acc[t] = zero4();
@@ -283,11 +315,6 @@ __global__ __launch_bounds__(256, kMinWaves) void k_gate_up(GateUpArgs a) {
   __syncthreads();
   if (wave < ntile) {
     const int t = wave;  // gate tile t, up tile GT + t
-    float gsc = 1.f, usc = 1.f;
-    if constexpr (FMT == MOE_FMT_NVFP4) {
-      gsc = glob[(size_t)e * 2 * I + rows[t]];
-      usc = glob[(size_t)e * 2 * I + rows[GT + t]];
-    }
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       float gv = 0.f, uv = 0.f;
@@ -296,8 +323,8 @@ __global__ __launch_bounds__(256, kMinWaves) void k_gate_up(GateUpArgs a) {
         gv += red[w][t][j][lane];
         uv += red[w][GT + t][j][lane];
       }
-      gv *= gsc;
-      uv *= usc;
+      gv *= gsc[t];
+      uv *= usc[t];
       const float hv = gv / (1.f + __expf(-gv)) * uv;
       a.h[(size_t)(p0 + 4 * g + j) * a.Il + c0 + 16 * t + r] = bf16_bits(hv);
     }
@@ -346,31 +373,39 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
   f32x4_t acc[DNT];
 #pragma unroll
   for (int t = 0; t < DNT; t++) acc[t] = zero4();
-  const rsrc_t ra = make_rsrc(a.h, (uint32_t)a.h_rows * Il * 2);
-  const uint32_t a_row = (uint32_t)(p0 + r) * Il * 2;
-  for (int kw0 = 0; kw0 < Il; kw0 += 128 * COUNT)  // runs of COUNT steps; the tail is masked
-    mma_run<FMT, DNT, COUNT>(ra, a_row, m, rows, a.lo, kw0, Il - kw0, g, acc);
+  // epilogue metadata first, so its latency hides under the weight loads
   const int P = a.T * a.k;
+  int dst[4];
+  float wgt[4];
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const int p = p0 + 4 * g + j;
-    int dst;
-    float wgt = 1.f;
     if (!is_shared) {
       const int f = a.sorted_ids[p];
-      dst = f < P ? f : -1;
-      if (dst >= 0) wgt = a.topk_w[f];
+      dst[j] = f < P ? f : -1;
+      wgt[j] = f < P ? a.topk_w[f] : 0.f;
     } else {
       const int t = p - a.cap;
-      dst = t < a.T ? P + t : -1;
+      dst[j] = t < a.T ? P + t : -1;
+      wgt[j] = 1.f;
     }
-    if (dst < 0) continue;
+  }
+  float dglob[DNT];
+#pragma unroll
+  for (int t = 0; t < DNT; t++) dglob[t] = FMT == MOE_FMT_NVFP4 ? glob[(size_t)e * H + n0 + 16 * t + r] : 1.f;
+  // padding rows (no pair / past T) point past h: they read zeros without a memory request
+  const bool real = is_shared ? (p0 - a.cap + r < a.T) : (a.sorted_ids[p0 + r] < P);
+  const rsrc_t ra = make_rsrc(a.h, (uint32_t)a.h_rows * Il * 2);
+  const uint32_t a_row = real ? (uint32_t)(p0 + r) * Il * 2 : 0x80000000u;
+  for (int kw0 = 0; kw0 < Il; kw0 += 128 * COUNT)  // runs of COUNT steps; the tail is masked
+    mma_run<FMT, DNT, COUNT>(ra, a_row, m, rows, a.lo, kw0, Il - kw0, g, acc);
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    if (dst[j] < 0) continue;
 #pragma unroll
     for (int t = 0; t < DNT; t++) {
       if (t >= ntile) break;
-      float y = acc[t][j];
-      if constexpr (FMT == MOE_FMT_NVFP4) y *= glob[(size_t)e * H + rows[t]];
-      a.Y[(size_t)dst * H + n0 + 16 * t + r] = wgt * y;
+      a.Y[(size_t)dst[j] * H + n0 + 16 * t + r] = wgt[j] * acc[t][j] * dglob[t];
     }
   }
 }

@@ -106,7 +106,7 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
 // in LDS.  Phase 2: wave w selects for token w.  Each lane sorts its NS keys (experts
 // l + 64q) descending; each round takes the wave-wide maximum of the lanes' heads and the
 // winning lane shifts its keys.
-template <int NS>
+template <int NS, int KSMAX>
 __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, int KS, int T, int E,
                                               const float *__restrict__ bias, int k, int renormalize,
                                               float *__restrict__ logits_out, int32_t *__restrict__ ids,
@@ -114,21 +114,29 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, in
   __shared__ float lg[4][NS * 64];
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * 4;
-  for (int i = threadIdx.x; i < 4 * E; i += 256) {
-    const int tt = i / E, e = i - tt * E, t = t0 + tt;
-    if (t >= T) continue;
-    float s = 0.f;
-    for (int k0 = 0; k0 < KS; k0 += 4) {
-      float v[4];
+  for (int e = threadIdx.x; e < E; e += 256) {
+    // 4 tokens x KSMAX partials, every load unconditional (indices clamped) so all are in
+    // flight at once; values past KS or T are masked, sums run in split order
+    float v[4][KSMAX];
+    const rsrc_t pr = make_rsrc(part, (uint32_t)KS * T * E * 4);
 #pragma unroll
-      for (int q = 0; q < 4; q++) v[q] = part[((size_t)min(k0 + q, KS - 1) * T + t) * E + e];
+    for (int tt = 0; tt < 4; tt++) {
+      const uint32_t vo = ((uint32_t)min(t0 + tt, T - 1) * E + e) * 4;  // token + expert (VGPR)
 #pragma unroll
-      for (int q = 0; q < 4; q++)
-        if (k0 + q < KS) s += v[q];
+      for (int q = 0; q < KSMAX; q++)  // split slice (SGPR offset)
+        v[tt][q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                 pr, (int)vo, (int)((uint32_t)min(q, KS - 1) * T * E * 4), 0));
     }
-    if (bias) s += bias[e];
-    if (logits_out) logits_out[(size_t)t * E + e] = s;
-    lg[tt][e] = s;
+    const float b = bias ? bias[e] : 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 4; tt++) {
+      float s = 0.f;
+#pragma unroll
+      for (int q = 0; q < KSMAX; q++) s += q < KS ? v[tt][q] : 0.f;
+      s += b;
+      if (t0 + tt < T && logits_out) logits_out[(size_t)(t0 + tt) * E + e] = s;
+      lg[tt][e] = s;
+    }
   }
   __syncthreads();
   const int t = t0 + wave;
@@ -180,20 +188,29 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, in
   if (lane < k) wts[(size_t)t * k + lane] = expf(mine - top) / z;
 }
 
-static hipError_t launch_topk_ns(const float *part, int KS, int T, int E, const float *bias, int k, int renormalize,
-                                 float *logits_out, int32_t *ids, float *wts, hipStream_t s) {
+template <int KSMAX>
+static void launch_topk_ks(const float *part, int KS, int T, int E, const float *bias, int k, int renormalize,
+                           float *logits_out, int32_t *ids, float *wts, hipStream_t s) {
   const dim3 grid((T + 3) / 4), block(256);
   const int slots = (E + 63) / 64;
   if (slots <= 1)
-    hipLaunchKernelGGL(k_topk<1>, grid, block, 0, s, part, KS, T, E, bias, k, renormalize, logits_out, ids, wts);
+    hipLaunchKernelGGL((k_topk<1, KSMAX>), grid, block, 0, s, part, KS, T, E, bias, k, renormalize, logits_out, ids, wts);
   else if (slots <= 2)
-    hipLaunchKernelGGL(k_topk<2>, grid, block, 0, s, part, KS, T, E, bias, k, renormalize, logits_out, ids, wts);
+    hipLaunchKernelGGL((k_topk<2, KSMAX>), grid, block, 0, s, part, KS, T, E, bias, k, renormalize, logits_out, ids, wts);
   else if (slots <= 4)
-    hipLaunchKernelGGL(k_topk<4>, grid, block, 0, s, part, KS, T, E, bias, k, renormalize, logits_out, ids, wts);
+    hipLaunchKernelGGL((k_topk<4, KSMAX>), grid, block, 0, s, part, KS, T, E, bias, k, renormalize, logits_out, ids, wts);
   else if (slots <= 8)
-    hipLaunchKernelGGL(k_topk<8>, grid, block, 0, s, part, KS, T, E, bias, k, renormalize, logits_out, ids, wts);
+    hipLaunchKernelGGL((k_topk<8, KSMAX>), grid, block, 0, s, part, KS, T, E, bias, k, renormalize, logits_out, ids, wts);
   else
-    hipLaunchKernelGGL(k_topk<16>, grid, block, 0, s, part, KS, T, E, bias, k, renormalize, logits_out, ids, wts);
+    hipLaunchKernelGGL((k_topk<16, KSMAX>), grid, block, 0, s, part, KS, T, E, bias, k, renormalize, logits_out, ids, wts);
+}
+
+static hipError_t launch_topk_ns(const float *part, int KS, int T, int E, const float *bias, int k, int renormalize,
+                                 float *logits_out, int32_t *ids, float *wts, hipStream_t s) {
+  if (KS <= 1)
+    launch_topk_ks<1>(part, 1, T, E, bias, k, renormalize, logits_out, ids, wts, s);
+  else
+    launch_topk_ks<16>(part, KS, T, E, bias, k, renormalize, logits_out, ids, wts, s);
   return hipGetLastError();
 }
 
@@ -201,7 +218,7 @@ static hipError_t launch_topk_ns(const float *part, int KS, int T, int E, const 
 int router_ksplit(int T, int E, int H) {
   const int base = ((E + 63) / 64) * ((T + 15) / 16);
   int ks = 1;
-  while (base * ks < 256 && ks < 16 && ks * 2 <= H / 128 && (H / 128) % (ks * 2) == 0) ks *= 2;
+  while (base * ks < 128 && ks < 16 && ks * 2 <= H / 128 && (H / 128) % (ks * 2) == 0) ks *= 2;
   return ks;
 }
 
