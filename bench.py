@@ -207,6 +207,19 @@ def run(args):
     return cfg, results
 
 
+def copy_calibration(mib):
+    import torch
+    n = (mib << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
+                      "launches": 3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -219,7 +232,13 @@ def main():
     ap.add_argument("--no-points", action="store_true", help="only the headline point")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain elementwise copy of MIB MiB (fp32 negate: reads and writes MIB MiB "
+                         "each) three times, as the known-size kernel that HBM byte counters are scaled by")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer runs on one rank's intermediate slice and this build has "
               "no multi-GPU path (the cross-rank all-reduce of partials is out of scope). Use --gpus 1.",
