@@ -157,7 +157,13 @@ int moe_align(const int32_t *topk_ids, int T, int k, int E, const moe_align_out 
 
 /* ------------------------------------------------------------------ expert layer */
 
-/* Device workspace moe_expert_forward needs for (routed, shared, T, k, block_m, slice). */
+/* Device workspace moe_expert_forward needs for (routed, shared, T, k, block_m, slice):
+ * with rows = capacity + 16*ceil(T/16) if shared else capacity, Il = hi - lo, and each
+ * term rounded up to 256 bytes,
+ *   NVFP4, FP8_BLOCK128:  rows*Il*2  +  (T*k + T_shared)*H*4
+ *   MXFP4:  2*rows*Il + 2*rows*Il/32 + 2*T*H + 2*T*H/32  +  (T*k + T_shared)*H*4
+ * (the intermediate activation, MXFP4's activation planes, and per-pair partial rows).
+ * Returns 0 for arguments moe_expert_forward would reject as invalid. */
 size_t moe_workspace_bytes(const moe_bank *routed, const moe_bank *shared, int T, int k,
                            int block_m, int slice_lo, int slice_hi);
 
@@ -171,6 +177,10 @@ size_t moe_workspace_bytes(const moe_bank *routed, const moe_bank *shared, int T
  *     g_i = x_t . Wg_e[i],  u_i = x_t . Wu_e[I + i]    for i in [lo, hi)  (gate rows
  *       [lo, hi), up rows [I+lo, I+hi): issue #62 "What it touches" item 1)
  *     a_i = silu(g_i) * u_i, rounded to bf16 (the A16 activation of the down GEMM)
+ *   MXFP4 runs on the native scaled FP4 MFMA, whose activation operand is 8-bit at most:
+ *   x and a are carried as two e4m3 planes, hi = e4m3(v/X1)*X1 and lo = e4m3((v-hi)/X2)*X2,
+ *   with e8m0 X1, X2 per 32 elements (about bf16's 8 significant bits), so its results
+ *   equal the W4A16 ones to within the documented tolerance, not bit for bit.
  *     y_n = sum_{i in [lo,hi)} a_i Wd_e[n, i]       for n in [0, H)  (down columns)
  *   out[t, :] = sum_j topk_w[t, j] * y(pair t*k+j)  +  shared(x_t)
  *   where the shared expert (weight 1, same slice) is added to the routed partial before

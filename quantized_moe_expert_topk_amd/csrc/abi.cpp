@@ -137,8 +137,9 @@ int check_align_out(const moe_align_out *al, int T, int k, int E) {
 }
 
 struct FwdPlan {
-  int Il, n_routed_sub, n_shared_sub, shared_rows, P, Psh;
-  size_t h_bytes, y_off, y_bytes, total;
+  int Il, n_routed_sub, n_shared_sub, shared_rows, h_rows, P, Psh;
+  // workspace layout: [h][x planes (MXFP4)][Y]; MXFP4 h is [hq][hs], x is [xq][xs]
+  size_t hs_off, xq_off, xs_off, y_off, y_bytes, total;
 };
 
 FwdPlan plan_forward(const moe_bank *routed, const moe_bank *shared, int T, int k, int cap, int lo, int hi) {
@@ -147,12 +148,21 @@ FwdPlan plan_forward(const moe_bank *routed, const moe_bank *shared, int T, int 
   p.n_routed_sub = cap / 16;
   p.n_shared_sub = shared ? (T + 15) / 16 : 0;
   p.shared_rows = p.n_shared_sub * 16;
+  p.h_rows = cap + p.shared_rows;
   p.P = T * k;
   p.Psh = shared ? T : 0;
-  p.h_bytes = align_up((size_t)(cap + p.shared_rows) * p.Il * 2, 256);
-  p.y_off = p.h_bytes;
-  p.y_bytes = align_up((size_t)(p.P + p.Psh) * routed->H * 4, 256);
-  p.total = p.h_bytes + p.y_bytes;
+  const size_t rows = (size_t)p.h_rows, Il = (size_t)p.Il, H = (size_t)routed->H;
+  if (routed->fmt == MOE_FMT_MXFP4_E8M0) {
+    p.hs_off = align_up(2 * rows * Il, 256);
+    p.xq_off = p.hs_off + align_up(2 * rows * (Il / 32), 256);
+    p.xs_off = p.xq_off + align_up(2 * (size_t)T * H, 256);
+    p.y_off = p.xs_off + align_up(2 * (size_t)T * (H / 32), 256);
+  } else {
+    p.hs_off = p.xq_off = p.xs_off = 0;
+    p.y_off = align_up(rows * Il * 2, 256);
+  }
+  p.y_bytes = align_up((size_t)(p.P + p.Psh) * H * 4, 256);
+  p.total = p.y_off + p.y_bytes;
   return p;
 }
 
@@ -207,15 +217,24 @@ qmoe::GateUpArgs gate_up_args(const moe_bank *routed, const moe_bank *shared, co
   a.lo = lo;
   a.Il = p.Il;
   gate_up_ksplit(routed->H, &a.kwaves, &a.ksteps);
-  a.h = static_cast<uint16_t *>(workspace);
+  char *ws = static_cast<char *>(workspace);
+  a.h = reinterpret_cast<uint16_t *>(ws);
+  a.h_rows = p.h_rows;
+  a.hq = reinterpret_cast<uint8_t *>(ws);
+  a.hs = reinterpret_cast<uint8_t *>(ws + p.hs_off);
+  a.xq = reinterpret_cast<const uint8_t *>(ws + p.xq_off);
+  a.xs = reinterpret_cast<const uint8_t *>(ws + p.xs_off);
   return a;
 }
 
 qmoe::DownArgs down_args(const moe_bank *routed, const moe_bank *shared, int T, int k, const float *topk_w,
                          const moe_align_out *al, int lo, const FwdPlan &p, void *workspace) {
   qmoe::DownArgs a;
-  a.h = static_cast<const uint16_t *>(workspace);
-  a.h_rows = al->capacity + p.shared_rows;
+  const char *ws = static_cast<const char *>(workspace);
+  a.h = reinterpret_cast<const uint16_t *>(ws);
+  a.hq = reinterpret_cast<const uint8_t *>(ws);
+  a.hs = reinterpret_cast<const uint8_t *>(ws + p.hs_off);
+  a.h_rows = p.h_rows;
   a.T = T;
   a.H = routed->H;
   a.k = k;
@@ -243,6 +262,13 @@ qmoe::DownArgs down_args(const moe_bank *routed, const moe_bank *shared, int T, 
 int run_gate_up(const moe_bank *routed, const moe_bank *shared, const void *x, int T, int k,
                 const moe_align_out *al, int lo, const FwdPlan &p, void *workspace, hipStream_t s) {
   qmoe::GateUpArgs a = gate_up_args(routed, shared, x, T, k, al, lo, p, workspace);
+  if (routed->fmt == MOE_FMT_MXFP4_E8M0) {
+    char *ws = static_cast<char *>(workspace);
+    const int rc = hip_status(qmoe::launch_act_mx8(a.x, T, routed->H, reinterpret_cast<uint8_t *>(ws + p.xq_off),
+                                                   reinterpret_cast<uint8_t *>(ws + p.xs_off), s),
+                              "activation split launch");
+    if (rc) return rc;
+  }
   return hip_status(qmoe::launch_gate_up(routed->fmt, a, p.n_shared_sub, s), "gate_up launch");
 }
 

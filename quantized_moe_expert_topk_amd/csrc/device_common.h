@@ -118,3 +118,85 @@ __device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {
 
 // Wave-wide helpers (wave64).
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63u); }
+
+// ---------------------------------------------------------------------------- scaled FP4 MFMA
+//
+// v_mfma_scale_f32_16x16x128_f8f6f4 with A = fp8 e4m3 (cbsz 0) and B = fp4 e2m1 (blgp 4),
+// operand layouts as measured on gfx950 (wave64, lane l, g = l / 16):
+//   A (16 x 128): lane l holds row l % 16; bytes 0..15 are K [16g, 16g+16) and bytes
+//                 16..31 are K [64+16g, 64+16g+16)
+//   B (128 x 16): lane l holds column l % 16, K [32g, 32g+32) as 32 nibbles (low nibble
+//                 first) in the first 4 dwords
+//   scales:       byte 0 of lane l's scale operand is the e8m0 scale of row (A) or
+//                 column (B) l % 16 over the 32-wide K block g
+//   D:            as the bf16 MFMA (lane l holds D[4g + j][l % 16])
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
+
+__device__ __forceinline__ f32x4_t mfma_scale_e4m3_e2m1(const uint4 &a0, const uint4 &a1, const uint4 &b, uint32_t sa,
+                                                        uint32_t sb, f32x4_t c) {
+  const i32x8_t av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+  const i32x8_t bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 4, 0, (int)sa, 0, (int)sb);
+}
+
+// Two f32 -> two e4m3 bytes (round to nearest even; inputs clamped to the format's +-448).
+__device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
+  a = fminf(fmaxf(a, -448.f), 448.f);
+  b = fminf(fmaxf(b, -448.f), 448.f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// e8m0 block scale for values of magnitude up to amax: the smallest power of two X with
+// amax / X <= 448 (e4m3's largest finite value), so that the top binade of the block uses
+// all of e4m3's precision and nothing saturates; at least 2^-126 so that X is a normal f32.
+// Returns the byte e (X = 2^(e-127)).
+__device__ __forceinline__ uint32_t e8m0_for_amax(float amax) {
+  const uint32_t b = __float_as_uint(amax);
+  const int eb = (int)((b >> 23) & 0xFFu);                        // biased exponent of amax
+  const int e = eb - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);   // mantissa above 1.75 -> next binade
+  return (uint32_t)max(e, 1);
+}
+__device__ __forceinline__ float e8m0_inv(uint32_t e) { return __uint_as_float((254u - e) << 23); }
+
+// Wave-internal max over the 16 lanes of each row (lanes 16q .. 16q+15) and over quads.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));  // quad_perm [1,0,3,2]
+  return fmaxf(v, dpp_f32<0x4E>(v));  // quad_perm [2,3,0,1]
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = quad_max(v);
+  v = fmaxf(v, dpp_f32<0x141>(v));  // row_half_mirror
+  return fmaxf(v, dpp_f32<0x140>(v));  // row_mirror
+}
+
+// Split values into two e4m3 planes with one e8m0 scale each for their 32-element block:
+//   hi = e4m3(v / X1) * X1,  lo = e4m3((v - hi) / X2) * X2
+// amax_fn reduces a magnitude over the lanes that share the block.  Returns the plane
+// bytes of NV values (NV = 2: 16 bits per plane) and the two scale bytes.
+template <int NV, typename AmaxFn>
+__device__ __forceinline__ void mx8_split(const float (&v)[NV], AmaxFn amax_fn, uint32_t (&qhi)[NV / 2],
+                                          uint32_t (&qlo)[NV / 2], uint32_t &s1, uint32_t &s2) {
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; i++) m = fmaxf(m, fabsf(v[i]));
+  s1 = e8m0_for_amax(amax_fn(m));
+  const float inv1 = e8m0_inv(s1), x1 = __uint_as_float(s1 << 23);
+  float res[NV];
+  float m2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; i += 2) {
+    const uint32_t q = e4m3x2(v[i] * inv1, v[i + 1] * inv1);
+    qhi[i / 2] = q;
+    res[i] = v[i] - e4m3_to_f32(q) * x1;
+    res[i + 1] = v[i + 1] - e4m3_to_f32(q >> 8) * x1;
+    m2 = fmaxf(m2, fmaxf(fabsf(res[i]), fabsf(res[i + 1])));
+  }
+  s2 = e8m0_for_amax(amax_fn(m2));
+  const float inv2 = e8m0_inv(s2);
+#pragma unroll
+  for (int i = 0; i < NV; i += 2) qlo[i / 2] = e4m3x2(res[i] * inv2, res[i + 1] * inv2);
+}

@@ -8,13 +8,17 @@
 // [lo,hi): FreeToken issue #62 "What it touches" item 1), and so is the math (issue #520
 // section 4 "Expert sharding": silu(gate)*up @ down, linear in the intermediate index).
 //
-// Weights are dequantized in registers to bf16 and fed to v_mfma_f32_16x16x32_bf16 (W4A16
-// for the FP4 formats, W8A16 for fp8-block):
+// NVFP4 and fp8-block weights are dequantized in registers to bf16 and fed to
+// v_mfma_f32_16x16x32_bf16 (W4A16 / W8A16):
 //   NVFP4      e2m1 * e4m3 group scale (exact in bf16); the fp32 per-row global is applied
 //              to the fp32 accumulator in the epilogue.
-//   MXFP4      e2m1 * 2^(e8m0-127) by the scaled conversion instruction (exact).
 //   FP8_BLOCK  e4m3 -> bf16 exact; the fp32 128x128 block scale multiplies each 128-wide
 //              K chunk's partial sum.
+// MXFP4 (e8m0 per 32) runs on the native scaled MFMA v_mfma_scale_f32_16x16x128_f8f6f4: the
+// raw e2m1 codes and e8m0 bytes are the B operand and its scales, with no dequantization.
+// Its A operand cannot be 16-bit, so x (and h) are carried as two e4m3 planes with e8m0
+// block scales, hi = e4m3(v/X1)*X1 and lo = e4m3((v-hi)/X2)*X2 (about 8 significant bits,
+// the precision of bf16), and each chunk takes one MFMA per plane.
 //
 // Tiling: a workgroup is 4 waves over 16 rows of the pair list (one aligned sub-block of a
 // single expert).  gate_up: 32 slice columns of gate and of up (4 MFMA tiles), K split over
@@ -241,6 +245,102 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
   }
 }
 
+// An activation matrix [rows, K] carried as two e4m3 planes (hi, lo) with an e8m0 scale per
+// 32-element block of each row: q holds plane 0 then plane 1, s the scales likewise.
+struct ActMX {
+  rsrc_t q, s;
+  uint32_t qplane, splane;  // bytes per plane
+  uint32_t K;               // row width in elements
+};
+
+// The MXFP4 counterpart of mma_run: same chunk mapping and grouping (2 chunks per group),
+// but each chunk is two scaled MFMAs (hi and lo plane of A) on the raw FP4 codes.  Within
+// a chunk, lane group g holds A's K [16g, 16g+16) and [64+16g, +16) and B's K [32g, 32g+32)
+// (the instruction's operand layout), so both operands cover the same 128 K indices.
+// Positions at or past kvalid contribute zero: their A bytes and B codes are replaced by
+// zeros and their scales by 1, so stale workspace bytes never reach the MFMA.
+//   a_q, a_s: byte offsets of this lane's row in the planes and in the scales (or
+//             0x80000000 for a padding row, which reads zeros without a memory request)
+template <int NT, int COUNT>
+__device__ __forceinline__ void mma_run_mx(const ActMX &A, uint32_t a_q, uint32_t a_s,
+                                           const WMat<MOE_FMT_MXFP4_E8M0> &m, const uint32_t (&rows)[NT],
+                                           int b_k0, int kw0, int kvalid, int g, f32x4_t (&acc)[NT]) {
+  constexpr int FMT = MOE_FMT_MXFP4_E8M0;
+  const uint32_t K = (uint32_t)m.K;
+  const bool bsal = ((K / 32) % 4 == 0) && (((b_k0 + kw0) / 32) % 4 == 0);
+  const bool asal = ((A.K / 32) % 4 == 0) && ((kw0 / 32) % 4 == 0);
+  const uint4 z = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int i0 = 0; i0 < COUNT; i0 += 2) {
+    const int kg = kw0 + (128 * i0 < kvalid ? 128 * i0 : 0);
+    uint4 bsp[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++) bsp[t] = load_scale_span<FMT>(m.scales, rows[t] * (K / 32) + (b_k0 + kg) / 32, bsal);
+    const uint4 ash = load_scale_span<FMT>(A.s, a_s + kg / 32, asal);
+    const uint4 asl = load_scale_span<FMT>(A.s, A.splane + a_s + kg / 32, asal);
+    uint4 ah[2][2], al[2][2], c[2][NT];
+#pragma unroll
+    for (int ii = 0; ii < 2; ii++) {
+      const int i = i0 + ii;
+      if (i >= COUNT) break;
+      const int kc = kw0 + (128 * i < kvalid ? 128 * i : 0);
+      ah[ii][0] = buf_load16(A.q, a_q + kc + 16 * g);
+      ah[ii][1] = buf_load16(A.q, a_q + kc + 64 + 16 * g);
+      al[ii][0] = buf_load16(A.q, A.qplane + a_q + kc + 16 * g);
+      al[ii][1] = buf_load16(A.q, A.qplane + a_q + kc + 64 + 16 * g);
+      const int kr = 128 * i + 32 * g;
+      const int k = kw0 + (kr < kvalid ? kr : 0);
+#pragma unroll
+      for (int t = 0; t < NT; t++) c[ii][t] = buf_load16(m.codes, rows[t] * (K / 2) + (b_k0 + k) / 2);
+    }
+#pragma unroll
+    for (int ii = 0; ii < 2; ii++) {
+      const int i = i0 + ii;
+      if (i >= COUNT) break;
+      const int rel = 128 * i;
+      const bool vb = rel + 32 * g < kvalid;  // this lane group's 32-wide block (both scales)
+      const bool v0 = rel + 16 * g < kvalid, v1 = rel + 64 + 16 * g < kvalid;
+      const uint4 h0 = v0 ? ah[ii][0] : z, h1 = v1 ? ah[ii][1] : z;
+      const uint4 l0 = v0 ? al[ii][0] : z, l1 = v1 ? al[ii][1] : z;
+      const uint32_t sh = vb ? (span_scales<FMT>(ash, ii, g) & 0xFFu) : 127u;
+      const uint32_t sl = vb ? (span_scales<FMT>(asl, ii, g) & 0xFFu) : 127u;
+#pragma unroll
+      for (int t = 0; t < NT; t++) {
+        const uint4 cb = vb ? c[ii][t] : z;
+        const uint32_t sb = vb ? (span_scales<FMT>(bsp[t], ii, g) & 0xFFu) : 127u;
+        acc[t] = mfma_scale_e4m3_e2m1(h0, h1, cb, sh, sb, acc[t]);
+        acc[t] = mfma_scale_e4m3_e2m1(l0, l1, cb, sl, sb, acc[t]);
+      }
+    }
+  }
+}
+
+// x [rows, K] bf16 -> two e4m3 planes + e8m0 scales (ActMX layout).  A thread converts 8
+// consecutive elements; the 4 lanes of a quad hold one 32-element block (K % 32 == 0).
+__global__ __launch_bounds__(256) void k_act_mx8(const uint16_t *__restrict__ x, int rows, int K,
+                                                 uint8_t *__restrict__ q, uint8_t *__restrict__ sc) {
+  const size_t n8 = (size_t)rows * (K / 8);
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;  // n8 is a multiple of 4: quads leave together
+  const uint4 raw = *reinterpret_cast<const uint4 *>(x + i * 8);
+  float v[8];
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    v[2 * j] = __uint_as_float(w[j] << 16);
+    v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+  }
+  uint32_t qh[4], ql[4], s1, s2;
+  mx8_split<8>(v, [](float m) { return quad_max(m); }, qh, ql, s1, s2);
+  const size_t plane = (size_t)rows * K;
+  *reinterpret_cast<uint2 *>(q + i * 8) = make_uint2(qh[0] | (qh[1] << 16), qh[2] | (qh[3] << 16));
+  *reinterpret_cast<uint2 *>(q + plane + i * 8) = make_uint2(ql[0] | (ql[1] << 16), ql[2] | (ql[3] << 16));
+  if ((i & 3) == 0) {
+    sc[i / 4] = (uint8_t)s1;
+    sc[plane / 32 + i / 4] = (uint8_t)s2;
+  }
+}
+
 // ---------------------------------------------------------------------------- gate_up
 
 // Workgroup = 4 waves on one 16-row block and GCOLS slice columns [c0, c0+GCOLS): tiles
@@ -254,6 +354,7 @@ constexpr int kMinWaves = 3;  // waves per SIMD the expert kernels are compiled 
 template <int FMT, int COUNT>
 __global__ __launch_bounds__(256, kMinWaves) void k_gate_up(GateUpArgs a) {
   __shared__ float red[4][2 * GT][4][64];  // [wave][tile][j][lane]
+  __shared__ float hbuf[16][GCOLS + 1];     // MXFP4: the block's h before the plane split
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int sb = blockIdx.x;
@@ -297,16 +398,27 @@ __global__ __launch_bounds__(256, kMinWaves) void k_gate_up(GateUpArgs a) {
     gsc[t] = FMT == MOE_FMT_NVFP4 ? glob[(size_t)e * 2 * I + rows[t]] : 1.f;
     usc[t] = FMT == MOE_FMT_NVFP4 ? glob[(size_t)e * 2 * I + rows[GT + t]] : 1.f;
   }
-  // padding rows point past the activation buffer: they read zeros without a memory request
-  const rsrc_t ra = make_rsrc(a.x, (uint32_t)a.T * H * 2);
-  const uint32_t a_row = tok >= 0 ? (uint32_t)tok * H * 2 : 0x80000000u;
   f32x4_t acc[2 * GT];
 #pragma unroll
   for (int t = 0; t < 2 * GT; t++) acc[t] = zero4();
   // K split: wave w < a.kwaves takes [w*kw, (w+1)*kw), kw = 128 * a.ksteps
-  if (wave < a.kwaves) {  // COUNT >= ksteps; steps past ksteps are masked
-    const int kw = 128 * a.ksteps;
-    mma_run<FMT, 2 * GT, COUNT>(ra, a_row, m, rows, 0, wave * kw, kw, g, acc);
+  // in runs of COUNT steps.  Padding rows point past the
+  // activation buffer: they read zeros without a memory request.
+  const int kw = 128 * a.ksteps;
+  if constexpr (FMT == MOE_FMT_MXFP4_E8M0) {
+    const uint32_t T = (uint32_t)a.T;
+    const ActMX A{make_rsrc(a.xq, 2 * T * H), make_rsrc(a.xs, 2 * T * (H / 32)), T * H, T * (H / 32), (uint32_t)H};
+    const uint32_t aq = tok >= 0 ? (uint32_t)tok * H : 0x80000000u;
+    const uint32_t as = tok >= 0 ? (uint32_t)tok * (H / 32) : 0x80000000u;
+    if (wave < a.kwaves)
+      for (int kk = 0; kk < kw; kk += 128 * COUNT)  // runs of COUNT steps; the tail is masked
+        mma_run_mx<2 * GT, COUNT>(A, aq, as, m, rows, 0, wave * kw + kk, kw - kk, g, acc);
+  } else {
+    const rsrc_t ra = make_rsrc(a.x, (uint32_t)a.T * H * 2);
+    const uint32_t a_row = tok >= 0 ? (uint32_t)tok * H * 2 : 0x80000000u;
+    if (wave < a.kwaves)
+      for (int kk = 0; kk < kw; kk += 128 * COUNT)
+        mma_run<FMT, 2 * GT, COUNT>(ra, a_row, m, rows, 0, wave * kw + kk, kw - kk, g, acc);
   }
 #pragma unroll
   for (int t = 0; t < 2 * GT; t++)
@@ -326,7 +438,27 @@ __global__ __launch_bounds__(256, kMinWaves) void k_gate_up(GateUpArgs a) {
       gv *= gsc[t];
       uv *= usc[t];
       const float hv = gv / (1.f + __expf(-gv)) * uv;
-      a.h[(size_t)(p0 + 4 * g + j) * a.Il + c0 + 16 * t + r] = bf16_bits(hv);
+      if constexpr (FMT == MOE_FMT_MXFP4_E8M0)
+        hbuf[4 * g + j][16 * t + r] = hv;
+      else
+        a.h[(size_t)(p0 + 4 * g + j) * a.Il + c0 + 16 * t + r] = bf16_bits(hv);
+    }
+  }
+  if constexpr (FMT == MOE_FMT_MXFP4_E8M0) {
+    // h rows of this block, columns [c0, c0 + 32) = one e8m0 block: 16 lanes per row
+    __syncthreads();
+    const int row = threadIdx.x >> 4, cp = (threadIdx.x & 15) * 2;
+    const float v[2] = {hbuf[row][cp], hbuf[row][cp + 1]};
+    uint32_t qh[1], ql[1], s1, s2;
+    mx8_split<2>(v, [](float x) { return row16_max(x); }, qh, ql, s1, s2);
+    const size_t Il = (size_t)a.Il, hplane = (size_t)a.h_rows * Il, splane = (size_t)a.h_rows * (Il / 32);
+    const size_t o = (size_t)(p0 + row) * Il + c0 + cp;
+    *reinterpret_cast<uint16_t *>(a.hq + o) = (uint16_t)qh[0];
+    *reinterpret_cast<uint16_t *>(a.hq + hplane + o) = (uint16_t)ql[0];
+    if ((threadIdx.x & 15) == 0) {
+      const size_t so = (size_t)(p0 + row) * (Il / 32) + c0 / 32;
+      a.hs[so] = (uint8_t)s1;
+      a.hs[splane + so] = (uint8_t)s2;
     }
   }
 }
@@ -395,10 +527,19 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
   for (int t = 0; t < DNT; t++) dglob[t] = FMT == MOE_FMT_NVFP4 ? glob[(size_t)e * H + n0 + 16 * t + r] : 1.f;
   // padding rows (no pair / past T) point past h: they read zeros without a memory request
   const bool real = is_shared ? (p0 - a.cap + r < a.T) : (a.sorted_ids[p0 + r] < P);
-  const rsrc_t ra = make_rsrc(a.h, (uint32_t)a.h_rows * Il * 2);
-  const uint32_t a_row = real ? (uint32_t)(p0 + r) * Il * 2 : 0x80000000u;
-  for (int kw0 = 0; kw0 < Il; kw0 += 128 * COUNT)  // runs of COUNT steps; the tail is masked
-    mma_run<FMT, DNT, COUNT>(ra, a_row, m, rows, a.lo, kw0, Il - kw0, g, acc);
+  if constexpr (FMT == MOE_FMT_MXFP4_E8M0) {
+    const uint32_t hr = (uint32_t)a.h_rows, ul = (uint32_t)Il;
+    const ActMX A{make_rsrc(a.hq, 2 * hr * ul), make_rsrc(a.hs, 2 * hr * (ul / 32)), hr * ul, hr * (ul / 32), ul};
+    const uint32_t aq = real ? (uint32_t)(p0 + r) * ul : 0x80000000u;
+    const uint32_t as = real ? (uint32_t)(p0 + r) * (ul / 32) : 0x80000000u;
+    for (int kw0 = 0; kw0 < Il; kw0 += 128 * COUNT)  // runs of COUNT steps; the tail is masked
+      mma_run_mx<DNT, COUNT>(A, aq, as, m, rows, a.lo, kw0, Il - kw0, g, acc);
+  } else {
+    const rsrc_t ra = make_rsrc(a.h, (uint32_t)a.h_rows * Il * 2);
+    const uint32_t a_row = real ? (uint32_t)(p0 + r) * Il * 2 : 0x80000000u;
+    for (int kw0 = 0; kw0 < Il; kw0 += 128 * COUNT)
+      mma_run<FMT, DNT, COUNT>(ra, a_row, m, rows, a.lo, kw0, Il - kw0, g, acc);
+  }
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     if (dst[j] < 0) continue;
@@ -446,15 +587,22 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ Y, in
 // ---------------------------------------------------------------------------- launchers
 
 // Step count of a K run as a template argument: 1, 2, 4 or 8 (runs are masked past K).
-static int count_class(int steps) { return steps <= 1 ? 1 : steps <= 2 ? 2 : steps <= 4 ? 4 : 8; }
+// Longer K ranges loop over runs; fp8-block and MXFP4 keep runs at 4 steps or fewer, past
+// which their per-step operand registers no longer fit the occupancy target.
+static int count_class(int fmt, int steps) {
+  const int c = steps <= 1 ? 1 : steps <= 2 ? 2 : steps <= 4 ? 4 : 8;
+  return fmt == MOE_FMT_NVFP4 ? c : (c < 4 ? c : 4);
+}
 
 template <int FMT>
 static void launch_gate_up_fmt(const GateUpArgs &a, dim3 grid, hipStream_t s) {
-  switch (count_class(a.ksteps)) {
+  switch (count_class(FMT, a.ksteps)) {
     case 1: hipLaunchKernelGGL((k_gate_up<FMT, 1>), grid, dim3(256), 0, s, a); break;
     case 2: hipLaunchKernelGGL((k_gate_up<FMT, 2>), grid, dim3(256), 0, s, a); break;
     case 4: hipLaunchKernelGGL((k_gate_up<FMT, 4>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_gate_up<FMT, 8>), grid, dim3(256), 0, s, a); break;
+    default:
+      if constexpr (FMT == MOE_FMT_NVFP4) hipLaunchKernelGGL((k_gate_up<FMT, 8>), grid, dim3(256), 0, s, a);
+      break;
   }
 }
 
@@ -470,11 +618,13 @@ hipError_t launch_gate_up(int fmt, const GateUpArgs &a, int n_shared_sub, hipStr
 
 template <int FMT>
 static void launch_down_fmt(const DownArgs &a, dim3 grid, hipStream_t s) {
-  switch (count_class((a.Il + 127) / 128)) {
+  switch (count_class(FMT, (a.Il + 127) / 128)) {
     case 1: hipLaunchKernelGGL((k_down<FMT, 1>), grid, dim3(256), 0, s, a); break;
     case 2: hipLaunchKernelGGL((k_down<FMT, 2>), grid, dim3(256), 0, s, a); break;
     case 4: hipLaunchKernelGGL((k_down<FMT, 4>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_down<FMT, 8>), grid, dim3(256), 0, s, a); break;
+    default:
+      if constexpr (FMT == MOE_FMT_NVFP4) hipLaunchKernelGGL((k_down<FMT, 8>), grid, dim3(256), 0, s, a);
+      break;
   }
 }
 
@@ -485,6 +635,13 @@ hipError_t launch_down(int fmt, const DownArgs &a, int n_shared_sub, hipStream_t
     case MOE_FMT_MXFP4_E8M0: launch_down_fmt<MOE_FMT_MXFP4_E8M0>(a, grid, s); break;
     default: launch_down_fmt<MOE_FMT_FP8_BLOCK128>(a, grid, s); break;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_act_mx8(const uint16_t *x, int rows, int K, uint8_t *q, uint8_t *sc, hipStream_t s) {
+  const size_t n8 = (size_t)rows * (K / 8);
+  if (n8 == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_act_mx8, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, x, rows, K, q, sc);
   return hipGetLastError();
 }
 

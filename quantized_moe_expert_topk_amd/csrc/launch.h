@@ -21,11 +21,16 @@ struct GateUpArgs {
   int block_m, cap, n_routed_sub;  // n_routed_sub = cap / 16
   int lo, Il;
   int kwaves, ksteps;  // K split of gate_up: kwaves waves x ksteps steps of 128 (H = 128*kwaves*ksteps)
-  uint16_t *h;  // [cap + 16 * n_shared_sub, Il] bf16
+  uint16_t *h;  // [h_rows, Il] bf16 (NVFP4, fp8-block)
+  int h_rows;   // cap + 16 * n_shared_sub
+  // MXFP4: x and h as two e4m3 planes with e8m0 scales per 32 (plane 1 follows plane 0)
+  const uint8_t *xq, *xs;  // [2][T][H], [2][T][H/32]
+  uint8_t *hq, *hs;        // [2][h_rows][Il], [2][h_rows][Il/32]
 };
 
 struct DownArgs {
   const uint16_t *h;
+  const uint8_t *hq, *hs;  // MXFP4 (see GateUpArgs)
   int h_rows;  // rows of h (cap + shared rows)
   int T, H, k;
   const uint8_t *dn, *dns;
@@ -52,6 +57,7 @@ hipError_t launch_align(const int32_t *ids, int T, int k, int E, int BM, int cap
                         int32_t *hist, hipStream_t s);
 hipError_t launch_gate_up(int fmt, const GateUpArgs &a, int n_shared_sub, hipStream_t s);
 hipError_t launch_down(int fmt, const DownArgs &a, int n_shared_sub, hipStream_t s);
+hipError_t launch_act_mx8(const uint16_t *x, int rows, int K, uint8_t *q, uint8_t *sc, hipStream_t s);
 hipError_t launch_combine(const float *Y, int T, int k, int H, int has_shared, void *out, int out_bf16,
                           hipStream_t s);
 

@@ -143,7 +143,9 @@ FORWARD_CASES = [(1, 16, (0, 128)), (1, 16, (0, 64)), (1, 16, (64, 128)),
                  (2, 1, (0, 256)), (2, 8, (0, 256)), (2, 32, (0, 256)), (2, 64, (0, 256)), (2, 64, (0, 512)),
                  (2, 1, (0, 512)),
                  (4, 1, (0, 256)), (4, 64, (0, 256)), (4, 64, (0, 512)),
-                 (5, 1, (0, 1024)), (5, 16, (0, 1024)), (5, 16, (1024, 2048))]
+                 (5, 1, (0, 1024)), (5, 16, (0, 1024)), (5, 16, (1024, 2048)),
+                 # MXFP4 slices off the 128-wide chunk grid: a masked K tail, unaligned scale spans
+                 (5, 16, (0, 96)), (5, 16, (32, 160)), (5, 1, (992, 2048))]
 
 
 @pytest.mark.parametrize("cid,T,sl", FORWARD_CASES)
@@ -181,7 +183,7 @@ def test_full_layer_matches_oracle(cid, T, sl):
 
 
 @pytest.mark.parametrize("cid,T,cuts", [(1, 16, (0, 64, 128)), (2, 64, (0, 256, 512)), (4, 64, (0, 256, 512)),
-                                        (2, 8, (0, 128, 384, 512))])
+                                        (2, 8, (0, 128, 384, 512)), (5, 16, (0, 96, 1024, 2048))])
 def test_gpu_slices_sum_to_gpu_full(cid, T, cuts):
     """Linearity in the intermediate index on the GPU: disjoint slices tiling [0, I) sum to
     the unsliced GPU result (issue #520 section 4)."""
