@@ -158,7 +158,7 @@ int moe_align(const int32_t *topk_ids, int T, int k, int E, const moe_align_out 
 /* ------------------------------------------------------------------ expert layer */
 
 /* Device workspace moe_expert_forward needs for (routed, shared, T, k, block_m, slice):
- * with rows = capacity + 16*ceil(T/16) if shared else capacity, Il = hi - lo, and each
+ * with rows = capacity + 128*ceil(T/128) if shared else capacity, Il = hi - lo, and each
  * term rounded up to 256 bytes,
  *   NVFP4, FP8_BLOCK128:  rows*Il*2  +  (T*k + T_shared)*H*4
  *   MXFP4:  2*rows*Il + 2*rows*Il/32 + 2*T*H + 2*T*H/32  +  (T*k + T_shared)*H*4
@@ -194,7 +194,11 @@ size_t moe_workspace_bytes(const moe_bank *routed, const moe_bank *shared, int T
  *               multiple_of=128)).  The kernels additionally need (hi - lo) % 32 == 0.
  *   out         [T, H] f32 (out_dtype MOE_OUT_F32) or bf16 (MOE_OUT_BF16), overwritten.
  *   workspace   >= moe_workspace_bytes(...) bytes of device memory.
- * Experts that received no tokens are never read. */
+ * Experts that received no tokens are never read.  The align block size picks the kernels:
+ * al->block_m a multiple of 128 runs NVFP4 and FP8_BLOCK128 on LDS-tiled GEMMs that reuse
+ * each weight tile across 128 pair rows (for many tokens per expert); other block sizes,
+ * and MXFP4, run the streaming kernels that read each selected weight byte once per
+ * 16-row block (for few tokens per expert).  Both compute the same result. */
 int moe_expert_forward(const moe_bank *routed, const moe_bank *shared, const void *x_bf16,
                        int T, int k, const float *topk_w, const moe_align_out *al,
                        int slice_lo, int slice_hi, void *out, int out_dtype, void *workspace,

@@ -208,10 +208,13 @@ def moe_expert_down(routed: DeviceBank, shared: DeviceBank | None, topk_w: torch
         slice_lo, slice_hi, _ptr(out), code, _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
-def choose_block_m(T: int, k: int, E: int) -> int:
+def choose_block_m(T: int, k: int, E: int, fmt: str | None = None) -> int:
     """Rows per aligned block: 16 while experts see few tokens each, larger as the mean
-    number of pairs per expert grows."""
+    number of pairs per expert grows; 128 (the LDS-tiled GEMMs) once experts see enough
+    tokens to reuse each weight tile, for the formats those kernels cover."""
     mean = T * k / max(E, 1)
+    if mean >= 32 and fmt in ("nvfp4", "fp8blk"):
+        return 128
     if mean <= 16:
         return 16
     if mean <= 64:
@@ -230,7 +233,7 @@ class MoeLayer:
         dev = w_router.device
         self.routed, self.shared, self.w_router, self.bias = routed, shared, w_router, bias
         self.T, self.k, self.lo, self.hi, self.renormalize = T, k, slice_lo, slice_hi, renormalize
-        self.block_m = block_m or choose_block_m(T, k, routed.E)
+        self.block_m = block_m or choose_block_m(T, k, routed.E, routed.fmt)
         E = routed.E
         self.logits = torch.empty((T, E), dtype=torch.float32, device=dev)
         self.ids = torch.empty((T, k), dtype=torch.int32, device=dev)

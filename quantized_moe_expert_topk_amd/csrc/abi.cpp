@@ -137,7 +137,8 @@ int check_align_out(const moe_align_out *al, int T, int k, int E) {
 }
 
 struct FwdPlan {
-  int Il, n_routed_sub, n_shared_sub, shared_rows, h_rows, P, Psh;
+  int Il, n_routed_sub, n_shared_sub, n_shared_tiles, shared_rows, h_rows, P, Psh;
+  bool tiled;  // 128-row align blocks (NVFP4, FP8_BLOCK128): the LDS-tiled kernels
   // workspace layout: [h][x planes (MXFP4)][Y]; MXFP4 h is [hq][hs], x is [xq][xs]
   size_t hs_off, xq_off, xs_off, y_off, y_bytes, total;
 };
@@ -147,8 +148,10 @@ FwdPlan plan_forward(const moe_bank *routed, const moe_bank *shared, int T, int 
   p.Il = hi - lo;
   p.n_routed_sub = cap / 16;
   p.n_shared_sub = shared ? (T + 15) / 16 : 0;
-  p.shared_rows = p.n_shared_sub * 16;
+  p.n_shared_tiles = shared ? (T + 127) / 128 : 0;
+  p.shared_rows = p.n_shared_tiles * 128;  // room for whole 128-row tiles
   p.h_rows = cap + p.shared_rows;
+  p.tiled = false;
   p.P = T * k;
   p.Psh = shared ? T : 0;
   const size_t rows = (size_t)p.h_rows, Il = (size_t)p.Il, H = (size_t)routed->H;
@@ -187,6 +190,7 @@ int check_forward(const moe_bank *routed, const moe_bank *shared, int T, int k, 
   if (rc) return rc;
   if ((long long)T * k > (1LL << 30)) return fail(MOE_ERR_UNSUPPORTED, "T*k too large");
   *plan = plan_forward(routed, shared, T, k, al->capacity, lo, hi);
+  plan->tiled = al->block_m % 128 == 0 && routed->fmt != MOE_FMT_MXFP4_E8M0;
   if (workspace_bytes < plan->total)
     return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, plan->total);
   if (!workspace && plan->total) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
@@ -269,6 +273,7 @@ int run_gate_up(const moe_bank *routed, const moe_bank *shared, const void *x, i
                               "activation split launch");
     if (rc) return rc;
   }
+  if (p.tiled) return hip_status(qmoe::launch_gate_up_tiled(routed->fmt, a, p.n_shared_tiles, s), "gate_up launch");
   return hip_status(qmoe::launch_gate_up(routed->fmt, a, p.n_shared_sub, s), "gate_up launch");
 }
 
@@ -276,7 +281,8 @@ int run_down(const moe_bank *routed, const moe_bank *shared, int T, int k, const
              const moe_align_out *al, int lo, const FwdPlan &p, void *out, int out_dtype, void *workspace,
              hipStream_t s) {
   qmoe::DownArgs a = down_args(routed, shared, T, k, topk_w, al, lo, p, workspace);
-  int rc = hip_status(qmoe::launch_down(routed->fmt, a, p.n_shared_sub, s), "down launch");
+  int rc = p.tiled ? hip_status(qmoe::launch_down_tiled(routed->fmt, a, p.n_shared_tiles, s), "down launch")
+                   : hip_status(qmoe::launch_down(routed->fmt, a, p.n_shared_sub, s), "down launch");
   if (rc) return rc;
   return hip_status(qmoe::launch_combine(a.Y, T, k, routed->H, shared != nullptr, out, out_dtype == MOE_OUT_BF16, s),
                     "combine launch");

@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "qmoe.h"
+
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
@@ -114,6 +116,38 @@ __device__ __forceinline__ uint32_t buf_load1(rsrc_t r, uint32_t off) {
 
 __device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
+// ---------------------------------------------------------------------------- weights
+
+// One expert's weight matrix [rows, K] (K = row width in elements) as buffer resources.
+template <int FMT>
+struct WMat {
+  rsrc_t codes, scales;
+  int K;
+};
+
+template <int FMT>
+__device__ __forceinline__ WMat<FMT> weight_matrix(const uint8_t *codes, const uint8_t *scales, int e, int rows,
+                                                   int K) {
+  WMat<FMT> m;
+  m.K = K;
+  if constexpr (FMT == MOE_FMT_NVFP4) {
+    m.codes = make_rsrc(codes + (size_t)e * rows * (K / 2), (uint32_t)rows * (K / 2));
+    m.scales = make_rsrc(scales + (size_t)e * rows * (K / 16), (uint32_t)rows * (K / 16));
+  } else if constexpr (FMT == MOE_FMT_MXFP4_E8M0) {
+    m.codes = make_rsrc(codes + (size_t)e * rows * (K / 2), (uint32_t)rows * (K / 2));
+    m.scales = make_rsrc(scales + (size_t)e * rows * (K / 32), (uint32_t)rows * (K / 32));
+  } else {
+    m.codes = make_rsrc(codes + (size_t)e * rows * K, (uint32_t)rows * K);
+    m.scales = make_rsrc(scales + (size_t)e * (rows / 128) * (K / 128) * 4, (uint32_t)(rows / 128) * (K / 128) * 4);
+  }
+  return m;
+}
+
+__device__ __forceinline__ void zero_frags(frag8 (&b)[4]) {
+#pragma unroll
+  for (int q = 0; q < 4; q++) b[q].q = make_uint4(0, 0, 0, 0);
 }
 
 // Wave-wide helpers (wave64).

@@ -32,33 +32,6 @@
 
 namespace qmoe {
 
-// ---------------------------------------------------------------------------- B operand
-
-// One expert's weight matrix [rows, K] (K = row width in elements) as buffer resources.
-template <int FMT>
-struct WMat {
-  rsrc_t codes, scales;
-  int K;
-};
-
-template <int FMT>
-__device__ __forceinline__ WMat<FMT> weight_matrix(const uint8_t *codes, const uint8_t *scales, int e, int rows,
-                                                   int K) {
-  WMat<FMT> m;
-  m.K = K;
-  if constexpr (FMT == MOE_FMT_NVFP4) {
-    m.codes = make_rsrc(codes + (size_t)e * rows * (K / 2), (uint32_t)rows * (K / 2));
-    m.scales = make_rsrc(scales + (size_t)e * rows * (K / 16), (uint32_t)rows * (K / 16));
-  } else if constexpr (FMT == MOE_FMT_MXFP4_E8M0) {
-    m.codes = make_rsrc(codes + (size_t)e * rows * (K / 2), (uint32_t)rows * (K / 2));
-    m.scales = make_rsrc(scales + (size_t)e * rows * (K / 32), (uint32_t)rows * (K / 32));
-  } else {
-    m.codes = make_rsrc(codes + (size_t)e * rows * K, (uint32_t)rows * K);
-    m.scales = make_rsrc(scales + (size_t)e * (rows / 128) * (K / 128) * 4, (uint32_t)(rows / 128) * (K / 128) * 4);
-  }
-  return m;
-}
-
 // Scale run of one lane: NB consecutive scale bytes starting at byte `off` (any
 // alignment), gathered with dword loads and funnel shifts.  Bytes past the resource read
 // as 0 (buffer range check).
@@ -121,11 +94,6 @@ __device__ __forceinline__ void decode_mxfp4(const uint4 &c, uint32_t e8, frag8 
   fp4x8_pow2_to_bf16(c.y, p, b[1]);
   fp4x8_pow2_to_bf16(c.z, p, b[2]);
   fp4x8_pow2_to_bf16(c.w, p, b[3]);
-}
-
-__device__ __forceinline__ void zero_frags(frag8 (&b)[4]) {
-#pragma unroll
-  for (int q = 0; q < 4; q++) b[q].q = make_uint4(0, 0, 0, 0);
 }
 
 // Scale bytes of one tile row for a group of 2 K steps (chunk mapping): NVFP4 16 bytes

@@ -57,6 +57,10 @@ hipError_t launch_align(const int32_t *ids, int T, int k, int E, int BM, int cap
                         int32_t *hist, hipStream_t s);
 hipError_t launch_gate_up(int fmt, const GateUpArgs &a, int n_shared_sub, hipStream_t s);
 hipError_t launch_down(int fmt, const DownArgs &a, int n_shared_sub, hipStream_t s);
+// Tiled kernels for align blocks of 128 rows (NVFP4, FP8_BLOCK128); the shared expert's
+// rows are ceil(T/128) tiles after the routed ones.
+hipError_t launch_gate_up_tiled(int fmt, const GateUpArgs &a, int n_shared_tiles, hipStream_t s);
+hipError_t launch_down_tiled(int fmt, const DownArgs &a, int n_shared_tiles, hipStream_t s);
 hipError_t launch_act_mx8(const uint16_t *x, int rows, int K, uint8_t *q, uint8_t *sc, hipStream_t s);
 hipError_t launch_combine(const float *Y, int T, int k, int H, int has_shared, void *out, int out_bf16,
                           hipStream_t s);

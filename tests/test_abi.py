@@ -116,12 +116,12 @@ def test_workspace_bytes_formula():
     lib = L.lib()
     T, k, bm = 16, 2, 16
     cap = qm.moe_align_capacity(T, k, 8, bm)
-    h = -(-((cap + 16) * 64 * 2) // 256) * 256
+    h = -(-((cap + 128) * 64 * 2) // 256) * 256
     y = -(-((T * k + T) * 256 * 4) // 256) * 256
     assert lib.moe_workspace_bytes(ctypes.byref(b), ctypes.byref(s), T, k, bm, 0, 64) == h + y
     # MXFP4: the intermediate and the activation as two e4m3 planes plus their e8m0 scales
     mb, ms = _bank(fmt=3, glob=False), _bank(fmt=3, E=1, glob=False)
     up = lambda n: -(-n // 256) * 256  # noqa: E731
-    rows = cap + 16
+    rows = cap + 128
     want = up(2 * rows * 64) + up(2 * rows * 2) + up(2 * T * 256) + up(2 * T * 8) + y
     assert lib.moe_workspace_bytes(ctypes.byref(mb), ctypes.byref(ms), T, k, bm, 0, 64) == want

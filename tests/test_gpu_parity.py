@@ -4,6 +4,8 @@ Routing selection and alignment are compared bit for bit; expert outputs must me
 max|delta| <= 1e-2 * max|ref| + 1e-3.  Inputs come from the seeded generator or from the
 oracle, never from the GPU path.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -163,6 +165,38 @@ def test_expert_forward_any_block_m(bm):
     inp, r = inputs_for(2, 64)
     ref = O.expert_forward(inp.routed, inp.shared, inp.x, r["ids"], r["w"], 0, 256)
     check_close(f"cfg2 T=64 bm={bm}", _forward_gpu(inp, r["ids"], r["w"], 0, 256, bm=bm), ref)
+
+
+TILED_CASES = [(1, 16, (0, 128)), (1, 16, (32, 96)), (2, 64, (0, 256)), (2, 32, (0, 96)), (2, 8, (64, 512)),
+               (4, 64, (0, 256)), (4, 64, (256, 512))]
+
+
+@pytest.mark.parametrize("cid,T,sl", TILED_CASES)
+def test_tiled_kernels_match_oracle(cid, T, sl):
+    """128-row align blocks select the LDS-tiled GEMMs (NVFP4, fp8-block); small cases
+    cover partial column tiles and a 32-wide K tail."""
+    inp, r = inputs_for(cid, T)
+    lo, hi = sl
+    ref = O.expert_forward(inp.routed, inp.shared, inp.x, r["ids"], r["w"], lo, hi)
+    check_close(f"tiled cfg{cid} T={T} [{lo},{hi})", _forward_gpu(inp, r["ids"], r["w"], lo, hi, bm=128), ref)
+
+
+@pytest.mark.parametrize("cid,T,sl,bm", [(3, 8192, (0, 512), 128), (3, 8192, (0, 256), 128),
+                                         (4, 4096, (0, 256), 128), (3, 8192, (0, 512), 64)])
+def test_prefill_full_size_sampled_rows(cid, T, sl, bm):
+    """Full-size prefill on the GPU (every tile of the real routing, Zipf-skewed for
+    config 3), checked on a seeded sample of token rows the oracle computes one by one."""
+    inp, r = inputs_for(cid, T)
+    lo, hi = sl
+    got = _forward_gpu(inp, r["ids"], r["w"], lo, hi, bm=bm)
+    rows = np.sort(np.random.default_rng(11).choice(T, 12, replace=False))
+    # the hottest expert's first and last tokens, where its many row tiles begin and end
+    hot = np.flatnonzero((r["ids"] == np.bincount(r["ids"].ravel()).argmax()).any(1))
+    rows = np.unique(np.concatenate([rows, hot[:2], hot[-2:], [T - 1]]))
+    sub = dataclasses.replace(inp, x=np.ascontiguousarray(inp.x[rows]))
+    ref = O.expert_forward(sub.routed, sub.shared, sub.x, r["ids"][rows], r["w"][rows], lo, hi)
+    check_close(f"prefill cfg{cid} T={T} [{lo},{hi}) bm={bm} rows={len(rows)}", got[rows], ref)
+    assert np.isfinite(got).all()
 
 
 @pytest.mark.parametrize("cid,T,sl", [(1, 16, (0, 128)), (2, 64, (0, 256)), (5, 16, (0, 1024))])
