@@ -4,7 +4,7 @@
 // [lo,hi) of one rank's slice: FreeToken issue #62 "What it touches" item 1; SwiGLU expert
 // linear in the intermediate index: issue #520 section 4), tiled for reuse instead of
 // streaming: a workgroup owns a 128-row block of the aligned pair list (one expert) and 128
-// weight rows, and walks K in stages of 64.  Per stage the activation tile (gathered token
+// weight rows, and walks K in stages of 64 (gate_up) or 32 (down).  Per stage the activation tile (gathered token
 // rows of x, or rows of h) and the weight tile are staged in LDS, the weight tile
 // dequantized to bf16 once per workgroup; 4 waves then run 2 x 2 blocks of 64 x 64 outputs
 // on v_mfma_f32_16x16x32_bf16.  LDS is double buffered: the global loads of stage s+1 are
@@ -20,86 +20,134 @@
 namespace qmoe {
 namespace {
 
-constexpr int TM = 128;       // pair rows per tile = one align block of 128
-constexpr int TW = 128;       // weight rows per tile
-constexpr int TK = 64;        // K per stage
-constexpr int LDP = TK + 8;   // LDS row pitch in bf16 elements (144 B: 16-row reads hit distinct banks)
+constexpr int TM = 128;  // pair rows per tile = one align block of 128
+constexpr int TW = 128;  // weight rows per tile
 
+// K per stage TK is 64 (gate_up: K = H is long) or 32 (down: K = the slice, short, where
+// the smaller LDS footprint lets more workgroups share a CU).  Derived sizes:
+template <int TK> struct Stage {
+  static constexpr int CPR = TK / 8;    // 16-byte chunks per LDS row (bf16)
+  static constexpr int NQ = CPR / 2;    // activation chunks each thread stages per stage
+  static constexpr int RPI = 64 / CPR;  // tile rows one wave instruction covers when staging
+  static constexpr int WK = TK / 2;     // weights per thread per stage (half a tile row)
+};
+
+// LDS tiles are stored XOR-swizzled: K chunk c (elements [8c, 8c+8)) of tile row R sits at
+// chunk c ^ (R & 7) of its 128-byte row (TK 64) or c ^ ((R >> 1) & 3) of its 64-byte row
+// (TK 32).  The MFMA operand reads (16 rows x one chunk per lane group) and the stores
+// then run at full LDS bandwidth on gfx950, which a plain or padded pitch does not reach
+// for 16-row reads.
+template <int TK>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return TK == 64 ? 8 * (chunk ^ (row & 7)) : 8 * (chunk ^ ((row >> 1) & 3));
+}
+
+template <int TK>
 struct TileLDS {
-  uint16_t a[2][TM][LDP];
-  uint16_t b[2][TW][LDP];
+  uint16_t a[2][TM][TK];
+  uint16_t b[2][TW][TK];
 };
 
 // ---------------------------------------------------------------- stage loads and stores
 
-// Activation tile: a thread moves 4 pieces of 16 B; piece q is row 32*wave + 8*q + lane/8,
-// columns [8*(lane%8), +8) of the stage (each row's 128 B are read by 8 adjacent lanes).
+// Activation tile: thread chunk q covers row 32*wave + RPI*q + lane/CPR, K chunk lane%CPR
+// (adjacent lanes read one row's TK*2 bytes).
+template <int TK>
+__device__ __forceinline__ int a_row_of(int wave, int lane, int q) {
+  return 32 * wave + Stage<TK>::RPI * q + lane / Stage<TK>::CPR;
+}
+
+template <int TK>
 struct ATile {
-  uint4 v[4];
+  uint4 v[Stage<TK>::NQ];
 };
 
-__device__ __forceinline__ void a_fetch(rsrc_t ra, const uint32_t (&row_off)[4], int k0, int seg, ATile &t) {
+template <int TK>
+__device__ __forceinline__ void a_fetch(rsrc_t ra, const uint32_t (&row_off)[Stage<TK>::NQ], int k0, int lane,
+                                        ATile<TK> &t) {
 #pragma unroll
-  for (int q = 0; q < 4; q++) t.v[q] = buf_load16(ra, row_off[q] + (uint32_t)(k0 + 8 * seg) * 2);
+  for (int q = 0; q < Stage<TK>::NQ; q++)
+    t.v[q] = buf_load16(ra, row_off[q] + (uint32_t)(k0 + 8 * (lane % Stage<TK>::CPR)) * 2);
 }
 
-__device__ __forceinline__ void a_store(uint16_t (*la)[LDP], const ATile &t, int wave, int lane) {
+template <int TK>
+__device__ __forceinline__ void a_store(uint16_t (*la)[TK], const ATile<TK> &t, int wave, int lane) {
 #pragma unroll
-  for (int q = 0; q < 4; q++)
-    *reinterpret_cast<uint4 *>(&la[32 * wave + 8 * q + (lane >> 3)][8 * (lane & 7)]) = t.v[q];
+  for (int q = 0; q < Stage<TK>::NQ; q++) {
+    const int row = a_row_of<TK>(wave, lane, q);
+    *reinterpret_cast<uint4 *>(&la[row][swz<TK>(row, lane % Stage<TK>::CPR)]) = t.v[q];
+  }
 }
 
-// Weight tile: a thread owns tile row tid/2 and the 32-wide K half tid%2 of the stage.
+// Weight tile: a thread owns tile row tid/2 and the K half tid%2 of the stage (WK weights).
 struct BTile {
-  uint4 c0, c1;  // codes: 16 B (FP4) or 32 B (FP8)
-  uint32_t sc;   // NVFP4: the two e4m3 group scales
+  uint4 c0, c1;  // codes: WK/2 bytes (FP4) or WK bytes (FP8)
+  uint32_t sc;   // NVFP4: the e4m3 scales of the WK/16 groups
 };
 
-template <int FMT>
+template <int FMT, int TK>
 __device__ __forceinline__ void b_fetch(const WMat<FMT> &m, uint32_t row, int k, BTile &t) {
   const uint32_t K = (uint32_t)m.K;
   if constexpr (FMT == MOE_FMT_NVFP4) {
-    t.c0 = buf_load16(m.codes, row * (K / 2) + k / 2);
-    t.sc = buf_load2(m.scales, row * (K / 16) + k / 16);
+    if constexpr (TK == 64) {
+      t.sc = buf_load2(m.scales, row * (K / 16) + k / 16);
+      t.c0 = buf_load16(m.codes, row * (K / 2) + k / 2);
+    } else {
+      t.sc = buf_load1(m.scales, row * (K / 16) + k / 16);
+      const uint2 v =
+          __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(m.codes, (int)(row * (K / 2) + k / 2), 0, 0));
+      t.c0 = make_uint4(v.x, v.y, 0, 0);
+    }
   } else {
     t.c0 = buf_load16(m.codes, row * K + k);
-    t.c1 = buf_load16(m.codes, row * K + k + 16);
+    if constexpr (TK == 64) t.c1 = buf_load16(m.codes, row * K + k + 16);
   }
 }
 
-template <int FMT>
-__device__ __forceinline__ void b_store(uint16_t *dst, const BTile &t, bool valid) {
-  frag8 f[4];
+// Dequantizes and stores this thread's WK weights (chunks (WK/8)*half + q) of tile row `row`.
+template <int FMT, int TK>
+__device__ __forceinline__ void b_store(uint16_t *rowp, int row, int half, const BTile &t, bool valid) {
+  constexpr int NC = Stage<TK>::WK / 8;
+  frag8 f[NC];
   if constexpr (FMT == MOE_FMT_NVFP4) {
-    const float s0 = e4m3_to_f32(t.sc & 0xFFu), s1 = e4m3_to_f32((t.sc >> 8) & 0xFFu);
+    const float s0 = e4m3_to_f32(t.sc & 0xFFu);
     fp4x8_mul_to_bf16(t.c0.x, s0, f[0]);
     fp4x8_mul_to_bf16(t.c0.y, s0, f[1]);
-    fp4x8_mul_to_bf16(t.c0.z, s1, f[2]);
-    fp4x8_mul_to_bf16(t.c0.w, s1, f[3]);
+    if constexpr (NC == 4) {
+      const float s1 = e4m3_to_f32((t.sc >> 8) & 0xFFu);
+      fp4x8_mul_to_bf16(t.c0.z, s1, f[2]);
+      fp4x8_mul_to_bf16(t.c0.w, s1, f[3]);
+    }
   } else {
     fp8x8_to_bf16(t.c0.x, t.c0.y, f[0]);
     fp8x8_to_bf16(t.c0.z, t.c0.w, f[1]);
-    fp8x8_to_bf16(t.c1.x, t.c1.y, f[2]);
-    fp8x8_to_bf16(t.c1.z, t.c1.w, f[3]);
+    if constexpr (NC == 4) {
+      fp8x8_to_bf16(t.c1.x, t.c1.y, f[2]);
+      fp8x8_to_bf16(t.c1.z, t.c1.w, f[3]);
+    }
   }
-  if (!valid) zero_frags(f);
+  if (!valid)
 #pragma unroll
-  for (int q = 0; q < 4; q++) *reinterpret_cast<uint4 *>(dst + 8 * q) = f[q].q;
+    for (int q = 0; q < NC; q++) f[q].q = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int q = 0; q < NC; q++) *reinterpret_cast<uint4 *>(rowp + swz<TK>(row, NC * half + q)) = f[q].q;
 }
 
 // ---------------------------------------------------------------- the MFMA stage
 
-// acc[i][j] += A rows (a_row0 + 16 i) x weight rows brow[j], over the stage's 64 K.
-__device__ __forceinline__ void mma_stage(const uint16_t (*la)[LDP], const uint16_t (*lb)[LDP], int a_row0,
+// acc[i][j] += A rows (a_row0 + 16 i) x weight rows brow[j], over the stage's K.
+template <int TK>
+__device__ __forceinline__ void mma_stage(const uint16_t (*la)[TK], const uint16_t (*lb)[TK], int a_row0,
                                           const int (&brow)[4], int lane, f32x4_t (&acc)[4][4]) {
   const int r = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int kk = 0; kk < TK; kk += 32) {
     frag8 a[4], b[4];
 #pragma unroll
-    for (int i = 0; i < 4; i++) a[i].q = *reinterpret_cast<const uint4 *>(&la[a_row0 + 16 * i + r][kk + 8 * g]);
+    for (int i = 0; i < 4; i++)
+      a[i].q = *reinterpret_cast<const uint4 *>(&la[a_row0 + 16 * i + r][swz<TK>(r, kk / 8 + g)]);
 #pragma unroll
-    for (int j = 0; j < 4; j++) b[j].q = *reinterpret_cast<const uint4 *>(&lb[brow[j] + r][kk + 8 * g]);
+    for (int j = 0; j < 4; j++) b[j].q = *reinterpret_cast<const uint4 *>(&lb[brow[j] + r][swz<TK>(r, kk / 8 + g)]);
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
@@ -119,17 +167,18 @@ __device__ __forceinline__ void fold_block(f32x4_t (&acc)[4][4], f32x4_t (&part)
     }
 }
 
-// The K loop shared by both GEMMs.  Thread roles: activation pieces (4 rows given by
+// The K loop shared by both GEMMs.  Thread roles: activation chunks (NQ rows given by
 // a_off, byte offsets of the rows' K origin, 0x80000000 for rows that read zeros) and the
 // weight tile row `wrow` of matrix m (half `bhalf` of each stage, zeroed unless wvalid).
 // K runs over [0, nK*TK) relative to the weight column b_k0; weight K halves at or past
 // kvalid load zeros.  FP8: scale(kb, j) gives the weight_scale_inv of col tile j, K block kb.
-template <int FMT, typename ScaleFn>
-__device__ __forceinline__ void tiled_k_loop(TileLDS &lds, rsrc_t ra, const uint32_t (&a_off)[4], const WMat<FMT> &m,
+template <int FMT, int TK, typename ScaleFn>
+__device__ __forceinline__ void tiled_k_loop(TileLDS<TK> &lds, rsrc_t ra, const uint32_t (&a_off)[Stage<TK>::NQ],
+                                             const WMat<FMT> &m,
                                              uint32_t wrow, bool wvalid, int b_k0, int nK, int kvalid,
                                              const int (&brow)[4], ScaleFn scale, f32x4_t (&acc)[4][4]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int seg = lane & 7, brr = tid >> 1, bhalf = tid & 1;
+  const int brr = tid >> 1, bhalf = tid & 1;
   const int a_row0 = (wave >> 1) * 64;
   f32x4_t part[4][4];
   if constexpr (FMT == MOE_FMT_FP8_BLOCK128) {
@@ -138,37 +187,46 @@ __device__ __forceinline__ void tiled_k_loop(TileLDS &lds, rsrc_t ra, const uint
 #pragma unroll
       for (int j = 0; j < 4; j++) part[i][j] = zero4();
   }
-  ATile at;
-  BTile bt;
-  a_fetch(ra, a_off, 0, seg, at);
-  b_fetch<FMT>(m, wrow, b_k0 + 32 * bhalf, bt);
-  a_store(lds.a[0], at, wave, lane);
-  b_store<FMT>(&lds.b[0][brr][32 * bhalf], bt, wvalid && 32 * bhalf < kvalid);
+  // Loads run two stages ahead of the multiply: register set s%2 receives stage s+2 while
+  // stage s multiplies out of LDS buffer s%2 and stage s+1 (in registers since the
+  // previous stage) is stored to LDS buffer (s+1)%2.
+  ATile<TK> at[2];
+  BTile bt[2];
+  auto fetch = [&](int st, ATile<TK> &ta, BTile &tb) {  // weight loads first: oldest in the queue
+    const int kb = st * TK + (TK / 2) * bhalf;
+    b_fetch<FMT, TK>(m, wrow, b_k0 + (kb < kvalid ? kb : 0), tb);
+    a_fetch<TK>(ra, a_off, st * TK, lane, ta);
+  };
+  auto store = [&](int st, const ATile<TK> &ta, const BTile &tb) {
+    a_store<TK>(lds.a[st & 1], ta, wave, lane);
+    b_store<FMT, TK>(lds.b[st & 1][brr], brr, bhalf, tb, wvalid && st * TK + (TK / 2) * bhalf < kvalid);
+  };
+  // Fetches are unconditional (stages past the end reload the last one, unused) so that
+  // every path has the same loads in flight and the compiler's waits stay partial.
+  fetch(0, at[0], bt[0]);
+  fetch(nK > 1 ? 1 : 0, at[1], bt[1]);
+  store(0, at[0], bt[0]);
   __syncthreads();
-  for (int s = 0; s < nK; s++) {
-    const int cur = s & 1;
-    const bool more = s + 1 < nK;
-    const int kn = (s + 1) * TK + 32 * bhalf;  // next stage's weight K (relative)
-    if (more) {
-      a_fetch(ra, a_off, (s + 1) * TK, seg, at);
-      b_fetch<FMT>(m, wrow, b_k0 + (kn < kvalid ? kn : 0), bt);
-    }
+  auto stage = [&](int st, ATile<TK> &ta_free, BTile &tb_free, const ATile<TK> &ta_next, const BTile &tb_next) {
+    fetch(st + 2 < nK ? st + 2 : nK - 1, ta_free, tb_free);
     if constexpr (FMT == MOE_FMT_FP8_BLOCK128) {
-      mma_stage(lds.a[cur], lds.b[cur], a_row0, brow, lane, part);
-      if (s & 1) {
+      mma_stage<TK>(lds.a[st & 1], lds.b[st & 1], a_row0, brow, lane, part);
+      constexpr int SPB = 128 / TK;  // stages per 128-wide scale block
+      if (st % SPB == SPB - 1) {
         float sc[4];
 #pragma unroll
-        for (int j = 0; j < 4; j++) sc[j] = scale(s >> 1, j);
+        for (int j = 0; j < 4; j++) sc[j] = scale(st / SPB, j);
         fold_block(acc, part, sc);
       }
     } else {
-      mma_stage(lds.a[cur], lds.b[cur], a_row0, brow, lane, acc);
+      mma_stage<TK>(lds.a[st & 1], lds.b[st & 1], a_row0, brow, lane, acc);
     }
-    if (more) {
-      a_store(lds.a[cur ^ 1], at, wave, lane);
-      b_store<FMT>(&lds.b[cur ^ 1][brr][32 * bhalf], bt, wvalid && kn < kvalid);
-    }
+    if (st + 1 < nK) store(st + 1, ta_next, tb_next);
     __syncthreads();
+  };
+  for (int st = 0; st < nK; st += 2) {
+    stage(st, at[0], bt[0], at[1], bt[1]);
+    if (st + 1 < nK) stage(st + 1, at[1], bt[1], at[0], bt[0]);
   }
 }
 
@@ -189,7 +247,8 @@ __device__ __forceinline__ void zero_acc(f32x4_t (&acc)[4][4]) {
 // rows 64 wm + [0,64) and the gate/up column pairs c0 + 32 wn + [0,32), so SwiGLU is local.
 template <int FMT>
 __global__ __launch_bounds__(256, 2) void k_gate_up_tiled(GateUpArgs a) {
-  __shared__ TileLDS lds;
+  constexpr int TK = 64;
+  __shared__ TileLDS<TK> lds;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4, wm = wave >> 1, wn = wave & 1;
   const int n_routed = a.cap / TM;
@@ -216,10 +275,10 @@ __global__ __launch_bounds__(256, 2) void k_gate_up_tiled(GateUpArgs a) {
   const int T = a.T, H = a.H, I = a.I, Il = a.Il, P = a.T * a.k;
   const WMat<FMT> m = weight_matrix<FMT>(codes, scales, e, 2 * I, H);
   const rsrc_t ra = make_rsrc(a.x, (uint32_t)T * H * 2);
-  uint32_t a_off[4];
+  uint32_t a_off[Stage<TK>::NQ];
 #pragma unroll
-  for (int q = 0; q < 4; q++) {
-    const int p = p0 + 32 * wave + 8 * q + (lane >> 3);
+  for (int q = 0; q < Stage<TK>::NQ; q++) {
+    const int p = p0 + a_row_of<TK>(wave, lane, q);
     int tok;
     if (!is_shared) {
       const int f = a.sorted_ids[p];
@@ -240,7 +299,7 @@ __global__ __launch_bounds__(256, 2) void k_gate_up_tiled(GateUpArgs a) {
     const int wr = (j < 2 ? 0 : I) + a.lo + c0 + 32 * wn + 16 * (j & 1);
     return buf_load_f32(m.scales, (uint32_t)((wr / 128) * (H / 128) + kb) * 4);
   };
-  tiled_k_loop<FMT>(lds, ra, a_off, m, wrow, wvalid, 0, H / TK, H, brow, scale, acc);
+  tiled_k_loop<FMT, TK>(lds, ra, a_off, m, wrow, wvalid, 0, H / TK, H, brow, scale, acc);
   // epilogue: per-row globals (NVFP4), SwiGLU, h in bf16
   float gg[2], ug[2];
 #pragma unroll
@@ -271,7 +330,8 @@ __global__ __launch_bounds__(256, 2) void k_gate_up_tiled(GateUpArgs a) {
 // K = the slice [lo, hi).  Wave (wm, wn) owns rows 64 wm + [0,64), columns 64 wn + [0,64).
 template <int FMT>
 __global__ __launch_bounds__(256, 2) void k_down_tiled(DownArgs a) {
-  __shared__ TileLDS lds;
+  constexpr int TK = 32;
+  __shared__ TileLDS<TK> lds;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4, wm = wave >> 1, wn = wave & 1;
   const int n_routed = a.cap / TM;
@@ -298,9 +358,9 @@ __global__ __launch_bounds__(256, 2) void k_down_tiled(DownArgs a) {
   const int T = a.T, H = a.H, I = a.I, Il = a.Il, P = a.T * a.k;
   const WMat<FMT> m = weight_matrix<FMT>(codes, scales, e, H, I);
   const rsrc_t ra = make_rsrc(a.h, (uint32_t)a.h_rows * Il * 2);
-  uint32_t a_off[4];
+  uint32_t a_off[Stage<TK>::NQ];
 #pragma unroll
-  for (int q = 0; q < 4; q++) a_off[q] = (uint32_t)(p0 + 32 * wave + 8 * q + (lane >> 3)) * Il * 2;
+  for (int q = 0; q < Stage<TK>::NQ; q++) a_off[q] = (uint32_t)(p0 + a_row_of<TK>(wave, lane, q)) * Il * 2;
   const uint32_t wrow = (uint32_t)(n0 + (tid >> 1));
   const int brow[4] = {64 * wn, 64 * wn + 16, 64 * wn + 32, 64 * wn + 48};
   f32x4_t acc[4][4];
@@ -309,7 +369,7 @@ __global__ __launch_bounds__(256, 2) void k_down_tiled(DownArgs a) {
     const int wr = n0 + 64 * wn + 16 * j;
     return buf_load_f32(m.scales, (uint32_t)((wr / 128) * (I / 128) + a.lo / 128 + kb) * 4);
   };
-  tiled_k_loop<FMT>(lds, ra, a_off, m, wrow, true, a.lo, (Il + TK - 1) / TK, Il, brow, scale, acc);
+  tiled_k_loop<FMT, TK>(lds, ra, a_off, m, wrow, true, a.lo, (Il + TK - 1) / TK, Il, brow, scale, acc);
   float dg[4];
 #pragma unroll
   for (int j = 0; j < 4; j++) dg[j] = FMT == MOE_FMT_NVFP4 ? glob[(size_t)e * H + n0 + 64 * wn + 16 * j + r] : 1.f;
