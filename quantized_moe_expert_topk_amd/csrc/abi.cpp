@@ -189,6 +189,11 @@ int check_forward(const moe_bank *routed, const moe_bank *shared, int T, int k, 
   rc = check_align_out(al, T, k, routed->E);
   if (rc) return rc;
   if ((long long)T * k > (1LL << 30)) return fail(MOE_ERR_UNSUPPORTED, "T*k too large");
+  // kernels address x, the intermediate and each expert's matrices with 32-bit offsets
+  const long long Il = hi - lo, rows = (long long)al->capacity + 128LL * ((T + 127) / 128);
+  if ((long long)T * routed->H * 2 >= (1LL << 31) || rows * Il * 2 >= (1LL << 31) ||
+      2LL * routed->I * routed->H >= (1LL << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "tensor exceeds 2 GiB (32-bit buffer offsets)");
   *plan = plan_forward(routed, shared, T, k, al->capacity, lo, hi);
   plan->tiled = al->block_m % 128 == 0 && routed->fmt != MOE_FMT_MXFP4_E8M0;
   if (workspace_bytes < plan->total)
@@ -342,6 +347,8 @@ int moe_route(const void *x_bf16, int T, int H, const void *w_router_bf16, int E
   if (E > 1024 || k > 64) return fail(MOE_ERR_UNSUPPORTED, "moe_route: needs E <= 1024 and k <= 64");
   if (H % 128) return fail(MOE_ERR_UNSUPPORTED, "moe_route: H=%d must be a multiple of 128", H);
   if (T > 16 * 65535) return fail(MOE_ERR_UNSUPPORTED, "moe_route: T=%d too large", T);
+  if ((long long)T * H * 2 >= (1LL << 31) || (long long)E * H * 2 >= (1LL << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_route: x or the router weight exceeds 2 GiB (32-bit buffer offsets)");
   const size_t need = moe_route_workspace_bytes(T, H, E);
   if (workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "moe_route: workspace %zu < %zu", workspace_bytes, need);
   if (need && !workspace) return fail(MOE_ERR_INVALID_ARG, "moe_route: workspace is NULL");

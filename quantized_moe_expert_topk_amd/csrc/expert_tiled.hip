@@ -79,10 +79,13 @@ __device__ __forceinline__ void a_store(uint16_t (*la)[TK], const ATile<TK> &t, 
   }
 }
 
+// Plain bf16 weights (the router): no scales, no dequantization.
+constexpr int kFmtBf16 = 0;
+
 // Weight tile: a thread owns tile row tid/2 and the K half tid%2 of the stage (WK weights).
 struct BTile {
-  uint4 c0, c1;  // codes: WK/2 bytes (FP4) or WK bytes (FP8)
-  uint32_t sc;   // NVFP4: the e4m3 scales of the WK/16 groups
+  uint4 c0, c1, c2, c3;  // codes: WK/2 bytes (FP4), WK bytes (FP8) or 2*WK bytes (bf16)
+  uint32_t sc;           // NVFP4: the e4m3 scales of the WK/16 groups
 };
 
 template <int FMT, int TK>
@@ -97,6 +100,14 @@ __device__ __forceinline__ void b_fetch(const WMat<FMT> &m, uint32_t row, int k,
       const uint2 v =
           __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(m.codes, (int)(row * (K / 2) + k / 2), 0, 0));
       t.c0 = make_uint4(v.x, v.y, 0, 0);
+    }
+  } else if constexpr (FMT == kFmtBf16) {
+    const uint32_t o = (row * K + k) * 2;
+    t.c0 = buf_load16(m.codes, o);
+    t.c1 = buf_load16(m.codes, o + 16);
+    if constexpr (TK == 64) {
+      t.c2 = buf_load16(m.codes, o + 32);
+      t.c3 = buf_load16(m.codes, o + 48);
     }
   } else {
     t.c0 = buf_load16(m.codes, row * K + k);
@@ -117,6 +128,13 @@ __device__ __forceinline__ void b_store(uint16_t *rowp, int row, int half, const
       const float s1 = e4m3_to_f32((t.sc >> 8) & 0xFFu);
       fp4x8_mul_to_bf16(t.c0.z, s1, f[2]);
       fp4x8_mul_to_bf16(t.c0.w, s1, f[3]);
+    }
+  } else if constexpr (FMT == kFmtBf16) {
+    f[0].q = t.c0;
+    f[1].q = t.c1;
+    if constexpr (NC == 4) {
+      f[2].q = t.c2;
+      f[3].q = t.c3;
     }
   } else {
     fp8x8_to_bf16(t.c0.x, t.c0.y, f[0]);
@@ -394,7 +412,65 @@ __global__ __launch_bounds__(256, 2) void k_down_tiled(DownArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- router
+
+// logits (or split-K partials) of many tokens: tile (blockIdx.x, blockIdx.y, blockIdx.z) =
+// tokens [t0, t0 + 128) x experts [e0, e0 + 128) over K = [kbeg, kbeg + kchunk) of H; wave
+// (wm, wn) owns tokens 64 wm + [0,64) and experts 64 wn + [0,64).  The bias is added here
+// only without a K split (the top-k kernel adds it after summing the partials otherwise).
+__global__ __launch_bounds__(256, 2) void k_router_tiled(const uint16_t *__restrict__ x, int T, int H,
+                                                         const uint16_t *__restrict__ w, int E,
+                                                         const float *__restrict__ bias, int kchunk,
+                                                         float *__restrict__ part) {
+  constexpr int TK = 64;
+  __shared__ TileLDS<TK> lds;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4, wm = wave >> 1, wn = wave & 1;
+  const int t0 = blockIdx.x * TM, e0 = blockIdx.y * TW, kbeg = blockIdx.z * kchunk;
+  const rsrc_t ra = make_rsrc(x, (uint32_t)T * H * 2);
+  uint32_t a_off[Stage<TK>::NQ];
+#pragma unroll
+  for (int q = 0; q < Stage<TK>::NQ; q++) {
+    const int t = t0 + a_row_of<TK>(wave, lane, q);
+    a_off[q] = t < T ? (uint32_t)(t * H + kbeg) * 2 : 0x80000000u;
+  }
+  WMat<kFmtBf16> m;
+  m.codes = m.scales = make_rsrc(w, (uint32_t)E * H * 2);
+  m.K = H;
+  const int ew = e0 + (tid >> 1);
+  const bool wvalid = ew < E;
+  const int brow[4] = {64 * wn, 64 * wn + 16, 64 * wn + 32, 64 * wn + 48};
+  f32x4_t acc[4][4];
+  zero_acc(acc);
+  auto noscale = [](int, int) { return 1.f; };
+  tiled_k_loop<kFmtBf16, TK>(lds, ra, a_off, m, (uint32_t)(wvalid ? ew : 0), wvalid, kbeg, kchunk / TK, kchunk, brow,
+                             noscale, acc);
+  float* dst = part + (size_t)blockIdx.z * T * E;
+  const bool add_bias = bias && gridDim.z == 1;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int e = e0 + 64 * wn + 16 * j + r;
+    if (e >= E) continue;
+    const float bv = add_bias ? bias[e] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) {
+        const int t = t0 + 64 * wm + 16 * i + 4 * g + jj;
+        if (t < T) dst[(size_t)t * E + e] = acc[i][j][jj] + bv;
+      }
+  }
+}
+
 // ---------------------------------------------------------------- launchers
+
+hipError_t launch_router_tiled(const uint16_t *x, int T, int H, const uint16_t *w, int E, const float *bias, int ks,
+                               float *part, hipStream_t s) {
+  const dim3 grid((T + TM - 1) / TM, (E + TW - 1) / TW, ks);
+  hipLaunchKernelGGL(k_router_tiled, grid, dim3(256), 0, s, x, T, H, w, E, bias, H / ks, part);
+  return hipGetLastError();
+}
+
 
 hipError_t launch_gate_up_tiled(int fmt, const GateUpArgs &a, int n_shared_tiles, hipStream_t s) {
   const dim3 grid(a.cap / TM + n_shared_tiles, (a.Il + 63) / 64);

@@ -50,6 +50,8 @@ size_t router_workspace_bytes(int T, int E, int H);
 hipError_t launch_route(const uint16_t *x, int T, int H, const uint16_t *w, int E, const float *bias, int k,
                         int renormalize, float *logits, int32_t *ids, float *wts, float *partial,
                         hipStream_t s);
+hipError_t launch_router_tiled(const uint16_t *x, int T, int H, const uint16_t *w, int E, const float *bias, int ks,
+                               float *part, hipStream_t s);
 hipError_t launch_topk(const float *logits, int T, int E, const float *bias, int k, int renormalize,
                        int32_t *ids, float *wts, hipStream_t s);
 hipError_t launch_align(const int32_t *ids, int T, int k, int E, int BM, int cap, int32_t *sorted_ids,

@@ -215,7 +215,18 @@ static hipError_t launch_topk_ns(const float *part, int KS, int T, int E, const 
 }
 
 // K splits for the router GEMM: enough workgroups to cover the chip at small T.
+// Large batches run the router on the LDS-tiled GEMM (128 tokens x 128 experts per
+// workgroup), small ones on k_router_partial; both split K until about 512 (tiled) or 128
+// workgroups are in flight.
+static bool router_tiled(int T) { return T >= 1024; }
+
 int router_ksplit(int T, int E, int H) {
+  if (router_tiled(T)) {  // K ranges stay whole 64-wide stages
+    const int base = ((T + 127) / 128) * ((E + 127) / 128);
+    int ks = 1;
+    while (base * ks < 512 && ks < 8 && (H / 64) % (ks * 2) == 0) ks *= 2;
+    return ks;
+  }
   const int base = ((E + 63) / 64) * ((T + 15) / 16);
   int ks = 1;
   while (base * ks < 128 && ks < 16 && ks * 2 <= H / 128 && (H / 128) % (ks * 2) == 0) ks *= 2;
@@ -232,9 +243,14 @@ hipError_t launch_route(const uint16_t *x, int T, int H, const uint16_t *w, int 
                         hipStream_t s) {
   const int ks = router_ksplit(T, E, H);
   float *part = ks > 1 ? partial : logits;
-  dim3 grid((E + 63) / 64, (T + 15) / 16, ks);
-  hipLaunchKernelGGL(k_router_partial, grid, dim3(256), 0, s, x, T, H, w, E, bias, H / ks, part);
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  if (router_tiled(T)) {
+    e = launch_router_tiled(x, T, H, w, E, bias, ks, part, s);
+  } else {
+    dim3 grid((E + 63) / 64, (T + 15) / 16, ks);
+    hipLaunchKernelGGL(k_router_partial, grid, dim3(256), 0, s, x, T, H, w, E, bias, H / ks, part);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return e;
   // with one split the GEMM already added the bias and wrote the logits in place
   return launch_topk_ns(part, ks, T, E, ks > 1 ? bias : nullptr, k, renormalize, ks > 1 ? logits : nullptr, ids, wts,

@@ -90,6 +90,23 @@ def test_route_matches_oracle(cid, T):
         assert (lg_ref[t][ids_g[t]] >= kth - 2 * NEAR_TIE).all()
 
 
+@pytest.mark.parametrize("T,E,H,k,with_bias", [(1500, 200, 1024, 6, True), (1024, 256, 4096, 8, False),
+                                               (2077, 64, 384, 4, False)])
+def test_tiled_router_shapes_match_oracle(T, E, H, k, with_bias):
+    """Batches of 1024 tokens and more run the router on the LDS-tiled GEMM (split over
+    K): ragged token and expert tiles, with and without a bias."""
+    x = S.tokens(3, T, H)
+    wr = S.router_weight(3, E, H)
+    bias = S.zipf_bias(3, E, 1.1) if with_bias else None
+    lg_ref, ids_ref, w_ref, gap = O.route(x, wr, bias, k, True)
+    lg, ids, w = qm.moe_route(bf16_dev(x), bf16_dev(wr), to_dev(bias), k, True)
+    lerr = np.abs(lg.cpu().numpy() - lg_ref).max()
+    assert lerr <= 5e-6, lerr
+    sure = gap > NEAR_TIE
+    np.testing.assert_array_equal(ids.cpu().numpy()[sure], ids_ref[sure])
+    assert np.abs(w.cpu().numpy()[sure] - w_ref[sure]).max() <= 1e-5
+
+
 def test_route_is_deterministic():
     cfg = S.CONFIGS[3]
     x = bf16_dev(S.tokens(cfg.seed, 4096, cfg.H))
