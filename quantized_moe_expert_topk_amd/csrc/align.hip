@@ -5,9 +5,10 @@
 //
 // Three passes over chunks of 1024 pairs, none of them ordered by atomics, so the result
 // is deterministic:
-//   1. k_align_hist    per-chunk expert histograms            -> hist[chunk][E]
+//   1. k_align_hist    per-chunk expert histograms -> hist[chunk][E]; also fills every slot
+//                      of sorted_ids with the sentinel (pass 3 overwrites the pairs' slots)
 //   2. k_align_scan    per-expert exclusive prefix over chunks (in place), counts, padded
-//                      offsets, block_expert, and the sentinel in every padding slot
+//                      offsets and block_expert
 //   3. k_align_scatter stable rank of each pair inside its chunk (ballot match masks per
 //                      64-pair row, prefix over the 16 rows of the chunk) -> sorted_ids
 #include "device_common.h"
@@ -18,9 +19,11 @@ namespace qmoe {
 constexpr int kChunk = 1024;  // pairs per chunk = 16 rows of 64
 
 __global__ __launch_bounds__(256) void k_align_hist(const int32_t *__restrict__ ids, int P, int E,
-                                                    int32_t *__restrict__ hist) {
+                                                    int32_t *__restrict__ hist, int nchunk, int cap,
+                                                    int32_t *__restrict__ sorted_ids) {
   extern __shared__ int32_t cnt[];  // [E]
   for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+  for (int p = blockIdx.x * blockDim.x + threadIdx.x; p < cap; p += gridDim.x * blockDim.x) sorted_ids[p] = P;
   __syncthreads();
   const int base = blockIdx.x * kChunk;
   for (int i = threadIdx.x; i < kChunk; i += blockDim.x) {
@@ -31,25 +34,31 @@ __global__ __launch_bounds__(256) void k_align_hist(const int32_t *__restrict__ 
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(size_t)blockIdx.x * E + e] = cnt[e];
+  if ((int)blockIdx.x < nchunk)
+    for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(size_t)blockIdx.x * E + e] = cnt[e];
 }
 
 // One workgroup of 1024 threads.  Thread e owns expert e (E <= 1024).
 __global__ __launch_bounds__(1024) void k_align_scan(int32_t *__restrict__ hist, int nchunk, int E, int BM,
-                                                     int P, int cap, int32_t *__restrict__ sorted_ids,
-                                                     int32_t *__restrict__ block_expert,
+                                                     int P, int cap, int32_t *__restrict__ block_expert,
                                                      int32_t *__restrict__ counts,
                                                      int32_t *__restrict__ offsets,
                                                      int32_t *__restrict__ total_padded) {
-  __shared__ int32_t scan[1024];
+  __shared__ int32_t start_of[1025];  // padded start of expert e; start_of[E] = total
   __shared__ int32_t wsum[16];
   const int e = threadIdx.x;
   int run = 0;
   if (e < E) {
-    for (int c = 0; c < nchunk; c++) {
-      const int v = hist[(size_t)c * E + e];
-      hist[(size_t)c * E + e] = run;  // exclusive prefix: where chunk c's pairs of e start
-      run += v;
+    // exclusive prefix over chunks, 8 independent loads at a time
+    for (int c0 = 0; c0 < nchunk; c0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; u++) v[u] = c0 + u < nchunk ? hist[(size_t)(c0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        if (c0 + u < nchunk) hist[(size_t)(c0 + u) * E + e] = run;  // where chunk c's pairs of e start
+        run += v[u];
+      }
     }
     counts[e] = run;
   }
@@ -67,21 +76,33 @@ __global__ __launch_bounds__(1024) void k_align_scan(int32_t *__restrict__ hist,
   int wbase = 0;
   for (int w = 0; w < wave; w++) wbase += wsum[w];
   const int start = wbase + inc - padded;
-  scan[threadIdx.x] = start;
-  __syncthreads();
   int total = 0;
   for (int w = 0; w < 16; w++) total += wsum[w];
   if (e < E) {
     offsets[e] = start;
-    for (int b = start / BM; b < (start + padded) / BM; b++) block_expert[b] = e;
-    for (int p = start + run; p < start + padded; p++) sorted_ids[p] = P;  // padding slots
+    start_of[e] = start;
   }
   if (e == 0) {
     offsets[E] = total;
     total_padded[0] = total;
+    start_of[E] = total;
   }
-  for (int b = total / BM + threadIdx.x; b < cap / BM; b += blockDim.x) block_expert[b] = -1;
-  for (int p = total + threadIdx.x; p < cap; p += blockDim.x) sorted_ids[p] = P;
+  __syncthreads();
+  // block b belongs to the last expert whose padded start is <= b*BM (starts ascend; an
+  // empty expert shares its start with the next one), or to none past the total
+  for (int b = threadIdx.x; b < cap / BM; b += blockDim.x) {
+    const int p = b * BM;
+    int owner = -1;
+    if (p < total) {
+      int lo = 0, hi = E - 1;  // largest e with start_of[e] <= p
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (start_of[mid] <= p) lo = mid; else hi = mid - 1;
+      }
+      owner = lo;
+    }
+    block_expert[b] = owner;
+  }
 }
 
 // One workgroup (256 threads = 4 waves) per chunk; wave w handles rows 4w..4w+3 of 64 pairs.
@@ -216,11 +237,11 @@ hipError_t launch_align(const int32_t *ids, int T, int k, int E, int BM, int cap
     return hipGetLastError();
   }
   const int nchunk = (P + kChunk - 1) / kChunk;
-  if (nchunk > 0) {
-    hipLaunchKernelGGL(k_align_hist, dim3(nchunk), dim3(256), E * sizeof(int32_t), s, ids, P, E, hist);
-  }
-  hipLaunchKernelGGL(k_align_scan, dim3(1), dim3(1024), 0, s, hist, nchunk, E, BM, P, cap, sorted_ids,
-                     block_expert, counts, offsets, total_padded);
+  // at least one workgroup, which also writes the sentinels when there are no pairs
+  hipLaunchKernelGGL(k_align_hist, dim3(nchunk > 0 ? nchunk : 1), dim3(256), E * sizeof(int32_t), s, ids, P, E,
+                     hist, nchunk, cap, sorted_ids);
+  hipLaunchKernelGGL(k_align_scan, dim3(1), dim3(1024), 0, s, hist, nchunk, E, BM, P, cap, block_expert, counts,
+                     offsets, total_padded);
   if (nchunk > 0) {
     hipLaunchKernelGGL(k_align_scatter, dim3(nchunk), dim3(256), 16 * E * sizeof(int32_t), s, ids, P, E,
                        hist, offsets, sorted_ids);

@@ -123,6 +123,7 @@ def test_route_is_deterministic():
     (16, 2, 8, 16, "rand"), (1, 8, 256, 16, "rand"), (64, 8, 256, 16, "rand"), (8192, 8, 256, 64, "rand"),
     (4096, 8, 256, 32, "rand"), (130, 8, 1000, 16, "rand"), (3000, 4, 7, 128, "rand"), (1, 1, 1, 16, "rand"),
     (500, 8, 256, 16, "one_expert"), (257, 3, 256, 256, "two_experts"), (8192, 8, 256, 16, "zipf"),
+    (8192, 8, 256, 128, "zipf"), (100, 2, 600, 128, "rand"), (4096, 8, 256, 128, "one_expert"),
 ])
 def test_align_is_bit_exact(T, k, E, bm, kind):
     if kind == "rand":
