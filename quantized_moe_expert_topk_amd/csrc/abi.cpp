@@ -289,7 +289,8 @@ int run_down(const moe_bank *routed, const moe_bank *shared, int T, int k, const
   int rc = p.tiled ? hip_status(qmoe::launch_down_tiled(routed->fmt, a, p.n_shared_tiles, s), "down launch")
                    : hip_status(qmoe::launch_down(routed->fmt, a, p.n_shared_sub, s), "down launch");
   if (rc) return rc;
-  return hip_status(qmoe::launch_combine(a.Y, T, k, routed->H, shared != nullptr, out, out_dtype == MOE_OUT_BF16, s),
+  return hip_status(qmoe::launch_combine(a.Y, p.tiled, T, k, routed->H, shared != nullptr, out,
+                                         out_dtype == MOE_OUT_BF16, s),
                     "combine launch");
 }
 

@@ -521,34 +521,44 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
 
 // ---------------------------------------------------------------------------- combine
 
-__global__ __launch_bounds__(256) void k_combine(const float *__restrict__ Y, int T, int k, int H, int has_shared,
+// out[t] = sum_j Y[t*k + j] + Y[T*k + t] (shared), in this order, in fp32.  Y rows are fp32
+// (streaming kernels) or bf16 (tiled kernels); a thread owns 8 consecutive columns.
+template <bool YBF16>
+__global__ __launch_bounds__(256) void k_combine(const void *__restrict__ Yv, int T, int k, int H, int has_shared,
                                                  void *__restrict__ out, int out_bf16) {
   const int t = blockIdx.y;
-  const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
+  const int n = (blockIdx.x * 256 + threadIdx.x) * 8;
   if (n >= H) return;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; j++) {
-    const float4 v = *reinterpret_cast<const float4 *>(Y + (size_t)(t * k + j) * H + n);
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
-  }
-  if (has_shared) {
-    const float4 v = *reinterpret_cast<const float4 *>(Y + (size_t)(T * k + t) * H + n);
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
-  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto add_row = [&](size_t row) {
+    if constexpr (YBF16) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(Yv) + row * H + n);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        acc[2 * q] += __uint_as_float(w[q] << 16);
+        acc[2 * q + 1] += __uint_as_float(w[q] & 0xFFFF0000u);
+      }
+    } else {
+      const float *y = reinterpret_cast<const float *>(Yv) + row * H + n;
+      const float4 v0 = *reinterpret_cast<const float4 *>(y), v1 = *reinterpret_cast<const float4 *>(y + 4);
+      acc[0] += v0.x; acc[1] += v0.y; acc[2] += v0.z; acc[3] += v0.w;
+      acc[4] += v1.x; acc[5] += v1.y; acc[6] += v1.z; acc[7] += v1.w;
+    }
+  };
+  for (int j = 0; j < k; j++) add_row((size_t)t * k + j);
+  if (has_shared) add_row((size_t)T * k + t);
   if (out_bf16) {
-    uint16_t *o = reinterpret_cast<uint16_t *>(out) + (size_t)t * H + n;
-    uint2 pk;
-    pk.x = (uint32_t)bf16_bits(acc.x) | ((uint32_t)bf16_bits(acc.y) << 16);
-    pk.y = (uint32_t)bf16_bits(acc.z) | ((uint32_t)bf16_bits(acc.w) << 16);
-    *reinterpret_cast<uint2 *>(o) = pk;
+    uint4 pk;
+    pk.x = (uint32_t)bf16_bits(acc[0]) | ((uint32_t)bf16_bits(acc[1]) << 16);
+    pk.y = (uint32_t)bf16_bits(acc[2]) | ((uint32_t)bf16_bits(acc[3]) << 16);
+    pk.z = (uint32_t)bf16_bits(acc[4]) | ((uint32_t)bf16_bits(acc[5]) << 16);
+    pk.w = (uint32_t)bf16_bits(acc[6]) | ((uint32_t)bf16_bits(acc[7]) << 16);
+    *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out) + (size_t)t * H + n) = pk;
   } else {
-    *reinterpret_cast<float4 *>(reinterpret_cast<float *>(out) + (size_t)t * H + n) = acc;
+    float *o = reinterpret_cast<float *>(out) + (size_t)t * H + n;
+    *reinterpret_cast<float4 *>(o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    *reinterpret_cast<float4 *>(o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
   }
 }
 
@@ -613,10 +623,13 @@ hipError_t launch_act_mx8(const uint16_t *x, int rows, int K, uint8_t *q, uint8_
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const float *Y, int T, int k, int H, int has_shared, void *out, int out_bf16,
+hipError_t launch_combine(const void *Y, bool y_bf16, int T, int k, int H, int has_shared, void *out, int out_bf16,
                           hipStream_t s) {
-  dim3 grid((H / 4 + 255) / 256, T);
-  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, s, Y, T, k, H, has_shared, out, out_bf16);
+  dim3 grid((H / 8 + 255) / 256, T);
+  if (y_bf16)
+    hipLaunchKernelGGL(k_combine<true>, grid, dim3(256), 0, s, Y, T, k, H, has_shared, out, out_bf16);
+  else
+    hipLaunchKernelGGL(k_combine<false>, grid, dim3(256), 0, s, Y, T, k, H, has_shared, out, out_bf16);
   return hipGetLastError();
 }
 

@@ -346,6 +346,8 @@ __global__ __launch_bounds__(256, 2) void k_gate_up_tiled(GateUpArgs a) {
 
 // Tile (blockIdx.x, blockIdx.y): h rows [p0, p0 + 128) and hidden columns [n0, n0 + 128);
 // K = the slice [lo, hi).  Wave (wm, wn) owns rows 64 wm + [0,64), columns 64 wn + [0,64).
+// The weighted per-pair rows go to Y in bf16: at prefill sizes Y is the largest stream of
+// the layer (pairs x H), and the combine sums its rows in fp32.
 template <int FMT>
 __global__ __launch_bounds__(256, 2) void k_down_tiled(DownArgs a) {
   constexpr int TK = 32;
@@ -407,8 +409,9 @@ __global__ __launch_bounds__(256, 2) void k_down_tiled(DownArgs a) {
         wgt = 1.f;
       }
       if (dst < 0) continue;
+      uint16_t *yrow = reinterpret_cast<uint16_t *>(a.Y) + (size_t)dst * H + n0 + 64 * wn + r;
 #pragma unroll
-      for (int j = 0; j < 4; j++) a.Y[(size_t)dst * H + n0 + 64 * wn + 16 * j + r] = wgt * acc[i][j][jj] * dg[j];
+      for (int j = 0; j < 4; j++) yrow[16 * j] = bf16_bits(wgt * acc[i][j][jj] * dg[j]);
     }
 }
 

@@ -42,7 +42,7 @@ struct DownArgs {
   int block_m, cap, n_routed_sub;
   int lo, Il;
   const float *topk_w;  // [T * k]
-  float *Y;             // [T * k + T_shared, H]
+  float *Y;             // [T * k + T_shared, H] fp32 (streaming kernels) or bf16 (tiled kernels)
 };
 
 int router_ksplit(int T, int E, int H);
@@ -64,7 +64,8 @@ hipError_t launch_down(int fmt, const DownArgs &a, int n_shared_sub, hipStream_t
 hipError_t launch_gate_up_tiled(int fmt, const GateUpArgs &a, int n_shared_tiles, hipStream_t s);
 hipError_t launch_down_tiled(int fmt, const DownArgs &a, int n_shared_tiles, hipStream_t s);
 hipError_t launch_act_mx8(const uint16_t *x, int rows, int K, uint8_t *q, uint8_t *sc, hipStream_t s);
-hipError_t launch_combine(const float *Y, int T, int k, int H, int has_shared, void *out, int out_bf16,
+// Y rows in fp32 (streaming kernels) or bf16 (tiled kernels).
+hipError_t launch_combine(const void *Y, bool y_bf16, int T, int k, int H, int has_shared, void *out, int out_bf16,
                           hipStream_t s);
 
 }  // namespace qmoe
