@@ -135,25 +135,45 @@ __device__ __forceinline__ uint32_t span_scales(const uint4 &sp, int s, int g) {
 //   ra, a_row: activation buffer and the byte offset of this lane's row; a row past the
 //              buffer end reads as zeros without a memory request (padding rows)
 //   m, rows:   weight matrix and this lane's row of each tile;  b_k0: K offset in the row
+//   lsc:       if not null, this wave's LDS region of NT*16 rows x RB bytes: the run's
+//              FP4 scale bytes are fetched with one row per lane (RB = 128*COUNT/sdiv bytes,
+//              wide loads issued before the first group's weight loads), staged there and
+//              read back per lane, instead of every lane group loading its rows' spans
 template <int FMT, int NT, int COUNT>
 __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FMT> &m, const uint32_t (&rows)[NT],
-                                        int b_k0, int kw0, int kvalid, int g, f32x4_t (&acc)[NT]) {
+                                        int b_k0, int kw0, int kvalid, int g, f32x4_t (&acc)[NT],
+                                        uint8_t *lsc = nullptr) {
   constexpr bool FP4 = FMT != MOE_FMT_FP8_BLOCK128;
   constexpr int NPF = FP4 ? 2 : 1;
   const uint32_t K = (uint32_t)m.K;
   const int sdiv = FMT == MOE_FMT_NVFP4 ? 16 : 32;
+  const int lane = lane_id(), r = lane & 15;
   // spans are dword aligned when the row pitch and the run start are (uniform)
   const bool sal = ((K / sdiv) % 4 == 0) && (((b_k0 + kw0) / sdiv) % 4 == 0);
+  constexpr int RB = FP4 ? 128 * COUNT / (FMT == MOE_FMT_NVFP4 ? 16 : 32) : 16;  // staged bytes per row
+  constexpr int SQ = RB / 16;
+  uint4 stg[SQ > 0 ? SQ : 1];
+  if constexpr (FP4 && SQ > 0) {
+    if (lsc) {  // lane l fetches row l of the NT*16 tile rows (NT*16 == 64 lanes)
+      const uint32_t row = rows[(lane >> 4) % NT];
+#pragma unroll
+      for (int q = 0; q < SQ; q++) stg[q] = buf_load16(m.scales, row * (K / sdiv) + (b_k0 + kw0) / sdiv + 16 * q);
+    }
+  }
 #pragma unroll
   for (int i0 = 0; i0 < COUNT; i0 += NPF) {
     ARaw ar[NPF];
     uint4 c0[NPF][NT], c1[NPF][NT];
     uint4 sp[NT];
+    uint32_t lsv[NPF][NT];
     float bs[NPF][NT];
     if constexpr (FP4) {
       const int kg = kw0 + (128 * i0 < kvalid ? 128 * i0 : 0);
+      if (!lsc) {
 #pragma unroll
-      for (int t = 0; t < NT; t++) sp[t] = load_scale_span<FMT>(m.scales, rows[t] * (K / sdiv) + (b_k0 + kg) / sdiv, sal);
+        for (int t = 0; t < NT; t++)
+          sp[t] = load_scale_span<FMT>(m.scales, rows[t] * (K / sdiv) + (b_k0 + kg) / sdiv, sal);
+      }
     }
 #pragma unroll
     for (int ii = 0; ii < NPF; ii++) {
@@ -175,6 +195,29 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
         }
       }
     }
+    if constexpr (FP4) {
+      if (lsc) {  // scale bytes from the wave's LDS region (staged once per run)
+        if constexpr (SQ > 0) {
+          if (i0 == 0) {  // the first group's weight loads are in flight by now
+#pragma unroll
+            for (int q = 0; q < SQ; q++) *reinterpret_cast<uint4 *>(lsc + lane * RB + 16 * q) = stg[q];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          }
+        }
+#pragma unroll
+        for (int ii = 0; ii < NPF; ii++) {
+          const int kr = 128 * (i0 + ii) + 32 * g;
+          const int kb = (kr < kvalid ? kr : 0) / sdiv;  // this lane's first scale byte in the run
+#pragma unroll
+          for (int t = 0; t < NT; t++) {
+            const uint8_t *p = lsc + (16 * t + r) * RB + kb;
+            lsv[ii][t] = FMT == MOE_FMT_NVFP4 ? (uint32_t)*reinterpret_cast<const uint16_t *>(p) : (uint32_t)*p;
+          }
+        }
+      }
+    }
 #pragma unroll
     for (int ii = 0; ii < NPF; ii++) {
       const int i = i0 + ii;
@@ -187,10 +230,10 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
       for (int t = 0; t < NT; t++) {
         frag8 bv[4];
         if constexpr (FMT == MOE_FMT_NVFP4) {
-          const uint32_t sc = span_scales<FMT>(sp[t], ii, g);
+          const uint32_t sc = lsc ? lsv[ii][t] : span_scales<FMT>(sp[t], ii, g);
           decode_nvfp4(c0[ii][t], sc & 0xFFu, (sc >> 8) & 0xFFu, bv);
         } else if constexpr (FMT == MOE_FMT_MXFP4_E8M0) {
-          decode_mxfp4(c0[ii][t], span_scales<FMT>(sp[t], ii, g) & 0xFFu, bv);
+          decode_mxfp4(c0[ii][t], (lsc ? lsv[ii][t] : span_scales<FMT>(sp[t], ii, g)) & 0xFFu, bv);
         } else {
           fp8x8_to_bf16(c0[ii][t].x, c0[ii][t].y, bv[0]);
           fp8x8_to_bf16(c0[ii][t].z, c0[ii][t].w, bv[1]);
@@ -229,12 +272,25 @@ struct ActMX {
 // zeros and their scales by 1, so stale workspace bytes never reach the MFMA.
 //   a_q, a_s: byte offsets of this lane's row in the planes and in the scales (or
 //             0x80000000 for a padding row, which reads zeros without a memory request)
+//   lsc: as in mma_run (this wave's LDS region for the run's staged scale bytes, or null)
 template <int NT, int COUNT>
 __device__ __forceinline__ void mma_run_mx(const ActMX &A, uint32_t a_q, uint32_t a_s,
                                            const WMat<MOE_FMT_MXFP4_E8M0> &m, const uint32_t (&rows)[NT],
-                                           int b_k0, int kw0, int kvalid, int g, f32x4_t (&acc)[NT]) {
+                                           int b_k0, int kw0, int kvalid, int g, f32x4_t (&acc)[NT],
+                                           uint8_t *lsc = nullptr) {
   constexpr int FMT = MOE_FMT_MXFP4_E8M0;
   const uint32_t K = (uint32_t)m.K;
+  const int lane = lane_id(), r = lane & 15;
+  constexpr int RB = 4 * COUNT;  // staged scale bytes per row (one e8m0 per 32 K)
+  constexpr int SQ = RB / 16;
+  uint4 stg[SQ > 0 ? SQ : 1];
+  if constexpr (SQ > 0) {
+    if (lsc) {
+      const uint32_t row = rows[(lane >> 4) % NT];
+#pragma unroll
+      for (int q = 0; q < SQ; q++) stg[q] = buf_load16(m.scales, row * (K / 32) + (b_k0 + kw0) / 32 + 16 * q);
+    }
+  }
   const bool bsal = ((K / 32) % 4 == 0) && (((b_k0 + kw0) / 32) % 4 == 0);
   const bool asal = ((A.K / 32) % 4 == 0) && ((kw0 / 32) % 4 == 0);
   const uint4 z = make_uint4(0, 0, 0, 0);
@@ -242,8 +298,11 @@ __device__ __forceinline__ void mma_run_mx(const ActMX &A, uint32_t a_q, uint32_
   for (int i0 = 0; i0 < COUNT; i0 += 2) {
     const int kg = kw0 + (128 * i0 < kvalid ? 128 * i0 : 0);
     uint4 bsp[NT];
+    uint32_t lsv[2][NT];
+    if (!lsc) {
 #pragma unroll
-    for (int t = 0; t < NT; t++) bsp[t] = load_scale_span<FMT>(m.scales, rows[t] * (K / 32) + (b_k0 + kg) / 32, bsal);
+      for (int t = 0; t < NT; t++) bsp[t] = load_scale_span<FMT>(m.scales, rows[t] * (K / 32) + (b_k0 + kg) / 32, bsal);
+    }
     const uint4 ash = load_scale_span<FMT>(A.s, a_s + kg / 32, asal);
     const uint4 asl = load_scale_span<FMT>(A.s, A.splane + a_s + kg / 32, asal);
     uint4 ah[2][2], al[2][2], c[2][NT];
@@ -261,6 +320,24 @@ __device__ __forceinline__ void mma_run_mx(const ActMX &A, uint32_t a_q, uint32_
 #pragma unroll
       for (int t = 0; t < NT; t++) c[ii][t] = buf_load16(m.codes, rows[t] * (K / 2) + (b_k0 + k) / 2);
     }
+    if (lsc) {  // B scale bytes from the wave's LDS region (staged once per run)
+      if constexpr (SQ > 0) {
+        if (i0 == 0) {
+#pragma unroll
+          for (int q = 0; q < SQ; q++) *reinterpret_cast<uint4 *>(lsc + lane * RB + 16 * q) = stg[q];
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+      }
+#pragma unroll
+      for (int ii = 0; ii < 2; ii++) {
+        const int kr = 128 * (i0 + ii) + 32 * g;
+        const int kb = (kr < kvalid ? kr : 0) / 32;
+#pragma unroll
+        for (int t = 0; t < NT; t++) lsv[ii][t] = lsc[(16 * t + r) * RB + kb];
+      }
+    }
 #pragma unroll
     for (int ii = 0; ii < 2; ii++) {
       const int i = i0 + ii;
@@ -275,7 +352,7 @@ __device__ __forceinline__ void mma_run_mx(const ActMX &A, uint32_t a_q, uint32_
 #pragma unroll
       for (int t = 0; t < NT; t++) {
         const uint4 cb = vb ? c[ii][t] : z;
-        const uint32_t sb = vb ? (span_scales<FMT>(bsp[t], ii, g) & 0xFFu) : 127u;
+        const uint32_t sb = vb ? ((lsc ? lsv[ii][t] : span_scales<FMT>(bsp[t], ii, g)) & 0xFFu) : 127u;
         acc[t] = mfma_scale_e4m3_e2m1(h0, h1, cb, sh, sb, acc[t]);
         acc[t] = mfma_scale_e4m3_e2m1(l0, l1, cb, sl, sb, acc[t]);
       }
@@ -323,6 +400,8 @@ template <int FMT, int COUNT>
 __global__ __launch_bounds__(256, kMinWaves) void k_gate_up(GateUpArgs a) {
   __shared__ float red[4][2 * GT][4][64];  // [wave][tile][j][lane]
   __shared__ float hbuf[16][GCOLS + 1];     // MXFP4: the block's h before the plane split
+  // FP4: per wave, the scale bytes of the workgroup's 2*GCOLS weight rows over one run
+  __shared__ __attribute__((aligned(16))) uint8_t lsc[FMT == MOE_FMT_FP8_BLOCK128 ? 16 : 4 * 2 * GCOLS * (128 * COUNT / (FMT == MOE_FMT_NVFP4 ? 16 : 32))];
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int sb = blockIdx.x;
@@ -366,6 +445,14 @@ __global__ __launch_bounds__(256, kMinWaves) void k_gate_up(GateUpArgs a) {
     gsc[t] = FMT == MOE_FMT_NVFP4 ? glob[(size_t)e * 2 * I + rows[t]] : 1.f;
     usc[t] = FMT == MOE_FMT_NVFP4 ? glob[(size_t)e * 2 * I + rows[GT + t]] : 1.f;
   }
+  // FP4 scales are staged per wave (one row per lane) when the run's scale bytes are whole
+  // 16-byte pieces at 16-byte aligned offsets (uniform); otherwise lanes load their spans
+  uint8_t *wsc = nullptr;
+  if constexpr (FMT != MOE_FMT_FP8_BLOCK128) {
+    constexpr int sdiv = FMT == MOE_FMT_NVFP4 ? 16 : 32;
+    constexpr int RB = 128 * COUNT / sdiv;
+    if (RB % 16 == 0 && (H / sdiv) % 16 == 0) wsc = &lsc[wave * 2 * GCOLS * RB];
+  }
   f32x4_t acc[2 * GT];
 #pragma unroll
   for (int t = 0; t < 2 * GT; t++) acc[t] = zero4();
@@ -380,13 +467,13 @@ __global__ __launch_bounds__(256, kMinWaves) void k_gate_up(GateUpArgs a) {
     const uint32_t as = tok >= 0 ? (uint32_t)tok * (H / 32) : 0x80000000u;
     if (wave < a.kwaves)
       for (int kk = 0; kk < kw; kk += 128 * COUNT)  // runs of COUNT steps; the tail is masked
-        mma_run_mx<2 * GT, COUNT>(A, aq, as, m, rows, 0, wave * kw + kk, kw - kk, g, acc);
+        mma_run_mx<2 * GT, COUNT>(A, aq, as, m, rows, 0, wave * kw + kk, kw - kk, g, acc, wsc);
   } else {
     const rsrc_t ra = make_rsrc(a.x, (uint32_t)a.T * H * 2);
     const uint32_t a_row = tok >= 0 ? (uint32_t)tok * H * 2 : 0x80000000u;
     if (wave < a.kwaves)
       for (int kk = 0; kk < kw; kk += 128 * COUNT)
-        mma_run<FMT, 2 * GT, COUNT>(ra, a_row, m, rows, 0, wave * kw + kk, kw - kk, g, acc);
+        mma_run<FMT, 2 * GT, COUNT>(ra, a_row, m, rows, 0, wave * kw + kk, kw - kk, g, acc, wsc);
   }
 #pragma unroll
   for (int t = 0; t < 2 * GT; t++)
