@@ -526,6 +526,8 @@ constexpr int DNT = 4;
 
 template <int FMT, int COUNT>
 __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
+  // FP4: per wave, the scale bytes of its 16*DNT weight rows over one run
+  __shared__ __attribute__((aligned(16))) uint8_t lsc[FMT == MOE_FMT_FP8_BLOCK128 ? 16 : 4 * 16 * DNT * (128 * COUNT / (FMT == MOE_FMT_NVFP4 ? 16 : 32))];
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int sb = blockIdx.x;
@@ -554,6 +556,14 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
   const int H = a.H, I = a.I, Il = a.Il;
   const int ntile = min(DNT, (H - n0) / 16);
   const WMat<FMT> m = weight_matrix<FMT>(codes, scales, e, H, I);
+  // FP4 scales are staged per wave when each run's scale bytes are whole, 16-byte aligned
+  // pieces (uniform: slice start, row pitch and run length); otherwise lanes load spans
+  uint8_t *wsc = nullptr;
+  if constexpr (FMT != MOE_FMT_FP8_BLOCK128) {
+    constexpr int sdiv = FMT == MOE_FMT_NVFP4 ? 16 : 32;
+    constexpr int RB = 128 * COUNT / sdiv;
+    if (RB % 16 == 0 && (I / sdiv) % 16 == 0 && (a.lo / sdiv) % 16 == 0) wsc = &lsc[wave * 16 * DNT * RB];
+  }
   uint32_t rows[DNT];  // rows inside this expert's [H, I] matrix
 #pragma unroll
   for (int t = 0; t < DNT; t++) rows[t] = n0 + 16 * (t < ntile ? t : 0) + r;
@@ -588,12 +598,12 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
     const uint32_t aq = real ? (uint32_t)(p0 + r) * ul : 0x80000000u;
     const uint32_t as = real ? (uint32_t)(p0 + r) * (ul / 32) : 0x80000000u;
     for (int kw0 = 0; kw0 < Il; kw0 += 128 * COUNT)  // runs of COUNT steps; the tail is masked
-      mma_run_mx<DNT, COUNT>(A, aq, as, m, rows, a.lo, kw0, Il - kw0, g, acc);
+      mma_run_mx<DNT, COUNT>(A, aq, as, m, rows, a.lo, kw0, Il - kw0, g, acc, wsc);
   } else {
     const rsrc_t ra = make_rsrc(a.h, (uint32_t)a.h_rows * Il * 2);
     const uint32_t a_row = real ? (uint32_t)(p0 + r) * Il * 2 : 0x80000000u;
     for (int kw0 = 0; kw0 < Il; kw0 += 128 * COUNT)
-      mma_run<FMT, DNT, COUNT>(ra, a_row, m, rows, a.lo, kw0, Il - kw0, g, acc);
+      mma_run<FMT, DNT, COUNT>(ra, a_row, m, rows, a.lo, kw0, Il - kw0, g, acc, wsc);
   }
 #pragma unroll
   for (int j = 0; j < 4; j++) {
@@ -683,13 +693,11 @@ hipError_t launch_gate_up(int fmt, const GateUpArgs &a, int n_shared_sub, hipStr
 
 template <int FMT>
 static void launch_down_fmt(const DownArgs &a, dim3 grid, hipStream_t s) {
-  switch (count_class(FMT, (a.Il + 127) / 128)) {
+  // runs of at most 4 steps (down loops over runs; longer ones exceed the register budget)
+  switch (count_class(MOE_FMT_FP8_BLOCK128, (a.Il + 127) / 128)) {
     case 1: hipLaunchKernelGGL((k_down<FMT, 1>), grid, dim3(256), 0, s, a); break;
     case 2: hipLaunchKernelGGL((k_down<FMT, 2>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_down<FMT, 4>), grid, dim3(256), 0, s, a); break;
-    default:
-      if constexpr (FMT == MOE_FMT_NVFP4) hipLaunchKernelGGL((k_down<FMT, 8>), grid, dim3(256), 0, s, a);
-      break;
+    default: hipLaunchKernelGGL((k_down<FMT, 4>), grid, dim3(256), 0, s, a); break;
   }
 }
 
