@@ -239,13 +239,17 @@ __device__ __forceinline__ void tiled_k_loop(TileLDS<TK> &lds, rsrc_t ra, const 
     } else {
       mma_stage<TK>(lds.a[st & 1], lds.b[st & 1], a_row0, brow, lane, acc);
     }
-    if (st + 1 < nK) store(st + 1, ta_next, tb_next);
+    // unconditional (after the last stage it fills the idle buffer, which nobody reads) so
+    // that every path through the loop leaves the same loads in flight
+    store(st + 1, ta_next, tb_next);
     __syncthreads();
   };
-  for (int st = 0; st < nK; st += 2) {
+  int st = 0;
+  for (; st + 1 < nK; st += 2) {
     stage(st, at[0], bt[0], at[1], bt[1]);
-    if (st + 1 < nK) stage(st + 1, at[1], bt[1], at[0], bt[0]);
+    stage(st + 1, at[1], bt[1], at[0], bt[0]);
   }
+  if (st < nK) stage(st, at[0], bt[0], at[1], bt[1]);  // odd stage count: the last one, peeled
 }
 
 __device__ __forceinline__ void zero_acc(f32x4_t (&acc)[4][4]) {
