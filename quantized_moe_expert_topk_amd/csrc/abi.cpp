@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -226,6 +227,14 @@ qmoe::GateUpArgs gate_up_args(const moe_bank *routed, const moe_bank *shared, co
   a.lo = lo;
   a.Il = p.Il;
   gate_up_ksplit(routed->H, &a.kwaves, &a.ksteps);
+  // Few pairs: at most about one wave per SIMD would be busy, so split K over 8 waves
+  // per workgroup (half the K range, one round trip fewer per wave) when H allows it.
+  // The bound on the busy 16-row blocks is the pair count (or E), plus the shared blocks.
+  const long long blocks = std::min<long long>((long long)T * k, routed->E) + p.n_shared_sub;
+  if (!p.tiled && (routed->H / 128) % 8 == 0 && blocks * (p.Il / 32) * 4 < 2048) {
+    a.kwaves = 8;
+    a.ksteps = routed->H / 1024;
+  }
   char *ws = static_cast<char *>(workspace);
   a.h = reinterpret_cast<uint16_t *>(ws);
   a.h_rows = p.h_rows;

@@ -396,12 +396,14 @@ constexpr int GCOLS = 32;
 constexpr int GT = GCOLS / 16;
 constexpr int kMinWaves = 3;  // waves per SIMD the expert kernels are compiled for
 
-template <int FMT, int COUNT>
-__global__ __launch_bounds__(256, kMinWaves) void k_gate_up(GateUpArgs a) {
-  __shared__ float red[4][2 * GT][4][64];  // [wave][tile][j][lane]
-  __shared__ float hbuf[16][GCOLS + 1];     // MXFP4: the block's h before the plane split
+// KW = waves per workgroup, all splitting K: 4, or 8 when few pairs leave most of the chip
+// idle (each wave then covers half the K range, one round trip fewer).
+template <int FMT, int COUNT, int KW>
+__global__ __launch_bounds__(64 * KW, kMinWaves) void k_gate_up(GateUpArgs a) {
+  __shared__ float red[KW][2 * GT][4][64];  // [wave][tile][j][lane]
+  __shared__ float hbuf[16][GCOLS + 1];      // MXFP4: the block's h before the plane split
   // FP4: per wave, the scale bytes of the workgroup's 2*GCOLS weight rows over one run
-  __shared__ __attribute__((aligned(16))) uint8_t lsc[FMT == MOE_FMT_FP8_BLOCK128 ? 16 : 4 * 2 * GCOLS * (128 * COUNT / (FMT == MOE_FMT_NVFP4 ? 16 : 32))];
+  __shared__ __attribute__((aligned(16))) uint8_t lsc[FMT == MOE_FMT_FP8_BLOCK128 ? 16 : KW * 2 * GCOLS * (128 * COUNT / (FMT == MOE_FMT_NVFP4 ? 16 : 32))];
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int sb = blockIdx.x;
@@ -486,7 +488,7 @@ __global__ __launch_bounds__(256, kMinWaves) void k_gate_up(GateUpArgs a) {
     for (int j = 0; j < 4; j++) {
       float gv = 0.f, uv = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; w++) {
+      for (int w = 0; w < KW; w++) {
         gv += red[w][t][j][lane];
         uv += red[w][GT + t][j][lane];
       }
@@ -502,6 +504,7 @@ __global__ __launch_bounds__(256, kMinWaves) void k_gate_up(GateUpArgs a) {
   if constexpr (FMT == MOE_FMT_MXFP4_E8M0) {
     // h rows of this block, columns [c0, c0 + 32) = one e8m0 block: 16 lanes per row
     __syncthreads();
+    if (threadIdx.x >= 256) return;  // waves 4.. (KW = 8) have no rows here
     const int row = threadIdx.x >> 4, cp = (threadIdx.x & 15) * 2;
     const float v[2] = {hbuf[row][cp], hbuf[row][cp + 1]};
     uint32_t qh[1], ql[1], s1, s2;
@@ -669,16 +672,25 @@ static int count_class(int fmt, int steps) {
   return fmt == MOE_FMT_NVFP4 ? c : (c < 4 ? c : 4);
 }
 
-template <int FMT>
-static void launch_gate_up_fmt(const GateUpArgs &a, dim3 grid, hipStream_t s) {
+template <int FMT, int KW>
+static void launch_gate_up_kw(const GateUpArgs &a, dim3 grid, hipStream_t s) {
+  const dim3 block(64 * KW);
   switch (count_class(FMT, a.ksteps)) {
-    case 1: hipLaunchKernelGGL((k_gate_up<FMT, 1>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_gate_up<FMT, 2>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_gate_up<FMT, 4>), grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_gate_up<FMT, 1, KW>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_gate_up<FMT, 2, KW>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_gate_up<FMT, 4, KW>), grid, block, 0, s, a); break;
     default:
-      if constexpr (FMT == MOE_FMT_NVFP4) hipLaunchKernelGGL((k_gate_up<FMT, 8>), grid, dim3(256), 0, s, a);
+      if constexpr (FMT == MOE_FMT_NVFP4) hipLaunchKernelGGL((k_gate_up<FMT, 8, KW>), grid, block, 0, s, a);
       break;
   }
+}
+
+template <int FMT>
+static void launch_gate_up_fmt(const GateUpArgs &a, dim3 grid, hipStream_t s) {
+  if (a.kwaves > 4)
+    launch_gate_up_kw<FMT, 8>(a, grid, s);
+  else
+    launch_gate_up_kw<FMT, 4>(a, grid, s);
 }
 
 hipError_t launch_gate_up(int fmt, const GateUpArgs &a, int n_shared_sub, hipStream_t s) {
