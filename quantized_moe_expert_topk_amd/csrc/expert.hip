@@ -415,10 +415,11 @@ __global__ __launch_bounds__(64 * KW, kMinWaves) void k_gate_up(GateUpArgs a) {
   const float *glob;
   if (!is_shared) {
     p0 = sb * 16;
-    if (p0 >= __builtin_amdgcn_readfirstlane(a.total_padded[0])) return;  // uniform over the workgroup
-    e = __builtin_amdgcn_readfirstlane(a.block_expert[p0 / a.block_m]);
+    // three independent loads in flight together (p0 < cap indexes both arrays)
+    const int tp = a.total_padded[0], eb = a.block_expert[p0 / a.block_m], f = a.sorted_ids[p0 + r];
+    if (p0 >= __builtin_amdgcn_readfirstlane(tp)) return;  // uniform over the workgroup
+    e = __builtin_amdgcn_readfirstlane(eb);
     if (e < 0) return;
-    const int f = a.sorted_ids[p0 + r];
     tok = f < a.T * a.k ? f / a.k : -1;
     codes = a.gu;
     scales = a.gus;
@@ -541,10 +542,14 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
   const uint8_t *codes;
   const uint8_t *scales;
   const float *glob;
+  int f0 = 0;  // pair of this lane's row (routed blocks)
   if (!is_shared) {
     p0 = sb * 16;
-    if (p0 >= __builtin_amdgcn_readfirstlane(a.total_padded[0])) return;
-    e = __builtin_amdgcn_readfirstlane(a.block_expert[p0 / a.block_m]);
+    // independent loads in flight together (p0 < cap indexes both arrays)
+    const int tp = a.total_padded[0], eb = a.block_expert[p0 / a.block_m];
+    f0 = a.sorted_ids[p0 + r];
+    if (p0 >= __builtin_amdgcn_readfirstlane(tp)) return;
+    e = __builtin_amdgcn_readfirstlane(eb);
     if (e < 0) return;
     codes = a.dn;
     scales = a.dns;
@@ -594,7 +599,7 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
 #pragma unroll
   for (int t = 0; t < DNT; t++) dglob[t] = FMT == MOE_FMT_NVFP4 ? glob[(size_t)e * H + n0 + 16 * t + r] : 1.f;
   // padding rows (no pair / past T) point past h: they read zeros without a memory request
-  const bool real = is_shared ? (p0 - a.cap + r < a.T) : (a.sorted_ids[p0 + r] < P);
+  const bool real = is_shared ? (p0 - a.cap + r < a.T) : (f0 < P);
   if constexpr (FMT == MOE_FMT_MXFP4_E8M0) {
     const uint32_t hr = (uint32_t)a.h_rows, ul = (uint32_t)Il;
     const ActMX A{make_rsrc(a.hq, 2 * hr * ul), make_rsrc(a.hs, 2 * hr * (ul / 32)), hr * ul, hr * (ul / 32), ul};

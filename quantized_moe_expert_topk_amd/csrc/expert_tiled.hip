@@ -281,8 +281,9 @@ __global__ __launch_bounds__(256, 2) void k_gate_up_tiled(GateUpArgs a) {
   const float *glob;
   if (!is_shared) {
     p0 = blockIdx.x * TM;
-    if (p0 >= __builtin_amdgcn_readfirstlane(a.total_padded[0])) return;
-    e = __builtin_amdgcn_readfirstlane(a.block_expert[p0 / a.block_m]);
+    const int tp = a.total_padded[0], eb = a.block_expert[p0 / a.block_m];  // both in flight (p0 < cap)
+    if (p0 >= __builtin_amdgcn_readfirstlane(tp)) return;
+    e = __builtin_amdgcn_readfirstlane(eb);
     if (e < 0) return;
     codes = a.gu;
     scales = a.gus;
@@ -366,8 +367,9 @@ __global__ __launch_bounds__(256, 2) void k_down_tiled(DownArgs a) {
   const float *glob;
   if (!is_shared) {
     p0 = blockIdx.x * TM;
-    if (p0 >= __builtin_amdgcn_readfirstlane(a.total_padded[0])) return;
-    e = __builtin_amdgcn_readfirstlane(a.block_expert[p0 / a.block_m]);
+    const int tp = a.total_padded[0], eb = a.block_expert[p0 / a.block_m];  // both in flight (p0 < cap)
+    if (p0 >= __builtin_amdgcn_readfirstlane(tp)) return;
+    e = __builtin_amdgcn_readfirstlane(eb);
     if (e < 0) return;
     codes = a.dn;
     scales = a.dns;
