@@ -126,9 +126,10 @@ def run(args):
     def to_dev(a):
         return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    def dbank(b):
-        return qm.DeviceBank(b.fmt, b.E, b.H, b.I, to_dev(b.gate_up), to_dev(b.gate_up_scale), to_dev(b.down),
-                             to_dev(b.down_scale), to_dev(b.gate_up_global), to_dev(b.down_global))
+    def dbank(b):  # uploaded row-major, reordered once into the kernels' tile-16 layout
+        return qm.moe_pack_bank(qm.DeviceBank(b.fmt, b.E, b.H, b.I, to_dev(b.gate_up), to_dev(b.gate_up_scale),
+                                              to_dev(b.down), to_dev(b.down_scale), to_dev(b.gate_up_global),
+                                              to_dev(b.down_global)))
 
     t0 = time.time()
     inst = []

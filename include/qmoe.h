@@ -65,6 +65,22 @@ typedef enum {
   MOE_FMT_MXFP4_E8M0 = 3
 } moe_format;
 
+/* Byte order of a bank's weight codes and FP4 scales (moe_bank.layout).
+ *   MOE_LAYOUT_ROWS    row-major, as stored by the checkpoint (the shapes below).
+ *   MOE_LAYOUT_TILE16  the order the expert kernels read, made by moe_pack_bank: every
+ *     group of 16 consecutive rows of a matrix (rows of all experts counted together) is
+ *     stored piece-major.  For codes the piece is 16 bytes (32 FP4 or 16 FP8 elements):
+ *     byte b of row r sits at (r/16)*16*P + (b/16)*256 + (r%16)*16 + b%16, P = bytes per
+ *     row.  FP4 scales use the scale bytes of one 32-element piece as their unit
+ *     (NVFP4 2 bytes, MXFP4 1): byte j of row r sits at
+ *     (r/16)*16*S + (j/u)*16*u + (r%16)*u + j%u, S = scale bytes per row, u = unit.
+ *     Sizes are unchanged; FP8_BLOCK128 scales and the NVFP4 globals keep their order.
+ *     One wave load is then one contiguous 1 KB run that is already in the matrix-core
+ *     operand order (16 rows x 64 bytes), and any slice of rows or columns on a
+ *     multiple of 32 elements stays addressable. */
+#define MOE_LAYOUT_ROWS 0
+#define MOE_LAYOUT_TILE16 1
+
 /* One bank of E experts, full-I layout, expert-major and row-major per matrix
  * (issue #520 patch, nvfp4.py layout()/pack(); issue #62 "What it touches" item 1):
  *   gate_up        [E, 2I, H] weights: gate rows [0, I), up rows [I, 2I); K = H.
@@ -78,7 +94,9 @@ typedef enum {
  *                  MXFP4: u8 e8m0 [E, H, I/32].
  *   down_global    NVFP4 only: f32 [E, H]; NULL otherwise.
  * A rank that stores only its own slice passes that storage as a bank with I = hi - lo
- * and the slice [0, I) (PR #70: TP=1 is the identity layout). */
+ * and the slice [0, I) (PR #70: TP=1 is the identity layout).
+ * `layout` is MOE_LAYOUT_ROWS or MOE_LAYOUT_TILE16 (the order of gate_up, down and their
+ * FP4 scales); moe_expert_forward reads TILE16 banks only. */
 typedef struct {
   int32_t fmt; /* moe_format */
   int32_t E, H, I;
@@ -88,7 +106,19 @@ typedef struct {
   const void *down;
   const void *down_scale;
   const float *down_global;
+  int32_t layout; /* MOE_LAYOUT_* */
 } moe_bank;
+
+/* moe_pack_bank -- reorders a MOE_LAYOUT_ROWS bank into MOE_LAYOUT_TILE16 storage, once,
+ * when the weights are loaded (a pure permutation of bytes: values and formats unchanged).
+ *   src   a ROWS bank (device pointers).
+ *   dst   a TILE16 bank of the same fmt, E, H and I whose gate_up, gate_up_scale, down and
+ *         down_scale point at device buffers of the same sizes as src's, not overlapping
+ *         them; dst's FP8_BLOCK128 scales and NVFP4 globals, when they are other buffers
+ *         than src's, receive a plain copy.  The caller owns both banks' storage.
+ * Requires 16 | 2I, 16 | H and whole 16-byte code pieces per row (H and I multiples of 32
+ * for the FP4 formats, of 16 for FP8).  Enqueued on `stream`; no host synchronisation. */
+int moe_pack_bank(const moe_bank *src, const moe_bank *dst, void *stream);
 
 /* ------------------------------------------------------------------ routing */
 
@@ -187,7 +217,8 @@ size_t moe_workspace_bytes(const moe_bank *routed, const moe_bank *shared, int T
  *   any reduction across ranks (PR #70 ownership table and the paragraph after it).
  * Companion scales are sliced with their weight's axis; the NVFP4 per-row globals of
  * gate_up follow its rows and down_global is used whole (PR #637 "Implementation notes").
- *   routed      E-expert bank; shared: NULL or a 1-expert bank of the same format, H and I.
+ *   routed      E-expert bank; shared: NULL or a 1-expert bank of the same format, H and I;
+ *               both in MOE_LAYOUT_TILE16 (moe_pack_bank), else MOE_ERR_UNSUPPORTED.
  *   x_bf16      [T, H] bf16; topk_w [T, k] f32; al: the moe_align output for these ids.
  *   slice_lo/hi multiples of the format block (NVFP4 16, MXFP4 32, FP8_BLOCK128 128), with
  *               0 <= lo < hi <= I (issue #62 "What it touches" item 2; PR #70 div_tp(...,

@@ -17,10 +17,11 @@ MOE_ERR_HIP = -5
 
 MOE_FMT = {"nvfp4": 1, "fp8blk": 2, "mxfp4": 3}
 MOE_OUT_F32, MOE_OUT_BF16 = 0, 1
+MOE_LAYOUT_ROWS, MOE_LAYOUT_TILE16 = 0, 1
 
 # every entry point include/qmoe.h declares
 EXPORTS = ("moe_route", "moe_route_workspace_bytes", "moe_route_from_logits", "moe_align_capacity", "moe_align_workspace_bytes", "moe_align",
-           "moe_workspace_bytes", "moe_expert_forward", "moe_expert_gate_up", "moe_expert_down",
+           "moe_workspace_bytes", "moe_pack_bank", "moe_expert_forward", "moe_expert_gate_up", "moe_expert_down",
            "moe_status_string", "moe_last_error")
 
 
@@ -28,7 +29,7 @@ class MoeBankStruct(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int32), ("E", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
                 ("gate_up", ctypes.c_void_p), ("gate_up_scale", ctypes.c_void_p),
                 ("gate_up_global", ctypes.c_void_p), ("down", ctypes.c_void_p),
-                ("down_scale", ctypes.c_void_p), ("down_global", ctypes.c_void_p)]
+                ("down_scale", ctypes.c_void_p), ("down_global", ctypes.c_void_p), ("layout", ctypes.c_int32)]
 
 
 class MoeAlignOutStruct(ctypes.Structure):
@@ -70,6 +71,7 @@ def lib() -> ctypes.CDLL:
         L.moe_align.argtypes = [vp, i32, i32, i32, pa, vp, sz, vp]
         L.moe_workspace_bytes.argtypes = [pb, pb, i32, i32, i32, i32, i32]
         L.moe_workspace_bytes.restype = sz
+        L.moe_pack_bank.argtypes = [pb, pb, vp]
         L.moe_expert_forward.argtypes = [pb, pb, vp, i32, i32, vp, pa, i32, i32, vp, i32, vp, sz, vp]
         L.moe_expert_gate_up.argtypes = [pb, pb, vp, i32, i32, pa, i32, i32, vp, sz, vp]
         L.moe_expert_down.argtypes = [pb, pb, i32, i32, vp, pa, i32, i32, vp, i32, vp, sz, vp]

@@ -10,7 +10,8 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import MOE_FMT, MOE_OUT_BF16, MOE_OUT_F32, MoeAlignOutStruct, MoeBankStruct, check, lib
+from ._lib import (MOE_FMT, MOE_LAYOUT_ROWS, MOE_LAYOUT_TILE16, MOE_OUT_BF16, MOE_OUT_F32, MoeAlignOutStruct,
+                   MoeBankStruct, check, lib)
 
 
 def _ptr(t: torch.Tensor | None):
@@ -33,7 +34,9 @@ def _need(t: torch.Tensor, dtype, shape, name):
 
 @dataclass
 class DeviceBank:
-    """One bank of E experts on the GPU, in the full-I layout of ``moe_bank``."""
+    """One bank of E experts on the GPU, in the full-I layout of ``moe_bank``; ``layout`` is
+    MOE_LAYOUT_ROWS (the checkpoint's row-major order) or MOE_LAYOUT_TILE16 (the kernels' order,
+    made once by :func:`moe_pack_bank`)."""
     fmt: str
     E: int
     H: int
@@ -44,13 +47,15 @@ class DeviceBank:
     down_scale: torch.Tensor
     gate_up_global: torch.Tensor | None = None
     down_global: torch.Tensor | None = None
+    layout: int = MOE_LAYOUT_ROWS
 
     def struct(self) -> MoeBankStruct:
         return MoeBankStruct(MOE_FMT[self.fmt], self.E, self.H, self.I, self.gate_up.data_ptr(),
                              self.gate_up_scale.data_ptr(),
                              self.gate_up_global.data_ptr() if self.gate_up_global is not None else None,
                              self.down.data_ptr(), self.down_scale.data_ptr(),
-                             self.down_global.data_ptr() if self.down_global is not None else None)
+                             self.down_global.data_ptr() if self.down_global is not None else None,
+                             self.layout)
 
     def nbytes_expert(self) -> int:
         ts = [self.gate_up, self.gate_up_scale, self.down, self.down_scale, self.gate_up_global, self.down_global]
@@ -70,6 +75,21 @@ class AlignOut:
     def struct(self) -> MoeAlignOutStruct:
         return MoeAlignOutStruct(self.sorted_ids.data_ptr(), self.block_expert.data_ptr(), self.counts.data_ptr(),
                                  self.offsets.data_ptr(), self.total_padded.data_ptr(), self.block_m, self.capacity)
+
+
+def moe_pack_bank(bank: DeviceBank, stream=None) -> DeviceBank:
+    """The bank reordered into MOE_LAYOUT_TILE16 (new code and FP4 scale storage; the FP8 block
+    scales and NVFP4 globals are shared with ``bank``).  A packed bank is returned as is."""
+    if bank.layout == MOE_LAYOUT_TILE16:
+        return bank
+    fp4 = bank.fmt != "fp8blk"
+    dst = DeviceBank(bank.fmt, bank.E, bank.H, bank.I, torch.empty_like(bank.gate_up),
+                     torch.empty_like(bank.gate_up_scale) if fp4 else bank.gate_up_scale,
+                     torch.empty_like(bank.down), torch.empty_like(bank.down_scale) if fp4 else bank.down_scale,
+                     bank.gate_up_global, bank.down_global, MOE_LAYOUT_TILE16)
+    src_s, dst_s = bank.struct(), dst.struct()
+    check("moe_pack_bank", lib().moe_pack_bank(ctypes.byref(src_s), ctypes.byref(dst_s), _stream(stream)))
+    return dst
 
 
 # ----------------------------------------------------------------------------- routing
@@ -225,12 +245,15 @@ def choose_block_m(T: int, k: int, E: int, fmt: str | None = None) -> int:
 class MoeLayer:
     """Pre-allocated buffers for one (bank, T, slice) and the three calls of one layer:
     moe_route -> moe_align -> moe_expert_forward on one stream, host-sync free, so it can
-    be captured in a HIP graph."""
+    be captured in a HIP graph.  Row-major banks are packed (moe_pack_bank) here, once; pass
+    packed banks to share their storage between layers."""
 
     def __init__(self, routed: DeviceBank, shared: DeviceBank | None, w_router: torch.Tensor,
                  bias: torch.Tensor | None, T: int, k: int, slice_lo: int, slice_hi: int,
                  renormalize: bool = True, block_m: int | None = None, out_dtype=torch.float32):
         dev = w_router.device
+        routed = moe_pack_bank(routed)
+        shared = moe_pack_bank(shared) if shared is not None else None
         self.routed, self.shared, self.w_router, self.bias = routed, shared, w_router, bias
         self.T, self.k, self.lo, self.hi, self.renormalize = T, k, slice_lo, slice_hi, renormalize
         self.block_m = block_m or choose_block_m(T, k, routed.E, routed.fmt)

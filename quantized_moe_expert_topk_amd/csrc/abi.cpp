@@ -109,7 +109,48 @@ int check_bank(const moe_bank *b, const char *name) {
   if (b->I % 32)
     return fail(MOE_ERR_UNSUPPORTED, "%s bank: I=%d must be a multiple of 32 (row pitch of 16-byte loads)",
                 name, b->I);
+  if (b->layout != MOE_LAYOUT_TILE16)
+    return fail(MOE_ERR_UNSUPPORTED, "%s bank: layout %d; the expert kernels read MOE_LAYOUT_TILE16 banks "
+                "(reorder once with moe_pack_bank)", name, b->layout);
   return MOE_OK;
+}
+
+// Bytes of each array of a bank (codes and scales of gate_up and down, NVFP4 globals).
+struct BankSizes {
+  size_t gu, gus, gug, dn, dns, dng;
+  uint32_t gu_pitch, gus_pitch, dn_pitch, dns_pitch;  // bytes per row (codes, FP4 scales)
+  int unit;                                           // FP4 scale bytes per 32-element piece
+};
+
+BankSizes bank_sizes(const moe_bank *b) {
+  BankSizes z{};
+  const size_t E = (size_t)b->E, H = (size_t)b->H, I = (size_t)b->I;
+  const bool fp8 = b->fmt == MOE_FMT_FP8_BLOCK128;
+  z.gu_pitch = (uint32_t)(fp8 ? H : H / 2);
+  z.dn_pitch = (uint32_t)(fp8 ? I : I / 2);
+  z.gu = E * 2 * I * z.gu_pitch;
+  z.dn = E * H * z.dn_pitch;
+  if (fp8) {
+    z.gus = E * (2 * I / 128) * (H / 128) * 4;
+    z.dns = E * (H / 128) * (I / 128) * 4;
+  } else {
+    const size_t sdiv = b->fmt == MOE_FMT_NVFP4 ? 16 : 32;
+    z.unit = b->fmt == MOE_FMT_NVFP4 ? 2 : 1;
+    z.gus_pitch = (uint32_t)(H / sdiv);
+    z.dns_pitch = (uint32_t)(I / sdiv);
+    z.gus = E * 2 * I * z.gus_pitch;
+    z.dns = E * H * z.dns_pitch;
+  }
+  if (b->fmt == MOE_FMT_NVFP4) {
+    z.gug = E * 2 * I * 4;
+    z.dng = E * H * 4;
+  }
+  return z;
+}
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
 }
 
 int check_slice(const moe_bank *b, int lo, int hi) {
@@ -405,6 +446,69 @@ int moe_align(const int32_t *topk_ids, int T, int k, int E, const moe_align_out 
                                        out->block_expert, out->counts, out->offsets, out->total_padded,
                                        static_cast<int32_t *>(workspace), static_cast<hipStream_t>(stream)),
                     "align launch");
+}
+
+int moe_pack_bank(const moe_bank *src, const moe_bank *dst, void *stream) {
+  if (!src || !dst) return fail(MOE_ERR_INVALID_ARG, "moe_pack_bank: NULL bank");
+  if (!format_block(src->fmt)) return fail(MOE_ERR_INVALID_ARG, "moe_pack_bank: unknown format %d", src->fmt);
+  if (src->layout != MOE_LAYOUT_ROWS || dst->layout != MOE_LAYOUT_TILE16)
+    return fail(MOE_ERR_INVALID_ARG, "moe_pack_bank: src layout must be ROWS (%d) and dst TILE16 (%d)",
+                src->layout, dst->layout);
+  if (dst->fmt != src->fmt || dst->E != src->E || dst->H != src->H || dst->I != src->I)
+    return fail(MOE_ERR_INVALID_ARG, "moe_pack_bank: src and dst differ in fmt, E, H or I");
+  if (src->E < 1 || src->H < 1 || src->I < 1)
+    return fail(MOE_ERR_INVALID_ARG, "moe_pack_bank: E=%d H=%d I=%d must be positive", src->E, src->H, src->I);
+  const int piece = src->fmt == MOE_FMT_FP8_BLOCK128 ? 16 : 32;  // elements per 16-byte code piece
+  if (src->H % piece || src->I % piece || src->H % 128 || (src->fmt == MOE_FMT_FP8_BLOCK128 && src->I % 128))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_pack_bank: H=%d and I=%d need whole %d-element pieces per row", src->H,
+                src->I, piece);
+  if ((long long)src->E * 2 * src->I * src->H > (1LL << 40))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_pack_bank: bank too large");
+  const moe_bank *b[2] = {src, dst};
+  for (const moe_bank *x : b) {
+    if (!x->gate_up || !x->gate_up_scale || !x->down || !x->down_scale)
+      return fail(MOE_ERR_INVALID_ARG, "moe_pack_bank: NULL weight or scale pointer");
+    if (x->fmt == MOE_FMT_NVFP4 && (!x->gate_up_global || !x->down_global))
+      return fail(MOE_ERR_INVALID_ARG, "moe_pack_bank: NVFP4 needs gate_up_global and down_global");
+    if ((reinterpret_cast<uintptr_t>(x->gate_up) | reinterpret_cast<uintptr_t>(x->down)) % 16)
+      return fail(MOE_ERR_INVALID_ARG, "moe_pack_bank: weight codes must be 16-byte aligned");
+  }
+  const BankSizes z = bank_sizes(src);
+  const bool fp8 = src->fmt == MOE_FMT_FP8_BLOCK128;
+  if (overlap(src->gate_up, z.gu, dst->gate_up, z.gu) || overlap(src->down, z.dn, dst->down, z.dn) ||
+      (!fp8 && (overlap(src->gate_up_scale, z.gus, dst->gate_up_scale, z.gus) ||
+                overlap(src->down_scale, z.dns, dst->down_scale, z.dns))))
+    return fail(MOE_ERR_INVALID_ARG, "moe_pack_bank: dst codes or FP4 scales overlap src");
+  int rc = check_device();
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t E = (size_t)src->E, H = (size_t)src->H, I = (size_t)src->I;
+  rc = hip_status(qmoe::launch_pack_tile16(src->gate_up, const_cast<void *>(dst->gate_up), E * 2 * I, z.gu_pitch,
+                                           16, s), "pack launch");
+  if (rc) return rc;
+  rc = hip_status(qmoe::launch_pack_tile16(src->down, const_cast<void *>(dst->down), E * H, z.dn_pitch, 16, s),
+                  "pack launch");
+  if (rc) return rc;
+  if (!fp8) {
+    rc = hip_status(qmoe::launch_pack_tile16(src->gate_up_scale, const_cast<void *>(dst->gate_up_scale), E * 2 * I,
+                                             z.gus_pitch, z.unit, s), "pack launch");
+    if (rc) return rc;
+    rc = hip_status(qmoe::launch_pack_tile16(src->down_scale, const_cast<void *>(dst->down_scale), E * H,
+                                             z.dns_pitch, z.unit, s), "pack launch");
+    if (rc) return rc;
+  }
+  // order-free arrays: plain copies when dst has its own storage
+  const struct { const void *from; const void *to; size_t n; } same[4] = {
+      {fp8 ? src->gate_up_scale : nullptr, dst->gate_up_scale, z.gus},
+      {fp8 ? src->down_scale : nullptr, dst->down_scale, z.dns},
+      {src->gate_up_global, dst->gate_up_global, z.gug},
+      {src->down_global, dst->down_global, z.dng}};
+  for (const auto &c : same) {
+    if (!c.from || !c.to || c.from == c.to || !c.n) continue;
+    rc = hip_status(hipMemcpyAsync(const_cast<void *>(c.to), c.from, c.n, hipMemcpyDeviceToDevice, s), "pack copy");
+    if (rc) return rc;
+  }
+  return ok();
 }
 
 int moe_expert_gate_up(const moe_bank *routed, const moe_bank *shared, const void *x_bf16, int T, int k,

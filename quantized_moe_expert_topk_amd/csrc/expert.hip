@@ -23,10 +23,12 @@
 // Tiling: a workgroup is 4 waves over 16 rows of the pair list (one aligned sub-block of a
 // single expert).  gate_up: 32 slice columns of gate and of up (4 MFMA tiles), K split over
 // the 4 waves and reduced through LDS.  down: each wave owns 4 x 16 hidden columns over the
-// whole slice.  K advances in 128-wide chunks: lane group g = l/16 reads the contiguous
-// run [kc+32g, kc+32g+32) of its row of both operands (the MFMA slots of A and B carry the
-// same K indices).  A wave issues the loads of 2 chunks before decoding either of them,
-// so the weight bytes are in flight while the VALU dequantizes.
+// whole slice.  K advances in 128-wide chunks: lane group g = l/16 reads the run
+// [kc+32g, kc+32g+32) of its row of both operands (FP4; the MFMA slots of A and B carry the
+// same K indices).  The weights are in the tile-16 layout (MOE_LAYOUT_TILE16), so one wave
+// load of a tile is a contiguous 1 KB run already in operand order.  A wave issues the
+// loads of 2 chunks before decoding either of them, so the weight bytes are in flight while
+// the VALU dequantizes.
 #include "device_common.h"
 #include "launch.h"
 
@@ -96,9 +98,10 @@ __device__ __forceinline__ void decode_mxfp4(const uint4 &c, uint32_t e8, frag8 
   fp4x8_pow2_to_bf16(c.w, p, b[3]);
 }
 
-// Scale bytes of one tile row for a group of 2 K steps (chunk mapping): NVFP4 16 bytes
+// Scale bytes of one row-major row for a group of 2 K steps (chunk mapping): NVFP4 16 bytes
 // (2 steps x 4 lane groups x 2 groups of 16), MXFP4 8 bytes (2 x 4 x 1).  All four lane
-// groups of a row load the same span; each lane then selects its own bytes.
+// groups of a row load the same span; each lane then selects its own bytes.  Used for the
+// MXFP4 activation planes, which are row-major.
 template <int FMT>
 __device__ __forceinline__ uint4 load_scale_span(rsrc_t r, uint32_t off, bool aligned) {
   constexpr int NB = FMT == MOE_FMT_NVFP4 ? 16 : 8;
@@ -126,78 +129,104 @@ __device__ __forceinline__ uint32_t span_scales(const uint4 &sp, int s, int g) {
   }
 }
 
+// Weight rows are stored in 16-row tiles, piece-major (MOE_LAYOUT_TILE16): piece c (16
+// code bytes) of row R sits at tile_off(R) + 256 c, with tile_off(R) = (R & ~15) * P +
+// (R & 15) * 16 for P code bytes per row, and the FP4 scale bytes of piece c (SP of them) at
+// (R & ~15) * S + 16 SP c + (R & 15) SP for S scale bytes per row.  A wave's load of one
+// piece index over the 16 rows of a tile is then one contiguous 1 KB run.
+template <int FMT>
+__device__ __forceinline__ uint32_t code_tile_off(uint32_t row, uint32_t K) {
+  return (row & ~15u) * (FMT == MOE_FMT_FP8_BLOCK128 ? K : K / 2) + (row & 15u) * 16;
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t scale_tile_off(uint32_t row, uint32_t K) {
+  constexpr uint32_t SP = FMT == MOE_FMT_NVFP4 ? 2 : 1;
+  return (row & ~15u) * (K / 32) * SP + (row & 15u) * SP;
+}
+
 // Multiply-accumulate a wave's K range [kw0, kw0 + 128*COUNT) of one 16-row A block against
-// NT weight tiles.  Step i is the 128-wide chunk [kw0 + 128 i, +128); lane group g reads
-// its 32-wide piece [32 g, 32 g + 32) (one contiguous 64 B run of each of 16 rows per code
-// load), so every MFMA stays inside one 128x128 FP8 scale block.  Positions at or past
-// kvalid (relative to kw0) contribute zero and load from clamped in-bounds offsets.  Steps
-// are taken in groups of 2 (FP4) or 1 (FP8) whose loads are all issued before decoding.
+// NT weight tiles.  Step i is the 128-wide chunk [kw0 + 128 i, +128).  FP4: lane group
+// g = l/16 takes the 32-element piece [32 g, 32 g + 32) of the step from both operands.
+// FP8: lane group g takes [16 g, 16 g + 16) and [64 + 16 g, +16), so each of the two code
+// loads covers 4 consecutive pieces of every tile row (one 1 KB run per tile).  Either way
+// every MFMA stays inside one 128x128 FP8 scale block.  Positions at or past kvalid
+// (relative to kw0) contribute zero and load from clamped in-bounds offsets.  Steps are
+// taken in groups of 2 (FP4) or 1 (FP8) whose loads are all issued before decoding.
 //   ra, a_row: activation buffer and the byte offset of this lane's row; a row past the
 //              buffer end reads as zeros without a memory request (padding rows)
-//   m, rows:   weight matrix and this lane's row of each tile;  b_k0: K offset in the row
-//   lsc:       if not null, this wave's LDS region of NT*16 rows x RB bytes: the run's
-//              FP4 scale bytes are fetched with one row per lane (RB = 128*COUNT/sdiv bytes,
-//              wide loads issued before the first group's weight loads), staged there and
-//              read back per lane, instead of every lane group loading its rows' spans
+//   m, rows:   weight matrix (tile-16 layout) and this lane's row of each tile (the NT
+//              tiles start on multiples of 16);  b_k0: K offset in the row
+//   lsc:       FP4 with RB = 4 * COUNT * SP a multiple of 16: this wave's LDS region of
+//              NT x 16 RB bytes.  The run's scale bytes (one contiguous 16 RB-byte run per
+//              tile in this layout) are fetched with 16-byte loads issued before the first
+//              group's weight loads, staged there and read back per lane.  Shorter runs
+//              (lsc unused) load each lane's SP scale bytes per step and tile.
 template <int FMT, int NT, int COUNT>
 __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FMT> &m, const uint32_t (&rows)[NT],
                                         int b_k0, int kw0, int kvalid, int g, f32x4_t (&acc)[NT],
                                         uint8_t *lsc = nullptr) {
   constexpr bool FP4 = FMT != MOE_FMT_FP8_BLOCK128;
   constexpr int NPF = FP4 ? 2 : 1;
+  constexpr int SP = FMT == MOE_FMT_NVFP4 ? 2 : 1;
   const uint32_t K = (uint32_t)m.K;
-  const int sdiv = FMT == MOE_FMT_NVFP4 ? 16 : 32;
   const int lane = lane_id(), r = lane & 15;
-  // spans are dword aligned when the row pitch and the run start are (uniform)
-  const bool sal = ((K / sdiv) % 4 == 0) && (((b_k0 + kw0) / sdiv) % 4 == 0);
-  constexpr int RB = FP4 ? 128 * COUNT / (FMT == MOE_FMT_NVFP4 ? 16 : 32) : 16;  // staged bytes per row
+  uint32_t cb[NT], sb[NT];
+#pragma unroll
+  for (int t = 0; t < NT; t++) {
+    cb[t] = code_tile_off<FMT>(rows[t], K);
+    sb[t] = FP4 ? scale_tile_off<FMT>(rows[t], K) : 0;
+  }
+  constexpr int RB = FP4 ? 4 * COUNT * SP : 16;  // staged scale bytes per lane (16 lanes per tile)
   constexpr int SQ = RB / 16;
   uint4 stg[SQ > 0 ? SQ : 1];
   if constexpr (FP4 && SQ > 0) {
-    if (lsc) {  // lane l fetches row l of the NT*16 tile rows (NT*16 == 64 lanes)
-      const uint32_t row = rows[(lane >> 4) % NT];
+    {  // lanes 16t..16t+15 fetch tile t's run
+      const uint32_t run = (rows[(lane >> 4) % NT] & ~15u) * (K / 32) * SP + ((b_k0 + kw0) / 32) * 16 * SP;
 #pragma unroll
-      for (int q = 0; q < SQ; q++) stg[q] = buf_load16(m.scales, row * (K / sdiv) + (b_k0 + kw0) / sdiv + 16 * q);
+      for (int q = 0; q < SQ; q++) stg[q] = buf_load16(m.scales, run + r * RB + 16 * q);
     }
   }
 #pragma unroll
   for (int i0 = 0; i0 < COUNT; i0 += NPF) {
     ARaw ar[NPF];
     uint4 c0[NPF][NT], c1[NPF][NT];
-    uint4 sp[NT];
     uint32_t lsv[NPF][NT];
     float bs[NPF][NT];
-    if constexpr (FP4) {
-      const int kg = kw0 + (128 * i0 < kvalid ? 128 * i0 : 0);
-      if (!lsc) {
-#pragma unroll
-        for (int t = 0; t < NT; t++)
-          sp[t] = load_scale_span<FMT>(m.scales, rows[t] * (K / sdiv) + (b_k0 + kg) / sdiv, sal);
-      }
-    }
 #pragma unroll
     for (int ii = 0; ii < NPF; ii++) {
       const int i = i0 + ii;
       if (i >= COUNT) break;
-      const int kr = 128 * i + 32 * g;  // position relative to kw0
-      const int k = kw0 + (kr < kvalid ? kr : 0);
+      if constexpr (FP4) {
+        const int kr = 128 * i + 32 * g;
+        const int k = kw0 + (kr < kvalid ? kr : 0);  // this lane's piece, relative to b_k0
 #pragma unroll
-      for (int q = 0; q < 4; q++) ar[ii].q[q] = buf_load16(ra, a_row + k * 2 + 16 * q);
+        for (int q = 0; q < 4; q++) ar[ii].q[q] = buf_load16(ra, a_row + k * 2 + 16 * q);
+        const uint32_t pc = (uint32_t)(b_k0 + k) / 32;
 #pragma unroll
-      for (int t = 0; t < NT; t++) {
-        if constexpr (FP4) {
-          c0[ii][t] = buf_load16(m.codes, rows[t] * (K / 2) + (b_k0 + k) / 2);
-        } else {
-          const uint32_t o = rows[t] * K + b_k0 + k;
-          c0[ii][t] = buf_load16(m.codes, o);
-          c1[ii][t] = buf_load16(m.codes, o + 16);
+        for (int t = 0; t < NT; t++) c0[ii][t] = buf_load16(m.codes, cb[t] + pc * 256);
+        if constexpr (SQ == 0) {
+#pragma unroll
+          for (int t = 0; t < NT; t++)
+            lsv[ii][t] = SP == 2 ? buf_load2(m.scales, sb[t] + pc * 32) : buf_load1(m.scales, sb[t] + pc * 16);
+        }
+      } else {
+        const int kc = kw0 + (128 * i < kvalid ? 128 * i : 0);  // the step
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+          ar[ii].q[q] = buf_load16(ra, a_row + (kc + 16 * g + (q >= 2 ? 64 : 0)) * 2 + 16 * (q & 1));
+        const uint32_t pc = (uint32_t)(b_k0 + kc) / 16 + g;
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+          c0[ii][t] = buf_load16(m.codes, cb[t] + pc * 256);
+          c1[ii][t] = buf_load16(m.codes, cb[t] + (pc + 4) * 256);
           bs[ii][t] = buf_load_f32(m.scales, ((rows[t] / 128) * (K / 128) + (b_k0 + kw0 + 128 * i) / 128) * 4);
         }
       }
     }
-    if constexpr (FP4) {
-      if (lsc) {  // scale bytes from the wave's LDS region (staged once per run)
-        if constexpr (SQ > 0) {
+    if constexpr (FP4 && SQ > 0) {
+      {  // scale bytes from the wave's LDS region (staged once per run)
+        {
           if (i0 == 0) {  // the first group's weight loads are in flight by now
 #pragma unroll
             for (int q = 0; q < SQ; q++) *reinterpret_cast<uint4 *>(lsc + lane * RB + 16 * q) = stg[q];
@@ -209,11 +238,11 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
 #pragma unroll
         for (int ii = 0; ii < NPF; ii++) {
           const int kr = 128 * (i0 + ii) + 32 * g;
-          const int kb = (kr < kvalid ? kr : 0) / sdiv;  // this lane's first scale byte in the run
+          const int cr = (kr < kvalid ? kr : 0) / 32;  // this lane's piece within the run
 #pragma unroll
           for (int t = 0; t < NT; t++) {
-            const uint8_t *p = lsc + (16 * t + r) * RB + kb;
-            lsv[ii][t] = FMT == MOE_FMT_NVFP4 ? (uint32_t)*reinterpret_cast<const uint16_t *>(p) : (uint32_t)*p;
+            const uint8_t *p = lsc + 16 * t * RB + cr * 16 * SP + r * SP;
+            lsv[ii][t] = SP == 2 ? (uint32_t)*reinterpret_cast<const uint16_t *>(p) : (uint32_t)*p;
           }
         }
       }
@@ -222,7 +251,8 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
     for (int ii = 0; ii < NPF; ii++) {
       const int i = i0 + ii;
       if (i >= COUNT) break;
-      const bool v = 128 * i + 32 * g < kvalid;
+      const bool v0 = 128 * i + (FP4 ? 32 : 16) * g < kvalid;  // first (FP4: only) half of the lane's K
+      const bool v1 = 128 * i + 64 + 16 * g < kvalid;          // FP8 second half
       frag8 av[4];
 #pragma unroll
       for (int q = 0; q < 4; q++) av[q].q = ar[ii].q[q];
@@ -230,17 +260,21 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
       for (int t = 0; t < NT; t++) {
         frag8 bv[4];
         if constexpr (FMT == MOE_FMT_NVFP4) {
-          const uint32_t sc = lsc ? lsv[ii][t] : span_scales<FMT>(sp[t], ii, g);
-          decode_nvfp4(c0[ii][t], sc & 0xFFu, (sc >> 8) & 0xFFu, bv);
+          decode_nvfp4(c0[ii][t], lsv[ii][t] & 0xFFu, (lsv[ii][t] >> 8) & 0xFFu, bv);
         } else if constexpr (FMT == MOE_FMT_MXFP4_E8M0) {
-          decode_mxfp4(c0[ii][t], (lsc ? lsv[ii][t] : span_scales<FMT>(sp[t], ii, g)) & 0xFFu, bv);
+          decode_mxfp4(c0[ii][t], lsv[ii][t] & 0xFFu, bv);
         } else {
           fp8x8_to_bf16(c0[ii][t].x, c0[ii][t].y, bv[0]);
           fp8x8_to_bf16(c0[ii][t].z, c0[ii][t].w, bv[1]);
           fp8x8_to_bf16(c1[ii][t].x, c1[ii][t].y, bv[2]);
           fp8x8_to_bf16(c1[ii][t].z, c1[ii][t].w, bv[3]);
         }
-        if (!v) zero_frags(bv);
+        if constexpr (FP4) {
+          if (!v0) zero_frags(bv);
+        } else {
+          if (!v0) bv[0].q = bv[1].q = make_uint4(0, 0, 0, 0);
+          if (!v1) bv[2].q = bv[3].q = make_uint4(0, 0, 0, 0);
+        }
         if constexpr (FMT == MOE_FMT_FP8_BLOCK128) {
           f32x4_t tmp = zero4();
 #pragma unroll
@@ -264,15 +298,15 @@ struct ActMX {
   uint32_t K;               // row width in elements
 };
 
-// The MXFP4 counterpart of mma_run: same chunk mapping and grouping (2 chunks per group),
-// but each chunk is two scaled MFMAs (hi and lo plane of A) on the raw FP4 codes.  Within
-// a chunk, lane group g holds A's K [16g, 16g+16) and [64+16g, +16) and B's K [32g, 32g+32)
-// (the instruction's operand layout), so both operands cover the same 128 K indices.
-// Positions at or past kvalid contribute zero: their A bytes and B codes are replaced by
-// zeros and their scales by 1, so stale workspace bytes never reach the MFMA.
+// The MXFP4 counterpart of mma_run: same chunk mapping, grouping (2 chunks per group) and
+// weight layout, but each chunk is two scaled MFMAs (hi and lo plane of A) on the raw FP4
+// codes.  Within a chunk, lane group g holds A's K [16g, 16g+16) and [64+16g, +16) and B's
+// K [32g, 32g+32) (the instruction's operand layout), so both operands cover the same 128
+// K indices.  Positions at or past kvalid contribute zero: their A bytes and B codes are
+// replaced by zeros and their scales by 1, so stale workspace bytes never reach the MFMA.
 //   a_q, a_s: byte offsets of this lane's row in the planes and in the scales (or
 //             0x80000000 for a padding row, which reads zeros without a memory request)
-//   lsc: as in mma_run (this wave's LDS region for the run's staged scale bytes, or null)
+//   lsc: as in mma_run (required when RB = 4 * COUNT is a multiple of 16)
 template <int NT, int COUNT>
 __device__ __forceinline__ void mma_run_mx(const ActMX &A, uint32_t a_q, uint32_t a_s,
                                            const WMat<MOE_FMT_MXFP4_E8M0> &m, const uint32_t (&rows)[NT],
@@ -281,27 +315,30 @@ __device__ __forceinline__ void mma_run_mx(const ActMX &A, uint32_t a_q, uint32_
   constexpr int FMT = MOE_FMT_MXFP4_E8M0;
   const uint32_t K = (uint32_t)m.K;
   const int lane = lane_id(), r = lane & 15;
-  constexpr int RB = 4 * COUNT;  // staged scale bytes per row (one e8m0 per 32 K)
+  constexpr int RB = 4 * COUNT;  // staged scale bytes per lane (one e8m0 per 32 K)
   constexpr int SQ = RB / 16;
   uint4 stg[SQ > 0 ? SQ : 1];
   if constexpr (SQ > 0) {
-    if (lsc) {
-      const uint32_t row = rows[(lane >> 4) % NT];
+    {
+      const uint32_t run = (rows[(lane >> 4) % NT] & ~15u) * (K / 32) + ((b_k0 + kw0) / 32) * 16;
 #pragma unroll
-      for (int q = 0; q < SQ; q++) stg[q] = buf_load16(m.scales, row * (K / 32) + (b_k0 + kw0) / 32 + 16 * q);
+      for (int q = 0; q < SQ; q++) stg[q] = buf_load16(m.scales, run + r * RB + 16 * q);
     }
   }
-  const bool bsal = ((K / 32) % 4 == 0) && (((b_k0 + kw0) / 32) % 4 == 0);
   const bool asal = ((A.K / 32) % 4 == 0) && ((kw0 / 32) % 4 == 0);
   const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
   for (int i0 = 0; i0 < COUNT; i0 += 2) {
     const int kg = kw0 + (128 * i0 < kvalid ? 128 * i0 : 0);
-    uint4 bsp[NT];
     uint32_t lsv[2][NT];
-    if (!lsc) {
+    if constexpr (SQ == 0) {
 #pragma unroll
-      for (int t = 0; t < NT; t++) bsp[t] = load_scale_span<FMT>(m.scales, rows[t] * (K / 32) + (b_k0 + kg) / 32, bsal);
+      for (int ii = 0; ii < 2; ii++) {
+        const int kr = 128 * (i0 + ii) + 32 * g;
+        const uint32_t pc = (uint32_t)(b_k0 + kw0 + (kr < kvalid ? kr : 0)) / 32;
+#pragma unroll
+        for (int t = 0; t < NT; t++) lsv[ii][t] = buf_load1(m.scales, scale_tile_off<FMT>(rows[t], K) + pc * 16);
+      }
     }
     const uint4 ash = load_scale_span<FMT>(A.s, a_s + kg / 32, asal);
     const uint4 asl = load_scale_span<FMT>(A.s, A.splane + a_s + kg / 32, asal);
@@ -316,12 +353,12 @@ __device__ __forceinline__ void mma_run_mx(const ActMX &A, uint32_t a_q, uint32_
       al[ii][0] = buf_load16(A.q, A.qplane + a_q + kc + 16 * g);
       al[ii][1] = buf_load16(A.q, A.qplane + a_q + kc + 64 + 16 * g);
       const int kr = 128 * i + 32 * g;
-      const int k = kw0 + (kr < kvalid ? kr : 0);
+      const uint32_t pc = (uint32_t)(b_k0 + kw0 + (kr < kvalid ? kr : 0)) / 32;
 #pragma unroll
-      for (int t = 0; t < NT; t++) c[ii][t] = buf_load16(m.codes, rows[t] * (K / 2) + (b_k0 + k) / 2);
+      for (int t = 0; t < NT; t++) c[ii][t] = buf_load16(m.codes, code_tile_off<FMT>(rows[t], K) + pc * 256);
     }
-    if (lsc) {  // B scale bytes from the wave's LDS region (staged once per run)
-      if constexpr (SQ > 0) {
+    if constexpr (SQ > 0) {  // B scale bytes from the wave's LDS region (staged once per run)
+      {
         if (i0 == 0) {
 #pragma unroll
           for (int q = 0; q < SQ; q++) *reinterpret_cast<uint4 *>(lsc + lane * RB + 16 * q) = stg[q];
@@ -333,9 +370,9 @@ __device__ __forceinline__ void mma_run_mx(const ActMX &A, uint32_t a_q, uint32_
 #pragma unroll
       for (int ii = 0; ii < 2; ii++) {
         const int kr = 128 * (i0 + ii) + 32 * g;
-        const int kb = (kr < kvalid ? kr : 0) / 32;
+        const int cr = (kr < kvalid ? kr : 0) / 32;
 #pragma unroll
-        for (int t = 0; t < NT; t++) lsv[ii][t] = lsc[(16 * t + r) * RB + kb];
+        for (int t = 0; t < NT; t++) lsv[ii][t] = lsc[16 * t * RB + cr * 16 + r];
       }
     }
 #pragma unroll
@@ -351,10 +388,10 @@ __device__ __forceinline__ void mma_run_mx(const ActMX &A, uint32_t a_q, uint32_
       const uint32_t sl = vb ? (span_scales<FMT>(asl, ii, g) & 0xFFu) : 127u;
 #pragma unroll
       for (int t = 0; t < NT; t++) {
-        const uint4 cb = vb ? c[ii][t] : z;
-        const uint32_t sb = vb ? ((lsc ? lsv[ii][t] : span_scales<FMT>(bsp[t], ii, g)) & 0xFFu) : 127u;
-        acc[t] = mfma_scale_e4m3_e2m1(h0, h1, cb, sh, sb, acc[t]);
-        acc[t] = mfma_scale_e4m3_e2m1(l0, l1, cb, sl, sb, acc[t]);
+        const uint4 cbv = vb ? c[ii][t] : z;
+        const uint32_t sbv = vb ? (lsv[ii][t] & 0xFFu) : 127u;
+        acc[t] = mfma_scale_e4m3_e2m1(h0, h1, cbv, sh, sbv, acc[t]);
+        acc[t] = mfma_scale_e4m3_e2m1(l0, l1, cbv, sl, sbv, acc[t]);
       }
     }
   }
@@ -448,13 +485,13 @@ __global__ __launch_bounds__(64 * KW, kMinWaves) void k_gate_up(GateUpArgs a) {
     gsc[t] = FMT == MOE_FMT_NVFP4 ? glob[(size_t)e * 2 * I + rows[t]] : 1.f;
     usc[t] = FMT == MOE_FMT_NVFP4 ? glob[(size_t)e * 2 * I + rows[GT + t]] : 1.f;
   }
-  // FP4 scales are staged per wave (one row per lane) when the run's scale bytes are whole
-  // 16-byte pieces at 16-byte aligned offsets (uniform); otherwise lanes load their spans
+  // FP4 scales are staged per wave when a run's scale bytes per tile are whole 16-byte
+  // pieces (runs of at least 2 steps for NVFP4, 4 for MXFP4); otherwise lanes load theirs
   uint8_t *wsc = nullptr;
   if constexpr (FMT != MOE_FMT_FP8_BLOCK128) {
     constexpr int sdiv = FMT == MOE_FMT_NVFP4 ? 16 : 32;
     constexpr int RB = 128 * COUNT / sdiv;
-    if (RB % 16 == 0 && (H / sdiv) % 16 == 0) wsc = &lsc[wave * 2 * GCOLS * RB];
+    if (RB % 16 == 0) wsc = &lsc[wave * 2 * GCOLS * RB];
   }
   f32x4_t acc[2 * GT];
 #pragma unroll
@@ -564,13 +601,13 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
   const int H = a.H, I = a.I, Il = a.Il;
   const int ntile = min(DNT, (H - n0) / 16);
   const WMat<FMT> m = weight_matrix<FMT>(codes, scales, e, H, I);
-  // FP4 scales are staged per wave when each run's scale bytes are whole, 16-byte aligned
-  // pieces (uniform: slice start, row pitch and run length); otherwise lanes load spans
+  // FP4 scales are staged per wave when a run's scale bytes per tile are whole 16-byte
+  // pieces (runs of at least 2 steps for NVFP4, 4 for MXFP4); otherwise lanes load theirs
   uint8_t *wsc = nullptr;
   if constexpr (FMT != MOE_FMT_FP8_BLOCK128) {
     constexpr int sdiv = FMT == MOE_FMT_NVFP4 ? 16 : 32;
     constexpr int RB = 128 * COUNT / sdiv;
-    if (RB % 16 == 0 && (I / sdiv) % 16 == 0 && (a.lo / sdiv) % 16 == 0) wsc = &lsc[wave * 16 * DNT * RB];
+    if (RB % 16 == 0) wsc = &lsc[wave * 16 * DNT * RB];
   }
   uint32_t rows[DNT];  // rows inside this expert's [H, I] matrix
 #pragma unroll

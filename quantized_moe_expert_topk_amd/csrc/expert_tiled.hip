@@ -82,27 +82,55 @@ __device__ __forceinline__ void a_store(uint16_t (*la)[TK], const ATile<TK> &t, 
 // Plain bf16 weights (the router): no scales, no dequantization.
 constexpr int kFmtBf16 = 0;
 
-// Weight tile: a thread owns tile row tid/2 and the K half tid%2 of the stage (WK weights).
+// Weight tile: thread tid stages tile row b_row_of(tid) and part b_half_of(tid) of every
+// stage (WK weights).  The quantized weights are in the tile-16 layout (MOE_LAYOUT_TILE16:
+// 16-row tiles stored piece-major, a piece = 16 code bytes), and a 32-thread group covers
+// one tile: threads 0-15 its rows' part 0, threads 16-31 the same rows' part 1, two
+// adjacent 256-byte pieces (one 512-byte run).  NVFP4 with TK 32 (8 bytes per thread, half
+// a piece) and the row-major bf16 router weights pair the threads of a row instead.
+template <int FMT, int TK>
+constexpr bool kPairMap = FMT == kFmtBf16 || (FMT == MOE_FMT_NVFP4 && TK == 32);
+
+template <int FMT, int TK>
+__device__ __forceinline__ int b_row_of(int tid) {
+  return kPairMap<FMT, TK> ? tid >> 1 : 16 * (tid >> 5) + (tid & 15);
+}
+
+template <int FMT, int TK>
+__device__ __forceinline__ int b_half_of(int tid) {
+  return kPairMap<FMT, TK> ? tid & 1 : (tid >> 4) & 1;
+}
+
 struct BTile {
   uint4 c0, c1, c2, c3;  // codes: WK/2 bytes (FP4), WK bytes (FP8) or 2*WK bytes (bf16)
   uint32_t sc;           // NVFP4: the e4m3 scales of the WK/16 groups
 };
 
+// Loads part `half` of the stage starting at K offset ks (a multiple of TK) of matrix row `row`:
+//   NVFP4 TK 64: piece ks/32 + half (32 elements) and its 2 scale bytes
+//   NVFP4 TK 32: bytes [8 half, 8 half + 8) of piece ks/32 and its scale byte `half`
+//   FP8   TK 64: pieces ks/16 + half and ks/16 + half + 2 (16 elements each)
+//   FP8   TK 32: piece ks/16 + half
+//   bf16       : elements [ks + TK/2 half, +TK/2) of the row-major row
 template <int FMT, int TK>
-__device__ __forceinline__ void b_fetch(const WMat<FMT> &m, uint32_t row, int k, BTile &t) {
+__device__ __forceinline__ void b_fetch(const WMat<FMT> &m, uint32_t row, int ks, int half, BTile &t) {
   const uint32_t K = (uint32_t)m.K;
   if constexpr (FMT == MOE_FMT_NVFP4) {
+    const uint32_t cb = (row & ~15u) * (K / 2) + (row & 15u) * 16;
+    const uint32_t sb = (row & ~15u) * (K / 16) + (row & 15u) * 2;
     if constexpr (TK == 64) {
-      t.sc = buf_load2(m.scales, row * (K / 16) + k / 16);
-      t.c0 = buf_load16(m.codes, row * (K / 2) + k / 2);
+      const uint32_t pc = (uint32_t)ks / 32 + half;
+      t.sc = buf_load2(m.scales, sb + pc * 32);
+      t.c0 = buf_load16(m.codes, cb + pc * 256);
     } else {
-      t.sc = buf_load1(m.scales, row * (K / 16) + k / 16);
-      const uint2 v =
-          __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(m.codes, (int)(row * (K / 2) + k / 2), 0, 0));
+      const uint32_t pc = (uint32_t)ks / 32;
+      t.sc = buf_load1(m.scales, sb + pc * 32 + half);
+      const uint2 v = __builtin_bit_cast(
+          uint2, __builtin_amdgcn_raw_buffer_load_b64(m.codes, (int)(cb + pc * 256 + 8 * half), 0, 0));
       t.c0 = make_uint4(v.x, v.y, 0, 0);
     }
   } else if constexpr (FMT == kFmtBf16) {
-    const uint32_t o = (row * K + k) * 2;
+    const uint32_t o = (row * K + ks + (TK / 2) * half) * 2;
     t.c0 = buf_load16(m.codes, o);
     t.c1 = buf_load16(m.codes, o + 16);
     if constexpr (TK == 64) {
@@ -110,12 +138,15 @@ __device__ __forceinline__ void b_fetch(const WMat<FMT> &m, uint32_t row, int k,
       t.c3 = buf_load16(m.codes, o + 48);
     }
   } else {
-    t.c0 = buf_load16(m.codes, row * K + k);
-    if constexpr (TK == 64) t.c1 = buf_load16(m.codes, row * K + k + 16);
+    const uint32_t cb = (row & ~15u) * K + (row & 15u) * 16;
+    const uint32_t pc = (uint32_t)ks / 16 + half;
+    t.c0 = buf_load16(m.codes, cb + pc * 256);
+    if constexpr (TK == 64) t.c1 = buf_load16(m.codes, cb + (pc + 2) * 256);
   }
 }
 
-// Dequantizes and stores this thread's WK weights (chunks (WK/8)*half + q) of tile row `row`.
+// Dequantizes and stores this thread's WK weights of tile row `row` (the 8-element K chunks
+// b_fetch's part `half` covers).
 template <int FMT, int TK>
 __device__ __forceinline__ void b_store(uint16_t *rowp, int row, int half, const BTile &t, bool valid) {
   constexpr int NC = Stage<TK>::WK / 8;
@@ -148,7 +179,11 @@ __device__ __forceinline__ void b_store(uint16_t *rowp, int row, int half, const
 #pragma unroll
     for (int q = 0; q < NC; q++) f[q].q = make_uint4(0, 0, 0, 0);
 #pragma unroll
-  for (int q = 0; q < NC; q++) *reinterpret_cast<uint4 *>(rowp + swz<TK>(row, NC * half + q)) = f[q].q;
+  for (int q = 0; q < NC; q++) {
+    // FP8 TK 64 holds pieces half and half + 2: chunks 2 half + {0,1} and 4 + 2 half + {0,1}
+    const int c = (FMT == MOE_FMT_FP8_BLOCK128 && TK == 64) ? (q < 2 ? 2 * half + q : 2 + 2 * half + q) : NC * half + q;
+    *reinterpret_cast<uint4 *>(rowp + swz<TK>(row, c)) = f[q].q;
+  }
 }
 
 // ---------------------------------------------------------------- the MFMA stage
@@ -187,16 +222,17 @@ __device__ __forceinline__ void fold_block(f32x4_t (&acc)[4][4], f32x4_t (&part)
 
 // The K loop shared by both GEMMs.  Thread roles: activation chunks (NQ rows given by
 // a_off, byte offsets of the rows' K origin, 0x80000000 for rows that read zeros) and the
-// weight tile row `wrow` of matrix m (half `bhalf` of each stage, zeroed unless wvalid).
-// K runs over [0, nK*TK) relative to the weight column b_k0; weight K halves at or past
-// kvalid load zeros.  FP8: scale(kb, j) gives the weight_scale_inv of col tile j, K block kb.
+// weight tile row `wrow` of matrix m (part b_half_of(tid) of each stage, zeroed unless
+// wvalid).  K runs over [0, nK*TK) relative to the weight column b_k0; stages at or past
+// kvalid (a multiple of TK in every caller) load clamped offsets and store zeros.
+// FP8: scale(kb, j) gives the weight_scale_inv of col tile j, K block kb.
 template <int FMT, int TK, typename ScaleFn>
 __device__ __forceinline__ void tiled_k_loop(TileLDS<TK> &lds, rsrc_t ra, const uint32_t (&a_off)[Stage<TK>::NQ],
                                              const WMat<FMT> &m,
                                              uint32_t wrow, bool wvalid, int b_k0, int nK, int kvalid,
                                              const int (&brow)[4], ScaleFn scale, f32x4_t (&acc)[4][4]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int brr = tid >> 1, bhalf = tid & 1;
+  const int brr = b_row_of<FMT, TK>(tid), bhalf = b_half_of<FMT, TK>(tid);
   const int a_row0 = (wave >> 1) * 64;
   f32x4_t part[4][4];
   if constexpr (FMT == MOE_FMT_FP8_BLOCK128) {
@@ -211,8 +247,8 @@ __device__ __forceinline__ void tiled_k_loop(TileLDS<TK> &lds, rsrc_t ra, const 
   ATile<TK> at[2];
   BTile bt[2];
   auto fetch = [&](int st, ATile<TK> &ta, BTile &tb) {  // weight loads first: oldest in the queue
-    const int kb = st * TK + (TK / 2) * bhalf;
-    b_fetch<FMT, TK>(m, wrow, b_k0 + (kb < kvalid ? kb : 0), tb);
+    const int kb = st * TK;
+    b_fetch<FMT, TK>(m, wrow, b_k0 + (kb < kvalid ? kb : 0), bhalf, tb);
     a_fetch<TK>(ra, a_off, st * TK, lane, ta);
   };
   auto store = [&](int st, const ATile<TK> &ta, const BTile &tb) {
@@ -311,7 +347,7 @@ __global__ __launch_bounds__(256, 2) void k_gate_up_tiled(GateUpArgs a) {
     }
     a_off[q] = tok >= 0 ? (uint32_t)tok * H * 2 : 0x80000000u;
   }
-  const int brr = tid >> 1;
+  const int brr = b_row_of<FMT, TK>(tid);
   const int bc = c0 + (brr & 63);  // slice column of this thread's weight row
   const bool wvalid = bc < Il;
   const uint32_t wrow = (uint32_t)((brr < 64 ? 0 : I) + a.lo + (wvalid ? bc : c0));
@@ -387,7 +423,7 @@ __global__ __launch_bounds__(256, 2) void k_down_tiled(DownArgs a) {
   uint32_t a_off[Stage<TK>::NQ];
 #pragma unroll
   for (int q = 0; q < Stage<TK>::NQ; q++) a_off[q] = (uint32_t)(p0 + a_row_of<TK>(wave, lane, q)) * Il * 2;
-  const uint32_t wrow = (uint32_t)(n0 + (tid >> 1));
+  const uint32_t wrow = (uint32_t)(n0 + b_row_of<FMT, TK>(tid));
   const int brow[4] = {64 * wn, 64 * wn + 16, 64 * wn + 32, 64 * wn + 48};
   f32x4_t acc[4][4];
   zero_acc(acc);
@@ -446,7 +482,7 @@ __global__ __launch_bounds__(256, 2) void k_router_tiled(const uint16_t *__restr
   WMat<kFmtBf16> m;
   m.codes = m.scales = make_rsrc(w, (uint32_t)E * H * 2);
   m.K = H;
-  const int ew = e0 + (tid >> 1);
+  const int ew = e0 + b_row_of<kFmtBf16, TK>(tid);
   const bool wvalid = ew < E;
   const int brow[4] = {64 * wn, 64 * wn + 16, 64 * wn + 32, 64 * wn + 48};
   f32x4_t acc[4][4];

@@ -63,6 +63,9 @@ hipError_t launch_down(int fmt, const DownArgs &a, int n_shared_sub, hipStream_t
 // rows are ceil(T/128) tiles after the routed ones.
 hipError_t launch_gate_up_tiled(int fmt, const GateUpArgs &a, int n_shared_tiles, hipStream_t s);
 hipError_t launch_down_tiled(int fmt, const DownArgs &a, int n_shared_tiles, hipStream_t s);
+// moe_pack_bank: [rows, pitch] bytes -> 16-row tiles stored piece-major in units of `unit`
+// (16, 2 or 1) bytes.
+hipError_t launch_pack_tile16(const void *src, void *dst, size_t rows, uint32_t pitch, int unit, hipStream_t s);
 hipError_t launch_act_mx8(const uint16_t *x, int rows, int K, uint8_t *q, uint8_t *sc, hipStream_t s);
 // Y rows in fp32 (streaming kernels) or bf16 (tiled kernels).
 hipError_t launch_combine(const void *Y, bool y_bf16, int T, int k, int H, int has_shared, void *out, int out_bf16,

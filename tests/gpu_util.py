@@ -15,10 +15,19 @@ def to_dev(a: np.ndarray | None, dev="cuda"):
     return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def device_bank(b, dev="cuda") -> qm.DeviceBank:
-    return qm.DeviceBank(b.fmt, b.E, b.H, b.I, to_dev(b.gate_up, dev), to_dev(b.gate_up_scale, dev),
+def device_bank(b, dev="cuda", packed=True) -> qm.DeviceBank:
+    """Upload a row-major bank; by default reorder it into the kernels' tile-16 layout."""
+    bank = qm.DeviceBank(b.fmt, b.E, b.H, b.I, to_dev(b.gate_up, dev), to_dev(b.gate_up_scale, dev),
                          to_dev(b.down, dev), to_dev(b.down_scale, dev), to_dev(b.gate_up_global, dev),
                          to_dev(b.down_global, dev))
+    return qm.moe_pack_bank(bank) if packed else bank
+
+
+def tile16_np(a: np.ndarray, unit: int) -> np.ndarray:
+    """The MOE_LAYOUT_TILE16 order of a row-major [rows, pitch] byte matrix, written as an
+    index transform: 16-row tiles, each stored as its units (of `unit` bytes) column by column."""
+    R, P = a.shape
+    return a.reshape(R // 16, 16, P // unit, unit).transpose(0, 2, 1, 3).reshape(R, P)
 
 
 def bf16_dev(bits: np.ndarray, dev="cuda") -> torch.Tensor:

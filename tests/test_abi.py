@@ -45,8 +45,9 @@ def test_align_capacity_and_workspace_sizes():
     assert qm.moe_align_workspace_bytes(0, 8, 256) == 0
 
 
-def _bank(fmt=1, E=8, H=256, I=128, glob=True):
-    return L.MoeBankStruct(fmt, E, H, I, FAKE, FAKE, FAKE if glob else None, FAKE, FAKE, FAKE if glob else None)
+def _bank(fmt=1, E=8, H=256, I=128, glob=True, layout=L.MOE_LAYOUT_TILE16, base=FAKE):
+    return L.MoeBankStruct(fmt, E, H, I, base, base, base if glob else None, base, base, base if glob else None,
+                           layout)
 
 
 def _align(bm=16, cap=None, T=16, k=2, E=8):
@@ -85,6 +86,8 @@ def _fwd(bank=None, shared=None, T=16, k=2, lo=0, hi=128, al=None, ws=1 << 30, o
     (dict(shared=_bank(E=1, I=64)), L.MOE_ERR_INVALID_ARG),    # and the same I
     (dict(out_dtype=5), L.MOE_ERR_INVALID_ARG),
     (dict(x=None), L.MOE_ERR_INVALID_ARG),
+    (dict(bank=_bank(layout=L.MOE_LAYOUT_ROWS)), L.MOE_ERR_UNSUPPORTED),  # kernels read TILE16 banks
+    (dict(shared=_bank(E=1, layout=L.MOE_LAYOUT_ROWS)), L.MOE_ERR_UNSUPPORTED),
 ])
 def test_forward_rejects_bad_arguments_before_any_launch(kw, code):
     rc, msg = _fwd(**kw)
@@ -125,3 +128,25 @@ def test_workspace_bytes_formula():
     rows = cap + 128
     want = up(2 * rows * 64) + up(2 * rows * 2) + up(2 * T * 256) + up(2 * T * 8) + y
     assert lib.moe_workspace_bytes(ctypes.byref(mb), ctypes.byref(ms), T, k, bm, 0, 64) == want
+
+
+def _pack(src, dst):
+    rc = L.lib().moe_pack_bank(ctypes.byref(src) if src else None, ctypes.byref(dst) if dst else None, None)
+    return rc, L.lib().moe_last_error().decode()
+
+
+@pytest.mark.parametrize("src,dst,code", [
+    (None, _bank(), L.MOE_ERR_INVALID_ARG),
+    (_bank(layout=L.MOE_LAYOUT_TILE16), _bank(base=0x40000000), L.MOE_ERR_INVALID_ARG),   # src must be ROWS
+    (_bank(layout=L.MOE_LAYOUT_ROWS), _bank(layout=L.MOE_LAYOUT_ROWS, base=0x40000000), L.MOE_ERR_INVALID_ARG),
+    (_bank(layout=L.MOE_LAYOUT_ROWS), _bank(I=256, base=0x40000000), L.MOE_ERR_INVALID_ARG),  # shape differs
+    (_bank(layout=L.MOE_LAYOUT_ROWS), _bank(), L.MOE_ERR_INVALID_ARG),                    # dst overlaps src
+    (_bank(layout=L.MOE_LAYOUT_ROWS, base=0x10008), _bank(base=0x40000000), L.MOE_ERR_INVALID_ARG),  # unaligned
+    (_bank(layout=L.MOE_LAYOUT_ROWS, glob=False), _bank(base=0x40000000, glob=False), L.MOE_ERR_INVALID_ARG),
+    (_bank(layout=L.MOE_LAYOUT_ROWS, I=48), _bank(I=48, base=0x40000000), L.MOE_ERR_UNSUPPORTED),  # half pieces
+    (_bank(fmt=9, layout=L.MOE_LAYOUT_ROWS), _bank(fmt=9, base=0x40000000), L.MOE_ERR_INVALID_ARG),
+])
+def test_pack_bank_rejects_bad_arguments_before_any_launch(src, dst, code):
+    rc, msg = _pack(src, dst)
+    assert rc == code, (rc, msg)
+    assert msg

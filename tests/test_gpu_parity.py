@@ -13,7 +13,7 @@ import torch
 import quantized_moe_expert_topk_amd as qm
 from oracle import oracle as O
 from synth import synth as S
-from tests.gpu_util import align_np, bf16_dev, check_close, device_bank, to_dev
+from tests.gpu_util import align_np, bf16_dev, check_close, device_bank, tile16_np, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -147,6 +147,48 @@ def test_align_is_bit_exact(T, k, E, bm, kind):
 
 
 # ----------------------------------------------------------------------------- expert layer
+
+# ----------------------------------------------------------------------------- weight layout
+
+@pytest.mark.parametrize("fmt,E,H,I", [("nvfp4", 3, 256, 128), ("fp8blk", 2, 256, 256), ("mxfp4", 3, 512, 192)])
+def test_pack_bank_is_the_tile16_permutation(fmt, E, H, I):
+    """moe_pack_bank puts every code and FP4 scale byte at its MOE_LAYOUT_TILE16 position
+    (bit-exact against the index transform of the row-major arrays) and leaves the
+    order-free arrays (FP8 block scales, NVFP4 globals) as they are."""
+    b = S.routed_bank(11, fmt, E, H, I)
+    pk = device_bank(b, packed=True)
+    torch.cuda.synchronize()
+    assert pk.layout == qm.MOE_LAYOUT_TILE16
+
+    def rows2d(a):
+        a = np.ascontiguousarray(a)
+        return a.reshape(-1, a.shape[-1])
+
+    def got(t):
+        return t.cpu().numpy().reshape(-1, t.shape[-1])
+
+    np.testing.assert_array_equal(got(pk.gate_up), tile16_np(rows2d(b.gate_up), 16))
+    np.testing.assert_array_equal(got(pk.down), tile16_np(rows2d(b.down), 16))
+    if fmt == "fp8blk":
+        np.testing.assert_array_equal(pk.gate_up_scale.cpu().numpy(), b.gate_up_scale)
+        np.testing.assert_array_equal(pk.down_scale.cpu().numpy(), b.down_scale)
+    else:
+        unit = 2 if fmt == "nvfp4" else 1
+        np.testing.assert_array_equal(got(pk.gate_up_scale), tile16_np(rows2d(b.gate_up_scale), unit))
+        np.testing.assert_array_equal(got(pk.down_scale), tile16_np(rows2d(b.down_scale), unit))
+    if fmt == "nvfp4":
+        np.testing.assert_array_equal(pk.gate_up_global.cpu().numpy(), b.gate_up_global)
+        np.testing.assert_array_equal(pk.down_global.cpu().numpy(), b.down_global)
+
+
+def test_forward_rejects_row_major_bank():
+    inp, r = inputs_for(1, 8)
+    rows = device_bank(inp.routed, packed=False)
+    dev = "cuda"
+    al = qm.moe_align(to_dev(r["ids"].astype(np.int32), dev), inp.routed.E, 16)
+    with pytest.raises(qm.MoeError, match="TILE16"):
+        qm.moe_expert_forward(rows, None, bf16_dev(inp.x), to_dev(r["w"].astype(np.float32), dev), al, 0, 128)
+
 
 def _forward_gpu(inp, ids, w, lo, hi, bm=None, out_dtype=torch.float32, banks=None):
     cfg = inp.cfg
