@@ -388,9 +388,12 @@ size_t moe_route_workspace_bytes(int T, int H, int E) {
   return qmoe::router_workspace_bytes(T, E, H);
 }
 
-int moe_route(const void *x_bf16, int T, int H, const void *w_router_bf16, int E, const float *bias, int k,
-              int renormalize, float *logits, int32_t *topk_ids, float *topk_w, void *workspace,
-              size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+int check_route(const void *x_bf16, int T, int H, const void *w_router_bf16, int E, int k, const float *logits,
+                const int32_t *topk_ids, const float *topk_w) {
   if (!w_router_bf16 || (T > 0 && (!x_bf16 || !logits || !topk_ids || !topk_w)))
     return fail(MOE_ERR_INVALID_ARG, "moe_route: NULL required pointer");
   if (T < 0 || H < 1 || E < 1) return fail(MOE_ERR_INVALID_ARG, "moe_route: T=%d H=%d E=%d", T, H, E);
@@ -400,6 +403,18 @@ int moe_route(const void *x_bf16, int T, int H, const void *w_router_bf16, int E
   if (T > 16 * 65535) return fail(MOE_ERR_UNSUPPORTED, "moe_route: T=%d too large", T);
   if ((long long)T * H * 2 >= (1LL << 31) || (long long)E * H * 2 >= (1LL << 31))
     return fail(MOE_ERR_UNSUPPORTED, "moe_route: x or the router weight exceeds 2 GiB (32-bit buffer offsets)");
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_route(const void *x_bf16, int T, int H, const void *w_router_bf16, int E, const float *bias, int k,
+              int renormalize, float *logits, int32_t *topk_ids, float *topk_w, void *workspace,
+              size_t workspace_bytes, void *stream) {
+  int rc0 = check_route(x_bf16, T, H, w_router_bf16, E, k, logits, topk_ids, topk_w);
+  if (rc0) return rc0;
   const size_t need = moe_route_workspace_bytes(T, H, E);
   if (workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "moe_route: workspace %zu < %zu", workspace_bytes, need);
   if (need && !workspace) return fail(MOE_ERR_INVALID_ARG, "moe_route: workspace is NULL");

@@ -13,6 +13,7 @@
 //                      64-pair row, prefix over the 16 rows of the chunk) -> sorted_ids
 #include "device_common.h"
 #include "launch.h"
+#include "route_align_dev.h"
 
 namespace qmoe {
 
@@ -158,73 +159,14 @@ __global__ __launch_bounds__(256) void k_align_scatter(const int32_t *__restrict
 }
 
 // Single-workgroup path for P <= 1024 pairs and E <= 512 (decode): histogram, scan, sentinels and the
-// stable scatter in one launch.  16 waves; wave w owns row w (pairs [64w, 64w+64)).
+// stable scatter in one launch of 1024 threads.
 __global__ __launch_bounds__(1024) void k_align_small(const int32_t *__restrict__ ids, int P, int E, int BM,
                                                       int cap, int32_t *__restrict__ sorted_ids,
                                                       int32_t *__restrict__ block_expert,
                                                       int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
                                                       int32_t *__restrict__ total_padded) {
   extern __shared__ int32_t lds[];  // rowcnt [16][E], then start [E]
-  int32_t *rowcnt = lds;
-  int32_t *start_of = lds + 16 * E;
-  __shared__ int32_t wsum[16];
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < 16 * E; i += blockDim.x) rowcnt[i] = 0;
-  __syncthreads();
-  int nbits = 0;
-  while ((1 << nbits) < E) nbits++;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int f = wave * 64 + lane;
-  int e = f < P ? ids[f] : -1;
-  if (e < 0 || e >= E) e = -1;
-  uint64_t peers = __ballot(e >= 0);
-  for (int bit = 0; bit < nbits; bit++) {
-    const uint64_t m = __ballot(e >= 0 && ((e >> bit) & 1));
-    peers &= ((e >> bit) & 1) ? m : ~m;
-  }
-  const int rank = __popcll(peers & below);
-  if (e >= 0 && rank == 0) rowcnt[wave * E + e] = __popcll(peers);
-  __syncthreads();
-  // per expert: exclusive prefix over the 16 rows and the total count (thread x owns x, x+1024, ...)
-  int run = 0;
-  const int x = threadIdx.x;
-  if (x < E) {
-    for (int rr = 0; rr < 16; rr++) {
-      const int v = rowcnt[rr * E + x];
-      rowcnt[rr * E + x] = run;
-      run += v;
-    }
-    counts[x] = run;
-  }
-  const int padded = x < E ? (run + BM - 1) / BM * BM : 0;
-  int inc = padded;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(inc, off);
-    if (lane >= off) inc += o;
-  }
-  if (lane == 63) wsum[wave] = inc;
-  __syncthreads();
-  int wbase = 0, total = 0;
-  for (int w = 0; w < 16; w++) {
-    if (w < wave) wbase += wsum[w];
-    total += wsum[w];
-  }
-  const int start = wbase + inc - padded;
-  if (x < E) {
-    start_of[x] = start;
-    offsets[x] = start;
-    for (int b = start / BM; b < (start + padded) / BM; b++) block_expert[b] = x;
-    for (int p = start + run; p < start + padded; p++) sorted_ids[p] = P;
-  }
-  if (x == 0) {
-    offsets[E] = total;
-    total_padded[0] = total;
-  }
-  for (int b = total / BM + x; b < cap / BM; b += blockDim.x) block_expert[b] = -1;
-  for (int p = total + x; p < cap; p += blockDim.x) sorted_ids[p] = P;
-  __syncthreads();
-  if (e >= 0) sorted_ids[start_of[e] + rowcnt[wave * E + e] + rank] = f;
+  align_block_1024(ids, P, E, BM, cap, sorted_ids, block_expert, counts, offsets, total_padded, lds);
 }
 
 hipError_t launch_align(const int32_t *ids, int T, int k, int E, int BM, int cap, int32_t *sorted_ids,

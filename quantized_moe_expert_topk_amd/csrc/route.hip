@@ -14,6 +14,7 @@
 //                     wave-wide (value, lower index) maximum built from DPP row steps.
 #include "device_common.h"
 #include "launch.h"
+#include "route_align_dev.h"
 
 namespace qmoe {
 
@@ -29,24 +30,10 @@ __global__ __launch_bounds__(256) void k_router_partial(const uint16_t *__restri
   const int t0 = blockIdx.y * 16, e0 = blockIdx.x * 64 + wave * 16;
   if (e0 >= E) return;
   const int ks = blockIdx.z;
-  const int kbeg = ks * kchunk, kend = kbeg + kchunk;
-  const int ta = t0 + r, eb = e0 + r;
-  const bool va = ta < T, vb = eb < E;
-  const uint4 *xa = reinterpret_cast<const uint4 *>(x + (size_t)(va ? ta : 0) * H);
-  const uint4 *wb = reinterpret_cast<const uint4 *>(w + (size_t)(vb ? eb : 0) * H);
-  f32x4_t acc = zero4();
-  for (int kc = kbeg; kc < kend; kc += 128) {
-    const int q = (kc + 32 * g) >> 3;  // uint4 index (8 bf16 each)
-    frag8 a[4], b[4];
-#pragma unroll
-    for (int s = 0; s < 4; s++) {
-      a[s].q = va ? xa[q + s] : make_uint4(0, 0, 0, 0);
-      b[s].q = vb ? wb[q + s] : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int s = 0; s < 4; s++) acc = mfma_bf16(a[s], b[s], acc);
-  }
-  if (vb) {
+  const int kbeg = ks * kchunk;
+  const f32x4_t acc = router_wave_partial(x, T, H, w, E, t0, e0, kbeg, kbeg + kchunk);
+  const int eb = e0 + r;
+  if (eb < E) {
     const float bv = (bias && ks == 0 && gridDim.z == 1) ? bias[eb] : 0.f;
     float *dst = part + (size_t)ks * T * E;
 #pragma unroll
@@ -58,48 +45,6 @@ __global__ __launch_bounds__(256) void k_router_partial(const uint16_t *__restri
 }
 
 // ---------------------------------------------------------------------------- top-k
-
-// Ordered 64-bit key: larger logit first, then lower index.  Float bits are mapped to an
-// unsigned order (sign flip) in the upper half; the lower half is ~index.
-__device__ __forceinline__ uint64_t rank_key(float v, int idx) {
-  uint32_t u = __float_as_uint(v);
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)u << 32) | (uint32_t)(~(uint32_t)idx);
-}
-
-__device__ __forceinline__ int key_index(uint64_t key) { return (int)(~(uint32_t)key); }
-
-__device__ __forceinline__ float key_value(uint64_t key) {
-  uint32_t u = (uint32_t)(key >> 32);
-  u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
-  return __uint_as_float(u);
-}
-
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_max(uint64_t k) {
-  const uint32_t lo = (uint32_t)k, hi = (uint32_t)(k >> 32);
-  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, 0xF, 0xF, false);
-  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, 0xF, 0xF, false);
-  const uint64_t o = ((uint64_t)ohi << 32) | olo;
-  return o > k ? o : k;
-}
-
-// Wave-wide maximum of the 64-bit key, returned to every lane (uniform).
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
-  k = dpp_max<0xB1>(k);   // quad_perm [1,0,3,2]
-  k = dpp_max<0x4E>(k);   // quad_perm [2,3,0,1]
-  k = dpp_max<0x141>(k);  // row_half_mirror
-  k = dpp_max<0x140>(k);  // row_mirror: every lane now holds its 16-lane row's maximum
-  uint64_t best = 0;
-#pragma unroll
-  for (int row = 0; row < 4; row++) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, 16 * row);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 16 * row);
-    const uint64_t rk = ((uint64_t)hi << 32) | lo;
-    best = rk > best ? rk : best;
-  }
-  return best;
-}
 
 // Four tokens per workgroup.  Phase 1: all threads sum the KS partials of the 4 tokens'
 // logits (fixed order, independent loads), add the bias, write the logits and stage them
@@ -140,52 +85,7 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, in
   }
   __syncthreads();
   const int t = t0 + wave;
-  if (t >= T) return;
-  uint64_t key[NS];
-  float vals[NS];
-#pragma unroll
-  for (int q = 0; q < NS; q++) {
-    const int e = lane + 64 * q;
-    vals[q] = e < E ? lg[wave][e] : -INFINITY;
-    key[q] = e < E ? rank_key(vals[q] != vals[q] ? -INFINITY : vals[q], e) : 0;  // NaN ranks last
-  }
-  // descending sort of the lane's keys (odd-even transposition network)
-#pragma unroll
-  for (int pass = 0; pass < NS; pass++)
-#pragma unroll
-    for (int q = pass & 1; q + 1 < NS; q += 2)
-      if (key[q] < key[q + 1]) {
-        const uint64_t tmp = key[q];
-        key[q] = key[q + 1];
-        key[q + 1] = tmp;
-      }
-  float mine = 0.f, top = 0.f;
-  for (int j = 0; j < k; j++) {
-    const uint64_t best = wave_max_key(key[0]);
-    const int bi = key_index(best);
-    const float bv = key_value(best);
-    if (key[0] == best) {  // keys are unique (index in the low half): exactly one lane
-#pragma unroll
-      for (int q = 0; q + 1 < NS; q++) key[q] = key[q + 1];
-      key[NS - 1] = 0;
-    }
-    if (lane == j) mine = bv;
-    if (j == 0) top = bv;
-    if (lane == 0) ids[(size_t)t * k + j] = bi;
-  }
-  // softmax weights
-  float z;
-  if (renormalize) {
-    z = lane < k ? expf(mine - top) : 0.f;
-  } else {
-    z = 0.f;
-#pragma unroll
-    for (int q = 0; q < NS; q++)
-      if (lane + 64 * q < E) z += expf(vals[q] - top);
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
-  if (lane < k) wts[(size_t)t * k + lane] = expf(mine - top) / z;
+  if (t < T) select_topk<NS>(lg[wave], E, k, renormalize, t, ids, wts);
 }
 
 template <int KSMAX>

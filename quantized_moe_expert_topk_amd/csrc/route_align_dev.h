@@ -1,0 +1,205 @@
+// route_align_dev.h -- device routines shared by the routing kernels (route.hip) and the
+// alignment kernels (align.hip): the per-wave router tile, the per-token top-k selection
+// and the single-workgroup counting sort.  Each kernel that uses them computes exactly what
+// its stand-alone counterpart computes, in the same order.
+#pragma once
+
+#include "device_common.h"
+
+namespace qmoe {
+
+// One wave's split-K router tile: 16 tokens [t0, t0+16) x 16 experts [e0, e0+16) over K
+// [kbeg, kend) of H.  K advances 128 per step: lane group g = l/16 loads the contiguous
+// 32-element run [kc + 32g, kc + 32g + 32) of its row for both operands.  Tokens past T
+// and experts past E read zeros.
+__device__ __forceinline__ f32x4_t router_wave_partial(const uint16_t *__restrict__ x, int T, int H,
+                                                       const uint16_t *__restrict__ w, int E, int t0, int e0,
+                                                       int kbeg, int kend) {
+  const int lane = lane_id(), r = lane & 15, g = lane >> 4;
+  const int ta = t0 + r, eb = e0 + r;
+  const bool va = ta < T, vb = eb < E;
+  const uint4 *xa = reinterpret_cast<const uint4 *>(x + (size_t)(va ? ta : 0) * H);
+  const uint4 *wb = reinterpret_cast<const uint4 *>(w + (size_t)(vb ? eb : 0) * H);
+  f32x4_t acc = zero4();
+  for (int kc = kbeg; kc < kend; kc += 128) {
+    const int q = (kc + 32 * g) >> 3;  // uint4 index (8 bf16 each)
+    frag8 a[4], b[4];
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      a[s].q = va ? xa[q + s] : make_uint4(0, 0, 0, 0);
+      b[s].q = vb ? wb[q + s] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; s++) acc = mfma_bf16(a[s], b[s], acc);
+  }
+  return acc;
+}
+
+// Ordered 64-bit key: larger logit first, then lower index.  Float bits are mapped to an
+// unsigned order (sign flip) in the upper half; the lower half is ~index.
+__device__ __forceinline__ uint64_t rank_key(float v, int idx) {
+  uint32_t u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)(~(uint32_t)idx);
+}
+
+__device__ __forceinline__ int key_index(uint64_t key) { return (int)(~(uint32_t)key); }
+
+__device__ __forceinline__ float key_value(uint64_t key) {
+  uint32_t u = (uint32_t)(key >> 32);
+  u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
+  return __uint_as_float(u);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max(uint64_t k) {
+  const uint32_t lo = (uint32_t)k, hi = (uint32_t)(k >> 32);
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, 0xF, 0xF, false);
+  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, 0xF, 0xF, false);
+  const uint64_t o = ((uint64_t)ohi << 32) | olo;
+  return o > k ? o : k;
+}
+
+// Wave-wide maximum of the 64-bit key, returned to every lane (uniform).
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+  k = dpp_max<0xB1>(k);   // quad_perm [1,0,3,2]
+  k = dpp_max<0x4E>(k);   // quad_perm [2,3,0,1]
+  k = dpp_max<0x141>(k);  // row_half_mirror
+  k = dpp_max<0x140>(k);  // row_mirror: every lane now holds its 16-lane row's maximum
+  uint64_t best = 0;
+#pragma unroll
+  for (int row = 0; row < 4; row++) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, 16 * row);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 16 * row);
+    const uint64_t rk = ((uint64_t)hi << 32) | lo;
+    best = rk > best ? rk : best;
+  }
+  return best;
+}
+
+// Top-k of token t by one wave from its E logits `lg` (any memory; E <= 64 NS): each lane
+// sorts its NS keys (experts l + 64q) descending; each round takes the wave-wide maximum of
+// the lanes' heads and the winning lane shifts its keys.  Writes ids[t*k + j] in rank order
+// and the softmax weights (over the k picks when renormalize, else over all E).
+template <int NS>
+__device__ __forceinline__ void select_topk(const float *lg, int E, int k, int renormalize, int t,
+                                            int32_t *__restrict__ ids, float *__restrict__ wts) {
+  const int lane = lane_id();
+  uint64_t key[NS];
+  float vals[NS];
+#pragma unroll
+  for (int q = 0; q < NS; q++) {
+    const int e = lane + 64 * q;
+    vals[q] = e < E ? lg[e] : -INFINITY;
+    key[q] = e < E ? rank_key(vals[q] != vals[q] ? -INFINITY : vals[q], e) : 0;  // NaN ranks last
+  }
+  // descending sort of the lane's keys (odd-even transposition network)
+#pragma unroll
+  for (int pass = 0; pass < NS; pass++)
+#pragma unroll
+    for (int q = pass & 1; q + 1 < NS; q += 2)
+      if (key[q] < key[q + 1]) {
+        const uint64_t tmp = key[q];
+        key[q] = key[q + 1];
+        key[q + 1] = tmp;
+      }
+  float mine = 0.f, top = 0.f;
+  for (int j = 0; j < k; j++) {
+    const uint64_t best = wave_max_key(key[0]);
+    const int bi = key_index(best);
+    const float bv = key_value(best);
+    if (key[0] == best) {  // keys are unique (index in the low half): exactly one lane
+#pragma unroll
+      for (int q = 0; q + 1 < NS; q++) key[q] = key[q + 1];
+      key[NS - 1] = 0;
+    }
+    if (lane == j) mine = bv;
+    if (j == 0) top = bv;
+    if (lane == 0) ids[(size_t)t * k + j] = bi;
+  }
+  // softmax weights
+  float z;
+  if (renormalize) {
+    z = lane < k ? expf(mine - top) : 0.f;
+  } else {
+    z = 0.f;
+#pragma unroll
+    for (int q = 0; q < NS; q++)
+      if (lane + 64 * q < E) z += expf(vals[q] - top);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
+  if (lane < k) wts[(size_t)t * k + lane] = expf(mine - top) / z;
+}
+
+// Stable counting sort of P <= 1024 pairs (ids[f], f < P) over E <= 512 experts by one
+// workgroup of exactly 1024 threads: histogram, scan, sentinels and the stable scatter.
+// Wave w owns row w (pairs [64w, 64w+64)); thread x owns expert x in the scan.
+// lds: 17*E int32 of dynamic LDS (rowcnt [16][E], then start [E]).
+__device__ __forceinline__ void align_block_1024(const int32_t *__restrict__ ids, int P, int E, int BM, int cap,
+                                                 int32_t *__restrict__ sorted_ids, int32_t *__restrict__ block_expert,
+                                                 int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+                                                 int32_t *__restrict__ total_padded, int32_t *lds) {
+  int32_t *rowcnt = lds;
+  int32_t *start_of = lds + 16 * E;
+  __shared__ int32_t wsum[16];
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < 16 * E; i += blockDim.x) rowcnt[i] = 0;
+  __syncthreads();
+  int nbits = 0;
+  while ((1 << nbits) < E) nbits++;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int f = wave * 64 + lane;
+  int e = f < P ? ids[f] : -1;
+  if (e < 0 || e >= E) e = -1;
+  uint64_t peers = __ballot(e >= 0);
+  for (int bit = 0; bit < nbits; bit++) {
+    const uint64_t m = __ballot(e >= 0 && ((e >> bit) & 1));
+    peers &= ((e >> bit) & 1) ? m : ~m;
+  }
+  const int rank = __popcll(peers & below);
+  if (e >= 0 && rank == 0) rowcnt[wave * E + e] = __popcll(peers);
+  __syncthreads();
+  // per expert: exclusive prefix over the 16 rows and the total count
+  int run = 0;
+  const int x = threadIdx.x;
+  if (x < E) {
+    for (int rr = 0; rr < 16; rr++) {
+      const int v = rowcnt[rr * E + x];
+      rowcnt[rr * E + x] = run;
+      run += v;
+    }
+    counts[x] = run;
+  }
+  const int padded = x < E ? (run + BM - 1) / BM * BM : 0;
+  int inc = padded;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(inc, off);
+    if (lane >= off) inc += o;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  int wbase = 0, total = 0;
+  for (int w = 0; w < 16; w++) {
+    if (w < wave) wbase += wsum[w];
+    total += wsum[w];
+  }
+  const int start = wbase + inc - padded;
+  if (x < E) {
+    start_of[x] = start;
+    offsets[x] = start;
+    for (int b = start / BM; b < (start + padded) / BM; b++) block_expert[b] = x;
+    for (int p = start + run; p < start + padded; p++) sorted_ids[p] = P;
+  }
+  if (x == 0) {
+    offsets[E] = total;
+    total_padded[0] = total;
+  }
+  for (int b = total / BM + x; b < cap / BM; b += blockDim.x) block_expert[b] = -1;
+  for (int p = total + x; p < cap; p += blockDim.x) sorted_ids[p] = P;
+  __syncthreads();
+  if (e >= 0) sorted_ids[start_of[e] + rowcnt[wave * E + e] + rank] = f;
+}
+
+}  // namespace qmoe

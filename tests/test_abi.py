@@ -150,3 +150,4 @@ def test_pack_bank_rejects_bad_arguments_before_any_launch(src, dst, code):
     rc, msg = _pack(src, dst)
     assert rc == code, (rc, msg)
     assert msg
+
