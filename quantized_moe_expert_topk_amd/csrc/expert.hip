@@ -90,6 +90,18 @@ __device__ __forceinline__ void decode_nvfp4(const uint4 &c, uint32_t s0, uint32
   fp4x8_mul_to_bf16(c.w, f1, b[3]);
 }
 
+//   NVFP4 to f16: the two e4m3 scales (low 16 bits of sc) become one f16 pair, and each
+//   half multiplies its 16 codes with packed f16 multiplies (1 VALU per weight, against 2 for
+//   the f32 path above)
+__device__ __forceinline__ void decode_nvfp4_f16(const uint4 &c, uint32_t sc, frag8 (&b)[4]) {
+  const f16x2_t s = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, false);
+  const f16x2_t s0 = __builtin_shufflevector(s, s, 0, 0), s1 = __builtin_shufflevector(s, s, 1, 1);
+  fp4x8_mul_to_f16(c.x, s0, b[0]);
+  fp4x8_mul_to_f16(c.y, s0, b[1]);
+  fp4x8_mul_to_f16(c.z, s1, b[2]);
+  fp4x8_mul_to_f16(c.w, s1, b[3]);
+}
+
 __device__ __forceinline__ void decode_mxfp4(const uint4 &c, uint32_t e8, frag8 (&b)[4]) {
   const float p = e8m0_to_f32(e8);
   fp4x8_pow2_to_bf16(c.x, p, b[0]);
@@ -162,10 +174,11 @@ __device__ __forceinline__ uint32_t scale_tile_off(uint32_t row, uint32_t K) {
 //              tile in this layout) are fetched with 16-byte loads issued before the first
 //              group's weight loads, staged there and read back per lane.  Shorter runs
 //              (lsc unused) load each lane's SP scale bytes per step and tile.
-template <int FMT, int NT, int COUNT>
+template <int FMT, int NT, int COUNT, bool F16 = false>
 __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FMT> &m, const uint32_t (&rows)[NT],
                                         int b_k0, int kw0, int kvalid, int g, f32x4_t (&acc)[NT],
                                         uint8_t *lsc = nullptr) {
+  static_assert(!F16 || FMT == MOE_FMT_NVFP4, "the f16 path is for NVFP4 weights");
   constexpr bool FP4 = FMT != MOE_FMT_FP8_BLOCK128;
   constexpr int NPF = FP4 ? 2 : 1;
   constexpr int SP = FMT == MOE_FMT_NVFP4 ? 2 : 1;
@@ -255,11 +268,18 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
       const bool v1 = 128 * i + 64 + 16 * g < kvalid;          // FP8 second half
       frag8 av[4];
 #pragma unroll
-      for (int q = 0; q < 4; q++) av[q].q = ar[ii].q[q];
+      for (int q = 0; q < 4; q++) {
+        if constexpr (F16)
+          bf16x8_to_f16(ar[ii].q[q], av[q]);  // once per chunk, shared by the NT tiles
+        else
+          av[q].q = ar[ii].q[q];
+      }
 #pragma unroll
       for (int t = 0; t < NT; t++) {
         frag8 bv[4];
-        if constexpr (FMT == MOE_FMT_NVFP4) {
+        if constexpr (F16) {
+          decode_nvfp4_f16(c0[ii][t], lsv[ii][t], bv);
+        } else if constexpr (FMT == MOE_FMT_NVFP4) {
           decode_nvfp4(c0[ii][t], lsv[ii][t] & 0xFFu, (lsv[ii][t] >> 8) & 0xFFu, bv);
         } else if constexpr (FMT == MOE_FMT_MXFP4_E8M0) {
           decode_mxfp4(c0[ii][t], lsv[ii][t] & 0xFFu, bv);
@@ -281,6 +301,9 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
           for (int q = 0; q < 4; q++) tmp = mfma_bf16(av[q], bv[q], tmp);
 #pragma unroll
           for (int j = 0; j < 4; j++) acc[t][j] += bs[ii][t] * tmp[j];
+        } else if constexpr (F16) {
+#pragma unroll
+          for (int q = 0; q < 4; q++) acc[t] = mfma_f16(av[q], bv[q], acc[t]);
         } else {
 #pragma unroll
           for (int q = 0; q < 4; q++) acc[t] = mfma_bf16(av[q], bv[q], acc[t]);
@@ -288,6 +311,18 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
       }
     }
   }
+}
+
+// True (wave-uniform) if any lane holds a non-finite accumulator: after an f16 run that means
+// an activation beyond the f16 range (or a non-finite input), and the run is redone in bf16.
+template <int NT>
+__device__ __forceinline__ bool any_nonfinite(const f32x4_t (&acc)[NT]) {
+  bool bad = false;
+#pragma unroll
+  for (int t = 0; t < NT; t++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) bad |= !__builtin_isfinite(acc[t][j]);
+  return __ballot(bad) != 0;
 }
 
 // An activation matrix [rows, K] carried as two e4m3 planes (hi, lo) with an e8m0 scale per
@@ -511,9 +546,21 @@ __global__ __launch_bounds__(64 * KW, kMinWaves) void k_gate_up(GateUpArgs a) {
   } else {
     const rsrc_t ra = make_rsrc(a.x, (uint32_t)a.T * H * 2);
     const uint32_t a_row = tok >= 0 ? (uint32_t)tok * H * 2 : 0x80000000u;
-    if (wave < a.kwaves)
+    if (wave < a.kwaves) {
+      // NVFP4: f16 operands (exact weights, x exact up to 65504); a wave whose x overflows
+      // f16 redoes its K range with bf16 operands
+      constexpr bool F16 = FMT == MOE_FMT_NVFP4;
       for (int kk = 0; kk < kw; kk += 128 * COUNT)
-        mma_run<FMT, 2 * GT, COUNT>(ra, a_row, m, rows, 0, wave * kw + kk, kw - kk, g, acc, wsc);
+        mma_run<FMT, 2 * GT, COUNT, F16>(ra, a_row, m, rows, 0, wave * kw + kk, kw - kk, g, acc, wsc);
+      if constexpr (F16) {
+        if (any_nonfinite(acc)) {  // rare: one step at a time, few registers
+#pragma unroll
+          for (int t = 0; t < 2 * GT; t++) acc[t] = zero4();
+          for (int kk = 0; kk < kw; kk += 128)
+            mma_run<FMT, 2 * GT, 1>(ra, a_row, m, rows, 0, wave * kw + kk, kw - kk, g, acc);
+        }
+      }
+    }
   }
 #pragma unroll
   for (int t = 0; t < 2 * GT; t++)
@@ -647,8 +694,17 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
   } else {
     const rsrc_t ra = make_rsrc(a.h, (uint32_t)a.h_rows * Il * 2);
     const uint32_t a_row = real ? (uint32_t)(p0 + r) * Il * 2 : 0x80000000u;
+    constexpr bool F16 = FMT == MOE_FMT_NVFP4;  // as in gate_up: f16 operands, bf16 redo on overflow
     for (int kw0 = 0; kw0 < Il; kw0 += 128 * COUNT)
-      mma_run<FMT, DNT, COUNT>(ra, a_row, m, rows, a.lo, kw0, Il - kw0, g, acc, wsc);
+      mma_run<FMT, DNT, COUNT, F16>(ra, a_row, m, rows, a.lo, kw0, Il - kw0, g, acc, wsc);
+    if constexpr (F16) {
+      if (any_nonfinite(acc)) {  // rare: one step at a time, few registers
+#pragma unroll
+        for (int t = 0; t < DNT; t++) acc[t] = zero4();
+        for (int kw0 = 0; kw0 < Il; kw0 += 128)
+          mma_run<FMT, DNT, 1>(ra, a_row, m, rows, a.lo, kw0, Il - kw0, g, acc);
+      }
+    }
   }
 #pragma unroll
   for (int j = 0; j < 4; j++) {

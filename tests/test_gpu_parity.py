@@ -220,6 +220,24 @@ def test_expert_forward_matches_oracle(cid, T, sl):
     check_close(f"cfg{cid} T={T} slice=[{lo},{hi})", got, ref)
 
 
+def test_f16_overflow_tokens_redo_in_bf16():
+    """NVFP4 decode runs its matrix-core operands in f16; tokens whose activations exceed the
+    f16 range (two rows of x scaled by 2^16, so h overflows too) make the waves that see them
+    redo their work in bf16, in gate_up and in down.  Both the scaled rows and the others must
+    match the oracle."""
+    inp, r = inputs_for(2, 8)
+    x = inp.x.copy()
+    rows = [0, 5]
+    big = (x[rows].astype(np.uint32) << 16).view(np.float32) * np.float32(65536.0)  # exact in bf16
+    x[rows] = (big.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.abs(big).max() > 65504
+    ref = O.expert_forward(inp.routed, inp.shared, x, r["ids"], r["w"], 0, 256)
+    got = _forward_gpu(dataclasses.replace(inp, x=x), r["ids"], r["w"], 0, 256, banks=dev_banks(inp))
+    rest = [t for t in range(8) if t not in rows]
+    check_close("f16 overflow rows", got[rows], ref[rows])
+    check_close("other rows", got[rest], ref[rest])
+
+
 @pytest.mark.parametrize("bm", [16, 32, 64, 128])
 def test_expert_forward_any_block_m(bm):
     inp, r = inputs_for(2, 64)
