@@ -720,43 +720,51 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
 // ---------------------------------------------------------------------------- combine
 
 // out[t] = sum_j Y[t*k + j] + Y[T*k + t] (shared), in this order, in fp32.  Y rows are fp32
-// (streaming kernels) or bf16 (tiled kernels); a thread owns 8 consecutive columns.
+// (streaming kernels) or bf16 (tiled kernels); a thread owns 4 consecutive columns (H % 128 == 0).
 template <bool YBF16>
 __global__ __launch_bounds__(256) void k_combine(const void *__restrict__ Yv, int T, int k, int H, int has_shared,
                                                  void *__restrict__ out, int out_bf16) {
   const int t = blockIdx.y;
-  const int n = (blockIdx.x * 256 + threadIdx.x) * 8;
+  const int n = (blockIdx.x * 256 + threadIdx.x) * 4;  // 4 columns per thread
   if (n >= H) return;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  auto add_row = [&](size_t row) {
-    if constexpr (YBF16) {
-      const uint4 v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(Yv) + row * H + n);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  const int nrows = k + (has_shared ? 1 : 0);  // the token's k pair rows, then its shared row
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < nrows; j0 += 8) {
+    // up to 8 rows loaded before any is added (all in flight), then summed in row order
+    float v[8][4];
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
-        acc[2 * q] += __uint_as_float(w[q] << 16);
-        acc[2 * q + 1] += __uint_as_float(w[q] & 0xFFFF0000u);
+    for (int u = 0; u < 8; u++) {
+      const int j = j0 + u;
+      const size_t row = j < k ? (size_t)t * k + j : (size_t)T * k + t;
+      if (j < nrows) {
+        if constexpr (YBF16) {
+          const uint2 w = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(Yv) + row * H + n);
+          v[u][0] = __uint_as_float(w.x << 16);
+          v[u][1] = __uint_as_float(w.x & 0xFFFF0000u);
+          v[u][2] = __uint_as_float(w.y << 16);
+          v[u][3] = __uint_as_float(w.y & 0xFFFF0000u);
+        } else {
+          const float4 w = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(Yv) + row * H + n);
+          v[u][0] = w.x;
+          v[u][1] = w.y;
+          v[u][2] = w.z;
+          v[u][3] = w.w;
+        }
       }
-    } else {
-      const float *y = reinterpret_cast<const float *>(Yv) + row * H + n;
-      const float4 v0 = *reinterpret_cast<const float4 *>(y), v1 = *reinterpret_cast<const float4 *>(y + 4);
-      acc[0] += v0.x; acc[1] += v0.y; acc[2] += v0.z; acc[3] += v0.w;
-      acc[4] += v1.x; acc[5] += v1.y; acc[6] += v1.z; acc[7] += v1.w;
     }
-  };
-  for (int j = 0; j < k; j++) add_row((size_t)t * k + j);
-  if (has_shared) add_row((size_t)T * k + t);
+#pragma unroll
+    for (int u = 0; u < 8; u++)
+      if (j0 + u < nrows)
+#pragma unroll
+        for (int c = 0; c < 4; c++) acc[c] += v[u][c];
+  }
   if (out_bf16) {
-    uint4 pk;
-    pk.x = (uint32_t)bf16_bits(acc[0]) | ((uint32_t)bf16_bits(acc[1]) << 16);
-    pk.y = (uint32_t)bf16_bits(acc[2]) | ((uint32_t)bf16_bits(acc[3]) << 16);
-    pk.z = (uint32_t)bf16_bits(acc[4]) | ((uint32_t)bf16_bits(acc[5]) << 16);
-    pk.w = (uint32_t)bf16_bits(acc[6]) | ((uint32_t)bf16_bits(acc[7]) << 16);
-    *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out) + (size_t)t * H + n) = pk;
+    const uint2 pk = make_uint2((uint32_t)bf16_bits(acc[0]) | ((uint32_t)bf16_bits(acc[1]) << 16),
+                                (uint32_t)bf16_bits(acc[2]) | ((uint32_t)bf16_bits(acc[3]) << 16));
+    *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(out) + (size_t)t * H + n) = pk;
   } else {
-    float *o = reinterpret_cast<float *>(out) + (size_t)t * H + n;
-    *reinterpret_cast<float4 *>(o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    *reinterpret_cast<float4 *>(o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    *reinterpret_cast<float4 *>(reinterpret_cast<float *>(out) + (size_t)t * H + n) =
+        make_float4(acc[0], acc[1], acc[2], acc[3]);
   }
 }
 
@@ -830,7 +838,7 @@ hipError_t launch_act_mx8(const uint16_t *x, int rows, int K, uint8_t *q, uint8_
 
 hipError_t launch_combine(const void *Y, bool y_bf16, int T, int k, int H, int has_shared, void *out, int out_bf16,
                           hipStream_t s) {
-  dim3 grid((H / 8 + 255) / 256, T);
+  dim3 grid((H / 4 + 255) / 256, T);
   if (y_bf16)
     hipLaunchKernelGGL(k_combine<true>, grid, dim3(256), 0, s, Y, T, k, H, has_shared, out, out_bf16);
   else

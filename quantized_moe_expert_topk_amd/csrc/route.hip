@@ -109,6 +109,8 @@ static hipError_t launch_topk_ns(const float *part, int KS, int T, int E, const 
                                  float *logits_out, int32_t *ids, float *wts, hipStream_t s) {
   if (KS <= 1)
     launch_topk_ks<1>(part, 1, T, E, bias, k, renormalize, logits_out, ids, wts, s);
+  else if (KS <= 8)
+    launch_topk_ks<8>(part, KS, T, E, bias, k, renormalize, logits_out, ids, wts, s);
   else
     launch_topk_ks<16>(part, KS, T, E, bias, k, renormalize, logits_out, ids, wts, s);
   return hipGetLastError();

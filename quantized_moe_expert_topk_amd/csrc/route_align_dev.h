@@ -21,16 +21,23 @@ __device__ __forceinline__ f32x4_t router_wave_partial(const uint16_t *__restric
   const uint4 *xa = reinterpret_cast<const uint4 *>(x + (size_t)(va ? ta : 0) * H);
   const uint4 *wb = reinterpret_cast<const uint4 *>(w + (size_t)(vb ? eb : 0) * H);
   f32x4_t acc = zero4();
-  for (int kc = kbeg; kc < kend; kc += 128) {
-    const int q = (kc + 32 * g) >> 3;  // uint4 index (8 bf16 each)
-    frag8 a[4], b[4];
+  for (int kc = kbeg; kc < kend; kc += 256) {  // two steps' loads in flight, then their MFMAs in order
+    frag8 a[2][4], b[2][4];
 #pragma unroll
-    for (int s = 0; s < 4; s++) {
-      a[s].q = va ? xa[q + s] : make_uint4(0, 0, 0, 0);
-      b[s].q = vb ? wb[q + s] : make_uint4(0, 0, 0, 0);
+    for (int st = 0; st < 2; st++) {
+      const bool in = kc + 128 * st < kend;
+      const int q = (kc + 128 * st + 32 * g) >> 3;  // uint4 index (8 bf16 each)
+#pragma unroll
+      for (int s = 0; s < 4; s++) {
+        a[st][s].q = va && in ? xa[q + s] : make_uint4(0, 0, 0, 0);
+        b[st][s].q = vb && in ? wb[q + s] : make_uint4(0, 0, 0, 0);
+      }
     }
 #pragma unroll
-    for (int s = 0; s < 4; s++) acc = mfma_bf16(a[s], b[s], acc);
+    for (int st = 0; st < 2; st++)
+      if (kc + 128 * st < kend)
+#pragma unroll
+        for (int s = 0; s < 4; s++) acc = mfma_bf16(a[st][s], b[st][s], acc);
   }
   return acc;
 }
@@ -144,13 +151,13 @@ __device__ __forceinline__ void align_block_1024(const int32_t *__restrict__ ids
   int32_t *start_of = lds + 16 * E;
   __shared__ int32_t wsum[16];
   const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int f = wave * 64 + lane;
+  int e = f < P ? ids[f] : -1;  // in flight while the counters are cleared
   for (int i = threadIdx.x; i < 16 * E; i += blockDim.x) rowcnt[i] = 0;
   __syncthreads();
   int nbits = 0;
   while ((1 << nbits) < E) nbits++;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int f = wave * 64 + lane;
-  int e = f < P ? ids[f] : -1;
   if (e < 0 || e >= E) e = -1;
   uint64_t peers = __ballot(e >= 0);
   for (int bit = 0; bit < nbits; bit++) {
@@ -164,10 +171,13 @@ __device__ __forceinline__ void align_block_1024(const int32_t *__restrict__ ids
   int run = 0;
   const int x = threadIdx.x;
   if (x < E) {
+    int v[16];  // all 16 reads before the writes
+#pragma unroll
+    for (int rr = 0; rr < 16; rr++) v[rr] = rowcnt[rr * E + x];
+#pragma unroll
     for (int rr = 0; rr < 16; rr++) {
-      const int v = rowcnt[rr * E + x];
       rowcnt[rr * E + x] = run;
-      run += v;
+      run += v[rr];
     }
     counts[x] = run;
   }
