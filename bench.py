@@ -36,8 +36,9 @@ WORKLOADS = {
     3: (8192, (0, 512), [(8192, (0, 256))]),
     4: (64, (0, 256), [(1, (0, 256)), (4096, (0, 256))]),
     5: (16, (0, 1024), [(1, (0, 1024)), (256, (0, 1024))]),
+    6: (64, (0, 256), [(1, (0, 256)), (8192, (0, 512))]),
 }
-INSTANCES = {2: 3, 3: 3, 4: 2, 5: 1}   # layer instances rotated (>= 1 GiB of banks for 2-4)
+INSTANCES = {2: 3, 3: 3, 4: 2, 5: 1, 6: 1}   # layer instances rotated (>= 1 GiB of banks for 2-4, 6)
 BATCHES = 4                            # token batches rotated
 
 
@@ -51,6 +52,8 @@ def expert_slice_bytes(fmt, H, Il):
         return 3 * Il * H * 9 // 16 + 8 * Il + 4 * H
     if fmt == "fp8blk":
         return 3 * Il * H + 4 * (2 * Il * H + H * Il) // 16384
+    if fmt == "bf16":
+        return 3 * Il * H * 2
     return 3 * Il * H * 17 // 32
 
 
@@ -59,6 +62,8 @@ def gate_up_slice_bytes(fmt, H, Il):
         return 2 * Il * H * 9 // 16 + 8 * Il
     if fmt == "fp8blk":
         return 2 * Il * H + 4 * (2 * Il * H) // 16384
+    if fmt == "bf16":
+        return 2 * Il * H * 2
     return 2 * Il * H * 17 // 32
 
 

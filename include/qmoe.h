@@ -58,18 +58,22 @@ extern "C" {
  *   MOE_FMT_MXFP4_E8M0: packed e2m1 codes with an e8m0 scale per 32 consecutive K
  *     elements; W = e2m1 * 2^(e8m0 - 127) (the DeepSeek-V4 routed FP4 experts' 32-element
  *     scale blocks, PR #70 "Checkpoint loading"; issue #62 "What it touches" item 2).
+ *   MOE_FMT_BF16: unquantized bf16 stacked experts, the first format the pages stage through
+ *     the same slicing (issue #62 "Suggested staging" item 1; PR #637 "What is sharded": bf16
+ *     stacked experts are split like the quantized ones); no scales or globals.
  * Packed FP4 stores two codes per byte, the even K index in the low nibble. */
 typedef enum {
   MOE_FMT_NVFP4 = 1,
   MOE_FMT_FP8_BLOCK128 = 2,
-  MOE_FMT_MXFP4_E8M0 = 3
+  MOE_FMT_MXFP4_E8M0 = 3,
+  MOE_FMT_BF16 = 4
 } moe_format;
 
 /* Byte order of a bank's weight codes and FP4 scales (moe_bank.layout).
  *   MOE_LAYOUT_ROWS    row-major, as stored by the checkpoint (the shapes below).
  *   MOE_LAYOUT_TILE16  the order the expert kernels read, made by moe_pack_bank: every
  *     group of 16 consecutive rows of a matrix (rows of all experts counted together) is
- *     stored piece-major.  For codes the piece is 16 bytes (32 FP4 or 16 FP8 elements):
+ *     stored piece-major.  For codes the piece is 16 bytes (32 FP4, 16 FP8 or 8 BF16 elements):
  *     byte b of row r sits at (r/16)*16*P + (b/16)*256 + (r%16)*16 + b%16, P = bytes per
  *     row.  FP4 scales use the scale bytes of one 32-element piece as their unit
  *     (NVFP4 2 bytes, MXFP4 1): byte j of row r sits at
@@ -84,14 +88,15 @@ typedef enum {
 /* One bank of E experts, full-I layout, expert-major and row-major per matrix
  * (issue #520 patch, nvfp4.py layout()/pack(); issue #62 "What it touches" item 1):
  *   gate_up        [E, 2I, H] weights: gate rows [0, I), up rows [I, 2I); K = H.
- *                  NVFP4/MXFP4: u8 [E, 2I, H/2]; FP8_BLOCK128: u8 e4m3 [E, 2I, H].
+ *                  NVFP4/MXFP4: u8 [E, 2I, H/2]; FP8_BLOCK128: u8 e4m3 [E, 2I, H];
+ *                  BF16: bf16 [E, 2I, H].
  *   gate_up_scale  NVFP4: u8 e4m3 [E, 2I, H/16]; FP8_BLOCK128: f32 [E, 2I/128, H/128];
- *                  MXFP4: u8 e8m0 [E, 2I, H/32].
+ *                  MXFP4: u8 e8m0 [E, 2I, H/32]; BF16: unused (NULL allowed).
  *   gate_up_global NVFP4 only: f32 [E, 2I] (per output row); NULL otherwise.
  *   down           [E, H, I] weights; K = I.  NVFP4/MXFP4: u8 [E, H, I/2];
- *                  FP8_BLOCK128: u8 e4m3 [E, H, I].
+ *                  FP8_BLOCK128: u8 e4m3 [E, H, I]; BF16: bf16 [E, H, I].
  *   down_scale     NVFP4: u8 e4m3 [E, H, I/16]; FP8_BLOCK128: f32 [E, H/128, I/128];
- *                  MXFP4: u8 e8m0 [E, H, I/32].
+ *                  MXFP4: u8 e8m0 [E, H, I/32]; BF16: unused (NULL allowed).
  *   down_global    NVFP4 only: f32 [E, H]; NULL otherwise.
  * A rank that stores only its own slice passes that storage as a bank with I = hi - lo
  * and the slice [0, I) (PR #70: TP=1 is the identity layout).
@@ -117,7 +122,8 @@ typedef struct {
  *         them; dst's FP8_BLOCK128 scales and NVFP4 globals, when they are other buffers
  *         than src's, receive a plain copy.  The caller owns both banks' storage.
  * Requires 16 | 2I, 16 | H and whole 16-byte code pieces per row (H and I multiples of 32
- * for the FP4 formats, of 16 for FP8).  Enqueued on `stream`; no host synchronisation. */
+ * for the FP4 formats, of 16 for FP8, of 8 for BF16).  Enqueued on `stream`; no host
+ * synchronisation. */
 int moe_pack_bank(const moe_bank *src, const moe_bank *dst, void *stream);
 
 /* ------------------------------------------------------------------ routing */
@@ -220,13 +226,13 @@ size_t moe_workspace_bytes(const moe_bank *routed, const moe_bank *shared, int T
  *   routed      E-expert bank; shared: NULL or a 1-expert bank of the same format, H and I;
  *               both in MOE_LAYOUT_TILE16 (moe_pack_bank), else MOE_ERR_UNSUPPORTED.
  *   x_bf16      [T, H] bf16; topk_w [T, k] f32; al: the moe_align output for these ids.
- *   slice_lo/hi multiples of the format block (NVFP4 16, MXFP4 32, FP8_BLOCK128 128), with
+ *   slice_lo/hi multiples of the format block (NVFP4 16, MXFP4 32, FP8_BLOCK128 128, BF16 1), with
  *               0 <= lo < hi <= I (issue #62 "What it touches" item 2; PR #70 div_tp(...,
  *               multiple_of=128)).  The kernels additionally need (hi - lo) % 32 == 0.
  *   out         [T, H] f32 (out_dtype MOE_OUT_F32) or bf16 (MOE_OUT_BF16), overwritten.
  *   workspace   >= moe_workspace_bytes(...) bytes of device memory.
  * Experts that received no tokens are never read.  The align block size picks the kernels:
- * al->block_m a multiple of 128 runs NVFP4 and FP8_BLOCK128 on LDS-tiled GEMMs that reuse
+ * al->block_m a multiple of 128 runs NVFP4, FP8_BLOCK128 and BF16 on LDS-tiled GEMMs that reuse
  * each weight tile across 128 pair rows (for many tokens per expert); other block sizes,
  * and MXFP4, run the streaming kernels that read each selected weight byte once per
  * 16-row block (for few tokens per expert).  Both compute the same result, except that the

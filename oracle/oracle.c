@@ -100,6 +100,8 @@ double oracle_weight_gate_up(const oracle_bank *b, int e, int r, int c) {
     const float *si = (const float *)b->gate_up_scale + (size_t)e * (2 * I / 128) * (H / 128);
     return oracle_e4m3fn(code) * (double)si[(r / 128) * (H / 128) + c / 128];
   }
+  if (b->fmt == ORACLE_BF16) /* unquantized bf16 stacked experts (issue #62 "Suggested staging" 1) */
+    return oracle_bf16(((const uint16_t *)b->gate_up)[((size_t)e * 2 * I + r) * (size_t)H + c]);
   /* MXFP4 */
   const uint8_t *codes = b->gate_up + ((size_t)e * 2 * I + r) * (size_t)(H / 2);
   const uint8_t *sc = (const uint8_t *)b->gate_up_scale + ((size_t)e * 2 * I + r) * (size_t)(H / 32);
@@ -120,6 +122,8 @@ double oracle_weight_down(const oracle_bank *b, int e, int n, int i) {
     const float *si = (const float *)b->down_scale + (size_t)e * (H / 128) * (I / 128);
     return oracle_e4m3fn(code) * (double)si[(n / 128) * (I / 128) + i / 128];
   }
+  if (b->fmt == ORACLE_BF16)
+    return oracle_bf16(((const uint16_t *)b->down)[((size_t)e * H + n) * (size_t)I + i]);
   const uint8_t *codes = b->down + ((size_t)e * H + n) * (size_t)(I / 2);
   const uint8_t *sc = (const uint8_t *)b->down_scale + ((size_t)e * H + n) * (size_t)(I / 32);
   return oracle_e2m1(nibble(codes, i)) * oracle_e8m0(sc[i / 32]);

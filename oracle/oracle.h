@@ -8,6 +8,7 @@
 #define ORACLE_NVFP4 1
 #define ORACLE_FP8BLK 2
 #define ORACLE_MXFP4 3
+#define ORACLE_BF16 4
 
 /* One bank of E experts in the full-I layout (expert-major, row-major per matrix).
  *   NVFP4 : gate_up u8 [E,2I,H/2], gate_up_scale e4m3 [E,2I,H/16], gate_up_global f32 [E,2I],
@@ -15,7 +16,9 @@
  *   FP8BLK: gate_up e4m3 [E,2I,H], gate_up_scale f32 [E,2I/128,H/128],
  *           down e4m3 [E,H,I], down_scale f32 [E,H/128,I/128]
  *   MXFP4 : gate_up u8 [E,2I,H/2], gate_up_scale e8m0 [E,2I,H/32],
- *           down u8 [E,H,I/2], down_scale e8m0 [E,H,I/32] */
+ *           down u8 [E,H,I/2], down_scale e8m0 [E,H,I/32]
+ *   BF16  : gate_up bf16 bits [E,2I,H], down bf16 bits [E,H,I] (passed through the u8 pointers);
+ *           no scales or globals */
 typedef struct {
   int fmt, E, H, I;
   const uint8_t *gate_up;

@@ -14,7 +14,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-FMT = {"nvfp4": 1, "fp8blk": 2, "mxfp4": 3}
+FMT = {"nvfp4": 1, "fp8blk": 2, "mxfp4": 3, "bf16": 4}
 
 
 def build(force: bool = False) -> str:

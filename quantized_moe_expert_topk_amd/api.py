@@ -82,7 +82,7 @@ def moe_pack_bank(bank: DeviceBank, stream=None) -> DeviceBank:
     scales and NVFP4 globals are shared with ``bank``).  A packed bank is returned as is."""
     if bank.layout == MOE_LAYOUT_TILE16:
         return bank
-    fp4 = bank.fmt != "fp8blk"
+    fp4 = bank.fmt in ("nvfp4", "mxfp4")  # their scales are reordered too
     dst = DeviceBank(bank.fmt, bank.E, bank.H, bank.I, torch.empty_like(bank.gate_up),
                      torch.empty_like(bank.gate_up_scale) if fp4 else bank.gate_up_scale,
                      torch.empty_like(bank.down), torch.empty_like(bank.down_scale) if fp4 else bank.down_scale,
@@ -233,7 +233,7 @@ def choose_block_m(T: int, k: int, E: int, fmt: str | None = None) -> int:
     number of pairs per expert grows; 128 (the LDS-tiled GEMMs) once experts see enough
     tokens to reuse each weight tile, for the formats those kernels cover."""
     mean = T * k / max(E, 1)
-    if mean >= 32 and fmt in ("nvfp4", "fp8blk"):
+    if mean >= 32 and fmt in ("nvfp4", "fp8blk", "bf16"):
         return 128
     if mean <= 16:
         return 16

@@ -63,6 +63,7 @@ int format_block(int fmt) {
     case MOE_FMT_NVFP4: return 16;
     case MOE_FMT_FP8_BLOCK128: return 128;
     case MOE_FMT_MXFP4_E8M0: return 32;
+    case MOE_FMT_BF16: return 1;
     default: return 0;
   }
 }
@@ -72,6 +73,7 @@ const char *format_name(int fmt) {
     case MOE_FMT_NVFP4: return "NVFP4";
     case MOE_FMT_FP8_BLOCK128: return "FP8_BLOCK128";
     case MOE_FMT_MXFP4_E8M0: return "MXFP4_E8M0";
+    case MOE_FMT_BF16: return "BF16";
     default: return "unknown";
   }
 }
@@ -96,7 +98,7 @@ int check_bank(const moe_bank *b, const char *name) {
   if (b->E < 1 || b->H < 1 || b->I < 1)
     return fail(MOE_ERR_INVALID_ARG, "%s bank: E=%d H=%d I=%d must be positive", name, b->E, b->H, b->I);
   if (b->E > 1024) return fail(MOE_ERR_UNSUPPORTED, "%s bank: E=%d > 1024", name, b->E);
-  if (!b->gate_up || !b->gate_up_scale || !b->down || !b->down_scale)
+  if (!b->gate_up || !b->down || (b->fmt != MOE_FMT_BF16 && (!b->gate_up_scale || !b->down_scale)))
     return fail(MOE_ERR_INVALID_ARG, "%s bank: NULL weight or scale pointer", name);
   if (b->fmt == MOE_FMT_NVFP4 && (!b->gate_up_global || !b->down_global))
     return fail(MOE_ERR_INVALID_ARG, "%s bank: NVFP4 needs gate_up_global and down_global", name);
@@ -125,12 +127,14 @@ struct BankSizes {
 BankSizes bank_sizes(const moe_bank *b) {
   BankSizes z{};
   const size_t E = (size_t)b->E, H = (size_t)b->H, I = (size_t)b->I;
-  const bool fp8 = b->fmt == MOE_FMT_FP8_BLOCK128;
-  z.gu_pitch = (uint32_t)(fp8 ? H : H / 2);
-  z.dn_pitch = (uint32_t)(fp8 ? I : I / 2);
+  const bool fp8 = b->fmt == MOE_FMT_FP8_BLOCK128, bf16 = b->fmt == MOE_FMT_BF16;
+  z.gu_pitch = (uint32_t)(bf16 ? 2 * H : fp8 ? H : H / 2);
+  z.dn_pitch = (uint32_t)(bf16 ? 2 * I : fp8 ? I : I / 2);
   z.gu = E * 2 * I * z.gu_pitch;
   z.dn = E * H * z.dn_pitch;
-  if (fp8) {
+  if (bf16) {
+    z.gus = z.dns = 0;
+  } else if (fp8) {
     z.gus = E * (2 * I / 128) * (H / 128) * 4;
     z.dns = E * (H / 128) * (I / 128) * 4;
   } else {
@@ -473,7 +477,7 @@ int moe_pack_bank(const moe_bank *src, const moe_bank *dst, void *stream) {
     return fail(MOE_ERR_INVALID_ARG, "moe_pack_bank: src and dst differ in fmt, E, H or I");
   if (src->E < 1 || src->H < 1 || src->I < 1)
     return fail(MOE_ERR_INVALID_ARG, "moe_pack_bank: E=%d H=%d I=%d must be positive", src->E, src->H, src->I);
-  const int piece = src->fmt == MOE_FMT_FP8_BLOCK128 ? 16 : 32;  // elements per 16-byte code piece
+  const int piece = src->fmt == MOE_FMT_BF16 ? 8 : src->fmt == MOE_FMT_FP8_BLOCK128 ? 16 : 32;  // per 16-byte piece
   if (src->H % piece || src->I % piece || src->H % 128 || (src->fmt == MOE_FMT_FP8_BLOCK128 && src->I % 128))
     return fail(MOE_ERR_UNSUPPORTED, "moe_pack_bank: H=%d and I=%d need whole %d-element pieces per row", src->H,
                 src->I, piece);
@@ -481,7 +485,7 @@ int moe_pack_bank(const moe_bank *src, const moe_bank *dst, void *stream) {
     return fail(MOE_ERR_UNSUPPORTED, "moe_pack_bank: bank too large");
   const moe_bank *b[2] = {src, dst};
   for (const moe_bank *x : b) {
-    if (!x->gate_up || !x->gate_up_scale || !x->down || !x->down_scale)
+    if (!x->gate_up || !x->down || (x->fmt != MOE_FMT_BF16 && (!x->gate_up_scale || !x->down_scale)))
       return fail(MOE_ERR_INVALID_ARG, "moe_pack_bank: NULL weight or scale pointer");
     if (x->fmt == MOE_FMT_NVFP4 && (!x->gate_up_global || !x->down_global))
       return fail(MOE_ERR_INVALID_ARG, "moe_pack_bank: NVFP4 needs gate_up_global and down_global");
@@ -489,9 +493,9 @@ int moe_pack_bank(const moe_bank *src, const moe_bank *dst, void *stream) {
       return fail(MOE_ERR_INVALID_ARG, "moe_pack_bank: weight codes must be 16-byte aligned");
   }
   const BankSizes z = bank_sizes(src);
-  const bool fp8 = src->fmt == MOE_FMT_FP8_BLOCK128;
+  const bool fp8 = src->fmt == MOE_FMT_FP8_BLOCK128, fp4 = !fp8 && src->fmt != MOE_FMT_BF16;
   if (overlap(src->gate_up, z.gu, dst->gate_up, z.gu) || overlap(src->down, z.dn, dst->down, z.dn) ||
-      (!fp8 && (overlap(src->gate_up_scale, z.gus, dst->gate_up_scale, z.gus) ||
+      (fp4 && (overlap(src->gate_up_scale, z.gus, dst->gate_up_scale, z.gus) ||
                 overlap(src->down_scale, z.dns, dst->down_scale, z.dns))))
     return fail(MOE_ERR_INVALID_ARG, "moe_pack_bank: dst codes or FP4 scales overlap src");
   int rc = check_device();
@@ -504,7 +508,7 @@ int moe_pack_bank(const moe_bank *src, const moe_bank *dst, void *stream) {
   rc = hip_status(qmoe::launch_pack_tile16(src->down, const_cast<void *>(dst->down), E * H, z.dn_pitch, 16, s),
                   "pack launch");
   if (rc) return rc;
-  if (!fp8) {
+  if (fp4) {
     rc = hip_status(qmoe::launch_pack_tile16(src->gate_up_scale, const_cast<void *>(dst->gate_up_scale), E * 2 * I,
                                              z.gus_pitch, z.unit, s), "pack launch");
     if (rc) return rc;

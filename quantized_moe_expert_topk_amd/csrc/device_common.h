@@ -167,6 +167,9 @@ __device__ __forceinline__ WMat<FMT> weight_matrix(const uint8_t *codes, const u
   } else if constexpr (FMT == MOE_FMT_MXFP4_E8M0) {
     m.codes = make_rsrc(codes + (size_t)e * rows * (K / 2), (uint32_t)rows * (K / 2));
     m.scales = make_rsrc(scales + (size_t)e * rows * (K / 32), (uint32_t)rows * (K / 32));
+  } else if constexpr (FMT == MOE_FMT_BF16) {
+    m.codes = make_rsrc(codes + (size_t)e * rows * K * 2, (uint32_t)rows * K * 2);
+    m.scales = m.codes;  // unused
   } else {
     m.codes = make_rsrc(codes + (size_t)e * rows * K, (uint32_t)rows * K);
     m.scales = make_rsrc(scales + (size_t)e * (rows / 128) * (K / 128) * 4, (uint32_t)(rows / 128) * (K / 128) * 4);

@@ -148,7 +148,7 @@ __device__ __forceinline__ uint32_t span_scales(const uint4 &sp, int s, int g) {
 // piece index over the 16 rows of a tile is then one contiguous 1 KB run.
 template <int FMT>
 __device__ __forceinline__ uint32_t code_tile_off(uint32_t row, uint32_t K) {
-  return (row & ~15u) * (FMT == MOE_FMT_FP8_BLOCK128 ? K : K / 2) + (row & 15u) * 16;
+  return (row & ~15u) * (FMT == MOE_FMT_BF16 ? 2 * K : FMT == MOE_FMT_FP8_BLOCK128 ? K : K / 2) + (row & 15u) * 16;
 }
 
 template <int FMT>
@@ -161,7 +161,9 @@ __device__ __forceinline__ uint32_t scale_tile_off(uint32_t row, uint32_t K) {
 // NT weight tiles.  Step i is the 128-wide chunk [kw0 + 128 i, +128).  FP4: lane group
 // g = l/16 takes the 32-element piece [32 g, 32 g + 32) of the step from both operands.
 // FP8: lane group g takes [16 g, 16 g + 16) and [64 + 16 g, +16), so each of the two code
-// loads covers 4 consecutive pieces of every tile row (one 1 KB run per tile).  Either way
+// loads covers 4 consecutive pieces of every tile row (one 1 KB run per tile).  BF16: MFMA q
+// of the step takes [32 q, 32 q + 32), lane group g its 8 elements [32 q + 8 g, +8) (pieces
+// 4q..4q+3: again one 1 KB run per tile and MFMA, no dequantization).  Either way
 // every MFMA stays inside one 128x128 FP8 scale block.  Positions at or past kvalid
 // (relative to kw0) contribute zero and load from clamped in-bounds offsets.  Steps are
 // taken in groups of 2 (FP4) or 1 (FP8) whose loads are all issued before decoding.
@@ -179,7 +181,8 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
                                         int b_k0, int kw0, int kvalid, int g, f32x4_t (&acc)[NT],
                                         uint8_t *lsc = nullptr) {
   static_assert(!F16 || FMT == MOE_FMT_NVFP4, "the f16 path is for NVFP4 weights");
-  constexpr bool FP4 = FMT != MOE_FMT_FP8_BLOCK128;
+  constexpr bool FP4 = FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_MXFP4_E8M0;
+  constexpr bool BF16 = FMT == MOE_FMT_BF16;
   constexpr int NPF = FP4 ? 2 : 1;
   constexpr int SP = FMT == MOE_FMT_NVFP4 ? 2 : 1;
   const uint32_t K = (uint32_t)m.K;
@@ -203,7 +206,7 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
 #pragma unroll
   for (int i0 = 0; i0 < COUNT; i0 += NPF) {
     ARaw ar[NPF];
-    uint4 c0[NPF][NT], c1[NPF][NT];
+    uint4 c0[NPF][NT], c1[NPF][NT], c2[NPF][NT], c3[NPF][NT];
     uint32_t lsv[NPF][NT];
     float bs[NPF][NT];
 #pragma unroll
@@ -222,6 +225,18 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
 #pragma unroll
           for (int t = 0; t < NT; t++)
             lsv[ii][t] = SP == 2 ? buf_load2(m.scales, sb[t] + pc * 32) : buf_load1(m.scales, sb[t] + pc * 16);
+        }
+      } else if constexpr (BF16) {
+        const int kc = kw0 + (128 * i < kvalid ? 128 * i : 0);  // the step
+#pragma unroll
+        for (int q = 0; q < 4; q++) ar[ii].q[q] = buf_load16(ra, a_row + (kc + 32 * q + 8 * g) * 2);
+        const uint32_t pc = (uint32_t)(b_k0 + kc) / 8 + g;
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+          c0[ii][t] = buf_load16(m.codes, cb[t] + pc * 256);
+          c1[ii][t] = buf_load16(m.codes, cb[t] + (pc + 4) * 256);
+          c2[ii][t] = buf_load16(m.codes, cb[t] + (pc + 8) * 256);
+          c3[ii][t] = buf_load16(m.codes, cb[t] + (pc + 12) * 256);
         }
       } else {
         const int kc = kw0 + (128 * i < kvalid ? 128 * i : 0);  // the step
@@ -283,6 +298,11 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
           decode_nvfp4(c0[ii][t], lsv[ii][t] & 0xFFu, (lsv[ii][t] >> 8) & 0xFFu, bv);
         } else if constexpr (FMT == MOE_FMT_MXFP4_E8M0) {
           decode_mxfp4(c0[ii][t], lsv[ii][t] & 0xFFu, bv);
+        } else if constexpr (BF16) {
+          bv[0].q = c0[ii][t];
+          bv[1].q = c1[ii][t];
+          bv[2].q = c2[ii][t];
+          bv[3].q = c3[ii][t];
         } else {
           fp8x8_to_bf16(c0[ii][t].x, c0[ii][t].y, bv[0]);
           fp8x8_to_bf16(c0[ii][t].z, c0[ii][t].w, bv[1]);
@@ -291,6 +311,10 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
         }
         if constexpr (FP4) {
           if (!v0) zero_frags(bv);
+        } else if constexpr (BF16) {  // kvalid is a multiple of 32: per MFMA slot
+#pragma unroll
+          for (int q = 0; q < 4; q++)
+            if (128 * i + 32 * q >= kvalid) bv[q].q = make_uint4(0, 0, 0, 0);
         } else {
           if (!v0) bv[0].q = bv[1].q = make_uint4(0, 0, 0, 0);
           if (!v1) bv[2].q = bv[3].q = make_uint4(0, 0, 0, 0);
@@ -475,7 +499,7 @@ __global__ __launch_bounds__(64 * KW, kMinWaves) void k_gate_up(GateUpArgs a) {
   __shared__ float red[KW][2 * GT][4][64];  // [wave][tile][j][lane]
   __shared__ float hbuf[16][GCOLS + 1];      // MXFP4: the block's h before the plane split
   // FP4: per wave, the scale bytes of the workgroup's 2*GCOLS weight rows over one run
-  __shared__ __attribute__((aligned(16))) uint8_t lsc[FMT == MOE_FMT_FP8_BLOCK128 ? 16 : KW * 2 * GCOLS * (128 * COUNT / (FMT == MOE_FMT_NVFP4 ? 16 : 32))];
+  __shared__ __attribute__((aligned(16))) uint8_t lsc[(FMT == MOE_FMT_FP8_BLOCK128 || FMT == MOE_FMT_BF16) ? 16 : KW * 2 * GCOLS * (128 * COUNT / (FMT == MOE_FMT_NVFP4 ? 16 : 32))];
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int sb = blockIdx.x;
@@ -523,7 +547,7 @@ __global__ __launch_bounds__(64 * KW, kMinWaves) void k_gate_up(GateUpArgs a) {
   // FP4 scales are staged per wave when a run's scale bytes per tile are whole 16-byte
   // pieces (runs of at least 2 steps for NVFP4, 4 for MXFP4); otherwise lanes load theirs
   uint8_t *wsc = nullptr;
-  if constexpr (FMT != MOE_FMT_FP8_BLOCK128) {
+  if constexpr (FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_MXFP4_E8M0) {
     constexpr int sdiv = FMT == MOE_FMT_NVFP4 ? 16 : 32;
     constexpr int RB = 128 * COUNT / sdiv;
     if (RB % 16 == 0) wsc = &lsc[wave * 2 * GCOLS * RB];
@@ -615,7 +639,7 @@ constexpr int DNT = 4;
 template <int FMT, int COUNT>
 __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
   // FP4: per wave, the scale bytes of its 16*DNT weight rows over one run
-  __shared__ __attribute__((aligned(16))) uint8_t lsc[FMT == MOE_FMT_FP8_BLOCK128 ? 16 : 4 * 16 * DNT * (128 * COUNT / (FMT == MOE_FMT_NVFP4 ? 16 : 32))];
+  __shared__ __attribute__((aligned(16))) uint8_t lsc[(FMT == MOE_FMT_FP8_BLOCK128 || FMT == MOE_FMT_BF16) ? 16 : 4 * 16 * DNT * (128 * COUNT / (FMT == MOE_FMT_NVFP4 ? 16 : 32))];
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int sb = blockIdx.x;
@@ -651,7 +675,7 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
   // FP4 scales are staged per wave when a run's scale bytes per tile are whole 16-byte
   // pieces (runs of at least 2 steps for NVFP4, 4 for MXFP4); otherwise lanes load theirs
   uint8_t *wsc = nullptr;
-  if constexpr (FMT != MOE_FMT_FP8_BLOCK128) {
+  if constexpr (FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_MXFP4_E8M0) {
     constexpr int sdiv = FMT == MOE_FMT_NVFP4 ? 16 : 32;
     constexpr int RB = 128 * COUNT / sdiv;
     if (RB % 16 == 0) wsc = &lsc[wave * 16 * DNT * RB];
@@ -771,8 +795,8 @@ __global__ __launch_bounds__(256) void k_combine(const void *__restrict__ Yv, in
 // ---------------------------------------------------------------------------- launchers
 
 // Step count of a K run as a template argument: 1, 2, 4 or 8 (runs are masked past K).
-// Longer K ranges loop over runs; fp8-block and MXFP4 keep runs at 4 steps or fewer, past
-// which their per-step operand registers no longer fit the occupancy target.
+// Longer K ranges loop over runs; fp8-block, MXFP4 and bf16 keep runs at 4 steps or fewer,
+// past which their per-step operand registers no longer fit the occupancy target.
 static int count_class(int fmt, int steps) {
   const int c = steps <= 1 ? 1 : steps <= 2 ? 2 : steps <= 4 ? 4 : 8;
   return fmt == MOE_FMT_NVFP4 ? c : (c < 4 ? c : 4);
@@ -804,6 +828,7 @@ hipError_t launch_gate_up(int fmt, const GateUpArgs &a, int n_shared_sub, hipStr
   switch (fmt) {
     case MOE_FMT_NVFP4: launch_gate_up_fmt<MOE_FMT_NVFP4>(a, grid, s); break;
     case MOE_FMT_MXFP4_E8M0: launch_gate_up_fmt<MOE_FMT_MXFP4_E8M0>(a, grid, s); break;
+    case MOE_FMT_BF16: launch_gate_up_fmt<MOE_FMT_BF16>(a, grid, s); break;
     default: launch_gate_up_fmt<MOE_FMT_FP8_BLOCK128>(a, grid, s); break;
   }
   return hipGetLastError();
@@ -824,6 +849,7 @@ hipError_t launch_down(int fmt, const DownArgs &a, int n_shared_sub, hipStream_t
   switch (fmt) {
     case MOE_FMT_NVFP4: launch_down_fmt<MOE_FMT_NVFP4>(a, grid, s); break;
     case MOE_FMT_MXFP4_E8M0: launch_down_fmt<MOE_FMT_MXFP4_E8M0>(a, grid, s); break;
+    case MOE_FMT_BF16: launch_down_fmt<MOE_FMT_BF16>(a, grid, s); break;
     default: launch_down_fmt<MOE_FMT_FP8_BLOCK128>(a, grid, s); break;
   }
   return hipGetLastError();

@@ -111,7 +111,8 @@ struct BTile {
 //   NVFP4 TK 32: bytes [8 half, 8 half + 8) of piece ks/32 and its scale byte `half`
 //   FP8   TK 64: pieces ks/16 + half and ks/16 + half + 2 (16 elements each)
 //   FP8   TK 32: piece ks/16 + half
-//   bf16       : elements [ks + TK/2 half, +TK/2) of the row-major row
+//   BF16 (tile-16 bank) TK 64: pieces ks/8 + 4 half + {0..3};  TK 32: ks/8 + 2 half + {0,1}
+//   bf16 router (row-major): elements [ks + TK/2 half, +TK/2) of the row
 template <int FMT, int TK>
 __device__ __forceinline__ void b_fetch(const WMat<FMT> &m, uint32_t row, int ks, int half, BTile &t) {
   const uint32_t K = (uint32_t)m.K;
@@ -128,6 +129,15 @@ __device__ __forceinline__ void b_fetch(const WMat<FMT> &m, uint32_t row, int ks
       const uint2 v = __builtin_bit_cast(
           uint2, __builtin_amdgcn_raw_buffer_load_b64(m.codes, (int)(cb + pc * 256 + 8 * half), 0, 0));
       t.c0 = make_uint4(v.x, v.y, 0, 0);
+    }
+  } else if constexpr (FMT == MOE_FMT_BF16) {
+    const uint32_t cb = (row & ~15u) * (2 * K) + (row & 15u) * 16;
+    const uint32_t pc = (uint32_t)ks / 8 + (TK / 16) * half;
+    t.c0 = buf_load16(m.codes, cb + pc * 256);
+    t.c1 = buf_load16(m.codes, cb + (pc + 1) * 256);
+    if constexpr (TK == 64) {
+      t.c2 = buf_load16(m.codes, cb + (pc + 2) * 256);
+      t.c3 = buf_load16(m.codes, cb + (pc + 3) * 256);
     }
   } else if constexpr (FMT == kFmtBf16) {
     const uint32_t o = (row * K + ks + (TK / 2) * half) * 2;
@@ -160,7 +170,7 @@ __device__ __forceinline__ void b_store(uint16_t *rowp, int row, int half, const
       fp4x8_mul_to_bf16(t.c0.z, s1, f[2]);
       fp4x8_mul_to_bf16(t.c0.w, s1, f[3]);
     }
-  } else if constexpr (FMT == kFmtBf16) {
+  } else if constexpr (FMT == kFmtBf16 || FMT == MOE_FMT_BF16) {
     f[0].q = t.c0;
     f[1].q = t.c1;
     if constexpr (NC == 4) {
@@ -521,6 +531,8 @@ hipError_t launch_gate_up_tiled(int fmt, const GateUpArgs &a, int n_shared_tiles
   const dim3 grid(a.cap / TM + n_shared_tiles, (a.Il + 63) / 64);
   if (fmt == MOE_FMT_NVFP4)
     hipLaunchKernelGGL(k_gate_up_tiled<MOE_FMT_NVFP4>, grid, dim3(256), 0, s, a);
+  else if (fmt == MOE_FMT_BF16)
+    hipLaunchKernelGGL(k_gate_up_tiled<MOE_FMT_BF16>, grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(k_gate_up_tiled<MOE_FMT_FP8_BLOCK128>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
@@ -530,6 +542,8 @@ hipError_t launch_down_tiled(int fmt, const DownArgs &a, int n_shared_tiles, hip
   const dim3 grid(a.cap / TM + n_shared_tiles, a.H / TW);
   if (fmt == MOE_FMT_NVFP4)
     hipLaunchKernelGGL(k_down_tiled<MOE_FMT_NVFP4>, grid, dim3(256), 0, s, a);
+  else if (fmt == MOE_FMT_BF16)
+    hipLaunchKernelGGL(k_down_tiled<MOE_FMT_BF16>, grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(k_down_tiled<MOE_FMT_FP8_BLOCK128>, grid, dim3(256), 0, s, a);
   return hipGetLastError();

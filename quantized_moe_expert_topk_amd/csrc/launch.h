@@ -59,7 +59,7 @@ hipError_t launch_align(const int32_t *ids, int T, int k, int E, int BM, int cap
                         int32_t *hist, hipStream_t s);
 hipError_t launch_gate_up(int fmt, const GateUpArgs &a, int n_shared_sub, hipStream_t s);
 hipError_t launch_down(int fmt, const DownArgs &a, int n_shared_sub, hipStream_t s);
-// Tiled kernels for align blocks of 128 rows (NVFP4, FP8_BLOCK128); the shared expert's
+// Tiled kernels for align blocks of 128 rows (NVFP4, FP8_BLOCK128, BF16); the shared expert's
 // rows are ceil(T/128) tiles after the routed ones.
 hipError_t launch_gate_up_tiled(int fmt, const GateUpArgs &a, int n_shared_tiles, hipStream_t s);
 hipError_t launch_down_tiled(int fmt, const DownArgs &a, int n_shared_tiles, hipStream_t s);

@@ -121,7 +121,7 @@ def logits_f32(seed: int, index: int, T: int, E: int) -> np.ndarray:
 
 # ----------------------------------------------------------------------------- banks
 
-FORMATS = ("nvfp4", "fp8blk", "mxfp4")
+FORMATS = ("nvfp4", "fp8blk", "mxfp4", "bf16")
 
 
 @dataclass
@@ -131,7 +131,7 @@ class Bank:
     E: int
     H: int
     I: int
-    gate_up: np.ndarray            # nvfp4/mxfp4: u8 [E, 2I, H/2]; fp8blk: u8 [E, 2I, H]
+    gate_up: np.ndarray            # nvfp4/mxfp4: u8 [E, 2I, H/2]; fp8blk: u8 [E, 2I, H]; bf16: u16 bits [E, 2I, H]
     gate_up_scale: np.ndarray      # nvfp4: u8 e4m3 [E, 2I, H/16]; fp8blk: f32 [E, 2I/128, H/128]; mxfp4: u8 e8m0 [E, 2I, H/32]
     down: np.ndarray               # nvfp4/mxfp4: u8 [E, H, I/2]; fp8blk: u8 [E, H, I]
     down_scale: np.ndarray         # nvfp4: u8 [E, H, I/16]; fp8blk: f32 [E, H/128, I/128]; mxfp4: u8 [E, H, I/32]
@@ -167,6 +167,12 @@ def _alloc_bank(fmt: str, E: int, H: int, I: int) -> Bank:
                     gate_up_scale=np.zeros((E, 2 * I, H // 32), np.uint8),
                     down=np.zeros((E, H, I // 2), np.uint8),
                     down_scale=np.zeros((E, H, I // 32), np.uint8))
+    if fmt == "bf16":  # unquantized: no scales (empty placeholders keep the arrays uniform)
+        return Bank(fmt, E, H, I,
+                    gate_up=np.zeros((E, 2 * I, H), np.uint16),
+                    gate_up_scale=np.zeros((E, 0), np.uint8),
+                    down=np.zeros((E, H, I), np.uint16),
+                    down_scale=np.zeros((E, 0), np.uint8))
     raise ValueError(f"unknown format {fmt!r}")
 
 
@@ -181,6 +187,9 @@ def _fill_expert(b: Bank, e: int, seed: int, tag_gu: int, tag_dn: int, index: in
     elif b.fmt == "fp8blk":
         L.synth_fp8blk_matrix(seed, tag_gu, index, 2 * I, H, s, _p(b.gate_up[e]), _p(b.gate_up_scale[e]))
         L.synth_fp8blk_matrix(seed, tag_dn, index, H, I, s, _p(b.down[e]), _p(b.down_scale[e]))
+    elif b.fmt == "bf16":
+        b.gate_up[e] = bf16_normal(seed, tag_gu, index, (2 * I, H), s)
+        b.down[e] = bf16_normal(seed, tag_dn, index, (H, I), s)
     else:
         L.synth_mxfp4_matrix(seed, tag_gu, index, 2 * I, H, s, _p(b.gate_up[e]), _p(b.gate_up_scale[e]))
         L.synth_mxfp4_matrix(seed, tag_dn, index, H, I, s, _p(b.down[e]), _p(b.down_scale[e]))
@@ -210,6 +219,12 @@ def slice_bank(b: Bank, lo: int, hi: int) -> Bank:
     Copies, never views (issue #520 section 4, ".clone()")."""
     I, Il = b.I, hi - lo
     gu_rows = np.r_[lo:hi, I + lo:I + hi]
+    if b.fmt == "bf16":
+        return Bank(b.fmt, b.E, b.H, Il,
+                    gate_up=np.ascontiguousarray(b.gate_up[:, gu_rows]),
+                    gate_up_scale=b.gate_up_scale.copy(),
+                    down=np.ascontiguousarray(b.down[:, :, lo:hi]),
+                    down_scale=b.down_scale.copy())
     if b.fmt == "fp8blk":
         blk_rows = np.r_[lo // 128:hi // 128, (I + lo) // 128:(I + hi) // 128]
         return Bank(b.fmt, b.E, b.H, Il,
@@ -262,6 +277,8 @@ CONFIGS = {
                    2048, 256, 8, 512, False, (1, 64, 4096), ((0, 256), (0, 512))),
     5: LayerConfig(5, "DeepSeek-V4-Flash-shaped MXFP4 (e8m0 per 32) layer H=4096 E=256 top-8 I=2048 + shared",
                    "mxfp4", 4096, 256, 8, 2048, True, (1, 16, 256), ((0, 1024), (0, 2048))),
+    6: LayerConfig(6, "Qwen3.6-35B-A3B-shaped bf16 stacked-expert layer H=2048 E=256 top-8 I=512 + shared",
+                   "bf16", 2048, 256, 8, 512, True, (1, 64, 8192), ((0, 256), (0, 512))),
 }
 
 

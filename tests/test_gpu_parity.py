@@ -150,7 +150,8 @@ def test_align_is_bit_exact(T, k, E, bm, kind):
 
 # ----------------------------------------------------------------------------- weight layout
 
-@pytest.mark.parametrize("fmt,E,H,I", [("nvfp4", 3, 256, 128), ("fp8blk", 2, 256, 256), ("mxfp4", 3, 512, 192)])
+@pytest.mark.parametrize("fmt,E,H,I", [("nvfp4", 3, 256, 128), ("fp8blk", 2, 256, 256), ("mxfp4", 3, 512, 192),
+                                       ("bf16", 2, 256, 96)])
 def test_pack_bank_is_the_tile16_permutation(fmt, E, H, I):
     """moe_pack_bank puts every code and FP4 scale byte at its MOE_LAYOUT_TILE16 position
     (bit-exact against the index transform of the row-major arrays) and leaves the
@@ -160,19 +161,20 @@ def test_pack_bank_is_the_tile16_permutation(fmt, E, H, I):
     torch.cuda.synchronize()
     assert pk.layout == qm.MOE_LAYOUT_TILE16
 
-    def rows2d(a):
+    def rows2d(a):  # byte rows
         a = np.ascontiguousarray(a)
-        return a.reshape(-1, a.shape[-1])
+        return a.view(np.uint8).reshape(a.shape[0] * a.shape[1], -1)
 
     def got(t):
-        return t.cpu().numpy().reshape(-1, t.shape[-1])
+        a = t.cpu().numpy()
+        return a.view(np.uint8).reshape(a.shape[0] * a.shape[1], -1)
 
     np.testing.assert_array_equal(got(pk.gate_up), tile16_np(rows2d(b.gate_up), 16))
     np.testing.assert_array_equal(got(pk.down), tile16_np(rows2d(b.down), 16))
     if fmt == "fp8blk":
         np.testing.assert_array_equal(pk.gate_up_scale.cpu().numpy(), b.gate_up_scale)
         np.testing.assert_array_equal(pk.down_scale.cpu().numpy(), b.down_scale)
-    else:
+    elif fmt != "bf16":
         unit = 2 if fmt == "nvfp4" else 1
         np.testing.assert_array_equal(got(pk.gate_up_scale), tile16_np(rows2d(b.gate_up_scale), unit))
         np.testing.assert_array_equal(got(pk.down_scale), tile16_np(rows2d(b.down_scale), unit))
@@ -207,7 +209,9 @@ FORWARD_CASES = [(1, 16, (0, 128)), (1, 16, (0, 64)), (1, 16, (64, 128)),
                  (4, 1, (0, 256)), (4, 64, (0, 256)), (4, 64, (0, 512)),
                  (5, 1, (0, 1024)), (5, 16, (0, 1024)), (5, 16, (1024, 2048)),
                  # MXFP4 slices off the 128-wide chunk grid: a masked K tail, unaligned scale spans
-                 (5, 16, (0, 96)), (5, 16, (32, 160)), (5, 1, (992, 2048))]
+                 (5, 16, (0, 96)), (5, 16, (32, 160)), (5, 1, (992, 2048)),
+                 # bf16 stacked experts (issue #62 "Suggested staging" item 1)
+                 (6, 1, (0, 256)), (6, 64, (0, 256)), (6, 16, (32, 160)), (6, 8, (0, 512))]
 
 
 @pytest.mark.parametrize("cid,T,sl", FORWARD_CASES)
@@ -246,12 +250,12 @@ def test_expert_forward_any_block_m(bm):
 
 
 TILED_CASES = [(1, 16, (0, 128)), (1, 16, (32, 96)), (2, 64, (0, 256)), (2, 32, (0, 96)), (2, 8, (64, 512)),
-               (4, 64, (0, 256)), (4, 64, (256, 512))]
+               (4, 64, (0, 256)), (4, 64, (256, 512)), (6, 64, (0, 256)), (6, 32, (32, 160))]
 
 
 @pytest.mark.parametrize("cid,T,sl", TILED_CASES)
 def test_tiled_kernels_match_oracle(cid, T, sl):
-    """128-row align blocks select the LDS-tiled GEMMs (NVFP4, fp8-block); small cases
+    """128-row align blocks select the LDS-tiled GEMMs (NVFP4, fp8-block, bf16); small cases
     cover partial column tiles and a 32-wide K tail."""
     inp, r = inputs_for(cid, T)
     lo, hi = sl

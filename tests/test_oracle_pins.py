@@ -143,7 +143,7 @@ def test_fp8blk_one_hot_probe_locates_block_scale():
     assert W[200, 129] == -2.0 * b.down_scale[0, 1, 1] and np.count_nonzero(W) == 1
 
 
-@pytest.mark.parametrize("fmt,H,I", [("nvfp4", 256, 64), ("fp8blk", 256, 128), ("mxfp4", 256, 64)])
+@pytest.mark.parametrize("fmt,H,I", [("nvfp4", 256, 64), ("fp8blk", 256, 128), ("mxfp4", 256, 64), ("bf16", 128, 64)])
 def test_dequant_reconstructs_generated_normals(fmt, H, I):
     """The oracle's decode of the generator's codes reproduces the N(0, 0.02) weights the
     generator drew, within each format's rounding bound.  Decoder and encoder are separate
@@ -155,7 +155,9 @@ def test_dequant_reconstructs_generated_normals(fmt, H, I):
         w_dn = S.normal_f64(seed, S.TAG_DOWN, e, H * I, S.WEIGHT_SIGMA).reshape(H, I)
         for W, ref in ((O.dequant_gate_up(b, e), w_gu), (O.dequant_down(b, e), w_dn)):
             err = np.abs(W - ref)
-            if fmt == "fp8blk":
+            if fmt == "bf16":  # round to nearest with 8 significant bits: half an ulp <= 2^-8 |w|
+                bound = np.abs(ref) * 2.0 ** -8 * 1.0001
+            elif fmt == "fp8blk":
                 # e4m3 relative step 2^-3 -> |err| <= 2^-4 |w| (normals), plus subnormal floor
                 si = np.repeat(np.repeat(np.abs(ref).reshape(ref.shape[0] // 128, 128, -1, 128)
                                          .max(axis=(1, 3)) / 448, 128, 0), 128, 1)
@@ -168,7 +170,7 @@ def test_dequant_reconstructs_generated_normals(fmt, H, I):
                 bound = amax / 6 * (1 + 1 / 16) * 1.0001 + 1e-12 if fmt == "nvfp4" else amax / 4 * 1.0001
             assert (err <= bound).all(), (fmt, float((err / bound).max()))
             rel = np.linalg.norm(W - ref) / np.linalg.norm(ref)
-            assert rel < {"nvfp4": 0.1, "mxfp4": 0.15, "fp8blk": 0.04}[fmt], rel
+            assert rel < {"nvfp4": 0.1, "mxfp4": 0.15, "fp8blk": 0.04, "bf16": 0.003}[fmt], rel
 
 
 # ------------------------------------------------------------------ routing
@@ -310,7 +312,7 @@ def _dense_swiglu(x64, Wgu, Wd, lo, hi, I):
     return (g / (1 + np.exp(-g)) * u) @ Wd[:, lo:hi].T
 
 
-@pytest.mark.parametrize("fmt,H,I", [("nvfp4", 128, 64), ("fp8blk", 256, 256), ("mxfp4", 128, 64)])
+@pytest.mark.parametrize("fmt,H,I", [("nvfp4", 128, 64), ("fp8blk", 256, 256), ("mxfp4", 128, 64), ("bf16", 128, 64)])
 def test_forward_single_expert_is_dense_swiglu(fmt, H, I):
     """E=1, k=1, weight 1: a plain SwiGLU FFN on the dequantized matrices (numpy matmul)."""
     b = S.routed_bank(21, fmt, 1, H, I)
@@ -364,7 +366,8 @@ def test_forward_all_ones_closed_form():
 
 @pytest.mark.parametrize("fmt,H,I,cuts", [("nvfp4", 128, 128, (0, 16, 64, 128)),
                                           ("fp8blk", 256, 384, (0, 128, 384)),
-                                          ("mxfp4", 128, 128, (0, 32, 96, 128))])
+                                          ("mxfp4", 128, 128, (0, 32, 96, 128)),
+                                          ("bf16", 128, 96, (0, 32, 64, 96))])
 def test_forward_slices_sum_to_full(fmt, H, I, cuts):
     """Linearity in the intermediate index (issue #520 section 4): the partials of disjoint
     slices tiling [0, I) sum to the unsliced layer, routed and shared alike."""
