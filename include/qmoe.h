@@ -84,6 +84,14 @@ typedef enum {
  *     multiple of 32 elements stays addressable. */
 #define MOE_LAYOUT_ROWS 0
 #define MOE_LAYOUT_TILE16 1
+/* MOE_LAYOUT_MXFP4_T  MXFP4 as some checkpoints store it, transposed (issue #62 "What it
+ *     touches" item 3: blocks_t [K/2, N], sliced along N, the scales sliced differently):
+ *     every expert matrix W [N, K] is stored as codes [K/2, N] (byte b of column n holds
+ *     elements 2b, 2b+1 of row n, the even one in the low nibble) and e8m0 scales [K/32, N];
+ *     gate_up has N = 2I (gate columns [0, I), up [I, 2I)) and K = H, down N = H and K = I.
+ *     A rank's slice of such a bank is a column range of gate_up (two ranges) and a row
+ *     range of down.  Accepted as moe_pack_bank's source only. */
+#define MOE_LAYOUT_MXFP4_T 2
 
 /* One bank of E experts, full-I layout, expert-major and row-major per matrix
  * (issue #520 patch, nvfp4.py layout()/pack(); issue #62 "What it touches" item 1):
@@ -114,9 +122,10 @@ typedef struct {
   int32_t layout; /* MOE_LAYOUT_* */
 } moe_bank;
 
-/* moe_pack_bank -- reorders a MOE_LAYOUT_ROWS bank into MOE_LAYOUT_TILE16 storage, once,
- * when the weights are loaded (a pure permutation of bytes: values and formats unchanged).
- *   src   a ROWS bank (device pointers).
+/* moe_pack_bank -- reorders a MOE_LAYOUT_ROWS (or, for MXFP4, MOE_LAYOUT_MXFP4_T) bank into
+ * MOE_LAYOUT_TILE16 storage, once, when the weights are loaded (a pure permutation of bytes:
+ * values and formats unchanged).
+ *   src   a ROWS bank, or an MXFP4 bank in MOE_LAYOUT_MXFP4_T (device pointers).
  *   dst   a TILE16 bank of the same fmt, E, H and I whose gate_up, gate_up_scale, down and
  *         down_scale point at device buffers of the same sizes as src's, not overlapping
  *         them; dst's FP8_BLOCK128 scales and NVFP4 globals, when they are other buffers

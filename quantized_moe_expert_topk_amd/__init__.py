@@ -3,7 +3,8 @@
 The compute lives in ``libqmoe.so`` (hand-written HIP kernels behind the C ABI of
 ``include/qmoe.h``); this package is its Python binding.
 """
-from ._lib import EXPORTS, LIB_PATH, MOE_LAYOUT_ROWS, MOE_LAYOUT_TILE16, MoeError, lib  # noqa: F401
+from ._lib import (EXPORTS, LIB_PATH, MOE_LAYOUT_MXFP4_T, MOE_LAYOUT_ROWS, MOE_LAYOUT_TILE16,  # noqa: F401
+                   MoeError, lib)
 from .api import (AlignOut, DeviceBank, MoeLayer, alloc_align, choose_block_m, moe_align,  # noqa: F401
                   moe_align_capacity, moe_align_workspace_bytes, moe_expert_down, moe_expert_forward,
                   moe_expert_gate_up, moe_pack_bank, moe_route, moe_route_from_logits,

@@ -17,7 +17,7 @@ MOE_ERR_HIP = -5
 
 MOE_FMT = {"nvfp4": 1, "fp8blk": 2, "mxfp4": 3, "bf16": 4}
 MOE_OUT_F32, MOE_OUT_BF16 = 0, 1
-MOE_LAYOUT_ROWS, MOE_LAYOUT_TILE16 = 0, 1
+MOE_LAYOUT_ROWS, MOE_LAYOUT_TILE16, MOE_LAYOUT_MXFP4_T = 0, 1, 2
 
 # every entry point include/qmoe.h declares
 EXPORTS = ("moe_route", "moe_route_workspace_bytes", "moe_route_from_logits", "moe_align_capacity", "moe_align_workspace_bytes", "moe_align",

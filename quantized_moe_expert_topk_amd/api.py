@@ -78,15 +78,25 @@ class AlignOut:
 
 
 def moe_pack_bank(bank: DeviceBank, stream=None) -> DeviceBank:
-    """The bank reordered into MOE_LAYOUT_TILE16 (new code and FP4 scale storage; the FP8 block
-    scales and NVFP4 globals are shared with ``bank``).  A packed bank is returned as is."""
+    """The bank reordered into MOE_LAYOUT_TILE16 (new code and FP4 scale storage, in the
+    row-major shapes; the FP8 block scales and NVFP4 globals are shared with ``bank``).  The
+    source is row-major, or for MXFP4 also transposed (MOE_LAYOUT_MXFP4_T).  A packed bank is
+    returned as is."""
     if bank.layout == MOE_LAYOUT_TILE16:
         return bank
-    fp4 = bank.fmt in ("nvfp4", "mxfp4")  # their scales are reordered too
-    dst = DeviceBank(bank.fmt, bank.E, bank.H, bank.I, torch.empty_like(bank.gate_up),
-                     torch.empty_like(bank.gate_up_scale) if fp4 else bank.gate_up_scale,
-                     torch.empty_like(bank.down), torch.empty_like(bank.down_scale) if fp4 else bank.down_scale,
-                     bank.gate_up_global, bank.down_global, MOE_LAYOUT_TILE16)
+    E, H, I = bank.E, bank.H, bank.I
+
+    def like(t, rows, cols):  # new storage, [E, rows, cols] of t's dtype
+        return torch.empty((E, rows, cols), dtype=t.dtype, device=t.device)
+
+    if bank.fmt in ("nvfp4", "mxfp4"):  # codes and scales are reordered
+        sdiv = 16 if bank.fmt == "nvfp4" else 32
+        gu, dn = like(bank.gate_up, 2 * I, H // 2), like(bank.down, H, I // 2)
+        gus, dns = like(bank.gate_up_scale, 2 * I, H // sdiv), like(bank.down_scale, H, I // sdiv)
+    else:  # codes only
+        gu, dn = torch.empty_like(bank.gate_up), torch.empty_like(bank.down)
+        gus, dns = bank.gate_up_scale, bank.down_scale
+    dst = DeviceBank(bank.fmt, E, H, I, gu, gus, dn, dns, bank.gate_up_global, bank.down_global, MOE_LAYOUT_TILE16)
     src_s, dst_s = bank.struct(), dst.struct()
     check("moe_pack_bank", lib().moe_pack_bank(ctypes.byref(src_s), ctypes.byref(dst_s), _stream(stream)))
     return dst

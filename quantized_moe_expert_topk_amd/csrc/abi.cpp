@@ -470,9 +470,12 @@ int moe_align(const int32_t *topk_ids, int T, int k, int E, const moe_align_out 
 int moe_pack_bank(const moe_bank *src, const moe_bank *dst, void *stream) {
   if (!src || !dst) return fail(MOE_ERR_INVALID_ARG, "moe_pack_bank: NULL bank");
   if (!format_block(src->fmt)) return fail(MOE_ERR_INVALID_ARG, "moe_pack_bank: unknown format %d", src->fmt);
-  if (src->layout != MOE_LAYOUT_ROWS || dst->layout != MOE_LAYOUT_TILE16)
-    return fail(MOE_ERR_INVALID_ARG, "moe_pack_bank: src layout must be ROWS (%d) and dst TILE16 (%d)",
+  const bool transposed = src->layout == MOE_LAYOUT_MXFP4_T;
+  if ((src->layout != MOE_LAYOUT_ROWS && !transposed) || dst->layout != MOE_LAYOUT_TILE16)
+    return fail(MOE_ERR_INVALID_ARG, "moe_pack_bank: src layout must be ROWS or MXFP4_T (%d) and dst TILE16 (%d)",
                 src->layout, dst->layout);
+  if (transposed && src->fmt != MOE_FMT_MXFP4_E8M0)
+    return fail(MOE_ERR_INVALID_ARG, "moe_pack_bank: the transposed layout is for MXFP4 banks");
   if (dst->fmt != src->fmt || dst->E != src->E || dst->H != src->H || dst->I != src->I)
     return fail(MOE_ERR_INVALID_ARG, "moe_pack_bank: src and dst differ in fmt, E, H or I");
   if (src->E < 1 || src->H < 1 || src->I < 1)
@@ -502,6 +505,18 @@ int moe_pack_bank(const moe_bank *src, const moe_bank *dst, void *stream) {
   if (rc) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t E = (size_t)src->E, H = (size_t)src->H, I = (size_t)src->I;
+  if (transposed) {  // gather each matrix's columns: codes [K/2, N] and scales [K/32, N] per expert
+    const struct { const void *from; const void *to; size_t N; uint32_t pitch; int unit; } t[4] = {
+        {src->gate_up, dst->gate_up, 2 * I, z.gu_pitch, 16}, {src->down, dst->down, H, z.dn_pitch, 16},
+        {src->gate_up_scale, dst->gate_up_scale, 2 * I, z.gus_pitch, 1},
+        {src->down_scale, dst->down_scale, H, z.dns_pitch, 1}};
+    for (const auto &m : t) {
+      rc = hip_status(qmoe::launch_pack_tile16_t(m.from, const_cast<void *>(m.to), E, m.N, m.pitch, m.unit, s),
+                      "pack launch");
+      if (rc) return rc;
+    }
+    return ok();
+  }
   rc = hip_status(qmoe::launch_pack_tile16(src->gate_up, const_cast<void *>(dst->gate_up), E * 2 * I, z.gu_pitch,
                                            16, s), "pack launch");
   if (rc) return rc;

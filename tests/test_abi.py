@@ -145,6 +145,7 @@ def _pack(src, dst):
     (_bank(layout=L.MOE_LAYOUT_ROWS, glob=False), _bank(base=0x40000000, glob=False), L.MOE_ERR_INVALID_ARG),
     (_bank(layout=L.MOE_LAYOUT_ROWS, I=48), _bank(I=48, base=0x40000000), L.MOE_ERR_UNSUPPORTED),  # half pieces
     (_bank(fmt=9, layout=L.MOE_LAYOUT_ROWS), _bank(fmt=9, base=0x40000000), L.MOE_ERR_INVALID_ARG),
+    (_bank(fmt=1, layout=L.MOE_LAYOUT_MXFP4_T), _bank(base=0x40000000), L.MOE_ERR_INVALID_ARG),  # NVFP4 transposed
 ])
 def test_pack_bank_rejects_bad_arguments_before_any_launch(src, dst, code):
     rc, msg = _pack(src, dst)

@@ -183,6 +183,52 @@ def test_pack_bank_is_the_tile16_permutation(fmt, E, H, I):
         np.testing.assert_array_equal(pk.down_global.cpu().numpy(), b.down_global)
 
 
+def _transposed_mx(b):
+    """The MOE_LAYOUT_MXFP4_T arrays of a row-major MXFP4 bank: codes [E, K/2, N], scales [E, K/32, N]."""
+    return tuple(np.ascontiguousarray(a.transpose(0, 2, 1)) for a in (b.gate_up, b.gate_up_scale, b.down, b.down_scale))
+
+
+def _dev_transposed(b, arrays, I=None):
+    gu, gus, dn, dns = (to_dev(a) for a in arrays)
+    return qm.DeviceBank("mxfp4", b.E, b.H, b.I if I is None else I, gu, gus, dn, dns, layout=qm.MOE_LAYOUT_MXFP4_T)
+
+
+def test_pack_bank_from_transposed_mxfp4_equals_row_major():
+    """An MXFP4 bank stored transposed (blocks_t [K/2, N], scales [K/32, N]) packs to exactly
+    the bytes of the same bank stored row-major."""
+    b = S.routed_bank(13, "mxfp4", 3, 512, 192)
+    want = device_bank(b)
+    got = qm.moe_pack_bank(_dev_transposed(b, _transposed_mx(b)))
+    torch.cuda.synchronize()
+    for name in ("gate_up", "gate_up_scale", "down", "down_scale"):
+        assert torch.equal(getattr(got, name), getattr(want, name)), name
+
+
+def test_transposed_mxfp4_rank_slice_matches_full_bank():
+    """A rank's own storage of a transposed MXFP4 bank: gate_up columns [lo,hi) and [I+lo,I+hi)
+    of blocks_t and its scales, down rows [lo/2,hi/2) of blocks_t and [lo/32,hi/32) of its scales
+    (the slice is along N for gate_up and along K for down).  Packed, it gives the same result as
+    the full bank's slice [lo, hi), and both match the oracle."""
+    E, H, I, k, T, lo, hi = 8, 512, 256, 2, 12, 64, 192
+    b, sh = S.routed_bank(17, "mxfp4", E, H, I), S.shared_bank(17, "mxfp4", H, I)
+    x = S.tokens(17, T, H)
+    _, ids, w, _ = O.route(x, S.router_weight(17, E, H), None, k, True)
+    ref = O.expert_forward(b, sh, x, ids, w, lo, hi)
+
+    def rank(bank):
+        gu, gus, dn, dns = _transposed_mx(bank)
+        cols = np.r_[lo:hi, I + lo:I + hi]
+        own = (gu[:, :, cols], gus[:, :, cols], dn[:, lo // 2:hi // 2, :], dns[:, lo // 32:hi // 32, :])
+        return qm.moe_pack_bank(_dev_transposed(bank, [np.ascontiguousarray(a) for a in own], I=hi - lo))
+
+    al = qm.moe_align(to_dev(ids.astype(np.int32)), E, 16)
+    xd, wd = bf16_dev(x), to_dev(w.astype(np.float32))
+    full = qm.moe_expert_forward(device_bank(b), device_bank(sh), xd, wd, al, lo, hi).cpu().numpy()
+    own = qm.moe_expert_forward(rank(b), rank(sh), xd, wd, al, 0, hi - lo).cpu().numpy()
+    np.testing.assert_array_equal(own, full)
+    check_close("transposed MXFP4 rank slice", own, ref)
+
+
 def test_forward_rejects_row_major_bank():
     inp, r = inputs_for(1, 8)
     rows = device_bank(inp.routed, packed=False)
