@@ -79,6 +79,23 @@ double oracle_bf16(unsigned bits) {
   return (double)f;
 }
 
+/* IEEE binary16: sign, 5-bit exponent (bias 15), 10-bit fraction; exponent 0 = subnormal. */
+double oracle_f16(unsigned bits) {
+  const unsigned E = (bits >> 10) & 31u, f = bits & 1023u;
+  double v;
+  if (E == 31u) v = f ? NAN : INFINITY;
+  else if (E == 0u) v = ldexp((double)f, -24);
+  else v = ldexp(1.0 + (double)f / 1024.0, (int)E - 15);
+  return (bits & 0x8000u) ? -v : v;
+}
+
+/* q4_0 code of element c of a row (32-element blocks of 16 bytes; byte j holds element j in
+ * its low nibble and element j + 16 in its high nibble). */
+static inline unsigned q4_0_code(const uint8_t *row, int c) {
+  const uint8_t b = row[16 * (c / 32) + (c % 32) % 16];
+  return (c % 32) < 16 ? (unsigned)(b & 15u) : (unsigned)(b >> 4);
+}
+
 static inline unsigned nibble(const uint8_t *row, int c) {
   uint8_t b = row[c >> 1];
   return (c & 1) ? (unsigned)(b >> 4) : (unsigned)(b & 15u); /* even index in the low nibble */
@@ -102,6 +119,11 @@ double oracle_weight_gate_up(const oracle_bank *b, int e, int r, int c) {
   }
   if (b->fmt == ORACLE_BF16) /* unquantized bf16 stacked experts (issue #62 "Suggested staging" 1) */
     return oracle_bf16(((const uint16_t *)b->gate_up)[((size_t)e * 2 * I + r) * (size_t)H + c]);
+  if (b->fmt == ORACLE_Q4_0) { /* 32-element blocks (issue #62 "What it touches" item 2) */
+    const uint8_t *codes = b->gate_up + ((size_t)e * 2 * I + r) * (size_t)(H / 2);
+    const uint16_t *d = (const uint16_t *)b->gate_up_scale + ((size_t)e * 2 * I + r) * (size_t)(H / 32);
+    return ((double)q4_0_code(codes, c) - 8.0) * oracle_f16(d[c / 32]);
+  }
   /* MXFP4 */
   const uint8_t *codes = b->gate_up + ((size_t)e * 2 * I + r) * (size_t)(H / 2);
   const uint8_t *sc = (const uint8_t *)b->gate_up_scale + ((size_t)e * 2 * I + r) * (size_t)(H / 32);
@@ -124,6 +146,11 @@ double oracle_weight_down(const oracle_bank *b, int e, int n, int i) {
   }
   if (b->fmt == ORACLE_BF16)
     return oracle_bf16(((const uint16_t *)b->down)[((size_t)e * H + n) * (size_t)I + i]);
+  if (b->fmt == ORACLE_Q4_0) {
+    const uint8_t *codes = b->down + ((size_t)e * H + n) * (size_t)(I / 2);
+    const uint16_t *d = (const uint16_t *)b->down_scale + ((size_t)e * H + n) * (size_t)(I / 32);
+    return ((double)q4_0_code(codes, i) - 8.0) * oracle_f16(d[i / 32]);
+  }
   const uint8_t *codes = b->down + ((size_t)e * H + n) * (size_t)(I / 2);
   const uint8_t *sc = (const uint8_t *)b->down_scale + ((size_t)e * H + n) * (size_t)(I / 32);
   return oracle_e2m1(nibble(codes, i)) * oracle_e8m0(sc[i / 32]);

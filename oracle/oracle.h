@@ -9,6 +9,7 @@
 #define ORACLE_FP8BLK 2
 #define ORACLE_MXFP4 3
 #define ORACLE_BF16 4
+#define ORACLE_Q4_0 5
 
 /* One bank of E experts in the full-I layout (expert-major, row-major per matrix).
  *   NVFP4 : gate_up u8 [E,2I,H/2], gate_up_scale e4m3 [E,2I,H/16], gate_up_global f32 [E,2I],
@@ -18,7 +19,10 @@
  *   MXFP4 : gate_up u8 [E,2I,H/2], gate_up_scale e8m0 [E,2I,H/32],
  *           down u8 [E,H,I/2], down_scale e8m0 [E,H,I/32]
  *   BF16  : gate_up bf16 bits [E,2I,H], down bf16 bits [E,H,I] (passed through the u8 pointers);
- *           no scales or globals */
+ *           no scales or globals
+ *   Q4_0  : gate_up u8 [E,2I,H/2], gate_up_scale fp16 bits [E,2I,H/32], down u8 [E,H,I/2],
+ *           down_scale fp16 bits [E,H,I/32]; 32-element blocks, byte j of a block holds
+ *           element j (low nibble) and j+16 (high nibble); w = (q - 8) * d */
 typedef struct {
   int fmt, E, H, I;
   const uint8_t *gate_up;
@@ -33,6 +37,7 @@ double oracle_e2m1(unsigned code);
 double oracle_e4m3fn(unsigned b);
 double oracle_e8m0(unsigned b);
 double oracle_bf16(unsigned bits);
+double oracle_f16(unsigned bits);
 double oracle_weight_gate_up(const oracle_bank *b, int e, int r, int c);
 double oracle_weight_down(const oracle_bank *b, int e, int n, int i);
 void oracle_router_logits(const uint16_t *x, int T, int H, const uint16_t *Wr, int E,

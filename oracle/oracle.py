@@ -14,7 +14,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-FMT = {"nvfp4": 1, "fp8blk": 2, "mxfp4": 3, "bf16": 4}
+FMT = {"nvfp4": 1, "fp8blk": 2, "mxfp4": 3, "bf16": 4, "q4_0": 5}
 
 
 def build(force: bool = False) -> str:
@@ -46,7 +46,7 @@ def lib():
             build()
         L = ctypes.CDLL(_LIB_PATH)
         vp, i32, u32, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_double
-        for name in ("oracle_e2m1", "oracle_e4m3fn", "oracle_e8m0", "oracle_bf16"):
+        for name in ("oracle_e2m1", "oracle_e4m3fn", "oracle_e8m0", "oracle_bf16", "oracle_f16"):
             getattr(L, name).restype = dbl
             getattr(L, name).argtypes = [u32]
         pb = ctypes.POINTER(_Bank)
@@ -104,6 +104,10 @@ def e8m0(b: int) -> float:
 
 def bf16(bits: int) -> float:
     return lib().oracle_bf16(bits)
+
+
+def f16(bits: int) -> float:
+    return lib().oracle_f16(bits)
 
 
 def weight_gate_up(bank, e, r, c) -> float:

@@ -240,6 +240,63 @@ void synth_mxfp4_matrix(uint64_t seed, uint32_t tag, uint32_t index, int rows, i
 
 /* Per-expert router bias with Zipf(s) popularity: expert e gets rank pi(e)+1 of a seeded
  * permutation pi and bias ln p_rank, p_r = r^-s / sum_{r'=1..E} r'^-s. */
+/* IEEE binary16 bits of v, round to nearest even (subnormals included; |v| >= 65520 -> inf). */
+static uint16_t to_f16(double v) {
+  const uint16_t sign = v < 0.0 ? 0x8000u : 0u;
+  const double a = fabs(v);
+  if (a == 0.0) return sign;
+  if (a >= 65520.0) return (uint16_t)(sign | 0x7C00u);
+  int e;
+  const double m = frexp(a, &e); /* a = m * 2^e, m in [0.5, 1) */
+  int E = e + 14;                 /* biased exponent of a normal result */
+  if (E >= 1) {
+    long f = lrint((2.0 * m - 1.0) * 1024.0);
+    if (f == 1024) {
+      f = 0;
+      E += 1;
+    }
+    if (E >= 31) return (uint16_t)(sign | 0x7C00u);
+    return (uint16_t)(sign | (E << 10) | f);
+  }
+  return (uint16_t)(sign | lrint(a * 16777216.0)); /* subnormal: units of 2^-24 (1024 -> smallest normal) */
+}
+
+static double val_f16(uint16_t b) {
+  const int E = (b >> 10) & 31, f = b & 1023;
+  const double v = E == 0 ? ldexp((double)f, -24) : ldexp(1.0 + f / 1024.0, E - 15);
+  return (b & 0x8000u) ? -v : v;
+}
+
+/* q4_0 (llama.cpp's 32-element blocks): per block, the element of largest magnitude m sets
+ * d = m / -8 (stored as fp16), codes q = clamp(floor(v / d + 8.5), 0, 15), so w = (q - 8) d;
+ * byte j of a block holds element j in its low nibble and element j + 16 in its high nibble.
+ * codes [rows, cols/2], d [rows, cols/32] fp16 bits. */
+void synth_q4_0_matrix(uint64_t seed, uint32_t tag, uint32_t index, int rows, int cols, double sigma,
+                       uint8_t *codes, uint16_t *d) {
+  uint64_t key = synth_key(seed, tag, index);
+#pragma omp parallel for schedule(static)
+  for (int r = 0; r < rows; r++) {
+    double w[32];
+    for (int b = 0; b < cols / 32; b++) {
+      double m = 0.0;
+      for (int c = 0; c < 32; c++) {
+        w[c] = sigma * normal_at(key, (uint64_t)r * (uint64_t)cols + (uint64_t)(32 * b + c));
+        if (fabs(w[c]) > fabs(m)) m = w[c];
+      }
+      const uint16_t db = to_f16(m / -8.0);
+      d[(size_t)r * (cols / 32) + b] = db;
+      const double dv = val_f16(db), id = dv != 0.0 ? 1.0 / dv : 0.0;
+      uint8_t *blk = codes + (size_t)r * (cols / 2) + 16 * b;
+      for (int j = 0; j < 16; j++) {
+        int q0 = (int)floor(w[j] * id + 8.5), q1 = (int)floor(w[j + 16] * id + 8.5);
+        q0 = q0 < 0 ? 0 : q0 > 15 ? 15 : q0;
+        q1 = q1 < 0 ? 0 : q1 > 15 ? 15 : q1;
+        blk[j] = (uint8_t)(q0 | (q1 << 4));
+      }
+    }
+  }
+}
+
 void synth_zipf_bias(uint64_t seed, uint32_t tag, int E, double s, float *bias) {
   int *perm = (int *)malloc(sizeof(int) * (size_t)E);
   for (int e = 0; e < E; e++) perm[e] = e;

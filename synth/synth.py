@@ -60,6 +60,7 @@ def lib():
         L.synth_nvfp4_matrix.argtypes = [u64, u32, u32, i32, i32, dbl, vp, vp, vp]
         L.synth_fp8blk_matrix.argtypes = [u64, u32, u32, i32, i32, dbl, vp, vp]
         L.synth_mxfp4_matrix.argtypes = [u64, u32, u32, i32, i32, dbl, vp, vp]
+        L.synth_q4_0_matrix.argtypes = [u64, u32, u32, i32, i32, dbl, vp, vp]
         L.synth_zipf_bias.argtypes = [u64, u32, i32, dbl, vp]
         L.synth_randint.argtypes = [u64, u32, u32, i64, i32, vp]
         _lib = L
@@ -121,7 +122,7 @@ def logits_f32(seed: int, index: int, T: int, E: int) -> np.ndarray:
 
 # ----------------------------------------------------------------------------- banks
 
-FORMATS = ("nvfp4", "fp8blk", "mxfp4", "bf16")
+FORMATS = ("nvfp4", "fp8blk", "mxfp4", "bf16", "q4_0")
 
 
 @dataclass
@@ -167,6 +168,12 @@ def _alloc_bank(fmt: str, E: int, H: int, I: int) -> Bank:
                     gate_up_scale=np.zeros((E, 2 * I, H // 32), np.uint8),
                     down=np.zeros((E, H, I // 2), np.uint8),
                     down_scale=np.zeros((E, H, I // 32), np.uint8))
+    if fmt == "q4_0":  # codes as FP4 (llama.cpp block order), fp16 d bits per 32
+        return Bank(fmt, E, H, I,
+                    gate_up=np.zeros((E, 2 * I, H // 2), np.uint8),
+                    gate_up_scale=np.zeros((E, 2 * I, H // 32), np.uint16),
+                    down=np.zeros((E, H, I // 2), np.uint8),
+                    down_scale=np.zeros((E, H, I // 32), np.uint16))
     if fmt == "bf16":  # unquantized: no scales (empty placeholders keep the arrays uniform)
         return Bank(fmt, E, H, I,
                     gate_up=np.zeros((E, 2 * I, H), np.uint16),
@@ -187,6 +194,9 @@ def _fill_expert(b: Bank, e: int, seed: int, tag_gu: int, tag_dn: int, index: in
     elif b.fmt == "fp8blk":
         L.synth_fp8blk_matrix(seed, tag_gu, index, 2 * I, H, s, _p(b.gate_up[e]), _p(b.gate_up_scale[e]))
         L.synth_fp8blk_matrix(seed, tag_dn, index, H, I, s, _p(b.down[e]), _p(b.down_scale[e]))
+    elif b.fmt == "q4_0":
+        L.synth_q4_0_matrix(seed, tag_gu, index, 2 * I, H, s, _p(b.gate_up[e]), _p(b.gate_up_scale[e]))
+        L.synth_q4_0_matrix(seed, tag_dn, index, H, I, s, _p(b.down[e]), _p(b.down_scale[e]))
     elif b.fmt == "bf16":
         b.gate_up[e] = bf16_normal(seed, tag_gu, index, (2 * I, H), s)
         b.down[e] = bf16_normal(seed, tag_dn, index, (H, I), s)
@@ -279,6 +289,8 @@ CONFIGS = {
                    "mxfp4", 4096, 256, 8, 2048, True, (1, 16, 256), ((0, 1024), (0, 2048))),
     6: LayerConfig(6, "Qwen3.6-35B-A3B-shaped bf16 stacked-expert layer H=2048 E=256 top-8 I=512 + shared",
                    "bf16", 2048, 256, 8, 512, True, (1, 64, 8192), ((0, 256), (0, 512))),
+    7: LayerConfig(7, "Qwen3.6-35B-A3B-shaped q4_0 (32-element blocks) expert layer H=2048 E=256 top-8 I=512",
+                   "q4_0", 2048, 256, 8, 512, False, (1, 64), ((0, 256), (0, 512))),
 }
 
 

@@ -71,6 +71,37 @@ def test_e8m0_all_codes_match_torch():
     assert O.e8m0(127) == 1.0 and O.e8m0(0) == 2.0 ** -127
 
 
+def test_f16_all_codes_match_numpy():
+    """The q4_0 block scale decoder against numpy's binary16 for all 65536 codes."""
+    codes = np.arange(65536, dtype=np.uint16)
+    ref = codes.view(np.float16).astype(np.float64)
+    got = np.array([O.f16(int(c)) for c in codes])
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all()
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+
+
+def test_q4_0_one_hot_probe_locates_nibble_and_block_scale():
+    """q4_0: a single code 9 (value 1 * d) at element c of row r, scale d = 2^-(b % 5) for block
+    b, every other code 8 (zero): the oracle reads c through the block's nibble order (element j
+    in byte j's low nibble, j + 16 in its high nibble) and the block's fp16 scale."""
+    H, I = 128, 64
+    b = S.routed_bank(1, "q4_0", 1, H, I)
+    b.gate_up[:] = 0x88
+    for blk in range(H // 32):
+        b.gate_up_scale[0, :, blk] = np.float16(2.0 ** -(blk % 5)).view(np.uint16)
+    for r, c in ((0, 0), (3, 15), (5, 16), (7, 31), (2 * I - 1, 70), (9, 127)):
+        blk, j = c // 32, c % 32
+        byte = 16 * blk + (j % 16)
+        old = int(b.gate_up[0, r, byte])
+        b.gate_up[0, r, byte] = (old & 0xF0) | 9 if j < 16 else (old & 0x0F) | 0x90
+        W = O.dequant_gate_up(b, 0)
+        assert W[r, c] == 2.0 ** -(blk % 5), (r, c)
+        W[r, c] = 0
+        assert (W == 0).all(), (r, c)
+        b.gate_up[0, r, byte] = old
+
+
 def test_bf16_matches_torch():
     bits = np.array([0, 0x3F80, 0xBF80, 0x0001, 0x7F7F, 0xC2F7, 0x3E4C, 0x8000], np.uint16)
     ref = _bf16_to_f64(bits)
@@ -143,7 +174,8 @@ def test_fp8blk_one_hot_probe_locates_block_scale():
     assert W[200, 129] == -2.0 * b.down_scale[0, 1, 1] and np.count_nonzero(W) == 1
 
 
-@pytest.mark.parametrize("fmt,H,I", [("nvfp4", 256, 64), ("fp8blk", 256, 128), ("mxfp4", 256, 64), ("bf16", 128, 64)])
+@pytest.mark.parametrize("fmt,H,I", [("nvfp4", 256, 64), ("fp8blk", 256, 128), ("mxfp4", 256, 64), ("bf16", 128, 64),
+                                     ("q4_0", 256, 64)])
 def test_dequant_reconstructs_generated_normals(fmt, H, I):
     """The oracle's decode of the generator's codes reproduces the N(0, 0.02) weights the
     generator drew, within each format's rounding bound.  Decoder and encoder are separate
@@ -157,6 +189,10 @@ def test_dequant_reconstructs_generated_normals(fmt, H, I):
             err = np.abs(W - ref)
             if fmt == "bf16":  # round to nearest with 8 significant bits: half an ulp <= 2^-8 |w|
                 bound = np.abs(ref) * 2.0 ** -8 * 1.0001
+            elif fmt == "q4_0":  # levels -8..7 of step d = amax/8: half a step, except that an
+                # element near -amax's opposite extreme clamps to +7 (one full step off)
+                amax = np.repeat(np.abs(ref).reshape(ref.shape[0], -1, 32).max(axis=2), 32, axis=1)
+                bound = amax / 8 * (1 + 2.0 ** -10) * 1.0001 + amax * 2.0 ** -11
             elif fmt == "fp8blk":
                 # e4m3 relative step 2^-3 -> |err| <= 2^-4 |w| (normals), plus subnormal floor
                 si = np.repeat(np.repeat(np.abs(ref).reshape(ref.shape[0] // 128, 128, -1, 128)
@@ -170,7 +206,7 @@ def test_dequant_reconstructs_generated_normals(fmt, H, I):
                 bound = amax / 6 * (1 + 1 / 16) * 1.0001 + 1e-12 if fmt == "nvfp4" else amax / 4 * 1.0001
             assert (err <= bound).all(), (fmt, float((err / bound).max()))
             rel = np.linalg.norm(W - ref) / np.linalg.norm(ref)
-            assert rel < {"nvfp4": 0.1, "mxfp4": 0.15, "fp8blk": 0.04, "bf16": 0.003}[fmt], rel
+            assert rel < {"nvfp4": 0.1, "mxfp4": 0.15, "fp8blk": 0.04, "bf16": 0.003, "q4_0": 0.12}[fmt], rel
 
 
 # ------------------------------------------------------------------ routing
@@ -312,7 +348,8 @@ def _dense_swiglu(x64, Wgu, Wd, lo, hi, I):
     return (g / (1 + np.exp(-g)) * u) @ Wd[:, lo:hi].T
 
 
-@pytest.mark.parametrize("fmt,H,I", [("nvfp4", 128, 64), ("fp8blk", 256, 256), ("mxfp4", 128, 64), ("bf16", 128, 64)])
+@pytest.mark.parametrize("fmt,H,I", [("nvfp4", 128, 64), ("fp8blk", 256, 256), ("mxfp4", 128, 64), ("bf16", 128, 64),
+                                     ("q4_0", 128, 128)])
 def test_forward_single_expert_is_dense_swiglu(fmt, H, I):
     """E=1, k=1, weight 1: a plain SwiGLU FFN on the dequantized matrices (numpy matmul)."""
     b = S.routed_bank(21, fmt, 1, H, I)
@@ -367,7 +404,8 @@ def test_forward_all_ones_closed_form():
 @pytest.mark.parametrize("fmt,H,I,cuts", [("nvfp4", 128, 128, (0, 16, 64, 128)),
                                           ("fp8blk", 256, 384, (0, 128, 384)),
                                           ("mxfp4", 128, 128, (0, 32, 96, 128)),
-                                          ("bf16", 128, 96, (0, 32, 64, 96))])
+                                          ("bf16", 128, 96, (0, 32, 64, 96)),
+                                          ("q4_0", 128, 256, (0, 128, 256))])
 def test_forward_slices_sum_to_full(fmt, H, I, cuts):
     """Linearity in the intermediate index (issue #520 section 4): the partials of disjoint
     slices tiling [0, I) sum to the unsliced layer, routed and shared alike."""
