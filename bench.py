@@ -37,8 +37,9 @@ WORKLOADS = {
     4: (64, (0, 256), [(1, (0, 256)), (4096, (0, 256))]),
     5: (16, (0, 1024), [(1, (0, 1024)), (256, (0, 1024))]),
     6: (64, (0, 256), [(1, (0, 256)), (8192, (0, 512))]),
+    7: (64, (0, 256), [(1, (0, 256)), (64, (0, 512))]),
 }
-INSTANCES = {2: 3, 3: 3, 4: 2, 5: 1, 6: 1}   # layer instances rotated (>= 1 GiB of banks for 2-4, 6)
+INSTANCES = {2: 3, 3: 3, 4: 2, 5: 1, 6: 1, 7: 3}   # layer instances rotated (>= 1 GiB of banks for 2-4, 6, 7)
 BATCHES = 4                            # token batches rotated
 
 
@@ -50,6 +51,8 @@ def expert_slice_bytes(fmt, H, Il):
     """Bytes of one expert's slice (both projections), SURVEY-style algorithmic count."""
     if fmt == "nvfp4":
         return 3 * Il * H * 9 // 16 + 8 * Il + 4 * H
+    if fmt == "q4_0":  # 4-bit codes and an fp16 scale per 32
+        return 3 * Il * H * 9 // 16
     if fmt == "fp8blk":
         return 3 * Il * H + 4 * (2 * Il * H + H * Il) // 16384
     if fmt == "bf16":
@@ -60,6 +63,8 @@ def expert_slice_bytes(fmt, H, Il):
 def gate_up_slice_bytes(fmt, H, Il):
     if fmt == "nvfp4":
         return 2 * Il * H * 9 // 16 + 8 * Il
+    if fmt == "q4_0":
+        return 2 * Il * H * 9 // 16
     if fmt == "fp8blk":
         return 2 * Il * H + 4 * (2 * Il * H) // 16384
     if fmt == "bf16":

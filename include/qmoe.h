@@ -61,12 +61,17 @@ extern "C" {
  *   MOE_FMT_BF16: unquantized bf16 stacked experts, the first format the pages stage through
  *     the same slicing (issue #62 "Suggested staging" item 1; PR #637 "What is sharded": bf16
  *     stacked experts are split like the quantized ones); no scales or globals.
+ *   MOE_FMT_Q4_0: 4-bit codes in 32-element blocks with an fp16 scale d per block (issue #62
+ *     "What it touches" item 2 and "Suggested staging" item 3), in llama.cpp's q4_0 order:
+ *     byte j of a block's 16 holds element j (low nibble) and element j + 16 (high nibble);
+ *     W = (q - 8) * d.  The kernels take slices on multiples of 128 for this format.
  * Packed FP4 stores two codes per byte, the even K index in the low nibble. */
 typedef enum {
   MOE_FMT_NVFP4 = 1,
   MOE_FMT_FP8_BLOCK128 = 2,
   MOE_FMT_MXFP4_E8M0 = 3,
-  MOE_FMT_BF16 = 4
+  MOE_FMT_BF16 = 4,
+  MOE_FMT_Q4_0 = 5
 } moe_format;
 
 /* Byte order of a bank's weight codes and FP4 scales (moe_bank.layout).
@@ -79,6 +84,10 @@ typedef enum {
  *     (NVFP4 2 bytes, MXFP4 1): byte j of row r sits at
  *     (r/16)*16*S + (j/u)*16*u + (r%16)*u + j%u, S = scale bytes per row, u = unit.
  *     Sizes are unchanged; FP8_BLOCK128 scales and the NVFP4 globals keep their order.
+ *     Q4_0 differs: its 16-byte piece (s, g) of a row holds, for each of the 4 blocks of the
+ *     128-element step s, the 8 elements [8g, 8g+8) of that block as one dword, element 2i in
+ *     bits [4i, 4i+4) and element 2i+1 in bits [16+4i, 20+4i); its scale unit is the 8 bytes
+ *     of one step's 4 scales.
  *     One wave load is then one contiguous 1 KB run that is already in the matrix-core
  *     operand order (16 rows x 64 bytes), and any slice of rows or columns on a
  *     multiple of 32 elements stays addressable. */
@@ -96,15 +105,17 @@ typedef enum {
 /* One bank of E experts, full-I layout, expert-major and row-major per matrix
  * (issue #520 patch, nvfp4.py layout()/pack(); issue #62 "What it touches" item 1):
  *   gate_up        [E, 2I, H] weights: gate rows [0, I), up rows [I, 2I); K = H.
- *                  NVFP4/MXFP4: u8 [E, 2I, H/2]; FP8_BLOCK128: u8 e4m3 [E, 2I, H];
+ *                  NVFP4/MXFP4/Q4_0: u8 [E, 2I, H/2]; FP8_BLOCK128: u8 e4m3 [E, 2I, H];
  *                  BF16: bf16 [E, 2I, H].
  *   gate_up_scale  NVFP4: u8 e4m3 [E, 2I, H/16]; FP8_BLOCK128: f32 [E, 2I/128, H/128];
- *                  MXFP4: u8 e8m0 [E, 2I, H/32]; BF16: unused (NULL allowed).
+ *                  MXFP4: u8 e8m0 [E, 2I, H/32]; Q4_0: fp16 [E, 2I, H/32];
+ *                  BF16: unused (NULL allowed).
  *   gate_up_global NVFP4 only: f32 [E, 2I] (per output row); NULL otherwise.
- *   down           [E, H, I] weights; K = I.  NVFP4/MXFP4: u8 [E, H, I/2];
+ *   down           [E, H, I] weights; K = I.  NVFP4/MXFP4/Q4_0: u8 [E, H, I/2];
  *                  FP8_BLOCK128: u8 e4m3 [E, H, I]; BF16: bf16 [E, H, I].
  *   down_scale     NVFP4: u8 e4m3 [E, H, I/16]; FP8_BLOCK128: f32 [E, H/128, I/128];
- *                  MXFP4: u8 e8m0 [E, H, I/32]; BF16: unused (NULL allowed).
+ *                  MXFP4: u8 e8m0 [E, H, I/32]; Q4_0: fp16 [E, H, I/32];
+ *                  BF16: unused (NULL allowed).
  *   down_global    NVFP4 only: f32 [E, H]; NULL otherwise.
  * A rank that stores only its own slice passes that storage as a bank with I = hi - lo
  * and the slice [0, I) (PR #70: TP=1 is the identity layout).
@@ -131,7 +142,7 @@ typedef struct {
  *         them; dst's FP8_BLOCK128 scales and NVFP4 globals, when they are other buffers
  *         than src's, receive a plain copy.  The caller owns both banks' storage.
  * Requires 16 | 2I, 16 | H and whole 16-byte code pieces per row (H and I multiples of 32
- * for the FP4 formats, of 16 for FP8, of 8 for BF16).  Enqueued on `stream`; no host
+ * for the FP4 formats, of 16 for FP8, of 8 for BF16, of 128 for Q4_0).  Enqueued on `stream`; no host
  * synchronisation. */
 int moe_pack_bank(const moe_bank *src, const moe_bank *dst, void *stream);
 
@@ -235,7 +246,8 @@ size_t moe_workspace_bytes(const moe_bank *routed, const moe_bank *shared, int T
  *   routed      E-expert bank; shared: NULL or a 1-expert bank of the same format, H and I;
  *               both in MOE_LAYOUT_TILE16 (moe_pack_bank), else MOE_ERR_UNSUPPORTED.
  *   x_bf16      [T, H] bf16; topk_w [T, k] f32; al: the moe_align output for these ids.
- *   slice_lo/hi multiples of the format block (NVFP4 16, MXFP4 32, FP8_BLOCK128 128, BF16 1), with
+ *   slice_lo/hi multiples of the format block (NVFP4 16, MXFP4 32, FP8_BLOCK128 128, BF16 1,
+ *               Q4_0 32; the Q4_0 kernels need 128, else MOE_ERR_UNSUPPORTED), with
  *               0 <= lo < hi <= I (issue #62 "What it touches" item 2; PR #70 div_tp(...,
  *               multiple_of=128)).  The kernels additionally need (hi - lo) % 32 == 0.
  *   out         [T, H] f32 (out_dtype MOE_OUT_F32) or bf16 (MOE_OUT_BF16), overwritten.
@@ -243,7 +255,7 @@ size_t moe_workspace_bytes(const moe_bank *routed, const moe_bank *shared, int T
  * Experts that received no tokens are never read.  The align block size picks the kernels:
  * al->block_m a multiple of 128 runs NVFP4, FP8_BLOCK128 and BF16 on LDS-tiled GEMMs that reuse
  * each weight tile across 128 pair rows (for many tokens per expert); other block sizes,
- * and MXFP4, run the streaming kernels that read each selected weight byte once per
+ * and MXFP4 and Q4_0, run the streaming kernels that read each selected weight byte once per
  * 16-row block (for few tokens per expert).  Both compute the same result, except that the
  * tiled kernels round each weighted pair row topk_w * y to bf16 before the fp32 sum (the
  * pair rows are the layer's largest stream at many tokens; the streaming kernels keep

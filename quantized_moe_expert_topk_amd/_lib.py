@@ -15,7 +15,7 @@ MOE_ERR_UNSUPPORTED = -3
 MOE_ERR_WORKSPACE = -4
 MOE_ERR_HIP = -5
 
-MOE_FMT = {"nvfp4": 1, "fp8blk": 2, "mxfp4": 3, "bf16": 4}
+MOE_FMT = {"nvfp4": 1, "fp8blk": 2, "mxfp4": 3, "bf16": 4, "q4_0": 5}
 MOE_OUT_F32, MOE_OUT_BF16 = 0, 1
 MOE_LAYOUT_ROWS, MOE_LAYOUT_TILE16, MOE_LAYOUT_MXFP4_T = 0, 1, 2
 

@@ -89,8 +89,8 @@ def moe_pack_bank(bank: DeviceBank, stream=None) -> DeviceBank:
     def like(t, rows, cols):  # new storage, [E, rows, cols] of t's dtype
         return torch.empty((E, rows, cols), dtype=t.dtype, device=t.device)
 
-    if bank.fmt in ("nvfp4", "mxfp4"):  # codes and scales are reordered
-        sdiv = 16 if bank.fmt == "nvfp4" else 32
+    if bank.fmt in ("nvfp4", "mxfp4", "q4_0"):  # codes and scales are reordered
+        sdiv = 16 if bank.fmt == "nvfp4" else 32  # scale elements per row: K / sdiv
         gu, dn = like(bank.gate_up, 2 * I, H // 2), like(bank.down, H, I // 2)
         gus, dns = like(bank.gate_up_scale, 2 * I, H // sdiv), like(bank.down_scale, H, I // sdiv)
     else:  # codes only

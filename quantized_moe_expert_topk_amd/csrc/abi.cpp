@@ -64,6 +64,7 @@ int format_block(int fmt) {
     case MOE_FMT_FP8_BLOCK128: return 128;
     case MOE_FMT_MXFP4_E8M0: return 32;
     case MOE_FMT_BF16: return 1;
+    case MOE_FMT_Q4_0: return 32;
     default: return 0;
   }
 }
@@ -74,6 +75,7 @@ const char *format_name(int fmt) {
     case MOE_FMT_FP8_BLOCK128: return "FP8_BLOCK128";
     case MOE_FMT_MXFP4_E8M0: return "MXFP4_E8M0";
     case MOE_FMT_BF16: return "BF16";
+    case MOE_FMT_Q4_0: return "Q4_0";
     default: return "unknown";
   }
 }
@@ -111,6 +113,9 @@ int check_bank(const moe_bank *b, const char *name) {
   if (b->I % 32)
     return fail(MOE_ERR_UNSUPPORTED, "%s bank: I=%d must be a multiple of 32 (row pitch of 16-byte loads)",
                 name, b->I);
+  if (b->fmt == MOE_FMT_Q4_0 && b->I % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "%s bank: Q4_0 needs I=%d to be a multiple of 128 (4 blocks per piece row)",
+                name, b->I);
   if (b->layout != MOE_LAYOUT_TILE16)
     return fail(MOE_ERR_UNSUPPORTED, "%s bank: layout %d; the expert kernels read MOE_LAYOUT_TILE16 banks "
                 "(reorder once with moe_pack_bank)", name, b->layout);
@@ -121,7 +126,7 @@ int check_bank(const moe_bank *b, const char *name) {
 struct BankSizes {
   size_t gu, gus, gug, dn, dns, dng;
   uint32_t gu_pitch, gus_pitch, dn_pitch, dns_pitch;  // bytes per row (codes, FP4 scales)
-  int unit;                                           // FP4 scale bytes per 32-element piece
+  int unit;  // reordered scale bytes per unit: NVFP4 2, MXFP4 1 (per 32 elements), Q4_0 8 (per 128)
 };
 
 BankSizes bank_sizes(const moe_bank *b) {
@@ -137,9 +142,9 @@ BankSizes bank_sizes(const moe_bank *b) {
   } else if (fp8) {
     z.gus = E * (2 * I / 128) * (H / 128) * 4;
     z.dns = E * (H / 128) * (I / 128) * 4;
-  } else {
-    const size_t sdiv = b->fmt == MOE_FMT_NVFP4 ? 16 : 32;
-    z.unit = b->fmt == MOE_FMT_NVFP4 ? 2 : 1;
+  } else {  // per-row scales: NVFP4 one byte per 16, MXFP4 one byte per 32, Q4_0 fp16 per 32
+    const size_t sdiv = b->fmt == MOE_FMT_NVFP4 ? 16 : b->fmt == MOE_FMT_Q4_0 ? 16 : 32;
+    z.unit = b->fmt == MOE_FMT_NVFP4 ? 2 : b->fmt == MOE_FMT_Q4_0 ? 8 : 1;
     z.gus_pitch = (uint32_t)(H / sdiv);
     z.dns_pitch = (uint32_t)(I / sdiv);
     z.gus = E * 2 * I * z.gus_pitch;
@@ -166,6 +171,8 @@ int check_slice(const moe_bank *b, int lo, int hi) {
                 format_name(b->fmt), blk);
   if (lo % 32 || hi % 32)
     return fail(MOE_ERR_UNSUPPORTED, "slice [%d, %d): the kernels need lo and hi multiples of 32", lo, hi);
+  if (b->fmt == MOE_FMT_Q4_0 && (lo % 128 || hi % 128))
+    return fail(MOE_ERR_UNSUPPORTED, "slice [%d, %d): the Q4_0 kernels need lo and hi multiples of 128", lo, hi);
   return MOE_OK;
 }
 
@@ -241,7 +248,7 @@ int check_forward(const moe_bank *routed, const moe_bank *shared, int T, int k, 
       2LL * routed->I * routed->H >= (1LL << 31))
     return fail(MOE_ERR_UNSUPPORTED, "tensor exceeds 2 GiB (32-bit buffer offsets)");
   *plan = plan_forward(routed, shared, T, k, al->capacity, lo, hi);
-  plan->tiled = al->block_m % 128 == 0 && routed->fmt != MOE_FMT_MXFP4_E8M0;
+  plan->tiled = al->block_m % 128 == 0 && routed->fmt != MOE_FMT_MXFP4_E8M0 && routed->fmt != MOE_FMT_Q4_0;
   if (workspace_bytes < plan->total)
     return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, plan->total);
   if (!workspace && plan->total) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
@@ -480,7 +487,9 @@ int moe_pack_bank(const moe_bank *src, const moe_bank *dst, void *stream) {
     return fail(MOE_ERR_INVALID_ARG, "moe_pack_bank: src and dst differ in fmt, E, H or I");
   if (src->E < 1 || src->H < 1 || src->I < 1)
     return fail(MOE_ERR_INVALID_ARG, "moe_pack_bank: E=%d H=%d I=%d must be positive", src->E, src->H, src->I);
-  const int piece = src->fmt == MOE_FMT_BF16 ? 8 : src->fmt == MOE_FMT_FP8_BLOCK128 ? 16 : 32;  // per 16-byte piece
+  // elements per 16-byte piece (Q4_0: a piece row of 4 pieces covers 4 whole blocks)
+  const int piece = src->fmt == MOE_FMT_BF16 ? 8 : src->fmt == MOE_FMT_FP8_BLOCK128 ? 16
+                    : src->fmt == MOE_FMT_Q4_0 ? 128 : 32;
   if (src->H % piece || src->I % piece || src->H % 128 || (src->fmt == MOE_FMT_FP8_BLOCK128 && src->I % 128))
     return fail(MOE_ERR_UNSUPPORTED, "moe_pack_bank: H=%d and I=%d need whole %d-element pieces per row", src->H,
                 src->I, piece);
@@ -496,11 +505,13 @@ int moe_pack_bank(const moe_bank *src, const moe_bank *dst, void *stream) {
       return fail(MOE_ERR_INVALID_ARG, "moe_pack_bank: weight codes must be 16-byte aligned");
   }
   const BankSizes z = bank_sizes(src);
+  // fp4: per-row scales that are reordered with the codes (NVFP4, MXFP4, Q4_0)
   const bool fp8 = src->fmt == MOE_FMT_FP8_BLOCK128, fp4 = !fp8 && src->fmt != MOE_FMT_BF16;
+  const bool q4 = src->fmt == MOE_FMT_Q4_0;
   if (overlap(src->gate_up, z.gu, dst->gate_up, z.gu) || overlap(src->down, z.dn, dst->down, z.dn) ||
       (fp4 && (overlap(src->gate_up_scale, z.gus, dst->gate_up_scale, z.gus) ||
                 overlap(src->down_scale, z.dns, dst->down_scale, z.dns))))
-    return fail(MOE_ERR_INVALID_ARG, "moe_pack_bank: dst codes or FP4 scales overlap src");
+    return fail(MOE_ERR_INVALID_ARG, "moe_pack_bank: dst codes or scales overlap src");
   int rc = check_device();
   if (rc) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -517,11 +528,19 @@ int moe_pack_bank(const moe_bank *src, const moe_bank *dst, void *stream) {
     }
     return ok();
   }
-  rc = hip_status(qmoe::launch_pack_tile16(src->gate_up, const_cast<void *>(dst->gate_up), E * 2 * I, z.gu_pitch,
-                                           16, s), "pack launch");
-  if (rc) return rc;
-  rc = hip_status(qmoe::launch_pack_tile16(src->down, const_cast<void *>(dst->down), E * H, z.dn_pitch, 16, s),
-                  "pack launch");
+  if (q4) {  // codes: nibble order changes too
+    rc = hip_status(qmoe::launch_pack_q4_0(src->gate_up, const_cast<void *>(dst->gate_up), E * 2 * I, z.gu_pitch, s),
+                    "pack launch");
+    if (rc) return rc;
+    rc = hip_status(qmoe::launch_pack_q4_0(src->down, const_cast<void *>(dst->down), E * H, z.dn_pitch, s),
+                    "pack launch");
+  } else {
+    rc = hip_status(qmoe::launch_pack_tile16(src->gate_up, const_cast<void *>(dst->gate_up), E * 2 * I,
+                                             z.gu_pitch, 16, s), "pack launch");
+    if (rc) return rc;
+    rc = hip_status(qmoe::launch_pack_tile16(src->down, const_cast<void *>(dst->down), E * H, z.dn_pitch, 16, s),
+                    "pack launch");
+  }
   if (rc) return rc;
   if (fp4) {
     rc = hip_status(qmoe::launch_pack_tile16(src->gate_up_scale, const_cast<void *>(dst->gate_up_scale), E * 2 * I,

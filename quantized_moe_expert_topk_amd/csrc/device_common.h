@@ -109,6 +109,20 @@ __device__ __forceinline__ void fp4x8_pow2_to_bf16(uint32_t codes, float pow2, f
   out.h[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, pow2, 3);
 }
 
+// Q4_0 codes of 8 elements (one dword: element 2i in bits [4i, 4i+4), element 2i+1 in bits
+// [16+4i, 20+4i)) -> 8 bf16 of 128 + q.  0x4300 is bf16 128, whose last mantissa bit is
+// worth 1, so or-ing a 4-bit code into the mantissa adds it exactly.
+__device__ __forceinline__ void q4x8_to_bf16_biased(uint32_t d, frag8 &out) {
+  out.u[0] = (d & 0x000F000Fu) | 0x43004300u;
+  out.u[1] = ((d >> 4) & 0x000F000Fu) | 0x43004300u;
+  out.u[2] = ((d >> 8) & 0x000F000Fu) | 0x43004300u;
+  out.u[3] = ((d >> 12) & 0x000F000Fu) | 0x43004300u;
+}
+
+__device__ __forceinline__ float f16_to_f32(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits & 0xFFFFu));
+}
+
 // 8 e4m3 codes (two dwords, element i in byte i) -> 8 bf16 (exact).
 __device__ __forceinline__ void fp8x8_to_bf16(uint32_t lo, uint32_t hi, frag8 &out) {
   out.h[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
@@ -143,6 +157,10 @@ __device__ __forceinline__ uint32_t buf_load1(rsrc_t r, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
 }
 
+__device__ __forceinline__ uint2 buf_load8(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
+
 __device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
 }
@@ -167,6 +185,9 @@ __device__ __forceinline__ WMat<FMT> weight_matrix(const uint8_t *codes, const u
   } else if constexpr (FMT == MOE_FMT_MXFP4_E8M0) {
     m.codes = make_rsrc(codes + (size_t)e * rows * (K / 2), (uint32_t)rows * (K / 2));
     m.scales = make_rsrc(scales + (size_t)e * rows * (K / 32), (uint32_t)rows * (K / 32));
+  } else if constexpr (FMT == MOE_FMT_Q4_0) {  // fp16 scale per 32 elements
+    m.codes = make_rsrc(codes + (size_t)e * rows * (K / 2), (uint32_t)rows * (K / 2));
+    m.scales = make_rsrc(scales + (size_t)e * rows * (K / 16), (uint32_t)rows * (K / 16));
   } else if constexpr (FMT == MOE_FMT_BF16) {
     m.codes = make_rsrc(codes + (size_t)e * rows * K * 2, (uint32_t)rows * K * 2);
     m.scales = m.codes;  // unused

@@ -14,6 +14,9 @@
 //              to the fp32 accumulator in the epilogue.
 //   FP8_BLOCK  e4m3 -> bf16 exact; the fp32 128x128 block scale multiplies each 128-wide
 //              K chunk's partial sum.
+//   BF16       used as stored.
+//   Q4_0       codes -> bf16 128 + q exactly; the -136 offset and the fp16 block scale are
+//              applied per 32-wide block to the fp32 MFMA results (mma_run).
 // MXFP4 (e8m0 per 32) runs on the native scaled MFMA v_mfma_scale_f32_16x16x128_f8f6f4: the
 // raw e2m1 codes and e8m0 bytes are the B operand and its scales, with no dequantization.
 // Its A operand cannot be 16-bit, so x (and h) are carried as two e4m3 planes with e8m0
@@ -163,10 +166,18 @@ __device__ __forceinline__ uint32_t scale_tile_off(uint32_t row, uint32_t K) {
 // FP8: lane group g takes [16 g, 16 g + 16) and [64 + 16 g, +16), so each of the two code
 // loads covers 4 consecutive pieces of every tile row (one 1 KB run per tile).  BF16: MFMA q
 // of the step takes [32 q, 32 q + 32), lane group g its 8 elements [32 q + 8 g, +8) (pieces
-// 4q..4q+3: again one 1 KB run per tile and MFMA, no dequantization).  Either way
+// 4q..4q+3: again one 1 KB run per tile and MFMA, no dequantization).  Q4_0: MFMA q of the
+// step is block q (K [32 q, 32 q + 32)), lane group g its elements [8 g, 8 g + 8); the lane's
+// one 16-byte piece (step, g) holds one dword of each of the 4 blocks.  Either way
 // every MFMA stays inside one 128x128 FP8 scale block.  Positions at or past kvalid
 // (relative to kw0) contribute zero and load from clamped in-bounds offsets.  Steps are
-// taken in groups of 2 (FP4) or 1 (FP8) whose loads are all issued before decoding.
+// taken in groups of 2 (FP4, Q4_0) or 1 (FP8, BF16) whose loads are all issued before decoding.
+// Q4_0 keeps the weights exact in bf16 without a subtraction per weight: the codes become
+// bf16 128 + q by bit operations alone, and since (q - 8) d = ((128 + q) - 136) d, block q's
+// partial sum is d (x . (128 + q) - 136 sum(x)), where the second term is one MFMA of x
+// against a constant -136 operand per block, shared by the NT tiles and fed in as the
+// accumulator input of each tile's MFMA; d (fp16, per weight row and block) then scales the
+// fp32 result.  kvalid is a multiple of 128 for Q4_0 (whole steps).
 //   ra, a_row: activation buffer and the byte offset of this lane's row; a row past the
 //              buffer end reads as zeros without a memory request (padding rows)
 //   m, rows:   weight matrix (tile-16 layout) and this lane's row of each tile (the NT
@@ -183,7 +194,8 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
   static_assert(!F16 || FMT == MOE_FMT_NVFP4, "the f16 path is for NVFP4 weights");
   constexpr bool FP4 = FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_MXFP4_E8M0;
   constexpr bool BF16 = FMT == MOE_FMT_BF16;
-  constexpr int NPF = FP4 ? 2 : 1;
+  constexpr bool Q4 = FMT == MOE_FMT_Q4_0;
+  constexpr int NPF = (FP4 || Q4) ? 2 : 1;
   constexpr int SP = FMT == MOE_FMT_NVFP4 ? 2 : 1;
   const uint32_t K = (uint32_t)m.K;
   const int lane = lane_id(), r = lane & 15;
@@ -191,7 +203,8 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
 #pragma unroll
   for (int t = 0; t < NT; t++) {
     cb[t] = code_tile_off<FMT>(rows[t], K);
-    sb[t] = FP4 ? scale_tile_off<FMT>(rows[t], K) : 0;
+    // Q4_0 scales: tile-16 order in units of one step's 4 fp16 (8 bytes)
+    sb[t] = FP4 ? scale_tile_off<FMT>(rows[t], K) : Q4 ? (rows[t] & ~15u) * (K / 16) + (rows[t] & 15u) * 8 : 0;
   }
   constexpr int RB = FP4 ? 4 * COUNT * SP : 16;  // staged scale bytes per lane (16 lanes per tile)
   constexpr int SQ = RB / 16;
@@ -209,6 +222,7 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
     uint4 c0[NPF][NT], c1[NPF][NT], c2[NPF][NT], c3[NPF][NT];
     uint32_t lsv[NPF][NT];
     float bs[NPF][NT];
+    uint2 qsv[NPF][NT];  // Q4_0: the 4 fp16 block scales of the step
 #pragma unroll
     for (int ii = 0; ii < NPF; ii++) {
       const int i = i0 + ii;
@@ -225,6 +239,16 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
 #pragma unroll
           for (int t = 0; t < NT; t++)
             lsv[ii][t] = SP == 2 ? buf_load2(m.scales, sb[t] + pc * 32) : buf_load1(m.scales, sb[t] + pc * 16);
+        }
+      } else if constexpr (Q4) {
+        const int kc = kw0 + (128 * i < kvalid ? 128 * i : 0);  // the step
+#pragma unroll
+        for (int q = 0; q < 4; q++) ar[ii].q[q] = buf_load16(ra, a_row + (kc + 32 * q + 8 * g) * 2);
+        const uint32_t st = (uint32_t)(b_k0 + kc) / 128;
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+          c0[ii][t] = buf_load16(m.codes, cb[t] + (4 * st + g) * 256);
+          qsv[ii][t] = buf_load8(m.scales, sb[t] + st * 128);
         }
       } else if constexpr (BF16) {
         const int kc = kw0 + (128 * i < kvalid ? 128 * i : 0);  // the step
@@ -288,6 +312,29 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
           bf16x8_to_f16(ar[ii].q[q], av[q]);  // once per chunk, shared by the NT tiles
         else
           av[q].q = ar[ii].q[q];
+      }
+      if constexpr (Q4) {
+        if (128 * i >= kvalid) continue;  // wave-uniform: a whole step past the range
+        frag8 neg;  // bf16 -136 in every slot
+        neg.q = make_uint4(0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u);
+        f32x4_t ns[4];
+#pragma unroll
+        for (int q = 0; q < 4; q++) ns[q] = mfma_bf16(av[q], neg, zero4());
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+          const uint32_t dw[4] = {c0[ii][t].x, c0[ii][t].y, c0[ii][t].z, c0[ii][t].w};
+          const float d[4] = {f16_to_f32(qsv[ii][t].x), f16_to_f32(qsv[ii][t].x >> 16), f16_to_f32(qsv[ii][t].y),
+                              f16_to_f32(qsv[ii][t].y >> 16)};
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            frag8 bq;
+            q4x8_to_bf16_biased(dw[q], bq);
+            const f32x4_t tmp = mfma_bf16(av[q], bq, ns[q]);
+#pragma unroll
+            for (int j = 0; j < 4; j++) acc[t][j] += d[q] * tmp[j];
+          }
+        }
+        continue;
       }
 #pragma unroll
       for (int t = 0; t < NT; t++) {
@@ -499,7 +546,7 @@ __global__ __launch_bounds__(64 * KW, kMinWaves) void k_gate_up(GateUpArgs a) {
   __shared__ float red[KW][2 * GT][4][64];  // [wave][tile][j][lane]
   __shared__ float hbuf[16][GCOLS + 1];      // MXFP4: the block's h before the plane split
   // FP4: per wave, the scale bytes of the workgroup's 2*GCOLS weight rows over one run
-  __shared__ __attribute__((aligned(16))) uint8_t lsc[(FMT == MOE_FMT_FP8_BLOCK128 || FMT == MOE_FMT_BF16) ? 16 : KW * 2 * GCOLS * (128 * COUNT / (FMT == MOE_FMT_NVFP4 ? 16 : 32))];
+  __shared__ __attribute__((aligned(16))) uint8_t lsc[(FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_MXFP4_E8M0) ? KW * 2 * GCOLS * (128 * COUNT / (FMT == MOE_FMT_NVFP4 ? 16 : 32)) : 16];
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int sb = blockIdx.x;
@@ -639,7 +686,7 @@ constexpr int DNT = 4;
 template <int FMT, int COUNT>
 __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
   // FP4: per wave, the scale bytes of its 16*DNT weight rows over one run
-  __shared__ __attribute__((aligned(16))) uint8_t lsc[(FMT == MOE_FMT_FP8_BLOCK128 || FMT == MOE_FMT_BF16) ? 16 : 4 * 16 * DNT * (128 * COUNT / (FMT == MOE_FMT_NVFP4 ? 16 : 32))];
+  __shared__ __attribute__((aligned(16))) uint8_t lsc[(FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_MXFP4_E8M0) ? 4 * 16 * DNT * (128 * COUNT / (FMT == MOE_FMT_NVFP4 ? 16 : 32)) : 16];
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int sb = blockIdx.x;
@@ -829,6 +876,7 @@ hipError_t launch_gate_up(int fmt, const GateUpArgs &a, int n_shared_sub, hipStr
     case MOE_FMT_NVFP4: launch_gate_up_fmt<MOE_FMT_NVFP4>(a, grid, s); break;
     case MOE_FMT_MXFP4_E8M0: launch_gate_up_fmt<MOE_FMT_MXFP4_E8M0>(a, grid, s); break;
     case MOE_FMT_BF16: launch_gate_up_fmt<MOE_FMT_BF16>(a, grid, s); break;
+    case MOE_FMT_Q4_0: launch_gate_up_fmt<MOE_FMT_Q4_0>(a, grid, s); break;
     default: launch_gate_up_fmt<MOE_FMT_FP8_BLOCK128>(a, grid, s); break;
   }
   return hipGetLastError();
@@ -850,6 +898,7 @@ hipError_t launch_down(int fmt, const DownArgs &a, int n_shared_sub, hipStream_t
     case MOE_FMT_NVFP4: launch_down_fmt<MOE_FMT_NVFP4>(a, grid, s); break;
     case MOE_FMT_MXFP4_E8M0: launch_down_fmt<MOE_FMT_MXFP4_E8M0>(a, grid, s); break;
     case MOE_FMT_BF16: launch_down_fmt<MOE_FMT_BF16>(a, grid, s); break;
+    case MOE_FMT_Q4_0: launch_down_fmt<MOE_FMT_Q4_0>(a, grid, s); break;
     default: launch_down_fmt<MOE_FMT_FP8_BLOCK128>(a, grid, s); break;
   }
   return hipGetLastError();

@@ -64,12 +64,14 @@ hipError_t launch_down(int fmt, const DownArgs &a, int n_shared_sub, hipStream_t
 hipError_t launch_gate_up_tiled(int fmt, const GateUpArgs &a, int n_shared_tiles, hipStream_t s);
 hipError_t launch_down_tiled(int fmt, const DownArgs &a, int n_shared_tiles, hipStream_t s);
 // moe_pack_bank: [rows, pitch] bytes -> 16-row tiles stored piece-major in units of `unit`
-// (16, 2 or 1) bytes.
+// (16, 8, 2 or 1) bytes.
 hipError_t launch_pack_tile16(const void *src, void *dst, size_t rows, uint32_t pitch, int unit, hipStream_t s);
 // Same destination order from E column-major matrices: src[e] is [pitch, N] bytes (row n of
 // the destination = column n of the source), unit 16 or 1.
 hipError_t launch_pack_tile16_t(const void *src, void *dst, size_t E, size_t N, uint32_t pitch, int unit,
                                 hipStream_t s);
+// Q4_0 codes [rows, pitch] -> the tile-16 piece order with the nibbles regrouped per piece.
+hipError_t launch_pack_q4_0(const void *src, void *dst, size_t rows, uint32_t pitch, hipStream_t s);
 hipError_t launch_act_mx8(const uint16_t *x, int rows, int K, uint8_t *q, uint8_t *sc, hipStream_t s);
 // Y rows in fp32 (streaming kernels) or bf16 (tiled kernels).
 hipError_t launch_combine(const void *Y, bool y_bf16, int T, int k, int H, int has_shared, void *out, int out_bf16,

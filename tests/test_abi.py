@@ -80,6 +80,9 @@ def _fwd(bank=None, shared=None, T=16, k=2, lo=0, hi=128, al=None, ws=1 << 30, o
     (dict(bank=_bank(fmt=2, I=192), hi=128), L.MOE_ERR_ALIGNMENT),  # fp8-block I % 128
     (dict(bank=_bank(fmt=2, I=256), lo=64, hi=192), L.MOE_ERR_ALIGNMENT),  # fp8-block slice % 128
     (dict(bank=_bank(fmt=3), lo=16, hi=128), L.MOE_ERR_ALIGNMENT),  # MXFP4 block is 32
+    (dict(bank=_bank(fmt=5, glob=False, I=256), lo=16, hi=128), L.MOE_ERR_ALIGNMENT),  # Q4_0 block is 32
+    (dict(bank=_bank(fmt=5, glob=False, I=256), lo=32, hi=160), L.MOE_ERR_UNSUPPORTED),  # Q4_0 kernels: 128
+    (dict(bank=_bank(fmt=5, glob=False, I=96), hi=96), L.MOE_ERR_UNSUPPORTED),  # Q4_0 bank I % 128
     (dict(al=_align(bm=8)), L.MOE_ERR_UNSUPPORTED),
     (dict(al=_align(cap=32)), L.MOE_ERR_INVALID_ARG),
     (dict(shared=_bank(E=2)), L.MOE_ERR_INVALID_ARG),          # shared must be one expert
@@ -146,6 +149,8 @@ def _pack(src, dst):
     (_bank(layout=L.MOE_LAYOUT_ROWS, I=48), _bank(I=48, base=0x40000000), L.MOE_ERR_UNSUPPORTED),  # half pieces
     (_bank(fmt=9, layout=L.MOE_LAYOUT_ROWS), _bank(fmt=9, base=0x40000000), L.MOE_ERR_INVALID_ARG),
     (_bank(fmt=1, layout=L.MOE_LAYOUT_MXFP4_T), _bank(base=0x40000000), L.MOE_ERR_INVALID_ARG),  # NVFP4 transposed
+    (_bank(fmt=5, glob=False, I=64, layout=L.MOE_LAYOUT_ROWS), _bank(fmt=5, glob=False, I=64, base=0x40000000),
+     L.MOE_ERR_UNSUPPORTED),  # Q4_0 pieces hold 4 whole blocks: I % 128
 ])
 def test_pack_bank_rejects_bad_arguments_before_any_launch(src, dst, code):
     rc, msg = _pack(src, dst)

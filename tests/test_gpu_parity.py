@@ -183,6 +183,43 @@ def test_pack_bank_is_the_tile16_permutation(fmt, E, H, I):
         np.testing.assert_array_equal(pk.down_global.cpu().numpy(), b.down_global)
 
 
+def q4_0_pieces_np(a: np.ndarray) -> np.ndarray:
+    """The MOE_LAYOUT_TILE16 bytes of row-major q4_0 codes [rows, H/2], written from the layout's
+    definition: piece (s, g) of a row holds one little-endian dword per block 4s+q, made of that
+    block's elements 8g..8g+7 (element 8g+2i at bit 4i, element 8g+2i+1 at bit 16+4i), and the
+    pieces go to their tile-16 places like any 16-byte unit."""
+    R, P = a.shape
+    blk = a.reshape(R, P // 16, 16)
+    el = np.concatenate([blk & 0xF, blk >> 4], axis=2).astype(np.uint32)  # [R, block, element]
+    el = el.reshape(R, P // 64, 4, 4, 8)                                    # [R, s, q, g, j]
+    j = np.arange(8)
+    shift = np.where(j % 2 == 0, 4 * (j // 2), 16 + 4 * (j // 2)).astype(np.uint32)
+    dw = (el << shift).sum(axis=-1, dtype=np.uint32)                        # disjoint bits
+    rows = np.ascontiguousarray(dw.transpose(0, 1, 3, 2)).astype("<u4").reshape(R, -1).view(np.uint8)
+    return tile16_np(rows, 16)
+
+
+def test_pack_bank_q4_0_regroups_nibbles():
+    """Q4_0 codes are regrouped per 16-byte piece (bit-exact against the layout written out
+    above); the fp16 scales move in units of one step's 4 scales (8 bytes)."""
+    b = S.routed_bank(19, "q4_0", 3, 256, 128)
+    pk = device_bank(b, packed=True)
+    torch.cuda.synchronize()
+
+    def rows2d(a):
+        a = np.ascontiguousarray(a)
+        return a.view(np.uint8).reshape(a.shape[0] * a.shape[1], -1)
+
+    def got(t):
+        a = t.cpu().numpy()
+        return a.view(np.uint8).reshape(a.shape[0] * a.shape[1], -1)
+
+    np.testing.assert_array_equal(got(pk.gate_up), q4_0_pieces_np(rows2d(b.gate_up)))
+    np.testing.assert_array_equal(got(pk.down), q4_0_pieces_np(rows2d(b.down)))
+    np.testing.assert_array_equal(got(pk.gate_up_scale), tile16_np(rows2d(b.gate_up_scale), 8))
+    np.testing.assert_array_equal(got(pk.down_scale), tile16_np(rows2d(b.down_scale), 8))
+
+
 def _transposed_mx(b):
     """The MOE_LAYOUT_MXFP4_T arrays of a row-major MXFP4 bank: codes [E, K/2, N], scales [E, K/32, N]."""
     return tuple(np.ascontiguousarray(a.transpose(0, 2, 1)) for a in (b.gate_up, b.gate_up_scale, b.down, b.down_scale))
@@ -257,7 +294,9 @@ FORWARD_CASES = [(1, 16, (0, 128)), (1, 16, (0, 64)), (1, 16, (64, 128)),
                  # MXFP4 slices off the 128-wide chunk grid: a masked K tail, unaligned scale spans
                  (5, 16, (0, 96)), (5, 16, (32, 160)), (5, 1, (992, 2048)),
                  # bf16 stacked experts (issue #62 "Suggested staging" item 1)
-                 (6, 1, (0, 256)), (6, 64, (0, 256)), (6, 16, (32, 160)), (6, 8, (0, 512))]
+                 (6, 1, (0, 256)), (6, 64, (0, 256)), (6, 16, (32, 160)), (6, 8, (0, 512)),
+                 # q4_0 experts (issue #62 "Suggested staging" item 3), no shared expert
+                 (7, 1, (0, 256)), (7, 64, (0, 256)), (7, 16, (128, 384)), (7, 8, (0, 512)), (7, 3, (384, 512))]
 
 
 @pytest.mark.parametrize("cid,T,sl", FORWARD_CASES)
@@ -345,7 +384,8 @@ def test_full_layer_matches_oracle(cid, T, sl):
 
 
 @pytest.mark.parametrize("cid,T,cuts", [(1, 16, (0, 64, 128)), (2, 64, (0, 256, 512)), (4, 64, (0, 256, 512)),
-                                        (2, 8, (0, 128, 384, 512)), (5, 16, (0, 96, 1024, 2048))])
+                                        (2, 8, (0, 128, 384, 512)), (5, 16, (0, 96, 1024, 2048)),
+                                        (7, 16, (0, 128, 384, 512))])
 def test_gpu_slices_sum_to_gpu_full(cid, T, cuts):
     """Linearity in the intermediate index on the GPU: disjoint slices tiling [0, I) sum to
     the unsliced GPU result (issue #520 section 4)."""
