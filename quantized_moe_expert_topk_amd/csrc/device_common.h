@@ -36,6 +36,17 @@ __device__ __forceinline__ f32x4_t mfma_bf16(const frag8 &a, const frag8 &b, f32
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
 }
 
+// v_mfma_f32_32x32x16_bf16 (wave64, lane l, h = l / 32, i = 0..7, j = 0..15), as measured:
+//   A (32x16): lane l holds A[l % 32][8 h + i];  B (16x32): lane l holds B[8 h + i][l % 32]
+//   D (32x32): lane l register j holds D[8 (j / 4) + 4 h + j % 4][l % 32]
+// One wave issuing these back to back keeps the matrix core near its peak, which the
+// 16x16x32 form does not reach with a single wave per SIMD.
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+__device__ __forceinline__ f32x16_t mfma32_bf16(const frag8 &a, const frag8 &b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ f32x4_t mfma_f16(const frag8 &a, const frag8 &b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a.f, b.f, c, 0, 0, 0);
 }

@@ -1,4 +1,5 @@
-// expert_tiled.hip -- the expert GEMMs for many tokens per expert (prefill), gfx950.
+// expert_tiled.hip -- fp8-block and bf16 expert GEMMs for many tokens per expert (prefill),
+// and the router GEMM for many tokens, gfx950.  (NVFP4 prefill runs in expert_wide.hip.)
 //
 // Same computation as expert.hip (gate rows [lo,hi), up rows [I+lo, I+hi), down columns
 // [lo,hi) of one rank's slice: FreeToken issue #62 "What it touches" item 1; SwiGLU expert
@@ -10,8 +11,7 @@
 // on v_mfma_f32_16x16x32_bf16.  LDS is double buffered: the global loads of stage s+1 are
 // in flight while stage s multiplies, and one barrier per stage separates the buffers.
 //
-//   NVFP4      e2m1 * e4m3 group scale, exact in bf16; the per-row fp32 global is applied
-//              in the epilogue (W4A16).
+//   BF16       used as stored.
 //   FP8_BLOCK  e4m3 -> bf16 exact; each 128-wide K block's partial product is scaled by
 //              its fp32 weight_scale_inv and added to the accumulator (W8A16).
 #include "device_common.h"
@@ -86,10 +86,10 @@ constexpr int kFmtBf16 = 0;
 // stage (WK weights).  The quantized weights are in the tile-16 layout (MOE_LAYOUT_TILE16:
 // 16-row tiles stored piece-major, a piece = 16 code bytes), and a 32-thread group covers
 // one tile: threads 0-15 its rows' part 0, threads 16-31 the same rows' part 1, two
-// adjacent 256-byte pieces (one 512-byte run).  NVFP4 with TK 32 (8 bytes per thread, half
-// a piece) and the row-major bf16 router weights pair the threads of a row instead.
+// adjacent 256-byte pieces (one 512-byte run).  The row-major bf16 router weights pair the
+// threads of a row instead.
 template <int FMT, int TK>
-constexpr bool kPairMap = FMT == kFmtBf16 || (FMT == MOE_FMT_NVFP4 && TK == 32);
+constexpr bool kPairMap = FMT == kFmtBf16;
 
 template <int FMT, int TK>
 __device__ __forceinline__ int b_row_of(int tid) {
@@ -102,13 +102,10 @@ __device__ __forceinline__ int b_half_of(int tid) {
 }
 
 struct BTile {
-  uint4 c0, c1, c2, c3;  // codes: WK/2 bytes (FP4), WK bytes (FP8) or 2*WK bytes (bf16)
-  uint32_t sc;           // NVFP4: the e4m3 scales of the WK/16 groups
+  uint4 c0, c1, c2, c3;  // codes: WK bytes (FP8) or 2*WK bytes (bf16)
 };
 
 // Loads part `half` of the stage starting at K offset ks (a multiple of TK) of matrix row `row`:
-//   NVFP4 TK 64: piece ks/32 + half (32 elements) and its 2 scale bytes
-//   NVFP4 TK 32: bytes [8 half, 8 half + 8) of piece ks/32 and its scale byte `half`
 //   FP8   TK 64: pieces ks/16 + half and ks/16 + half + 2 (16 elements each)
 //   FP8   TK 32: piece ks/16 + half
 //   BF16 (tile-16 bank) TK 64: pieces ks/8 + 4 half + {0..3};  TK 32: ks/8 + 2 half + {0,1}
@@ -116,21 +113,7 @@ struct BTile {
 template <int FMT, int TK>
 __device__ __forceinline__ void b_fetch(const WMat<FMT> &m, uint32_t row, int ks, int half, BTile &t) {
   const uint32_t K = (uint32_t)m.K;
-  if constexpr (FMT == MOE_FMT_NVFP4) {
-    const uint32_t cb = (row & ~15u) * (K / 2) + (row & 15u) * 16;
-    const uint32_t sb = (row & ~15u) * (K / 16) + (row & 15u) * 2;
-    if constexpr (TK == 64) {
-      const uint32_t pc = (uint32_t)ks / 32 + half;
-      t.sc = buf_load2(m.scales, sb + pc * 32);
-      t.c0 = buf_load16(m.codes, cb + pc * 256);
-    } else {
-      const uint32_t pc = (uint32_t)ks / 32;
-      t.sc = buf_load1(m.scales, sb + pc * 32 + half);
-      const uint2 v = __builtin_bit_cast(
-          uint2, __builtin_amdgcn_raw_buffer_load_b64(m.codes, (int)(cb + pc * 256 + 8 * half), 0, 0));
-      t.c0 = make_uint4(v.x, v.y, 0, 0);
-    }
-  } else if constexpr (FMT == MOE_FMT_BF16) {
+  if constexpr (FMT == MOE_FMT_BF16) {
     const uint32_t cb = (row & ~15u) * (2 * K) + (row & 15u) * 16;
     const uint32_t pc = (uint32_t)ks / 8 + (TK / 16) * half;
     t.c0 = buf_load16(m.codes, cb + pc * 256);
@@ -161,16 +144,7 @@ template <int FMT, int TK>
 __device__ __forceinline__ void b_store(uint16_t *rowp, int row, int half, const BTile &t, bool valid) {
   constexpr int NC = Stage<TK>::WK / 8;
   frag8 f[NC];
-  if constexpr (FMT == MOE_FMT_NVFP4) {
-    const float s0 = e4m3_to_f32(t.sc & 0xFFu);
-    fp4x8_mul_to_bf16(t.c0.x, s0, f[0]);
-    fp4x8_mul_to_bf16(t.c0.y, s0, f[1]);
-    if constexpr (NC == 4) {
-      const float s1 = e4m3_to_f32((t.sc >> 8) & 0xFFu);
-      fp4x8_mul_to_bf16(t.c0.z, s1, f[2]);
-      fp4x8_mul_to_bf16(t.c0.w, s1, f[3]);
-    }
-  } else if constexpr (FMT == kFmtBf16 || FMT == MOE_FMT_BF16) {
+  if constexpr (FMT == kFmtBf16 || FMT == MOE_FMT_BF16) {
     f[0].q = t.c0;
     f[1].q = t.c1;
     if constexpr (NC == 4) {
@@ -324,7 +298,6 @@ __global__ __launch_bounds__(256, 2) void k_gate_up_tiled(GateUpArgs a) {
   const int c0 = blockIdx.y * 64;
   int p0, e;
   const uint8_t *codes, *scales;
-  const float *glob;
   if (!is_shared) {
     p0 = blockIdx.x * TM;
     const int tp = a.total_padded[0], eb = a.block_expert[p0 / a.block_m];  // both in flight (p0 < cap)
@@ -333,13 +306,11 @@ __global__ __launch_bounds__(256, 2) void k_gate_up_tiled(GateUpArgs a) {
     if (e < 0) return;
     codes = a.gu;
     scales = a.gus;
-    glob = a.gug;
   } else {
     p0 = a.cap + (blockIdx.x - n_routed) * TM;
     e = 0;
     codes = a.sgu;
     scales = a.sgus;
-    glob = a.sgug;
   }
   const int T = a.T, H = a.H, I = a.I, Il = a.Il, P = a.T * a.k;
   const WMat<FMT> m = weight_matrix<FMT>(codes, scales, e, 2 * I, H);
@@ -369,15 +340,7 @@ __global__ __launch_bounds__(256, 2) void k_gate_up_tiled(GateUpArgs a) {
     return buf_load_f32(m.scales, (uint32_t)((wr / 128) * (H / 128) + kb) * 4);
   };
   tiled_k_loop<FMT, TK>(lds, ra, a_off, m, wrow, wvalid, 0, H / TK, H, brow, scale, acc);
-  // epilogue: per-row globals (NVFP4), SwiGLU, h in bf16
-  float gg[2], ug[2];
-#pragma unroll
-  for (int j = 0; j < 2; j++) {
-    const int col = c0 + 32 * wn + 16 * j + r;
-    const int cc = col < Il ? col : c0;
-    gg[j] = FMT == MOE_FMT_NVFP4 ? glob[(size_t)e * 2 * I + a.lo + cc] : 1.f;
-    ug[j] = FMT == MOE_FMT_NVFP4 ? glob[(size_t)e * 2 * I + I + a.lo + cc] : 1.f;
-  }
+  // epilogue: SwiGLU, h in bf16
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
@@ -387,7 +350,7 @@ __global__ __launch_bounds__(256, 2) void k_gate_up_tiled(GateUpArgs a) {
       for (int j = 0; j < 2; j++) {
         const int col = c0 + 32 * wn + 16 * j + r;
         if (col >= Il) continue;
-        const float gv = acc[i][j][jj] * gg[j], uv = acc[i][j + 2][jj] * ug[j];
+        const float gv = acc[i][j][jj], uv = acc[i][j + 2][jj];
         a.h[row * Il + col] = bf16_bits(gv / (1.f + __expf(-gv)) * uv);
       }
     }
@@ -410,7 +373,6 @@ __global__ __launch_bounds__(256, 2) void k_down_tiled(DownArgs a) {
   const int n0 = blockIdx.y * TW;
   int p0, e;
   const uint8_t *codes, *scales;
-  const float *glob;
   if (!is_shared) {
     p0 = blockIdx.x * TM;
     const int tp = a.total_padded[0], eb = a.block_expert[p0 / a.block_m];  // both in flight (p0 < cap)
@@ -419,13 +381,11 @@ __global__ __launch_bounds__(256, 2) void k_down_tiled(DownArgs a) {
     if (e < 0) return;
     codes = a.dn;
     scales = a.dns;
-    glob = a.dng;
   } else {
     p0 = a.cap + (blockIdx.x - n_routed) * TM;
     e = 0;
     codes = a.sdn;
     scales = a.sdns;
-    glob = a.sdng;
   }
   const int T = a.T, H = a.H, I = a.I, Il = a.Il, P = a.T * a.k;
   const WMat<FMT> m = weight_matrix<FMT>(codes, scales, e, H, I);
@@ -442,9 +402,6 @@ __global__ __launch_bounds__(256, 2) void k_down_tiled(DownArgs a) {
     return buf_load_f32(m.scales, (uint32_t)((wr / 128) * (I / 128) + a.lo / 128 + kb) * 4);
   };
   tiled_k_loop<FMT, TK>(lds, ra, a_off, m, wrow, true, a.lo, (Il + TK - 1) / TK, Il, brow, scale, acc);
-  float dg[4];
-#pragma unroll
-  for (int j = 0; j < 4; j++) dg[j] = FMT == MOE_FMT_NVFP4 ? glob[(size_t)e * H + n0 + 64 * wn + 16 * j + r] : 1.f;
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
@@ -463,7 +420,7 @@ __global__ __launch_bounds__(256, 2) void k_down_tiled(DownArgs a) {
       if (dst < 0) continue;
       uint16_t *yrow = reinterpret_cast<uint16_t *>(a.Y) + (size_t)dst * H + n0 + 64 * wn + r;
 #pragma unroll
-      for (int j = 0; j < 4; j++) yrow[16 * j] = bf16_bits(wgt * acc[i][j][jj] * dg[j]);
+      for (int j = 0; j < 4; j++) yrow[16 * j] = bf16_bits(wgt * acc[i][j][jj]);
     }
 }
 
@@ -529,9 +486,8 @@ hipError_t launch_router_tiled(const uint16_t *x, int T, int H, const uint16_t *
 
 hipError_t launch_gate_up_tiled(int fmt, const GateUpArgs &a, int n_shared_tiles, hipStream_t s) {
   const dim3 grid(a.cap / TM + n_shared_tiles, (a.Il + 63) / 64);
-  if (fmt == MOE_FMT_NVFP4)
-    hipLaunchKernelGGL(k_gate_up_tiled<MOE_FMT_NVFP4>, grid, dim3(256), 0, s, a);
-  else if (fmt == MOE_FMT_BF16)
+  if (fmt == MOE_FMT_NVFP4) return launch_gate_up_wide(a, n_shared_tiles, s);
+  if (fmt == MOE_FMT_BF16)
     hipLaunchKernelGGL(k_gate_up_tiled<MOE_FMT_BF16>, grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(k_gate_up_tiled<MOE_FMT_FP8_BLOCK128>, grid, dim3(256), 0, s, a);
@@ -540,9 +496,8 @@ hipError_t launch_gate_up_tiled(int fmt, const GateUpArgs &a, int n_shared_tiles
 
 hipError_t launch_down_tiled(int fmt, const DownArgs &a, int n_shared_tiles, hipStream_t s) {
   const dim3 grid(a.cap / TM + n_shared_tiles, a.H / TW);
-  if (fmt == MOE_FMT_NVFP4)
-    hipLaunchKernelGGL(k_down_tiled<MOE_FMT_NVFP4>, grid, dim3(256), 0, s, a);
-  else if (fmt == MOE_FMT_BF16)
+  if (fmt == MOE_FMT_NVFP4) return launch_down_wide(a, n_shared_tiles, s);
+  if (fmt == MOE_FMT_BF16)
     hipLaunchKernelGGL(k_down_tiled<MOE_FMT_BF16>, grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(k_down_tiled<MOE_FMT_FP8_BLOCK128>, grid, dim3(256), 0, s, a);

@@ -1,0 +1,368 @@
+// expert_wide.hip -- NVFP4 expert GEMMs for many tokens per expert (prefill), gfx950.
+//
+// Same computation as expert.hip and expert_tiled.hip (gate rows [lo,hi), up rows
+// [I+lo, I+hi), down columns [lo,hi) of one rank's slice: FreeToken issue #62 "What it
+// touches" item 1; SwiGLU expert linear in the intermediate index: issue #520 section 4;
+// NVFP4 W4A16 with the e4m3 group scale exact in bf16 and the per-row fp32 global applied
+// to the fp32 result: issue #520 section 2).
+//
+// Work split: a workgroup owns a 128-row block of the aligned pair list (one expert) and 256
+// weight rows; each of its 4 waves owns all 128 rows x 64 weight rows, 4 x 2 tiles of
+// v_mfma_f32_32x32x16_bf16 (the 32x32 form keeps the matrix core near its peak with one wave
+// per SIMD, which the register budget here allows).  Only the activation tile goes through
+// LDS (gathered x rows or h rows, 128 x 128 bf16 per K stage, double buffered, one barrier
+// per stage).  The weights are read straight into registers in operand order: lane l of a
+// wave holds weight row l % 32 of a 32-row tile and the contiguous K half
+// [64 h, 64 h + 64) of each 128-wide stage (h = l / 32), i.e. two 16-byte code pieces of the
+// tile-16 layout, and MFMA c of the stage takes K [64 h + 8 c, +8) from both operands.  Each
+// wave dequantizes only its own 64 rows; per stage it runs 64 MFMAs against 4 KB of codes.
+//
+// K loop: stage s multiplies from LDS buffer s%2 and weight register set s%2, while the
+// activation loads of stage s+2 and the weight loads of stage s+2 (issued once set s%2 is
+// consumed) are in flight and stage s+1 is stored to the other LDS buffer.
+//
+// Workgroup order: the dispatcher assigns workgroup L to XCD L mod 8.  The row blocks in use
+// (the routed ones below total_padded, then the shared expert's) are dealt to the XCDs in
+// turn, and the column groups of a row block, which share its activation rows, run back to
+// back on the same XCD.  (Giving each XCD a contiguous run of row blocks instead, so that
+// consecutive blocks of one expert share its weights in L2, measured slower.)
+#include "device_common.h"
+#include "launch.h"
+
+namespace qmoe {
+namespace {
+
+constexpr int WM = 128;          // pair rows per workgroup (one align block of 128)
+constexpr int WK = 128;          // K per stage
+constexpr int WCOLS = 256;       // weight rows per workgroup (64 per wave)
+
+// Output tile of one wave after the K loop: 128 rows x 64 bf16, rows padded to 72 so that
+// the two row groups a 32x32 result register covers (rows 4 apart) fall in different banks.
+constexpr int OPITCH = 72;
+
+struct __attribute__((aligned(16))) WideLDS {
+  union {
+    uint16_t a[2][WM][WK];           // K loop: activation tiles, 2 x 32 KB
+    uint16_t o[4][WM][OPITCH];       // epilogue: each wave's output tile, 4 x 18 KB
+  };
+  int32_t dst[WM];  // down: destination row of each pair row (-1: none)
+  float wgt[WM];    // down: its routing weight
+};
+
+// K chunk c (elements [8c, 8c+8)) of tile row R sits at chunk c ^ (R & 15) of its 256-byte
+// row: a fragment read (16 consecutive rows, one chunk index per 16 lanes) and a 16-lane row
+// store then touch every bank once.
+__device__ __forceinline__ int wswz(int R, int c) { return 8 * (c ^ (R & 15)); }
+
+struct AStage {
+  uint4 v[8];  // chunk tid%16 of rows tid/16 + 16q
+};
+
+struct BStage {
+  uint4 c[2][2];     // [column tile][piece]: 32 e2m1 codes each
+  uint32_t s[2][2];  // the pieces' two e4m3 group scales
+};
+
+// The pipelined K loop.  a_off: byte offsets of the K origin of the thread's 8 activation
+// rows (0x80000000: a row that reads zeros).  cb/sb: tile-16 code and scale offsets of this
+// lane's weight row in each of the wave's two 32-row column tiles.  K runs over nK stages
+// from weight column b_k0; positions at or past kvalid (a multiple of 32) contribute zero
+// (TAIL: kvalid may end inside a stage; otherwise it is nK * 128).
+template <bool TAIL>
+__device__ __forceinline__ void wide_k_loop(WideLDS &lds, rsrc_t ra, const uint32_t (&a_off)[8],
+                                            const WMat<MOE_FMT_NVFP4> &m, const uint32_t (&cb)[2],
+                                            const uint32_t (&sb)[2], int b_k0, int nK, int kvalid,
+                                            f32x16_t (&acc)[4][2]) {
+  const int tid = threadIdx.x, lane = tid & 63, r32 = lane & 31, h = lane >> 5;
+  const int ac = tid & 15;  // the activation chunk this thread stages
+  AStage at;
+  BStage bt[2];
+  auto fetch_a = [&](int st, AStage &t) {
+    const int k = st * WK + 8 * ac;
+    const uint32_t kk = (uint32_t)(k < kvalid ? k : 0);
+#pragma unroll
+    for (int q = 0; q < 8; q++) t.v[q] = buf_load16(ra, a_off[q] + kk * 2);
+  };
+  auto fetch_b = [&](int st, BStage &t) {
+#pragma unroll
+    for (int p = 0; p < 2; p++) {
+      const int k = st * WK + 64 * h + 32 * p;
+      const uint32_t pc = (uint32_t)(b_k0 + (k < kvalid ? k : 0)) / 32;
+#pragma unroll
+      for (int ct = 0; ct < 2; ct++) {
+        t.c[ct][p] = buf_load16(m.codes, cb[ct] + pc * 256);
+        t.s[ct][p] = buf_load2(m.scales, sb[ct] + pc * 32);
+      }
+    }
+  };
+  auto store_a = [&](int st, const AStage &t) {
+    const bool ok = !TAIL || st * WK + 8 * ac < kvalid;
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+      const int R = (tid >> 4) + 16 * q;
+      *reinterpret_cast<uint4 *>(&lds.a[st & 1][R][wswz(R, ac)]) = ok ? t.v[q] : make_uint4(0, 0, 0, 0);
+    }
+  };
+  // MFMA c of a stage takes K [64 h + 8 c, +8) in this lane.  Chunks are software pipelined:
+  // the A fragments of chunk c+1 are read (and its B fragments dequantized) before chunk c's
+  // MFMAs issue, so the LDS latency and the VALU work hide under the matrix core.
+  auto read_a = [&](int st, int c, frag8 (&f)[4]) {
+#pragma unroll
+    for (int mi = 0; mi < 4; mi++)
+      f[mi].q = *reinterpret_cast<const uint4 *>(&lds.a[st & 1][32 * mi + r32][wswz(r32, 8 * h + c)]);
+  };
+  auto dec_b = [&](int st, int c, const BStage &t, frag8 (&f)[2]) {
+    const int p = c >> 2, d = c & 3;
+    const bool bvalid = !TAIL || st * WK + 64 * h + 32 * p < kvalid;
+#pragma unroll
+    for (int ct = 0; ct < 2; ct++) {
+      const uint4 &cv = t.c[ct][p];
+      const uint32_t code = d == 0 ? cv.x : d == 1 ? cv.y : d == 2 ? cv.z : cv.w;
+      fp4x8_mul_to_bf16(code, e4m3_to_f32(t.s[ct][p] >> (8 * (d >> 1))), f[ct]);
+      if (!bvalid) f[ct].q = make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto compute = [&](int st, const BStage &t) {
+#pragma unroll
+    for (int c = 0; c < 8; c++) {
+      frag8 af[4], bf[2];
+      read_a(st, c, af);
+      dec_b(st, c, t, bf);
+#pragma unroll
+      for (int mi = 0; mi < 4; mi++)
+#pragma unroll
+        for (int ct = 0; ct < 2; ct++) acc[mi][ct] = mfma32_bf16(af[mi], bf[ct], acc[mi][ct]);
+    }
+  };
+  fetch_a(0, at);
+  fetch_b(0, bt[0]);
+  fetch_b(1, bt[1]);
+  store_a(0, at);
+  __syncthreads();
+  // Fetches past the last stage reload clamped offsets (unused) and the store after the
+  // last stage fills the idle buffer with zeros, so every path keeps the same loads in flight.
+  auto stage = [&](int st, BStage &b_cur) {
+    fetch_a(st + 1, at);
+    compute(st, b_cur);
+    fetch_b(st + 2, b_cur);
+    store_a(st + 1, at);
+    __syncthreads();
+  };
+  int st = 0;
+  for (; st + 1 < nK; st += 2) {
+    stage(st, bt[0]);
+    stage(st + 1, bt[1]);
+  }
+  if (st < nK) stage(st, bt[0]);
+}
+
+// Grid position -> (row block, column group); false for positions past the row blocks in
+// use.  n_used: routed row blocks in use (total_padded / 128); n_cap: routed row blocks of the
+// capacity; n_rb: n_cap plus the shared expert's row blocks.
+__device__ __forceinline__ bool wide_block(int n_used, int n_cap, int n_rb, int ncg, int &rb, int &cg) {
+  const int N = n_used + (n_rb - n_cap);
+  const int L = blockIdx.x, j = L >> 3;
+  const int idx = (j / ncg) * 8 + (L & 7);
+  cg = j % ncg;
+  rb = idx < n_used ? idx : n_cap + (idx - n_used);
+  return idx < N;
+}
+
+__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[4][2]) {
+#pragma unroll
+  for (int mi = 0; mi < 4; mi++)
+#pragma unroll
+    for (int ct = 0; ct < 2; ct++)
+#pragma unroll
+      for (int j = 0; j < 16; j++) acc[mi][ct][j] = 0.f;
+}
+
+// Row of the 32-row tile that register j of this lane holds.
+__device__ __forceinline__ int d_row(int lane, int j) { return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3); }
+
+}  // namespace
+
+// gate_up + SwiGLU.  Column group cg covers slice columns [c0, c0 + 128): wave w owns gate
+// rows lo + c0 + 32 w + [0, 32) (column tile 0) and the matching up rows I + ... (column
+// tile 1), so SwiGLU stays in registers.
+__global__ __launch_bounds__(256, 2) void k_gate_up_wide(GateUpArgs a, int n_rb, int ncg) {
+  __shared__ WideLDS lds;
+  const int n_routed = a.cap / WM;
+  int rb, cg;
+  if (!wide_block(__builtin_amdgcn_readfirstlane(a.total_padded[0]) / WM, n_routed, n_rb, ncg, rb, cg)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool is_shared = rb >= n_routed;
+  const int c0 = cg * (WCOLS / 2);
+  int p0, e;
+  const uint8_t *codes, *scales;
+  const float *glob;
+  if (!is_shared) {
+    p0 = rb * WM;
+    e = __builtin_amdgcn_readfirstlane(a.block_expert[p0 / a.block_m]);
+    if (e < 0) return;
+    codes = a.gu;
+    scales = a.gus;
+    glob = a.gug;
+  } else {
+    p0 = a.cap + (rb - n_routed) * WM;
+    e = 0;
+    codes = a.sgu;
+    scales = a.sgus;
+    glob = a.sgug;
+  }
+  const int T = a.T, H = a.H, I = a.I, Il = a.Il, P = a.T * a.k;
+  const WMat<MOE_FMT_NVFP4> m = weight_matrix<MOE_FMT_NVFP4>(codes, scales, e, 2 * I, H);
+  const rsrc_t ra = make_rsrc(a.x, (uint32_t)T * H * 2);
+  uint32_t a_off[8];
+#pragma unroll
+  for (int q = 0; q < 8; q++) {
+    const int p = p0 + (tid >> 4) + 16 * q;
+    int tok;
+    if (!is_shared) {
+      const int f = a.sorted_ids[p];
+      tok = f < P ? f / a.k : -1;
+    } else {
+      tok = p - a.cap < T ? p - a.cap : -1;
+    }
+    a_off[q] = tok >= 0 ? (uint32_t)tok * H * 2 : 0x80000000u;
+  }
+  const int col = c0 + 32 * wave + (lane & 31);  // this lane's slice column (B operand and D)
+  const int cc = col < Il ? col : (lane & 31);   // columns past the slice read row lane%32 (unused)
+  uint32_t cb[2], sb[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ct++) {
+    const uint32_t row = (uint32_t)((ct == 0 ? 0 : I) + a.lo + cc);
+    cb[ct] = (row & ~15u) * (uint32_t)(H / 2) + (row & 15u) * 16;
+    sb[ct] = (row & ~15u) * (uint32_t)(H / 16) + (row & 15u) * 2;
+  }
+  const float gg = glob[(size_t)e * 2 * I + a.lo + cc], ug = glob[(size_t)e * 2 * I + I + a.lo + cc];
+  f32x16_t acc[4][2];
+  zero_acc(acc);
+  wide_k_loop<false>(lds, ra, a_off, m, cb, sb, 0, H / WK, H, acc);
+  // h through LDS (the K loop ended with a barrier): each wave's 128 x 32 block, then rows
+  // leave as 16-byte chunks (4 lanes per 64-byte row segment)
+  uint16_t (*o)[OPITCH] = lds.o[wave];
+#pragma unroll
+  for (int mi = 0; mi < 4; mi++)
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      const float gv = acc[mi][0][j] * gg, uv = acc[mi][1][j] * ug;
+      o[32 * mi + d_row(lane, j)][lane & 31] = bf16_bits(gv / (1.f + __expf(-gv)) * uv);
+    }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int ch = lane & 3, c8 = c0 + 32 * wave + 8 * ch;  // this lane's 8 columns
+  if (c8 < Il) {
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+      const int R = (lane >> 2) + 16 * q;
+      *reinterpret_cast<uint4 *>(a.h + (size_t)(p0 + R) * Il + c8) = *reinterpret_cast<const uint4 *>(&o[R][8 * ch]);
+    }
+  }
+}
+
+// down.  Column group cg covers hidden columns [cg * 256, +256): wave w owns 64 w + [0, 64)
+// of them (two 32-column tiles); K = the slice.  The weighted pair rows go to Y in bf16 (the
+// combine sums them in fp32), as in the other prefill kernels.
+__global__ __launch_bounds__(256, 2) void k_down_wide(DownArgs a, int n_rb, int ncg) {
+  __shared__ WideLDS lds;
+  const int n_routed = a.cap / WM;
+  int rb, cg;
+  if (!wide_block(__builtin_amdgcn_readfirstlane(a.total_padded[0]) / WM, n_routed, n_rb, ncg, rb, cg)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool is_shared = rb >= n_routed;
+  int p0, e;
+  const uint8_t *codes, *scales;
+  const float *glob;
+  if (!is_shared) {
+    p0 = rb * WM;
+    e = __builtin_amdgcn_readfirstlane(a.block_expert[p0 / a.block_m]);
+    if (e < 0) return;
+    codes = a.dn;
+    scales = a.dns;
+    glob = a.dng;
+  } else {
+    p0 = a.cap + (rb - n_routed) * WM;
+    e = 0;
+    codes = a.sdn;
+    scales = a.sdns;
+    glob = a.sdng;
+  }
+  const int T = a.T, H = a.H, I = a.I, Il = a.Il, P = a.T * a.k;
+  const WMat<MOE_FMT_NVFP4> m = weight_matrix<MOE_FMT_NVFP4>(codes, scales, e, H, I);
+  const rsrc_t ra = make_rsrc(a.h, (uint32_t)a.h_rows * Il * 2);
+  uint32_t a_off[8];
+#pragma unroll
+  for (int q = 0; q < 8; q++) a_off[q] = (uint32_t)(p0 + (tid >> 4) + 16 * q) * Il * 2;
+  int n[2];
+  uint32_t cb[2], sb[2];
+  float dg[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ct++) {
+    n[ct] = cg * WCOLS + 64 * wave + 32 * ct + (lane & 31);
+    const uint32_t row = (uint32_t)(n[ct] < H ? n[ct] : (lane & 31));  // columns past H read row lane%32 (unused)
+    cb[ct] = (row & ~15u) * (uint32_t)(I / 2) + (row & 15u) * 16;
+    sb[ct] = (row & ~15u) * (uint32_t)(I / 16) + (row & 15u) * 2;
+    dg[ct] = glob[(size_t)e * H + row];
+  }
+  if (tid < WM) {  // destination and weight of each pair row, read back in the epilogue
+    const int p = p0 + tid;
+    if (!is_shared) {
+      const int f = a.sorted_ids[p];
+      lds.dst[tid] = f < P ? f : -1;
+      lds.wgt[tid] = f < P ? a.topk_w[f] : 0.f;
+    } else {
+      lds.dst[tid] = p - a.cap < T ? P + (p - a.cap) : -1;
+      lds.wgt[tid] = 1.f;
+    }
+  }
+  f32x16_t acc[4][2];
+  zero_acc(acc);
+  if (Il % WK == 0)
+    wide_k_loop<false>(lds, ra, a_off, m, cb, sb, a.lo, Il / WK, Il, acc);
+  else
+    wide_k_loop<true>(lds, ra, a_off, m, cb, sb, a.lo, (Il + WK - 1) / WK, Il, acc);
+  // weighted rows through LDS (the K loop ended with a barrier, which also published
+  // dst/wgt): each wave's 128 x 64 block, then 16-byte chunks (8 lanes per 128-byte row)
+  uint16_t (*o)[OPITCH] = lds.o[wave];
+#pragma unroll
+  for (int mi = 0; mi < 4; mi++)
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      const int R = 32 * mi + d_row(lane, j);
+      const float w = lds.wgt[R];
+#pragma unroll
+      for (int ct = 0; ct < 2; ct++) o[R][32 * ct + (lane & 31)] = bf16_bits(w * acc[mi][ct][j] * dg[ct]);
+    }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int ch = lane & 7, n8 = cg * WCOLS + 64 * wave + 8 * ch;  // this lane's 8 columns
+  if (n8 < H) {
+#pragma unroll
+    for (int q = 0; q < 16; q++) {
+      const int R = (lane >> 3) + 8 * q;
+      const int d = lds.dst[R];
+      if (d >= 0)
+        *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(a.Y) + (size_t)d * H + n8) =
+            *reinterpret_cast<const uint4 *>(&o[R][8 * ch]);
+    }
+  }
+}
+
+hipError_t launch_gate_up_wide(const GateUpArgs &a, int n_shared_tiles, hipStream_t s) {
+  const int n_rb = a.cap / WM + n_shared_tiles, ncg = (a.Il + WCOLS / 2 - 1) / (WCOLS / 2);
+  const int grid = (n_rb + 7) / 8 * 8 * ncg;
+  hipLaunchKernelGGL(k_gate_up_wide, dim3(grid), dim3(256), 0, s, a, n_rb, ncg);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_wide(const DownArgs &a, int n_shared_tiles, hipStream_t s) {
+  const int n_rb = a.cap / WM + n_shared_tiles, ncg = (a.H + WCOLS - 1) / WCOLS;
+  const int grid = (n_rb + 7) / 8 * 8 * ncg;
+  hipLaunchKernelGGL(k_down_wide, dim3(grid), dim3(256), 0, s, a, n_rb, ncg);
+  return hipGetLastError();
+}
+
+}  // namespace qmoe
