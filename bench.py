@@ -141,12 +141,25 @@ def run(args):
                                               to_dev(b.down), to_dev(b.down_scale), to_dev(b.gate_up_global),
                                               to_dev(b.down_global)))
 
+    # Weight storage of a point's slice [lo, hi): "own" = the rank holds only its slice (gate
+    # rows [lo, hi), up rows [I+lo, I+hi), down columns [lo, hi) as a bank with I = hi - lo,
+    # run on [0, hi - lo)); "full" = the whole bank, run on [lo, hi).
+    slices = sorted({sl for _, sl in points})
     t0 = time.time()
     inst = []
     for r in range(R):
         li = S.layer_inputs(cfg, 1, instance=r)
-        inst.append(dict(routed=dbank(li.routed), shared=dbank(li.shared) if li.shared is not None else None,
-                         router=to_dev(li.router).view(torch.bfloat16), bias=to_dev(li.bias)))
+        banks = {}
+        for (lo, hi) in slices:
+            if args.storage == "own" and (lo, hi) != (0, cfg.I):
+                rb, sb = S.slice_bank(li.routed, lo, hi), (S.slice_bank(li.shared, lo, hi) if li.shared is not None else None)
+            else:
+                rb, sb = li.routed, li.shared
+            key = (lo, hi) if rb is not li.routed else None
+            if key not in banks:
+                banks[key] = (dbank(rb), dbank(sb) if sb is not None else None)
+            banks[(lo, hi)] = banks[key]
+        inst.append(dict(banks=banks, router=to_dev(li.router).view(torch.bfloat16), bias=to_dev(li.bias)))
         del li
     log(f"config {cid}: {R} layer instance(s) generated and uploaded in {time.time() - t0:.1f} s")
     Tmax = max(T for T, _ in points)
@@ -160,8 +173,9 @@ def run(args):
             I_ = inst[r]
             for b in range(BATCHES):
                 x = xs[b][:T].contiguous()
-                L = qm.MoeLayer(I_["routed"], I_["shared"], I_["router"], I_["bias"], T, cfg.k, lo, hi,
-                                cfg.renormalize)
+                rbank, sbank = I_["banks"][(lo, hi)]
+                klo = lo if rbank.I == cfg.I else 0  # the slice inside the bank this point runs on
+                L = qm.MoeLayer(rbank, sbank, I_["router"], I_["bias"], T, cfg.k, klo, klo + Il, cfg.renormalize)
                 L(x)  # eager run (warms up, and fixes this graph's routing for the byte count)
                 torch.cuda.synchronize()
                 counts = L.align.counts.cpu().numpy()
@@ -177,13 +191,24 @@ def run(args):
                 layers.append((L, x))
                 graphs.append(g)
         n = len(graphs)
-        for i in range(args.warmup):
-            graphs[i % n].replay()
+        # one graph over the whole rotation (n steps back to back) so that graph launches do
+        # not gap the steps; K steps = K // n rotations, then the first K % n single steps
+        g_all = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_all):
+            for L, x in layers:
+                L(x)
+
+        def run_steps(k):
+            for _ in range(k // n):
+                g_all.replay()
+            for i in range(k % n):
+                graphs[i].replay()
+
+        run_steps(args.warmup)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for i in range(args.steps):
-            graphs[i % n].replay()
+        run_steps(args.steps)
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / args.steps
@@ -195,7 +220,7 @@ def run(args):
         with torch.cuda.graph(gk):
             for i in range(reps):
                 L, x = layers[i % n]
-                qm.moe_expert_gate_up(L.routed, L.shared, x, L.k, L.align, lo, hi, L.ws)
+                qm.moe_expert_gate_up(L.routed, L.shared, x, L.k, L.align, L.lo, L.hi, L.ws)
         gk.replay()
         torch.cuda.synchronize()
         e0.record()
@@ -213,7 +238,7 @@ def run(args):
                   gate_up_gbs=k_bytes / (k_ms * 1e-3) / 1e9)
         log(json.dumps(pt))
         results.append(pt)
-        del layers, graphs, gk
+        del layers, graphs, gk, g_all
         torch.cuda.synchronize()
     return cfg, results
 
@@ -241,6 +266,8 @@ def main():
     ap.add_argument("--slice", type=str, default="")
     ap.add_argument("--instances", type=int, default=0)
     ap.add_argument("--no-points", action="store_true", help="only the headline point")
+    ap.add_argument("--storage", choices=("own", "full"), default="full",
+                    help="weights of a slice: the rank's own slice storage, or the full bank")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -275,7 +302,8 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": workload, "format": cfg.fmt, "H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I,
                    "shared_expert": cfg.shared, "T": head["T"], "slice": head["slice"], "instances_rotated":
-                   args.instances or INSTANCES[cfg.cid], "batches_rotated": BATCHES},
+                   args.instances or INSTANCES[cfg.cid], "batches_rotated": BATCHES,
+                   "weight_storage": "rank's own slice" if args.storage == "own" else "full bank, sliced"},
         "layer_hbm_frac": head["layer_hbm_frac"], "layer_mfma_frac": head["layer_mfma_frac"],
         "roofline": roof, "points": results,
     }
