@@ -348,6 +348,25 @@ def test_tiled_kernels_match_oracle(cid, T, sl):
     check_close(f"tiled cfg{cid} T={T} [{lo},{hi})", _forward_gpu(inp, r["ids"], r["w"], lo, hi, bm=128), ref)
 
 
+@pytest.mark.parametrize("H,I,sl,T,bm", [(384, 224, (0, 224), 300, 128), (384, 224, (32, 160), 257, 256),
+                                          (256, 128, (0, 128), 1, 128), (640, 96, (0, 96), 700, 128)])
+def test_wide_kernels_ragged_shapes(H, I, sl, T, bm):
+    """NVFP4 prefill GEMMs on shapes that leave partial work everywhere: a last down column group
+    half past H (H = 384, 640), a last gate_up column group partly past the slice and a down K
+    tail (slice widths 224, 128 and 96 are not multiples of 128), shared-expert rows ending inside a
+    32-row tile, align blocks of 256 rows, and a single token."""
+    E, k, seed = 6, 2, 23
+    b, sh = S.routed_bank(seed, "nvfp4", E, H, I), S.shared_bank(seed, "nvfp4", H, I)
+    x = S.tokens(seed, T, H)
+    _, ids, w, _ = O.route(x, S.router_weight(seed, E, H), None, k, True)
+    lo, hi = sl
+    ref = O.expert_forward(b, sh, x, ids, w, lo, hi)
+    al = qm.moe_align(to_dev(ids.astype(np.int32)), E, bm)
+    got = qm.moe_expert_forward(device_bank(b), device_bank(sh), bf16_dev(x), to_dev(w.astype(np.float32)), al,
+                                lo, hi).float().cpu().numpy()
+    check_close(f"wide H={H} I={I} [{lo},{hi}) T={T} bm={bm}", got, ref)
+
+
 @pytest.mark.parametrize("cid,T,sl,bm", [(3, 8192, (0, 512), 128), (3, 8192, (0, 256), 128),
                                          (4, 4096, (0, 256), 128), (3, 8192, (0, 512), 64)])
 def test_prefill_full_size_sampled_rows(cid, T, sl, bm):
