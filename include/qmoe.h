@@ -257,9 +257,8 @@ size_t moe_workspace_bytes(const moe_bank *routed, const moe_bank *shared, int T
  * each weight tile across 128 pair rows (for many tokens per expert); other block sizes,
  * and MXFP4 and Q4_0, run the streaming kernels that read each selected weight byte once per
  * 16-row block (for few tokens per expert).  Both compute the same result, except that the
- * tiled kernels round each weighted pair row topk_w * y to bf16 before the fp32 sum (the
- * pair rows are the layer's largest stream at many tokens; the streaming kernels keep
- * them in fp32). */
+ * tiled kernels round each pair row y to bf16 before the fp32 weighted sum (the pair rows
+ * are the layer's largest stream at many tokens; the streaming kernels keep them in fp32). */
 int moe_expert_forward(const moe_bank *routed, const moe_bank *shared, const void *x_bf16,
                        int T, int k, const float *topk_w, const moe_align_out *al,
                        int slice_lo, int slice_hi, void *out, int out_dtype, void *workspace,

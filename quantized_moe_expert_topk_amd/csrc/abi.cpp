@@ -297,8 +297,8 @@ qmoe::GateUpArgs gate_up_args(const moe_bank *routed, const moe_bank *shared, co
   return a;
 }
 
-qmoe::DownArgs down_args(const moe_bank *routed, const moe_bank *shared, int T, int k, const float *topk_w,
-                         const moe_align_out *al, int lo, const FwdPlan &p, void *workspace) {
+qmoe::DownArgs down_args(const moe_bank *routed, const moe_bank *shared, int T, int k, const moe_align_out *al,
+                         int lo, const FwdPlan &p, void *workspace) {
   qmoe::DownArgs a;
   const char *ws = static_cast<const char *>(workspace);
   a.h = reinterpret_cast<const uint16_t *>(ws);
@@ -324,7 +324,6 @@ qmoe::DownArgs down_args(const moe_bank *routed, const moe_bank *shared, int T, 
   a.n_routed_sub = p.n_routed_sub;
   a.lo = lo;
   a.Il = p.Il;
-  a.topk_w = topk_w;
   a.Y = reinterpret_cast<float *>(static_cast<char *>(workspace) + p.y_off);
   return a;
 }
@@ -346,11 +345,11 @@ int run_gate_up(const moe_bank *routed, const moe_bank *shared, const void *x, i
 int run_down(const moe_bank *routed, const moe_bank *shared, int T, int k, const float *topk_w,
              const moe_align_out *al, int lo, const FwdPlan &p, void *out, int out_dtype, void *workspace,
              hipStream_t s) {
-  qmoe::DownArgs a = down_args(routed, shared, T, k, topk_w, al, lo, p, workspace);
+  qmoe::DownArgs a = down_args(routed, shared, T, k, al, lo, p, workspace);
   int rc = p.tiled ? hip_status(qmoe::launch_down_tiled(routed->fmt, a, p.n_shared_tiles, s), "down launch")
                    : hip_status(qmoe::launch_down(routed->fmt, a, p.n_shared_sub, s), "down launch");
   if (rc) return rc;
-  return hip_status(qmoe::launch_combine(a.Y, p.tiled, T, k, routed->H, shared != nullptr, out,
+  return hip_status(qmoe::launch_combine(a.Y, p.tiled, topk_w, T, k, routed->H, shared != nullptr, out,
                                          out_dtype == MOE_OUT_BF16, s),
                     "combine launch");
 }

@@ -2,8 +2,10 @@
 //
 // gate_up: for every row of the aligned pair list (and every token for the shared expert)
 //   g_i = x . Wg[lo+i],  u_i = x . Wu[I+lo+i],  h_i = silu(g_i) * u_i  (bf16)
-// down:    y_n = sum_i h_i Wd[n, lo+i], scaled by the routing weight and written per pair
-// combine: out[t] = sum_j Y[t*k+j] + Y_shared[t]  (fixed order, deterministic)
+// down:    y_n = sum_i h_i Wd[n, lo+i], written per pair
+// combine: out[t] = sum_j topk_w[t,j] Y[t*k+j] + Y_shared[t]  (fixed order, deterministic; the
+//          routing weight is applied here, where it is a direct load, not in down, where it
+//          would be a load through sorted_ids behind another load)
 // The slice geometry is the pages' (gate rows [lo,hi), up rows [I+lo, I+hi), down columns
 // [lo,hi): FreeToken issue #62 "What it touches" item 1), and so is the math (issue #520
 // section 4 "Expert sharding": silu(gate)*up @ down, linear in the intermediate index).
@@ -733,21 +735,18 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
   f32x4_t acc[DNT];
 #pragma unroll
   for (int t = 0; t < DNT; t++) acc[t] = zero4();
-  // epilogue metadata first, so its latency hides under the weight loads
+  // destination rows first, so their latency hides under the weight loads
   const int P = a.T * a.k;
   int dst[4];
-  float wgt[4];
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const int p = p0 + 4 * g + j;
     if (!is_shared) {
       const int f = a.sorted_ids[p];
       dst[j] = f < P ? f : -1;
-      wgt[j] = f < P ? a.topk_w[f] : 0.f;
     } else {
       const int t = p - a.cap;
       dst[j] = t < a.T ? P + t : -1;
-      wgt[j] = 1.f;
     }
   }
   float dglob[DNT];
@@ -783,30 +782,34 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
 #pragma unroll
     for (int t = 0; t < DNT; t++) {
       if (t >= ntile) break;
-      a.Y[(size_t)dst[j] * H + n0 + 16 * t + r] = wgt[j] * acc[t][j] * dglob[t];
+      a.Y[(size_t)dst[j] * H + n0 + 16 * t + r] = acc[t][j] * dglob[t];
     }
   }
 }
 
 // ---------------------------------------------------------------------------- combine
 
-// out[t] = sum_j Y[t*k + j] + Y[T*k + t] (shared), in this order, in fp32.  Y rows are fp32
-// (streaming kernels) or bf16 (tiled kernels); a thread owns 4 consecutive columns (H % 128 == 0).
+// out[t] = sum_j w[t*k + j] Y[t*k + j] + Y[T*k + t] (shared, weight 1), in this order, in
+// fp32.  Y rows are fp32 (streaming kernels) or bf16 (tiled kernels); a thread owns 4
+// consecutive columns (H % 128 == 0).
 template <bool YBF16>
-__global__ __launch_bounds__(256) void k_combine(const void *__restrict__ Yv, int T, int k, int H, int has_shared,
-                                                 void *__restrict__ out, int out_bf16) {
+__global__ __launch_bounds__(256) void k_combine(const void *__restrict__ Yv, const float *__restrict__ w, int T,
+                                                 int k, int H, int has_shared, void *__restrict__ out,
+                                                 int out_bf16) {
   const int t = blockIdx.y;
   const int n = (blockIdx.x * 256 + threadIdx.x) * 4;  // 4 columns per thread
   if (n >= H) return;
   const int nrows = k + (has_shared ? 1 : 0);  // the token's k pair rows, then its shared row
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   for (int j0 = 0; j0 < nrows; j0 += 8) {
-    // up to 8 rows loaded before any is added (all in flight), then summed in row order
-    float v[8][4];
+    // up to 8 rows (and their weights) loaded before any is added (all in flight), then
+    // summed in row order
+    float v[8][4], wj[8];
 #pragma unroll
     for (int u = 0; u < 8; u++) {
       const int j = j0 + u;
       const size_t row = j < k ? (size_t)t * k + j : (size_t)T * k + t;
+      wj[u] = j < k ? w[row] : 1.f;  // row < T * k for routed rows
       if (j < nrows) {
         if constexpr (YBF16) {
           const uint2 w = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(Yv) + row * H + n);
@@ -827,7 +830,7 @@ __global__ __launch_bounds__(256) void k_combine(const void *__restrict__ Yv, in
     for (int u = 0; u < 8; u++)
       if (j0 + u < nrows)
 #pragma unroll
-        for (int c = 0; c < 4; c++) acc[c] += v[u][c];
+        for (int c = 0; c < 4; c++) acc[c] += wj[u] * v[u][c];
   }
   if (out_bf16) {
     const uint2 pk = make_uint2((uint32_t)bf16_bits(acc[0]) | ((uint32_t)bf16_bits(acc[1]) << 16),
@@ -911,13 +914,13 @@ hipError_t launch_act_mx8(const uint16_t *x, int rows, int K, uint8_t *q, uint8_
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const void *Y, bool y_bf16, int T, int k, int H, int has_shared, void *out, int out_bf16,
-                          hipStream_t s) {
+hipError_t launch_combine(const void *Y, bool y_bf16, const float *topk_w, int T, int k, int H, int has_shared,
+                          void *out, int out_bf16, hipStream_t s) {
   dim3 grid((H / 4 + 255) / 256, T);
   if (y_bf16)
-    hipLaunchKernelGGL(k_combine<true>, grid, dim3(256), 0, s, Y, T, k, H, has_shared, out, out_bf16);
+    hipLaunchKernelGGL(k_combine<true>, grid, dim3(256), 0, s, Y, topk_w, T, k, H, has_shared, out, out_bf16);
   else
-    hipLaunchKernelGGL(k_combine<false>, grid, dim3(256), 0, s, Y, T, k, H, has_shared, out, out_bf16);
+    hipLaunchKernelGGL(k_combine<false>, grid, dim3(256), 0, s, Y, topk_w, T, k, H, has_shared, out, out_bf16);
   return hipGetLastError();
 }
 

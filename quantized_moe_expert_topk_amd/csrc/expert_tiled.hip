@@ -360,8 +360,8 @@ __global__ __launch_bounds__(256, 2) void k_gate_up_tiled(GateUpArgs a) {
 
 // Tile (blockIdx.x, blockIdx.y): h rows [p0, p0 + 128) and hidden columns [n0, n0 + 128);
 // K = the slice [lo, hi).  Wave (wm, wn) owns rows 64 wm + [0,64), columns 64 wn + [0,64).
-// The weighted per-pair rows go to Y in bf16: at prefill sizes Y is the largest stream of
-// the layer (pairs x H), and the combine sums its rows in fp32.
+// The per-pair rows go to Y in bf16: at prefill sizes Y is the largest stream of the layer
+// (pairs x H), and the combine weights and sums its rows in fp32.
 template <int FMT>
 __global__ __launch_bounds__(256, 2) void k_down_tiled(DownArgs a) {
   constexpr int TK = 32;
@@ -408,19 +408,16 @@ __global__ __launch_bounds__(256, 2) void k_down_tiled(DownArgs a) {
     for (int jj = 0; jj < 4; jj++) {
       const int p = p0 + 64 * wm + 16 * i + 4 * g + jj;
       int dst;
-      float wgt;
       if (!is_shared) {
         const int f = a.sorted_ids[p];
         dst = f < P ? f : -1;
-        wgt = f < P ? a.topk_w[f] : 0.f;
       } else {
         dst = p - a.cap < T ? P + (p - a.cap) : -1;
-        wgt = 1.f;
       }
       if (dst < 0) continue;
       uint16_t *yrow = reinterpret_cast<uint16_t *>(a.Y) + (size_t)dst * H + n0 + 64 * wn + r;
 #pragma unroll
-      for (int j = 0; j < 4; j++) yrow[16 * j] = bf16_bits(wgt * acc[i][j][jj]);
+      for (int j = 0; j < 4; j++) yrow[16 * j] = bf16_bits(acc[i][j][jj]);
     }
 }
 

@@ -46,7 +46,6 @@ struct __attribute__((aligned(16))) WideLDS {
     uint16_t o[4][WM][OPITCH];       // epilogue: each wave's output tile, 4 x 18 KB
   };
   int32_t dst[WM];  // down: destination row of each pair row (-1: none)
-  float wgt[WM];    // down: its routing weight
 };
 
 // K chunk c (elements [8c, 8c+8)) of tile row R sits at chunk c ^ (R & 15) of its 256-byte
@@ -263,8 +262,8 @@ __global__ __launch_bounds__(256, 2) void k_gate_up_wide(GateUpArgs a, int n_rb,
 }
 
 // down.  Column group cg covers hidden columns [cg * 256, +256): wave w owns 64 w + [0, 64)
-// of them (two 32-column tiles); K = the slice.  The weighted pair rows go to Y in bf16 (the
-// combine sums them in fp32), as in the other prefill kernels.
+// of them (two 32-column tiles); K = the slice.  The pair rows go to Y in bf16 (the combine
+// weights and sums them in fp32), as in the other prefill kernels.
 __global__ __launch_bounds__(256, 2) void k_down_wide(DownArgs a, int n_rb, int ncg) {
   __shared__ WideLDS lds;
   const int n_routed = a.cap / WM;
@@ -306,15 +305,13 @@ __global__ __launch_bounds__(256, 2) void k_down_wide(DownArgs a, int n_rb, int 
     sb[ct] = (row & ~15u) * (uint32_t)(I / 16) + (row & 15u) * 2;
     dg[ct] = glob[(size_t)e * H + row];
   }
-  if (tid < WM) {  // destination and weight of each pair row, read back in the epilogue
+  if (tid < WM) {  // destination of each pair row, read back in the epilogue
     const int p = p0 + tid;
     if (!is_shared) {
       const int f = a.sorted_ids[p];
       lds.dst[tid] = f < P ? f : -1;
-      lds.wgt[tid] = f < P ? a.topk_w[f] : 0.f;
     } else {
       lds.dst[tid] = p - a.cap < T ? P + (p - a.cap) : -1;
-      lds.wgt[tid] = 1.f;
     }
   }
   f32x16_t acc[4][2];
@@ -323,17 +320,16 @@ __global__ __launch_bounds__(256, 2) void k_down_wide(DownArgs a, int n_rb, int 
     wide_k_loop<false>(lds, ra, a_off, m, cb, sb, a.lo, Il / WK, Il, acc);
   else
     wide_k_loop<true>(lds, ra, a_off, m, cb, sb, a.lo, (Il + WK - 1) / WK, Il, acc);
-  // weighted rows through LDS (the K loop ended with a barrier, which also published
-  // dst/wgt): each wave's 128 x 64 block, then 16-byte chunks (8 lanes per 128-byte row)
+  // pair rows through LDS (the K loop ended with a barrier, which also published dst): each
+  // wave's 128 x 64 block, then 16-byte chunks (8 lanes per 128-byte row)
   uint16_t (*o)[OPITCH] = lds.o[wave];
 #pragma unroll
   for (int mi = 0; mi < 4; mi++)
 #pragma unroll
     for (int j = 0; j < 16; j++) {
       const int R = 32 * mi + d_row(lane, j);
-      const float w = lds.wgt[R];
 #pragma unroll
-      for (int ct = 0; ct < 2; ct++) o[R][32 * ct + (lane & 31)] = bf16_bits(w * acc[mi][ct][j] * dg[ct]);
+      for (int ct = 0; ct < 2; ct++) o[R][32 * ct + (lane & 31)] = bf16_bits(acc[mi][ct][j] * dg[ct]);
     }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();

@@ -41,8 +41,7 @@ struct DownArgs {
   const int32_t *sorted_ids, *block_expert, *total_padded;
   int block_m, cap, n_routed_sub;
   int lo, Il;
-  const float *topk_w;  // [T * k]
-  float *Y;             // [T * k + T_shared, H] fp32 (streaming kernels) or bf16 (tiled kernels)
+  float *Y;  // [T * k + T_shared, H] unweighted pair rows: fp32 (streaming kernels) or bf16 (tiled kernels)
 };
 
 int router_ksplit(int T, int E, int H);
@@ -77,8 +76,9 @@ hipError_t launch_pack_tile16_t(const void *src, void *dst, size_t E, size_t N, 
 // Q4_0 codes [rows, pitch] -> the tile-16 piece order with the nibbles regrouped per piece.
 hipError_t launch_pack_q4_0(const void *src, void *dst, size_t rows, uint32_t pitch, hipStream_t s);
 hipError_t launch_act_mx8(const uint16_t *x, int rows, int K, uint8_t *q, uint8_t *sc, hipStream_t s);
-// Y rows in fp32 (streaming kernels) or bf16 (tiled kernels).
-hipError_t launch_combine(const void *Y, bool y_bf16, int T, int k, int H, int has_shared, void *out, int out_bf16,
-                          hipStream_t s);
+// Y rows (unweighted) in fp32 (streaming kernels) or bf16 (tiled kernels); the combine applies
+// the routing weights topk_w [T * k].
+hipError_t launch_combine(const void *Y, bool y_bf16, const float *topk_w, int T, int k, int H, int has_shared,
+                          void *out, int out_bf16, hipStream_t s);
 
 }  // namespace qmoe
