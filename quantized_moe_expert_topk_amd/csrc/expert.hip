@@ -735,17 +735,17 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
   f32x4_t acc[DNT];
 #pragma unroll
   for (int t = 0; t < DNT; t++) acc[t] = zero4();
-  // destination rows first, so their latency hides under the weight loads
+  // destination rows: lane r of every lane group already holds the pair of row r (f0), and
+  // this lane's result rows are 4g + j, so they come from a cross-lane shuffle, not a load
   const int P = a.T * a.k;
   int dst[4];
 #pragma unroll
   for (int j = 0; j < 4; j++) {
-    const int p = p0 + 4 * g + j;
     if (!is_shared) {
-      const int f = a.sorted_ids[p];
+      const int f = __shfl(f0, 4 * g + j);
       dst[j] = f < P ? f : -1;
     } else {
-      const int t = p - a.cap;
+      const int t = p0 + 4 * g + j - a.cap;
       dst[j] = t < a.T ? P + t : -1;
     }
   }
