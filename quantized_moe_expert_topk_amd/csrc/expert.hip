@@ -188,7 +188,9 @@ __device__ __forceinline__ uint32_t scale_tile_off(uint32_t row, uint32_t K) {
 //              NT x 16 RB bytes.  The run's scale bytes (one contiguous 16 RB-byte run per
 //              tile in this layout) are fetched with 16-byte loads issued before the first
 //              group's weight loads, staged there and read back per lane.  Shorter runs
-//              (lsc unused) load each lane's SP scale bytes per step and tile.
+//              (lsc unused) load each lane's SP scale bytes per step and tile.  Q4_0 stages
+//              the same way (its 2 scale bytes per 32 elements give NVFP4's run length) and
+//              reads back the 8 bytes of its row per step.
 template <int FMT, int NT, int COUNT, bool F16 = false>
 __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FMT> &m, const uint32_t (&rows)[NT],
                                         int b_k0, int kw0, int kvalid, int g, f32x4_t (&acc)[NT],
@@ -198,7 +200,8 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
   constexpr bool BF16 = FMT == MOE_FMT_BF16;
   constexpr bool Q4 = FMT == MOE_FMT_Q4_0;
   constexpr int NPF = (FP4 || Q4) ? 2 : 1;
-  constexpr int SP = FMT == MOE_FMT_NVFP4 ? 2 : 1;
+  constexpr int SP = (FMT == MOE_FMT_NVFP4 || Q4) ? 2 : 1;  // scale bytes per 32 elements
+  constexpr bool STAGE = FP4 || Q4;                          // formats with per-row scale runs
   const uint32_t K = (uint32_t)m.K;
   const int lane = lane_id(), r = lane & 15;
   uint32_t cb[NT], sb[NT];
@@ -208,10 +211,10 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
     // Q4_0 scales: tile-16 order in units of one step's 4 fp16 (8 bytes)
     sb[t] = FP4 ? scale_tile_off<FMT>(rows[t], K) : Q4 ? (rows[t] & ~15u) * (K / 16) + (rows[t] & 15u) * 8 : 0;
   }
-  constexpr int RB = FP4 ? 4 * COUNT * SP : 16;  // staged scale bytes per lane (16 lanes per tile)
+  constexpr int RB = STAGE ? 4 * COUNT * SP : 16;  // staged scale bytes per lane (16 lanes per tile)
   constexpr int SQ = RB / 16;
   uint4 stg[SQ > 0 ? SQ : 1];
-  if constexpr (FP4 && SQ > 0) {
+  if constexpr (STAGE && SQ > 0) {
     {  // lanes 16t..16t+15 fetch tile t's run
       const uint32_t run = (rows[(lane >> 4) % NT] & ~15u) * (K / 32) * SP + ((b_k0 + kw0) / 32) * 16 * SP;
 #pragma unroll
@@ -250,7 +253,7 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
 #pragma unroll
         for (int t = 0; t < NT; t++) {
           c0[ii][t] = buf_load16(m.codes, cb[t] + (4 * st + g) * 256);
-          qsv[ii][t] = buf_load8(m.scales, sb[t] + st * 128);
+          if constexpr (SQ == 0) qsv[ii][t] = buf_load8(m.scales, sb[t] + st * 128);
         }
       } else if constexpr (BF16) {
         const int kc = kw0 + (128 * i < kvalid ? 128 * i : 0);  // the step
@@ -278,7 +281,7 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
         }
       }
     }
-    if constexpr (FP4 && SQ > 0) {
+    if constexpr (STAGE && SQ > 0) {
       {  // scale bytes from the wave's LDS region (staged once per run)
         {
           if (i0 == 0) {  // the first group's weight loads are in flight by now
@@ -291,12 +294,19 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
         }
 #pragma unroll
         for (int ii = 0; ii < NPF; ii++) {
-          const int kr = 128 * (i0 + ii) + 32 * g;
-          const int cr = (kr < kvalid ? kr : 0) / 32;  // this lane's piece within the run
+          if constexpr (Q4) {  // the 4 scales of this lane's row for the step (a run of 128-byte steps)
+            const int ist = 128 * (i0 + ii) < kvalid ? i0 + ii : 0;
 #pragma unroll
-          for (int t = 0; t < NT; t++) {
-            const uint8_t *p = lsc + 16 * t * RB + cr * 16 * SP + r * SP;
-            lsv[ii][t] = SP == 2 ? (uint32_t)*reinterpret_cast<const uint16_t *>(p) : (uint32_t)*p;
+            for (int t = 0; t < NT; t++)
+              qsv[ii][t] = *reinterpret_cast<const uint2 *>(lsc + 16 * t * RB + ist * 128 + r * 8);
+          } else {
+            const int kr = 128 * (i0 + ii) + 32 * g;
+            const int cr = (kr < kvalid ? kr : 0) / 32;  // this lane's piece within the run
+#pragma unroll
+            for (int t = 0; t < NT; t++) {
+              const uint8_t *p = lsc + 16 * t * RB + cr * 16 * SP + r * SP;
+              lsv[ii][t] = SP == 2 ? (uint32_t)*reinterpret_cast<const uint16_t *>(p) : (uint32_t)*p;
+            }
           }
         }
       }
@@ -548,7 +558,7 @@ __global__ __launch_bounds__(64 * KW, kMinWaves) void k_gate_up(GateUpArgs a) {
   __shared__ float red[KW][2 * GT][4][64];  // [wave][tile][j][lane]
   __shared__ float hbuf[16][GCOLS + 1];      // MXFP4: the block's h before the plane split
   // FP4: per wave, the scale bytes of the workgroup's 2*GCOLS weight rows over one run
-  __shared__ __attribute__((aligned(16))) uint8_t lsc[(FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_MXFP4_E8M0) ? KW * 2 * GCOLS * (128 * COUNT / (FMT == MOE_FMT_NVFP4 ? 16 : 32)) : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t lsc[(FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_MXFP4_E8M0 || FMT == MOE_FMT_Q4_0) ? KW * 2 * GCOLS * (128 * COUNT / (FMT == MOE_FMT_MXFP4_E8M0 ? 32 : 16)) : 16];
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int sb = blockIdx.x;
@@ -593,11 +603,12 @@ __global__ __launch_bounds__(64 * KW, kMinWaves) void k_gate_up(GateUpArgs a) {
     gsc[t] = FMT == MOE_FMT_NVFP4 ? glob[(size_t)e * 2 * I + rows[t]] : 1.f;
     usc[t] = FMT == MOE_FMT_NVFP4 ? glob[(size_t)e * 2 * I + rows[GT + t]] : 1.f;
   }
-  // FP4 scales are staged per wave when a run's scale bytes per tile are whole 16-byte
-  // pieces (runs of at least 2 steps for NVFP4, 4 for MXFP4); otherwise lanes load theirs
+  // FP4 and Q4_0 scales are staged per wave when a run's scale bytes per tile are whole
+  // 16-byte pieces (runs of at least 2 steps for NVFP4 and Q4_0, 4 for MXFP4); otherwise
+  // lanes load theirs
   uint8_t *wsc = nullptr;
-  if constexpr (FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_MXFP4_E8M0) {
-    constexpr int sdiv = FMT == MOE_FMT_NVFP4 ? 16 : 32;
+  if constexpr (FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_MXFP4_E8M0 || FMT == MOE_FMT_Q4_0) {
+    constexpr int sdiv = FMT == MOE_FMT_MXFP4_E8M0 ? 32 : 16;  // elements per scale byte
     constexpr int RB = 128 * COUNT / sdiv;
     if (RB % 16 == 0) wsc = &lsc[wave * 2 * GCOLS * RB];
   }
@@ -688,7 +699,7 @@ constexpr int DNT = 4;
 template <int FMT, int COUNT>
 __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
   // FP4: per wave, the scale bytes of its 16*DNT weight rows over one run
-  __shared__ __attribute__((aligned(16))) uint8_t lsc[(FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_MXFP4_E8M0) ? 4 * 16 * DNT * (128 * COUNT / (FMT == MOE_FMT_NVFP4 ? 16 : 32)) : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t lsc[(FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_MXFP4_E8M0 || FMT == MOE_FMT_Q4_0) ? 4 * 16 * DNT * (128 * COUNT / (FMT == MOE_FMT_MXFP4_E8M0 ? 32 : 16)) : 16];
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int sb = blockIdx.x;
@@ -721,11 +732,12 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
   const int H = a.H, I = a.I, Il = a.Il;
   const int ntile = min(DNT, (H - n0) / 16);
   const WMat<FMT> m = weight_matrix<FMT>(codes, scales, e, H, I);
-  // FP4 scales are staged per wave when a run's scale bytes per tile are whole 16-byte
-  // pieces (runs of at least 2 steps for NVFP4, 4 for MXFP4); otherwise lanes load theirs
+  // FP4 and Q4_0 scales are staged per wave when a run's scale bytes per tile are whole
+  // 16-byte pieces (runs of at least 2 steps for NVFP4 and Q4_0, 4 for MXFP4); otherwise
+  // lanes load theirs
   uint8_t *wsc = nullptr;
-  if constexpr (FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_MXFP4_E8M0) {
-    constexpr int sdiv = FMT == MOE_FMT_NVFP4 ? 16 : 32;
+  if constexpr (FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_MXFP4_E8M0 || FMT == MOE_FMT_Q4_0) {
+    constexpr int sdiv = FMT == MOE_FMT_MXFP4_E8M0 ? 32 : 16;  // elements per scale byte
     constexpr int RB = 128 * COUNT / sdiv;
     if (RB % 16 == 0) wsc = &lsc[wave * 16 * DNT * RB];
   }
