@@ -48,7 +48,7 @@ def log(msg):
 
 
 def expert_slice_bytes(fmt, H, Il):
-    """Bytes of one expert's slice (both projections), SURVEY-style algorithmic count."""
+    """Algorithmic bytes of one expert's slice (both projections): codes, scales and globals read once."""
     if fmt == "nvfp4":
         return 3 * Il * H * 9 // 16 + 8 * Il + 4 * H
     if fmt == "q4_0":  # 4-bit codes and an fp16 scale per 32
@@ -278,9 +278,8 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the layer runs on one rank's intermediate slice and this build has "
-              "no multi-GPU path (the cross-rank all-reduce of partials is out of scope). Use --gpus 1.",
-              file=sys.stderr)
+        print("bench.py measures one GPU: the layer runs on one rank's intermediate slice, and the cross-rank "
+              "all-reduce of the partials is not implemented. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
     cfg, results = run(args)
     head = results[0]
