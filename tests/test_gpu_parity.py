@@ -414,12 +414,15 @@ def test_gpu_slices_sum_to_gpu_full(cid, T, cuts):
     check_close(f"slice sum cfg{cid} T={T} cuts={cuts}", parts, full.astype(np.float64))
 
 
-def test_pre_sliced_bank_equals_slice_of_full_bank():
-    """A rank's own storage [0, Il) gives bit-identical results to [lo, hi) of the full bank."""
-    inp, r = inputs_for(2, 32)
+@pytest.mark.parametrize("cid", [2, 6, 7])
+def test_pre_sliced_bank_equals_slice_of_full_bank(cid):
+    """A rank's own storage [0, Il) gives bit-identical results to [lo, hi) of the full bank
+    (NVFP4 with a shared expert, bf16, q4_0)."""
+    inp, r = inputs_for(cid, 32)
     for lo, hi in ((0, 256), (256, 512), (128, 384)):
         full = _forward_gpu(inp, r["ids"], r["w"], lo, hi)
-        own = (device_bank(S.slice_bank(inp.routed, lo, hi)), device_bank(S.slice_bank(inp.shared, lo, hi)))
+        own = (device_bank(S.slice_bank(inp.routed, lo, hi)),
+               device_bank(S.slice_bank(inp.shared, lo, hi)) if inp.shared is not None else None)
         mine = _forward_gpu(inp, r["ids"], r["w"], 0, hi - lo, banks=own)
         np.testing.assert_array_equal(mine, full)
 
