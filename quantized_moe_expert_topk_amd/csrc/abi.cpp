@@ -191,7 +191,7 @@ int check_align_out(const moe_align_out *al, int T, int k, int E) {
 
 struct FwdPlan {
   int Il, n_routed_sub, n_shared_sub, n_shared_tiles, shared_rows, h_rows, P, Psh;
-  bool tiled;  // 128-row align blocks (NVFP4, FP8_BLOCK128): the LDS-tiled kernels
+  bool tiled;  // 128-row align blocks (NVFP4, FP8_BLOCK128, BF16): the tiled prefill kernels
   // workspace layout: [h][x planes (MXFP4)][Y]; MXFP4 h is [hq][hs], x is [xq][xs]
   size_t hs_off, xq_off, xs_off, y_off, y_bytes, total;
 };

@@ -10,10 +10,12 @@
 // [lo,hi): FreeToken issue #62 "What it touches" item 1), and so is the math (issue #520
 // section 4 "Expert sharding": silu(gate)*up @ down, linear in the intermediate index).
 //
-// NVFP4 and fp8-block weights are dequantized in registers to bf16 and fed to
-// v_mfma_f32_16x16x32_bf16 (W4A16 / W8A16):
-//   NVFP4      e2m1 * e4m3 group scale (exact in bf16); the fp32 per-row global is applied
-//              to the fp32 accumulator in the epilogue.
+// NVFP4 and fp8-block weights are dequantized in registers and fed to the 16x16x32 MFMA
+// (W4A16 / W8A16):
+//   NVFP4      e2m1 * e4m3 group scale, exact in f16 (and bf16): the activation fragment is
+//              converted to f16 once per chunk and v_mfma_f32_16x16x32_f16 runs; a wave whose
+//              accumulators turn non-finite (an activation beyond f16's range) redoes its K
+//              range in bf16.  The fp32 per-row global is applied in the epilogue.
 //   FP8_BLOCK  e4m3 -> bf16 exact; the fp32 128x128 block scale multiplies each 128-wide
 //              K chunk's partial sum.
 //   BF16       used as stored.
