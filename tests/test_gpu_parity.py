@@ -368,7 +368,8 @@ def test_wide_kernels_ragged_shapes(H, I, sl, T, bm):
 
 
 @pytest.mark.parametrize("cid,T,sl,bm", [(3, 8192, (0, 512), 128), (3, 8192, (0, 256), 128),
-                                         (4, 4096, (0, 256), 128), (3, 8192, (0, 512), 64)])
+                                         (4, 4096, (0, 256), 128), (3, 8192, (0, 512), 64),
+                                         (6, 8192, (0, 512), 128), (5, 256, (0, 1024), None)])
 def test_prefill_full_size_sampled_rows(cid, T, sl, bm):
     """Full-size prefill on the GPU (every tile of the real routing, Zipf-skewed for
     config 3), checked on a seeded sample of token rows the oracle computes one by one."""
