@@ -1,4 +1,4 @@
-// expert_wide.hip -- NVFP4 expert GEMMs for many tokens per expert (prefill), gfx950.
+// expert_wide.hip -- NVFP4 and bf16 expert GEMMs for many tokens per expert (prefill), gfx950.
 //
 // Same computation as expert.hip and expert_tiled.hip (gate rows [lo,hi), up rows
 // [I+lo, I+hi), down columns [lo,hi) of one rank's slice: FreeToken issue #62 "What it
@@ -16,6 +16,9 @@
 // [64 h, 64 h + 64) of each 128-wide stage (h = l / 32), i.e. two 16-byte code pieces of the
 // tile-16 layout, and MFMA c of the stage takes K [64 h + 8 c, +8) from both operands.  Each
 // wave dequantizes only its own 64 rows; per stage it runs 64 MFMAs against 4 KB of codes.
+// bf16 weights (no dequantization, 2 bytes per weight) take 64-wide K stages instead, so that
+// two stages of a lane's weights still fit its registers: lane l then holds K [32 h, 32 h + 32)
+// of each stage, four 16-byte pieces.
 //
 // K loop: stage s multiplies from LDS buffer s%2 and weight register set s%2, while the
 // activation loads of stage s+2 and the weight loads of stage s+2 (issued once set s%2 is
@@ -33,8 +36,11 @@ namespace qmoe {
 namespace {
 
 constexpr int WM = 128;          // pair rows per workgroup (one align block of 128)
-constexpr int WK = 128;          // K per stage
 constexpr int WCOLS = 256;       // weight rows per workgroup (64 per wave)
+
+// K per stage: 128 for NVFP4 (4 KB of codes per wave), 64 for bf16 (8 KB per wave).
+template <int FMT>
+constexpr int kWideK = FMT == MOE_FMT_BF16 ? 64 : 128;
 
 // Output tile of one wave after the K loop: 128 rows x 64 bf16, rows padded to 72 so that
 // the two row groups a 32x32 result register covers (rows 4 apart) fall in different banks.
@@ -42,24 +48,35 @@ constexpr int OPITCH = 72;
 
 struct __attribute__((aligned(16))) WideLDS {
   union {
-    uint16_t a[2][WM][WK];           // K loop: activation tiles, 2 x 32 KB
+    uint16_t a[2 * WM * 128];        // K loop: activation tiles, 2 x [128][WK] (32 or 16 KB each)
     uint16_t o[4][WM][OPITCH];       // epilogue: each wave's output tile, 4 x 18 KB
   };
   int32_t dst[WM];  // down: destination row of each pair row (-1: none)
 };
 
-// K chunk c (elements [8c, 8c+8)) of tile row R sits at chunk c ^ (R & 15) of its 256-byte
-// row: a fragment read (16 consecutive rows, one chunk index per 16 lanes) and a 16-lane row
-// store then touch every bank once.
-__device__ __forceinline__ int wswz(int R, int c) { return 8 * (c ^ (R & 15)); }
+// K chunk c (elements [8c, 8c+8)) of tile row R is stored XOR-swizzled so that a fragment read
+// (16 consecutive rows, one chunk index per 16 lanes) and a row store touch every bank once:
+// 256-byte rows (WK 128) at chunk c ^ (R & 15); 128-byte rows (WK 64, two rows per 256 bytes of
+// banks) at chunk c ^ ((R >> 1) & 7).
+template <int WK>
+__device__ __forceinline__ int wswz(int R, int c) {
+  return WK == 128 ? 8 * (c ^ (R & 15)) : 8 * (c ^ ((R >> 1) & 7));
+}
 
+// A thread's share of one activation stage: chunk tid % CPR of rows tid / CPR + RSTEP q.
+template <int WK>
 struct AStage {
-  uint4 v[8];  // chunk tid%16 of rows tid/16 + 16q
+  static constexpr int CPR = WK / 8, NQ = WM * CPR / 256, RSTEP = 256 / CPR;
+  uint4 v[NQ];
 };
 
+// A lane's weights of one stage.  NVFP4: [column tile][piece] codes (32 e2m1 each) and the
+// pieces' two e4m3 group scales; bf16: [column tile][piece] 8 bf16 each.
+template <int FMT>
 struct BStage {
-  uint4 c[2][2];     // [column tile][piece]: 32 e2m1 codes each
-  uint32_t s[2][2];  // the pieces' two e4m3 group scales
+  static constexpr int NP = FMT == MOE_FMT_BF16 ? 4 : 2;
+  uint4 c[2][NP];
+  uint32_t s[2][FMT == MOE_FMT_BF16 ? 1 : 2];
 };
 
 // The pipelined K loop.  a_off: byte offsets of the K origin of the thread's 8 activation
@@ -67,63 +84,84 @@ struct BStage {
 // lane's weight row in each of the wave's two 32-row column tiles.  K runs over nK stages
 // from weight column b_k0; positions at or past kvalid (a multiple of 32) contribute zero
 // (TAIL: kvalid may end inside a stage; otherwise it is nK * 128).
-template <bool TAIL>
-__device__ __forceinline__ void wide_k_loop(WideLDS &lds, rsrc_t ra, const uint32_t (&a_off)[8],
-                                            const WMat<MOE_FMT_NVFP4> &m, const uint32_t (&cb)[2],
-                                            const uint32_t (&sb)[2], int b_k0, int nK, int kvalid,
-                                            f32x16_t (&acc)[4][2]) {
+// AFFINE: the activation rows are consecutive, a_off[q] = a_off[0] + q * a_stride (down, whose
+// h rows are; only a_off[0] is read, which keeps 7 registers free).
+template <int FMT, bool TAIL, bool AFFINE>
+__device__ __forceinline__ void wide_k_loop(WideLDS &lds, rsrc_t ra,
+                                            const uint32_t (&a_off)[AStage<kWideK<FMT>>::NQ], uint32_t a_stride,
+                                            const WMat<FMT> &m, const uint32_t (&cb)[2], const uint32_t (&sb)[2],
+                                            int b_k0, int nK, int kvalid, f32x16_t (&acc)[4][2]) {
+  constexpr int WK = kWideK<FMT>;
+  using AS = AStage<WK>;
+  using BS = BStage<FMT>;
   const int tid = threadIdx.x, lane = tid & 63, r32 = lane & 31, h = lane >> 5;
-  const int ac = tid & 15;  // the activation chunk this thread stages
-  AStage at;
-  BStage bt[2];
-  auto fetch_a = [&](int st, AStage &t) {
+  const int ac = tid % AS::CPR;  // the activation chunk this thread stages
+  AS at;
+  BS bt[2];
+  auto abuf = [&](int st) { return &lds.a[(st & 1) * WM * WK]; };  // [WM][WK]
+  auto fetch_a = [&](int st, AS &t) {
     const int k = st * WK + 8 * ac;
     const uint32_t kk = (uint32_t)(k < kvalid ? k : 0);
 #pragma unroll
-    for (int q = 0; q < 8; q++) t.v[q] = buf_load16(ra, a_off[q] + kk * 2);
+    for (int q = 0; q < AS::NQ; q++) t.v[q] = buf_load16(ra, (AFFINE ? a_off[0] + q * a_stride : a_off[q]) + kk * 2);
   };
-  auto fetch_b = [&](int st, BStage &t) {
+  auto fetch_b = [&](int st, BS &t) {
+    if constexpr (FMT == MOE_FMT_BF16) {  // pieces of 8: K [32 h + 8 p, +8) of the stage
+      const int k = st * WK + 32 * h;
+      const uint32_t pc = (uint32_t)(b_k0 + (k < kvalid ? k : 0)) / 8;
 #pragma unroll
-    for (int p = 0; p < 2; p++) {
-      const int k = st * WK + 64 * h + 32 * p;
-      const uint32_t pc = (uint32_t)(b_k0 + (k < kvalid ? k : 0)) / 32;
+      for (int p = 0; p < 4; p++)
 #pragma unroll
-      for (int ct = 0; ct < 2; ct++) {
-        t.c[ct][p] = buf_load16(m.codes, cb[ct] + pc * 256);
-        t.s[ct][p] = buf_load2(m.scales, sb[ct] + pc * 32);
+        for (int ct = 0; ct < 2; ct++) t.c[ct][p] = buf_load16(m.codes, cb[ct] + (pc + p) * 256);
+    } else {  // pieces of 32: K [64 h + 32 p, +32) of the stage
+#pragma unroll
+      for (int p = 0; p < 2; p++) {
+        const int k = st * WK + 64 * h + 32 * p;
+        const uint32_t pc = (uint32_t)(b_k0 + (k < kvalid ? k : 0)) / 32;
+#pragma unroll
+        for (int ct = 0; ct < 2; ct++) {
+          t.c[ct][p] = buf_load16(m.codes, cb[ct] + pc * 256);
+          t.s[ct][p] = buf_load2(m.scales, sb[ct] + pc * 32);
+        }
       }
     }
   };
-  auto store_a = [&](int st, const AStage &t) {
+  auto store_a = [&](int st, const AS &t) {
     const bool ok = !TAIL || st * WK + 8 * ac < kvalid;
+    uint16_t *b = abuf(st);
 #pragma unroll
-    for (int q = 0; q < 8; q++) {
-      const int R = (tid >> 4) + 16 * q;
-      *reinterpret_cast<uint4 *>(&lds.a[st & 1][R][wswz(R, ac)]) = ok ? t.v[q] : make_uint4(0, 0, 0, 0);
+    for (int q = 0; q < AS::NQ; q++) {
+      const int R = tid / AS::CPR + AS::RSTEP * q;
+      *reinterpret_cast<uint4 *>(b + R * WK + wswz<WK>(R, ac)) = ok ? t.v[q] : make_uint4(0, 0, 0, 0);
     }
   };
-  // MFMA c of a stage takes K [64 h + 8 c, +8) in this lane.  Chunks are software pipelined:
-  // the A fragments of chunk c+1 are read (and its B fragments dequantized) before chunk c's
-  // MFMAs issue, so the LDS latency and the VALU work hide under the matrix core.
+  // MFMA c of a stage takes K [(WK / 2) h + 8 c, +8) in this lane.
   auto read_a = [&](int st, int c, frag8 (&f)[4]) {
+    const uint16_t *b = abuf(st);
 #pragma unroll
     for (int mi = 0; mi < 4; mi++)
-      f[mi].q = *reinterpret_cast<const uint4 *>(&lds.a[st & 1][32 * mi + r32][wswz(r32, 8 * h + c)]);
+      f[mi].q = *reinterpret_cast<const uint4 *>(b + (32 * mi + r32) * WK + wswz<WK>(r32, (WK / 16) * h + c));
   };
-  auto dec_b = [&](int st, int c, const BStage &t, frag8 (&f)[2]) {
-    const int p = c >> 2, d = c & 3;
-    const bool bvalid = !TAIL || st * WK + 64 * h + 32 * p < kvalid;
+  auto dec_b = [&](int st, int c, const BS &t, frag8 (&f)[2]) {
+    if constexpr (FMT == MOE_FMT_BF16) {
+      const bool bvalid = !TAIL || st * WK + 32 * h < kvalid;
 #pragma unroll
-    for (int ct = 0; ct < 2; ct++) {
-      const uint4 &cv = t.c[ct][p];
-      const uint32_t code = d == 0 ? cv.x : d == 1 ? cv.y : d == 2 ? cv.z : cv.w;
-      fp4x8_mul_to_bf16(code, e4m3_to_f32(t.s[ct][p] >> (8 * (d >> 1))), f[ct]);
-      if (!bvalid) f[ct].q = make_uint4(0, 0, 0, 0);
+      for (int ct = 0; ct < 2; ct++) f[ct].q = bvalid ? t.c[ct][c] : make_uint4(0, 0, 0, 0);
+    } else {
+      const int p = c >> 2, d = c & 3;
+      const bool bvalid = !TAIL || st * WK + 64 * h + 32 * p < kvalid;
+#pragma unroll
+      for (int ct = 0; ct < 2; ct++) {
+        const uint4 &cv = t.c[ct][p];
+        const uint32_t code = d == 0 ? cv.x : d == 1 ? cv.y : d == 2 ? cv.z : cv.w;
+        fp4x8_mul_to_bf16(code, e4m3_to_f32(t.s[ct][p] >> (8 * (d >> 1))), f[ct]);
+        if (!bvalid) f[ct].q = make_uint4(0, 0, 0, 0);
+      }
     }
   };
-  auto compute = [&](int st, const BStage &t) {
+  auto compute = [&](int st, const BS &t) {
 #pragma unroll
-    for (int c = 0; c < 8; c++) {
+    for (int c = 0; c < WK / 16; c++) {
       frag8 af[4], bf[2];
       read_a(st, c, af);
       dec_b(st, c, t, bf);
@@ -140,7 +178,7 @@ __device__ __forceinline__ void wide_k_loop(WideLDS &lds, rsrc_t ra, const uint3
   __syncthreads();
   // Fetches past the last stage reload clamped offsets (unused) and the store after the
   // last stage fills the idle buffer with zeros, so every path keeps the same loads in flight.
-  auto stage = [&](int st, BStage &b_cur) {
+  auto stage = [&](int st, BS &b_cur) {
     fetch_a(st + 1, at);
     compute(st, b_cur);
     fetch_b(st + 2, b_cur);
@@ -184,7 +222,10 @@ __device__ __forceinline__ int d_row(int lane, int j) { return 8 * (j >> 2) + 4 
 // gate_up + SwiGLU.  Column group cg covers slice columns [c0, c0 + 128): wave w owns gate
 // rows lo + c0 + 32 w + [0, 32) (column tile 0) and the matching up rows I + ... (column
 // tile 1), so SwiGLU stays in registers.
+template <int FMT>
 __global__ __launch_bounds__(256, 2) void k_gate_up_wide(GateUpArgs a, int n_rb, int ncg) {
+  constexpr int WK = kWideK<FMT>;
+  using AS = AStage<WK>;
   __shared__ WideLDS lds;
   const int n_routed = a.cap / WM;
   int rb, cg;
@@ -210,12 +251,12 @@ __global__ __launch_bounds__(256, 2) void k_gate_up_wide(GateUpArgs a, int n_rb,
     glob = a.sgug;
   }
   const int T = a.T, H = a.H, I = a.I, Il = a.Il, P = a.T * a.k;
-  const WMat<MOE_FMT_NVFP4> m = weight_matrix<MOE_FMT_NVFP4>(codes, scales, e, 2 * I, H);
+  const WMat<FMT> m = weight_matrix<FMT>(codes, scales, e, 2 * I, H);
   const rsrc_t ra = make_rsrc(a.x, (uint32_t)T * H * 2);
-  uint32_t a_off[8];
+  uint32_t a_off[AS::NQ];
 #pragma unroll
-  for (int q = 0; q < 8; q++) {
-    const int p = p0 + (tid >> 4) + 16 * q;
+  for (int q = 0; q < AS::NQ; q++) {
+    const int p = p0 + tid / AS::CPR + AS::RSTEP * q;
     int tok;
     if (!is_shared) {
       const int f = a.sorted_ids[p];
@@ -231,13 +272,14 @@ __global__ __launch_bounds__(256, 2) void k_gate_up_wide(GateUpArgs a, int n_rb,
 #pragma unroll
   for (int ct = 0; ct < 2; ct++) {
     const uint32_t row = (uint32_t)((ct == 0 ? 0 : I) + a.lo + cc);
-    cb[ct] = (row & ~15u) * (uint32_t)(H / 2) + (row & 15u) * 16;
-    sb[ct] = (row & ~15u) * (uint32_t)(H / 16) + (row & 15u) * 2;
+    cb[ct] = (row & ~15u) * (uint32_t)(FMT == MOE_FMT_BF16 ? 2 * H : H / 2) + (row & 15u) * 16;
+    sb[ct] = (row & ~15u) * (uint32_t)(H / 16) + (row & 15u) * 2;  // NVFP4 scales
   }
-  const float gg = glob[(size_t)e * 2 * I + a.lo + cc], ug = glob[(size_t)e * 2 * I + I + a.lo + cc];
+  const float gg = FMT == MOE_FMT_NVFP4 ? glob[(size_t)e * 2 * I + a.lo + cc] : 1.f;
+  const float ug = FMT == MOE_FMT_NVFP4 ? glob[(size_t)e * 2 * I + I + a.lo + cc] : 1.f;
   f32x16_t acc[4][2];
   zero_acc(acc);
-  wide_k_loop<false>(lds, ra, a_off, m, cb, sb, 0, H / WK, H, acc);
+  wide_k_loop<FMT, false, false>(lds, ra, a_off, 0, m, cb, sb, 0, H / WK, H, acc);
   // h through LDS (the K loop ended with a barrier): each wave's 128 x 32 block, then rows
   // leave as 16-byte chunks (4 lanes per 64-byte row segment)
   uint16_t (*o)[OPITCH] = lds.o[wave];
@@ -264,7 +306,10 @@ __global__ __launch_bounds__(256, 2) void k_gate_up_wide(GateUpArgs a, int n_rb,
 // down.  Column group cg covers hidden columns [cg * 256, +256): wave w owns 64 w + [0, 64)
 // of them (two 32-column tiles); K = the slice.  The pair rows go to Y in bf16 (the combine
 // weights and sums them in fp32), as in the other prefill kernels.
+template <int FMT>
 __global__ __launch_bounds__(256, 2) void k_down_wide(DownArgs a, int n_rb, int ncg) {
+  constexpr int WK = kWideK<FMT>;
+  using AS = AStage<WK>;
   __shared__ WideLDS lds;
   const int n_routed = a.cap / WM;
   int rb, cg;
@@ -289,11 +334,10 @@ __global__ __launch_bounds__(256, 2) void k_down_wide(DownArgs a, int n_rb, int 
     glob = a.sdng;
   }
   const int T = a.T, H = a.H, I = a.I, Il = a.Il, P = a.T * a.k;
-  const WMat<MOE_FMT_NVFP4> m = weight_matrix<MOE_FMT_NVFP4>(codes, scales, e, H, I);
+  const WMat<FMT> m = weight_matrix<FMT>(codes, scales, e, H, I);
   const rsrc_t ra = make_rsrc(a.h, (uint32_t)a.h_rows * Il * 2);
-  uint32_t a_off[8];
-#pragma unroll
-  for (int q = 0; q < 8; q++) a_off[q] = (uint32_t)(p0 + (tid >> 4) + 16 * q) * Il * 2;
+  uint32_t a_off[AS::NQ] = {(uint32_t)(p0 + tid / AS::CPR) * Il * 2};  // rows RSTEP apart
+  const uint32_t a_stride = (uint32_t)AS::RSTEP * Il * 2;
   int n[2];
   uint32_t cb[2], sb[2];
   float dg[2];
@@ -301,9 +345,9 @@ __global__ __launch_bounds__(256, 2) void k_down_wide(DownArgs a, int n_rb, int 
   for (int ct = 0; ct < 2; ct++) {
     n[ct] = cg * WCOLS + 64 * wave + 32 * ct + (lane & 31);
     const uint32_t row = (uint32_t)(n[ct] < H ? n[ct] : (lane & 31));  // columns past H read row lane%32 (unused)
-    cb[ct] = (row & ~15u) * (uint32_t)(I / 2) + (row & 15u) * 16;
-    sb[ct] = (row & ~15u) * (uint32_t)(I / 16) + (row & 15u) * 2;
-    dg[ct] = glob[(size_t)e * H + row];
+    cb[ct] = (row & ~15u) * (uint32_t)(FMT == MOE_FMT_BF16 ? 2 * I : I / 2) + (row & 15u) * 16;
+    sb[ct] = (row & ~15u) * (uint32_t)(I / 16) + (row & 15u) * 2;  // NVFP4 scales
+    dg[ct] = FMT == MOE_FMT_NVFP4 ? glob[(size_t)e * H + row] : 1.f;
   }
   if (tid < WM) {  // destination of each pair row, read back in the epilogue
     const int p = p0 + tid;
@@ -317,9 +361,9 @@ __global__ __launch_bounds__(256, 2) void k_down_wide(DownArgs a, int n_rb, int 
   f32x16_t acc[4][2];
   zero_acc(acc);
   if (Il % WK == 0)
-    wide_k_loop<false>(lds, ra, a_off, m, cb, sb, a.lo, Il / WK, Il, acc);
+    wide_k_loop<FMT, false, true>(lds, ra, a_off, a_stride, m, cb, sb, a.lo, Il / WK, Il, acc);
   else
-    wide_k_loop<true>(lds, ra, a_off, m, cb, sb, a.lo, (Il + WK - 1) / WK, Il, acc);
+    wide_k_loop<FMT, true, true>(lds, ra, a_off, a_stride, m, cb, sb, a.lo, (Il + WK - 1) / WK, Il, acc);
   // pair rows through LDS (the K loop ended with a barrier, which also published dst): each
   // wave's 128 x 64 block, then 16-byte chunks (8 lanes per 128-byte row)
   uint16_t (*o)[OPITCH] = lds.o[wave];
@@ -347,17 +391,23 @@ __global__ __launch_bounds__(256, 2) void k_down_wide(DownArgs a, int n_rb, int 
   }
 }
 
-hipError_t launch_gate_up_wide(const GateUpArgs &a, int n_shared_tiles, hipStream_t s) {
+hipError_t launch_gate_up_wide(int fmt, const GateUpArgs &a, int n_shared_tiles, hipStream_t s) {
   const int n_rb = a.cap / WM + n_shared_tiles, ncg = (a.Il + WCOLS / 2 - 1) / (WCOLS / 2);
   const int grid = (n_rb + 7) / 8 * 8 * ncg;
-  hipLaunchKernelGGL(k_gate_up_wide, dim3(grid), dim3(256), 0, s, a, n_rb, ncg);
+  if (fmt == MOE_FMT_BF16)
+    hipLaunchKernelGGL(k_gate_up_wide<MOE_FMT_BF16>, dim3(grid), dim3(256), 0, s, a, n_rb, ncg);
+  else
+    hipLaunchKernelGGL(k_gate_up_wide<MOE_FMT_NVFP4>, dim3(grid), dim3(256), 0, s, a, n_rb, ncg);
   return hipGetLastError();
 }
 
-hipError_t launch_down_wide(const DownArgs &a, int n_shared_tiles, hipStream_t s) {
+hipError_t launch_down_wide(int fmt, const DownArgs &a, int n_shared_tiles, hipStream_t s) {
   const int n_rb = a.cap / WM + n_shared_tiles, ncg = (a.H + WCOLS - 1) / WCOLS;
   const int grid = (n_rb + 7) / 8 * 8 * ncg;
-  hipLaunchKernelGGL(k_down_wide, dim3(grid), dim3(256), 0, s, a, n_rb, ncg);
+  if (fmt == MOE_FMT_BF16)
+    hipLaunchKernelGGL(k_down_wide<MOE_FMT_BF16>, dim3(grid), dim3(256), 0, s, a, n_rb, ncg);
+  else
+    hipLaunchKernelGGL(k_down_wide<MOE_FMT_NVFP4>, dim3(grid), dim3(256), 0, s, a, n_rb, ncg);
   return hipGetLastError();
 }
 

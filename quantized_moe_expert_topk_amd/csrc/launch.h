@@ -62,10 +62,10 @@ hipError_t launch_down(int fmt, const DownArgs &a, int n_shared_sub, hipStream_t
 // rows are ceil(T/128) tiles after the routed ones.
 hipError_t launch_gate_up_tiled(int fmt, const GateUpArgs &a, int n_shared_tiles, hipStream_t s);
 hipError_t launch_down_tiled(int fmt, const DownArgs &a, int n_shared_tiles, hipStream_t s);
-// NVFP4 prefill GEMMs with only the activation tile in LDS (128 pair rows x 256 weight rows
-// per workgroup); same grid rows and outputs as the tiled kernels.
-hipError_t launch_gate_up_wide(const GateUpArgs &a, int n_shared_tiles, hipStream_t s);
-hipError_t launch_down_wide(const DownArgs &a, int n_shared_tiles, hipStream_t s);
+// NVFP4 and bf16 prefill GEMMs with only the activation tile in LDS (128 pair rows x 256
+// weight rows per workgroup); same grid rows and outputs as the tiled kernels.
+hipError_t launch_gate_up_wide(int fmt, const GateUpArgs &a, int n_shared_tiles, hipStream_t s);
+hipError_t launch_down_wide(int fmt, const DownArgs &a, int n_shared_tiles, hipStream_t s);
 // moe_pack_bank: [rows, pitch] bytes -> 16-row tiles stored piece-major in units of `unit`
 // (16, 8, 2 or 1) bytes.
 hipError_t launch_pack_tile16(const void *src, void *dst, size_t rows, uint32_t pitch, int unit, hipStream_t s);
