@@ -483,14 +483,14 @@ hipError_t launch_router_tiled(const uint16_t *x, int T, int H, const uint16_t *
 
 hipError_t launch_gate_up_tiled(int fmt, const GateUpArgs &a, int n_shared_tiles, hipStream_t s) {
   const dim3 grid(a.cap / TM + n_shared_tiles, (a.Il + 63) / 64);
-  if (fmt == MOE_FMT_NVFP4 || fmt == MOE_FMT_BF16) return launch_gate_up_wide(fmt, a, n_shared_tiles, s);
+  if (fmt == MOE_FMT_NVFP4 || fmt == MOE_FMT_BF16 || fmt == MOE_FMT_FP8_BLOCK128) return launch_gate_up_wide(fmt, a, n_shared_tiles, s);
   hipLaunchKernelGGL(k_gate_up_tiled<MOE_FMT_FP8_BLOCK128>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_down_tiled(int fmt, const DownArgs &a, int n_shared_tiles, hipStream_t s) {
   const dim3 grid(a.cap / TM + n_shared_tiles, a.H / TW);
-  if (fmt == MOE_FMT_NVFP4 || fmt == MOE_FMT_BF16) return launch_down_wide(fmt, a, n_shared_tiles, s);
+  if (fmt == MOE_FMT_NVFP4 || fmt == MOE_FMT_BF16 || fmt == MOE_FMT_FP8_BLOCK128) return launch_down_wide(fmt, a, n_shared_tiles, s);
   hipLaunchKernelGGL(k_down_tiled<MOE_FMT_FP8_BLOCK128>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -1,10 +1,12 @@
-// expert_wide.hip -- NVFP4 and bf16 expert GEMMs for many tokens per expert (prefill), gfx950.
+// expert_wide.hip -- NVFP4, fp8-block and bf16 expert GEMMs for many tokens per expert
+// (prefill), gfx950.
 //
 // Same computation as expert.hip and expert_tiled.hip (gate rows [lo,hi), up rows
 // [I+lo, I+hi), down columns [lo,hi) of one rank's slice: FreeToken issue #62 "What it
 // touches" item 1; SwiGLU expert linear in the intermediate index: issue #520 section 4;
 // NVFP4 W4A16 with the e4m3 group scale exact in bf16 and the per-row fp32 global applied
-// to the fp32 result: issue #520 section 2).
+// to the fp32 result: issue #520 section 2; fp8-block weights with one fp32 scale per 128 x 128
+// block: PR #637 "Implementation notes").
 //
 // Work split: a workgroup owns a 128-row block of the aligned pair list (one expert) and 256
 // weight rows; each of its 4 waves owns all 128 rows x 64 weight rows, 4 x 2 tiles of
@@ -18,7 +20,13 @@
 // wave dequantizes only its own 64 rows; per stage it runs 64 MFMAs against 4 KB of codes.
 // bf16 weights (no dequantization, 2 bytes per weight) take 64-wide K stages instead, so that
 // two stages of a lane's weights still fit its registers: lane l then holds K [32 h, 32 h + 32)
-// of each stage, four 16-byte pieces.
+// of each stage, four 16-byte pieces.  fp8-block weights (1 byte each, but 128-wide activation
+// stages would not fit beside them) take 64-wide stages too, two 16-byte pieces of 16 e4m3 per
+// lane, converted exactly to bf16; two stages make one 128 x 128 scale block of each 32-row
+// column tile.  The block scale cannot go into the bf16 operand exactly and a second set of
+// accumulators does not fit, so each tile's accumulators are held in units of the current
+// block's scale: entering a block with scale s' multiplies them by s / s' (s the previous
+// block's), and the epilogue multiplies by the last scale.
 //
 // K loop: stage s multiplies from LDS buffer s%2 and weight register set s%2, while the
 // activation loads of stage s+2 and the weight loads of stage s+2 (issued once set s%2 is
@@ -32,15 +40,17 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace qmoe {
 namespace {
 
 constexpr int WM = 128;          // pair rows per workgroup (one align block of 128)
 constexpr int WCOLS = 256;       // weight rows per workgroup (64 per wave)
 
-// K per stage: 128 for NVFP4 (4 KB of codes per wave), 64 for bf16 (8 KB per wave).
+// K per stage: 128 for NVFP4 (4 KB of codes per wave), 64 for bf16 (8 KB) and fp8-block (4 KB).
 template <int FMT>
-constexpr int kWideK = FMT == MOE_FMT_BF16 ? 64 : 128;
+constexpr int kWideK = FMT == MOE_FMT_NVFP4 ? 128 : 64;
 
 // Output tile of one wave after the K loop: 128 rows x 64 bf16, rows padded to 72 so that
 // the two row groups a 32x32 result register covers (rows 4 apart) fall in different banks.
@@ -71,26 +81,32 @@ struct AStage {
 };
 
 // A lane's weights of one stage.  NVFP4: [column tile][piece] codes (32 e2m1 each) and the
-// pieces' two e4m3 group scales; bf16: [column tile][piece] 8 bf16 each.
+// pieces' two e4m3 group scales; fp8-block: [column tile][piece] 16 e4m3 each and the tile's
+// block scale; bf16: [column tile][piece] 8 bf16 each.
 template <int FMT>
 struct BStage {
   static constexpr int NP = FMT == MOE_FMT_BF16 ? 4 : 2;
   uint4 c[2][NP];
-  uint32_t s[2][FMT == MOE_FMT_BF16 ? 1 : 2];
+  uint32_t s[2][2];
+  float bs[2];
 };
 
 // The pipelined K loop.  a_off: byte offsets of the K origin of the thread's 8 activation
 // rows (0x80000000: a row that reads zeros).  cb/sb: tile-16 code and scale offsets of this
-// lane's weight row in each of the wave's two 32-row column tiles.  K runs over nK stages
-// from weight column b_k0; positions at or past kvalid (a multiple of 32) contribute zero
-// (TAIL: kvalid may end inside a stage; otherwise it is nK * 128).
+// lane's weight row in each of the wave's two 32-row column tiles (fp8-block: sb is the
+// offset of the tile's row of block scales).  K runs over nK stages from weight column b_k0;
+// positions at or past kvalid (a multiple of 32) contribute zero (TAIL: kvalid may end inside
+// a stage; otherwise it is nK * WK).  fp8-block: post[ct] receives the scale the
+// accumulators of column tile ct are left in units of (0 while every block scale was 0);
+// b_k0 is a multiple of 128, so even stages start a scale block.
 // AFFINE: the activation rows are consecutive, a_off[q] = a_off[0] + q * a_stride (down, whose
 // h rows are; only a_off[0] is read, which keeps 7 registers free).
 template <int FMT, bool TAIL, bool AFFINE>
 __device__ __forceinline__ void wide_k_loop(WideLDS &lds, rsrc_t ra,
                                             const uint32_t (&a_off)[AStage<kWideK<FMT>>::NQ], uint32_t a_stride,
                                             const WMat<FMT> &m, const uint32_t (&cb)[2], const uint32_t (&sb)[2],
-                                            int b_k0, int nK, int kvalid, f32x16_t (&acc)[4][2]) {
+                                            int b_k0, int nK, int kvalid, f32x16_t (&acc)[4][2],
+                                            float (&post)[2]) {
   constexpr int WK = kWideK<FMT>;
   using AS = AStage<WK>;
   using BS = BStage<FMT>;
@@ -98,6 +114,8 @@ __device__ __forceinline__ void wide_k_loop(WideLDS &lds, rsrc_t ra,
   const int ac = tid % AS::CPR;  // the activation chunk this thread stages
   AS at;
   BS bt[2];
+  float scur[2] = {0.f, 0.f};  // fp8-block: the scale the accumulators are in units of
+  uint32_t zm[2] = {~0u, ~0u};  // fp8-block: all ones while the current block's scale is nonzero
   auto abuf = [&](int st) { return &lds.a[(st & 1) * WM * WK]; };  // [WM][WK]
   auto fetch_a = [&](int st, AS &t) {
     const int k = st * WK + 8 * ac;
@@ -113,6 +131,16 @@ __device__ __forceinline__ void wide_k_loop(WideLDS &lds, rsrc_t ra,
       for (int p = 0; p < 4; p++)
 #pragma unroll
         for (int ct = 0; ct < 2; ct++) t.c[ct][p] = buf_load16(m.codes, cb[ct] + (pc + p) * 256);
+    } else if constexpr (FMT == MOE_FMT_FP8_BLOCK128) {  // pieces of 16: K [32 h + 16 p, +16)
+      const int k = st * WK;
+      const uint32_t kk = (uint32_t)(b_k0 + (k < kvalid ? k : 0));
+      const uint32_t pc = kk / 16 + 2 * h;
+#pragma unroll
+      for (int p = 0; p < 2; p++)
+#pragma unroll
+        for (int ct = 0; ct < 2; ct++) t.c[ct][p] = buf_load16(m.codes, cb[ct] + (pc + p) * 256);
+#pragma unroll
+      for (int ct = 0; ct < 2; ct++) t.bs[ct] = buf_load_f32(m.scales, sb[ct] + kk / 128 * 4);
     } else {  // pieces of 32: K [64 h + 32 p, +32) of the stage
 #pragma unroll
       for (int p = 0; p < 2; p++) {
@@ -142,11 +170,21 @@ __device__ __forceinline__ void wide_k_loop(WideLDS &lds, rsrc_t ra,
     for (int mi = 0; mi < 4; mi++)
       f[mi].q = *reinterpret_cast<const uint4 *>(b + (32 * mi + r32) * WK + wswz<WK>(r32, (WK / 16) * h + c));
   };
+  // fp8-block: a zero block scale clears the codes (zm), so that its block adds nothing
   auto dec_b = [&](int st, int c, const BS &t, frag8 (&f)[2]) {
     if constexpr (FMT == MOE_FMT_BF16) {
       const bool bvalid = !TAIL || st * WK + 32 * h < kvalid;
 #pragma unroll
       for (int ct = 0; ct < 2; ct++) f[ct].q = bvalid ? t.c[ct][c] : make_uint4(0, 0, 0, 0);
+    } else if constexpr (FMT == MOE_FMT_FP8_BLOCK128) {
+      const int p = c >> 1;
+      const bool bvalid = !TAIL || st * WK + 32 * h + 16 * p < kvalid;
+#pragma unroll
+      for (int ct = 0; ct < 2; ct++) {
+        const uint4 &cv = t.c[ct][p];
+        fp8x8_to_bf16(((c & 1) ? cv.z : cv.x) & zm[ct], ((c & 1) ? cv.w : cv.y) & zm[ct], f[ct]);
+        if (!bvalid) f[ct].q = make_uint4(0, 0, 0, 0);
+      }
     } else {
       const int p = c >> 2, d = c & 3;
       const bool bvalid = !TAIL || st * WK + 64 * h + 32 * p < kvalid;
@@ -159,7 +197,22 @@ __device__ __forceinline__ void wide_k_loop(WideLDS &lds, rsrc_t ra,
       }
     }
   };
-  auto compute = [&](int st, const BS &t) {
+  // first: the stage starts an fp8 scale block (std::true_type or std::false_type)
+  auto compute = [&](int st, const BS &t, auto first) {
+    if constexpr (FMT == MOE_FMT_FP8_BLOCK128 && decltype(first)::value) {
+#pragma unroll
+      for (int ct = 0; ct < 2; ct++) {
+        const float sn = t.bs[ct];
+        const bool nz = sn != 0.f;
+        const float r = nz ? scur[ct] / sn : 1.f;
+        scur[ct] = nz ? sn : scur[ct];
+        zm[ct] = nz ? ~0u : 0u;
+#pragma unroll
+        for (int mi = 0; mi < 4; mi++)
+#pragma unroll
+          for (int j = 0; j < 16; j++) acc[mi][ct][j] *= r;
+      }
+    }
 #pragma unroll
     for (int c = 0; c < WK / 16; c++) {
       frag8 af[4], bf[2];
@@ -178,19 +231,23 @@ __device__ __forceinline__ void wide_k_loop(WideLDS &lds, rsrc_t ra,
   __syncthreads();
   // Fetches past the last stage reload clamped offsets (unused) and the store after the
   // last stage fills the idle buffer with zeros, so every path keeps the same loads in flight.
-  auto stage = [&](int st, BS &b_cur) {
+  auto stage = [&](int st, BS &b_cur, auto first) {
     fetch_a(st + 1, at);
-    compute(st, b_cur);
+    compute(st, b_cur, first);
     fetch_b(st + 2, b_cur);
     store_a(st + 1, at);
     __syncthreads();
   };
   int st = 0;
   for (; st + 1 < nK; st += 2) {
-    stage(st, bt[0]);
-    stage(st + 1, bt[1]);
+    stage(st, bt[0], std::true_type{});
+    stage(st + 1, bt[1], std::false_type{});
   }
-  if (st < nK) stage(st, bt[0]);
+  if (st < nK) stage(st, bt[0], std::true_type{});
+  if constexpr (FMT == MOE_FMT_FP8_BLOCK128) {
+    post[0] = scur[0];
+    post[1] = scur[1];
+  }
 }
 
 // Grid position -> (row block, column group); false for positions past the row blocks in
@@ -272,14 +329,16 @@ __global__ __launch_bounds__(256, 2) void k_gate_up_wide(GateUpArgs a, int n_rb,
 #pragma unroll
   for (int ct = 0; ct < 2; ct++) {
     const uint32_t row = (uint32_t)((ct == 0 ? 0 : I) + a.lo + cc);
-    cb[ct] = (row & ~15u) * (uint32_t)(FMT == MOE_FMT_BF16 ? 2 * H : H / 2) + (row & 15u) * 16;
-    sb[ct] = (row & ~15u) * (uint32_t)(H / 16) + (row & 15u) * 2;  // NVFP4 scales
+    cb[ct] = (row & ~15u) * (uint32_t)(FMT == MOE_FMT_BF16 ? 2 * H : FMT == MOE_FMT_FP8_BLOCK128 ? H : H / 2) +
+             (row & 15u) * 16;
+    sb[ct] = FMT == MOE_FMT_FP8_BLOCK128 ? row / 128 * (uint32_t)(H / 128) * 4
+                                         : (row & ~15u) * (uint32_t)(H / 16) + (row & 15u) * 2;
   }
-  const float gg = FMT == MOE_FMT_NVFP4 ? glob[(size_t)e * 2 * I + a.lo + cc] : 1.f;
-  const float ug = FMT == MOE_FMT_NVFP4 ? glob[(size_t)e * 2 * I + I + a.lo + cc] : 1.f;
+  float post[2] = {FMT == MOE_FMT_NVFP4 ? glob[(size_t)e * 2 * I + a.lo + cc] : 1.f,
+                   FMT == MOE_FMT_NVFP4 ? glob[(size_t)e * 2 * I + I + a.lo + cc] : 1.f};
   f32x16_t acc[4][2];
   zero_acc(acc);
-  wide_k_loop<FMT, false, false>(lds, ra, a_off, 0, m, cb, sb, 0, H / WK, H, acc);
+  wide_k_loop<FMT, false, false>(lds, ra, a_off, 0, m, cb, sb, 0, H / WK, H, acc, post);
   // h through LDS (the K loop ended with a barrier): each wave's 128 x 32 block, then rows
   // leave as 16-byte chunks (4 lanes per 64-byte row segment)
   uint16_t (*o)[OPITCH] = lds.o[wave];
@@ -287,7 +346,7 @@ __global__ __launch_bounds__(256, 2) void k_gate_up_wide(GateUpArgs a, int n_rb,
   for (int mi = 0; mi < 4; mi++)
 #pragma unroll
     for (int j = 0; j < 16; j++) {
-      const float gv = acc[mi][0][j] * gg, uv = acc[mi][1][j] * ug;
+      const float gv = acc[mi][0][j] * post[0], uv = acc[mi][1][j] * post[1];
       o[32 * mi + d_row(lane, j)][lane & 31] = bf16_bits(gv / (1.f + __expf(-gv)) * uv);
     }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -345,8 +404,10 @@ __global__ __launch_bounds__(256, 2) void k_down_wide(DownArgs a, int n_rb, int 
   for (int ct = 0; ct < 2; ct++) {
     n[ct] = cg * WCOLS + 64 * wave + 32 * ct + (lane & 31);
     const uint32_t row = (uint32_t)(n[ct] < H ? n[ct] : (lane & 31));  // columns past H read row lane%32 (unused)
-    cb[ct] = (row & ~15u) * (uint32_t)(FMT == MOE_FMT_BF16 ? 2 * I : I / 2) + (row & 15u) * 16;
-    sb[ct] = (row & ~15u) * (uint32_t)(I / 16) + (row & 15u) * 2;  // NVFP4 scales
+    cb[ct] = (row & ~15u) * (uint32_t)(FMT == MOE_FMT_BF16 ? 2 * I : FMT == MOE_FMT_FP8_BLOCK128 ? I : I / 2) +
+             (row & 15u) * 16;
+    sb[ct] = FMT == MOE_FMT_FP8_BLOCK128 ? row / 128 * (uint32_t)(I / 128) * 4
+                                         : (row & ~15u) * (uint32_t)(I / 16) + (row & 15u) * 2;
     dg[ct] = FMT == MOE_FMT_NVFP4 ? glob[(size_t)e * H + row] : 1.f;
   }
   if (tid < WM) {  // destination of each pair row, read back in the epilogue
@@ -361,9 +422,9 @@ __global__ __launch_bounds__(256, 2) void k_down_wide(DownArgs a, int n_rb, int 
   f32x16_t acc[4][2];
   zero_acc(acc);
   if (Il % WK == 0)
-    wide_k_loop<FMT, false, true>(lds, ra, a_off, a_stride, m, cb, sb, a.lo, Il / WK, Il, acc);
+    wide_k_loop<FMT, false, true>(lds, ra, a_off, a_stride, m, cb, sb, a.lo, Il / WK, Il, acc, dg);
   else
-    wide_k_loop<FMT, true, true>(lds, ra, a_off, a_stride, m, cb, sb, a.lo, (Il + WK - 1) / WK, Il, acc);
+    wide_k_loop<FMT, true, true>(lds, ra, a_off, a_stride, m, cb, sb, a.lo, (Il + WK - 1) / WK, Il, acc, dg);
   // pair rows through LDS (the K loop ended with a barrier, which also published dst): each
   // wave's 128 x 64 block, then 16-byte chunks (8 lanes per 128-byte row)
   uint16_t (*o)[OPITCH] = lds.o[wave];
@@ -396,6 +457,8 @@ hipError_t launch_gate_up_wide(int fmt, const GateUpArgs &a, int n_shared_tiles,
   const int grid = (n_rb + 7) / 8 * 8 * ncg;
   if (fmt == MOE_FMT_BF16)
     hipLaunchKernelGGL(k_gate_up_wide<MOE_FMT_BF16>, dim3(grid), dim3(256), 0, s, a, n_rb, ncg);
+  else if (fmt == MOE_FMT_FP8_BLOCK128)
+    hipLaunchKernelGGL(k_gate_up_wide<MOE_FMT_FP8_BLOCK128>, dim3(grid), dim3(256), 0, s, a, n_rb, ncg);
   else
     hipLaunchKernelGGL(k_gate_up_wide<MOE_FMT_NVFP4>, dim3(grid), dim3(256), 0, s, a, n_rb, ncg);
   return hipGetLastError();
@@ -406,6 +469,8 @@ hipError_t launch_down_wide(int fmt, const DownArgs &a, int n_shared_tiles, hipS
   const int grid = (n_rb + 7) / 8 * 8 * ncg;
   if (fmt == MOE_FMT_BF16)
     hipLaunchKernelGGL(k_down_wide<MOE_FMT_BF16>, dim3(grid), dim3(256), 0, s, a, n_rb, ncg);
+  else if (fmt == MOE_FMT_FP8_BLOCK128)
+    hipLaunchKernelGGL(k_down_wide<MOE_FMT_FP8_BLOCK128>, dim3(grid), dim3(256), 0, s, a, n_rb, ncg);
   else
     hipLaunchKernelGGL(k_down_wide<MOE_FMT_NVFP4>, dim3(grid), dim3(256), 0, s, a, n_rb, ncg);
   return hipGetLastError();

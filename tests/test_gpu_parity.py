@@ -348,15 +348,20 @@ def test_tiled_kernels_match_oracle(cid, T, sl):
     check_close(f"tiled cfg{cid} T={T} [{lo},{hi})", _forward_gpu(inp, r["ids"], r["w"], lo, hi, bm=128), ref)
 
 
-@pytest.mark.parametrize("H,I,sl,T,bm", [(384, 224, (0, 224), 300, 128), (384, 224, (32, 160), 257, 256),
-                                          (256, 128, (0, 128), 1, 128), (640, 96, (0, 96), 700, 128)])
-def test_wide_kernels_ragged_shapes(H, I, sl, T, bm):
-    """NVFP4 prefill GEMMs on shapes that leave partial work everywhere: a last down column group
+@pytest.mark.parametrize("fmt,H,I,sl,T,bm", [
+    ("nvfp4", 384, 224, (0, 224), 300, 128), ("nvfp4", 384, 224, (32, 160), 257, 256),
+    ("nvfp4", 256, 128, (0, 128), 1, 128), ("nvfp4", 640, 96, (0, 96), 700, 128),
+    ("fp8blk", 384, 256, (0, 256), 300, 128), ("fp8blk", 640, 384, (128, 384), 257, 256),
+    ("fp8blk", 256, 128, (0, 128), 1, 128),
+    ("bf16", 384, 224, (32, 160), 257, 256), ("bf16", 640, 96, (0, 96), 700, 128)])
+def test_wide_kernels_ragged_shapes(fmt, H, I, sl, T, bm):
+    """Prefill GEMMs on shapes that leave partial work everywhere: a last down column group
     half past H (H = 384, 640), a last gate_up column group partly past the slice and a down K
     tail (slice widths 224, 128 and 96 are not multiples of 128), shared-expert rows ending inside a
-    32-row tile, align blocks of 256 rows, and a single token."""
+    32-row tile, align blocks of 256 rows, and a single token.  fp8-block slices are multiples of
+    the 128-wide scale block."""
     E, k, seed = 6, 2, 23
-    b, sh = S.routed_bank(seed, "nvfp4", E, H, I), S.shared_bank(seed, "nvfp4", H, I)
+    b, sh = S.routed_bank(seed, fmt, E, H, I), S.shared_bank(seed, fmt, H, I)
     x = S.tokens(seed, T, H)
     _, ids, w, _ = O.route(x, S.router_weight(seed, E, H), None, k, True)
     lo, hi = sl
@@ -364,7 +369,35 @@ def test_wide_kernels_ragged_shapes(H, I, sl, T, bm):
     al = qm.moe_align(to_dev(ids.astype(np.int32)), E, bm)
     got = qm.moe_expert_forward(device_bank(b), device_bank(sh), bf16_dev(x), to_dev(w.astype(np.float32)), al,
                                 lo, hi).float().cpu().numpy()
-    check_close(f"wide H={H} I={I} [{lo},{hi}) T={T} bm={bm}", got, ref)
+    check_close(f"wide {fmt} H={H} I={I} [{lo},{hi}) T={T} bm={bm}", got, ref)
+
+
+@pytest.mark.parametrize("sl", [(0, 384), (128, 384)])
+def test_fp8_prefill_zero_block_scales(sl):
+    """fp8-block scales of 0 (an all-zero weight block) with nonzero codes: the block adds
+    nothing.  Zeros sit at the first K block of a tile, inside a tile's K run, over a whole
+    tile row of blocks (its gate output is 0) and in the shared expert; the prefill kernels keep
+    each tile's accumulators in units of its current block scale, so every one of these is a
+    separate path."""
+    E, H, I, T, k, seed = 4, 512, 384, 300, 2, 31
+    b, sh = S.routed_bank(seed, "fp8blk", E, H, I), S.shared_bank(seed, "fp8blk", H, I)
+    b.gate_up_scale[:, 0, 0] = 0            # gate rows [0,128): first K block
+    b.gate_up_scale[1:, 4, 2] = 0           # up rows [I+128, I+256): a middle K block
+    b.gate_up_scale[2, 1, :] = 0            # expert 2, gate rows [128,256): every K block
+    b.gate_up_scale[3, 3, 0:2] = 0          # expert 3, up rows [I, I+128): two leading blocks
+    b.down_scale[:, 1, 1] = 0               # down rows [128,256), K block 1
+    b.down_scale[0, 2, 0] = 0               # expert 0, down rows [256,384), first K block
+    sh.gate_up_scale[0, 0, 3] = 0           # shared expert, gate rows [0,128), last K block
+    sh.down_scale[0, 0, :] = 0              # shared expert, down rows [0,128): every K block
+    x = S.tokens(seed, T, H)
+    _, ids, w, _ = O.route(x, S.router_weight(seed, E, H), None, k, True)
+    lo, hi = sl
+    ref = O.expert_forward(b, sh, x, ids, w, lo, hi)
+    al = qm.moe_align(to_dev(ids.astype(np.int32)), E, 128)
+    got = qm.moe_expert_forward(device_bank(b), device_bank(sh), bf16_dev(x), to_dev(w.astype(np.float32)), al,
+                                lo, hi).float().cpu().numpy()
+    check_close(f"fp8 zero block scales [{lo},{hi})", got, ref)
+    assert np.isfinite(got).all()
 
 
 @pytest.mark.parametrize("cid,T,sl,bm", [(3, 8192, (0, 512), 128), (3, 8192, (0, 256), 128),
