@@ -253,11 +253,11 @@ size_t moe_workspace_bytes(const moe_bank *routed, const moe_bank *shared, int T
  *   out         [T, H] f32 (out_dtype MOE_OUT_F32) or bf16 (MOE_OUT_BF16), overwritten.
  *   workspace   >= moe_workspace_bytes(...) bytes of device memory.
  * Experts that received no tokens are never read.  The align block size picks the kernels:
- * al->block_m a multiple of 128 runs NVFP4, FP8_BLOCK128 and BF16 on tiled GEMMs that reuse
+ * al->block_m a multiple of 128 runs NVFP4, FP8_BLOCK128 and BF16 on prefill GEMMs that reuse
  * each weight across 128 pair rows (for many tokens per expert); other block sizes,
  * and MXFP4 and Q4_0, run the streaming kernels that read each selected weight byte once per
  * 16-row block (for few tokens per expert).  Both compute the same result, except that the
- * tiled kernels round each pair row y to bf16 before the fp32 weighted sum (the pair rows
+ * prefill GEMMs round each pair row y to bf16 before the fp32 weighted sum (the pair rows
  * are the layer's largest stream at many tokens; the streaming kernels keep them in fp32). */
 int moe_expert_forward(const moe_bank *routed, const moe_bank *shared, const void *x_bf16,
                        int T, int k, const float *topk_w, const moe_align_out *al,

@@ -240,7 +240,7 @@ def moe_expert_down(routed: DeviceBank, shared: DeviceBank | None, topk_w: torch
 
 def choose_block_m(T: int, k: int, E: int, fmt: str | None = None) -> int:
     """Rows per aligned block: 16 while experts see few tokens each, larger as the mean
-    number of pairs per expert grows; 128 (the tiled prefill GEMMs) once experts see enough
+    number of pairs per expert grows; 128 (the prefill GEMMs) once experts see enough
     tokens to reuse each weight tile, for the formats those kernels cover."""
     mean = T * k / max(E, 1)
     if mean >= 32 and fmt in ("nvfp4", "fp8blk", "bf16"):

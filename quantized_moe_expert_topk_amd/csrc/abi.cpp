@@ -191,7 +191,7 @@ int check_align_out(const moe_align_out *al, int T, int k, int E) {
 
 struct FwdPlan {
   int Il, n_routed_sub, n_shared_sub, n_shared_tiles, shared_rows, h_rows, P, Psh;
-  bool tiled;  // 128-row align blocks (NVFP4, FP8_BLOCK128, BF16): the tiled prefill kernels
+  bool tiled;  // 128-row align blocks (NVFP4, FP8_BLOCK128, BF16): the prefill GEMMs
   // workspace layout: [h][x planes (MXFP4)][Y]; MXFP4 h is [hq][hs], x is [xq][xs]
   size_t hs_off, xq_off, xs_off, y_off, y_bytes, total;
 };
@@ -338,7 +338,7 @@ int run_gate_up(const moe_bank *routed, const moe_bank *shared, const void *x, i
                               "activation split launch");
     if (rc) return rc;
   }
-  if (p.tiled) return hip_status(qmoe::launch_gate_up_tiled(routed->fmt, a, p.n_shared_tiles, s), "gate_up launch");
+  if (p.tiled) return hip_status(qmoe::launch_gate_up_wide(routed->fmt, a, p.n_shared_tiles, s), "gate_up launch");
   return hip_status(qmoe::launch_gate_up(routed->fmt, a, p.n_shared_sub, s), "gate_up launch");
 }
 
@@ -346,7 +346,7 @@ int run_down(const moe_bank *routed, const moe_bank *shared, int T, int k, const
              const moe_align_out *al, int lo, const FwdPlan &p, void *out, int out_dtype, void *workspace,
              hipStream_t s) {
   qmoe::DownArgs a = down_args(routed, shared, T, k, al, lo, p, workspace);
-  int rc = p.tiled ? hip_status(qmoe::launch_down_tiled(routed->fmt, a, p.n_shared_tiles, s), "down launch")
+  int rc = p.tiled ? hip_status(qmoe::launch_down_wide(routed->fmt, a, p.n_shared_tiles, s), "down launch")
                    : hip_status(qmoe::launch_down(routed->fmt, a, p.n_shared_sub, s), "down launch");
   if (rc) return rc;
   return hip_status(qmoe::launch_combine(a.Y, p.tiled, topk_w, T, k, routed->H, shared != nullptr, out,

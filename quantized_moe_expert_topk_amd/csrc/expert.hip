@@ -804,7 +804,7 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
 // ---------------------------------------------------------------------------- combine
 
 // out[t] = sum_j w[t*k + j] Y[t*k + j] + Y[T*k + t] (shared, weight 1), in this order, in
-// fp32.  Y rows are fp32 (streaming kernels) or bf16 (tiled kernels); a thread owns 4
+// fp32.  Y rows are fp32 (streaming kernels) or bf16 (prefill GEMMs); a thread owns 4
 // consecutive columns (H % 128 == 0).
 template <bool YBF16>
 __global__ __launch_bounds__(256) void k_combine(const void *__restrict__ Yv, const float *__restrict__ w, int T,

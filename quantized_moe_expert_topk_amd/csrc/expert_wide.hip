@@ -1,7 +1,7 @@
 // expert_wide.hip -- NVFP4, fp8-block and bf16 expert GEMMs for many tokens per expert
 // (prefill), gfx950.
 //
-// Same computation as expert.hip and expert_tiled.hip (gate rows [lo,hi), up rows
+// Same computation as the streaming kernels of expert.hip (gate rows [lo,hi), up rows
 // [I+lo, I+hi), down columns [lo,hi) of one rank's slice: FreeToken issue #62 "What it
 // touches" item 1; SwiGLU expert linear in the intermediate index: issue #520 section 4;
 // NVFP4 W4A16 with the e4m3 group scale exact in bf16 and the per-row fp32 global applied
@@ -459,8 +459,10 @@ hipError_t launch_gate_up_wide(int fmt, const GateUpArgs &a, int n_shared_tiles,
     hipLaunchKernelGGL(k_gate_up_wide<MOE_FMT_BF16>, dim3(grid), dim3(256), 0, s, a, n_rb, ncg);
   else if (fmt == MOE_FMT_FP8_BLOCK128)
     hipLaunchKernelGGL(k_gate_up_wide<MOE_FMT_FP8_BLOCK128>, dim3(grid), dim3(256), 0, s, a, n_rb, ncg);
-  else
+  else if (fmt == MOE_FMT_NVFP4)
     hipLaunchKernelGGL(k_gate_up_wide<MOE_FMT_NVFP4>, dim3(grid), dim3(256), 0, s, a, n_rb, ncg);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -471,8 +473,10 @@ hipError_t launch_down_wide(int fmt, const DownArgs &a, int n_shared_tiles, hipS
     hipLaunchKernelGGL(k_down_wide<MOE_FMT_BF16>, dim3(grid), dim3(256), 0, s, a, n_rb, ncg);
   else if (fmt == MOE_FMT_FP8_BLOCK128)
     hipLaunchKernelGGL(k_down_wide<MOE_FMT_FP8_BLOCK128>, dim3(grid), dim3(256), 0, s, a, n_rb, ncg);
-  else
+  else if (fmt == MOE_FMT_NVFP4)
     hipLaunchKernelGGL(k_down_wide<MOE_FMT_NVFP4>, dim3(grid), dim3(256), 0, s, a, n_rb, ncg);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -41,7 +41,7 @@ struct DownArgs {
   const int32_t *sorted_ids, *block_expert, *total_padded;
   int block_m, cap, n_routed_sub;
   int lo, Il;
-  float *Y;  // [T * k + T_shared, H] unweighted pair rows: fp32 (streaming kernels) or bf16 (tiled kernels)
+  float *Y;  // [T * k + T_shared, H] unweighted pair rows: fp32 (streaming kernels) or bf16 (prefill GEMMs)
 };
 
 int router_ksplit(int T, int E, int H);
@@ -58,12 +58,9 @@ hipError_t launch_align(const int32_t *ids, int T, int k, int E, int BM, int cap
                         int32_t *hist, hipStream_t s);
 hipError_t launch_gate_up(int fmt, const GateUpArgs &a, int n_shared_sub, hipStream_t s);
 hipError_t launch_down(int fmt, const DownArgs &a, int n_shared_sub, hipStream_t s);
-// Tiled kernels for align blocks of 128 rows (NVFP4, FP8_BLOCK128, BF16); the shared expert's
-// rows are ceil(T/128) tiles after the routed ones.
-hipError_t launch_gate_up_tiled(int fmt, const GateUpArgs &a, int n_shared_tiles, hipStream_t s);
-hipError_t launch_down_tiled(int fmt, const DownArgs &a, int n_shared_tiles, hipStream_t s);
-// NVFP4 and bf16 prefill GEMMs with only the activation tile in LDS (128 pair rows x 256
-// weight rows per workgroup); same grid rows and outputs as the tiled kernels.
+// Prefill GEMMs for align blocks of 128 rows (NVFP4, FP8_BLOCK128, BF16) with only the
+// activation tile in LDS (128 pair rows x 256 weight rows per workgroup); the shared expert's
+// rows are ceil(T/128) row blocks after the routed ones.
 hipError_t launch_gate_up_wide(int fmt, const GateUpArgs &a, int n_shared_tiles, hipStream_t s);
 hipError_t launch_down_wide(int fmt, const DownArgs &a, int n_shared_tiles, hipStream_t s);
 // moe_pack_bank: [rows, pitch] bytes -> 16-row tiles stored piece-major in units of `unit`
@@ -76,7 +73,7 @@ hipError_t launch_pack_tile16_t(const void *src, void *dst, size_t E, size_t N, 
 // Q4_0 codes [rows, pitch] -> the tile-16 piece order with the nibbles regrouped per piece.
 hipError_t launch_pack_q4_0(const void *src, void *dst, size_t rows, uint32_t pitch, hipStream_t s);
 hipError_t launch_act_mx8(const uint16_t *x, int rows, int K, uint8_t *q, uint8_t *sc, hipStream_t s);
-// Y rows (unweighted) in fp32 (streaming kernels) or bf16 (tiled kernels); the combine applies
+// Y rows (unweighted) in fp32 (streaming kernels) or bf16 (prefill GEMMs); the combine applies
 // the routing weights topk_w [T * k].
 hipError_t launch_combine(const void *Y, bool y_bf16, const float *topk_w, int T, int k, int H, int has_shared,
                           void *out, int out_bf16, hipStream_t s);

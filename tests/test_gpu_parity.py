@@ -340,7 +340,7 @@ TILED_CASES = [(1, 16, (0, 128)), (1, 16, (32, 96)), (2, 64, (0, 256)), (2, 32, 
 
 @pytest.mark.parametrize("cid,T,sl", TILED_CASES)
 def test_tiled_kernels_match_oracle(cid, T, sl):
-    """128-row align blocks select the LDS-tiled GEMMs (NVFP4, fp8-block, bf16); small cases
+    """128-row align blocks select the prefill GEMMs (NVFP4, fp8-block, bf16); small cases
     cover partial column tiles and a 32-wide K tail."""
     inp, r = inputs_for(cid, T)
     lo, hi = sl
