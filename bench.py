@@ -9,7 +9,11 @@ Default workload: the Qwen3.6-35B-A3B-shaped NVFP4 decode layer (H=2048, 256 exp
 I=512, shared expert I=512) on one rank's slice I_local=256, T=64 tokens; the other decode
 batch sizes and the full-I layer are reported under "points".  ``--config`` picks another
 workload (3: prefill T=8192 with Zipf routing, 4: fp8-block, 5: DeepSeek-V4-Flash-shaped
-MXFP4).  Prints ONE JSON line.
+MXFP4, 6: bf16 experts, 7: q4_0).  Prints ONE JSON line.
+
+Besides the mean over the K timed steps, each point reports the spread of the step time
+(p10 / p50 / p90 over separately timed rotations), and the line reports the bandwidth of a
+plain 1 GiB device copy measured on the same GPU, beside the fractions of the 8 TB/s peak.
 """
 from __future__ import annotations
 
@@ -28,6 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s at 1 GPU; decode HBM GB/s %peak; prefill MFMA %peak"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0}
+RIDGE_FLOP_PER_BYTE = MFMA_PEAK_TFLOPS["bf16"] * 1e12 / (HBM_PEAK_GBS * 1e9)
 KERNEL_SOURCES = ("expert.hip", "device_common.h")
 
 # (config id) -> (T of the headline point, slice of the headline point, other (T, slice) points)
@@ -212,6 +217,14 @@ def run(args):
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / args.steps
+        # spread: rotations timed one by one (events between whole-rotation replays)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.spread_rotations + 1)]
+        ev[0].record()
+        for i in range(args.spread_rotations):
+            g_all.replay()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        per_step = np.array([ev[i].elapsed_time(ev[i + 1]) / n for i in range(args.spread_rotations)])
         avg_bytes = sum(bytes_step[i % n] for i in range(args.steps)) / args.steps
         avg_flops = sum(flops_step[i % n] for i in range(args.steps)) / args.steps
         # dominant kernel: gate_up (+SwiGLU), launched back to back from one captured graph
@@ -230,6 +243,7 @@ def run(args):
         k_ms = e0.elapsed_time(e1) / reps
         k_bytes = sum(gu_bytes[i % n] for i in range(reps)) / reps
         pt = dict(T=T, slice=[lo, hi], ms_per_step=ms, tokens_per_s=T / (ms * 1e-3),
+                  ms_per_step_p10_p50_p90=[float(np.percentile(per_step, q)) for q in (10, 50, 90)],
                   layer_hbm_gbs=avg_bytes / (ms * 1e-3) / 1e9, layer_hbm_frac=avg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                   layer_tflops=avg_flops / (ms * 1e-3) / 1e12,
                   layer_mfma_frac=avg_flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"],
@@ -241,6 +255,29 @@ def run(args):
         del layers, graphs, gk, g_all
         torch.cuda.synchronize()
     return cfg, results
+
+
+def copy_bandwidth_gbs(mib=1024, reps=5):
+    """Bytes read + written per second by a plain device copy of `mib` MiB (torch copy_),
+    the best of `reps` timed launches: a STREAM-style reference for the HBM fractions."""
+    import torch
+    n = (mib << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3
+        best = t if best is None else min(best, t)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n * 4 / best / 1e9
 
 
 def copy_calibration(mib):
@@ -266,6 +303,8 @@ def main():
     ap.add_argument("--slice", type=str, default="")
     ap.add_argument("--instances", type=int, default=0)
     ap.add_argument("--no-points", action="store_true", help="only the headline point")
+    ap.add_argument("--spread-rotations", type=int, default=20,
+                    help="rotations timed one by one after the timed steps, for the p10/p50/p90 step time")
     ap.add_argument("--storage", choices=("own", "full"), default="full",
                     help="weights of a slice: the rank's own slice storage, or the full bank")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
@@ -281,15 +320,19 @@ def main():
         print("bench.py measures one GPU: the layer runs on one rank's intermediate slice, and the cross-rank "
               "all-reduce of the partials is not implemented. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    copy_gbs = copy_bandwidth_gbs()
     cfg, results = run(args)
+    for pt in results:
+        pt["layer_hbm_frac_of_copy"] = pt["layer_hbm_gbs"] / copy_gbs
     head = results[0]
     workload = f"{cfg.name}; T={head['T']}; slice [{head['slice'][0]},{head['slice'][1]})"
-    bound = "mfma" if cfg.cid == 3 else "hbm"
+    # the head point's arithmetic intensity against the ridge of the bf16 MFMA and HBM peaks
+    bound = "mfma" if head["alg_flops_per_step"] / head["alg_bytes_per_step"] > RIDGE_FLOP_PER_BYTE else "hbm"
     if bound == "hbm":
         roof = dict(bound="hbm", achieved=head["gate_up_gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=head["gate_up_gbs"] / HBM_PEAK_GBS)
+                    frac=head["gate_up_gbs"] / HBM_PEAK_GBS, frac_of_measured_copy=head["gate_up_gbs"] / copy_gbs)
     else:
-        tf = 2 * (head["T"] * cfg.k + head["T"]) * 2 * (head["slice"][1] - head["slice"][0]) * cfg.H
+        tf = 2 * (head["T"] * cfg.k + (head["T"] if cfg.shared else 0)) * 2 * (head["slice"][1] - head["slice"][0]) * cfg.H
         ach = tf / (head["gate_up_us"] * 1e-6) / 1e12
         roof = dict(bound="mfma", achieved=ach, peak=MFMA_PEAK_TFLOPS["bf16"], unit="TFLOP/s",
                     frac=ach / MFMA_PEAK_TFLOPS["bf16"])
@@ -304,6 +347,7 @@ def main():
                    args.instances or INSTANCES[cfg.cid], "batches_rotated": BATCHES,
                    "weight_storage": "rank's own slice" if args.storage == "own" else "full bank, sliced"},
         "layer_hbm_frac": head["layer_hbm_frac"], "layer_mfma_frac": head["layer_mfma_frac"],
+        "ms_per_step_p10_p50_p90": head["ms_per_step_p10_p50_p90"], "hbm_copy_gbs": copy_gbs,
         "roofline": roof, "points": results,
     }
     if not args.no_cpu_baseline:
