@@ -117,7 +117,21 @@ def cpu_baseline(cfg, T, lo, hi, budget_s):
         batches += 1
     return dict(value=done_tokens / t_used, unit="tokens/s", cores=O.num_threads(), kind="oracle",
                 sample=f"{batches} batch(es) of T={T} tokens, whole layer (route + expert forward), "
-                       f"slice [{lo},{hi}), {t_used:.1f} s of timed oracle work")
+                       f"slice [{lo},{hi}), {t_used:.1f} s of timed oracle work", cpu=host_cpu())
+
+
+def host_cpu():
+    """The host CPU's model name and its logical CPU count (Linux /proc/cpuinfo)."""
+    model, n = "unknown", 0
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    n += 1
+                    model = ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return f"{model}, {n} logical CPUs"
 
 
 def run(args):
