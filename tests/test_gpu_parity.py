@@ -372,6 +372,42 @@ def test_wide_kernels_ragged_shapes(fmt, H, I, sl, T, bm):
     check_close(f"wide {fmt} H={H} I={I} [{lo},{hi}) T={T} bm={bm}", got, ref)
 
 
+def _random_case(seed):
+    """A seeded draw of format, shapes, slice, routing width, token count, align block size and
+    shared expert, inside the constraints the ABI states for each format."""
+    rng = np.random.default_rng(1000 + seed)
+    fmt = S.FORMATS[seed % len(S.FORMATS)]
+    unit = {"nvfp4": 32, "fp8blk": 128, "mxfp4": 32, "bf16": 32, "q4_0": 128}[fmt]
+    E = int(rng.integers(2, 17))
+    H = 128 * int(rng.integers(1, 7))
+    I = unit * int(rng.integers(1, max(2, 768 // unit) + 1))
+    a, b = sorted(rng.choice(I // unit + 1, 2, replace=False))
+    lo, hi = unit * int(a), unit * int(b)
+    k = int(rng.integers(1, min(E, 8) + 1))
+    T = int(rng.choice([0, 1, 2, 7, 16, 33, 64, 129, 300]))
+    bm = int(rng.choice([16, 32, 64, 128]))
+    shared = bool(rng.integers(0, 2))
+    return fmt, E, H, I, lo, hi, k, T, bm, shared
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_random_shapes_match_oracle(seed):
+    """Seeded random layers over every format: the forward pass on the GPU against the oracle
+    (the streaming kernels for align blocks below 128 and for MXFP4 / Q4_0, the prefill GEMMs
+    otherwise), including T = 0, single tokens, slices anywhere in [0, I) and odd expert counts."""
+    fmt, E, H, I, lo, hi, k, T, bm, shared = _random_case(seed)
+    b = S.routed_bank(seed, fmt, E, H, I)
+    sh = S.shared_bank(seed, fmt, H, I) if shared else None
+    x = S.tokens(seed, T, H)
+    _, ids, w, _ = O.route(x, S.router_weight(seed, E, H), None, k, True)
+    ref = O.expert_forward(b, sh, x, ids, w, lo, hi)
+    al = qm.moe_align(to_dev(ids.astype(np.int32).reshape(T, k)), E, bm)
+    got = qm.moe_expert_forward(device_bank(b), device_bank(sh) if sh is not None else None, bf16_dev(x),
+                                to_dev(w.astype(np.float32).reshape(T, k)), al, lo, hi).float().cpu().numpy()
+    assert got.shape == (T, H)
+    check_close(f"random {fmt} E={E} H={H} I={I} [{lo},{hi}) k={k} T={T} bm={bm} shared={shared}", got, ref)
+
+
 @pytest.mark.parametrize("sl", [(0, 384), (128, 384)])
 def test_fp8_prefill_zero_block_scales(sl):
     """fp8-block scales of 0 (an all-zero weight block) with nonzero codes: the block adds
