@@ -146,6 +146,39 @@ def test_align_is_bit_exact(T, k, E, bm, kind):
         np.testing.assert_array_equal(again[key], got[key], err_msg=key)
 
 
+@pytest.mark.parametrize("seed", range(24))
+def test_random_route_then_align(seed):
+    """Seeded random routing problems (expert counts 1..1000, k up to 64, hidden sizes up to
+    2048, small and tiled-router batch sizes, with and without bias and renormalisation): the
+    GPU top-k against the oracle's (bit for bit away from near-ties), then the GPU alignment of
+    the GPU's picks against the oracle's alignment of the same picks, at a random block size."""
+    rng = np.random.default_rng(2000 + seed)
+    E = int(rng.choice([1, 2, 3, 7, 8, 64, 100, 256, 513, 1000]))
+    k = int(rng.integers(1, min(E, 64) + 1)) if rng.random() < 0.2 else int(rng.integers(1, min(E, 8) + 1))
+    H = 128 * int(rng.integers(1, 17))
+    T = int(rng.choice([1, 5, 16, 17, 64, 300, 1024, 1500]))
+    with_bias, renorm = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+    bm = 16 * int(rng.integers(1, 17))
+    x, wr = S.tokens(seed, T, H), S.router_weight(seed, E, H)
+    bias = S.zipf_bias(seed, E, 1.1) if with_bias else None
+    name = f"E={E} k={k} H={H} T={T} bias={with_bias} renorm={renorm} bm={bm}"
+    lg_ref, ids_ref, w_ref, gap = O.route(x, wr, bias, k, renorm)
+    lg, ids, w = qm.moe_route(bf16_dev(x), bf16_dev(wr), to_dev(bias), k, renorm)
+    lerr = np.abs(lg.cpu().numpy() - lg_ref).max()
+    assert lerr <= 5e-6, (name, lerr)
+    sure = gap > NEAR_TIE
+    ids_g = ids.cpu().numpy()
+    np.testing.assert_array_equal(ids_g[sure], ids_ref[sure], err_msg=name)
+    assert np.abs(w.cpu().numpy()[sure] - w_ref[sure]).max() <= 1e-5, name
+    for t in np.nonzero(~sure)[0]:
+        kth = np.sort(lg_ref[t])[::-1][k - 1]
+        assert (lg_ref[t][ids_g[t]] >= kth - 2 * NEAR_TIE).all(), name
+    ref = O.align(ids_g, E, bm)
+    got = align_np(qm.moe_align(ids, E, bm))
+    for key in ref:
+        np.testing.assert_array_equal(got[key], ref[key], err_msg=f"{name} {key}")
+
+
 # ----------------------------------------------------------------------------- expert layer
 
 # ----------------------------------------------------------------------------- weight layout
