@@ -33,7 +33,10 @@ METRIC = "MoE-layer tokens/s at 1 GPU; decode HBM GB/s %peak; prefill MFMA %peak
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0}
 RIDGE_FLOP_PER_BYTE = MFMA_PEAK_TFLOPS["bf16"] * 1e12 / (HBM_PEAK_GBS * 1e9)
-KERNEL_SOURCES = ("expert.hip", "device_common.h")
+# the sources each gate_up kernel is built from (counter summaries are keyed on their hash)
+KERNEL_SOURCES = {"k_gate_up": ("expert.hip", "device_common.h"),
+                  "k_gate_up_wide": ("expert_wide.hip", "device_common.h")}
+WIDE_FORMATS = ("nvfp4", "fp8blk", "bf16")  # formats whose 128-row align blocks run the wide GEMMs
 
 # (config id) -> (T of the headline point, slice of the headline point, other (T, slice) points)
 WORKLOADS = {
@@ -77,9 +80,9 @@ def gate_up_slice_bytes(fmt, H, Il):
     return 2 * Il * H * 17 // 32
 
 
-def kernel_source_hash():
+def kernel_source_hash(kernel_name="k_gate_up"):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kernel_name]:
         h.update(open(os.path.join(ROOT, "quantized_moe_expert_topk_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -93,7 +96,7 @@ def load_traffic(kernel_name, workload):
     try:
         d = json.load(open(p))
         e = d.get(f"{kernel_name}|{workload}")
-        if e and e.get("source_hash") == kernel_source_hash():
+        if e and e.get("source_hash") == kernel_source_hash(kernel_name):
             return e.get("bytes_per_launch")
     except (ValueError, OSError):
         pass
@@ -256,7 +259,7 @@ def run(args):
         torch.cuda.synchronize()
         k_ms = e0.elapsed_time(e1) / reps
         k_bytes = sum(gu_bytes[i % n] for i in range(reps)) / reps
-        pt = dict(T=T, slice=[lo, hi], ms_per_step=ms, tokens_per_s=T / (ms * 1e-3),
+        pt = dict(T=T, slice=[lo, hi], ms_per_step=ms, tokens_per_s=T / (ms * 1e-3), block_m=layers[0][0].block_m,
                   ms_per_step_p10_p50_p90=[float(np.percentile(per_step, q)) for q in (10, 50, 90)],
                   layer_hbm_gbs=avg_bytes / (ms * 1e-3) / 1e9, layer_hbm_frac=avg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                   layer_tflops=avg_flops / (ms * 1e-3) / 1e12,
@@ -350,8 +353,9 @@ def main():
         ach = tf / (head["gate_up_us"] * 1e-6) / 1e12
         roof = dict(bound="mfma", achieved=ach, peak=MFMA_PEAK_TFLOPS["bf16"], unit="TFLOP/s",
                     frac=ach / MFMA_PEAK_TFLOPS["bf16"])
-    roof["kernel"] = "k_gate_up (gate_up grouped GEMM + SwiGLU)"
-    roof["traffic"] = load_traffic("k_gate_up", f"cfg{cfg.cid}_T{head['T']}_slice{head['slice'][1] - head['slice'][0]}")
+    gk = "k_gate_up_wide" if head["block_m"] == 128 and cfg.fmt in WIDE_FORMATS else "k_gate_up"
+    roof["kernel"] = f"{gk} (gate_up grouped GEMM + SwiGLU)"
+    roof["traffic"] = load_traffic(gk, f"cfg{cfg.cid}_T{head['T']}_slice{head['slice'][1] - head['slice'][0]}")
     line = {
         "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
