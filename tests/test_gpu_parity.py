@@ -571,13 +571,18 @@ def test_zero_tokens_is_a_no_op():
     assert i2.shape == (0, 2)
 
 
-def test_graph_replays_match_eager():
-    """The three calls captured in a HIP graph: every replay (with eager work and
-    synchronisations in between) reproduces the eager result bit for bit."""
-    inp, r = inputs_for(2, 32)
+@pytest.mark.parametrize("cid,T,bm", [(2, 32, None), (3, 8192, 128), (4, 64, 128), (5, 16, None), (6, 64, 128),
+                                       (7, 16, None)])
+def test_graph_replays_match_eager(cid, T, bm):
+    """The three calls captured in a HIP graph, for every format and both kernel families
+    (streaming, and the prefill GEMMs at align blocks of 128): every replay (with eager work
+    and synchronisations in between) reproduces the eager result bit for bit."""
+    inp, r = inputs_for(cid, T)
     cfg = inp.cfg
     rb, sb = dev_banks(inp)
-    layer = qm.MoeLayer(rb, sb, bf16_dev(inp.router), None, 32, cfg.k, 0, 256)
+    bias = to_dev(inp.bias) if inp.bias is not None else None
+    half = cfg.I // 2
+    layer = qm.MoeLayer(rb, sb, bf16_dev(inp.router), bias, T, cfg.k, 0, half, cfg.renormalize, block_m=bm)
     x = bf16_dev(inp.x)
     eager = layer(x).clone()
     ids_eager = layer.ids.clone()
@@ -585,7 +590,7 @@ def test_graph_replays_match_eager():
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         layer(x)
-    other = qm.MoeLayer(rb, sb, bf16_dev(inp.router), None, 32, cfg.k, 256, 512)
+    other = qm.MoeLayer(rb, sb, bf16_dev(inp.router), bias, T, cfg.k, half, cfg.I, cfg.renormalize, block_m=bm)
     for _ in range(3):
         layer.out.zero_()
         layer.ids.fill_(-1)
