@@ -211,6 +211,22 @@ size_t moe_align_workspace_bytes(int T, int k, int E);
 int moe_align(const int32_t *topk_ids, int T, int k, int E, const moe_align_out *out,
               void *workspace, size_t workspace_bytes, void *stream);
 
+/* moe_route_align -- moe_route followed by moe_align on its topk_ids, in one call, for the
+ * decode step: same arguments, outputs and requirements as the two calls (the route
+ * arguments, then the align descriptor *out, whose every array is fully written), and
+ * results identical to them bit for bit.  For 1 <= T <= 16, E <= 512 and T*k <= 1024 the
+ * top-k selection and the counting sort run in one workgroup with the picks kept on chip
+ * (one kernel launch fewer than the two calls); otherwise it enqueues exactly what the two
+ * calls enqueue.
+ *   workspace  >= moe_route_align_workspace_bytes(T, H, E, k) bytes: the router's split-K
+ *              partials, then, 256-byte aligned, the alignment histograms.
+ * T == 0 enqueues nothing (as moe_route and moe_align). */
+size_t moe_route_align_workspace_bytes(int T, int H, int E, int k);
+int moe_route_align(const void *x_bf16, int T, int H, const void *w_router_bf16, int E,
+                    const float *bias, int k, int renormalize, float *logits, int32_t *topk_ids,
+                    float *topk_w, const moe_align_out *out, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
 /* ------------------------------------------------------------------ expert layer */
 
 /* Device workspace moe_expert_forward needs for (routed, shared, T, k, block_m, slice):

@@ -21,6 +21,7 @@ MOE_LAYOUT_ROWS, MOE_LAYOUT_TILE16, MOE_LAYOUT_MXFP4_T = 0, 1, 2
 
 # every entry point include/qmoe.h declares
 EXPORTS = ("moe_route", "moe_route_workspace_bytes", "moe_route_from_logits", "moe_align_capacity", "moe_align_workspace_bytes", "moe_align",
+           "moe_route_align_workspace_bytes", "moe_route_align",
            "moe_workspace_bytes", "moe_pack_bank", "moe_expert_forward", "moe_expert_gate_up", "moe_expert_down",
            "moe_status_string", "moe_last_error")
 
@@ -69,6 +70,9 @@ def lib() -> ctypes.CDLL:
         L.moe_align_workspace_bytes.argtypes = [i32, i32, i32]
         L.moe_align_workspace_bytes.restype = sz
         L.moe_align.argtypes = [vp, i32, i32, i32, pa, vp, sz, vp]
+        L.moe_route_align_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        L.moe_route_align_workspace_bytes.restype = sz
+        L.moe_route_align.argtypes = [vp, i32, i32, vp, i32, vp, i32, i32, vp, vp, vp, pa, vp, sz, vp]
         L.moe_workspace_bytes.argtypes = [pb, pb, i32, i32, i32, i32, i32]
         L.moe_workspace_bytes.restype = sz
         L.moe_pack_bank.argtypes = [pb, pb, vp]

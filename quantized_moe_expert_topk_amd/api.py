@@ -181,6 +181,40 @@ def moe_align(topk_ids: torch.Tensor, E: int, block_m: int, out: AlignOut | None
     return out
 
 
+def moe_route_align_workspace_bytes(T: int, H: int, E: int, k: int) -> int:
+    return int(lib().moe_route_align_workspace_bytes(T, H, E, k))
+
+
+def moe_route_align(x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor | None, k: int, block_m: int,
+                    renormalize: bool = True, logits=None, topk_ids=None, topk_w=None, out: AlignOut | None = None,
+                    workspace=None, stream=None):
+    """moe_route then moe_align in one call (one launch fewer for decode-sized batches).
+    Returns (logits, topk_ids, topk_w, AlignOut)."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    dev = x.device
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev) if logits is None else logits
+    topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev) if topk_ids is None else topk_ids
+    topk_w = torch.empty((T, k), dtype=torch.float32, device=dev) if topk_w is None else topk_w
+    _need(x, torch.bfloat16, (T, H), "x")
+    _need(w_router, torch.bfloat16, (E, H), "w_router")
+    if bias is not None:
+        _need(bias, torch.float32, (E,), "bias")
+    _need(logits, torch.float32, (T, E), "logits")
+    _need(topk_ids, torch.int32, (T, k), "topk_ids")
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    out = alloc_align(T, k, E, block_m, dev) if out is None else out
+    need = moe_route_align_workspace_bytes(T, H, E, k)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = out.struct()
+    check("moe_route_align", lib().moe_route_align(_ptr(x), T, H, _ptr(w_router), E, _ptr(bias), k, int(renormalize),
+                                                   _ptr(logits), _ptr(topk_ids), _ptr(topk_w), ctypes.byref(st),
+                                                   _ptr(workspace), ws_bytes, _stream(stream)))
+    return logits, topk_ids, topk_w, out
+
+
 # ----------------------------------------------------------------------------- expert layer
 
 def moe_workspace_bytes(routed: DeviceBank, shared: DeviceBank | None, T: int, k: int, block_m: int,
@@ -253,9 +287,9 @@ def choose_block_m(T: int, k: int, E: int, fmt: str | None = None) -> int:
 
 
 class MoeLayer:
-    """Pre-allocated buffers for one (bank, T, slice) and the three calls of one layer:
-    moe_route -> moe_align -> moe_expert_forward on one stream, host-sync free, so it can
-    be captured in a HIP graph.  Row-major banks are packed (moe_pack_bank) here, once; pass
+    """Pre-allocated buffers for one (bank, T, slice) and the calls of one layer:
+    moe_route_align (moe_route then moe_align) -> moe_expert_forward on one stream, host-sync
+    free, so it can be captured in a HIP graph.  Row-major banks are packed (moe_pack_bank) here, once; pass
     packed banks to share their storage between layers."""
 
     def __init__(self, routed: DeviceBank, shared: DeviceBank | None, w_router: torch.Tensor,
@@ -272,16 +306,15 @@ class MoeLayer:
         self.ids = torch.empty((T, k), dtype=torch.int32, device=dev)
         self.w = torch.empty((T, k), dtype=torch.float32, device=dev)
         self.align = alloc_align(T, k, E, self.block_m, dev)
-        self.align_ws = torch.empty(max(moe_align_workspace_bytes(T, k, E), 1), dtype=torch.uint8, device=dev)
-        self.route_ws = torch.empty(max(moe_route_workspace_bytes(T, routed.H, E), 1), dtype=torch.uint8, device=dev)
+        self.route_ws = torch.empty(max(moe_route_align_workspace_bytes(T, routed.H, E, k), 1), dtype=torch.uint8,
+                                    device=dev)
         self.ws = torch.empty(max(moe_workspace_bytes(routed, shared, T, k, self.block_m, slice_lo, slice_hi), 1),
                               dtype=torch.uint8, device=dev)
         self.out = torch.empty((T, routed.H), dtype=out_dtype, device=dev)
 
     def __call__(self, x: torch.Tensor, stream=None) -> torch.Tensor:
-        moe_route(x, self.w_router, self.bias, self.k, self.renormalize, self.logits, self.ids, self.w,
-                  self.route_ws, stream)
-        moe_align(self.ids, self.routed.E, self.block_m, self.align, self.align_ws, stream)
+        moe_route_align(x, self.w_router, self.bias, self.k, self.block_m, self.renormalize, self.logits, self.ids,
+                        self.w, self.align, self.route_ws, stream)
         moe_expert_forward(self.routed, self.shared, x, self.w, self.align, self.lo, self.hi, self.out,
                            self.out.dtype, self.ws, stream)
         return self.out

@@ -398,6 +398,11 @@ size_t moe_route_workspace_bytes(int T, int H, int E) {
   return qmoe::router_workspace_bytes(T, E, H);
 }
 
+size_t moe_route_align_workspace_bytes(int T, int H, int E, int k) {
+  // the router's partials, then (256-byte aligned) the align histograms
+  return (moe_route_workspace_bytes(T, H, E) + 255) / 256 * 256 + moe_align_workspace_bytes(T, k, E);
+}
+
 }  // extern "C"
 
 namespace {
@@ -471,6 +476,32 @@ int moe_align(const int32_t *topk_ids, int T, int k, int E, const moe_align_out 
                                        out->block_expert, out->counts, out->offsets, out->total_padded,
                                        static_cast<int32_t *>(workspace), static_cast<hipStream_t>(stream)),
                     "align launch");
+}
+
+int moe_route_align(const void *x_bf16, int T, int H, const void *w_router_bf16, int E, const float *bias, int k,
+                    int renormalize, float *logits, int32_t *topk_ids, float *topk_w, const moe_align_out *out,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+  int rc = check_route(x_bf16, T, H, w_router_bf16, E, k, logits, topk_ids, topk_w);
+  if (rc) return rc;
+  if ((long long)T * k > (1LL << 30)) return fail(MOE_ERR_UNSUPPORTED, "moe_route_align: T*k too large");
+  rc = check_align_out(out, T, k, E);
+  if (rc) return rc;
+  const size_t need = moe_route_align_workspace_bytes(T, H, E, k);
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "moe_route_align: workspace %zu < %zu", workspace_bytes, need);
+  if (need && !workspace) return fail(MOE_ERR_INVALID_ARG, "moe_route_align: workspace is NULL");
+  rc = check_device();
+  if (rc) return rc;
+  if (T == 0) return ok();
+  char *ws = static_cast<char *>(workspace);
+  const size_t hist_off = (moe_route_workspace_bytes(T, H, E) + 255) / 256 * 256;
+  return hip_status(qmoe::launch_route_align(static_cast<const uint16_t *>(x_bf16), T, H,
+                                             static_cast<const uint16_t *>(w_router_bf16), E, bias, k, renormalize,
+                                             logits, topk_ids, topk_w, reinterpret_cast<float *>(ws), out->block_m,
+                                             out->capacity, out->sorted_ids, out->block_expert, out->counts,
+                                             out->offsets, out->total_padded, reinterpret_cast<int32_t *>(ws + hist_off),
+                                             static_cast<hipStream_t>(stream)),
+                    "route_align launch");
 }
 
 int moe_pack_bank(const moe_bank *src, const moe_bank *dst, void *stream) {

@@ -56,6 +56,13 @@ hipError_t launch_topk(const float *logits, int T, int E, const float *bias, int
 hipError_t launch_align(const int32_t *ids, int T, int k, int E, int BM, int cap, int32_t *sorted_ids,
                         int32_t *block_expert, int32_t *counts, int32_t *offsets, int32_t *total_padded,
                         int32_t *hist, hipStream_t s);
+// route + align: one router GEMV and one top-k + align workgroup when route_align_fused(T, E, k),
+// else launch_route then launch_align.  partial and hist as for those two.
+bool route_align_fused(int T, int E, int k);
+hipError_t launch_route_align(const uint16_t *x, int T, int H, const uint16_t *w, int E, const float *bias, int k,
+                              int renormalize, float *logits, int32_t *ids, float *wts, float *partial, int BM,
+                              int cap, int32_t *sorted_ids, int32_t *block_expert, int32_t *counts,
+                              int32_t *offsets, int32_t *total_padded, int32_t *hist, hipStream_t s);
 hipError_t launch_gate_up(int fmt, const GateUpArgs &a, int n_shared_sub, hipStream_t s);
 hipError_t launch_down(int fmt, const DownArgs &a, int n_shared_sub, hipStream_t s);
 // Prefill GEMMs for align blocks of 128 rows (NVFP4, FP8_BLOCK128, BF16) with only the

@@ -5,13 +5,17 @@
 // and their softmax weights (renormalised over the k picks when norm_topk_prob is set:
 // FreeToken issue #62, second comment; PR #70 ownership table, "Router ... Replicated").
 //
-// Two kernels:
+// Kernels:
 //   k_router_partial  split-K GEMM: KS workgroup layers each reduce H/KS of K and write
 //                     their own partial [KS][T][E] (no atomics), so decode-sized batches
 //                     still spread the router weight over the whole chip.
 //   k_topk            sums the KS partials in a fixed order (plus bias), writes the
 //                     logits, then one wave per token selects k experts by k rounds of a
 //                     wave-wide (value, lower index) maximum built from DPP row steps.
+//   k_topk_align      for T <= 16: k_topk's work for every token in one workgroup of 1024
+//                     threads, then moe_align's single-workgroup counting sort on the picks,
+//                     which stay in LDS (moe_route_align; the same results as k_topk followed
+//                     by k_align_small, one launch and one global round trip fewer).
 #include "device_common.h"
 #include "launch.h"
 #include "route_align_dev.h"
@@ -51,15 +55,12 @@ __global__ __launch_bounds__(256) void k_router_partial(const uint16_t *__restri
 // in LDS.  Phase 2: wave w selects for token w.  Each lane sorts its NS keys (experts
 // l + 64q) descending; each round takes the wave-wide maximum of the lanes' heads and the
 // winning lane shifts its keys.
+// Phase 1 for tokens [t0, t0 + 4) by 256 threads (u = thread index among them): lg[tt][e].
 template <int NS, int KSMAX>
-__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, int KS, int T, int E,
-                                              const float *__restrict__ bias, int k, int renormalize,
-                                              float *__restrict__ logits_out, int32_t *__restrict__ ids,
-                                              float *__restrict__ wts) {
-  __shared__ float lg[4][NS * 64];
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * 4;
-  for (int e = threadIdx.x; e < E; e += 256) {
+__device__ __forceinline__ void topk_gather(const float *__restrict__ part, int KS, int T, int E,
+                                            const float *__restrict__ bias, float *__restrict__ logits_out,
+                                            int t0, int u, float (*lg)[NS * 64]) {
+  for (int e = u; e < E; e += 256) {
     // 4 tokens x KSMAX partials, every load unconditional (indices clamped) so all are in
     // flight at once; values past KS or T are masked, sums run in split order
     float v[4][KSMAX];
@@ -83,9 +84,43 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, in
       lg[tt][e] = s;
     }
   }
+}
+
+template <int NS, int KSMAX>
+__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, int KS, int T, int E,
+                                              const float *__restrict__ bias, int k, int renormalize,
+                                              float *__restrict__ logits_out, int32_t *__restrict__ ids,
+                                              float *__restrict__ wts) {
+  __shared__ float lg[4][NS * 64];
+  const int wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * 4;
+  topk_gather<NS, KSMAX>(part, KS, T, E, bias, logits_out, t0, threadIdx.x, lg);
   __syncthreads();
   const int t = t0 + wave;
   if (t < T) select_topk<NS>(lg[wave], E, k, renormalize, t, ids, wts);
+}
+
+// T <= 16 tokens, E <= 512 (NS <= 8), T * k <= 1024: thread group g = tid / 256 gathers tokens
+// [4g, 4g + 4), wave w selects token w, then the whole workgroup aligns the T * k picks.
+// Dynamic LDS: 17 * E int32 for the counting sort.
+template <int NS, int KSMAX>
+__global__ __launch_bounds__(1024) void k_topk_align(const float *__restrict__ part, int KS, int T, int E,
+                                                     const float *__restrict__ bias, int k, int renormalize,
+                                                     float *__restrict__ logits_out, int32_t *__restrict__ ids,
+                                                     float *__restrict__ wts, int BM, int cap,
+                                                     int32_t *__restrict__ sorted_ids,
+                                                     int32_t *__restrict__ block_expert, int32_t *__restrict__ counts,
+                                                     int32_t *__restrict__ offsets,
+                                                     int32_t *__restrict__ total_padded) {
+  extern __shared__ int32_t align_lds[];
+  __shared__ float lg[16][NS * 64];
+  __shared__ int32_t picks[1024];
+  const int wave = threadIdx.x >> 6, grp = threadIdx.x >> 8;
+  if (4 * grp < T) topk_gather<NS, KSMAX>(part, KS, T, E, bias, logits_out, 4 * grp, threadIdx.x & 255, &lg[4 * grp]);
+  __syncthreads();
+  if (wave < T) select_topk<NS, true>(lg[wave], E, k, renormalize, wave, ids, wts, picks);
+  __syncthreads();
+  align_block_1024(picks, T * k, E, BM, cap, sorted_ids, block_expert, counts, offsets, total_padded, align_lds);
 }
 
 template <int KSMAX>
@@ -162,6 +197,58 @@ hipError_t launch_route(const uint16_t *x, int T, int H, const uint16_t *w, int 
 hipError_t launch_topk(const float *logits, int T, int E, const float *bias, int k, int renormalize,
                        int32_t *ids, float *wts, hipStream_t s) {
   return launch_topk_ns(logits, 1, T, E, bias, k, renormalize, nullptr, ids, wts, s);
+}
+
+bool route_align_fused(int T, int E, int k) { return T >= 1 && T <= 16 && E <= 512 && T * k <= 1024; }
+
+template <int NS>
+static void launch_topk_align_ns(const float *part, int KS, int T, int E, const float *bias, int k, int renormalize,
+                                 float *logits_out, int32_t *ids, float *wts, int BM, int cap, int32_t *sorted_ids,
+                                 int32_t *block_expert, int32_t *counts, int32_t *offsets, int32_t *total_padded,
+                                 hipStream_t s) {
+  const size_t lds = 17 * (size_t)E * sizeof(int32_t);
+  if (KS <= 1)
+    hipLaunchKernelGGL((k_topk_align<NS, 1>), dim3(1), dim3(1024), lds, s, part, 1, T, E, bias, k, renormalize,
+                       logits_out, ids, wts, BM, cap, sorted_ids, block_expert, counts, offsets, total_padded);
+  else if (KS <= 8)
+    hipLaunchKernelGGL((k_topk_align<NS, 8>), dim3(1), dim3(1024), lds, s, part, KS, T, E, bias, k, renormalize,
+                       logits_out, ids, wts, BM, cap, sorted_ids, block_expert, counts, offsets, total_padded);
+  else
+    hipLaunchKernelGGL((k_topk_align<NS, 16>), dim3(1), dim3(1024), lds, s, part, KS, T, E, bias, k, renormalize,
+                       logits_out, ids, wts, BM, cap, sorted_ids, block_expert, counts, offsets, total_padded);
+}
+
+hipError_t launch_route_align(const uint16_t *x, int T, int H, const uint16_t *w, int E, const float *bias, int k,
+                              int renormalize, float *logits, int32_t *ids, float *wts, float *partial, int BM,
+                              int cap, int32_t *sorted_ids, int32_t *block_expert, int32_t *counts,
+                              int32_t *offsets, int32_t *total_padded, int32_t *hist, hipStream_t s) {
+  if (!route_align_fused(T, E, k)) {
+    hipError_t e = launch_route(x, T, H, w, E, bias, k, renormalize, logits, ids, wts, partial, s);
+    if (e != hipSuccess) return e;
+    return launch_align(ids, T, k, E, BM, cap, sorted_ids, block_expert, counts, offsets, total_padded, hist, s);
+  }
+  const int ks = router_ksplit(T, E, H);  // T <= 16: the split-K GEMV, as in launch_route
+  float *part = ks > 1 ? partial : logits;
+  dim3 grid((E + 63) / 64, (T + 15) / 16, ks);
+  hipLaunchKernelGGL(k_router_partial, grid, dim3(256), 0, s, x, T, H, w, E, bias, H / ks, part);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const float *b = ks > 1 ? bias : nullptr;
+  float *lo = ks > 1 ? logits : nullptr;
+  const int slots = (E + 63) / 64;
+  if (slots <= 1)
+    launch_topk_align_ns<1>(part, ks, T, E, b, k, renormalize, lo, ids, wts, BM, cap, sorted_ids, block_expert, counts,
+                            offsets, total_padded, s);
+  else if (slots <= 2)
+    launch_topk_align_ns<2>(part, ks, T, E, b, k, renormalize, lo, ids, wts, BM, cap, sorted_ids, block_expert, counts,
+                            offsets, total_padded, s);
+  else if (slots <= 4)
+    launch_topk_align_ns<4>(part, ks, T, E, b, k, renormalize, lo, ids, wts, BM, cap, sorted_ids, block_expert, counts,
+                            offsets, total_padded, s);
+  else
+    launch_topk_align_ns<8>(part, ks, T, E, b, k, renormalize, lo, ids, wts, BM, cap, sorted_ids, block_expert, counts,
+                            offsets, total_padded, s);
+  return hipGetLastError();
 }
 
 }  // namespace qmoe

@@ -87,10 +87,12 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
 // Top-k of token t by one wave from its E logits `lg` (any memory; E <= 64 NS): each lane
 // sorts its NS keys (experts l + 64q) descending; each round takes the wave-wide maximum of
 // the lanes' heads and the winning lane shifts its keys.  Writes ids[t*k + j] in rank order
-// and the softmax weights (over the k picks when renormalize, else over all E).
-template <int NS>
+// and the softmax weights (over the k picks when renormalize, else over all E).  COPY: the
+// ids also go to ids_copy (same index), e.g. an LDS array that a later step of the kernel reads.
+template <int NS, bool COPY = false>
 __device__ __forceinline__ void select_topk(const float *lg, int E, int k, int renormalize, int t,
-                                            int32_t *__restrict__ ids, float *__restrict__ wts) {
+                                            int32_t *__restrict__ ids, float *__restrict__ wts,
+                                            int32_t *ids_copy = nullptr) {
   const int lane = lane_id();
   uint64_t key[NS];
   float vals[NS];
@@ -123,6 +125,7 @@ __device__ __forceinline__ void select_topk(const float *lg, int E, int k, int r
     if (lane == j) mine = bv;
     if (j == 0) top = bv;
     if (lane == 0) ids[(size_t)t * k + j] = bi;
+    if (COPY && lane == 0) ids_copy[t * k + j] = bi;
   }
   // softmax weights
   float z;

@@ -116,6 +116,22 @@ def test_route_and_align_reject_bad_arguments():
     assert lib.moe_align(FAKE, 16, 2, 2048, ctypes.byref(al), FAKE, 1 << 20, None) == L.MOE_ERR_UNSUPPORTED
 
 
+def test_route_align_rejects_bad_arguments():
+    lib = L.lib()
+    W = 1 << 30
+    al = _align(T=16, k=2, E=8)
+    ra = lib.moe_route_align
+    assert ra(None, 16, 256, FAKE, 8, None, 2, 1, FAKE, FAKE, FAKE, ctypes.byref(al), FAKE, W, None) == L.MOE_ERR_INVALID_ARG
+    assert ra(FAKE, 16, 256, FAKE, 8, None, 9, 1, FAKE, FAKE, FAKE, ctypes.byref(al), FAKE, W, None) == L.MOE_ERR_INVALID_ARG
+    assert ra(FAKE, 16, 200, FAKE, 8, None, 2, 1, FAKE, FAKE, FAKE, ctypes.byref(al), FAKE, W, None) == L.MOE_ERR_UNSUPPORTED
+    small = _align(cap=16)
+    assert ra(FAKE, 16, 256, FAKE, 8, None, 2, 1, FAKE, FAKE, FAKE, ctypes.byref(small), FAKE, W, None) == L.MOE_ERR_INVALID_ARG
+    assert ra(FAKE, 16, 256, FAKE, 8, None, 2, 1, FAKE, FAKE, FAKE, None, FAKE, W, None) == L.MOE_ERR_INVALID_ARG
+    need = lib.moe_route_align_workspace_bytes(16, 256, 8, 2)
+    assert need >= lib.moe_route_workspace_bytes(16, 256, 8) + lib.moe_align_workspace_bytes(16, 2, 8)
+    assert ra(FAKE, 16, 256, FAKE, 8, None, 2, 1, FAKE, FAKE, FAKE, ctypes.byref(al), FAKE, need - 1, None) == L.MOE_ERR_WORKSPACE
+
+
 def test_workspace_bytes_formula():
     b = _bank(E=8, H=256, I=128)
     s = _bank(E=1, H=256, I=128)

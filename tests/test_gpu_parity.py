@@ -146,6 +146,34 @@ def test_align_is_bit_exact(T, k, E, bm, kind):
         np.testing.assert_array_equal(again[key], got[key], err_msg=key)
 
 
+@pytest.mark.parametrize("T,E,k,H,with_bias,renorm,bm", [
+    (1, 256, 8, 2048, False, True, 16), (2, 8, 2, 256, True, True, 16), (5, 3, 3, 128, False, False, 32),
+    (16, 512, 16, 384, True, True, 64), (16, 64, 64, 256, False, True, 128), (4, 1, 1, 128, False, True, 16),
+    (8, 100, 6, 640, True, False, 256),
+    (17, 256, 8, 2048, False, True, 16), (64, 256, 8, 2048, True, True, 16), (1, 513, 4, 256, False, True, 16),
+    (16, 128, 64, 128, False, True, 16), (1500, 200, 6, 1024, True, True, 128)])
+def test_route_align_equals_route_then_align(T, E, k, H, with_bias, renorm, bm):
+    """moe_route_align (one top-k + align workgroup for T <= 16, E <= 512, T*k <= 1024) gives
+    exactly the outputs of moe_route followed by moe_align, on both sides of that boundary."""
+    x, wr = bf16_dev(S.tokens(5, T, H)), bf16_dev(S.router_weight(5, E, H))
+    bias = to_dev(S.zipf_bias(5, E, 1.1)) if with_bias else None
+    lg1, ids1, w1 = qm.moe_route(x, wr, bias, k, renorm)
+    al1 = align_np(qm.moe_align(ids1, E, bm))
+    lg2, ids2, w2, al2 = qm.moe_route_align(x, wr, bias, k, bm, renorm)
+    assert torch.equal(lg1, lg2) and torch.equal(ids1, ids2) and torch.equal(w1, w2)
+    al2 = align_np(al2)
+    for key in al1:
+        np.testing.assert_array_equal(al2[key], al1[key], err_msg=key)
+    # and against the oracle's selection and alignment where the picks are pinned
+    _, ids_ref, _, gap = O.route(S.tokens(5, T, H), S.router_weight(5, E, H),
+                                 S.zipf_bias(5, E, 1.1) if with_bias else None, k, renorm)
+    if (gap > NEAR_TIE).all():
+        np.testing.assert_array_equal(ids2.cpu().numpy(), ids_ref)
+        ref = O.align(ids_ref, E, bm)
+        for key in ref:
+            np.testing.assert_array_equal(al2[key], ref[key], err_msg=key)
+
+
 @pytest.mark.parametrize("seed", range(24))
 def test_random_route_then_align(seed):
     """Seeded random routing problems (expert counts 1..1000, k up to 64, hidden sizes up to
