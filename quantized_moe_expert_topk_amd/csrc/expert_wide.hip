@@ -250,16 +250,15 @@ __device__ __forceinline__ void wide_k_loop(WideLDS &lds, rsrc_t ra,
   }
 }
 
-// Grid position -> (row block, column group); false for positions past the row blocks in
-// use.  n_used: routed row blocks in use (total_padded / 128); n_cap: routed row blocks of the
-// capacity; n_rb: n_cap plus the shared expert's row blocks.
-__device__ __forceinline__ bool wide_block(int n_used, int n_cap, int n_rb, int ncg, int &rb, int &cg) {
-  const int N = n_used + (n_rb - n_cap);
+// Grid position -> (row block index idx among those in use, column group cg); see the
+// workgroup order above.  Positions idx < n_used are routed row block idx; the next ones are
+// the shared expert's row blocks; the rest have no work.  The kernels load the routed block's
+// expert and pair ids at idx (clamped) together with total_padded, before they know which
+// case holds: one dependent round trip fewer before the first activation and weight loads.
+__device__ __forceinline__ void wide_position(int ncg, int &idx, int &cg) {
   const int L = blockIdx.x, j = L >> 3;
-  const int idx = (j / ncg) * 8 + (L & 7);
+  idx = (j / ncg) * 8 + (L & 7);
   cg = j % ncg;
-  rb = idx < n_used ? idx : n_cap + (idx - n_used);
-  return idx < N;
 }
 
 __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[4][2]) {
@@ -285,17 +284,31 @@ __global__ __launch_bounds__(256, 2) void k_gate_up_wide(GateUpArgs a, int n_rb,
   using AS = AStage<WK>;
   __shared__ WideLDS lds;
   const int n_routed = a.cap / WM;
-  int rb, cg;
-  if (!wide_block(__builtin_amdgcn_readfirstlane(a.total_padded[0]) / WM, n_routed, n_rb, ncg, rb, cg)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool is_shared = rb >= n_routed;
+  int idx, cg;
+  wide_position(ncg, idx, cg);
+  const int ridx = max(0, min(idx, n_routed - 1));  // the routed row block idx would be
+  const int tp = a.total_padded[0];
+  const int eb = a.block_expert[ridx * WM / a.block_m];
+  int sf[AS::NQ];  // pair ids of this thread's rows of that block
+#pragma unroll
+  for (int q = 0; q < AS::NQ; q++) sf[q] = a.sorted_ids[ridx * WM + tid / AS::CPR + AS::RSTEP * q];
+  // all of them in flight before the first wait (left alone, the compiler moves the loads
+  // whose values only the routed path uses below the exit test)
+  asm volatile("" ::"s"(tp), "s"(eb));
+#pragma unroll
+  for (int q = 0; q < AS::NQ; q++) asm volatile("" ::"v"(sf[q]));
+  const int n_used = __builtin_amdgcn_readfirstlane(tp) / WM;
+  if (idx >= n_used + (n_rb - n_routed)) return;
+  const bool is_shared = idx >= n_used;
+  const int rb = is_shared ? n_routed + (idx - n_used) : idx;
   const int c0 = cg * (WCOLS / 2);
   int p0, e;
   const uint8_t *codes, *scales;
   const float *glob;
   if (!is_shared) {
     p0 = rb * WM;
-    e = __builtin_amdgcn_readfirstlane(a.block_expert[p0 / a.block_m]);
+    e = __builtin_amdgcn_readfirstlane(eb);
     if (e < 0) return;
     codes = a.gu;
     scales = a.gus;
@@ -316,7 +329,7 @@ __global__ __launch_bounds__(256, 2) void k_gate_up_wide(GateUpArgs a, int n_rb,
     const int p = p0 + tid / AS::CPR + AS::RSTEP * q;
     int tok;
     if (!is_shared) {
-      const int f = a.sorted_ids[p];
+      const int f = sf[q];
       tok = f < P ? f / a.k : -1;
     } else {
       tok = p - a.cap < T ? p - a.cap : -1;
@@ -371,16 +384,24 @@ __global__ __launch_bounds__(256, 2) void k_down_wide(DownArgs a, int n_rb, int 
   using AS = AStage<WK>;
   __shared__ WideLDS lds;
   const int n_routed = a.cap / WM;
-  int rb, cg;
-  if (!wide_block(__builtin_amdgcn_readfirstlane(a.total_padded[0]) / WM, n_routed, n_rb, ncg, rb, cg)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool is_shared = rb >= n_routed;
+  int idx, cg;
+  wide_position(ncg, idx, cg);
+  const int ridx = max(0, min(idx, n_routed - 1));  // the routed row block idx would be
+  const int tp = a.total_padded[0];
+  const int eb = a.block_expert[ridx * WM / a.block_m];
+  const int sd = tid < WM ? a.sorted_ids[ridx * WM + tid] : 0;  // pair id of row tid of that block
+  asm volatile("" ::"s"(tp), "s"(eb), "v"(sd));  // all in flight before the first wait (see gate_up)
+  const int n_used = __builtin_amdgcn_readfirstlane(tp) / WM;
+  if (idx >= n_used + (n_rb - n_routed)) return;
+  const bool is_shared = idx >= n_used;
+  const int rb = is_shared ? n_routed + (idx - n_used) : idx;
   int p0, e;
   const uint8_t *codes, *scales;
   const float *glob;
   if (!is_shared) {
     p0 = rb * WM;
-    e = __builtin_amdgcn_readfirstlane(a.block_expert[p0 / a.block_m]);
+    e = __builtin_amdgcn_readfirstlane(eb);
     if (e < 0) return;
     codes = a.dn;
     scales = a.dns;
@@ -413,8 +434,7 @@ __global__ __launch_bounds__(256, 2) void k_down_wide(DownArgs a, int n_rb, int 
   if (tid < WM) {  // destination of each pair row, read back in the epilogue
     const int p = p0 + tid;
     if (!is_shared) {
-      const int f = a.sorted_ids[p];
-      lds.dst[tid] = f < P ? f : -1;
+      lds.dst[tid] = sd < P ? sd : -1;
     } else {
       lds.dst[tid] = p - a.cap < T ? P + (p - a.cap) : -1;
     }
