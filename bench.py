@@ -81,9 +81,14 @@ def gate_up_slice_bytes(fmt, H, Il):
 
 
 def kernel_source_hash(kernel_name="k_gate_up"):
+    """Hash of the code (comments and whitespace removed) of the sources a kernel is built from."""
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel_name]:
-        h.update(open(os.path.join(ROOT, "quantized_moe_expert_topk_amd", "csrc", f), "rb").read())
+        text = open(os.path.join(ROOT, "quantized_moe_expert_topk_amd", "csrc", f)).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

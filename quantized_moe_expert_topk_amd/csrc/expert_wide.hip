@@ -28,9 +28,10 @@
 // block's scale: entering a block with scale s' multiplies them by s / s' (s the previous
 // block's), and the epilogue multiplies by the last scale.
 //
-// K loop: stage s multiplies from LDS buffer s%2 and weight register set s%2, while the
-// activation loads of stage s+2 and the weight loads of stage s+2 (issued once set s%2 is
-// consumed) are in flight and stage s+1 is stored to the other LDS buffer.
+// K loop: stage s multiplies from LDS buffer s%2 and weight register set s%2.  Meanwhile the
+// activation loads of stage s+1 (issued as stage s starts, stored to the other LDS buffer as it
+// ends) and the weight loads of stage s+1 (issued during stage s-1) are in flight; the weight
+// loads of stage s+2 go out once set s%2 is consumed.
 //
 // Workgroup order: the dispatcher assigns workgroup L to XCD L mod 8.  The row blocks in use
 // (the routed ones below total_padded, then the shared expert's) are dealt to the XCDs in
