@@ -80,6 +80,15 @@ const char *format_name(int fmt) {
   }
 }
 
+// Grid order of the streaming kernels: column groups fastest (neighbouring workgroups read
+// adjacent pieces of one expert's slice) when the slice is wide and the pairs many; 16-row
+// sub-blocks fastest otherwise.  Measured on MI355X: T*k = 512 at Il = 512 and T*k = 2048 at
+// Il = 1024 are faster column-first, T*k = 512 at Il = 256 and T*k <= 128 are not.  The
+// sub-blocks then index grid y, limited to 65535.
+bool cols_fastest(int T, int k, int Il, int n_sub) {
+  return Il >= 512 && (long long)T * k >= 512 && n_sub <= 65535;
+}
+
 // gate_up K split: H = 128 * kwaves * ksteps with kwaves <= 4 and ksteps <= 8 (kwaves as
 // large as possible).  Returns false if H has no such factorisation.
 bool gate_up_ksplit(int H, int *kwaves, int *ksteps) {
@@ -287,6 +296,7 @@ qmoe::GateUpArgs gate_up_args(const moe_bank *routed, const moe_bank *shared, co
     a.kwaves = 8;
     a.ksteps = routed->H / 1024;
   }
+  a.cols_fastest = cols_fastest(T, k, p.Il, p.n_routed_sub + p.n_shared_sub);
   char *ws = static_cast<char *>(workspace);
   a.h = reinterpret_cast<uint16_t *>(ws);
   a.h_rows = p.h_rows;
@@ -324,6 +334,7 @@ qmoe::DownArgs down_args(const moe_bank *routed, const moe_bank *shared, int T, 
   a.n_routed_sub = p.n_routed_sub;
   a.lo = lo;
   a.Il = p.Il;
+  a.cols_fastest = cols_fastest(T, k, p.Il, p.n_routed_sub + p.n_shared_sub);
   a.Y = reinterpret_cast<float *>(static_cast<char *>(workspace) + p.y_off);
   return a;
 }

@@ -563,8 +563,8 @@ __global__ __launch_bounds__(64 * KW, kMinWaves) void k_gate_up(GateUpArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lsc[(FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_MXFP4_E8M0 || FMT == MOE_FMT_Q4_0) ? KW * 2 * GCOLS * (128 * COUNT / (FMT == MOE_FMT_MXFP4_E8M0 ? 32 : 16)) : 16];
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int sb = blockIdx.x;
-  const int c0 = blockIdx.y * GCOLS;
+  const int sb = a.cols_fastest ? blockIdx.y : blockIdx.x;
+  const int c0 = (a.cols_fastest ? blockIdx.x : blockIdx.y) * GCOLS;
   const bool is_shared = sb >= a.n_routed_sub;
   int p0, e, tok;
   const uint8_t *codes;
@@ -694,7 +694,7 @@ __global__ __launch_bounds__(64 * KW, kMinWaves) void k_gate_up(GateUpArgs a) {
 
 // ---------------------------------------------------------------------------- down
 
-// Wave w owns hidden columns [n0, n0 + 16*DNT), n0 = blockIdx.y*64*DNT + 16*DNT*w: DNT MFMA
+// Wave w owns hidden columns [n0, n0 + 16*DNT), n0 = group*64*DNT + 16*DNT*w: DNT MFMA
 // tiles sharing one A fragment (a row block of h); K = the slice width Il.
 constexpr int DNT = 4;
 
@@ -704,8 +704,8 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lsc[(FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_MXFP4_E8M0 || FMT == MOE_FMT_Q4_0) ? 4 * 16 * DNT * (128 * COUNT / (FMT == MOE_FMT_MXFP4_E8M0 ? 32 : 16)) : 16];
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int sb = blockIdx.x;
-  const int n0 = blockIdx.y * 64 * DNT + wave * 16 * DNT;  // first output column (hidden index)
+  const int sb = a.cols_fastest ? blockIdx.y : blockIdx.x;
+  const int n0 = (a.cols_fastest ? blockIdx.x : blockIdx.y) * 64 * DNT + wave * 16 * DNT;  // first output column
   if (n0 >= a.H) return;
   const bool is_shared = sb >= a.n_routed_sub;
   int p0, e;
@@ -888,7 +888,8 @@ static void launch_gate_up_fmt(const GateUpArgs &a, dim3 grid, hipStream_t s) {
 }
 
 hipError_t launch_gate_up(int fmt, const GateUpArgs &a, int n_shared_sub, hipStream_t s) {
-  dim3 grid(a.n_routed_sub + n_shared_sub, (a.Il + GCOLS - 1) / GCOLS);
+  const int nsub = a.n_routed_sub + n_shared_sub, ncol = (a.Il + GCOLS - 1) / GCOLS;
+  const dim3 grid = a.cols_fastest ? dim3(ncol, nsub) : dim3(nsub, ncol);
   switch (fmt) {
     case MOE_FMT_NVFP4: launch_gate_up_fmt<MOE_FMT_NVFP4>(a, grid, s); break;
     case MOE_FMT_MXFP4_E8M0: launch_gate_up_fmt<MOE_FMT_MXFP4_E8M0>(a, grid, s); break;
@@ -910,7 +911,8 @@ static void launch_down_fmt(const DownArgs &a, dim3 grid, hipStream_t s) {
 }
 
 hipError_t launch_down(int fmt, const DownArgs &a, int n_shared_sub, hipStream_t s) {
-  dim3 grid(a.n_routed_sub + n_shared_sub, (a.H + 64 * DNT - 1) / (64 * DNT));
+  const int nsub = a.n_routed_sub + n_shared_sub, ncol = (a.H + 64 * DNT - 1) / (64 * DNT);
+  const dim3 grid = a.cols_fastest ? dim3(ncol, nsub) : dim3(nsub, ncol);
   switch (fmt) {
     case MOE_FMT_NVFP4: launch_down_fmt<MOE_FMT_NVFP4>(a, grid, s); break;
     case MOE_FMT_MXFP4_E8M0: launch_down_fmt<MOE_FMT_MXFP4_E8M0>(a, grid, s); break;
