@@ -33,3 +33,24 @@ def test_expert_slice_bytes_match_a_rank_slice(fmt, H, I, lo, hi):
         down += 4 * (H * Il) // 16384
     assert bench.gate_up_slice_bytes(fmt, H, Il) == gate_up
     assert bench.expert_slice_bytes(fmt, H, Il) == gate_up + down
+
+
+def test_kernel_source_hash_ignores_comments_not_code(tmp_path, monkeypatch):
+    """The traffic counters are keyed on the kernel's code: an edit to comments or whitespace
+    keeps the key, an edit to code changes it, and each kernel hashes its own sources."""
+    csrc = tmp_path / "quantized_moe_expert_topk_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (csrc / "device_common.h").write_text("#pragma once\nint helper(int x) { return x + 1; }\n")
+    (csrc / "expert.hip").write_text("// streaming\n__global__ void k(int *p) { p[0] = 1; }\n")
+    (csrc / "expert_wide.hip").write_text("/* wide */\n__global__ void w(int *p) { p[0] = 2; }\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h0, w0 = bench.kernel_source_hash("k_gate_up"), bench.kernel_source_hash("k_gate_up_wide")
+    assert h0 != w0
+    (csrc / "expert.hip").write_text("// streaming kernels, reworded\n/* block\n comment */\n"
+                                     "__global__ void k(int *p) {   p[0] = 1;   }  // trailing\n")
+    assert bench.kernel_source_hash("k_gate_up") == h0
+    (csrc / "expert.hip").write_text("__global__ void k(int *p) { p[0] = 3; }\n")
+    assert bench.kernel_source_hash("k_gate_up") != h0
+    assert bench.kernel_source_hash("k_gate_up_wide") == w0
+    (csrc / "device_common.h").write_text("#pragma once\nint helper(int x) { return x + 2; }\n")
+    assert bench.kernel_source_hash("k_gate_up_wide") != w0
