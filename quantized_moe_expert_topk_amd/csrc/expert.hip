@@ -815,12 +815,16 @@ __global__ __launch_bounds__(256) void k_combine(const void *__restrict__ Yv, co
   if (n >= H) return;
   const int nrows = k + (has_shared ? 1 : 0);  // the token's k pair rows, then its shared row
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int j0 = 0; j0 < nrows; j0 += 8) {
-    // up to 8 rows (and their weights) loaded before any is added (all in flight), then
+  // rows in flight: 16 for the fp32 rows of the streaming kernels (k <= 15 plus the shared row
+  // in one round trip, measured faster at decode), 8 for the bf16 rows of the prefill GEMMs
+  // (16 measured slower there)
+  constexpr int NB = YBF16 ? 8 : 16;
+  for (int j0 = 0; j0 < nrows; j0 += NB) {
+    // up to NB rows (and their weights) loaded before any is added (all in flight), then
     // summed in row order
-    float v[8][4], wj[8];
+    float v[NB][4], wj[NB];
 #pragma unroll
-    for (int u = 0; u < 8; u++) {
+    for (int u = 0; u < NB; u++) {
       const int j = j0 + u;
       const size_t row = j < k ? (size_t)t * k + j : (size_t)T * k + t;
       wj[u] = j < k ? w[row] : 1.f;  // row < T * k for routed rows
@@ -841,7 +845,7 @@ __global__ __launch_bounds__(256) void k_combine(const void *__restrict__ Yv, co
       }
     }
 #pragma unroll
-    for (int u = 0; u < 8; u++)
+    for (int u = 0; u < NB; u++)
       if (j0 + u < nrows)
 #pragma unroll
         for (int c = 0; c < 4; c++) acc[c] += wj[u] * v[u][c];
