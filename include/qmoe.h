@@ -64,7 +64,8 @@ extern "C" {
  *   MOE_FMT_Q4_0: 4-bit codes in 32-element blocks with an fp16 scale d per block (issue #62
  *     "What it touches" item 2 and "Suggested staging" item 3), in llama.cpp's q4_0 order:
  *     byte j of a block's 16 holds element j (low nibble) and element j + 16 (high nibble);
- *     W = (q - 8) * d.  The kernels take slices on multiples of 128 for this format.
+ *     W = (q - 8) * d.  Slices are on the block, multiples of 32; a packed bank's I must
+ *     be a multiple of 128 (one 16-byte piece of each of 4 blocks per 128 elements).
  * Packed FP4 stores two codes per byte, the even K index in the low nibble. */
 typedef enum {
   MOE_FMT_NVFP4 = 1,
@@ -201,6 +202,16 @@ typedef struct {
 /* Rows needed for any routing: T*k + E*(block_m - 1), rounded up to block_m. */
 int32_t moe_align_capacity(int T, int k, int E, int block_m);
 
+/* moe_choose_block_m -- the align block size that selects the expert kernels best suited to
+ * T tokens routed k ways over E experts of format fmt (a moe_format, or 0 if not known yet).
+ * With m = T*k/E pairs per expert on average: 128 (the prefill GEMMs, which reuse each weight
+ * tile across 128 pair rows) when m >= 32 and fmt is NVFP4, FP8_BLOCK128 or BF16; otherwise
+ * the streaming kernels with 16 (m <= 16), 32 (m <= 64) or 64 rows.  A pure function of its
+ * arguments, so every rank picks the same kernels.  Returns MOE_ERR_INVALID_ARG for T < 0,
+ * k < 1 or E < 1.  Pass the result to moe_align_capacity / moe_align and, through the align
+ * descriptor, to moe_expert_forward. */
+int32_t moe_choose_block_m(int T, int k, int E, int fmt);
+
 /* Device workspace moe_align needs (per-chunk expert histograms). */
 size_t moe_align_workspace_bytes(int T, int k, int E);
 
@@ -261,14 +272,24 @@ size_t moe_workspace_bytes(const moe_bank *routed, const moe_bank *shared, int T
  * gate_up follow its rows and down_global is used whole (PR #637 "Implementation notes").
  *   routed      E-expert bank; shared: NULL or a 1-expert bank of the same format, H and I;
  *               both in MOE_LAYOUT_TILE16 (moe_pack_bank), else MOE_ERR_UNSUPPORTED.
+ *               This is where the call departs from taking banks exactly as the pages store
+ *               them: the shapes, the gate/up row ranges, the down column range and the
+ *               companion-scale slicing are the pages' (issue #62 "What it touches" item 1,
+ *               PR #637 "Implementation notes"), but the bytes of each 16-row tile must have
+ *               been reordered once, at load, by moe_pack_bank (a permutation; a rank's slice
+ *               stays a pointer range).  Row-major bytes would cost the streaming kernels
+ *               about a fifth of their read rate (16 different rows per wave load).
  *   x_bf16      [T, H] bf16; topk_w [T, k] f32; al: the moe_align output for these ids.
  *   slice_lo/hi multiples of the format block (NVFP4 16, MXFP4 32, FP8_BLOCK128 128, BF16 1,
- *               Q4_0 32; the Q4_0 kernels need 128, else MOE_ERR_UNSUPPORTED), with
- *               0 <= lo < hi <= I (issue #62 "What it touches" item 2; PR #70 div_tp(...,
- *               multiple_of=128)).  The kernels additionally need (hi - lo) % 32 == 0.
+ *               Q4_0 32), with 0 <= lo < hi <= I (issue #62 "What it touches" item 2; PR #70
+ *               div_tp(..., multiple_of=128)).  The kernels additionally need lo and hi to
+ *               be multiples of 32, else MOE_ERR_UNSUPPORTED.
  *   out         [T, H] f32 (out_dtype MOE_OUT_F32) or bf16 (MOE_OUT_BF16), overwritten.
  *   workspace   >= moe_workspace_bytes(...) bytes of device memory.
- * Experts that received no tokens are never read.  The align block size picks the kernels:
+ * A token one of whose ids lay outside [0, E) (a caller error: moe_align drops such pairs)
+ * gets an undefined output row; every other token's row is unaffected.
+ * Experts that received no tokens are never read.  The align block size picks the kernels
+ * (moe_choose_block_m gives the library's choice):
  * al->block_m a multiple of 128 runs NVFP4, FP8_BLOCK128 and BF16 on prefill GEMMs that reuse
  * each weight across 128 pair rows (for many tokens per expert); other block sizes,
  * and MXFP4 and Q4_0, run the streaming kernels that read each selected weight byte once per

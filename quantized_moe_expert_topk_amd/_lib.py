@@ -20,7 +20,8 @@ MOE_OUT_F32, MOE_OUT_BF16 = 0, 1
 MOE_LAYOUT_ROWS, MOE_LAYOUT_TILE16, MOE_LAYOUT_MXFP4_T = 0, 1, 2
 
 # every entry point include/qmoe.h declares
-EXPORTS = ("moe_route", "moe_route_workspace_bytes", "moe_route_from_logits", "moe_align_capacity", "moe_align_workspace_bytes", "moe_align",
+EXPORTS = ("moe_route", "moe_route_workspace_bytes", "moe_route_from_logits", "moe_align_capacity",
+           "moe_choose_block_m", "moe_align_workspace_bytes", "moe_align",
            "moe_route_align_workspace_bytes", "moe_route_align",
            "moe_workspace_bytes", "moe_pack_bank", "moe_expert_forward", "moe_expert_gate_up", "moe_expert_down",
            "moe_status_string", "moe_last_error")
@@ -67,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.moe_route_from_logits.argtypes = [vp, i32, i32, vp, i32, i32, vp, vp, vp]
         L.moe_align_capacity.argtypes = [i32, i32, i32, i32]
         L.moe_align_capacity.restype = ctypes.c_int32
+        L.moe_choose_block_m.argtypes = [i32, i32, i32, i32]
+        L.moe_choose_block_m.restype = ctypes.c_int32
         L.moe_align_workspace_bytes.argtypes = [i32, i32, i32]
         L.moe_align_workspace_bytes.restype = sz
         L.moe_align.argtypes = [vp, i32, i32, i32, pa, vp, sz, vp]

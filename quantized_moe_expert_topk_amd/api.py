@@ -273,17 +273,14 @@ def moe_expert_down(routed: DeviceBank, shared: DeviceBank | None, topk_w: torch
 
 
 def choose_block_m(T: int, k: int, E: int, fmt: str | None = None) -> int:
-    """Rows per aligned block: 16 while experts see few tokens each, larger as the mean
-    number of pairs per expert grows; 128 (the prefill GEMMs) once experts see enough
-    tokens to reuse each weight tile, for the formats those kernels cover."""
-    mean = T * k / max(E, 1)
-    if mean >= 32 and fmt in ("nvfp4", "fp8blk", "bf16"):
-        return 128
-    if mean <= 16:
-        return 16
-    if mean <= 64:
-        return 32
-    return 64
+    """The library's block-size policy (``moe_choose_block_m``): 16 while experts see few
+    tokens each, larger as the mean number of pairs per expert grows; 128 (the prefill GEMMs)
+    once experts see enough tokens to reuse each weight tile, for the formats those kernels
+    cover."""
+    bm = int(lib().moe_choose_block_m(T, k, E, MOE_FMT.get(fmt, 0) if fmt else 0))
+    if bm < 0:
+        check("moe_choose_block_m", bm)
+    return bm
 
 
 class MoeLayer:

@@ -180,8 +180,6 @@ int check_slice(const moe_bank *b, int lo, int hi) {
                 format_name(b->fmt), blk);
   if (lo % 32 || hi % 32)
     return fail(MOE_ERR_UNSUPPORTED, "slice [%d, %d): the kernels need lo and hi multiples of 32", lo, hi);
-  if (b->fmt == MOE_FMT_Q4_0 && (lo % 128 || hi % 128))
-    return fail(MOE_ERR_UNSUPPORTED, "slice [%d, %d): the Q4_0 kernels need lo and hi multiples of 128", lo, hi);
   return MOE_OK;
 }
 
@@ -391,6 +389,17 @@ int32_t moe_align_capacity(int T, int k, int E, int block_m) {
   const long long need = (long long)T * k + (long long)E * (block_m - 1);
   const long long cap = (need + block_m - 1) / block_m * block_m;
   return cap > 0x7fffffffLL ? -1 : (int32_t)cap;
+}
+
+int32_t moe_choose_block_m(int T, int k, int E, int fmt) {
+  if (T < 0 || k < 1 || E < 1) return fail(MOE_ERR_INVALID_ARG, "moe_choose_block_m: T=%d k=%d E=%d", T, k, E);
+  // pairs per expert on average, compared as T*k against multiples of E (no rounding)
+  const long long pairs = (long long)T * k, e = E;
+  const bool wide = fmt == MOE_FMT_NVFP4 || fmt == MOE_FMT_FP8_BLOCK128 || fmt == MOE_FMT_BF16;
+  if (wide && pairs >= 32 * e) return 128;
+  if (pairs <= 16 * e) return 16;
+  if (pairs <= 64 * e) return 32;
+  return 64;
 }
 
 size_t moe_align_workspace_bytes(int T, int k, int E) {

@@ -51,15 +51,28 @@ __device__ __forceinline__ f32x4_t mfma_f16(const frag8 &a, const frag8 &b, f32x
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a.f, b.f, c, 0, 0, 0);
 }
 
-// 8 bf16 -> 8 f16, round to nearest.  Exact for magnitudes in [2^-14, 65504]; larger ones
-// become inf (callers detect that and redo the work in bf16), smaller ones f16 subnormals.
-__device__ __forceinline__ void bf16x8_to_f16(const uint4 &in, frag8 &out) {
+// 8 bf16 -> 8 f16, round to nearest.  Exact for 2^-17 <= |v| <= 65504 (an f16 subnormal is a
+// multiple of 2^-24, and a bf16 value of that size is one); larger magnitudes become inf
+// (callers detect that and redo the work in bf16), smaller nonzero ones may round.
+// flag accumulates, per 16-bit half, the maximum over the values of (2 * bits + 0x9200)
+// mod 2^16: the doubling drops the sign bit, and the offset maps a magnitude m (bits) to a
+// value above kF16InexactFlag exactly when 0 < m < 0x3700 (2^-17); zero maps to the flag
+// value itself and every larger magnitude below it.  One multiply-add and one max per pair.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+constexpr uint32_t kF16InexactFlag = 0x9200u;
+
+__device__ __forceinline__ void bf16x8_to_f16(const uint4 &in, frag8 &out, uint32_t &flag) {
   const uint32_t w[4] = {in.x, in.y, in.z, in.w};
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const float lo = __uint_as_float(w[j] << 16), hi = __uint_as_float(w[j] & 0xFFFF0000u);
     out.fh[j] = f16x2_t{(_Float16)lo, (_Float16)hi};
+    const u16x2_t v = __builtin_bit_cast(u16x2_t, w[j]) * u16x2_t{2, 2} + u16x2_t{0x9200, 0x9200};
+    flag = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, flag), v));
   }
+  // taken here, where the raw words are live anyway; left alone, the compiler sinks the
+  // check to the end of the loop and keeps every raw word alive until then
+  asm volatile("" : "+v"(flag));
 }
 
 __device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }

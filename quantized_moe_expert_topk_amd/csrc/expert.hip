@@ -14,8 +14,10 @@
 // (W4A16 / W8A16):
 //   NVFP4      e2m1 * e4m3 group scale, exact in f16 (and bf16): the activation fragment is
 //              converted to f16 once per chunk and v_mfma_f32_16x16x32_f16 runs; a wave whose
-//              accumulators turn non-finite (an activation beyond f16's range) redoes its K
-//              range in bf16.  The fp32 per-row global is applied in the epilogue.
+//              accumulators turn non-finite (an activation beyond f16's range), or that saw
+//              a nonzero activation below 2^-17 (one f16 may round), redoes its K range in
+//              bf16.  The fp32 per-row global is applied in
+//              the epilogue.
 //   FP8_BLOCK  e4m3 -> bf16 exact; the fp32 128x128 block scale multiplies each 128-wide
 //              K chunk's partial sum.
 //   BF16       used as stored.
@@ -181,7 +183,11 @@ __device__ __forceinline__ uint32_t scale_tile_off(uint32_t row, uint32_t K) {
 // partial sum is d (x . (128 + q) - 136 sum(x)), where the second term is one MFMA of x
 // against a constant -136 operand per block, shared by the NT tiles and fed in as the
 // accumulator input of each tile's MFMA; d (fp16, per weight row and block) then scales the
-// fp32 result.  kvalid is a multiple of 128 for Q4_0 (whole steps).
+// fp32 result.  Q4_0 steps are 128-wide and aligned to the row (b_k0 + kw0 a multiple of 128);
+// a K range that starts or ends inside a step (a down slice on a multiple of 32) is given as
+// QMASK with kphase, the offset of the range's first element inside its first step: the
+// blocks of a step before kphase (counted from kw0 = 0) or at or past kvalid are skipped, and
+// the activation row is read kphase elements later than the step offsets say.
 //   ra, a_row: activation buffer and the byte offset of this lane's row; a row past the
 //              buffer end reads as zeros without a memory request (padding rows)
 //   m, rows:   weight matrix (tile-16 layout) and this lane's row of each tile (the NT
@@ -193,11 +199,13 @@ __device__ __forceinline__ uint32_t scale_tile_off(uint32_t row, uint32_t K) {
 //              (lsc unused) load each lane's SP scale bytes per step and tile.  Q4_0 stages
 //              the same way (its 2 scale bytes per 32 elements give NVFP4's run length) and
 //              reads back the 8 bytes of its row per step.
-template <int FMT, int NT, int COUNT, bool F16 = false>
+//   flag:      F16 only: the running packed maximum bf16x8_to_f16 keeps for this lane
+template <int FMT, int NT, int COUNT, bool F16 = false, bool QMASK = false>
 __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FMT> &m, const uint32_t (&rows)[NT],
                                         int b_k0, int kw0, int kvalid, int g, f32x4_t (&acc)[NT],
-                                        uint8_t *lsc = nullptr) {
+                                        uint8_t *lsc = nullptr, uint32_t *flag = nullptr, int kphase = 0) {
   static_assert(!F16 || FMT == MOE_FMT_NVFP4, "the f16 path is for NVFP4 weights");
+  static_assert(!QMASK || FMT == MOE_FMT_Q4_0, "block masks are for Q4_0 steps");
   constexpr bool FP4 = FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_MXFP4_E8M0;
   constexpr bool BF16 = FMT == MOE_FMT_BF16;
   constexpr bool Q4 = FMT == MOE_FMT_Q4_0;
@@ -250,7 +258,10 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
       } else if constexpr (Q4) {
         const int kc = kw0 + (128 * i < kvalid ? 128 * i : 0);  // the step
 #pragma unroll
-        for (int q = 0; q < 4; q++) ar[ii].q[q] = buf_load16(ra, a_row + (kc + 32 * q + 8 * g) * 2);
+        for (int q = 0; q < 4; q++) {  // blocks before kphase read element 0 (skipped below)
+          const int ka = kc + 32 * q + 8 * g - kphase;
+          ar[ii].q[q] = buf_load16(ra, a_row + (ka > 0 ? ka : 0) * 2);
+        }
         const uint32_t st = (uint32_t)(b_k0 + kc) / 128;
 #pragma unroll
         for (int t = 0; t < NT; t++) {
@@ -323,12 +334,15 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
 #pragma unroll
       for (int q = 0; q < 4; q++) {
         if constexpr (F16)
-          bf16x8_to_f16(ar[ii].q[q], av[q]);  // once per chunk, shared by the NT tiles
+          bf16x8_to_f16(ar[ii].q[q], av[q], *flag);  // once per chunk, shared by the NT tiles
         else
           av[q].q = ar[ii].q[q];
       }
       if constexpr (Q4) {
         if (128 * i >= kvalid) continue;  // wave-uniform: a whole step past the range
+        bool qv[4];  // wave-uniform: block q of the step lies inside the range
+#pragma unroll
+        for (int q = 0; q < 4; q++) qv[q] = !QMASK || (128 * i + 32 * q < kvalid && kw0 + 128 * i + 32 * q >= kphase);
         frag8 neg;  // bf16 -136 in every slot
         neg.q = make_uint4(0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u);
         f32x4_t ns[4];
@@ -341,6 +355,7 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
                               f16_to_f32(qsv[ii][t].y >> 16)};
 #pragma unroll
           for (int q = 0; q < 4; q++) {
+            if (!qv[q]) continue;
             frag8 bq;
             q4x8_to_bf16_biased(dw[q], bq);
             const f32x4_t tmp = mfma_bf16(av[q], bq, ns[q]);
@@ -408,6 +423,12 @@ __device__ __forceinline__ bool any_nonfinite(const f32x4_t (&acc)[NT]) {
 #pragma unroll
     for (int j = 0; j < 4; j++) bad |= !__builtin_isfinite(acc[t][j]);
   return __ballot(bad) != 0;
+}
+
+// True (wave-uniform) if any lane saw a nonzero activation below 2^-17 (flag: the packed
+// maximum from mma_run), which f16 may round: the wave's run is then redone in bf16.
+__device__ __forceinline__ bool any_inexact_f16(uint32_t flag) {
+  return __ballot(max(flag & 0xFFFFu, flag >> 16) > kF16InexactFlag) != 0;
 }
 
 // An activation matrix [rows, K] carried as two e4m3 planes (hi, lo) with an e8m0 scale per
@@ -633,13 +654,15 @@ __global__ __launch_bounds__(64 * KW, kMinWaves) void k_gate_up(GateUpArgs a) {
     const rsrc_t ra = make_rsrc(a.x, (uint32_t)a.T * H * 2);
     const uint32_t a_row = tok >= 0 ? (uint32_t)tok * H * 2 : 0x80000000u;
     if (wave < a.kwaves) {
-      // NVFP4: f16 operands (exact weights, x exact up to 65504); a wave whose x overflows
-      // f16 redoes its K range with bf16 operands
+      // NVFP4: f16 operands (exact weights, x exact for 2^-17 <= |x| <= 65504); a wave whose
+      // x overflows f16, or holds a nonzero value below that range, redoes its K range with
+      // bf16 operands
       constexpr bool F16 = FMT == MOE_FMT_NVFP4;
+      uint32_t flag = 0;
       for (int kk = 0; kk < kw; kk += 128 * COUNT)
-        mma_run<FMT, 2 * GT, COUNT, F16>(ra, a_row, m, rows, 0, wave * kw + kk, kw - kk, g, acc, wsc);
+        mma_run<FMT, 2 * GT, COUNT, F16>(ra, a_row, m, rows, 0, wave * kw + kk, kw - kk, g, acc, wsc, &flag);
       if constexpr (F16) {
-        if (any_nonfinite(acc)) {  // rare: one step at a time, few registers
+        if (any_nonfinite(acc) || any_inexact_f16(flag)) {  // rare: one step at a time, few registers
 #pragma unroll
           for (int t = 0; t < 2 * GT; t++) acc[t] = zero4();
           for (int kk = 0; kk < kw; kk += 128)
@@ -778,11 +801,16 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
   } else {
     const rsrc_t ra = make_rsrc(a.h, (uint32_t)a.h_rows * Il * 2);
     const uint32_t a_row = real ? (uint32_t)(p0 + r) * Il * 2 : 0x80000000u;
-    constexpr bool F16 = FMT == MOE_FMT_NVFP4;  // as in gate_up: f16 operands, bf16 redo on overflow
-    for (int kw0 = 0; kw0 < Il; kw0 += 128 * COUNT)
-      mma_run<FMT, DNT, COUNT, F16>(ra, a_row, m, rows, a.lo, kw0, Il - kw0, g, acc, wsc);
+    constexpr bool F16 = FMT == MOE_FMT_NVFP4;  // as in gate_up: f16 operands, bf16 redo when unsafe
+    // Q4_0 steps cover 128-element pieces of the row from its start: a slice starting at a
+    // multiple of 32 inside one starts kph elements into its first step
+    constexpr bool Q4 = FMT == MOE_FMT_Q4_0;
+    const int kph = Q4 ? a.lo & 127 : 0;
+    uint32_t flag = 0;
+    for (int kw0 = 0; kw0 < Il + kph; kw0 += 128 * COUNT)
+      mma_run<FMT, DNT, COUNT, F16, Q4>(ra, a_row, m, rows, a.lo - kph, kw0, Il + kph - kw0, g, acc, wsc, &flag, kph);
     if constexpr (F16) {
-      if (any_nonfinite(acc)) {  // rare: one step at a time, few registers
+      if (any_nonfinite(acc) || any_inexact_f16(flag)) {  // rare: one step at a time, few registers
 #pragma unroll
         for (int t = 0; t < DNT; t++) acc[t] = zero4();
         for (int kw0 = 0; kw0 < Il; kw0 += 128)
@@ -906,8 +934,10 @@ hipError_t launch_gate_up(int fmt, const GateUpArgs &a, int n_shared_sub, hipStr
 
 template <int FMT>
 static void launch_down_fmt(const DownArgs &a, dim3 grid, hipStream_t s) {
-  // runs of at most 4 steps (down loops over runs; longer ones exceed the register budget)
-  switch (count_class(MOE_FMT_FP8_BLOCK128, (a.Il + 127) / 128)) {
+  // runs of at most 4 steps (down loops over runs; longer ones exceed the register budget);
+  // Q4_0 steps start at multiples of 128 of the row, so a slice may touch one more
+  const int kph = FMT == MOE_FMT_Q4_0 ? a.lo & 127 : 0;
+  switch (count_class(MOE_FMT_FP8_BLOCK128, (a.Il + kph + 127) / 128)) {
     case 1: hipLaunchKernelGGL((k_down<FMT, 1>), grid, dim3(256), 0, s, a); break;
     case 2: hipLaunchKernelGGL((k_down<FMT, 2>), grid, dim3(256), 0, s, a); break;
     default: hipLaunchKernelGGL((k_down<FMT, 4>), grid, dim3(256), 0, s, a); break;

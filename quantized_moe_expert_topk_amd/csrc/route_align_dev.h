@@ -43,9 +43,10 @@ __device__ __forceinline__ f32x4_t router_wave_partial(const uint16_t *__restric
 }
 
 // Ordered 64-bit key: larger logit first, then lower index.  Float bits are mapped to an
-// unsigned order (sign flip) in the upper half; the lower half is ~index.
+// unsigned order (sign flip) in the upper half; the lower half is ~index.  -0.0 and +0.0
+// are one score (equal logits tie to the lower index), so zero is made +0.0 first.
 __device__ __forceinline__ uint64_t rank_key(float v, int idx) {
-  uint32_t u = __float_as_uint(v);
+  uint32_t u = __float_as_uint(v == 0.f ? 0.f : v);
   u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return ((uint64_t)u << 32) | (uint32_t)(~(uint32_t)idx);
 }

@@ -45,6 +45,28 @@ def test_align_capacity_and_workspace_sizes():
     assert qm.moe_align_workspace_bytes(0, 8, 256) == 0
 
 
+@pytest.mark.parametrize("T,k,E,fmt,bm", [
+    (1, 8, 256, "nvfp4", 16), (64, 8, 256, "nvfp4", 16), (512, 8, 256, "nvfp4", 16),   # <= 16 pairs/expert
+    (513, 8, 256, "nvfp4", 32), (1023, 8, 256, "nvfp4", 32),                         # (16, 32)
+    (1024, 8, 256, "nvfp4", 128), (8192, 8, 256, "nvfp4", 128), (4096, 8, 256, "fp8blk", 128),
+    (8192, 8, 256, "bf16", 128),                                                       # >= 32: prefill GEMMs
+    (1024, 8, 256, "mxfp4", 32), (2048, 8, 256, "mxfp4", 32), (2049, 8, 256, "mxfp4", 64),
+    (8192, 8, 256, "q4_0", 64), (1024, 8, 256, None, 32), (16, 2, 8, "nvfp4", 16), (0, 8, 256, "nvfp4", 16),
+])
+def test_choose_block_m_policy(T, k, E, fmt, bm):
+    """The library's block-size policy, through the C ABI: pairs per expert on average against
+    16, 32 and 64, and the prefill GEMMs (128) only for the formats they cover."""
+    assert qm.choose_block_m(T, k, E, fmt) == bm
+    assert L.lib().moe_choose_block_m(T, k, E, L.MOE_FMT.get(fmt, 0) if fmt else 0) == bm
+
+
+def test_choose_block_m_rejects_bad_sizes():
+    lib = L.lib()
+    for args in ((-1, 8, 256, 1), (4, 0, 256, 1), (4, 8, 0, 1)):
+        assert lib.moe_choose_block_m(*args) == L.MOE_ERR_INVALID_ARG
+        assert lib.moe_last_error()
+
+
 def _bank(fmt=1, E=8, H=256, I=128, glob=True, layout=L.MOE_LAYOUT_TILE16, base=FAKE):
     return L.MoeBankStruct(fmt, E, H, I, base, base, base if glob else None, base, base, base if glob else None,
                            layout)
@@ -81,7 +103,6 @@ def _fwd(bank=None, shared=None, T=16, k=2, lo=0, hi=128, al=None, ws=1 << 30, o
     (dict(bank=_bank(fmt=2, I=256), lo=64, hi=192), L.MOE_ERR_ALIGNMENT),  # fp8-block slice % 128
     (dict(bank=_bank(fmt=3), lo=16, hi=128), L.MOE_ERR_ALIGNMENT),  # MXFP4 block is 32
     (dict(bank=_bank(fmt=5, glob=False, I=256), lo=16, hi=128), L.MOE_ERR_ALIGNMENT),  # Q4_0 block is 32
-    (dict(bank=_bank(fmt=5, glob=False, I=256), lo=32, hi=160), L.MOE_ERR_UNSUPPORTED),  # Q4_0 kernels: 128
     (dict(bank=_bank(fmt=5, glob=False, I=96), hi=96), L.MOE_ERR_UNSUPPORTED),  # Q4_0 bank I % 128
     (dict(al=_align(bm=8)), L.MOE_ERR_UNSUPPORTED),
     (dict(al=_align(cap=32)), L.MOE_ERR_INVALID_ARG),

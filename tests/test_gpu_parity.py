@@ -69,6 +69,29 @@ def test_route_from_logits_selection_is_bit_exact(T, E, k, renorm, with_bias):
     assert np.abs(w.cpu().numpy() - w_ref).max() <= 2e-6
 
 
+@pytest.mark.parametrize("k", [1, 2, 3])
+def test_route_from_logits_signed_zeros_are_one_score(k):
+    """-0.0 and +0.0 are the same logit: the lower index ranks first whichever of the two
+    carries the sign bit (the stated tie rule), with and without a bias that is zero."""
+    T, E = 6, 40
+    lg = -1.0 - S.logits_f32(21, 3, T, E) ** 2     # every other logit is below -1
+    lg = lg.astype(np.float32)
+    lg[0, 5], lg[0, 9] = np.float32(-0.0), np.float32(0.0)    # lower index negative zero
+    lg[1, 5], lg[1, 9] = np.float32(0.0), np.float32(-0.0)    # lower index positive zero
+    lg[2, [3, 7, 30]] = np.float32(-0.0)                     # three negative zeros
+    lg[3, [3, 7, 30]] = [np.float32(0.0), np.float32(-0.0), np.float32(0.0)]
+    lg[4, 0], lg[4, E - 1] = np.float32(-0.0), np.float32(0.0)
+    lg[5, :] = np.float32(-0.0)
+    lg[5, ::2] = np.float32(0.0)
+    assert np.signbit(lg[0, 5]) and not np.signbit(lg[0, 9])
+    ids_ref, w_ref, _ = O.topk(lg.astype(np.float64), k, True)
+    for bias in (None, np.zeros(E, np.float32)):
+        ids, w = qm.moe_route_from_logits(to_dev(lg), k, to_dev(bias), True)
+        np.testing.assert_array_equal(ids.cpu().numpy(), ids_ref)
+        assert np.abs(w.cpu().numpy() - w_ref).max() <= 2e-6
+    assert (ids_ref[0, 0], ids_ref[1, 0], ids_ref[4, 0], ids_ref[5, 0]) == (5, 5, 0, 0)
+
+
 @pytest.mark.parametrize("cid,T", [(1, 16), (2, 1), (2, 64), (4, 64), (5, 16), (3, 8192)])
 def test_route_matches_oracle(cid, T):
     cfg = S.CONFIGS[cid]
@@ -357,7 +380,10 @@ FORWARD_CASES = [(1, 16, (0, 128)), (1, 16, (0, 64)), (1, 16, (64, 128)),
                  # bf16 stacked experts (issue #62 "Suggested staging" item 1)
                  (6, 1, (0, 256)), (6, 64, (0, 256)), (6, 16, (32, 160)), (6, 8, (0, 512)),
                  # q4_0 experts (issue #62 "Suggested staging" item 3), no shared expert
-                 (7, 1, (0, 256)), (7, 64, (0, 256)), (7, 16, (128, 384)), (7, 8, (0, 512)), (7, 3, (384, 512))]
+                 (7, 1, (0, 256)), (7, 64, (0, 256)), (7, 16, (128, 384)), (7, 8, (0, 512)), (7, 3, (384, 512)),
+                 # q4_0 slices on its 32-element block (issue #62 "What it touches" item 2): down's K
+                 # range starts or ends inside a 128-wide step
+                 (7, 16, (32, 160)), (7, 8, (96, 512)), (7, 1, (0, 32)), (7, 64, (224, 480)), (7, 5, (480, 512))]
 
 
 @pytest.mark.parametrize("cid,T,sl", FORWARD_CASES)
@@ -386,6 +412,58 @@ def test_f16_overflow_tokens_redo_in_bf16():
     rest = [t for t in range(8) if t not in rows]
     check_close("f16 overflow rows", got[rows], ref[rows])
     check_close("other rows", got[rest], ref[rest])
+
+
+@pytest.mark.parametrize("cid,T,scale_exp", [(2, 8, -20), (2, 8, -16), (2, 64, -30), (4, 64, -20), (5, 16, -20),
+                                             (6, 8, -20), (7, 8, -20)])
+def test_tiny_activation_rows_keep_their_precision(cid, T, scale_exp):
+    """Token rows scaled by 2^scale_exp (exact in bf16), so that x and h fall below the
+    f16 normal range the NVFP4 decode operands use: every format must keep those rows'
+    relative accuracy.  Each scaled row is checked against 1e-2 * its own max|ref|, without
+    the absolute floor of the layer-wide tolerance, which would hide any error at this size."""
+    inp, r = inputs_for(cid, T)
+    x = inp.x.copy()
+    rows = [1, T - 2] if T > 2 else [0]
+    f = (x[rows].astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** scale_exp)
+    x[rows] = (f.view(np.uint32) >> 16).astype(np.uint16)
+    assert ((x[rows].astype(np.uint32) << 16).view(np.float32) == f).all()  # exact
+    hi = inp.cfg.I // 2
+    ref = O.expert_forward(inp.routed, inp.shared, x, r["ids"], r["w"], 0, hi)
+    got = _forward_gpu(dataclasses.replace(inp, x=x), r["ids"], r["w"], 0, hi, banks=dev_banks(inp))
+    for t in rows:
+        err = float(np.abs(got[t] - ref[t]).max())
+        bound = 1e-2 * float(np.abs(ref[t]).max())
+        print(f"[tiny] cfg{cid} T={T} 2^{scale_exp} row {t}: max|d| {err:.3e}, bound {bound:.3e}, "
+              f"ratio {err / bound:.3f}", flush=True)
+        assert bound > 0 and err <= bound, (t, err, bound)
+    rest = [t for t in range(T) if t not in rows]
+    check_close(f"cfg{cid} rows beside the tiny ones", got[rest], ref[rest])
+
+
+@pytest.mark.parametrize("bm", [16, 128])
+def test_ids_outside_the_bank_leave_other_tokens_exact(bm):
+    """A caller error: ids outside [0, E) in two tokens.  moe_align drops those pairs (they
+    appear nowhere in its output) and the forward pass leaves every other token's row as the
+    oracle computes it."""
+    inp, r = inputs_for(2, 32)
+    E = inp.cfg.E
+    ids = r["ids"].copy()
+    ids[3, 2], ids[17, 7] = -1, E
+    al = qm.moe_align(to_dev(ids), E, bm)
+    got_al = align_np(al)
+    ok = np.ones(ids.shape, bool)
+    ok[3, 2] = ok[17, 7] = False
+    sid = got_al["sorted_ids"]
+    real = np.sort(sid[sid < ids.size])
+    np.testing.assert_array_equal(real, np.flatnonzero(ok.ravel()))
+    assert got_al["counts"].sum() == ids.size - 2
+    rb, sb = dev_banks(inp)
+    out = qm.moe_expert_forward(rb, sb, bf16_dev(inp.x), to_dev(r["w"].astype(np.float32)), al, 0, 256)
+    got = out.cpu().numpy()
+    good = [t for t in range(32) if t not in (3, 17)]
+    sub = dataclasses.replace(inp, x=np.ascontiguousarray(inp.x[good]))
+    ref = O.expert_forward(sub.routed, sub.shared, sub.x, r["ids"][good], r["w"][good], 0, 256)
+    check_close(f"tokens without dropped pairs bm={bm}", got[good], ref)
 
 
 @pytest.mark.parametrize("bm", [16, 32, 64, 128])
@@ -497,23 +575,34 @@ def test_fp8_prefill_zero_block_scales(sl):
     assert np.isfinite(got).all()
 
 
+_oracle_cache = {}
+
+
+def oracle_forward(cid, T, lo, hi):
+    """The whole-layer oracle output for config `cid`, T tokens, slice [lo, hi), with the
+    oracle's own routing (computed once per case: it is the slow part)."""
+    key = (cid, T, lo, hi)
+    if key not in _oracle_cache:
+        inp, r = inputs_for(cid, T)
+        _oracle_cache[key] = O.expert_forward(inp.routed, inp.shared, inp.x, r["ids"], r["w"], lo, hi)
+    return _oracle_cache[key]
+
+
 @pytest.mark.parametrize("cid,T,sl,bm", [(3, 8192, (0, 512), 128), (3, 8192, (0, 256), 128),
                                          (4, 4096, (0, 256), 128), (3, 8192, (0, 512), 64),
                                          (6, 8192, (0, 512), 128), (5, 256, (0, 1024), None)])
-def test_prefill_full_size_sampled_rows(cid, T, sl, bm):
-    """Full-size prefill on the GPU (every tile of the real routing, Zipf-skewed for
-    config 3), checked on a seeded sample of token rows the oracle computes one by one."""
+def test_prefill_full_size_every_row(cid, T, sl, bm):
+    """Full-size layers at the block size the benchmark runs them with (align blocks of 128:
+    the prefill GEMMs; 64 for config 3 runs the streaming kernels at full size), every token
+    row compared element by element with the whole-layer oracle.  Config 3 has the Zipf-skewed
+    routing, so its hot experts span many row blocks and their last blocks are ragged."""
     inp, r = inputs_for(cid, T)
     lo, hi = sl
+    print(f"[prefill] cfg{cid} T={T} [{lo},{hi}) bm={bm}: oracle ...", flush=True)
+    ref = oracle_forward(cid, T, lo, hi)
     got = _forward_gpu(inp, r["ids"], r["w"], lo, hi, bm=bm)
-    rows = np.sort(np.random.default_rng(11).choice(T, 12, replace=False))
-    # the hottest expert's first and last tokens, where its many row tiles begin and end
-    hot = np.flatnonzero((r["ids"] == np.bincount(r["ids"].ravel()).argmax()).any(1))
-    rows = np.unique(np.concatenate([rows, hot[:2], hot[-2:], [T - 1]]))
-    sub = dataclasses.replace(inp, x=np.ascontiguousarray(inp.x[rows]))
-    ref = O.expert_forward(sub.routed, sub.shared, sub.x, r["ids"][rows], r["w"][rows], lo, hi)
-    check_close(f"prefill cfg{cid} T={T} [{lo},{hi}) bm={bm} rows={len(rows)}", got[rows], ref)
     assert np.isfinite(got).all()
+    check_close(f"prefill cfg{cid} T={T} [{lo},{hi}) bm={bm} all {T} rows", got, ref)
 
 
 @pytest.mark.parametrize("cid,T,sl", [(1, 16, (0, 128)), (2, 64, (0, 256)), (5, 16, (0, 1024))])
@@ -533,16 +622,21 @@ def test_full_layer_matches_oracle(cid, T, sl):
     check_close(f"full layer cfg{cid} T={T} [{lo},{hi})", got[sure], ref[sure])
 
 
-@pytest.mark.parametrize("cid,T,cuts", [(1, 16, (0, 64, 128)), (2, 64, (0, 256, 512)), (4, 64, (0, 256, 512)),
-                                        (2, 8, (0, 128, 384, 512)), (5, 16, (0, 96, 1024, 2048)),
-                                        (7, 16, (0, 128, 384, 512))])
-def test_gpu_slices_sum_to_gpu_full(cid, T, cuts):
+@pytest.mark.parametrize("cid,T,cuts,bm", [
+    (1, 16, (0, 64, 128), None), (2, 64, (0, 256, 512), None), (4, 64, (0, 256, 512), None),
+    (2, 8, (0, 128, 384, 512), None), (5, 16, (0, 96, 1024, 2048), None), (7, 16, (0, 128, 384, 512), None),
+    (7, 16, (0, 32, 96, 288, 512), None),
+    # the prefill GEMMs (align blocks of 128): full-size Zipf prefill, fp8-block at T = 4096, and
+    # bf16 cut at 96 and 352 (slices of 96, 256 and 160: K tails inside a 64-wide stage)
+    (3, 8192, (0, 256, 512), 128), (4, 4096, (0, 256, 512), 128), (6, 8192, (0, 96, 352, 512), 128),
+    (2, 64, (0, 32, 160, 512), 128)])
+def test_gpu_slices_sum_to_gpu_full(cid, T, cuts, bm):
     """Linearity in the intermediate index on the GPU: disjoint slices tiling [0, I) sum to
-    the unsliced GPU result (issue #520 section 4)."""
+    the unsliced GPU result (issue #520 section 4), for both kernel families."""
     inp, r = inputs_for(cid, T)
-    full = _forward_gpu(inp, r["ids"], r["w"], 0, inp.cfg.I)
-    parts = sum(_forward_gpu(inp, r["ids"], r["w"], lo, hi) for lo, hi in zip(cuts[:-1], cuts[1:]))
-    check_close(f"slice sum cfg{cid} T={T} cuts={cuts}", parts, full.astype(np.float64))
+    full = _forward_gpu(inp, r["ids"], r["w"], 0, inp.cfg.I, bm=bm)
+    parts = sum(_forward_gpu(inp, r["ids"], r["w"], lo, hi, bm=bm) for lo, hi in zip(cuts[:-1], cuts[1:]))
+    check_close(f"slice sum cfg{cid} T={T} cuts={cuts} bm={bm}", parts, full.astype(np.float64))
 
 
 @pytest.mark.parametrize("cid", [2, 6, 7])

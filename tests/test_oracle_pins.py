@@ -340,6 +340,36 @@ def test_align_matches_stable_sort_definition(T, k, E, BM, kind):
         assert (np.diff(r) > 0).all() and (ids.reshape(-1)[r] == e).all()
 
 
+@pytest.mark.parametrize("T,k,E,BM,cap", [
+    # worked by hand: every expert's run can carry BM - 1 padding rows, then round up to BM
+    (16, 2, 8, 16, 160),      # 32 pairs + 8*15 = 152 -> 160
+    (1, 8, 256, 16, 3856),    # 8 + 256*15 = 3848 -> 3856
+    (8192, 8, 256, 128, 98048),  # 65536 + 256*127 = 98048, already a multiple of 128
+    (0, 8, 256, 16, 3840),    # no pairs: 256*15 = 3840
+    (3, 1, 1, 4, 8),          # 3 + 3 = 6 -> 8
+    (5, 2, 3, 1, 10),         # BM = 1: exactly the pairs
+])
+def test_align_capacity_hand_values(T, k, E, BM, cap):
+    assert O.align_capacity(T, k, E, BM) == cap
+
+
+@pytest.mark.parametrize("T,k,E,BM", [(2, 2, 3, 4), (3, 1, 3, 2), (1, 3, 4, 3), (4, 1, 2, 5)])
+def test_align_capacity_bounds_every_routing(T, k, E, BM):
+    """Brute force over every assignment of the T*k pairs to E experts: the padded total never
+    exceeds the capacity, the capacity is a multiple of BM, and the worst assignment comes
+    within one block of it when there are at least as many pairs as experts (one pair in each
+    of E - 1 experts, the rest in the last, pads every run but one by BM - 1)."""
+    cap = O.align_capacity(T, k, E, BM)
+    assert cap % BM == 0
+    worst = 0
+    for ids in itertools.product(range(E), repeat=T * k):
+        counts = np.bincount(np.array(ids), minlength=E)
+        worst = max(worst, int((-(-counts // BM) * BM).sum()))
+    assert worst <= cap
+    if T * k >= E:
+        assert cap - worst <= BM, (cap, worst)
+
+
 # ------------------------------------------------------------------ expert layer
 
 def _dense_swiglu(x64, Wgu, Wd, lo, hi, I):
