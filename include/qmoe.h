@@ -301,6 +301,27 @@ int moe_expert_forward(const moe_bank *routed, const moe_bank *shared, const voi
                        int slice_lo, int slice_hi, void *out, int out_dtype, void *workspace,
                        size_t workspace_bytes, void *stream);
 
+/* moe_expert_forward_static -- moe_expert_forward on a workspace the library owns, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, checks, kernels and results as
+ * moe_expert_forward, without workspace and workspace_bytes: the workspace is a fixed
+ * MOE_STATIC_SCRATCH_BYTES device array inside the library, one per GPU, held until the
+ * process ends.  The call allocates nothing (no hipMalloc, no allocating library routine).
+ *   Limit: a call whose moe_workspace_bytes(...) exceeds MOE_STATIC_SCRATCH_BYTES returns
+ *   MOE_ERR_WORKSPACE before anything is enqueued (64 MiB holds, e.g., the Qwen3.6-shaped
+ *   NVFP4 decode layer at T = 64 and the DeepSeek-V4-Flash-shaped MXFP4 layer at T = 256 on
+ *   a 1024-wide slice; prefill batches need moe_expert_forward and a caller workspace).
+ *   Sharing: every call on one GPU uses that GPU's one array, which keeps what the previous
+ *   call left there (no part of it needs to start at zero).  Calls that overlap in time on
+ *   one GPU (two streams, two threads, two graphs replayed concurrently) race on it and give
+ *   undefined results; order them on one stream.
+ *   The first call on a device looks up the array's device address for that device
+ *   (hipGetSymbolAddress); make that first call outside graph capture. */
+#define MOE_STATIC_SCRATCH_BYTES (64u << 20)
+int moe_expert_forward_static(const moe_bank *routed, const moe_bank *shared, const void *x_bf16, int T, int k,
+                              const float *topk_w, const moe_align_out *al, int slice_lo, int slice_hi,
+                              void *out, int out_dtype, void *stream);
+
 /* The two halves of moe_expert_forward, for callers that time or schedule them apart.
  * Both take the same arguments and the same workspace; moe_expert_down reads what
  * moe_expert_gate_up left in the workspace for the same (routed, shared, x, al, slice). */

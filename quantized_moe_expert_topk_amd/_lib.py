@@ -17,13 +17,15 @@ MOE_ERR_HIP = -5
 
 MOE_FMT = {"nvfp4": 1, "fp8blk": 2, "mxfp4": 3, "bf16": 4, "q4_0": 5}
 MOE_OUT_F32, MOE_OUT_BF16 = 0, 1
+MOE_STATIC_SCRATCH_BYTES = 64 << 20
 MOE_LAYOUT_ROWS, MOE_LAYOUT_TILE16, MOE_LAYOUT_MXFP4_T = 0, 1, 2
 
 # every entry point include/qmoe.h declares
 EXPORTS = ("moe_route", "moe_route_workspace_bytes", "moe_route_from_logits", "moe_align_capacity",
            "moe_choose_block_m", "moe_align_workspace_bytes", "moe_align",
            "moe_route_align_workspace_bytes", "moe_route_align",
-           "moe_workspace_bytes", "moe_pack_bank", "moe_expert_forward", "moe_expert_gate_up", "moe_expert_down",
+           "moe_workspace_bytes", "moe_pack_bank", "moe_expert_forward", "moe_expert_forward_static",
+           "moe_expert_gate_up", "moe_expert_down",
            "moe_status_string", "moe_last_error")
 
 
@@ -80,6 +82,7 @@ def lib() -> ctypes.CDLL:
         L.moe_workspace_bytes.restype = sz
         L.moe_pack_bank.argtypes = [pb, pb, vp]
         L.moe_expert_forward.argtypes = [pb, pb, vp, i32, i32, vp, pa, i32, i32, vp, i32, vp, sz, vp]
+        L.moe_expert_forward_static.argtypes = [pb, pb, vp, i32, i32, vp, pa, i32, i32, vp, i32, vp]
         L.moe_expert_gate_up.argtypes = [pb, pb, vp, i32, i32, pa, i32, i32, vp, sz, vp]
         L.moe_expert_down.argtypes = [pb, pb, i32, i32, vp, pa, i32, i32, vp, i32, vp, sz, vp]
         L.moe_status_string.argtypes = [i32]

@@ -251,6 +251,23 @@ def moe_expert_forward(routed: DeviceBank, shared: DeviceBank | None, x: torch.T
     return out
 
 
+def moe_expert_forward_static(routed: DeviceBank, shared: DeviceBank | None, x: torch.Tensor, topk_w: torch.Tensor,
+                              align: AlignOut, slice_lo: int, slice_hi: int, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """moe_expert_forward on the library's own fixed device scratch (no workspace argument);
+    ``out`` must be passed (this call allocates nothing, here or in the library)."""
+    T, H = x.shape
+    k = topk_w.shape[1]
+    _need(x, torch.bfloat16, (T, H), "x")
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    _need(out, out.dtype, (T, H), "out")
+    rs, ss, al = routed.struct(), (shared.struct() if shared is not None else None), align.struct()
+    code = MOE_OUT_BF16 if out.dtype == torch.bfloat16 else MOE_OUT_F32
+    check("moe_expert_forward_static", lib().moe_expert_forward_static(
+        ctypes.byref(rs), ctypes.byref(ss) if ss is not None else None, _ptr(x), T, k, _ptr(topk_w),
+        ctypes.byref(al), slice_lo, slice_hi, _ptr(out), code, _stream(stream)))
+    return out
+
+
 def moe_expert_gate_up(routed: DeviceBank, shared: DeviceBank | None, x: torch.Tensor, k: int, align: AlignOut,
                        slice_lo: int, slice_hi: int, workspace: torch.Tensor, stream=None) -> None:
     T, H = x.shape

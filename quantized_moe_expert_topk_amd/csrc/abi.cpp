@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdint>
 #include <cstring>
 #include <string>
 
@@ -262,6 +263,18 @@ int check_forward(const moe_bank *routed, const moe_bank *shared, int T, int k, 
   return MOE_OK;
 }
 
+// Every host-side check of moe_expert_forward's arguments.
+int check_forward_call(const moe_bank *routed, const moe_bank *shared, const void *x_bf16, int T, int k,
+                       const float *topk_w, const moe_align_out *al, int lo, int hi, void *out, int out_dtype,
+                       size_t workspace_bytes, const void *workspace, FwdPlan *plan) {
+  int rc = check_forward(routed, shared, T, k, al, lo, hi, workspace_bytes, workspace, plan);
+  if (rc) return rc;
+  if (T > 0 && (!x_bf16 || !topk_w || !out)) return fail(MOE_ERR_INVALID_ARG, "x, topk_w or out is NULL");
+  if (out_dtype != MOE_OUT_F32 && out_dtype != MOE_OUT_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "out_dtype=%d", out_dtype);
+  return MOE_OK;
+}
+
 qmoe::GateUpArgs gate_up_args(const moe_bank *routed, const moe_bank *shared, const void *x, int T, int k,
                               const moe_align_out *al, int lo, const FwdPlan &p, void *workspace) {
   qmoe::GateUpArgs a;
@@ -367,6 +380,24 @@ int run_down(const moe_bank *routed, const moe_bank *shared, int T, int k, const
 }
 
 }  // namespace
+
+namespace qmoe {
+
+int set_last_error(int code, const char *msg) { return fail(code, "%s", msg); }
+
+int forward_workspace_need(const moe_bank *routed, const moe_bank *shared, const void *x_bf16, int T, int k,
+                           const float *topk_w, const moe_align_out *al, int lo, int hi, void *out, int out_dtype,
+                           size_t *need) {
+  FwdPlan p;
+  static const char probe = 0;  // a non-NULL workspace: only the size is asked for here
+  const int rc = check_forward_call(routed, shared, x_bf16, T, k, topk_w, al, lo, hi, out, out_dtype, SIZE_MAX,
+                                    &probe, &p);
+  if (rc) return rc;
+  *need = p.total;
+  return MOE_OK;
+}
+
+}  // namespace qmoe
 
 extern "C" {
 
@@ -650,11 +681,9 @@ int moe_expert_forward(const moe_bank *routed, const moe_bank *shared, const voi
                        const float *topk_w, const moe_align_out *al, int slice_lo, int slice_hi, void *out,
                        int out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
   FwdPlan p;
-  int rc = check_forward(routed, shared, T, k, al, slice_lo, slice_hi, workspace_bytes, workspace, &p);
+  int rc = check_forward_call(routed, shared, x_bf16, T, k, topk_w, al, slice_lo, slice_hi, out, out_dtype,
+                              workspace_bytes, workspace, &p);
   if (rc) return rc;
-  if (T > 0 && (!x_bf16 || !topk_w || !out)) return fail(MOE_ERR_INVALID_ARG, "x, topk_w or out is NULL");
-  if (out_dtype != MOE_OUT_F32 && out_dtype != MOE_OUT_BF16)
-    return fail(MOE_ERR_INVALID_ARG, "out_dtype=%d", out_dtype);
   rc = check_device();
   if (rc) return rc;
   if (T == 0) return ok();

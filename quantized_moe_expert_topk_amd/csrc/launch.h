@@ -46,6 +46,13 @@ struct DownArgs {
   float *Y;  // [T * k + T_shared, H] unweighted pair rows: fp32 (streaming kernels) or bf16 (prefill GEMMs)
 };
 
+// Host side of the ABI (abi.cpp): record the detail text of a failing call (returns code),
+// and run every argument check of moe_expert_forward, giving the workspace bytes it needs.
+int set_last_error(int code, const char *msg);
+int forward_workspace_need(const moe_bank *routed, const moe_bank *shared, const void *x_bf16, int T, int k,
+                           const float *topk_w, const moe_align_out *al, int lo, int hi, void *out, int out_dtype,
+                           size_t *need);
+
 int router_ksplit(int T, int E, int H);
 size_t router_workspace_bytes(int T, int E, int H);
 hipError_t launch_route(const uint16_t *x, int T, int H, const uint16_t *w, int E, const float *bias, int k,

@@ -194,3 +194,25 @@ def test_pack_bank_rejects_bad_arguments_before_any_launch(src, dst, code):
     assert rc == code, (rc, msg)
     assert msg
 
+
+
+def test_forward_static_rejects_before_any_launch():
+    """moe_expert_forward_static checks its arguments like moe_expert_forward, and a call whose
+    workspace exceeds the library's fixed scratch fails with MOE_ERR_WORKSPACE, all before it
+    touches a device."""
+    lib = L.lib()
+    b = _bank(E=256, H=2048, I=512)
+    T, k, bm = 8192, 8, 128
+    al = _align(bm=bm, T=T, k=k, E=256)
+    assert lib.moe_workspace_bytes(ctypes.byref(b), None, T, k, bm, 0, 512) > L.MOE_STATIC_SCRATCH_BYTES
+    rc = lib.moe_expert_forward_static(ctypes.byref(b), None, FAKE, T, k, FAKE, ctypes.byref(al), 0, 512, FAKE, 0,
+                                       None)
+    assert rc == L.MOE_ERR_WORKSPACE and b"scratch" in lib.moe_last_error()
+    small = _align(T=16, k=2, E=8)
+    bad = _bank()
+    assert lib.moe_expert_forward_static(ctypes.byref(bad), None, FAKE, 16, 2, FAKE, ctypes.byref(small), 8, 128,
+                                         FAKE, 0, None) == L.MOE_ERR_ALIGNMENT
+    assert lib.moe_expert_forward_static(None, None, FAKE, 16, 2, FAKE, ctypes.byref(small), 0, 128, FAKE, 0,
+                                         None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_forward_static(ctypes.byref(bad), None, FAKE, 16, 2, FAKE, ctypes.byref(small), 0, 128,
+                                         FAKE, 7, None) == L.MOE_ERR_INVALID_ARG
