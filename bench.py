@@ -5,15 +5,19 @@ top-k) -> moe_align -> moe_expert_forward (gate_up + SwiGLU, down, combine with 
 expert).  Each step runs from a HIP graph; steps rotate over independently seeded layer
 instances and token batches so that re-read weights are not served by the Infinity Cache.
 
-Default workload: the Qwen3.6-35B-A3B-shaped NVFP4 decode layer (H=2048, 256 experts, top-8,
-I=512, shared expert I=512) on one rank's slice I_local=256, T=64 tokens; the other decode
-batch sizes and the full-I layer are reported under "points".  ``--config`` picks another
-workload (3: prefill T=8192 with Zipf routing, 4: fp8-block, 5: DeepSeek-V4-Flash-shaped
-MXFP4, 6: bf16 experts, 7: q4_0).  Prints ONE JSON line.
+Default run (no flags): the headline is the largest single-GPU workload, the
+DeepSeek-V4-Flash-shaped MXFP4 layer (H=4096, 256 experts, top-8, I=2048 with a shared
+expert) on one rank's slice I_local=1024 at T=256 tokens.  The JSON line's "points" add, each
+with its own roofline: that layer at T=1 and T=16; the Qwen3.6-35B-A3B-shaped NVFP4 prefill
+layer at T=8192 with Zipf(1.1)-skewed routing (full I, and the 256 slice), the measure of
+grouped-GEMM MFMA efficiency; the fp8-block layer at T=64 and T=4096; and the NVFP4 decode
+layer at T=1 and T=64.  ``--config N`` runs one configuration's own points instead (6: bf16
+experts, 7: q4_0 experts among them).  Prints ONE JSON line.
 
-Besides the mean over the K timed steps, each point reports the spread of the step time
-(p10 / p50 / p90 over separately timed rotations), and the line reports the bandwidth of a
-plain 1 GiB device copy measured on the same GPU, beside the fractions of the 8 TB/s peak.
+Each point reports the spread of the step time (p10 / p50 / p90 over separately timed
+rotations); the line reports the bandwidth of a plain 1 GiB device copy on the same GPU
+beside the fractions of the 8 TB/s peak.  The CPU baseline (the fp64 oracle on the host's
+physical cores, passive OpenMP waits) runs in a child process before the GPU is touched.
 """
 from __future__ import annotations
 
@@ -38,12 +42,17 @@ KERNEL_SOURCES = {"k_gate_up": ("expert.hip", "device_common.h"),
                   "k_gate_up_wide": ("expert_wide.hip", "device_common.h")}
 WIDE_FORMATS = ("nvfp4", "fp8blk", "bf16")  # formats whose 128-row align blocks run the wide GEMMs
 
-# (config id) -> (T of the headline point, slice of the headline point, other (T, slice) points)
+# the default run: (config id, T, slice); the first is the headline
+DEFAULT_POINTS = [(5, 256, (0, 1024)), (5, 16, (0, 1024)), (5, 1, (0, 1024)),
+                  (3, 8192, (0, 512)), (3, 8192, (0, 256)),
+                  (4, 64, (0, 256)), (4, 4096, (0, 256)),
+                  (2, 64, (0, 256)), (2, 1, (0, 256))]
+# --config N: (T of the head point, slice of the head point, other (T, slice) points)
 WORKLOADS = {
     2: (64, (0, 256), [(1, (0, 256)), (8, (0, 256)), (32, (0, 256)), (64, (0, 512)), (1, (0, 512))]),
     3: (8192, (0, 512), [(8192, (0, 256))]),
     4: (64, (0, 256), [(1, (0, 256)), (4096, (0, 256))]),
-    5: (16, (0, 1024), [(1, (0, 1024)), (256, (0, 1024))]),
+    5: (256, (0, 1024), [(1, (0, 1024)), (16, (0, 1024))]),
     6: (64, (0, 256), [(1, (0, 256)), (8192, (0, 512))]),
     7: (64, (0, 256), [(1, (0, 256)), (64, (0, 512))]),
 }
@@ -108,11 +117,39 @@ def load_traffic(kernel_name, workload):
     return None
 
 
-def cpu_baseline(cfg, T, lo, hi, budget_s):
-    """The oracle (fp64 C, OpenMP) on the host cores: whole layers over token batches of the
-    same workload until about budget_s seconds of work are done."""
+def host_topology():
+    """(CPU model name, logical CPUs this process may run on, physical cores among them) from
+    the scheduler affinity and the kernel's CPU topology (Linux)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    cpus = sorted(os.sched_getaffinity(0))
+    cores = set()
+    for c in cpus:
+        try:
+            base = f"/sys/devices/system/cpu/cpu{c}/topology/"
+            cores.add((open(base + "physical_package_id").read().strip(), open(base + "core_id").read().strip()))
+        except OSError:
+            cores.add(("?", str(c)))
+    return model, len(cpus), len(cores)
+
+
+# host threads the GPU box gives one GPU's jobs, whatever the machine shows
+HOST_CPU_SHARE = 16
+
+
+def cpu_baseline_child(cid, T, lo, hi, budget_s):
+    """The oracle (fp64 C, OpenMP) run in this process on whole layers of the workload (route
+    and expert forward) over successive token batches, until about budget_s seconds of work."""
     from oracle import oracle as O
     from synth import synth as S
+    cfg = S.CONFIGS[cid]
     done_tokens, t_used, batches = 0, 0.0, 0
     base = S.layer_inputs(cfg, T, batch=0)  # instance 0, all experts
     while t_used < budget_s and batches < 64:
@@ -123,42 +160,55 @@ def cpu_baseline(cfg, T, lo, hi, budget_s):
         t_used += time.perf_counter() - t0
         done_tokens += T
         batches += 1
-    return dict(value=done_tokens / t_used, unit="tokens/s", cores=O.num_threads(), kind="oracle",
-                sample=f"{batches} batch(es) of T={T} tokens, whole layer (route + expert forward), "
-                       f"slice [{lo},{hi}), {t_used:.1f} s of timed oracle work", cpu=host_cpu())
+    print(json.dumps(dict(value=done_tokens / t_used, threads=O.num_threads(), batches=batches, t_used=t_used)),
+          flush=True)
 
 
-def host_cpu():
-    """The host CPU's model name and its logical CPU count (Linux /proc/cpuinfo)."""
-    model, n = "unknown", 0
-    try:
-        with open("/proc/cpuinfo") as f:
-            for ln in f:
-                if ln.startswith("model name"):
-                    n += 1
-                    model = ln.split(":", 1)[1].strip()
-    except OSError:
-        pass
-    return f"{model}, {n} logical CPUs"
+def cpu_baseline(cid, T, lo, hi, budget_s):
+    """Runs cpu_baseline_child in a child Python process (started before this process touches
+    the GPU) with one OpenMP thread per physical core of the CPUs it may use (at most the
+    box's share), threads bound to cores and passive waits: spinning threads beyond the
+    physical cores are what the pages measured costing a 19x slowdown (issue #62 follow-up
+    comment on the OpenMP spin-wait)."""
+    import subprocess
+    model, logical, physical = host_topology()
+    threads = max(1, min(physical, HOST_CPU_SHARE))
+    env = dict(os.environ, OMP_NUM_THREADS=str(threads), OMP_WAIT_POLICY="passive", OMP_PROC_BIND="spread",
+               OMP_PLACES="cores")
+    cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-child", f"{cid},{T},{lo},{hi},{budget_s}"]
+    r = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=max(120, 8 * budget_s))
+    if r.returncode != 0:
+        raise RuntimeError(f"cpu baseline child failed: {r.stderr[-2000:]}")
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    return dict(value=d["value"], unit="tokens/s", cores=d["threads"], kind="oracle",
+                sample=f"{d['batches']} batch(es) of T={T} tokens of config {cid}, whole layer (route + expert "
+                       f"forward), slice [{lo},{hi}), {d['t_used']:.1f} s of timed oracle work",
+                cpu=f"{model}; {physical} physical cores / {logical} logical CPUs available, {threads} OpenMP "
+                    f"threads (one per physical core, box share {HOST_CPU_SHARE}), OMP_WAIT_POLICY=passive")
 
 
-def run(args):
+# the arithmetic each kernel family computes in (per format; streaming kernels / prefill GEMMs)
+DTYPES = {
+    ("nvfp4", False): "bf16 x bf16 MFMA (e2m1*e4m3 weights exact in bf16), fp32 accumulate",
+    ("nvfp4", True): "bf16 x bf16 MFMA (e2m1*e4m3 weights exact in bf16), fp32 accumulate",
+    ("fp8blk", False): "bf16 x bf16 MFMA (e4m3 weights exact), fp32 accumulate, fp32 block scales",
+    ("fp8blk", True): "bf16 x bf16 MFMA (e4m3 weights exact), fp32 accumulate, fp32 block scales",
+    ("mxfp4", False): "scaled MFMA e4m3 (activation as hi+lo planes, e8m0 per 32) x e2m1 (e8m0 per 32), fp32 accumulate",
+    ("bf16", False): "bf16 x bf16 MFMA, fp32 accumulate",
+    ("bf16", True): "bf16 x bf16 MFMA, fp32 accumulate",
+    ("q4_0", False): "bf16 x bf16 MFMA (codes as exact bf16 128+q, offset and fp16 scale in fp32), fp32 accumulate",
+}
+
+
+def run(args, plan):
+    """Times every (config, T, slice) point of the plan; returns the list of point dicts."""
     import torch
 
     import quantized_moe_expert_topk_amd as qm
     from synth import synth as S
 
-    cid = args.config
-    cfg = S.CONFIGS[cid]
-    head_T, head_slice, others = WORKLOADS[cid]
-    if args.T:
-        head_T = args.T
-    if args.slice:
-        head_slice = tuple(int(v) for v in args.slice.split(","))
-    points = [(head_T, head_slice)] + ([] if args.no_points else [p for p in others if p != (head_T, head_slice)])
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    R = args.instances or INSTANCES[cid]
 
     def to_dev(a):
         return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
@@ -168,115 +218,145 @@ def run(args):
                                               to_dev(b.down), to_dev(b.down_scale), to_dev(b.gate_up_global),
                                               to_dev(b.down_global)))
 
-    # Weight storage of a point's slice [lo, hi): "own" = the rank holds only its slice (gate
-    # rows [lo, hi), up rows [I+lo, I+hi), down columns [lo, hi) as a bank with I = hi - lo,
-    # run on [0, hi - lo)); "full" = the whole bank, run on [lo, hi).
-    slices = sorted({sl for _, sl in points})
-    t0 = time.time()
-    inst = []
-    for r in range(R):
-        li = S.layer_inputs(cfg, 1, instance=r)
-        banks = {}
-        for (lo, hi) in slices:
-            if args.storage == "own" and (lo, hi) != (0, cfg.I):
-                rb, sb = S.slice_bank(li.routed, lo, hi), (S.slice_bank(li.shared, lo, hi) if li.shared is not None else None)
-            else:
-                rb, sb = li.routed, li.shared
-            key = (lo, hi) if rb is not li.routed else None
-            if key not in banks:
-                banks[key] = (dbank(rb), dbank(sb) if sb is not None else None)
-            banks[(lo, hi)] = banks[key]
-        inst.append(dict(banks=banks, router=to_dev(li.router).view(torch.bfloat16), bias=to_dev(li.bias)))
-        del li
-    log(f"config {cid}: {R} layer instance(s) generated and uploaded in {time.time() - t0:.1f} s")
-    Tmax = max(T for T, _ in points)
-    xs = [to_dev(S.tokens(cfg.seed, Tmax, cfg.H, batch=b)).view(torch.bfloat16) for b in range(BATCHES)]
-
     results = []
-    for (T, (lo, hi)) in points:
-        Il = hi - lo
-        layers, graphs, bytes_step, flops_step, gu_bytes = [], [], [], [], []
+    for cid in dict.fromkeys(c for c, _, _ in plan):  # configs in plan order
+        cfg = S.CONFIGS[cid]
+        points = [(T, sl) for c, T, sl in plan if c == cid]
+        R = args.instances or INSTANCES[cid]
+        # Weight storage of a point's slice [lo, hi): "own" = the rank holds only its slice (gate
+        # rows [lo, hi), up rows [I+lo, I+hi), down columns [lo, hi) as a bank with I = hi - lo,
+        # run on [0, hi - lo)); "full" = the whole bank, run on [lo, hi).
+        slices = sorted({sl for _, sl in points})
+        t0 = time.time()
+        inst = []
         for r in range(R):
-            I_ = inst[r]
-            for b in range(BATCHES):
-                x = xs[b][:T].contiguous()
-                rbank, sbank = I_["banks"][(lo, hi)]
-                klo = lo if rbank.I == cfg.I else 0  # the slice inside the bank this point runs on
-                L = qm.MoeLayer(rbank, sbank, I_["router"], I_["bias"], T, cfg.k, klo, klo + Il, cfg.renormalize)
-                L(x)  # eager run (warms up, and fixes this graph's routing for the byte count)
-                torch.cuda.synchronize()
-                counts = L.align.counts.cpu().numpy()
-                active = int((counts > 0).sum()) + (1 if cfg.shared else 0)
-                pairs = T * cfg.k + (T if cfg.shared else 0)
-                bytes_step.append(active * expert_slice_bytes(cfg.fmt, cfg.H, Il) + cfg.E * cfg.H * 2
-                                  + T * cfg.H * 2 + T * cfg.H * 4 + (cfg.E * 4 if I_["bias"] is not None else 0))
-                flops_step.append(2 * pairs * 3 * Il * cfg.H + 2 * T * cfg.E * cfg.H)
-                gu_bytes.append(active * gate_up_slice_bytes(cfg.fmt, cfg.H, Il) + T * cfg.H * 2 + pairs * Il * 2)
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    L(x)
-                layers.append((L, x))
-                graphs.append(g)
-        n = len(graphs)
-        # one graph over the whole rotation (n steps back to back) so that graph launches do
-        # not gap the steps; K steps = K // n rotations, then the first K % n single steps
-        g_all = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_all):
-            for L, x in layers:
+            li = S.layer_inputs(cfg, 1, instance=r)
+            banks = {}
+            for (lo, hi) in slices:
+                if args.storage == "own" and (lo, hi) != (0, cfg.I):
+                    rb = S.slice_bank(li.routed, lo, hi)
+                    sb = S.slice_bank(li.shared, lo, hi) if li.shared is not None else None
+                else:
+                    rb, sb = li.routed, li.shared
+                key = (lo, hi) if rb is not li.routed else None
+                if key not in banks:
+                    banks[key] = (dbank(rb), dbank(sb) if sb is not None else None)
+                banks[(lo, hi)] = banks[key]
+            inst.append(dict(banks=banks, router=to_dev(li.router).view(torch.bfloat16), bias=to_dev(li.bias)))
+            del li
+        log(f"config {cid}: {R} layer instance(s) generated and uploaded in {time.time() - t0:.1f} s")
+        Tmax = max(T for T, _ in points)
+        xs = [to_dev(S.tokens(cfg.seed, Tmax, cfg.H, batch=b)).view(torch.bfloat16) for b in range(BATCHES)]
+        for (T, (lo, hi)) in points:
+            results.append(time_point(args, qm, torch, cfg, inst, xs, T, lo, hi, R))
+        del inst, xs
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return results
+
+
+def time_point(args, qm, torch, cfg, inst, xs, T, lo, hi, R):
+    Il = hi - lo
+    layers, graphs, bytes_step, flops_step, gu_bytes, gu_flops = [], [], [], [], [], []
+    for r in range(R):
+        I_ = inst[r]
+        for b in range(BATCHES):
+            x = xs[b][:T].contiguous()
+            rbank, sbank = I_["banks"][(lo, hi)]
+            klo = lo if rbank.I == cfg.I else 0  # the slice inside the bank this point runs on
+            L = qm.MoeLayer(rbank, sbank, I_["router"], I_["bias"], T, cfg.k, klo, klo + Il, cfg.renormalize)
+            L(x)  # eager run (warms up, and fixes this graph's routing for the byte count)
+            torch.cuda.synchronize()
+            counts = L.align.counts.cpu().numpy()
+            active = int((counts > 0).sum()) + (1 if cfg.shared else 0)
+            pairs = T * cfg.k + (T if cfg.shared else 0)
+            bytes_step.append(active * expert_slice_bytes(cfg.fmt, cfg.H, Il) + cfg.E * cfg.H * 2
+                              + T * cfg.H * 2 + T * cfg.H * 4 + (cfg.E * 4 if I_["bias"] is not None else 0))
+            flops_step.append(2 * pairs * 3 * Il * cfg.H + 2 * T * cfg.E * cfg.H)
+            gu_bytes.append(active * gate_up_slice_bytes(cfg.fmt, cfg.H, Il) + T * cfg.H * 2 + pairs * Il * 2)
+            gu_flops.append(2 * pairs * 2 * Il * cfg.H)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
                 L(x)
+            layers.append((L, x))
+            graphs.append(g)
+    n = len(graphs)
+    # one graph over the whole rotation (n steps back to back) so that graph launches do
+    # not gap the steps; K steps = K // n rotations, then the first K % n single steps
+    g_all = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_all):
+        for L, x in layers:
+            L(x)
 
-        def run_steps(k):
-            for _ in range(k // n):
-                g_all.replay()
-            for i in range(k % n):
-                graphs[i].replay()
-
-        run_steps(args.warmup)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        run_steps(args.steps)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / args.steps
-        # spread: rotations timed one by one (events between whole-rotation replays)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.spread_rotations + 1)]
-        ev[0].record()
-        for i in range(args.spread_rotations):
+    def run_steps(k):
+        for _ in range(k // n):
             g_all.replay()
-            ev[i + 1].record()
-        torch.cuda.synchronize()
-        per_step = np.array([ev[i].elapsed_time(ev[i + 1]) / n for i in range(args.spread_rotations)])
-        avg_bytes = sum(bytes_step[i % n] for i in range(args.steps)) / args.steps
-        avg_flops = sum(flops_step[i % n] for i in range(args.steps)) / args.steps
-        # dominant kernel: gate_up (+SwiGLU), launched back to back from one captured graph
-        gk = torch.cuda.CUDAGraph()
-        reps = max(1, min(args.steps, 64) // n) * n
-        with torch.cuda.graph(gk):
-            for i in range(reps):
-                L, x = layers[i % n]
-                qm.moe_expert_gate_up(L.routed, L.shared, x, L.k, L.align, L.lo, L.hi, L.ws)
-        gk.replay()
-        torch.cuda.synchronize()
-        e0.record()
-        gk.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        k_ms = e0.elapsed_time(e1) / reps
-        k_bytes = sum(gu_bytes[i % n] for i in range(reps)) / reps
-        pt = dict(T=T, slice=[lo, hi], ms_per_step=ms, tokens_per_s=T / (ms * 1e-3), block_m=layers[0][0].block_m,
-                  ms_per_step_p10_p50_p90=[float(np.percentile(per_step, q)) for q in (10, 50, 90)],
-                  layer_hbm_gbs=avg_bytes / (ms * 1e-3) / 1e9, layer_hbm_frac=avg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                  layer_tflops=avg_flops / (ms * 1e-3) / 1e12,
-                  layer_mfma_frac=avg_flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"],
-                  alg_bytes_per_step=avg_bytes, alg_flops_per_step=avg_flops,
-                  gate_up_us=k_ms * 1e3, gate_up_bytes=k_bytes,
-                  gate_up_gbs=k_bytes / (k_ms * 1e-3) / 1e9)
-        log(json.dumps(pt))
-        results.append(pt)
-        del layers, graphs, gk, g_all
-        torch.cuda.synchronize()
-    return cfg, results
+        for i in range(k % n):
+            graphs[i].replay()
+
+    run_steps(args.warmup)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run_steps(args.steps)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    # spread: rotations timed one by one (events between whole-rotation replays)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.spread_rotations + 1)]
+    ev[0].record()
+    for i in range(args.spread_rotations):
+        g_all.replay()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = np.array([ev[i].elapsed_time(ev[i + 1]) / n for i in range(args.spread_rotations)])
+    avg_bytes = sum(bytes_step[i % n] for i in range(args.steps)) / args.steps
+    avg_flops = sum(flops_step[i % n] for i in range(args.steps)) / args.steps
+    # dominant kernel: gate_up (+SwiGLU), launched back to back from one captured graph on the
+    # stream the events are recorded on (the graph replays on torch's current stream)
+    gk = torch.cuda.CUDAGraph()
+    reps = max(1, min(args.steps, 64) // n) * n
+    with torch.cuda.graph(gk):
+        for i in range(reps):
+            L, x = layers[i % n]
+            qm.moe_expert_gate_up(L.routed, L.shared, x, L.k, L.align, L.lo, L.hi, L.ws)
+    gk.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    gk.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    k_ms = e0.elapsed_time(e1) / reps
+    k_bytes = sum(gu_bytes[i % n] for i in range(reps)) / reps
+    k_flops = sum(gu_flops[i % n] for i in range(reps)) / reps
+    bm = layers[0][0].block_m
+    wide = bm % 128 == 0 and cfg.fmt in WIDE_FORMATS
+    kname = "k_gate_up_wide" if wide else "k_gate_up"
+    workload = f"{cfg.name}; T={T}; slice [{lo},{hi})"
+    # roofline of the dominant kernel: bound by the point's arithmetic intensity against the
+    # ridge of the bf16 MFMA and HBM peaks
+    if avg_flops / avg_bytes > RIDGE_FLOP_PER_BYTE:
+        ach = k_flops / (k_ms * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=ach, peak=MFMA_PEAK_TFLOPS["bf16"], unit="TFLOP/s",
+                    frac=ach / MFMA_PEAK_TFLOPS["bf16"], per_launch=k_flops)
+    else:
+        ach = k_bytes / (k_ms * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s", frac=ach / HBM_PEAK_GBS,
+                    per_launch=k_bytes)
+    roof.update(kernel=f"{kname} (gate_up grouped GEMM + SwiGLU)", kernel_us=k_ms * 1e3,
+                traffic=load_traffic(kname, f"cfg{cfg.cid}_T{T}_slice{Il}"))
+    pt = dict(config=cfg.cid, workload=workload, format=cfg.fmt, T=T, slice=[lo, hi], block_m=bm,
+              dtype=DTYPES[(cfg.fmt, wide)], ms_per_step=ms, tokens_per_s=T / (ms * 1e-3),
+              ms_per_step_p10_p50_p90=[float(np.percentile(per_step, q)) for q in (10, 50, 90)],
+              layer_hbm_gbs=avg_bytes / (ms * 1e-3) / 1e9, layer_hbm_frac=avg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+              layer_tflops=avg_flops / (ms * 1e-3) / 1e12,
+              layer_mfma_frac=avg_flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"],
+              alg_bytes_per_step=avg_bytes, alg_flops_per_step=avg_flops, roofline=roof,
+              instances_rotated=R, batches_rotated=BATCHES)
+    log(json.dumps(pt))
+    del layers, graphs, gk, g_all
+    torch.cuda.synchronize()
+    return pt
 
 
 def copy_bandwidth_gbs(mib=1024, reps=5):
@@ -320,9 +400,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=sorted(WORKLOADS))
-    ap.add_argument("--T", type=int, default=0)
-    ap.add_argument("--slice", type=str, default="")
+    ap.add_argument("--config", type=int, default=0, choices=[0] + sorted(WORKLOADS),
+                    help="0 (default): the headline and the cross-configuration points; N: config N's own points")
+    ap.add_argument("--T", type=int, default=0, help="with --config: the head point's T")
+    ap.add_argument("--slice", type=str, default="", help="with --config: the head point's slice lo,hi")
     ap.add_argument("--instances", type=int, default=0)
     ap.add_argument("--no-points", action="store_true", help="only the headline point")
     ap.add_argument("--spread-rotations", type=int, default=20,
@@ -331,10 +412,15 @@ def main():
                     help="weights of a slice: the rank's own slice storage, or the full bank")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-baseline-child", type=str, default="", help=argparse.SUPPRESS)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy of MIB MiB (fp32 negate: reads and writes MIB MiB "
                          "each) three times, as the known-size kernel that HBM byte counters are scaled by")
     args = ap.parse_args()
+    if args.cpu_baseline_child:
+        cid, T, lo, hi, budget = args.cpu_baseline_child.split(",")
+        cpu_baseline_child(int(cid), int(T), int(lo), int(hi), float(budget))
+        return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
@@ -342,39 +428,45 @@ def main():
         print("bench.py measures one GPU: the layer runs on one rank's intermediate slice, and the cross-rank "
               "all-reduce of the partials is not implemented. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.config:
+        head_T, head_slice, others = WORKLOADS[args.config]
+        head_T = args.T or head_T
+        head_slice = tuple(int(v) for v in args.slice.split(",")) if args.slice else head_slice
+        plan = [(args.config, head_T, head_slice)] + [(args.config, T, sl) for T, sl in others
+                                                      if (T, sl) != (head_T, head_slice)]
+    else:
+        plan = list(DEFAULT_POINTS)
+    if args.no_points:
+        plan = plan[:1]
+    cid, T, (lo, hi) = plan[0]
+    cpu = None
+    if not args.no_cpu_baseline:  # before anything touches the GPU
+        t0 = time.time()
+        cpu = cpu_baseline(cid, T, lo, hi, args.cpu_budget)
+        log(f"cpu baseline: {cpu['value']:.1f} tokens/s on {cpu['cores']} threads ({time.time() - t0:.1f} s)")
     copy_gbs = copy_bandwidth_gbs()
-    cfg, results = run(args)
+    results = run(args, plan)
     for pt in results:
         pt["layer_hbm_frac_of_copy"] = pt["layer_hbm_gbs"] / copy_gbs
+        if pt["roofline"]["bound"] == "hbm":
+            pt["roofline"]["frac_of_measured_copy"] = pt["roofline"]["achieved"] / copy_gbs
     head = results[0]
-    workload = f"{cfg.name}; T={head['T']}; slice [{head['slice'][0]},{head['slice'][1]})"
-    # the head point's arithmetic intensity against the ridge of the bf16 MFMA and HBM peaks
-    bound = "mfma" if head["alg_flops_per_step"] / head["alg_bytes_per_step"] > RIDGE_FLOP_PER_BYTE else "hbm"
-    if bound == "hbm":
-        roof = dict(bound="hbm", achieved=head["gate_up_gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=head["gate_up_gbs"] / HBM_PEAK_GBS, frac_of_measured_copy=head["gate_up_gbs"] / copy_gbs)
-    else:
-        tf = 2 * (head["T"] * cfg.k + (head["T"] if cfg.shared else 0)) * 2 * (head["slice"][1] - head["slice"][0]) * cfg.H
-        ach = tf / (head["gate_up_us"] * 1e-6) / 1e12
-        roof = dict(bound="mfma", achieved=ach, peak=MFMA_PEAK_TFLOPS["bf16"], unit="TFLOP/s",
-                    frac=ach / MFMA_PEAK_TFLOPS["bf16"])
-    gk = "k_gate_up_wide" if head["block_m"] == 128 and cfg.fmt in WIDE_FORMATS else "k_gate_up"
-    roof["kernel"] = f"{gk} (gate_up grouped GEMM + SwiGLU)"
-    roof["traffic"] = load_traffic(gk, f"cfg{cfg.cid}_T{head['T']}_slice{head['slice'][1] - head['slice'][0]}")
+    from synth import synth as S
+    cfg = S.CONFIGS[head["config"]]
     line = {
         "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": workload, "format": cfg.fmt, "H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I,
-                   "shared_expert": cfg.shared, "T": head["T"], "slice": head["slice"], "instances_rotated":
-                   args.instances or INSTANCES[cfg.cid], "batches_rotated": BATCHES,
+        "vs_baseline": None, "dtype": head["dtype"], "data": "synthetic",
+        "config": {"workload": head["workload"], "format": cfg.fmt, "H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I,
+                   "shared_expert": cfg.shared, "T": head["T"], "slice": head["slice"], "block_m": head["block_m"],
+                   "instances_rotated": head["instances_rotated"], "batches_rotated": BATCHES,
                    "weight_storage": "rank's own slice" if args.storage == "own" else "full bank, sliced"},
         "layer_hbm_frac": head["layer_hbm_frac"], "layer_mfma_frac": head["layer_mfma_frac"],
         "ms_per_step_p10_p50_p90": head["ms_per_step_p10_p50_p90"], "hbm_copy_gbs": copy_gbs,
-        "roofline": roof, "points": results,
+        "roofline": head["roofline"], "points": results,
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, head["T"], head["slice"][0], head["slice"][1], args.cpu_budget)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 

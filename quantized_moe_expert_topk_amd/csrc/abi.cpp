@@ -204,10 +204,21 @@ struct FwdPlan {
   size_t hs_off, xq_off, xs_off, y_off, y_bytes, total;
 };
 
-FwdPlan plan_forward(const moe_bank *routed, const moe_bank *shared, int T, int k, int cap, int lo, int hi) {
+// 16-row sub-blocks the streaming kernels launch for the routed pairs: all of the capacity's,
+// or fewer when no routing can fill them.  Expert e's run takes ceil(c_e / BM) blocks of BM
+// rows, so the runs in use hold at most P/16 + min(E, P) * BM/16 sub-blocks (P = T*k pairs);
+// sub-blocks past total_padded exit at once, but their workgroups still cost launch slots
+// (at T = 1, E = 256, BM = 16: 9 sub-blocks instead of 257).
+int routed_sub_blocks(int T, int k, int E, int BM, int cap) {
+  const long long P = (long long)T * k;
+  const long long bound = (P + 15) / 16 + std::min<long long>(E, P) * (BM / 16);
+  return (int)std::min<long long>(cap / 16, bound);
+}
+
+FwdPlan plan_forward(const moe_bank *routed, const moe_bank *shared, int T, int k, int cap, int BM, int lo, int hi) {
   FwdPlan p;
   p.Il = hi - lo;
-  p.n_routed_sub = cap / 16;
+  p.n_routed_sub = routed_sub_blocks(T, k, routed->E, BM, cap);
   p.n_shared_sub = shared ? (T + 15) / 16 : 0;
   p.n_shared_tiles = shared ? (T + 127) / 128 : 0;
   p.shared_rows = p.n_shared_tiles * 128;  // room for whole 128-row tiles
@@ -255,7 +266,7 @@ int check_forward(const moe_bank *routed, const moe_bank *shared, int T, int k, 
   if ((long long)T * routed->H * 2 >= (1LL << 31) || rows * Il * 2 >= (1LL << 31) ||
       2LL * routed->I * routed->H >= (1LL << 31))
     return fail(MOE_ERR_UNSUPPORTED, "tensor exceeds 2 GiB (32-bit buffer offsets)");
-  *plan = plan_forward(routed, shared, T, k, al->capacity, lo, hi);
+  *plan = plan_forward(routed, shared, T, k, al->capacity, al->block_m, lo, hi);
   plan->tiled = al->block_m % 128 == 0 && routed->fmt != MOE_FMT_MXFP4_E8M0 && routed->fmt != MOE_FMT_Q4_0;
   if (workspace_bytes < plan->total)
     return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, plan->total);
@@ -444,7 +455,7 @@ size_t moe_workspace_bytes(const moe_bank *routed, const moe_bank *shared, int T
   if (!routed || T < 0 || k < 1 || slice_hi <= slice_lo || block_m < 16) return 0;
   const int32_t cap = moe_align_capacity(T, k, routed->E, block_m);
   if (cap < 0) return 0;
-  return plan_forward(routed, shared, T, k, cap, slice_lo, slice_hi).total;
+  return plan_forward(routed, shared, T, k, cap, block_m, slice_lo, slice_hi).total;
 }
 
 size_t moe_route_workspace_bytes(int T, int H, int E) {

@@ -20,14 +20,9 @@ typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
 
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-
-union frag8 {  // 8 bf16 (or 8 f16) = 4 dwords = one MFMA operand slot of one lane
+union frag8 {  // 8 bf16 = 4 dwords = one MFMA operand slot of one lane
   bf16x8_t v;
   bf16x2_t h[4];
-  f16x8_t f;
-  f16x2_t fh[4];
   uint32_t u[4];
   uint4 q;
 };
@@ -45,34 +40,6 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
 __device__ __forceinline__ f32x16_t mfma32_bf16(const frag8 &a, const frag8 &b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ f32x4_t mfma_f16(const frag8 &a, const frag8 &b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a.f, b.f, c, 0, 0, 0);
-}
-
-// 8 bf16 -> 8 f16, round to nearest.  Exact for 2^-17 <= |v| <= 65504 (an f16 subnormal is a
-// multiple of 2^-24, and a bf16 value of that size is one); larger magnitudes become inf
-// (callers detect that and redo the work in bf16), smaller nonzero ones may round.
-// flag accumulates, per 16-bit half, the maximum over the values of (2 * bits + 0x9200)
-// mod 2^16: the doubling drops the sign bit, and the offset maps a magnitude m (bits) to a
-// value above kF16InexactFlag exactly when 0 < m < 0x3700 (2^-17); zero maps to the flag
-// value itself and every larger magnitude below it.  One multiply-add and one max per pair.
-typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
-constexpr uint32_t kF16InexactFlag = 0x9200u;
-
-__device__ __forceinline__ void bf16x8_to_f16(const uint4 &in, frag8 &out, uint32_t &flag) {
-  const uint32_t w[4] = {in.x, in.y, in.z, in.w};
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const float lo = __uint_as_float(w[j] << 16), hi = __uint_as_float(w[j] & 0xFFFF0000u);
-    out.fh[j] = f16x2_t{(_Float16)lo, (_Float16)hi};
-    const u16x2_t v = __builtin_bit_cast(u16x2_t, w[j]) * u16x2_t{2, 2} + u16x2_t{0x9200, 0x9200};
-    flag = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, flag), v));
-  }
-  // taken here, where the raw words are live anyway; left alone, the compiler sinks the
-  // check to the end of the loop and keeps every raw word alive until then
-  asm volatile("" : "+v"(flag));
 }
 
 __device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
@@ -114,15 +81,6 @@ __device__ __forceinline__ void fp4x8_mul_to_bf16(uint32_t codes, float s, frag8
   out.h[1] = pack_bf16(p1[0] * s, p1[1] * s);
   out.h[2] = pack_bf16(p2[0] * s, p2[1] * s);
   out.h[3] = pack_bf16(p3[0] * s, p3[1] * s);
-}
-
-// 8 e2m1 codes -> 8 f16 of code * s, s an f16 pair with the scale in both halves.  The
-// product has at most 6 significant bits and lies in [2^-10, 2688] for e4m3 scales: exact.
-__device__ __forceinline__ void fp4x8_mul_to_f16(uint32_t codes, f16x2_t s, frag8 &out) {
-  out.fh[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * s;
-  out.fh[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * s;
-  out.fh[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * s;
-  out.fh[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * s;
 }
 
 // 8 e2m1 codes -> 8 bf16 of code * 2^x, where pow2 is the f32 2^x (MXFP4 e8m0 scale).

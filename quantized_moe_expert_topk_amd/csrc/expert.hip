@@ -12,12 +12,9 @@
 //
 // NVFP4 and fp8-block weights are dequantized in registers and fed to the 16x16x32 MFMA
 // (W4A16 / W8A16):
-//   NVFP4      e2m1 * e4m3 group scale, exact in f16 (and bf16): the activation fragment is
-//              converted to f16 once per chunk and v_mfma_f32_16x16x32_f16 runs; a wave whose
-//              accumulators turn non-finite (an activation beyond f16's range), or that saw
-//              a nonzero activation below 2^-17 (one f16 may round), redoes its K range in
-//              bf16.  The fp32 per-row global is applied in
-//              the epilogue.
+//   NVFP4      e2m1 * e4m3 group scale has at most 6 significant bits: exact in bf16, so the
+//              bf16 activations meet exact weights in v_mfma_f32_16x16x32_bf16 (W4A16, fp32
+//              accumulation); the fp32 per-row global is applied in the epilogue.
 //   FP8_BLOCK  e4m3 -> bf16 exact; the fp32 128x128 block scale multiplies each 128-wide
 //              K chunk's partial sum.
 //   BF16       used as stored.
@@ -97,18 +94,6 @@ __device__ __forceinline__ void decode_nvfp4(const uint4 &c, uint32_t s0, uint32
   fp4x8_mul_to_bf16(c.y, f0, b[1]);
   fp4x8_mul_to_bf16(c.z, f1, b[2]);
   fp4x8_mul_to_bf16(c.w, f1, b[3]);
-}
-
-//   NVFP4 to f16: the two e4m3 scales (low 16 bits of sc) become one f16 pair, and each
-//   half multiplies its 16 codes with packed f16 multiplies (1 VALU per weight, against 2 for
-//   the f32 path above)
-__device__ __forceinline__ void decode_nvfp4_f16(const uint4 &c, uint32_t sc, frag8 (&b)[4]) {
-  const f16x2_t s = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, false);
-  const f16x2_t s0 = __builtin_shufflevector(s, s, 0, 0), s1 = __builtin_shufflevector(s, s, 1, 1);
-  fp4x8_mul_to_f16(c.x, s0, b[0]);
-  fp4x8_mul_to_f16(c.y, s0, b[1]);
-  fp4x8_mul_to_f16(c.z, s1, b[2]);
-  fp4x8_mul_to_f16(c.w, s1, b[3]);
 }
 
 __device__ __forceinline__ void decode_mxfp4(const uint4 &c, uint32_t e8, frag8 (&b)[4]) {
@@ -199,12 +184,10 @@ __device__ __forceinline__ uint32_t scale_tile_off(uint32_t row, uint32_t K) {
 //              (lsc unused) load each lane's SP scale bytes per step and tile.  Q4_0 stages
 //              the same way (its 2 scale bytes per 32 elements give NVFP4's run length) and
 //              reads back the 8 bytes of its row per step.
-//   flag:      F16 only: the running packed maximum bf16x8_to_f16 keeps for this lane
-template <int FMT, int NT, int COUNT, bool F16 = false, bool QMASK = false>
+template <int FMT, int NT, int COUNT, bool QMASK = false>
 __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FMT> &m, const uint32_t (&rows)[NT],
                                         int b_k0, int kw0, int kvalid, int g, f32x4_t (&acc)[NT],
-                                        uint8_t *lsc = nullptr, uint32_t *flag = nullptr, int kphase = 0) {
-  static_assert(!F16 || FMT == MOE_FMT_NVFP4, "the f16 path is for NVFP4 weights");
+                                        uint8_t *lsc = nullptr, int kphase = 0) {
   static_assert(!QMASK || FMT == MOE_FMT_Q4_0, "block masks are for Q4_0 steps");
   constexpr bool FP4 = FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_MXFP4_E8M0;
   constexpr bool BF16 = FMT == MOE_FMT_BF16;
@@ -332,12 +315,7 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
       const bool v1 = 128 * i + 64 + 16 * g < kvalid;          // FP8 second half
       frag8 av[4];
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
-        if constexpr (F16)
-          bf16x8_to_f16(ar[ii].q[q], av[q], *flag);  // once per chunk, shared by the NT tiles
-        else
-          av[q].q = ar[ii].q[q];
-      }
+      for (int q = 0; q < 4; q++) av[q].q = ar[ii].q[q];
       if constexpr (Q4) {
         if (128 * i >= kvalid) continue;  // wave-uniform: a whole step past the range
         bool qv[4];  // wave-uniform: block q of the step lies inside the range
@@ -368,9 +346,7 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
 #pragma unroll
       for (int t = 0; t < NT; t++) {
         frag8 bv[4];
-        if constexpr (F16) {
-          decode_nvfp4_f16(c0[ii][t], lsv[ii][t], bv);
-        } else if constexpr (FMT == MOE_FMT_NVFP4) {
+        if constexpr (FMT == MOE_FMT_NVFP4) {
           decode_nvfp4(c0[ii][t], lsv[ii][t] & 0xFFu, (lsv[ii][t] >> 8) & 0xFFu, bv);
         } else if constexpr (FMT == MOE_FMT_MXFP4_E8M0) {
           decode_mxfp4(c0[ii][t], lsv[ii][t] & 0xFFu, bv);
@@ -401,9 +377,6 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
           for (int q = 0; q < 4; q++) tmp = mfma_bf16(av[q], bv[q], tmp);
 #pragma unroll
           for (int j = 0; j < 4; j++) acc[t][j] += bs[ii][t] * tmp[j];
-        } else if constexpr (F16) {
-#pragma unroll
-          for (int q = 0; q < 4; q++) acc[t] = mfma_f16(av[q], bv[q], acc[t]);
         } else {
 #pragma unroll
           for (int q = 0; q < 4; q++) acc[t] = mfma_bf16(av[q], bv[q], acc[t]);
@@ -411,24 +384,6 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
       }
     }
   }
-}
-
-// True (wave-uniform) if any lane holds a non-finite accumulator: after an f16 run that means
-// an activation beyond the f16 range (or a non-finite input), and the run is redone in bf16.
-template <int NT>
-__device__ __forceinline__ bool any_nonfinite(const f32x4_t (&acc)[NT]) {
-  bool bad = false;
-#pragma unroll
-  for (int t = 0; t < NT; t++)
-#pragma unroll
-    for (int j = 0; j < 4; j++) bad |= !__builtin_isfinite(acc[t][j]);
-  return __ballot(bad) != 0;
-}
-
-// True (wave-uniform) if any lane saw a nonzero activation below 2^-17 (flag: the packed
-// maximum from mma_run), which f16 may round: the wave's run is then redone in bf16.
-__device__ __forceinline__ bool any_inexact_f16(uint32_t flag) {
-  return __ballot(max(flag & 0xFFFFu, flag >> 16) > kF16InexactFlag) != 0;
 }
 
 // An activation matrix [rows, K] carried as two e4m3 planes (hi, lo) with an e8m0 scale per
@@ -654,21 +609,8 @@ __global__ __launch_bounds__(64 * KW, kMinWaves) void k_gate_up(GateUpArgs a) {
     const rsrc_t ra = make_rsrc(a.x, (uint32_t)a.T * H * 2);
     const uint32_t a_row = tok >= 0 ? (uint32_t)tok * H * 2 : 0x80000000u;
     if (wave < a.kwaves) {
-      // NVFP4: f16 operands (exact weights, x exact for 2^-17 <= |x| <= 65504); a wave whose
-      // x overflows f16, or holds a nonzero value below that range, redoes its K range with
-      // bf16 operands
-      constexpr bool F16 = FMT == MOE_FMT_NVFP4;
-      uint32_t flag = 0;
       for (int kk = 0; kk < kw; kk += 128 * COUNT)
-        mma_run<FMT, 2 * GT, COUNT, F16>(ra, a_row, m, rows, 0, wave * kw + kk, kw - kk, g, acc, wsc, &flag);
-      if constexpr (F16) {
-        if (any_nonfinite(acc) || any_inexact_f16(flag)) {  // rare: one step at a time, few registers
-#pragma unroll
-          for (int t = 0; t < 2 * GT; t++) acc[t] = zero4();
-          for (int kk = 0; kk < kw; kk += 128)
-            mma_run<FMT, 2 * GT, 1>(ra, a_row, m, rows, 0, wave * kw + kk, kw - kk, g, acc);
-        }
-      }
+        mma_run<FMT, 2 * GT, COUNT>(ra, a_row, m, rows, 0, wave * kw + kk, kw - kk, g, acc, wsc);
     }
   }
 #pragma unroll
@@ -801,22 +743,12 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
   } else {
     const rsrc_t ra = make_rsrc(a.h, (uint32_t)a.h_rows * Il * 2);
     const uint32_t a_row = real ? (uint32_t)(p0 + r) * Il * 2 : 0x80000000u;
-    constexpr bool F16 = FMT == MOE_FMT_NVFP4;  // as in gate_up: f16 operands, bf16 redo when unsafe
     // Q4_0 steps cover 128-element pieces of the row from its start: a slice starting at a
     // multiple of 32 inside one starts kph elements into its first step
     constexpr bool Q4 = FMT == MOE_FMT_Q4_0;
     const int kph = Q4 ? a.lo & 127 : 0;
-    uint32_t flag = 0;
     for (int kw0 = 0; kw0 < Il + kph; kw0 += 128 * COUNT)
-      mma_run<FMT, DNT, COUNT, F16, Q4>(ra, a_row, m, rows, a.lo - kph, kw0, Il + kph - kw0, g, acc, wsc, &flag, kph);
-    if constexpr (F16) {
-      if (any_nonfinite(acc) || any_inexact_f16(flag)) {  // rare: one step at a time, few registers
-#pragma unroll
-        for (int t = 0; t < DNT; t++) acc[t] = zero4();
-        for (int kw0 = 0; kw0 < Il; kw0 += 128)
-          mma_run<FMT, DNT, 1>(ra, a_row, m, rows, a.lo, kw0, Il - kw0, g, acc);
-      }
-    }
+      mma_run<FMT, DNT, COUNT, Q4>(ra, a_row, m, rows, a.lo - kph, kw0, Il + kph - kw0, g, acc, wsc, kph);
   }
 #pragma unroll
   for (int j = 0; j < 4; j++) {

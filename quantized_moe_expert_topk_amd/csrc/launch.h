@@ -18,7 +18,7 @@ struct GateUpArgs {
   const float *sgug;
   int E, I;
   const int32_t *sorted_ids, *block_expert, *total_padded;
-  int block_m, cap, n_routed_sub;  // n_routed_sub = cap / 16
+  int block_m, cap, n_routed_sub;  // routed 16-row sub-blocks launched (<= cap / 16, see abi.cpp)
   int lo, Il;
   int kwaves, ksteps;  // K split of gate_up: kwaves waves x ksteps steps of 128 (H = 128*kwaves*ksteps)
   int cols_fastest;    // streaming kernels: grid x is the column group (else the 16-row sub-block)

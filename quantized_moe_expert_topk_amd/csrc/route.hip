@@ -102,7 +102,9 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, in
 
 // T <= 16 tokens, E <= 512 (NS <= 8), T * k <= 1024: thread group g = tid / 256 gathers tokens
 // [4g, 4g + 4), wave w selects token w, then the whole workgroup aligns the T * k picks.
-// Dynamic LDS: 17 * E int32 for the counting sort.
+// Dynamic LDS: 17 * E int32 for the counting sort.  (Larger batches in chunks of 16 tokens
+// measured slower than k_topk's workgroups in parallel followed by k_align_small: at T = 64,
+// 34 us against 11 us, every chunk paying the partial-sum loads' latency alone.)
 template <int NS, int KSMAX>
 __global__ __launch_bounds__(1024) void k_topk_align(const float *__restrict__ part, int KS, int T, int E,
                                                      const float *__restrict__ bias, int k, int renormalize,
@@ -153,8 +155,9 @@ static hipError_t launch_topk_ns(const float *part, int KS, int T, int E, const 
 
 // K splits for the router GEMM: enough workgroups to cover the chip at small T.
 // Large batches run the router on the LDS-tiled GEMM (128 tokens x 128 experts per
-// workgroup), small ones on k_router_partial; both split K until about 512 (tiled) or 128
-// workgroups are in flight.
+// workgroup), small ones on k_router_partial; both split K until about 512 workgroups are in
+// flight (at most 16 splits): a workgroup's K loop is a chain of dependent load round trips,
+// so shorter ones finish sooner (T = 256, H = 4096: 2 -> 8 splits, step 409 -> 402 us).
 static bool router_tiled(int T) { return T >= 1024; }
 
 int router_ksplit(int T, int E, int H) {
@@ -166,7 +169,7 @@ int router_ksplit(int T, int E, int H) {
   }
   const int base = ((E + 63) / 64) * ((T + 15) / 16);
   int ks = 1;
-  while (base * ks < 128 && ks < 16 && ks * 2 <= H / 128 && (H / 128) % (ks * 2) == 0) ks *= 2;
+  while (base * ks < 512 && ks < 16 && ks * 2 <= H / 128 && (H / 128) % (ks * 2) == 0) ks *= 2;
   return ks;
 }
 
@@ -175,19 +178,22 @@ size_t router_workspace_bytes(int T, int E, int H) {
   return ks > 1 ? (size_t)ks * T * E * sizeof(float) : 0;
 }
 
+// The router GEMM into part: the K-split partials [ks][T][E] when ks > 1, else the logits
+// with the bias added.
+static hipError_t launch_router_gemm(const uint16_t *x, int T, int H, const uint16_t *w, int E, const float *bias,
+                                     int ks, float *part, hipStream_t s) {
+  if (router_tiled(T)) return launch_router_tiled(x, T, H, w, E, bias, ks, part, s);
+  dim3 grid((E + 63) / 64, (T + 15) / 16, ks);
+  hipLaunchKernelGGL(k_router_partial, grid, dim3(256), 0, s, x, T, H, w, E, bias, H / ks, part);
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const uint16_t *x, int T, int H, const uint16_t *w, int E, const float *bias, int k,
                         int renormalize, float *logits, int32_t *ids, float *wts, float *partial,
                         hipStream_t s) {
   const int ks = router_ksplit(T, E, H);
   float *part = ks > 1 ? partial : logits;
-  hipError_t e;
-  if (router_tiled(T)) {
-    e = launch_router_tiled(x, T, H, w, E, bias, ks, part, s);
-  } else {
-    dim3 grid((E + 63) / 64, (T + 15) / 16, ks);
-    hipLaunchKernelGGL(k_router_partial, grid, dim3(256), 0, s, x, T, H, w, E, bias, H / ks, part);
-    e = hipGetLastError();
-  }
+  const hipError_t e = launch_router_gemm(x, T, H, w, E, bias, ks, part, s);
   if (e != hipSuccess) return e;
   // with one split the GEMM already added the bias and wrote the logits in place
   return launch_topk_ns(part, ks, T, E, ks > 1 ? bias : nullptr, k, renormalize, ks > 1 ? logits : nullptr, ids, wts,
@@ -227,11 +233,9 @@ hipError_t launch_route_align(const uint16_t *x, int T, int H, const uint16_t *w
     if (e != hipSuccess) return e;
     return launch_align(ids, T, k, E, BM, cap, sorted_ids, block_expert, counts, offsets, total_padded, hist, s);
   }
-  const int ks = router_ksplit(T, E, H);  // T <= 16: the split-K GEMV, as in launch_route
+  const int ks = router_ksplit(T, E, H);  // the router GEMM exactly as launch_route runs it
   float *part = ks > 1 ? partial : logits;
-  dim3 grid((E + 63) / 64, (T + 15) / 16, ks);
-  hipLaunchKernelGGL(k_router_partial, grid, dim3(256), 0, s, x, T, H, w, E, bias, H / ks, part);
-  const hipError_t e = hipGetLastError();
+  const hipError_t e = launch_router_gemm(x, T, H, w, E, bias, ks, part, s);
   if (e != hipSuccess) return e;
   const float *b = ks > 1 ? bias : nullptr;
   float *lo = ks > 1 ? logits : nullptr;
