@@ -158,15 +158,18 @@ __global__ __launch_bounds__(256) void k_align_scatter(const int32_t *__restrict
   }
 }
 
-// Single-workgroup path for P <= 1024 pairs and E <= 512 (decode): histogram, scan, sentinels and the
-// stable scatter in one launch of 1024 threads.
+// Single-workgroup path (decode and mid-size batches): histogram, scan, sentinels and the
+// stable scatter in one launch of 1024 threads, for P <= 1024 pairs and E <= 512 (RPW = 1), or
+// P <= 4096 and E <= 256 (RPW = 4: four rows of 64 pairs per wave; at T = 256, k = 8 one launch
+// instead of the three chunked passes).
+template <int RPW>
 __global__ __launch_bounds__(1024) void k_align_small(const int32_t *__restrict__ ids, int P, int E, int BM,
                                                       int cap, int32_t *__restrict__ sorted_ids,
                                                       int32_t *__restrict__ block_expert,
                                                       int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
                                                       int32_t *__restrict__ total_padded) {
-  extern __shared__ int32_t lds[];  // rowcnt [16][E], then start [E]
-  align_block_1024(ids, P, E, BM, cap, sorted_ids, block_expert, counts, offsets, total_padded, lds);
+  extern __shared__ int32_t lds[];  // rowcnt [16 RPW][E], then start [E]
+  align_block<RPW>(ids, P, E, BM, cap, sorted_ids, block_expert, counts, offsets, total_padded, lds);
 }
 
 hipError_t launch_align(const int32_t *ids, int T, int k, int E, int BM, int cap, int32_t *sorted_ids,
@@ -174,7 +177,12 @@ hipError_t launch_align(const int32_t *ids, int T, int k, int E, int BM, int cap
                         int32_t *hist, hipStream_t s) {
   const int P = T * k;
   if (P <= kChunk && E <= 512) {
-    hipLaunchKernelGGL(k_align_small, dim3(1), dim3(1024), 17 * E * sizeof(int32_t), s, ids, P, E, BM, cap,
+    hipLaunchKernelGGL(k_align_small<1>, dim3(1), dim3(1024), 17 * E * sizeof(int32_t), s, ids, P, E, BM, cap,
+                       sorted_ids, block_expert, counts, offsets, total_padded);
+    return hipGetLastError();
+  }
+  if (P <= 4 * kChunk && E <= 256) {
+    hipLaunchKernelGGL(k_align_small<4>, dim3(1), dim3(1024), 65 * E * sizeof(int32_t), s, ids, P, E, BM, cap,
                        sorted_ids, block_expert, counts, offsets, total_padded);
     return hipGetLastError();
   }

@@ -122,7 +122,7 @@ __global__ __launch_bounds__(1024) void k_topk_align(const float *__restrict__ p
   __syncthreads();
   if (wave < T) select_topk<NS, true>(lg[wave], E, k, renormalize, wave, ids, wts, picks);
   __syncthreads();
-  align_block_1024(picks, T * k, E, BM, cap, sorted_ids, block_expert, counts, offsets, total_padded, align_lds);
+  align_block<1>(picks, T * k, E, BM, cap, sorted_ids, block_expert, counts, offsets, total_padded, align_lds);
 }
 
 template <int KSMAX>

@@ -143,45 +143,60 @@ __device__ __forceinline__ void select_topk(const float *lg, int E, int k, int r
   if (lane < k) wts[(size_t)t * k + lane] = expf(mine - top) / z;
 }
 
-// Stable counting sort of P <= 1024 pairs (ids[f], f < P) over E <= 512 experts by one
+// Stable counting sort of P <= 1024 * RPW pairs (ids[f], f < P) over E experts by one
 // workgroup of exactly 1024 threads: histogram, scan, sentinels and the stable scatter.
-// Wave w owns row w (pairs [64w, 64w+64)); thread x owns expert x in the scan.
-// lds: 17*E int32 of dynamic LDS (rowcnt [16][E], then start [E]).
-__device__ __forceinline__ void align_block_1024(const int32_t *__restrict__ ids, int P, int E, int BM, int cap,
-                                                 int32_t *__restrict__ sorted_ids, int32_t *__restrict__ block_expert,
-                                                 int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
-                                                 int32_t *__restrict__ total_padded, int32_t *lds) {
+// The pairs form 16 * RPW rows of 64; wave w owns rows [RPW w, RPW w + RPW) and ranks each
+// pair among the equal ids of its row (ballot match masks); thread x owns expert x in the
+// scan (E <= 1024).  lds: (16 * RPW + 1) * E int32 of dynamic LDS (rowcnt [16 RPW][E], then
+// start [E]).
+template <int RPW>
+__device__ __forceinline__ void align_block(const int32_t *__restrict__ ids, int P, int E, int BM, int cap,
+                                            int32_t *__restrict__ sorted_ids, int32_t *__restrict__ block_expert,
+                                            int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+                                            int32_t *__restrict__ total_padded, int32_t *lds) {
+  constexpr int NR = 16 * RPW;  // rows of 64 pairs
   int32_t *rowcnt = lds;
-  int32_t *start_of = lds + 16 * E;
+  int32_t *start_of = lds + NR * E;
   __shared__ int32_t wsum[16];
   const int lane = lane_id(), wave = threadIdx.x >> 6;
-  const int f = wave * 64 + lane;
-  int e = f < P ? ids[f] : -1;  // in flight while the counters are cleared
-  for (int i = threadIdx.x; i < 16 * E; i += blockDim.x) rowcnt[i] = 0;
+  int e[RPW];
+#pragma unroll
+  for (int q = 0; q < RPW; q++) {  // in flight while the counters are cleared
+    const int f = (RPW * wave + q) * 64 + lane;
+    e[q] = f < P ? ids[f] : -1;
+  }
+  for (int i = threadIdx.x; i < NR * E; i += blockDim.x) rowcnt[i] = 0;
   __syncthreads();
   int nbits = 0;
   while ((1 << nbits) < E) nbits++;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  if (e < 0 || e >= E) e = -1;
-  uint64_t peers = __ballot(e >= 0);
-  for (int bit = 0; bit < nbits; bit++) {
-    const uint64_t m = __ballot(e >= 0 && ((e >> bit) & 1));
-    peers &= ((e >> bit) & 1) ? m : ~m;
+  int rank[RPW];
+#pragma unroll
+  for (int q = 0; q < RPW; q++) {
+    if (e[q] < 0 || e[q] >= E) e[q] = -1;
+    uint64_t peers = __ballot(e[q] >= 0);
+    for (int bit = 0; bit < nbits; bit++) {
+      const uint64_t m = __ballot(e[q] >= 0 && ((e[q] >> bit) & 1));
+      peers &= ((e[q] >> bit) & 1) ? m : ~m;
+    }
+    rank[q] = __popcll(peers & below);
+    if (e[q] >= 0 && rank[q] == 0) rowcnt[(RPW * wave + q) * E + e[q]] = __popcll(peers);
   }
-  const int rank = __popcll(peers & below);
-  if (e >= 0 && rank == 0) rowcnt[wave * E + e] = __popcll(peers);
   __syncthreads();
-  // per expert: exclusive prefix over the 16 rows and the total count
+  // per expert: exclusive prefix over the rows and the total count
   int run = 0;
   const int x = threadIdx.x;
   if (x < E) {
-    int v[16];  // all 16 reads before the writes
 #pragma unroll
-    for (int rr = 0; rr < 16; rr++) v[rr] = rowcnt[rr * E + x];
+    for (int r0 = 0; r0 < NR; r0 += 16) {
+      int v[16];  // 16 reads before their writes
 #pragma unroll
-    for (int rr = 0; rr < 16; rr++) {
-      rowcnt[rr * E + x] = run;
-      run += v[rr];
+      for (int rr = 0; rr < 16; rr++) v[rr] = rowcnt[(r0 + rr) * E + x];
+#pragma unroll
+      for (int rr = 0; rr < 16; rr++) {
+        rowcnt[(r0 + rr) * E + x] = run;
+        run += v[rr];
+      }
     }
     counts[x] = run;
   }
@@ -213,7 +228,11 @@ __device__ __forceinline__ void align_block_1024(const int32_t *__restrict__ ids
   for (int b = total / BM + x; b < cap / BM; b += blockDim.x) block_expert[b] = -1;
   for (int p = total + x; p < cap; p += blockDim.x) sorted_ids[p] = P;
   __syncthreads();
-  if (e >= 0) sorted_ids[start_of[e] + rowcnt[wave * E + e] + rank] = f;
+#pragma unroll
+  for (int q = 0; q < RPW; q++) {
+    const int row = RPW * wave + q;
+    if (e[q] >= 0) sorted_ids[start_of[e[q]] + rowcnt[row * E + e[q]] + rank[q]] = row * 64 + lane;
+  }
 }
 
 }  // namespace qmoe

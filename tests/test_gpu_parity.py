@@ -147,6 +147,10 @@ def test_route_is_deterministic():
     (4096, 8, 256, 32, "rand"), (130, 8, 1000, 16, "rand"), (3000, 4, 7, 128, "rand"), (1, 1, 1, 16, "rand"),
     (500, 8, 256, 16, "one_expert"), (257, 3, 256, 256, "two_experts"), (8192, 8, 256, 16, "zipf"),
     (8192, 8, 256, 128, "zipf"), (100, 2, 600, 128, "rand"), (4096, 8, 256, 128, "one_expert"),
+    # one workgroup with four rows of 64 pairs per wave (1024 < T*k <= 4096, E <= 256), and
+    # the sizes just past it
+    (256, 8, 256, 16, "rand"), (512, 8, 256, 64, "zipf"), (129, 8, 256, 16, "rand"), (300, 8, 200, 128, "one_expert"),
+    (1000, 4, 3, 32, "two_experts"), (513, 8, 256, 16, "rand"), (250, 8, 257, 16, "rand"),
 ])
 def test_align_is_bit_exact(T, k, E, bm, kind):
     if kind == "rand":
