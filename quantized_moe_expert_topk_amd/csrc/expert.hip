@@ -206,12 +206,15 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
   }
   constexpr int RB = STAGE ? 4 * COUNT * SP : 16;  // staged scale bytes per lane (16 lanes per tile)
   constexpr int SQ = RB / 16;
-  uint4 stg[SQ > 0 ? SQ : 1];
+  static_assert(NT % 4 == 0, "whole tiles per 16-lane group when staging scale runs");
+  constexpr int TPG = NT / 4;  // tiles whose scale runs one 16-lane group stages
+  uint4 stg[TPG][SQ > 0 ? SQ : 1];
   if constexpr (STAGE && SQ > 0) {
-    {  // lanes 16t..16t+15 fetch tile t's run
-      const uint32_t run = (rows[(lane >> 4) % NT] & ~15u) * (K / 32) * SP + ((b_k0 + kw0) / 32) * 16 * SP;
 #pragma unroll
-      for (int q = 0; q < SQ; q++) stg[q] = buf_load16(m.scales, run + r * RB + 16 * q);
+    for (int u = 0; u < TPG; u++) {  // lanes 16t..16t+15 fetch the runs of tiles t, t + 4, ...
+      const uint32_t run = (rows[(lane >> 4) + 4 * u] & ~15u) * (K / 32) * SP + ((b_k0 + kw0) / 32) * 16 * SP;
+#pragma unroll
+      for (int q = 0; q < SQ; q++) stg[u][q] = buf_load16(m.scales, run + r * RB + 16 * q);
     }
   }
 #pragma unroll
@@ -282,7 +285,9 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
         {
           if (i0 == 0) {  // the first group's weight loads are in flight by now
 #pragma unroll
-            for (int q = 0; q < SQ; q++) *reinterpret_cast<uint4 *>(lsc + lane * RB + 16 * q) = stg[q];
+            for (int u = 0; u < TPG; u++)
+#pragma unroll
+              for (int q = 0; q < SQ; q++) *reinterpret_cast<uint4 *>(lsc + (lane + 64 * u) * RB + 16 * q) = stg[u][q];
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -413,12 +418,15 @@ __device__ __forceinline__ void mma_run_mx(const ActMX &A, uint32_t a_q, uint32_
   const int lane = lane_id(), r = lane & 15;
   constexpr int RB = 4 * COUNT;  // staged scale bytes per lane (one e8m0 per 32 K)
   constexpr int SQ = RB / 16;
-  uint4 stg[SQ > 0 ? SQ : 1];
+  static_assert(NT % 4 == 0, "whole tiles per 16-lane group when staging scale runs");
+  constexpr int TPG = NT / 4;  // tiles whose scale runs one 16-lane group stages
+  uint4 stg[TPG][SQ > 0 ? SQ : 1];
   if constexpr (SQ > 0) {
-    {
-      const uint32_t run = (rows[(lane >> 4) % NT] & ~15u) * (K / 32) + ((b_k0 + kw0) / 32) * 16;
 #pragma unroll
-      for (int q = 0; q < SQ; q++) stg[q] = buf_load16(m.scales, run + r * RB + 16 * q);
+    for (int u = 0; u < TPG; u++) {  // lanes 16t..16t+15 fetch the runs of tiles t, t + 4, ...
+      const uint32_t run = (rows[(lane >> 4) + 4 * u] & ~15u) * (K / 32) + ((b_k0 + kw0) / 32) * 16;
+#pragma unroll
+      for (int q = 0; q < SQ; q++) stg[u][q] = buf_load16(m.scales, run + r * RB + 16 * q);
     }
   }
   const bool asal = ((A.K / 32) % 4 == 0) && ((kw0 / 32) % 4 == 0);
@@ -457,7 +465,9 @@ __device__ __forceinline__ void mma_run_mx(const ActMX &A, uint32_t a_q, uint32_
       {
         if (i0 == 0) {
 #pragma unroll
-          for (int q = 0; q < SQ; q++) *reinterpret_cast<uint4 *>(lsc + lane * RB + 16 * q) = stg[q];
+          for (int u = 0; u < TPG; u++)
+#pragma unroll
+            for (int q = 0; q < SQ; q++) *reinterpret_cast<uint4 *>(lsc + (lane + 64 * u) * RB + 16 * q) = stg[u][q];
           __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
           __builtin_amdgcn_wave_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -521,26 +531,32 @@ __global__ __launch_bounds__(256) void k_act_mx8(const uint16_t *__restrict__ x,
 
 // ---------------------------------------------------------------------------- gate_up
 
-// Workgroup = 4 waves on one 16-row block and GCOLS slice columns [c0, c0+GCOLS): tiles
+// Workgroup = KW waves on one 16-row block and GC slice columns [c0, c0+GC): tiles
 // 0..GT-1 are gate rows lo+c0+16t+[0,16), tiles GT..2GT-1 the matching up rows I+....  The
 // first kwaves waves split K into contiguous ranges; their partial sums are added in wave
-// order through LDS, then wave t < GT applies the SwiGLU epilogue of tile t.
-constexpr int GCOLS = 32;
-constexpr int GT = GCOLS / 16;
+// order through LDS, then wave t < GT applies the SwiGLU epilogue of tile t.  Every column
+// group of a row block reads the block's activation rows again.  Where those reads rival the
+// weight bytes (MXFP4 with several pairs per expert: an e4m3 activation pair per 4-bit
+// weight, re-read by 32 column groups at Il = 1024), GC = 64 halves them; its 8 tiles run at
+// 2 waves per SIMD (195 VGPRs).  Measured on MI355X, DeepSeek-V4-Flash-shaped layer, slice
+// 1024: T = 256 gate_up 232 -> 221 us; at T = 16 the halved workgroup count cost 1.7 us, so
+// the launcher takes GC = 64 only from 4 pairs per expert on average.
 constexpr int kMinWaves = 3;  // waves per SIMD the expert kernels are compiled for
 
 // KW = waves per workgroup, all splitting K: 4, or 8 when few pairs leave most of the chip
 // idle (each wave then covers half the K range, one round trip fewer).
-template <int FMT, int COUNT, int KW>
-__global__ __launch_bounds__(64 * KW, kMinWaves) void k_gate_up(GateUpArgs a) {
+template <int FMT, int COUNT, int KW, int GC = 32>
+__global__ __launch_bounds__(64 * KW, GC == 64 ? 2 : kMinWaves) void k_gate_up(GateUpArgs a) {
+  constexpr int GT = GC / 16;
+  static_assert(GT <= KW, "one wave per gate tile in the epilogue");
   __shared__ float red[KW][2 * GT][4][64];  // [wave][tile][j][lane]
-  __shared__ float hbuf[16][GCOLS + 1];      // MXFP4: the block's h before the plane split
-  // FP4: per wave, the scale bytes of the workgroup's 2*GCOLS weight rows over one run
-  __shared__ __attribute__((aligned(16))) uint8_t lsc[(FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_MXFP4_E8M0 || FMT == MOE_FMT_Q4_0) ? KW * 2 * GCOLS * (128 * COUNT / (FMT == MOE_FMT_MXFP4_E8M0 ? 32 : 16)) : 16];
+  __shared__ float hbuf[16][GC + 1];         // MXFP4: the block's h before the plane split
+  // FP4: per wave, the scale bytes of the workgroup's 2*GC weight rows over one run
+  __shared__ __attribute__((aligned(16))) uint8_t lsc[(FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_MXFP4_E8M0 || FMT == MOE_FMT_Q4_0) ? KW * 2 * GC * (128 * COUNT / (FMT == MOE_FMT_MXFP4_E8M0 ? 32 : 16)) : 16];
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int sb = a.cols_fastest ? blockIdx.y : blockIdx.x;
-  const int c0 = (a.cols_fastest ? blockIdx.x : blockIdx.y) * GCOLS;
+  const int c0 = (a.cols_fastest ? blockIdx.x : blockIdx.y) * GC;
   const bool is_shared = sb >= a.n_routed_sub;
   int p0, e, tok;
   const uint8_t *codes;
@@ -588,7 +604,7 @@ __global__ __launch_bounds__(64 * KW, kMinWaves) void k_gate_up(GateUpArgs a) {
   if constexpr (FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_MXFP4_E8M0 || FMT == MOE_FMT_Q4_0) {
     constexpr int sdiv = FMT == MOE_FMT_MXFP4_E8M0 ? 32 : 16;  // elements per scale byte
     constexpr int RB = 128 * COUNT / sdiv;
-    if (RB % 16 == 0) wsc = &lsc[wave * 2 * GCOLS * RB];
+    if (RB % 16 == 0) wsc = &lsc[wave * 2 * GC * RB];
   }
   f32x4_t acc[2 * GT];
 #pragma unroll
@@ -638,21 +654,24 @@ __global__ __launch_bounds__(64 * KW, kMinWaves) void k_gate_up(GateUpArgs a) {
     }
   }
   if constexpr (FMT == MOE_FMT_MXFP4_E8M0) {
-    // h rows of this block, columns [c0, c0 + 32) = one e8m0 block: 16 lanes per row
+    // h rows of this block, each 32-column block of [c0, c0 + GC) one e8m0 block: 16 lanes per
+    // (row, block), whole waves per block (a block past the slice is skipped by whole rows)
     __syncthreads();
-    if (threadIdx.x >= 256) return;  // waves 4.. (KW = 8) have no rows here
-    const int row = threadIdx.x >> 4, cp = (threadIdx.x & 15) * 2;
-    const float v[2] = {hbuf[row][cp], hbuf[row][cp + 1]};
-    uint32_t qh[1], ql[1], s1, s2;
-    mx8_split<2>(v, [](float x) { return row16_max(x); }, qh, ql, s1, s2);
-    const size_t Il = (size_t)a.Il, hplane = (size_t)a.h_rows * Il, splane = (size_t)a.h_rows * (Il / 32);
-    const size_t o = (size_t)(p0 + row) * Il + c0 + cp;
-    *reinterpret_cast<uint16_t *>(a.hq + o) = (uint16_t)qh[0];
-    *reinterpret_cast<uint16_t *>(a.hq + hplane + o) = (uint16_t)ql[0];
-    if ((threadIdx.x & 15) == 0) {
-      const size_t so = (size_t)(p0 + row) * (Il / 32) + c0 / 32;
-      a.hs[so] = (uint8_t)s1;
-      a.hs[splane + so] = (uint8_t)s2;
+    for (int item = threadIdx.x; item < 16 * 16 * (GC / 32); item += 64 * KW) {
+      const int blk = item >> 8, row = (item >> 4) & 15, cp = 32 * blk + (item & 15) * 2;
+      if (c0 + 32 * blk >= a.Il) break;  // uniform over the wave
+      const float v[2] = {hbuf[row][cp], hbuf[row][cp + 1]};
+      uint32_t qh[1], ql[1], s1, s2;
+      mx8_split<2>(v, [](float x) { return row16_max(x); }, qh, ql, s1, s2);
+      const size_t Il = (size_t)a.Il, hplane = (size_t)a.h_rows * Il, splane = (size_t)a.h_rows * (Il / 32);
+      const size_t o = (size_t)(p0 + row) * Il + c0 + cp;
+      *reinterpret_cast<uint16_t *>(a.hq + o) = (uint16_t)qh[0];
+      *reinterpret_cast<uint16_t *>(a.hq + hplane + o) = (uint16_t)ql[0];
+      if ((item & 15) == 0) {
+        const size_t so = (size_t)(p0 + row) * (Il / 32) + (c0 + 32 * blk) / 32;
+        a.hs[so] = (uint8_t)s1;
+        a.hs[splane + so] = (uint8_t)s2;
+      }
     }
   }
 }
@@ -830,36 +849,52 @@ static int count_class(int fmt, int steps) {
   return fmt == MOE_FMT_NVFP4 ? c : (c < 4 ? c : 4);
 }
 
-template <int FMT, int KW>
+template <int FMT, int KW, int GC>
 static void launch_gate_up_kw(const GateUpArgs &a, dim3 grid, hipStream_t s) {
   const dim3 block(64 * KW);
   switch (count_class(FMT, a.ksteps)) {
-    case 1: hipLaunchKernelGGL((k_gate_up<FMT, 1, KW>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_gate_up<FMT, 2, KW>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_gate_up<FMT, 4, KW>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_gate_up<FMT, 1, KW, GC>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_gate_up<FMT, 2, KW, GC>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_gate_up<FMT, 4, KW, GC>), grid, block, 0, s, a); break;
     default:
-      if constexpr (FMT == MOE_FMT_NVFP4) hipLaunchKernelGGL((k_gate_up<FMT, 8, KW>), grid, block, 0, s, a);
+      if constexpr (FMT == MOE_FMT_NVFP4) hipLaunchKernelGGL((k_gate_up<FMT, 8, KW, GC>), grid, block, 0, s, a);
       break;
   }
 }
 
+template <int FMT, int GC>
+static void launch_gate_up_gc(const GateUpArgs &a, int n_shared_sub, hipStream_t s) {
+  const int nsub = a.n_routed_sub + n_shared_sub, ncol = (a.Il + GC - 1) / GC;
+  const dim3 grid = a.cols_fastest ? dim3(ncol, nsub) : dim3(nsub, ncol);
+  if constexpr (GC == 32) {
+    if (a.kwaves > 4) {
+      launch_gate_up_kw<FMT, 8, GC>(a, grid, s);
+      return;
+    }
+  }
+  launch_gate_up_kw<FMT, 4, GC>(a, grid, s);
+}
+
 template <int FMT>
-static void launch_gate_up_fmt(const GateUpArgs &a, dim3 grid, hipStream_t s) {
-  if (a.kwaves > 4)
-    launch_gate_up_kw<FMT, 8>(a, grid, s);
-  else
-    launch_gate_up_kw<FMT, 4>(a, grid, s);
+static void launch_gate_up_grid(const GateUpArgs &a, int n_shared_sub, hipStream_t s) {
+  // 64 slice columns per workgroup for MXFP4 with at least 4 pairs per expert on average
+  // (the 8-wave K split, chosen only for few pairs, keeps 32)
+  if constexpr (FMT == MOE_FMT_MXFP4_E8M0) {
+    if ((long long)a.T * a.k >= 4LL * a.E && a.kwaves <= 4) {
+      launch_gate_up_gc<FMT, 64>(a, n_shared_sub, s);
+      return;
+    }
+  }
+  launch_gate_up_gc<FMT, 32>(a, n_shared_sub, s);
 }
 
 hipError_t launch_gate_up(int fmt, const GateUpArgs &a, int n_shared_sub, hipStream_t s) {
-  const int nsub = a.n_routed_sub + n_shared_sub, ncol = (a.Il + GCOLS - 1) / GCOLS;
-  const dim3 grid = a.cols_fastest ? dim3(ncol, nsub) : dim3(nsub, ncol);
   switch (fmt) {
-    case MOE_FMT_NVFP4: launch_gate_up_fmt<MOE_FMT_NVFP4>(a, grid, s); break;
-    case MOE_FMT_MXFP4_E8M0: launch_gate_up_fmt<MOE_FMT_MXFP4_E8M0>(a, grid, s); break;
-    case MOE_FMT_BF16: launch_gate_up_fmt<MOE_FMT_BF16>(a, grid, s); break;
-    case MOE_FMT_Q4_0: launch_gate_up_fmt<MOE_FMT_Q4_0>(a, grid, s); break;
-    default: launch_gate_up_fmt<MOE_FMT_FP8_BLOCK128>(a, grid, s); break;
+    case MOE_FMT_NVFP4: launch_gate_up_grid<MOE_FMT_NVFP4>(a, n_shared_sub, s); break;
+    case MOE_FMT_MXFP4_E8M0: launch_gate_up_grid<MOE_FMT_MXFP4_E8M0>(a, n_shared_sub, s); break;
+    case MOE_FMT_BF16: launch_gate_up_grid<MOE_FMT_BF16>(a, n_shared_sub, s); break;
+    case MOE_FMT_Q4_0: launch_gate_up_grid<MOE_FMT_Q4_0>(a, n_shared_sub, s); break;
+    default: launch_gate_up_grid<MOE_FMT_FP8_BLOCK128>(a, n_shared_sub, s); break;
   }
   return hipGetLastError();
 }

@@ -384,6 +384,9 @@ FORWARD_CASES = [(1, 16, (0, 128)), (1, 16, (0, 64)), (1, 16, (64, 128)),
                  (5, 1, (0, 1024)), (5, 16, (0, 1024)), (5, 16, (1024, 2048)),
                  # MXFP4 slices off the 128-wide chunk grid: a masked K tail, unaligned scale spans
                  (5, 16, (0, 96)), (5, 16, (32, 160)), (5, 1, (992, 2048)),
+                 # MXFP4 with 64 slice columns per gate_up workgroup (>= 4 pairs per expert), a
+                 # last column group half past the slice
+                 (5, 256, (0, 96)), (5, 256, (32, 160)), (5, 256, (1024, 2048)),
                  # bf16 stacked experts (issue #62 "Suggested staging" item 1)
                  (6, 1, (0, 256)), (6, 64, (0, 256)), (6, 16, (32, 160)), (6, 8, (0, 512)),
                  # q4_0 experts (issue #62 "Suggested staging" item 3), no shared expert
@@ -631,7 +634,7 @@ def test_full_layer_matches_oracle(cid, T, sl):
 @pytest.mark.parametrize("cid,T,cuts,bm", [
     (1, 16, (0, 64, 128), None), (2, 64, (0, 256, 512), None), (4, 64, (0, 256, 512), None),
     (2, 8, (0, 128, 384, 512), None), (5, 16, (0, 96, 1024, 2048), None), (7, 16, (0, 128, 384, 512), None),
-    (7, 16, (0, 32, 96, 288, 512), None),
+    (7, 16, (0, 32, 96, 288, 512), None), (5, 256, (0, 96, 1024, 2048), None),
     # the prefill GEMMs (align blocks of 128): full-size Zipf prefill, fp8-block at T = 4096, and
     # bf16 cut at 96 and 352 (slices of 96, 256 and 160: K tails inside a 64-wide stage)
     (3, 8192, (0, 256, 512), 128), (4, 4096, (0, 256, 512), 128), (6, 8192, (0, 96, 352, 512), 128),
