@@ -257,7 +257,7 @@ def run(args, plan):
 
 def time_point(args, qm, torch, cfg, inst, xs, T, lo, hi, R):
     Il = hi - lo
-    layers, graphs, bytes_step, flops_step, gu_bytes, gu_flops = [], [], [], [], [], []
+    layers, bytes_step, flops_step, gu_bytes, gu_flops = [], [], [], [], []
     for r in range(R):
         I_ = inst[r]
         for b in range(BATCHES):
@@ -275,30 +275,27 @@ def time_point(args, qm, torch, cfg, inst, xs, T, lo, hi, R):
             flops_step.append(2 * pairs * 3 * Il * cfg.H + 2 * T * cfg.E * cfg.H)
             gu_bytes.append(active * gate_up_slice_bytes(cfg.fmt, cfg.H, Il) + T * cfg.H * 2 + pairs * Il * 2)
             gu_flops.append(2 * pairs * 2 * Il * cfg.H)
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                L(x)
             layers.append((L, x))
-            graphs.append(g)
-    n = len(graphs)
-    # one graph over the whole rotation (n steps back to back) so that graph launches do
-    # not gap the steps; K steps = K // n rotations, then the first K % n single steps
-    g_all = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_all):
-        for L, x in layers:
-            L(x)
+    n = len(layers)
 
-    def run_steps(k):
-        for _ in range(k // n):
-            g_all.replay()
-        for i in range(k % n):
-            graphs[i].replay()
+    def capture(k):  # one graph of k steps back to back, cycling through the rotation
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(k):
+                L, x = layers[i % n]
+                L(x)
+        return g
 
-    run_steps(args.warmup)
+    # exactly W warm-up steps, then exactly K timed steps, each as one graph so that graph
+    # launches do not gap the steps; the rotation graph times the spread below
+    g_all = capture(n)
+    if args.warmup:
+        capture(args.warmup).replay()
+    g_timed = capture(args.steps)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    run_steps(args.steps)
+    g_timed.replay()
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
@@ -354,7 +351,7 @@ def time_point(args, qm, torch, cfg, inst, xs, T, lo, hi, R):
               alg_bytes_per_step=avg_bytes, alg_flops_per_step=avg_flops, roofline=roof,
               instances_rotated=R, batches_rotated=BATCHES)
     log(json.dumps(pt))
-    del layers, graphs, gk, g_all
+    del layers, gk, g_all, g_timed
     torch.cuda.synchronize()
     return pt
 
