@@ -90,6 +90,21 @@ bool cols_fastest(int T, int k, int Il, int n_sub) {
   return Il >= 512 && (long long)T * k >= 512 && n_sub <= 65535;
 }
 
+// Streaming kernels load the expert weights with the non-temporal hint from 128 pairs on: the
+// weights are read once, and the hint keeps them from evicting the reused activation rows
+// (measured on MI355X, T = 64: fp8-block step 90.6 -> 82.4 us, bf16 151.9 -> 138.7 us; the
+// DeepSeek-V4-Flash-shaped MXFP4 layer at T = 256 392 -> 378 us).  With few pairs the loads
+// are latency-bound and the hint measured slower (T = 1: 24.5 -> 25.6 us).  gate_up takes it
+// only for MXFP4 and bf16 weights (NVFP4 and q4_0 gate_up measured 0.7-1.5 us slower with it);
+// down only where one slice row of its weight holds at least 256 bytes (4-bit codes over a
+// 256-wide slice measured 1.5 us slower with it, over a 512-wide slice 2-5 us faster).
+bool nt_weights(int T, int k) { return (long long)T * k >= 128; }
+
+bool nt_down_weights(int fmt, int T, int k, int Il) {
+  const int bits = fmt == MOE_FMT_BF16 ? 16 : fmt == MOE_FMT_FP8_BLOCK128 ? 8 : 4;
+  return nt_weights(T, k) && (long long)Il * bits >= 256 * 8;
+}
+
 // gate_up K split: H = 128 * kwaves * ksteps with kwaves <= 4 and ksteps <= 8 (kwaves as
 // large as possible).  Returns false if H has no such factorisation.
 bool gate_up_ksplit(int H, int *kwaves, int *ksteps) {
@@ -322,6 +337,7 @@ qmoe::GateUpArgs gate_up_args(const moe_bank *routed, const moe_bank *shared, co
     a.ksteps = routed->H / 1024;
   }
   a.cols_fastest = cols_fastest(T, k, p.Il, p.n_routed_sub + p.n_shared_sub);
+  a.nt_weights = nt_weights(T, k);
   char *ws = static_cast<char *>(workspace);
   a.h = reinterpret_cast<uint16_t *>(ws);
   a.h_rows = p.h_rows;
@@ -360,6 +376,7 @@ qmoe::DownArgs down_args(const moe_bank *routed, const moe_bank *shared, int T, 
   a.lo = lo;
   a.Il = p.Il;
   a.cols_fastest = cols_fastest(T, k, p.Il, p.n_routed_sub + p.n_shared_sub);
+  a.nt_weights = nt_down_weights(routed->fmt, T, k, p.Il);
   a.Y = reinterpret_cast<float *>(static_cast<char *>(workspace) + p.y_off);
   return a;
 }

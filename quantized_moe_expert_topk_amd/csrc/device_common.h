@@ -139,6 +139,13 @@ __device__ __forceinline__ uint32_t buf_load1(rsrc_t r, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
 }
 
+// NT: the non-temporal hint, for bytes read once (streamed expert weights), so that they do
+// not push reused lines (activation rows, scales) out of the caches.
+template <bool NT>
+__device__ __forceinline__ uint4 buf_load16w(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, NT ? 2 : 0));
+}
+
 __device__ __forceinline__ uint2 buf_load8(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
 }

@@ -184,7 +184,8 @@ __device__ __forceinline__ uint32_t scale_tile_off(uint32_t row, uint32_t K) {
 //              (lsc unused) load each lane's SP scale bytes per step and tile.  Q4_0 stages
 //              the same way (its 2 scale bytes per 32 elements give NVFP4's run length) and
 //              reads back the 8 bytes of its row per step.
-template <int FMT, int NT, int COUNT, bool QMASK = false>
+//   NTW:       weight code loads carry the non-temporal hint
+template <int FMT, int NT, int COUNT, bool QMASK = false, bool NTW = false>
 __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FMT> &m, const uint32_t (&rows)[NT],
                                         int b_k0, int kw0, int kvalid, int g, f32x4_t (&acc)[NT],
                                         uint8_t *lsc = nullptr, int kphase = 0) {
@@ -235,7 +236,7 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
         for (int q = 0; q < 4; q++) ar[ii].q[q] = buf_load16(ra, a_row + k * 2 + 16 * q);
         const uint32_t pc = (uint32_t)(b_k0 + k) / 32;
 #pragma unroll
-        for (int t = 0; t < NT; t++) c0[ii][t] = buf_load16(m.codes, cb[t] + pc * 256);
+        for (int t = 0; t < NT; t++) c0[ii][t] = buf_load16w<NTW>(m.codes, cb[t] + pc * 256);
         if constexpr (SQ == 0) {
 #pragma unroll
           for (int t = 0; t < NT; t++)
@@ -251,7 +252,7 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
         const uint32_t st = (uint32_t)(b_k0 + kc) / 128;
 #pragma unroll
         for (int t = 0; t < NT; t++) {
-          c0[ii][t] = buf_load16(m.codes, cb[t] + (4 * st + g) * 256);
+          c0[ii][t] = buf_load16w<NTW>(m.codes, cb[t] + (4 * st + g) * 256);
           if constexpr (SQ == 0) qsv[ii][t] = buf_load8(m.scales, sb[t] + st * 128);
         }
       } else if constexpr (BF16) {
@@ -261,10 +262,10 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
         const uint32_t pc = (uint32_t)(b_k0 + kc) / 8 + g;
 #pragma unroll
         for (int t = 0; t < NT; t++) {
-          c0[ii][t] = buf_load16(m.codes, cb[t] + pc * 256);
-          c1[ii][t] = buf_load16(m.codes, cb[t] + (pc + 4) * 256);
-          c2[ii][t] = buf_load16(m.codes, cb[t] + (pc + 8) * 256);
-          c3[ii][t] = buf_load16(m.codes, cb[t] + (pc + 12) * 256);
+          c0[ii][t] = buf_load16w<NTW>(m.codes, cb[t] + pc * 256);
+          c1[ii][t] = buf_load16w<NTW>(m.codes, cb[t] + (pc + 4) * 256);
+          c2[ii][t] = buf_load16w<NTW>(m.codes, cb[t] + (pc + 8) * 256);
+          c3[ii][t] = buf_load16w<NTW>(m.codes, cb[t] + (pc + 12) * 256);
         }
       } else {
         const int kc = kw0 + (128 * i < kvalid ? 128 * i : 0);  // the step
@@ -274,8 +275,8 @@ __device__ __forceinline__ void mma_run(rsrc_t ra, uint32_t a_row, const WMat<FM
         const uint32_t pc = (uint32_t)(b_k0 + kc) / 16 + g;
 #pragma unroll
         for (int t = 0; t < NT; t++) {
-          c0[ii][t] = buf_load16(m.codes, cb[t] + pc * 256);
-          c1[ii][t] = buf_load16(m.codes, cb[t] + (pc + 4) * 256);
+          c0[ii][t] = buf_load16w<NTW>(m.codes, cb[t] + pc * 256);
+          c1[ii][t] = buf_load16w<NTW>(m.codes, cb[t] + (pc + 4) * 256);
           bs[ii][t] = buf_load_f32(m.scales, ((rows[t] / 128) * (K / 128) + (b_k0 + kw0 + 128 * i) / 128) * 4);
         }
       }
@@ -408,7 +409,7 @@ struct ActMX {
 //   a_q, a_s: byte offsets of this lane's row in the planes and in the scales (or
 //             0x80000000 for a padding row, which reads zeros without a memory request)
 //   lsc: as in mma_run (required when RB = 4 * COUNT is a multiple of 16)
-template <int NT, int COUNT>
+template <int NT, int COUNT, bool NTW = false>
 __device__ __forceinline__ void mma_run_mx(const ActMX &A, uint32_t a_q, uint32_t a_s,
                                            const WMat<MOE_FMT_MXFP4_E8M0> &m, const uint32_t (&rows)[NT],
                                            int b_k0, int kw0, int kvalid, int g, f32x4_t (&acc)[NT],
@@ -459,7 +460,7 @@ __device__ __forceinline__ void mma_run_mx(const ActMX &A, uint32_t a_q, uint32_
       const int kr = 128 * i + 32 * g;
       const uint32_t pc = (uint32_t)(b_k0 + kw0 + (kr < kvalid ? kr : 0)) / 32;
 #pragma unroll
-      for (int t = 0; t < NT; t++) c[ii][t] = buf_load16(m.codes, code_tile_off<FMT>(rows[t], K) + pc * 256);
+      for (int t = 0; t < NT; t++) c[ii][t] = buf_load16w<NTW>(m.codes, code_tile_off<FMT>(rows[t], K) + pc * 256);
     }
     if constexpr (SQ > 0) {  // B scale bytes from the wave's LDS region (staged once per run)
       {
@@ -545,7 +546,7 @@ constexpr int kMinWaves = 3;  // waves per SIMD the expert kernels are compiled 
 
 // KW = waves per workgroup, all splitting K: 4, or 8 when few pairs leave most of the chip
 // idle (each wave then covers half the K range, one round trip fewer).
-template <int FMT, int COUNT, int KW, int GC = 32>
+template <int FMT, int COUNT, int KW, int GC, bool NTW>
 __global__ __launch_bounds__(64 * KW, GC == 64 ? 2 : kMinWaves) void k_gate_up(GateUpArgs a) {
   constexpr int GT = GC / 16;
   static_assert(GT <= KW, "one wave per gate tile in the epilogue");
@@ -620,13 +621,13 @@ __global__ __launch_bounds__(64 * KW, GC == 64 ? 2 : kMinWaves) void k_gate_up(G
     const uint32_t as = tok >= 0 ? (uint32_t)tok * (H / 32) : 0x80000000u;
     if (wave < a.kwaves)
       for (int kk = 0; kk < kw; kk += 128 * COUNT)  // runs of COUNT steps; the tail is masked
-        mma_run_mx<2 * GT, COUNT>(A, aq, as, m, rows, 0, wave * kw + kk, kw - kk, g, acc, wsc);
+        mma_run_mx<2 * GT, COUNT, NTW>(A, aq, as, m, rows, 0, wave * kw + kk, kw - kk, g, acc, wsc);
   } else {
     const rsrc_t ra = make_rsrc(a.x, (uint32_t)a.T * H * 2);
     const uint32_t a_row = tok >= 0 ? (uint32_t)tok * H * 2 : 0x80000000u;
     if (wave < a.kwaves) {
       for (int kk = 0; kk < kw; kk += 128 * COUNT)
-        mma_run<FMT, 2 * GT, COUNT>(ra, a_row, m, rows, 0, wave * kw + kk, kw - kk, g, acc, wsc);
+        mma_run<FMT, 2 * GT, COUNT, false, NTW>(ra, a_row, m, rows, 0, wave * kw + kk, kw - kk, g, acc, wsc);
     }
   }
 #pragma unroll
@@ -682,7 +683,7 @@ __global__ __launch_bounds__(64 * KW, GC == 64 ? 2 : kMinWaves) void k_gate_up(G
 // tiles sharing one A fragment (a row block of h); K = the slice width Il.
 constexpr int DNT = 4;
 
-template <int FMT, int COUNT>
+template <int FMT, int COUNT, bool NTW>
 __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
   // FP4: per wave, the scale bytes of its 16*DNT weight rows over one run
   __shared__ __attribute__((aligned(16))) uint8_t lsc[(FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_MXFP4_E8M0 || FMT == MOE_FMT_Q4_0) ? 4 * 16 * DNT * (128 * COUNT / (FMT == MOE_FMT_MXFP4_E8M0 ? 32 : 16)) : 16];
@@ -758,7 +759,7 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
     const uint32_t aq = real ? (uint32_t)(p0 + r) * ul : 0x80000000u;
     const uint32_t as = real ? (uint32_t)(p0 + r) * (ul / 32) : 0x80000000u;
     for (int kw0 = 0; kw0 < Il; kw0 += 128 * COUNT)  // runs of COUNT steps; the tail is masked
-      mma_run_mx<DNT, COUNT>(A, aq, as, m, rows, a.lo, kw0, Il - kw0, g, acc, wsc);
+      mma_run_mx<DNT, COUNT, NTW>(A, aq, as, m, rows, a.lo, kw0, Il - kw0, g, acc, wsc);
   } else {
     const rsrc_t ra = make_rsrc(a.h, (uint32_t)a.h_rows * Il * 2);
     const uint32_t a_row = real ? (uint32_t)(p0 + r) * Il * 2 : 0x80000000u;
@@ -767,7 +768,7 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
     constexpr bool Q4 = FMT == MOE_FMT_Q4_0;
     const int kph = Q4 ? a.lo & 127 : 0;
     for (int kw0 = 0; kw0 < Il + kph; kw0 += 128 * COUNT)
-      mma_run<FMT, DNT, COUNT, Q4>(ra, a_row, m, rows, a.lo - kph, kw0, Il + kph - kw0, g, acc, wsc, kph);
+      mma_run<FMT, DNT, COUNT, Q4, NTW>(ra, a_row, m, rows, a.lo - kph, kw0, Il + kph - kw0, g, acc, wsc, kph);
   }
 #pragma unroll
   for (int j = 0; j < 4; j++) {
@@ -849,17 +850,30 @@ static int count_class(int fmt, int steps) {
   return fmt == MOE_FMT_NVFP4 ? c : (c < 4 ? c : 4);
 }
 
-template <int FMT, int KW, int GC>
-static void launch_gate_up_kw(const GateUpArgs &a, dim3 grid, hipStream_t s) {
+template <int FMT, int KW, int GC, bool NTW>
+static void launch_gate_up_nt(const GateUpArgs &a, dim3 grid, hipStream_t s) {
   const dim3 block(64 * KW);
   switch (count_class(FMT, a.ksteps)) {
-    case 1: hipLaunchKernelGGL((k_gate_up<FMT, 1, KW, GC>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_gate_up<FMT, 2, KW, GC>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_gate_up<FMT, 4, KW, GC>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_gate_up<FMT, 1, KW, GC, NTW>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_gate_up<FMT, 2, KW, GC, NTW>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_gate_up<FMT, 4, KW, GC, NTW>), grid, block, 0, s, a); break;
     default:
-      if constexpr (FMT == MOE_FMT_NVFP4) hipLaunchKernelGGL((k_gate_up<FMT, 8, KW, GC>), grid, block, 0, s, a);
+      if constexpr (FMT == MOE_FMT_NVFP4) hipLaunchKernelGGL((k_gate_up<FMT, 8, KW, GC, NTW>), grid, block, 0, s, a);
       break;
   }
+}
+
+template <int FMT, int KW, int GC>
+static void launch_gate_up_kw(const GateUpArgs &a, dim3 grid, hipStream_t s) {
+  // the non-temporal hint on weight loads only where it measured faster (gate_up: bf16 and
+  // MXFP4 weights, from 128 pairs)
+  if constexpr (FMT == MOE_FMT_MXFP4_E8M0 || FMT == MOE_FMT_BF16) {
+    if (a.nt_weights) {
+      launch_gate_up_nt<FMT, KW, GC, true>(a, grid, s);
+      return;
+    }
+  }
+  launch_gate_up_nt<FMT, KW, GC, false>(a, grid, s);
 }
 
 template <int FMT, int GC>
@@ -905,9 +919,18 @@ static void launch_down_fmt(const DownArgs &a, dim3 grid, hipStream_t s) {
   // Q4_0 steps start at multiples of 128 of the row, so a slice may touch one more
   const int kph = FMT == MOE_FMT_Q4_0 ? a.lo & 127 : 0;
   switch (count_class(MOE_FMT_FP8_BLOCK128, (a.Il + kph + 127) / 128)) {
-    case 1: hipLaunchKernelGGL((k_down<FMT, 1>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_down<FMT, 2>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_down<FMT, 4>), grid, dim3(256), 0, s, a); break;
+    case 1:
+      if (a.nt_weights) hipLaunchKernelGGL((k_down<FMT, 1, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((k_down<FMT, 1, false>), grid, dim3(256), 0, s, a);
+      break;
+    case 2:
+      if (a.nt_weights) hipLaunchKernelGGL((k_down<FMT, 2, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((k_down<FMT, 2, false>), grid, dim3(256), 0, s, a);
+      break;
+    default:
+      if (a.nt_weights) hipLaunchKernelGGL((k_down<FMT, 4, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((k_down<FMT, 4, false>), grid, dim3(256), 0, s, a);
+      break;
   }
 }
 

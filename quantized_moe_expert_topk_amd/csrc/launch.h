@@ -22,6 +22,7 @@ struct GateUpArgs {
   int lo, Il;
   int kwaves, ksteps;  // K split of gate_up: kwaves waves x ksteps steps of 128 (H = 128*kwaves*ksteps)
   int cols_fastest;    // streaming kernels: grid x is the column group (else the 16-row sub-block)
+  int nt_weights;      // streaming kernels: non-temporal weight loads (many pairs)
   uint16_t *h;  // [h_rows, Il] bf16 (NVFP4, fp8-block)
   int h_rows;   // cap + 16 * n_shared_sub
   // MXFP4: x and h as two e4m3 planes with e8m0 scales per 32 (plane 1 follows plane 0)
@@ -43,6 +44,7 @@ struct DownArgs {
   int block_m, cap, n_routed_sub;
   int lo, Il;
   int cols_fastest;  // as in GateUpArgs
+  int nt_weights;    // as in GateUpArgs
   float *Y;  // [T * k + T_shared, H] unweighted pair rows: fp32 (streaming kernels) or bf16 (prefill GEMMs)
 };
 
