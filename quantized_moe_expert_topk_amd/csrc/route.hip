@@ -155,16 +155,19 @@ static hipError_t launch_topk_ns(const float *part, int KS, int T, int E, const 
 
 // K splits for the router GEMM: enough workgroups to cover the chip at small T.
 // Large batches run the router on the LDS-tiled GEMM (128 tokens x 128 experts per
-// workgroup), small ones on k_router_partial; both split K until about 512 workgroups are in
-// flight (at most 16 splits): a workgroup's K loop is a chain of dependent load round trips,
-// so shorter ones finish sooner (T = 256, H = 4096: 2 -> 8 splits, step 409 -> 402 us).
+// workgroup), small ones on k_router_partial.  k_router_partial splits K until about 512
+// workgroups are in flight (at most 16 splits): a workgroup's K loop is a chain of dependent
+// load round trips, so shorter ones finish sooner (T = 256, H = 4096: 2 -> 8 splits, step
+// 409 -> 402 us).  The tiled GEMM splits until about 256 workgroups: every split adds T x E
+// fp32 partials that the top-k kernel reads back (E = 256: T = 8192 4 -> 2 splits, step
+// 646 -> 640 us; T = 4096 8 -> 4 splits, 269 -> 264 us).
 static bool router_tiled(int T) { return T >= 1024; }
 
 int router_ksplit(int T, int E, int H) {
   if (router_tiled(T)) {  // K ranges stay whole 64-wide stages
     const int base = ((T + 127) / 128) * ((E + 127) / 128);
     int ks = 1;
-    while (base * ks < 512 && ks < 8 && (H / 64) % (ks * 2) == 0) ks *= 2;
+    while (base * ks < 256 && ks < 8 && (H / 64) % (ks * 2) == 0) ks *= 2;
     return ks;
   }
   const int base = ((E + 63) / 64) * ((T + 15) / 16);
