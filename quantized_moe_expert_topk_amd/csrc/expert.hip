@@ -784,25 +784,25 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
 // ---------------------------------------------------------------------------- combine
 
 // out[t] = sum_j w[t*k + j] Y[t*k + j] + Y[T*k + t] (shared, weight 1), in this order, in
-// fp32.  Y rows are fp32 (streaming kernels) or bf16 (prefill GEMMs); a thread owns 4
-// consecutive columns (H % 128 == 0).
+// fp32.  Y rows are fp32 (streaming kernels, a thread owns 4 consecutive columns) or bf16
+// (prefill GEMMs, 8 columns: one 16-byte load per row); H % 128 == 0.
 template <bool YBF16>
 __global__ __launch_bounds__(256) void k_combine(const void *__restrict__ Yv, const float *__restrict__ w, int T,
                                                  int k, int H, int has_shared, void *__restrict__ out,
                                                  int out_bf16) {
+  constexpr int NC = YBF16 ? 8 : 4;  // columns per thread
   const int t = blockIdx.y;
-  const int n = (blockIdx.x * 256 + threadIdx.x) * 4;  // 4 columns per thread
+  const int n = (blockIdx.x * 256 + threadIdx.x) * NC;
   if (n >= H) return;
   const int nrows = k + (has_shared ? 1 : 0);  // the token's k pair rows, then its shared row
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float acc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; c++) acc[c] = 0.f;
   // rows in flight: 16 for the fp32 rows of the streaming kernels (k <= 15 plus the shared row
   // in one round trip, measured faster at decode), 8 for the bf16 rows of the prefill GEMMs
-  // (16 measured slower there)
   constexpr int NB = YBF16 ? 8 : 16;
   for (int j0 = 0; j0 < nrows; j0 += NB) {
-    // up to NB rows (and their weights) loaded before any is added (all in flight), then
-    // summed in row order
-    float v[NB][4], wj[NB];
+    float v[NB][NC], wj[NB];
 #pragma unroll
     for (int u = 0; u < NB; u++) {
       const int j = j0 + u;
@@ -810,17 +810,19 @@ __global__ __launch_bounds__(256) void k_combine(const void *__restrict__ Yv, co
       wj[u] = j < k ? w[row] : 1.f;  // row < T * k for routed rows
       if (j < nrows) {
         if constexpr (YBF16) {
-          const uint2 w = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(Yv) + row * H + n);
-          v[u][0] = __uint_as_float(w.x << 16);
-          v[u][1] = __uint_as_float(w.x & 0xFFFF0000u);
-          v[u][2] = __uint_as_float(w.y << 16);
-          v[u][3] = __uint_as_float(w.y & 0xFFFF0000u);
+          const uint4 q = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(Yv) + row * H + n);
+          const uint32_t d[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+          for (int c = 0; c < 4; c++) {
+            v[u][2 * c] = __uint_as_float(d[c] << 16);
+            v[u][2 * c + 1] = __uint_as_float(d[c] & 0xFFFF0000u);
+          }
         } else {
-          const float4 w = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(Yv) + row * H + n);
-          v[u][0] = w.x;
-          v[u][1] = w.y;
-          v[u][2] = w.z;
-          v[u][3] = w.w;
+          const float4 q = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(Yv) + row * H + n);
+          v[u][0] = q.x;
+          v[u][1] = q.y;
+          v[u][2] = q.z;
+          v[u][3] = q.w;
         }
       }
     }
@@ -828,15 +830,21 @@ __global__ __launch_bounds__(256) void k_combine(const void *__restrict__ Yv, co
     for (int u = 0; u < NB; u++)
       if (j0 + u < nrows)
 #pragma unroll
-        for (int c = 0; c < 4; c++) acc[c] += wj[u] * v[u][c];
+        for (int c = 0; c < NC; c++) acc[c] += wj[u] * v[u][c];
   }
   if (out_bf16) {
-    const uint2 pk = make_uint2((uint32_t)bf16_bits(acc[0]) | ((uint32_t)bf16_bits(acc[1]) << 16),
-                                (uint32_t)bf16_bits(acc[2]) | ((uint32_t)bf16_bits(acc[3]) << 16));
-    *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(out) + (size_t)t * H + n) = pk;
+    uint32_t pk[NC / 2];
+#pragma unroll
+    for (int c = 0; c < NC / 2; c++) pk[c] = (uint32_t)bf16_bits(acc[2 * c]) | ((uint32_t)bf16_bits(acc[2 * c + 1]) << 16);
+    uint16_t *o = reinterpret_cast<uint16_t *>(out) + (size_t)t * H + n;
+    if constexpr (NC == 8)
+      *reinterpret_cast<uint4 *>(o) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    else
+      *reinterpret_cast<uint2 *>(o) = make_uint2(pk[0], pk[1]);
   } else {
-    *reinterpret_cast<float4 *>(reinterpret_cast<float *>(out) + (size_t)t * H + n) =
-        make_float4(acc[0], acc[1], acc[2], acc[3]);
+    float *o = reinterpret_cast<float *>(out) + (size_t)t * H + n;
+#pragma unroll
+    for (int c = 0; c < NC; c += 4) *reinterpret_cast<float4 *>(o + c) = make_float4(acc[c], acc[c + 1], acc[c + 2], acc[c + 3]);
   }
 }
 
@@ -956,7 +964,7 @@ hipError_t launch_act_mx8(const uint16_t *x, int rows, int K, uint8_t *q, uint8_
 
 hipError_t launch_combine(const void *Y, bool y_bf16, const float *topk_w, int T, int k, int H, int has_shared,
                           void *out, int out_bf16, hipStream_t s) {
-  dim3 grid((H / 4 + 255) / 256, T);
+  dim3 grid((H / (y_bf16 ? 8 : 4) + 255) / 256, T);
   if (y_bf16)
     hipLaunchKernelGGL(k_combine<true>, grid, dim3(256), 0, s, Y, topk_w, T, k, H, has_shared, out, out_bf16);
   else

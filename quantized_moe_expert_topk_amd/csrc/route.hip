@@ -144,8 +144,13 @@ static void launch_topk_ks(const float *part, int KS, int T, int E, const float 
 
 static hipError_t launch_topk_ns(const float *part, int KS, int T, int E, const float *bias, int k, int renormalize,
                                  float *logits_out, int32_t *ids, float *wts, hipStream_t s) {
+  // the partial loads are unrolled KSMAX times (indices past KS clamped), so KSMAX follows KS
   if (KS <= 1)
     launch_topk_ks<1>(part, 1, T, E, bias, k, renormalize, logits_out, ids, wts, s);
+  else if (KS <= 2)
+    launch_topk_ks<2>(part, KS, T, E, bias, k, renormalize, logits_out, ids, wts, s);
+  else if (KS <= 4)
+    launch_topk_ks<4>(part, KS, T, E, bias, k, renormalize, logits_out, ids, wts, s);
   else if (KS <= 8)
     launch_topk_ks<8>(part, KS, T, E, bias, k, renormalize, logits_out, ids, wts, s);
   else
