@@ -399,6 +399,8 @@ int run_down(const moe_bank *routed, const moe_bank *shared, int T, int k, const
              const moe_align_out *al, int lo, const FwdPlan &p, void *out, int out_dtype, void *workspace,
              hipStream_t s) {
   qmoe::DownArgs a = down_args(routed, shared, T, k, al, lo, p, workspace);
+  if (!p.tiled && qmoe::down_t1_fused(routed->fmt, a, shared != nullptr))
+    return hip_status(qmoe::launch_down_t1(routed->fmt, a, topk_w, out, out_dtype == MOE_OUT_BF16, s), "down launch");
   int rc = p.tiled ? hip_status(qmoe::launch_down_wide(routed->fmt, a, p.n_shared_tiles, s), "down launch")
                    : hip_status(qmoe::launch_down(routed->fmt, a, p.n_shared_sub, s), "down launch");
   if (rc) return rc;

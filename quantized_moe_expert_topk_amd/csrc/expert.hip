@@ -683,15 +683,25 @@ __global__ __launch_bounds__(64 * KW, GC == 64 ? 2 : kMinWaves) void k_gate_up(G
 // tiles sharing one A fragment (a row block of h); K = the slice width Il.
 constexpr int DNT = 4;
 
+// Bytes of the per-wave LDS region down_wave stages FP4 / Q4_0 scale runs in (16 otherwise).
+template <int FMT, int COUNT>
+constexpr int down_lsc_bytes() {
+  return (FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_MXFP4_E8M0 || FMT == MOE_FMT_Q4_0)
+             ? 16 * DNT * (128 * COUNT / (FMT == MOE_FMT_MXFP4_E8M0 ? 32 : 16))
+             : 16;
+}
+
+// One wave's down tile: the 16 rows of sub-block sb (routed below a.n_routed_sub, then the
+// shared expert's) against hidden columns [n0, n0 + 16 DNT), K = the slice.  Returns false when
+// the sub-block holds no rows in use (past total_padded or no expert); otherwise acc[t][j] is
+// row 4g + j, column n0 + 16 t + r of the unweighted pair rows, before the per-row global
+// (dglob[t]), dst[j] the Y row of row 4g + j (-1: padding) and ntile the tiles inside H.
+// lsc: this wave's down_lsc_bytes<FMT, COUNT>() bytes of LDS.
 template <int FMT, int COUNT, bool NTW>
-__global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
-  // FP4: per wave, the scale bytes of its 16*DNT weight rows over one run
-  __shared__ __attribute__((aligned(16))) uint8_t lsc[(FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_MXFP4_E8M0 || FMT == MOE_FMT_Q4_0) ? 4 * 16 * DNT * (128 * COUNT / (FMT == MOE_FMT_MXFP4_E8M0 ? 32 : 16)) : 16];
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
+__device__ __forceinline__ bool down_wave(const DownArgs &a, int sb, int n0, uint8_t *lsc, f32x4_t (&acc)[DNT],
+                                          int (&dst)[4], float (&dglob)[DNT], int &ntile) {
+  const int lane = lane_id();
   const int r = lane & 15, g = lane >> 4;
-  const int sb = a.cols_fastest ? blockIdx.y : blockIdx.x;
-  const int n0 = (a.cols_fastest ? blockIdx.x : blockIdx.y) * 64 * DNT + wave * 16 * DNT;  // first output column
-  if (n0 >= a.H) return;
   const bool is_shared = sb >= a.n_routed_sub;
   int p0, e;
   const uint8_t *codes;
@@ -703,9 +713,9 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
     // independent loads in flight together (p0 < cap indexes both arrays)
     const int tp = a.total_padded[0], eb = a.block_expert[p0 / a.block_m];
     f0 = a.sorted_ids[p0 + r];
-    if (p0 >= __builtin_amdgcn_readfirstlane(tp)) return;
+    if (p0 >= __builtin_amdgcn_readfirstlane(tp)) return false;
     e = __builtin_amdgcn_readfirstlane(eb);
-    if (e < 0) return;
+    if (e < 0) return false;
     codes = a.dn;
     scales = a.dns;
     glob = a.dng;
@@ -717,7 +727,7 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
     glob = a.sdng;
   }
   const int H = a.H, I = a.I, Il = a.Il;
-  const int ntile = min(DNT, (H - n0) / 16);
+  ntile = min(DNT, (H - n0) / 16);
   const WMat<FMT> m = weight_matrix<FMT>(codes, scales, e, H, I);
   // FP4 and Q4_0 scales are staged per wave when a run's scale bytes per tile are whole
   // 16-byte pieces (runs of at least 2 steps for NVFP4 and Q4_0, 4 for MXFP4); otherwise
@@ -726,18 +736,16 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
   if constexpr (FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_MXFP4_E8M0 || FMT == MOE_FMT_Q4_0) {
     constexpr int sdiv = FMT == MOE_FMT_MXFP4_E8M0 ? 32 : 16;  // elements per scale byte
     constexpr int RB = 128 * COUNT / sdiv;
-    if (RB % 16 == 0) wsc = &lsc[wave * 16 * DNT * RB];
+    if (RB % 16 == 0) wsc = lsc;
   }
   uint32_t rows[DNT];  // rows inside this expert's [H, I] matrix
 #pragma unroll
   for (int t = 0; t < DNT; t++) rows[t] = n0 + 16 * (t < ntile ? t : 0) + r;
-  f32x4_t acc[DNT];
 #pragma unroll
   for (int t = 0; t < DNT; t++) acc[t] = zero4();
   // destination rows: lane r of every lane group already holds the pair of row r (f0), and
   // this lane's result rows are 4g + j, so they come from a cross-lane shuffle, not a load
   const int P = a.T * a.k;
-  int dst[4];
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     if (!is_shared) {
@@ -748,7 +756,6 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
       dst[j] = t < a.T ? P + t : -1;
     }
   }
-  float dglob[DNT];
 #pragma unroll
   for (int t = 0; t < DNT; t++) dglob[t] = FMT == MOE_FMT_NVFP4 ? glob[(size_t)e * H + n0 + 16 * t + r] : 1.f;
   // padding rows (no pair / past T) point past h: they read zeros without a memory request
@@ -770,6 +777,23 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
     for (int kw0 = 0; kw0 < Il + kph; kw0 += 128 * COUNT)
       mma_run<FMT, DNT, COUNT, Q4, NTW>(ra, a_row, m, rows, a.lo - kph, kw0, Il + kph - kw0, g, acc, wsc, kph);
   }
+  return true;
+}
+
+template <int FMT, int COUNT, bool NTW>
+__global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lsc[4 * down_lsc_bytes<FMT, COUNT>()];
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int r = lane & 15;
+  const int sb = a.cols_fastest ? blockIdx.y : blockIdx.x;
+  const int n0 = (a.cols_fastest ? blockIdx.x : blockIdx.y) * 64 * DNT + wave * 16 * DNT;  // first output column
+  if (n0 >= a.H) return;
+  f32x4_t acc[DNT];
+  int dst[4], ntile;
+  float dglob[DNT];
+  if (!down_wave<FMT, COUNT, NTW>(a, sb, n0, &lsc[wave * down_lsc_bytes<FMT, COUNT>()], acc, dst, dglob, ntile))
+    return;
+  const int H = a.H;
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     if (dst[j] < 0) continue;
@@ -779,6 +803,50 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
       a.Y[(size_t)dst[j] * H + n0 + 16 * t + r] = acc[t][j] * dglob[t];
     }
   }
+}
+
+// One token (T = 1): down and combine in one kernel.  A workgroup of 16 waves owns hidden
+// columns [64 x, 64 x + 64); wave w takes sub-block w (the routed ones, one pair each at
+// most, then the shared expert's at n_routed_sub), so every row the token's output sums is
+// in this workgroup.  The waves leave their rows (unweighted, after the per-row global, as
+// the Y rows) in LDS under the row's pair index (the shared row after the k pairs), and one
+// thread per column sums them as k_combine does: the k pairs in order, weighted, then the
+// shared row.  A row nobody writes (an id outside [0, E)) counts as zero.
+template <int FMT, int COUNT, bool NTW>
+__global__ __launch_bounds__(1024) void k_down_t1(DownArgs a, const float *__restrict__ topk_w, void *__restrict__ out,
+                                                  int out_bf16) {
+  __shared__ __attribute__((aligned(16))) uint8_t lsc[16 * down_lsc_bytes<FMT, COUNT>()];
+  __shared__ float rowv[17][64];  // [pair (k <= 15), then the shared row][column]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15;
+  const int n0 = blockIdx.x * 64, k = a.k;
+  for (int i = tid; i < 17 * 64; i += 1024) (&rowv[0][0])[i] = 0.f;
+  __syncthreads();
+  const int nsub = a.n_routed_sub + (a.sdn ? 1 : 0);
+  if (wave < nsub) {
+    f32x4_t acc[DNT];
+    int dst[4], ntile;
+    float dglob[DNT];
+    if (down_wave<FMT, COUNT, NTW>(a, wave, n0, &lsc[wave * down_lsc_bytes<FMT, COUNT>()], acc, dst, dglob, ntile)) {
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        if (dst[j] < 0) continue;  // dst: pair f < k, or k + 0 for the shared row
+#pragma unroll
+        for (int t = 0; t < DNT; t++)
+          if (t < ntile) rowv[dst[j]][16 * t + r] = acc[t][j] * dglob[t];
+      }
+    }
+  }
+  __syncthreads();
+  const int n = n0 + tid;
+  if (tid >= 64 || n >= a.H) return;
+  float s = 0.f;
+  for (int j = 0; j < k; j++) s += topk_w[j] * rowv[j][tid];
+  if (a.sdn) s += 1.f * rowv[k][tid];
+  if (out_bf16)
+    reinterpret_cast<uint16_t *>(out)[n] = bf16_bits(s);
+  else
+    reinterpret_cast<float *>(out)[n] = s;
 }
 
 // ---------------------------------------------------------------------------- combine
@@ -940,6 +1008,40 @@ static void launch_down_fmt(const DownArgs &a, dim3 grid, hipStream_t s) {
       else hipLaunchKernelGGL((k_down<FMT, 4, false>), grid, dim3(256), 0, s, a);
       break;
   }
+}
+
+template <int FMT>
+static void launch_down_t1_fmt(const DownArgs &a, const float *topk_w, void *out, int out_bf16, hipStream_t s) {
+  const dim3 grid((a.H + 63) / 64), block(1024);
+  const int kph = FMT == MOE_FMT_Q4_0 ? a.lo & 127 : 0;
+  switch (count_class(MOE_FMT_FP8_BLOCK128, (a.Il + kph + 127) / 128)) {
+    case 1: hipLaunchKernelGGL((k_down_t1<FMT, 1, false>), grid, block, 0, s, a, topk_w, out, out_bf16); break;
+    case 2: hipLaunchKernelGGL((k_down_t1<FMT, 2, false>), grid, block, 0, s, a, topk_w, out, out_bf16); break;
+    default: hipLaunchKernelGGL((k_down_t1<FMT, 4, false>), grid, block, 0, s, a, topk_w, out, out_bf16); break;
+  }
+}
+
+// Where the one-token kernel measured faster than down + combine (MI355X, steps of 200): fp8-block
+// 24.7 -> 22.2 us, bf16 28.2 -> 26.0, MXFP4 (slice 1024) 40.8 -> 40.3, NVFP4 and q4_0 on a 256
+// slice 24.5 -> 24.1 and 24.9 -> 24.5.  NVFP4 and q4_0 runs longer than two K steps do not fit
+// the 128 registers of a 1024-thread workgroup (NVFP4 at slice 512: 27.0 -> 29.0 us), so they
+// keep the two kernels.
+bool down_t1_fused(int fmt, const DownArgs &a, int has_shared) {
+  const int kph = fmt == MOE_FMT_Q4_0 ? a.lo & 127 : 0;
+  const int steps = (a.Il + kph + 127) / 128;
+  const bool fits = !(fmt == MOE_FMT_NVFP4 || fmt == MOE_FMT_Q4_0) || steps <= 2;
+  return a.T == 1 && a.k <= 15 && a.n_routed_sub + (has_shared ? 1 : 0) <= 16 && fits;
+}
+
+hipError_t launch_down_t1(int fmt, const DownArgs &a, const float *topk_w, void *out, int out_bf16, hipStream_t s) {
+  switch (fmt) {
+    case MOE_FMT_NVFP4: launch_down_t1_fmt<MOE_FMT_NVFP4>(a, topk_w, out, out_bf16, s); break;
+    case MOE_FMT_MXFP4_E8M0: launch_down_t1_fmt<MOE_FMT_MXFP4_E8M0>(a, topk_w, out, out_bf16, s); break;
+    case MOE_FMT_BF16: launch_down_t1_fmt<MOE_FMT_BF16>(a, topk_w, out, out_bf16, s); break;
+    case MOE_FMT_Q4_0: launch_down_t1_fmt<MOE_FMT_Q4_0>(a, topk_w, out, out_bf16, s); break;
+    default: launch_down_t1_fmt<MOE_FMT_FP8_BLOCK128>(a, topk_w, out, out_bf16, s); break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_down(int fmt, const DownArgs &a, int n_shared_sub, hipStream_t s) {

@@ -76,6 +76,10 @@ hipError_t launch_route_align(const uint16_t *x, int T, int H, const uint16_t *w
                               int32_t *offsets, int32_t *total_padded, int32_t *hist, hipStream_t s);
 hipError_t launch_gate_up(int fmt, const GateUpArgs &a, int n_shared_sub, hipStream_t s);
 hipError_t launch_down(int fmt, const DownArgs &a, int n_shared_sub, hipStream_t s);
+// One token: down and the combine in one launch (16 waves per 64 hidden columns, one per
+// sub-block) when down_t1_fused(fmt, a, has_shared); writes out directly.
+bool down_t1_fused(int fmt, const DownArgs &a, int has_shared);
+hipError_t launch_down_t1(int fmt, const DownArgs &a, const float *topk_w, void *out, int out_bf16, hipStream_t s);
 // Prefill GEMMs for align blocks of 128 rows (NVFP4, FP8_BLOCK128, BF16) with only the
 // activation tile in LDS (128 pair rows x 256 weight rows per workgroup); the shared expert's
 // rows are ceil(T/128) row blocks after the routed ones.
