@@ -705,11 +705,12 @@ def test_zero_tokens_is_a_no_op():
 
 
 @pytest.mark.parametrize("cid,T,bm", [(2, 32, None), (3, 8192, 128), (4, 64, 128), (5, 16, None), (6, 64, 128),
-                                       (7, 16, None)])
+                                       (7, 16, None), (2, 1, None), (5, 1, None)])
 def test_graph_replays_match_eager(cid, T, bm):
-    """The three calls captured in a HIP graph, for every format and both kernel families
-    (streaming, and the prefill GEMMs at align blocks of 128): every replay (with eager work
-    and synchronisations in between) reproduces the eager result bit for bit."""
+    """The three calls captured in a HIP graph, for every format and every kernel family
+    (streaming, the one-token down + combine at T = 1, and the prefill GEMMs at align blocks
+    of 128): every replay (with eager work and synchronisations in between) reproduces the
+    eager result bit for bit."""
     inp, r = inputs_for(cid, T)
     cfg = inp.cfg
     rb, sb = dev_banks(inp)
