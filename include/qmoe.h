@@ -243,7 +243,7 @@ int moe_route_align(const void *x_bf16, int T, int H, const void *w_router_bf16,
 /* Device workspace moe_expert_forward needs for (routed, shared, T, k, block_m, slice):
  * with rows = capacity + 128*ceil(T/128) if shared else capacity, Il = hi - lo, and each
  * term rounded up to 256 bytes,
- *   NVFP4, FP8_BLOCK128:  rows*Il*2  +  (T*k + T_shared)*H*4
+ *   NVFP4, FP8_BLOCK128, BF16, Q4_0:  rows*Il*2  +  (T*k + T_shared)*H*4
  *   MXFP4:  2*rows*Il + 2*rows*Il/32 + 2*T*H + 2*T*H/32  +  (T*k + T_shared)*H*4
  * (the intermediate activation, MXFP4's activation planes, and per-pair partial rows).
  * Returns 0 for arguments moe_expert_forward would reject as invalid. */
