@@ -38,7 +38,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0}
 RIDGE_FLOP_PER_BYTE = MFMA_PEAK_TFLOPS["bf16"] * 1e12 / (HBM_PEAK_GBS * 1e9)
 # the sources each gate_up kernel is built from (counter summaries are keyed on their hash)
-KERNEL_SOURCES = {"k_gate_up": ("expert.hip", "device_common.h"),
+KERNEL_SOURCES = {"k_gate_up": ("expert_kernels.h", "expert_mxfp4.hip", "device_common.h"),
                   "k_gate_up_wide": ("expert_wide.hip", "device_common.h")}
 WIDE_FORMATS = ("nvfp4", "fp8blk", "bf16")  # formats whose 128-row align blocks run the wide GEMMs
 
@@ -90,14 +90,16 @@ def gate_up_slice_bytes(fmt, H, Il):
 
 
 def kernel_source_hash(kernel_name="k_gate_up"):
-    """Hash of the code (comments and whitespace removed) of the sources a kernel is built from."""
+    """Hash of the code (comments and whitespace removed) of the sources a kernel is built from,
+    and of the compiler options given to those files."""
     import re
+    from quantized_moe_expert_topk_amd.build import FILE_FLAGS
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel_name]:
         text = open(os.path.join(ROOT, "quantized_moe_expert_topk_amd", "csrc", f)).read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
-        h.update(" ".join(text.split()).encode())
+        h.update(" ".join(text.split() + FILE_FLAGS.get(f, [])).encode())
     return h.hexdigest()[:16]
 
 

@@ -36,21 +36,27 @@ def test_expert_slice_bytes_match_a_rank_slice(fmt, H, I, lo, hi):
 
 
 def test_kernel_source_hash_ignores_comments_not_code(tmp_path, monkeypatch):
-    """The traffic counters are keyed on the kernel's code: an edit to comments or whitespace
-    keeps the key, an edit to code changes it, and each kernel hashes its own sources."""
+    """The traffic counters are keyed on the kernel's code and compiler options: an edit to
+    comments or whitespace keeps the key, an edit to code or to a file's options changes it,
+    and each kernel hashes its own sources."""
+    from quantized_moe_expert_topk_amd import build as qbuild
     csrc = tmp_path / "quantized_moe_expert_topk_amd" / "csrc"
     csrc.mkdir(parents=True)
     (csrc / "device_common.h").write_text("#pragma once\nint helper(int x) { return x + 1; }\n")
-    (csrc / "expert.hip").write_text("// streaming\n__global__ void k(int *p) { p[0] = 1; }\n")
+    (csrc / "expert_kernels.h").write_text("// streaming\n__global__ void k(int *p) { p[0] = 1; }\n")
+    (csrc / "expert_mxfp4.hip").write_text('#include "expert_kernels.h"\n')
     (csrc / "expert_wide.hip").write_text("/* wide */\n__global__ void w(int *p) { p[0] = 2; }\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     h0, w0 = bench.kernel_source_hash("k_gate_up"), bench.kernel_source_hash("k_gate_up_wide")
     assert h0 != w0
-    (csrc / "expert.hip").write_text("// streaming kernels, reworded\n/* block\n comment */\n"
-                                     "__global__ void k(int *p) {   p[0] = 1;   }  // trailing\n")
+    (csrc / "expert_kernels.h").write_text("// streaming kernels, reworded\n/* block\n comment */\n"
+                                           "__global__ void k(int *p) {   p[0] = 1;   }  // trailing\n")
     assert bench.kernel_source_hash("k_gate_up") == h0
-    (csrc / "expert.hip").write_text("__global__ void k(int *p) { p[0] = 3; }\n")
-    assert bench.kernel_source_hash("k_gate_up") != h0
+    (csrc / "expert_kernels.h").write_text("__global__ void k(int *p) { p[0] = 3; }\n")
+    h1 = bench.kernel_source_hash("k_gate_up")
+    assert h1 != h0
     assert bench.kernel_source_hash("k_gate_up_wide") == w0
+    monkeypatch.setitem(qbuild.FILE_FLAGS, "expert_mxfp4.hip", ["-mllvm", "-some-other-option"])
+    assert bench.kernel_source_hash("k_gate_up") != h1
     (csrc / "device_common.h").write_text("#pragma once\nint helper(int x) { return x + 2; }\n")
     assert bench.kernel_source_hash("k_gate_up_wide") != w0
