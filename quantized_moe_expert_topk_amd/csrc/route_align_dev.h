@@ -59,30 +59,39 @@ __device__ __forceinline__ float key_value(uint64_t key) {
   return __uint_as_float(u);
 }
 
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_max(uint64_t k) {
-  const uint32_t lo = (uint32_t)k, hi = (uint32_t)(k >> 32);
-  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, 0xF, 0xF, false);
-  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, 0xF, 0xF, false);
-  const uint64_t o = ((uint64_t)ohi << 32) | olo;
-  return o > k ? o : k;
+// 32-bit wave reductions.  The DPP row steps (quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror,
+// row_mirror) combine every lane of a 16-lane row exactly once, so each lane holds its row's
+// result; row_bcast:15 into rows 1 and 3, then row_bcast:31 into rows 2 and 3, fold rows 0-2
+// into row 3, and lane 63 holds the wave's result, which is returned to every lane.  Lanes a
+// step does not write keep their own value (update_dpp's `old`).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v, uint32_t old) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xF, false);
 }
 
-// Wave-wide maximum of the 64-bit key, returned to every lane (uniform).
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
-  k = dpp_max<0xB1>(k);   // quad_perm [1,0,3,2]
-  k = dpp_max<0x4E>(k);   // quad_perm [2,3,0,1]
-  k = dpp_max<0x141>(k);  // row_half_mirror
-  k = dpp_max<0x140>(k);  // row_mirror: every lane now holds its 16-lane row's maximum
-  uint64_t best = 0;
-#pragma unroll
-  for (int row = 0; row < 4; row++) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, 16 * row);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 16 * row);
-    const uint64_t rk = ((uint64_t)hi << 32) | lo;
-    best = rk > best ? rk : best;
-  }
-  return best;
+template <typename F>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, uint32_t identity, F op) {
+  v = op(v, dpp_u32<0xB1>(v, identity));   // quad_perm [1,0,3,2]
+  v = op(v, dpp_u32<0x4E>(v, identity));   // quad_perm [2,3,0,1]
+  v = op(v, dpp_u32<0x141>(v, identity));  // row_half_mirror
+  v = op(v, dpp_u32<0x140>(v, identity));  // row_mirror
+  v = op(v, dpp_u32<0x142, 0xA>(v, identity));  // row_bcast:15
+  v = op(v, dpp_u32<0x143, 0xC>(v, identity));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return wave_reduce_u32(v, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  return wave_reduce_u32(v, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  return __uint_as_float(wave_reduce_u32(__float_as_uint(v), 0u, [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }));
 }
 
 // Top-k of token t by one wave from its E logits `lg` (any memory; E <= 64 NS): each lane
@@ -113,12 +122,22 @@ __device__ __forceinline__ void select_topk(const float *lg, int E, int k, int r
         key[q] = key[q + 1];
         key[q + 1] = tmp;
       }
+  // Each round: the largest score among the lanes' heads (the upper half of the key), then the
+  // lowest expert index among the heads holding it (ties only), then the winner's lane shifts.
+  // A lane whose keys are used up holds 0, below every score (k <= E).
   float mine = 0.f, top = 0.f;
   for (int j = 0; j < k; j++) {
-    const uint64_t best = wave_max_key(key[0]);
-    const int bi = key_index(best);
-    const float bv = key_value(best);
-    if (key[0] == best) {  // keys are unique (index in the low half): exactly one lane
+    const uint32_t hv = (uint32_t)(key[0] >> 32);
+    const uint32_t m = wave_max_u32(hv);
+    const uint64_t cand = __ballot(hv == m);
+    int wl = __ffsll((unsigned long long)cand) - 1;
+    if (__popcll(cand) > 1) {
+      const uint32_t iv = hv == m ? (uint32_t)key_index(key[0]) : 0xFFFFFFFFu;
+      wl = __ffsll((unsigned long long)__ballot(iv == wave_min_u32(iv))) - 1;
+    }
+    const int bi = __builtin_amdgcn_readlane(key_index(key[0]), wl);
+    const float bv = key_value((uint64_t)m << 32);
+    if (lane == wl) {
 #pragma unroll
       for (int q = 0; q + 1 < NS; q++) key[q] = key[q + 1];
       key[NS - 1] = 0;
@@ -138,17 +157,30 @@ __device__ __forceinline__ void select_topk(const float *lg, int E, int k, int r
     for (int q = 0; q < NS; q++)
       if (lane + 64 * q < E) z += expf(vals[q] - top);
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
+  z = wave_sum_f32(z);
   if (lane < k) wts[(size_t)t * k + lane] = expf(mine - top) / z;
+}
+
+// Inclusive prefix sum over the wave (lane l gets the sum of lanes 0..l): row_shr 1, 2, 4, 8
+// within each 16-lane row (lanes shifted in from outside the row add 0), then row_bcast:15
+// and row_bcast:31 carry the rows' totals forward.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += (int)dpp_u32<0x111>((uint32_t)v, 0u);  // row_shr:1
+  v += (int)dpp_u32<0x112>((uint32_t)v, 0u);  // row_shr:2
+  v += (int)dpp_u32<0x114>((uint32_t)v, 0u);  // row_shr:4
+  v += (int)dpp_u32<0x118>((uint32_t)v, 0u);  // row_shr:8
+  v += (int)dpp_u32<0x142, 0xA>((uint32_t)v, 0u);  // row_bcast:15
+  v += (int)dpp_u32<0x143, 0xC>((uint32_t)v, 0u);  // row_bcast:31
+  return v;
 }
 
 // Stable counting sort of P <= 1024 * RPW pairs (ids[f], f < P) over E experts by one
 // workgroup of exactly 1024 threads: histogram, scan, sentinels and the stable scatter.
 // The pairs form 16 * RPW rows of 64; wave w owns rows [RPW w, RPW w + RPW) and ranks each
 // pair among the equal ids of its row (ballot match masks); thread x owns expert x in the
-// scan (E <= 1024).  lds: (16 * RPW + 1) * E int32 of dynamic LDS (rowcnt [16 RPW][E], then
-// start [E]).
+// scan (E <= 1024).  Every slot of sorted_ids and block_expert is first written as padding
+// (P, -1); the experts' blocks and the pairs overwrite theirs after the workgroup barriers.
+// lds: (16 * RPW + 1) * E int32 of dynamic LDS (rowcnt [16 RPW][E], then start [E]).
 template <int RPW>
 __device__ __forceinline__ void align_block(const int32_t *__restrict__ ids, int P, int E, int BM, int cap,
                                             int32_t *__restrict__ sorted_ids, int32_t *__restrict__ block_expert,
@@ -158,14 +190,21 @@ __device__ __forceinline__ void align_block(const int32_t *__restrict__ ids, int
   int32_t *rowcnt = lds;
   int32_t *start_of = lds + NR * E;
   __shared__ int32_t wsum[16];
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int lane = lane_id(), wave = threadIdx.x >> 6, x = threadIdx.x;
+  // block arithmetic: shifts when BM is a power of two, else divisions (uniform branch)
+  const bool pow2 = (BM & (BM - 1)) == 0;
+  const int sh = __builtin_ctz((unsigned)BM);
+  auto blocks = [&](int v) { return pow2 ? v >> sh : v / BM; };
   int e[RPW];
 #pragma unroll
-  for (int q = 0; q < RPW; q++) {  // in flight while the counters are cleared
+  for (int q = 0; q < RPW; q++) {  // in flight while the padding is written and the counters cleared
     const int f = (RPW * wave + q) * 64 + lane;
     e[q] = f < P ? ids[f] : -1;
   }
-  for (int i = threadIdx.x; i < NR * E; i += blockDim.x) rowcnt[i] = 0;
+  const int nblk = blocks(cap);
+  for (int p = x; p < cap; p += blockDim.x) sorted_ids[p] = P;
+  for (int b = x; b < nblk; b += blockDim.x) block_expert[b] = -1;
+  for (int i = x; i < NR * E; i += blockDim.x) rowcnt[i] = 0;
   __syncthreads();
   int nbits = 0;
   while ((1 << nbits) < E) nbits++;
@@ -173,6 +212,8 @@ __device__ __forceinline__ void align_block(const int32_t *__restrict__ ids, int
   int rank[RPW];
 #pragma unroll
   for (int q = 0; q < RPW; q++) {
+    rank[q] = 0;
+    if (RPW * wave * 64 + q * 64 >= P) continue;  // no pair in this row (uniform)
     if (e[q] < 0 || e[q] >= E) e[q] = -1;
     uint64_t peers = __ballot(e[q] >= 0);
     for (int bit = 0; bit < nbits; bit++) {
@@ -185,7 +226,6 @@ __device__ __forceinline__ void align_block(const int32_t *__restrict__ ids, int
   __syncthreads();
   // per expert: exclusive prefix over the rows and the total count
   int run = 0;
-  const int x = threadIdx.x;
   if (x < E) {
 #pragma unroll
     for (int r0 = 0; r0 < NR; r0 += 16) {
@@ -200,33 +240,27 @@ __device__ __forceinline__ void align_block(const int32_t *__restrict__ ids, int
     }
     counts[x] = run;
   }
-  const int padded = x < E ? (run + BM - 1) / BM * BM : 0;
-  int inc = padded;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(inc, off);
-    if (lane >= off) inc += o;
-  }
+  const int padded = x < E ? blocks(run + BM - 1) * BM : 0;
+  const int inc = wave_inclusive_scan(padded);
   if (lane == 63) wsum[wave] = inc;
   __syncthreads();
   int wbase = 0, total = 0;
+#pragma unroll
   for (int w = 0; w < 16; w++) {
-    if (w < wave) wbase += wsum[w];
-    total += wsum[w];
+    const int ws = wsum[w];
+    wbase += w < wave ? ws : 0;
+    total += ws;
   }
   const int start = wbase + inc - padded;
   if (x < E) {
     start_of[x] = start;
     offsets[x] = start;
-    for (int b = start / BM; b < (start + padded) / BM; b++) block_expert[b] = x;
-    for (int p = start + run; p < start + padded; p++) sorted_ids[p] = P;
+    for (int b = blocks(start); b < blocks(start + padded); b++) block_expert[b] = x;
   }
   if (x == 0) {
     offsets[E] = total;
     total_padded[0] = total;
   }
-  for (int b = total / BM + x; b < cap / BM; b += blockDim.x) block_expert[b] = -1;
-  for (int p = total + x; p < cap; p += blockDim.x) sorted_ids[p] = P;
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < RPW; q++) {

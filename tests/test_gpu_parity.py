@@ -153,6 +153,8 @@ def test_route_is_deterministic():
     # the sizes just past it
     (256, 8, 256, 16, "rand"), (512, 8, 256, 64, "zipf"), (129, 8, 256, 16, "rand"), (300, 8, 200, 128, "one_expert"),
     (1000, 4, 3, 32, "two_experts"), (513, 8, 256, 16, "rand"), (250, 8, 257, 16, "rand"),
+    # block sizes that are not powers of two (divisions instead of shifts)
+    (16, 2, 8, 48, "rand"), (300, 8, 200, 80, "rand"), (1, 8, 256, 208, "rand"), (5000, 2, 64, 112, "rand"),
 ])
 def test_align_is_bit_exact(T, k, E, bm, kind):
     if kind == "rand":
@@ -183,7 +185,9 @@ def test_align_is_bit_exact(T, k, E, bm, kind):
     (16, 128, 64, 128, False, True, 16), (1500, 200, 6, 1024, True, True, 128),
     # larger batches on both sides of 1024 pairs, the tiled router (T = 1024) and E = 512
     (128, 256, 8, 2048, True, True, 16), (129, 256, 8, 2048, False, True, 16), (37, 256, 8, 1024, True, False, 32),
-    (1024, 64, 1, 256, False, True, 16), (100, 512, 10, 384, True, True, 64)])
+    (1024, 64, 1, 256, False, True, 16), (100, 512, 10, 384, True, True, 64),
+    # block sizes that are not powers of two
+    (3, 256, 8, 2048, True, True, 48), (40, 256, 8, 1024, False, True, 176)])
 def test_route_align_equals_route_then_align(T, E, k, H, with_bias, renorm, bm):
     """moe_route_align (one top-k + align workgroup for T <= 16, E <= 512, T*k <= 1024) gives
     exactly the outputs of moe_route followed by moe_align, on both sides of that boundary."""
