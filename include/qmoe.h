@@ -333,6 +333,27 @@ int moe_expert_down(const moe_bank *routed, const moe_bank *shared, int T, int k
                     void *out, int out_dtype, void *workspace, size_t workspace_bytes,
                     void *stream);
 
+/* moe_layer_forward -- the whole layer in one call: moe_route_align (router GEMM, top-k,
+ * alignment), then moe_expert_forward on the slice [slice_lo, slice_hi) (gate_up + SwiGLU,
+ * down, the weighted combine with the shared expert).  The same arguments, requirements and
+ * checks as those two calls (H and E are routed->H and routed->E; the router arguments as in
+ * moe_route; *al receives the alignment), and the same outputs bit for bit: logits, topk_ids
+ * and topk_w, every array of *al, and out.
+ *   route_workspace >= moe_route_align_workspace_bytes(T, H, E, k) bytes;
+ *   workspace       >= moe_workspace_bytes(routed, shared, T, k, al->block_m, lo, hi) bytes.
+ * For one token (T = 1) on 16-row blocks, when the gate_up launch takes 8 waves per
+ * workgroup, the top-k and the alignment run inside the gate_up kernel: each routed
+ * workgroup sums the router's partial logits and ranks them itself, and the first writes the
+ * routing and alignment outputs, so the decode step of one token is the router, gate_up and
+ * down kernels (plus MXFP4's activation split), one launch and one kernel boundary fewer
+ * than the two calls.  Otherwise it enqueues exactly what the two calls enqueue.  T == 0
+ * enqueues nothing. */
+int moe_layer_forward(const void *x_bf16, int T, const void *w_router_bf16, const float *bias, int k,
+                      int renormalize, const moe_bank *routed, const moe_bank *shared, int slice_lo,
+                      int slice_hi, float *logits, int32_t *topk_ids, float *topk_w, const moe_align_out *al,
+                      void *out, int out_dtype, void *route_workspace, size_t route_workspace_bytes,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------------------ diagnostics */
 
 const char *moe_status_string(int status); /* static text for a status code */

@@ -25,7 +25,7 @@ EXPORTS = ("moe_route", "moe_route_workspace_bytes", "moe_route_from_logits", "m
            "moe_choose_block_m", "moe_align_workspace_bytes", "moe_align",
            "moe_route_align_workspace_bytes", "moe_route_align",
            "moe_workspace_bytes", "moe_pack_bank", "moe_expert_forward", "moe_expert_forward_static",
-           "moe_expert_gate_up", "moe_expert_down",
+           "moe_expert_gate_up", "moe_expert_down", "moe_layer_forward",
            "moe_status_string", "moe_last_error")
 
 
@@ -85,6 +85,8 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_forward_static.argtypes = [pb, pb, vp, i32, i32, vp, pa, i32, i32, vp, i32, vp]
         L.moe_expert_gate_up.argtypes = [pb, pb, vp, i32, i32, pa, i32, i32, vp, sz, vp]
         L.moe_expert_down.argtypes = [pb, pb, i32, i32, vp, pa, i32, i32, vp, i32, vp, sz, vp]
+        L.moe_layer_forward.argtypes = [vp, i32, vp, vp, i32, i32, pb, pb, i32, i32, vp, vp, vp, pa, vp, i32, vp, sz,
+                                        vp, sz, vp]
         L.moe_status_string.argtypes = [i32]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_last_error.argtypes = []

@@ -289,6 +289,35 @@ def moe_expert_down(routed: DeviceBank, shared: DeviceBank | None, topk_w: torch
         slice_lo, slice_hi, _ptr(out), code, _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
+def moe_layer_forward(x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor | None, k: int, renormalize: bool,
+                      routed: DeviceBank, shared: DeviceBank | None, slice_lo: int, slice_hi: int,
+                      logits: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, align: AlignOut,
+                      out: torch.Tensor, route_workspace: torch.Tensor | None, workspace: torch.Tensor,
+                      stream=None) -> torch.Tensor:
+    """The whole layer in one call (``moe_layer_forward``): moe_route_align then
+    moe_expert_forward, with the same outputs; for one token the top-k and the alignment run
+    inside the gate_up kernel."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    _need(x, torch.bfloat16, (T, H), "x")
+    _need(w_router, torch.bfloat16, (E, H), "w_router")
+    if bias is not None:
+        _need(bias, torch.float32, (E,), "bias")
+    _need(logits, torch.float32, (T, E), "logits")
+    _need(topk_ids, torch.int32, (T, k), "topk_ids")
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    _need(out, out.dtype, (T, H), "out")
+    rs, ss, al = routed.struct(), (shared.struct() if shared is not None else None), align.struct()
+    code = MOE_OUT_BF16 if out.dtype == torch.bfloat16 else MOE_OUT_F32
+    rws = route_workspace.numel() if route_workspace is not None else 0
+    check("moe_layer_forward", lib().moe_layer_forward(
+        _ptr(x), T, _ptr(w_router), _ptr(bias), k, int(renormalize), ctypes.byref(rs),
+        ctypes.byref(ss) if ss is not None else None, slice_lo, slice_hi, _ptr(logits), _ptr(topk_ids),
+        _ptr(topk_w), ctypes.byref(al), _ptr(out), code, _ptr(route_workspace), rws, _ptr(workspace),
+        workspace.numel(), _stream(stream)))
+    return out
+
+
 def choose_block_m(T: int, k: int, E: int, fmt: str | None = None) -> int:
     """The library's block-size policy (``moe_choose_block_m``): 16 while experts see few
     tokens each, larger as the mean number of pairs per expert grows; 128 (the prefill GEMMs)
@@ -301,8 +330,8 @@ def choose_block_m(T: int, k: int, E: int, fmt: str | None = None) -> int:
 
 
 class MoeLayer:
-    """Pre-allocated buffers for one (bank, T, slice) and the calls of one layer:
-    moe_route_align (moe_route then moe_align) -> moe_expert_forward on one stream, host-sync
+    """Pre-allocated buffers for one (bank, T, slice) and the call of one layer,
+    moe_layer_forward (moe_route_align, then moe_expert_forward) on one stream, host-sync
     free, so it can be captured in a HIP graph.  Row-major banks are packed (moe_pack_bank) here, once; pass
     packed banks to share their storage between layers."""
 
@@ -327,8 +356,6 @@ class MoeLayer:
         self.out = torch.empty((T, routed.H), dtype=out_dtype, device=dev)
 
     def __call__(self, x: torch.Tensor, stream=None) -> torch.Tensor:
-        moe_route_align(x, self.w_router, self.bias, self.k, self.block_m, self.renormalize, self.logits, self.ids,
-                        self.w, self.align, self.route_ws, stream)
-        moe_expert_forward(self.routed, self.shared, x, self.w, self.align, self.lo, self.hi, self.out,
-                           self.out.dtype, self.ws, stream)
-        return self.out
+        return moe_layer_forward(x, self.w_router, self.bias, self.k, self.renormalize, self.routed, self.shared,
+                                 self.lo, self.hi, self.logits, self.ids, self.w, self.align, self.out,
+                                 self.route_ws, self.ws, stream)

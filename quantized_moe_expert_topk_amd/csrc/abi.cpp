@@ -303,7 +303,7 @@ int check_forward_call(const moe_bank *routed, const moe_bank *shared, const voi
 
 qmoe::GateUpArgs gate_up_args(const moe_bank *routed, const moe_bank *shared, const void *x, int T, int k,
                               const moe_align_out *al, int lo, const FwdPlan &p, void *workspace) {
-  qmoe::GateUpArgs a;
+  qmoe::GateUpArgs a{};  // the one-token routing fields stay zero (route1 off)
   a.x = static_cast<const uint16_t *>(x);
   a.T = T;
   a.H = routed->H;
@@ -381,9 +381,9 @@ qmoe::DownArgs down_args(const moe_bank *routed, const moe_bank *shared, int T, 
   return a;
 }
 
-int run_gate_up(const moe_bank *routed, const moe_bank *shared, const void *x, int T, int k,
-                const moe_align_out *al, int lo, const FwdPlan &p, void *workspace, hipStream_t s) {
-  qmoe::GateUpArgs a = gate_up_args(routed, shared, x, T, k, al, lo, p, workspace);
+// gate_up for prepared arguments: MXFP4's activation planes, then the gate_up kernel.
+int launch_gate_up_args(const moe_bank *routed, const qmoe::GateUpArgs &a, int T, const FwdPlan &p,
+                        void *workspace, hipStream_t s) {
   if (routed->fmt == MOE_FMT_MXFP4_E8M0) {
     char *ws = static_cast<char *>(workspace);
     const int rc = hip_status(qmoe::launch_act_mx8(a.x, T, routed->H, reinterpret_cast<uint8_t *>(ws + p.xq_off),
@@ -393,6 +393,19 @@ int run_gate_up(const moe_bank *routed, const moe_bank *shared, const void *x, i
   }
   if (p.tiled) return hip_status(qmoe::launch_gate_up_wide(routed->fmt, a, p.n_shared_tiles, s), "gate_up launch");
   return hip_status(qmoe::launch_gate_up(routed->fmt, a, p.n_shared_sub, s), "gate_up launch");
+}
+
+int run_gate_up(const moe_bank *routed, const moe_bank *shared, const void *x, int T, int k,
+                const moe_align_out *al, int lo, const FwdPlan &p, void *workspace, hipStream_t s) {
+  const qmoe::GateUpArgs a = gate_up_args(routed, shared, x, T, k, al, lo, p, workspace);
+  return launch_gate_up_args(routed, a, T, p, workspace, s);
+}
+
+// moe_layer_forward's one-token path: one token on 16-row blocks, gate_up on the launch shape
+// its routing variant is built for (8 waves splitting K, which the launcher pairs with 32
+// slice columns, and cached weight loads).
+bool route1_path(const qmoe::GateUpArgs &a, const FwdPlan &p, int T, int block_m) {
+  return T == 1 && block_m == 16 && !p.tiled && a.kwaves == 8 && !a.nt_weights;
 }
 
 int run_down(const moe_bank *routed, const moe_bank *shared, int T, int k, const float *topk_w,
@@ -705,6 +718,62 @@ int moe_expert_down(const moe_bank *routed, const moe_bank *shared, int T, int k
   if (T == 0) return ok();
   return run_down(routed, shared, T, k, topk_w, al, slice_lo, p, out, out_dtype, workspace,
                   static_cast<hipStream_t>(stream));
+}
+
+int moe_layer_forward(const void *x_bf16, int T, const void *w_router_bf16, const float *bias, int k,
+                      int renormalize, const moe_bank *routed, const moe_bank *shared, int slice_lo, int slice_hi,
+                      float *logits, int32_t *topk_ids, float *topk_w, const moe_align_out *al, void *out,
+                      int out_dtype, void *route_workspace, size_t route_workspace_bytes, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  if (!routed) return fail(MOE_ERR_INVALID_ARG, "moe_layer_forward: routed bank is NULL");
+  const int H = routed->H, E = routed->E;
+  int rc = check_route(x_bf16, T, H, w_router_bf16, E, k, logits, topk_ids, topk_w);
+  if (rc) return rc;
+  FwdPlan p;
+  rc = check_forward_call(routed, shared, x_bf16, T, k, topk_w, al, slice_lo, slice_hi, out, out_dtype,
+                          workspace_bytes, workspace, &p);
+  if (rc) return rc;
+  const size_t rneed = moe_route_align_workspace_bytes(T, H, E, k);
+  if (route_workspace_bytes < rneed)
+    return fail(MOE_ERR_WORKSPACE, "moe_layer_forward: route workspace %zu < %zu", route_workspace_bytes, rneed);
+  if (rneed && !route_workspace) return fail(MOE_ERR_INVALID_ARG, "moe_layer_forward: route workspace is NULL");
+  rc = check_device();
+  if (rc) return rc;
+  if (T == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  qmoe::GateUpArgs a = gate_up_args(routed, shared, x_bf16, T, k, al, slice_lo, p, workspace);
+  if (!route1_path(a, p, T, al->block_m)) {  // exactly the two calls
+    rc = moe_route_align(x_bf16, T, H, w_router_bf16, E, bias, k, renormalize, logits, topk_ids, topk_w, al,
+                         route_workspace, route_workspace_bytes, stream);
+    if (rc) return rc;
+    rc = launch_gate_up_args(routed, a, T, p, workspace, s);
+    if (rc) return rc;
+    return run_down(routed, shared, T, k, topk_w, al, slice_lo, p, out, out_dtype, workspace, s);
+  }
+  // one token: the router GEMM, then gate_up ranks its logits in every routed workgroup and
+  // writes the routing and the alignment, which down reads
+  int ks = 1;
+  float *part = static_cast<float *>(route_workspace);
+  rc = hip_status(qmoe::launch_router(static_cast<const uint16_t *>(x_bf16), T, H,
+                                      static_cast<const uint16_t *>(w_router_bf16), E, bias, logits, part, &ks, s),
+                  "router launch");
+  if (rc) return rc;
+  a.route1 = 1;
+  a.r_part = ks > 1 ? part : logits;  // one split: the router added the bias into the logits
+  a.r_bias = ks > 1 ? bias : nullptr;
+  a.r_ks = ks;
+  a.r_renorm = renormalize;
+  a.r_logits = ks > 1 ? logits : nullptr;
+  a.r_ids = topk_ids;
+  a.r_w = topk_w;
+  a.al_sorted = al->sorted_ids;
+  a.al_block = al->block_expert;
+  a.al_counts = al->counts;
+  a.al_offsets = al->offsets;
+  a.al_total = al->total_padded;
+  rc = launch_gate_up_args(routed, a, T, p, workspace, s);
+  if (rc) return rc;
+  return run_down(routed, shared, T, k, topk_w, al, slice_lo, p, out, out_dtype, workspace, s);
 }
 
 int moe_expert_forward(const moe_bank *routed, const moe_bank *shared, const void *x_bf16, int T, int k,

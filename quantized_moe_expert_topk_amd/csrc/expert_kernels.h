@@ -44,6 +44,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "route_align_dev.h"
 
 namespace qmoe {
 
@@ -525,13 +526,142 @@ __device__ __forceinline__ void mma_run_mx(const ActMX &A, uint32_t a_q, uint32_
 // the launcher takes GC = 64 only from 4 pairs per expert on average.
 constexpr int kMinWaves = 3;  // waves per SIMD the expert kernels are compiled for
 
+// Routing of the one token of a whole-layer call, done by every routed gate_up workgroup
+// (NTH threads) in place of reading an alignment.  The logits are the router's split-K
+// partials summed in split order from +0, plus the bias: the float operations of the top-k
+// kernels, so the same values.  Order: the key (logit descending, index ascending; NaN as
+// -inf, -0 as +0: rank_key).  Thread x holds the keys of experts x + NTH q; each wave takes
+// the k largest of its experts by k rounds of a wave maximum (select_topk's rounds), and wave
+// 0 ranks the waves' candidates: the k of rank < k are the picks, in rank order, which is the
+// order the top-k kernels select them in.  The softmax weights repeat select_topk's
+// arithmetic on the same values.  For T = 1 and 16-row blocks the alignment is one block per
+// pick in expert order: pick number sb in that order is this workgroup's expert (returned in
+// e_out, its pair index in pair_out).  The writer workgroup also stores the logits, ids and
+// weights moe_route gives and every array moe_align gives for them.
+// scr: 4 E + 8 k NTH/64 + 1280 bytes of LDS, 8-byte aligned.
+template <int NTH>
+__device__ __forceinline__ void route_one_token(const GateUpArgs &a, int sb, bool writer, uint8_t *scr, int &e_out,
+                                                int &pair_out) {
+  constexpr int NW = NTH / 64, NQ = (1024 + NTH - 1) / NTH;  // waves; keys per thread for E <= 1024
+  const int E = a.E, k = a.k, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint64_t *cand = reinterpret_cast<uint64_t *>(scr);            // [NW][k] each wave's k largest
+  uint64_t *pkey = cand + NW * k;                                // [64] keys of the picks by rank
+  int32_t *pexp = reinterpret_cast<int32_t *>(pkey + 64);        // [64] their experts
+  int32_t *ord_e = pexp + 64, *ord_j = ord_e + 64;               // [64] picks in expert order: expert, rank
+  float *lg = reinterpret_cast<float *>(ord_j + 64);             // [E]
+  uint64_t key[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; q++) {
+    const int e = tid + NTH * q;
+    key[q] = 0;  // below every expert's key
+    if (e < E) {
+      float v[16];  // at most 16 splits, all loads in flight together
+#pragma unroll
+      for (int u = 0; u < 16; u++) v[u] = u < a.r_ks ? a.r_part[(size_t)u * E + e] : 0.f;
+      float sum = 0.f;
+#pragma unroll
+      for (int u = 0; u < 16; u++)
+        if (u < a.r_ks) sum += v[u];
+      sum += a.r_bias ? a.r_bias[e] : 0.f;
+      lg[e] = sum;
+      key[q] = rank_key(sum != sum ? -INFINITY : sum, e);
+      if (writer && a.r_logits) a.r_logits[e] = sum;
+    }
+  }
+  // descending order of the thread's keys (odd-even transposition)
+#pragma unroll
+  for (int pass = 0; pass < NQ; pass++)
+#pragma unroll
+    for (int q = pass & 1; q + 1 < NQ; q += 2)
+      if (key[q] < key[q + 1]) {
+        const uint64_t t = key[q];
+        key[q] = key[q + 1];
+        key[q + 1] = t;
+      }
+  // this wave's k largest: the largest head score, the lowest expert among the heads holding it
+  // (ties only), then the winner's lane shifts; an exhausted wave yields 0
+  for (int j = 0; j < k; j++) {
+    const uint32_t hv = (uint32_t)(key[0] >> 32);
+    const uint32_t m = wave_max_u32(hv);
+    const uint64_t cb = __ballot(hv == m);
+    int wl = __ffsll((unsigned long long)cb) - 1;
+    if (__popcll(cb) > 1) {
+      const uint32_t iv = hv == m ? (uint32_t)key_index(key[0]) : 0xFFFFFFFFu;
+      wl = __ffsll((unsigned long long)__ballot(iv == wave_min_u32(iv))) - 1;
+    }
+    const uint32_t klo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key[0], wl);
+    if (lane == 0) cand[wave * k + j] = m ? ((uint64_t)m << 32) | klo : 0;
+    if (lane == wl) {
+#pragma unroll
+      for (int q = 0; q + 1 < NQ; q++) key[q] = key[q + 1];
+      key[NQ - 1] = 0;
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int C = NW * k;  // candidates; distinct experts, and at least k of them are real
+    for (int c = lane; c < C; c += 64) {
+      const uint64_t me = cand[c];
+      int rank = 0;
+      for (int i = 0; i < C; i++) rank += cand[i] > me ? 1 : 0;
+      if (me && rank < k) {
+        pkey[rank] = me;
+        pexp[rank] = key_index(me);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const float top = key_value(pkey[0]);
+    const float mine = lane < k ? key_value(pkey[lane]) : 0.f;
+    float z;
+    if (a.r_renorm) {
+      z = lane < k ? expf(mine - top) : 0.f;
+    } else {
+      z = 0.f;
+      for (int e = lane; e < E; e += 64) z += expf(lg[e] - top);
+    }
+    z = wave_sum_f32(z);
+    if (writer && lane < k) {
+      a.r_ids[lane] = pexp[lane];
+      a.r_w[lane] = expf(mine - top) / z;
+    }
+    if (lane < k) {  // place in expert order (the picks are distinct experts)
+      const int ej = pexp[lane];
+      int rb = 0;
+      for (int j = 0; j < k; j++) rb += pexp[j] < ej ? 1 : 0;
+      ord_e[rb] = ej;
+      ord_j[rb] = lane;
+    }
+  }
+  __syncthreads();
+  e_out = ord_e[sb];
+  pair_out = ord_j[sb];
+  if (writer) {  // moe_align's output for these picks: P = k pairs, sentinel k, 16-row blocks
+    for (int p = tid; p < a.cap; p += NTH) a.al_sorted[p] = (p & 15) == 0 && (p >> 4) < k ? ord_j[p >> 4] : k;
+    for (int b = tid; b < a.cap / 16; b += NTH) a.al_block[b] = b < k ? ord_e[b] : -1;
+    for (int e = tid; e <= E; e += NTH) {
+      int below = 0, hit = 0;
+      for (int j = 0; j < k; j++) {
+        below += ord_e[j] < e ? 1 : 0;
+        hit |= ord_e[j] == e ? 1 : 0;
+      }
+      a.al_offsets[e] = 16 * below;
+      if (e < E) a.al_counts[e] = hit;
+    }
+    if (tid == 0) a.al_total[0] = 16 * k;
+  }
+  __syncthreads();  // every read of scr done before the caller reuses it
+}
+
 // KW = waves per workgroup, all splitting K: 4, or 8 when few pairs leave most of the chip
-// idle (each wave then covers half the K range, one round trip fewer).
-template <int FMT, int COUNT, int KW, int GC, bool NTW>
+// idle (each wave then covers half the K range, one round trip fewer).  ROUTE1: the
+// whole-layer call for one token (route_one_token in place of the alignment's reads).
+template <int FMT, int COUNT, int KW, int GC, bool NTW, bool ROUTE1 = false>
 __global__ __launch_bounds__(64 * KW, GC == 64 ? 2 : kMinWaves) void k_gate_up(GateUpArgs a) {
   constexpr int GT = GC / 16;
   static_assert(GT <= KW, "one wave per gate tile in the epilogue");
-  __shared__ float red[KW][2 * GT][4][64];  // [wave][tile][j][lane]
+  __shared__ __attribute__((aligned(16))) float red[KW][2 * GT][4][64];  // [wave][tile][j][lane]
   __shared__ float hbuf[16][GC + 1];         // MXFP4: the block's h before the plane split
   // FP4: per wave, the scale bytes of the workgroup's 2*GC weight rows over one run
   __shared__ __attribute__((aligned(16))) uint8_t lsc[(FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_MXFP4_E8M0 || FMT == MOE_FMT_Q4_0) ? KW * 2 * GC * (128 * COUNT / (FMT == MOE_FMT_MXFP4_E8M0 ? 32 : 16)) : 16];
@@ -546,12 +676,21 @@ __global__ __launch_bounds__(64 * KW, GC == 64 ? 2 : kMinWaves) void k_gate_up(G
   const float *glob;
   if (!is_shared) {
     p0 = sb * 16;
-    // three independent loads in flight together (p0 < cap indexes both arrays)
-    const int tp = a.total_padded[0], eb = a.block_expert[p0 / a.block_m], f = a.sorted_ids[p0 + r];
-    if (p0 >= __builtin_amdgcn_readfirstlane(tp)) return;  // uniform over the workgroup
-    e = __builtin_amdgcn_readfirstlane(eb);
-    if (e < 0) return;
-    tok = f < a.T * a.k ? f / a.k : -1;
+    if constexpr (ROUTE1) {  // one token: block sb holds pick sb (in expert order) in row 0
+      if (sb >= a.k) return;   // uniform over the workgroup
+      static_assert(sizeof(red) >= 4 * 1024 + 8 * KW * 64 + 1280, "routing scratch for E <= 1024, k <= 64");
+      int e1, j1;
+      route_one_token<64 * KW>(a, sb, sb == 0 && c0 == 0, reinterpret_cast<uint8_t *>(&red[0][0][0][0]), e1, j1);
+      e = __builtin_amdgcn_readfirstlane(e1);
+      tok = r == 0 ? 0 : -1;
+    } else {
+      // three independent loads in flight together (p0 < cap indexes both arrays)
+      const int tp = a.total_padded[0], eb = a.block_expert[p0 / a.block_m], f = a.sorted_ids[p0 + r];
+      if (p0 >= __builtin_amdgcn_readfirstlane(tp)) return;  // uniform over the workgroup
+      e = __builtin_amdgcn_readfirstlane(eb);
+      if (e < 0) return;
+      tok = f < a.T * a.k ? f / a.k : -1;
+    }
     codes = a.gu;
     scales = a.gus;
     glob = a.gug;
@@ -910,6 +1049,19 @@ static int count_class(int fmt, int steps) {
 template <int FMT, int KW, int GC, bool NTW>
 static void launch_gate_up_nt(const GateUpArgs &a, dim3 grid, hipStream_t s) {
   const dim3 block(64 * KW);
+  if constexpr (KW == 8 && GC == 32 && !NTW) {  // the one-token whole-layer call (route1_launchable)
+    if (a.route1) {
+      switch (count_class(FMT, a.ksteps)) {
+        case 1: hipLaunchKernelGGL((k_gate_up<FMT, 1, KW, GC, NTW, true>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((k_gate_up<FMT, 2, KW, GC, NTW, true>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((k_gate_up<FMT, 4, KW, GC, NTW, true>), grid, block, 0, s, a); break;
+        default:
+          if constexpr (FMT == MOE_FMT_NVFP4) hipLaunchKernelGGL((k_gate_up<FMT, 8, KW, GC, NTW, true>), grid, block, 0, s, a);
+          break;
+      }
+      return;
+    }
+  }
   switch (count_class(FMT, a.ksteps)) {
     case 1: hipLaunchKernelGGL((k_gate_up<FMT, 1, KW, GC, NTW>), grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL((k_gate_up<FMT, 2, KW, GC, NTW>), grid, block, 0, s, a); break;

@@ -102,12 +102,27 @@ struct BStage {
 // b_k0 is a multiple of 128, so even stages start a scale block.
 // AFFINE: the activation rows are consecutive, a_off[q] = a_off[0] + q * a_stride (down, whose
 // h rows are; only a_off[0] is read, which keeps 7 registers free).
-template <int FMT, bool TAIL, bool AFFINE>
+// WALK: the workgroup walks ncgs column groups of its row block in one pipeline.  Stage s of
+// the walk is stage s % nK of column group s / nK; boff(cgl, cb, sb) gives the weight offsets of
+// local column group cgl (cb/sb are then unused), and after the last stage of every group but
+// the last, epi(cgl) stores that group's results from acc (post: fp8-block as above) and clears
+// acc, between two barriers: its LDS tile overlaps the activation buffers.  Meanwhile the
+// weight loads of the next two stages and the activation loads of the next stage (the first
+// of the next group: the same rows) stay in flight.  The caller stores the last group after
+// the loop, as without WALK.  fp8-block needs nK even (scale blocks start on even stages).
+struct NoBOff {
+  __device__ void operator()(int, uint32_t (&)[2], uint32_t (&)[2]) const {}
+};
+struct NoEpi {
+  __device__ void operator()(int) const {}
+};
+
+template <int FMT, bool TAIL, bool AFFINE, bool WALK = false, class BOff = NoBOff, class Epi = NoEpi>
 __device__ __forceinline__ void wide_k_loop(WideLDS &lds, rsrc_t ra,
                                             const uint32_t (&a_off)[AStage<kWideK<FMT>>::NQ], uint32_t a_stride,
                                             const WMat<FMT> &m, const uint32_t (&cb)[2], const uint32_t (&sb)[2],
                                             int b_k0, int nK, int kvalid, f32x16_t (&acc)[4][2],
-                                            float (&post)[2]) {
+                                            float (&post)[2], int ncgs = 1, BOff boff = {}, Epi epi = {}) {
   constexpr int WK = kWideK<FMT>;
   using AS = AStage<WK>;
   using BS = BStage<FMT>;
@@ -124,7 +139,7 @@ __device__ __forceinline__ void wide_k_loop(WideLDS &lds, rsrc_t ra,
 #pragma unroll
     for (int q = 0; q < AS::NQ; q++) t.v[q] = buf_load16(ra, (AFFINE ? a_off[0] + q * a_stride : a_off[q]) + kk * 2);
   };
-  auto fetch_b = [&](int st, BS &t) {
+  auto fetch_b_at = [&](int st, const uint32_t (&cb)[2], const uint32_t (&sb)[2], BS &t) {
     if constexpr (FMT == MOE_FMT_BF16) {  // pieces of 8: K [32 h + 8 p, +8) of the stage
       const int k = st * WK + 32 * h;
       const uint32_t pc = (uint32_t)(b_k0 + (k < kvalid ? k : 0)) / 8;
@@ -155,9 +170,22 @@ __device__ __forceinline__ void wide_k_loop(WideLDS &lds, rsrc_t ra,
       }
     }
   };
-  auto store_a = [&](int st, const AS &t) {
+  // walk stage s: weights of stage s % nK of local column group s / nK (clamped to the last
+  // group past the walk: unused loads at in-bounds offsets)
+  auto fetch_b = [&](int s, BS &t) {
+    if constexpr (WALK) {
+      const int cgl = min(s / nK, ncgs - 1);
+      uint32_t cbx[2], sbx[2];
+      boff(cgl, cbx, sbx);
+      fetch_b_at(s - cgl * nK, cbx, sbx, t);
+    } else {
+      fetch_b_at(s, cb, sb, t);
+    }
+  };
+  // the activation tile of stage st (K position) into LDS buffer s % 2
+  auto store_a = [&](int s, int st, const AS &t) {
     const bool ok = !TAIL || st * WK + 8 * ac < kvalid;
-    uint16_t *b = abuf(st);
+    uint16_t *b = abuf(s);
 #pragma unroll
     for (int q = 0; q < AS::NQ; q++) {
       const int R = tid / AS::CPR + AS::RSTEP * q;
@@ -165,8 +193,8 @@ __device__ __forceinline__ void wide_k_loop(WideLDS &lds, rsrc_t ra,
     }
   };
   // MFMA c of a stage takes K [(WK / 2) h + 8 c, +8) in this lane.
-  auto read_a = [&](int st, int c, frag8 (&f)[4]) {
-    const uint16_t *b = abuf(st);
+  auto read_a = [&](int s, int c, frag8 (&f)[4]) {
+    const uint16_t *b = abuf(s);
 #pragma unroll
     for (int mi = 0; mi < 4; mi++)
       f[mi].q = *reinterpret_cast<const uint4 *>(b + (32 * mi + r32) * WK + wswz<WK>(r32, (WK / 16) * h + c));
@@ -199,7 +227,8 @@ __device__ __forceinline__ void wide_k_loop(WideLDS &lds, rsrc_t ra,
     }
   };
   // first: the stage starts an fp8 scale block (std::true_type or std::false_type)
-  auto compute = [&](int st, const BS &t, auto first) {
+  // walk stage s (LDS buffer s % 2) at K stage st
+  auto compute = [&](int s, int st, const BS &t, auto first) {
     if constexpr (FMT == MOE_FMT_FP8_BLOCK128 && decltype(first)::value) {
 #pragma unroll
       for (int ct = 0; ct < 2; ct++) {
@@ -217,7 +246,7 @@ __device__ __forceinline__ void wide_k_loop(WideLDS &lds, rsrc_t ra,
 #pragma unroll
     for (int c = 0; c < WK / 16; c++) {
       frag8 af[4], bf[2];
-      read_a(st, c, af);
+      read_a(s, c, af);
       dec_b(st, c, t, bf);
 #pragma unroll
       for (int mi = 0; mi < 4; mi++)
@@ -228,23 +257,51 @@ __device__ __forceinline__ void wide_k_loop(WideLDS &lds, rsrc_t ra,
   fetch_a(0, at);
   fetch_b(0, bt[0]);
   fetch_b(1, bt[1]);
-  store_a(0, at);
+  store_a(0, 0, at);
   __syncthreads();
   // Fetches past the last stage reload clamped offsets (unused) and the store after the
   // last stage fills the idle buffer with zeros, so every path keeps the same loads in flight.
-  auto stage = [&](int st, BS &b_cur, auto first) {
-    fetch_a(st + 1, at);
-    compute(st, b_cur, first);
-    fetch_b(st + 2, b_cur);
-    store_a(st + 1, at);
-    __syncthreads();
-  };
-  int st = 0;
-  for (; st + 1 < nK; st += 2) {
-    stage(st, bt[0], std::true_type{});
-    stage(st + 1, bt[1], std::false_type{});
+  if constexpr (!WALK) {
+    auto stage = [&](int st, BS &b_cur, auto first) {
+      fetch_a(st + 1, at);
+      compute(st, st, b_cur, first);
+      fetch_b(st + 2, b_cur);
+      store_a(st + 1, st + 1, at);
+      __syncthreads();
+    };
+    int st = 0;
+    for (; st + 1 < nK; st += 2) {
+      stage(st, bt[0], std::true_type{});
+      stage(st + 1, bt[1], std::false_type{});
+    }
+    if (st < nK) stage(st, bt[0], std::true_type{});
+  } else {
+    const int S = ncgs * nK;
+    auto stage = [&](int s, int st, BS &b_cur, auto first) __attribute__((always_inline)) {
+      const int stn = st + 1 == nK ? 0 : st + 1;
+      fetch_a(stn, at);
+      compute(s, st, b_cur, first);
+      fetch_b(s + 2, b_cur);
+      if (stn == 0 && s + 1 < S) {  // a column group ends and another follows
+        __syncthreads();
+        if constexpr (FMT == MOE_FMT_FP8_BLOCK128) {
+          post[0] = scur[0];
+          post[1] = scur[1];
+        }
+        epi(s / nK);
+        __syncthreads();
+      }
+      store_a(s + 1, stn, at);
+      __syncthreads();
+      return stn;
+    };
+    int s = 0, st = 0;
+    for (; s + 1 < S; s += 2) {
+      st = stage(s, st, bt[0], std::true_type{});
+      st = stage(s + 1, st, bt[1], std::false_type{});
+    }
+    if (s < S) stage(s, st, bt[0], std::true_type{});
   }
-  if (st < nK) stage(st, bt[0], std::true_type{});
   if constexpr (FMT == MOE_FMT_FP8_BLOCK128) {
     post[0] = scur[0];
     post[1] = scur[1];
@@ -378,16 +435,26 @@ __global__ __launch_bounds__(256, 2) void k_gate_up_wide(GateUpArgs a, int n_rb,
 
 // down.  Column group cg covers hidden columns [cg * 256, +256): wave w owns 64 w + [0, 64)
 // of them (two 32-column tiles); K = the slice.  The pair rows go to Y in bf16 (the combine
-// weights and sums them in fp32), as in the other prefill kernels.
+// weights and sums them in fp32), as in the other prefill kernels.  K is only the slice width
+// (2 to 8 stages), so for fp8-block a workgroup walks cgw consecutive column groups of its row
+// block in one pipeline (chunk ch of the grid: groups [ch cgw, ch cgw + cgw) past H clipped):
+// the metadata loads, the pipeline fill and the workgroup launch are paid once per walk, and
+// each group's stores overlap the next group's first weight loads.  Measured on MI355X, fp8-block
+// layer T = 4096, slice 256: 88.9 -> 82.4 us with walks of 2 groups (4: 93.9, 8: 99.7).  NVFP4
+// and bf16 keep one group per workgroup: their walk spills registers at the 256-register budget
+// and measured slower (NVFP4 prefill T = 8192, full I: 205 -> 222 us at 2 groups).
 template <int FMT>
-__global__ __launch_bounds__(256, 2) void k_down_wide(DownArgs a, int n_rb, int ncg) {
+constexpr bool kDownWalk = FMT == MOE_FMT_FP8_BLOCK128;
+
+template <int FMT>
+__global__ __launch_bounds__(256, 2) void k_down_wide(DownArgs a, int n_rb, int nch, int cgw) {
   constexpr int WK = kWideK<FMT>;
   using AS = AStage<WK>;
   __shared__ WideLDS lds;
   const int n_routed = a.cap / WM;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int idx, cg;
-  wide_position(ncg, idx, cg);
+  int idx, ch;
+  wide_position(nch, idx, ch);
   const int ridx = max(0, min(idx, n_routed - 1));  // the routed row block idx would be
   const int tp = a.total_padded[0];
   const int eb = a.block_expert[ridx * WM / a.block_m];
@@ -415,24 +482,32 @@ __global__ __launch_bounds__(256, 2) void k_down_wide(DownArgs a, int n_rb, int 
     glob = a.sdng;
   }
   const int T = a.T, H = a.H, I = a.I, Il = a.Il, P = a.T * a.k;
+  const int cg0 = ch * cgw, ncgs = min(cgw, (H + WCOLS - 1) / WCOLS - cg0);  // this walk's column groups
   const WMat<FMT> m = weight_matrix<FMT>(codes, scales, e, H, I);
   const rsrc_t ra = make_rsrc(a.h, (uint32_t)a.h_rows * Il * 2);
   uint32_t a_off[AS::NQ] = {(uint32_t)(p0 + tid / AS::CPR) * Il * 2};  // rows RSTEP apart
   const uint32_t a_stride = (uint32_t)AS::RSTEP * Il * 2;
-  int n[2];
-  uint32_t cb[2], sb[2];
-  float dg[2];
+  // weight row of tile ct of local column group cgl (columns past H read row lane % 32, unused)
+  auto wrow = [&](int cgl, int ct) __attribute__((always_inline)) {
+    const int n = (cg0 + cgl) * WCOLS + 64 * wave + 32 * ct + (lane & 31);
+    return (uint32_t)(n < H ? n : (lane & 31));
+  };
+  auto boff = [&](int cgl, uint32_t (&cb)[2], uint32_t (&sb)[2]) __attribute__((always_inline)) {
 #pragma unroll
-  for (int ct = 0; ct < 2; ct++) {
-    n[ct] = cg * WCOLS + 64 * wave + 32 * ct + (lane & 31);
-    const uint32_t row = (uint32_t)(n[ct] < H ? n[ct] : (lane & 31));  // columns past H read row lane%32 (unused)
-    cb[ct] = (row & ~15u) * (uint32_t)(FMT == MOE_FMT_BF16 ? 2 * I : FMT == MOE_FMT_FP8_BLOCK128 ? I : I / 2) +
-             (row & 15u) * 16;
-    sb[ct] = FMT == MOE_FMT_FP8_BLOCK128 ? row / 128 * (uint32_t)(I / 128) * 4
-                                         : (row & ~15u) * (uint32_t)(I / 16) + (row & 15u) * 2;
-    dg[ct] = FMT == MOE_FMT_NVFP4 ? glob[(size_t)e * H + row] : 1.f;
-  }
-  if (tid < WM) {  // destination of each pair row, read back in the epilogue
+    for (int ct = 0; ct < 2; ct++) {
+      const uint32_t row = wrow(cgl, ct);
+      cb[ct] = (row & ~15u) * (uint32_t)(FMT == MOE_FMT_BF16 ? 2 * I : FMT == MOE_FMT_FP8_BLOCK128 ? I : I / 2) +
+               (row & 15u) * 16;
+      sb[ct] = FMT == MOE_FMT_FP8_BLOCK128 ? row / 128 * (uint32_t)(I / 128) * 4
+                                           : (row & ~15u) * (uint32_t)(I / 16) + (row & 15u) * 2;
+    }
+  };
+  uint32_t cb[2], sb[2];
+  boff(0, cb, sb);
+  float dg[2];  // NVFP4: the per-row globals of the current column group; the loop's post
+#pragma unroll
+  for (int ct = 0; ct < 2; ct++) dg[ct] = FMT == MOE_FMT_NVFP4 ? glob[(size_t)e * H + wrow(0, ct)] : 1.f;
+  if (tid < WM) {  // destination of each pair row, read back in every epilogue
     const int p = p0 + tid;
     if (!is_shared) {
       lds.dst[tid] = sd < P ? sd : -1;
@@ -442,35 +517,49 @@ __global__ __launch_bounds__(256, 2) void k_down_wide(DownArgs a, int n_rb, int 
   }
   f32x16_t acc[4][2];
   zero_acc(acc);
+  // pair rows of local column group cgl through LDS (called after a barrier, which also
+  // published dst): each wave's 128 x 64 block, then 16-byte chunks (8 lanes per 128-byte row)
+  auto store_rows = [&](int cgl) __attribute__((always_inline)) {
+    uint16_t (*o)[OPITCH] = lds.o[wave];
+#pragma unroll
+    for (int mi = 0; mi < 4; mi++)
+#pragma unroll
+      for (int j = 0; j < 16; j++) {
+        const int R = 32 * mi + d_row(lane, j);
+#pragma unroll
+        for (int ct = 0; ct < 2; ct++) o[R][32 * ct + (lane & 31)] = bf16_bits(acc[mi][ct][j] * dg[ct]);
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int ch8 = lane & 7, n8 = (cg0 + cgl) * WCOLS + 64 * wave + 8 * ch8;  // this lane's 8 columns
+    if (n8 < H) {
+#pragma unroll
+      for (int q = 0; q < 16; q++) {
+        const int R = (lane >> 3) + 8 * q;
+        const int d = lds.dst[R];
+        if (d >= 0)
+          *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(a.Y) + (size_t)d * H + n8) =
+              *reinterpret_cast<const uint4 *>(&o[R][8 * ch8]);
+      }
+    }
+  };
+  // between column groups: store the finished one, clear acc, load the next group's globals
+  auto epi = [&](int cgl) __attribute__((always_inline)) {
+    store_rows(cgl);
+    zero_acc(acc);
+    if constexpr (FMT == MOE_FMT_NVFP4) {
+#pragma unroll
+      for (int ct = 0; ct < 2; ct++) dg[ct] = glob[(size_t)e * H + wrow(cgl + 1, ct)];
+    }
+  };
+  constexpr bool W = kDownWalk<FMT>;
   if (Il % WK == 0)
-    wide_k_loop<FMT, false, true>(lds, ra, a_off, a_stride, m, cb, sb, a.lo, Il / WK, Il, acc, dg);
+    wide_k_loop<FMT, false, true, W>(lds, ra, a_off, a_stride, m, cb, sb, a.lo, Il / WK, Il, acc, dg, ncgs, boff, epi);
   else
-    wide_k_loop<FMT, true, true>(lds, ra, a_off, a_stride, m, cb, sb, a.lo, (Il + WK - 1) / WK, Il, acc, dg);
-  // pair rows through LDS (the K loop ended with a barrier, which also published dst): each
-  // wave's 128 x 64 block, then 16-byte chunks (8 lanes per 128-byte row)
-  uint16_t (*o)[OPITCH] = lds.o[wave];
-#pragma unroll
-  for (int mi = 0; mi < 4; mi++)
-#pragma unroll
-    for (int j = 0; j < 16; j++) {
-      const int R = 32 * mi + d_row(lane, j);
-#pragma unroll
-      for (int ct = 0; ct < 2; ct++) o[R][32 * ct + (lane & 31)] = bf16_bits(acc[mi][ct][j] * dg[ct]);
-    }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const int ch = lane & 7, n8 = cg * WCOLS + 64 * wave + 8 * ch;  // this lane's 8 columns
-  if (n8 < H) {
-#pragma unroll
-    for (int q = 0; q < 16; q++) {
-      const int R = (lane >> 3) + 8 * q;
-      const int d = lds.dst[R];
-      if (d >= 0)
-        *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(a.Y) + (size_t)d * H + n8) =
-            *reinterpret_cast<const uint4 *>(&o[R][8 * ch]);
-    }
-  }
+    wide_k_loop<FMT, true, true, W>(lds, ra, a_off, a_stride, m, cb, sb, a.lo, (Il + WK - 1) / WK, Il, acc, dg, ncgs,
+                                    boff, epi);
+  store_rows(ncgs - 1);  // the K loop ended with a barrier
 }
 
 hipError_t launch_gate_up_wide(int fmt, const GateUpArgs &a, int n_shared_tiles, hipStream_t s) {
@@ -489,13 +578,15 @@ hipError_t launch_gate_up_wide(int fmt, const GateUpArgs &a, int n_shared_tiles,
 
 hipError_t launch_down_wide(int fmt, const DownArgs &a, int n_shared_tiles, hipStream_t s) {
   const int n_rb = a.cap / WM + n_shared_tiles, ncg = (a.H + WCOLS - 1) / WCOLS;
-  const int grid = (n_rb + 7) / 8 * 8 * ncg;
+  const int cgw = fmt == MOE_FMT_FP8_BLOCK128 ? (ncg < 2 ? ncg : 2) : 1;  // column groups per workgroup
+  const int nch = (ncg + cgw - 1) / cgw;
+  const int grid = (n_rb + 7) / 8 * 8 * nch;
   if (fmt == MOE_FMT_BF16)
-    hipLaunchKernelGGL(k_down_wide<MOE_FMT_BF16>, dim3(grid), dim3(256), 0, s, a, n_rb, ncg);
+    hipLaunchKernelGGL(k_down_wide<MOE_FMT_BF16>, dim3(grid), dim3(256), 0, s, a, n_rb, nch, cgw);
   else if (fmt == MOE_FMT_FP8_BLOCK128)
-    hipLaunchKernelGGL(k_down_wide<MOE_FMT_FP8_BLOCK128>, dim3(grid), dim3(256), 0, s, a, n_rb, ncg);
+    hipLaunchKernelGGL(k_down_wide<MOE_FMT_FP8_BLOCK128>, dim3(grid), dim3(256), 0, s, a, n_rb, nch, cgw);
   else if (fmt == MOE_FMT_NVFP4)
-    hipLaunchKernelGGL(k_down_wide<MOE_FMT_NVFP4>, dim3(grid), dim3(256), 0, s, a, n_rb, ncg);
+    hipLaunchKernelGGL(k_down_wide<MOE_FMT_NVFP4>, dim3(grid), dim3(256), 0, s, a, n_rb, nch, cgw);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

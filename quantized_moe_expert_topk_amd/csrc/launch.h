@@ -28,6 +28,18 @@ struct GateUpArgs {
   // MXFP4: x and h as two e4m3 planes with e8m0 scales per 32 (plane 1 follows plane 0)
   const uint8_t *xq, *xs;  // [2][T][H], [2][T][H/32]
   uint8_t *hq, *hs;        // [2][h_rows][Il], [2][h_rows][Il/32]
+  // Whole-layer call for one token (route1 != 0): the routed workgroups rank the router's
+  // logits themselves instead of reading an alignment; workgroup 0 writes the routing and the
+  // alignment outputs (the same arrays as sorted_ids, block_expert and total_padded above).
+  int route1;
+  const float *r_part;  // [r_ks][E] split-K partial logits, or the logits with the bias (r_ks == 1)
+  const float *r_bias;  // [E] added after the partials, or NULL
+  int r_ks;            // splits in r_part
+  int r_renorm;
+  float *r_logits;      // [E] output, or NULL
+  int32_t *r_ids;       // [k] output
+  float *r_w;           // [k] output
+  int32_t *al_sorted, *al_block, *al_counts, *al_offsets, *al_total;
 };
 
 struct DownArgs {
@@ -57,6 +69,10 @@ int forward_workspace_need(const moe_bank *routed, const moe_bank *shared, const
 
 int router_ksplit(int T, int E, int H);
 size_t router_workspace_bytes(int T, int E, int H);
+// The router GEMM of launch_route alone: split-K partials into partial when it splits K
+// (*ks > 1), else the logits with the bias added into logits.
+hipError_t launch_router(const uint16_t *x, int T, int H, const uint16_t *w, int E, const float *bias,
+                         float *logits, float *partial, int *ks, hipStream_t s);
 hipError_t launch_route(const uint16_t *x, int T, int H, const uint16_t *w, int E, const float *bias, int k,
                         int renormalize, float *logits, int32_t *ids, float *wts, float *partial,
                         hipStream_t s);

@@ -196,6 +196,12 @@ static hipError_t launch_router_gemm(const uint16_t *x, int T, int H, const uint
   return hipGetLastError();
 }
 
+hipError_t launch_router(const uint16_t *x, int T, int H, const uint16_t *w, int E, const float *bias,
+                         float *logits, float *partial, int *ks, hipStream_t s) {
+  *ks = router_ksplit(T, E, H);
+  return launch_router_gemm(x, T, H, w, E, bias, *ks, *ks > 1 ? partial : logits, s);
+}
+
 hipError_t launch_route(const uint16_t *x, int T, int H, const uint16_t *w, int E, const float *bias, int k,
                         int renormalize, float *logits, int32_t *ids, float *wts, float *partial,
                         hipStream_t s) {

@@ -15,6 +15,7 @@
 extern "C" int stub_launches(void);
 extern "C" int stub_failures(void);
 extern "C" void stub_set_workspace(const void *base, size_t bytes);
+extern "C" void stub_set_route_workspace(const void *base, size_t bytes);
 
 namespace {
 
@@ -169,6 +170,41 @@ void expert_layer(int fmt) {
   }
 }
 
+// moe_layer_forward: the one-token path (H = 1024 gives gate_up's 8-wave K split) and the
+// two calls' path, for every format, with the workspaces exact and one byte short.
+void layer_call(int fmt) {
+  const int E = 16, H = 1024, I = 256;
+  moe_bank routed = bank(fmt, E, H, I), shared = bank(fmt, 1, H, I);
+  void *x = dev(0x60), *wr = dev(0x61), *out = dev(0x62), *ws = dev(0x63), *rws = dev(0x64);
+  float *lg = static_cast<float *>(dev(0x65)), *tw = static_cast<float *>(dev(0x66));
+  int32_t *ids = static_cast<int32_t *>(dev(0x67));
+  const int lo = 0, hi = fmt == MOE_FMT_FP8_BLOCK128 ? 128 : 64;
+  for (int T : {1, 3}) {
+    const int k = 4;
+    moe_align_out al = align_desc(T, k, E, 16);
+    const size_t need = moe_workspace_bytes(&routed, &shared, T, k, 16, lo, hi);
+    const size_t rneed = moe_route_align_workspace_bytes(T, H, E, k);
+    stub_set_workspace(ws, need);
+    stub_set_route_workspace(rws, rneed);
+    const int before = stub_launches();
+    expect_rc(moe_layer_forward(x, T, wr, nullptr, k, 1, &routed, &shared, lo, hi, lg, ids, tw, &al, out,
+                                MOE_OUT_F32, rws, rneed, ws, need, nullptr),
+              MOE_OK, "layer forward");
+    expect(stub_launches() > before, "layer forward launches");
+    stub_set_workspace(nullptr, 0);
+    stub_set_route_workspace(nullptr, 0);
+    expect_rc(moe_layer_forward(x, T, wr, nullptr, k, 1, &routed, &shared, lo, hi, lg, ids, tw, &al, out,
+                                MOE_OUT_F32, rws, rneed - 1, ws, need, nullptr),
+              MOE_ERR_WORKSPACE, "layer forward with a short route workspace");
+    expect_rc(moe_layer_forward(x, T, wr, nullptr, k, 1, &routed, &shared, lo, hi, lg, ids, tw, &al, out,
+                                MOE_OUT_F32, rws, rneed, ws, need - 1, nullptr),
+              MOE_ERR_WORKSPACE, "layer forward with a short workspace");
+    expect_rc(moe_layer_forward(x, T, nullptr, nullptr, k, 1, &routed, &shared, lo, hi, lg, ids, tw, &al, out,
+                                MOE_OUT_F32, rws, rneed, ws, need, nullptr),
+              MOE_ERR_INVALID_ARG, "layer forward without a router weight");
+  }
+}
+
 void packing(int fmt) {
   const int E = 4, H = fmt == MOE_FMT_FP8_BLOCK128 ? 256 : 128, I = 128;
   moe_bank src = bank(fmt, E, H, I, MOE_LAYOUT_ROWS), dst = bank(fmt, E, H, I, MOE_LAYOUT_TILE16);
@@ -199,6 +235,7 @@ int main() {
   routing();
   for (int fmt : {MOE_FMT_NVFP4, MOE_FMT_FP8_BLOCK128, MOE_FMT_MXFP4_E8M0, MOE_FMT_BF16, MOE_FMT_Q4_0}) {
     expert_layer(fmt);
+    layer_call(fmt);
     packing(fmt);
   }
   if (stub_failures()) {

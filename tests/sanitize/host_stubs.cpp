@@ -32,6 +32,8 @@ void expect_inside(const void *base, const void *p, size_t bytes, const char *wh
   expect(q >= b && (size_t)(q - b) + bytes <= g_ws_bytes, what);
 }
 const void *g_ws_base = nullptr;
+const void *g_rws_base = nullptr;  // the route workspace the driver passed (NULL: unknown)
+size_t g_rws_bytes = 0;
 }  // namespace
 
 extern "C" {
@@ -40,6 +42,10 @@ int stub_failures(void) { return g_bad; }
 void stub_set_workspace(const void *base, size_t bytes) {
   g_ws_base = base;
   g_ws_bytes = bytes;
+}
+void stub_set_route_workspace(const void *base, size_t bytes) {
+  g_rws_base = base;
+  g_rws_bytes = bytes;
 }
 
 hipError_t hipGetDevice(int *dev) {
@@ -64,6 +70,17 @@ namespace qmoe {
 size_t router_workspace_bytes(int T, int E, int H) {
   expect(T > 0 && E > 0 && H > 0, "router sizes");
   return (size_t)16 * T * E * sizeof(float);
+}
+
+hipError_t launch_router(const uint16_t *x, int T, int H, const uint16_t *w, int E, const float *, float *logits,
+                         float *partial, int *ks, hipStream_t) {
+  expect(x && w && logits && T > 0 && H % 128 == 0 && E >= 1, "router args");
+  *ks = 2;  // the one-token path with split-K partials
+  expect(partial != nullptr, "router partials");
+  if (g_rws_base)
+    expect(partial == g_rws_base && (size_t)2 * T * E * 4 <= g_rws_bytes, "router partials inside the route workspace");
+  g_launches++;
+  return hipSuccess;
 }
 
 hipError_t launch_route(const uint16_t *x, int T, int H, const uint16_t *w, int E, const float *, int k, int,
@@ -108,6 +125,13 @@ static void check_expert_args(int T, int k, int E, int I, int lo, int Il, int bl
 hipError_t launch_gate_up(int, const GateUpArgs &a, int n_shared_sub, hipStream_t) {
   check_expert_args(a.T, a.k, a.E, a.I, a.lo, a.Il, a.block_m, a.cap, a.n_routed_sub);
   expect(a.kwaves * a.ksteps * 128 == a.H, "gate_up K split");
+  if (a.route1) {  // the one-token whole-layer path: every routing pointer set, 8 waves, 16-row blocks
+    expect(a.T == 1 && a.block_m == 16 && a.kwaves == 8 && a.k <= 64 && a.E <= 1024, "one-token routing shape");
+    expect(a.r_part && a.r_ks >= 1 && a.r_ids && a.r_w && a.al_sorted && a.al_block && a.al_counts &&
+               a.al_offsets && a.al_total,
+           "one-token routing pointers");
+    expect(a.n_routed_sub >= a.k, "a routed sub-block per pick");
+  }
   expect(a.h_rows >= a.cap + 16 * n_shared_sub, "intermediate rows");
   expect_inside(g_ws_base, a.h, (size_t)a.cap * a.Il * 2, "intermediate inside the workspace");
   g_launches++;

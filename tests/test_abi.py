@@ -86,7 +86,7 @@ def _fwd(bank=None, shared=None, T=16, k=2, lo=0, hi=128, al=None, ws=1 << 30, o
     return rc, lib.moe_last_error().decode()
 
 
-@pytest.mark.parametrize("kw,code", [
+FORWARD_REJECTS = [
     (dict(lo=8, hi=128), L.MOE_ERR_ALIGNMENT),                 # NVFP4 block is 16
     (dict(lo=64, hi=64), L.MOE_ERR_ALIGNMENT),                 # empty slice
     (dict(lo=0, hi=144), L.MOE_ERR_ALIGNMENT),                 # past I
@@ -112,9 +112,38 @@ def _fwd(bank=None, shared=None, T=16, k=2, lo=0, hi=128, al=None, ws=1 << 30, o
     (dict(x=None), L.MOE_ERR_INVALID_ARG),
     (dict(bank=_bank(layout=L.MOE_LAYOUT_ROWS)), L.MOE_ERR_UNSUPPORTED),  # kernels read TILE16 banks
     (dict(shared=_bank(E=1, layout=L.MOE_LAYOUT_ROWS)), L.MOE_ERR_UNSUPPORTED),
-])
+]
+
+
+@pytest.mark.parametrize("kw,code", FORWARD_REJECTS)
 def test_forward_rejects_bad_arguments_before_any_launch(kw, code):
     rc, msg = _fwd(**kw)
+    assert rc == code, (rc, msg)
+    assert msg
+
+
+def _layer(bank=None, shared=None, T=16, k=2, lo=0, hi=128, al=None, ws=1 << 30, out_dtype=0, x=FAKE, wr=FAKE,
+           rws=1 << 30, routed_null=False):
+    lib = L.lib()
+    bank = bank or _bank()
+    al = al or _align(T=T, k=k, E=bank.E)
+    rc = lib.moe_layer_forward(x, T, wr, None, k, 1, None if routed_null else ctypes.byref(bank),
+                               ctypes.byref(shared) if shared else None, lo, hi, FAKE, FAKE, FAKE, ctypes.byref(al),
+                               FAKE, out_dtype, FAKE, rws, FAKE, ws, None)
+    return rc, lib.moe_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code", FORWARD_REJECTS + [
+    (dict(wr=None), L.MOE_ERR_INVALID_ARG),                    # the router weight
+    (dict(rws=0), L.MOE_ERR_WORKSPACE),                        # the router's split-K partials
+    (dict(routed_null=True), L.MOE_ERR_INVALID_ARG),
+    (dict(bank=_bank(E=2048, I=128), k=2), L.MOE_ERR_UNSUPPORTED),  # the router needs E <= 1024
+    (dict(bank=_bank(E=128), k=65), L.MOE_ERR_UNSUPPORTED),          # and k <= 64
+])
+def test_layer_forward_rejects_bad_arguments_before_any_launch(kw, code):
+    """moe_layer_forward runs the checks of moe_route_align and moe_expert_forward: the same
+    codes for the forward's bad arguments, and the router's own."""
+    rc, msg = _layer(**kw)
     assert rc == code, (rc, msg)
     assert msg
 

@@ -620,7 +620,10 @@ def test_prefill_full_size_every_row(cid, T, sl, bm):
     check_close(f"prefill cfg{cid} T={T} [{lo},{hi}) bm={bm} all {T} rows", got, ref)
 
 
-@pytest.mark.parametrize("cid,T,sl", [(1, 16, (0, 128)), (2, 64, (0, 256)), (5, 16, (0, 1024))])
+@pytest.mark.parametrize("cid,T,sl", [(1, 16, (0, 128)), (2, 64, (0, 256)), (5, 16, (0, 1024)),
+                                      # one token: the whole-layer call's in-kernel routing
+                                      (2, 1, (0, 256)), (4, 1, (0, 256)), (5, 1, (0, 1024)), (6, 1, (0, 256)),
+                                      (7, 1, (0, 256))])
 def test_full_layer_matches_oracle(cid, T, sl):
     """The whole GPU path (route -> align -> forward) against the whole oracle layer,
     excluding tokens whose k-th/(k+1)-th logit gap is inside the near-tie window."""
@@ -635,6 +638,70 @@ def test_full_layer_matches_oracle(cid, T, sl):
     np.testing.assert_array_equal(layer.ids.cpu().numpy()[sure], r["ids"][sure])
     ref = O.expert_forward(inp.routed, inp.shared, inp.x, r["ids"], r["w"], lo, hi)
     check_close(f"full layer cfg{cid} T={T} [{lo},{hi})", got[sure], ref[sure])
+
+
+# fmt, E, H, I, k, T, slice, shared, bias, renormalize, block_m (None: the library's choice)
+LAYER_CALL_CASES = [
+    ("nvfp4", 256, 2048, 512, 8, 1, (0, 256), True, False, True, None),     # the Qwen3.6-shaped decode layer
+    ("nvfp4", 8, 1024, 128, 8, 1, (0, 128), False, True, False, None),      # k = E: every expert picked
+    ("nvfp4", 8, 1024, 128, 1, 1, (32, 96), True, True, True, None),        # k = 1
+    ("fp8blk", 256, 2048, 512, 8, 1, (0, 256), True, True, True, None),
+    ("mxfp4", 256, 4096, 2048, 8, 1, (0, 1024), True, False, True, None),   # the DeepSeek-V4-Flash-shaped layer
+    ("bf16", 64, 1024, 256, 6, 1, (0, 256), True, False, False, None),
+    ("q4_0", 100, 1024, 256, 8, 1, (32, 224), False, True, True, None),
+    ("nvfp4", 1000, 1024, 128, 64, 1, (0, 128), False, True, True, None),   # E = 1000, k = 64
+    # paths that enqueue the two calls: another block size, H without an 8-wave K split, T > 1
+    ("nvfp4", 256, 2048, 512, 8, 1, (0, 256), True, False, True, 32),
+    ("nvfp4", 8, 256, 128, 2, 1, (0, 128), False, False, True, None),
+    ("nvfp4", 256, 2048, 512, 8, 5, (0, 256), True, True, True, None),
+    ("mxfp4", 256, 4096, 2048, 8, 16, (0, 1024), True, False, True, None),
+]
+
+
+@pytest.mark.parametrize("case", LAYER_CALL_CASES, ids=lambda c: "-".join(str(v) for v in c))
+@pytest.mark.parametrize("ties", [False, True])
+def test_layer_forward_equals_the_two_calls(case, ties):
+    """moe_layer_forward gives exactly the outputs of moe_route_align followed by
+    moe_expert_forward (logits, ids, weights, every alignment array and the layer output, bit
+    for bit), both where one token's routing runs inside the gate_up kernel and where the call
+    enqueues the two calls.  ties: three router rows are one scaled row, so three experts
+    share the top logit (the lower index must rank first)."""
+    fmt, E, H, I, k, T, (lo, hi), shared, with_bias, renorm, bm = case
+    seed = 61
+    b = S.routed_bank(seed, fmt, E, H, I)
+    sh = S.shared_bank(seed, fmt, H, I) if shared else None
+    rb, sb = device_bank(b), (device_bank(sh) if sh is not None else None)
+    wr_np = S.router_weight(seed, E, H)
+    x_np = S.tokens(seed, T, H)
+    tied = sorted({E - 1, E // 2, 1 % E})
+    if ties:  # 8 times row 0, signed so that token 0's logit is large and positive (exact in bf16)
+        sgn = 1.0 if float(np.dot(x_np[0].astype(np.float64), wr_np[0].astype(np.float64))) >= 0 else -1.0
+        for e in tied:
+            wr_np[e] = (8 * sgn) * wr_np[0]
+    x, wr = bf16_dev(x_np), bf16_dev(wr_np)
+    bias = to_dev(S.zipf_bias(seed, E, 1.1) if not ties else np.zeros(E, np.float32)) if with_bias else None
+    bm = bm or qm.choose_block_m(T, k, E, fmt)
+    lg1, ids1, w1, al1 = qm.moe_route_align(x, wr, bias, k, bm, renorm)
+    out1 = qm.moe_expert_forward(rb, sb, x, w1, al1, lo, hi)
+    layer = qm.MoeLayer(rb, sb, wr, bias, T, k, lo, hi, renorm, block_m=bm)
+    for buf in (layer.logits, layer.w, layer.out):
+        buf.fill_(float("nan"))
+    for buf in (layer.ids, layer.align.sorted_ids, layer.align.block_expert, layer.align.counts,
+                layer.align.offsets, layer.align.total_padded):
+        buf.fill_(-7)
+    out2 = layer(x)
+    torch.cuda.synchronize()
+    assert torch.equal(layer.logits, lg1) and torch.equal(layer.ids, ids1) and torch.equal(layer.w, w1)
+    a1, a2 = align_np(al1), align_np(layer.align)
+    for key in a1:
+        np.testing.assert_array_equal(a2[key], a1[key], err_msg=key)
+    assert torch.equal(out2, out1)
+    if ties:  # equal logits rank by index
+        row = [int(e) for e in ids1[0].cpu().numpy()]
+        picked = [e for e in row if e in tied]
+        assert picked == sorted(picked), row
+        if row[0] in tied:
+            assert row[0] == tied[0], row
 
 
 @pytest.mark.parametrize("cid,T,cuts,bm", [
