@@ -393,6 +393,8 @@ FORWARD_CASES = [(1, 16, (0, 128)), (1, 16, (0, 64)), (1, 16, (64, 128)),
                  # MXFP4 with 64 slice columns per gate_up workgroup (>= 4 pairs per expert), a
                  # last column group half past the slice
                  (5, 256, (0, 96)), (5, 256, (32, 160)), (5, 256, (1024, 2048)),
+                 # MXFP4 slices of 3, 4 and 8 K steps, with K tails inside a step
+                 (5, 16, (0, 480)), (5, 64, (512, 896)), (5, 256, (32, 1024)),
                  # bf16 stacked experts (issue #62 "Suggested staging" item 1)
                  (6, 1, (0, 256)), (6, 64, (0, 256)), (6, 16, (32, 160)), (6, 8, (0, 512)),
                  # q4_0 experts (issue #62 "Suggested staging" item 3), no shared expert
