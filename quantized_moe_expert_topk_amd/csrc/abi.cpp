@@ -381,10 +381,11 @@ qmoe::DownArgs down_args(const moe_bank *routed, const moe_bank *shared, int T, 
   return a;
 }
 
-// gate_up for prepared arguments: MXFP4's activation planes, then the gate_up kernel.
+// gate_up for prepared arguments: MXFP4's activation planes (unless the router GEMM already
+// wrote them: planes_ready), then the gate_up kernel.
 int launch_gate_up_args(const moe_bank *routed, const qmoe::GateUpArgs &a, int T, const FwdPlan &p,
-                        void *workspace, hipStream_t s) {
-  if (routed->fmt == MOE_FMT_MXFP4_E8M0) {
+                        void *workspace, hipStream_t s, bool planes_ready = false) {
+  if (routed->fmt == MOE_FMT_MXFP4_E8M0 && !planes_ready) {
     char *ws = static_cast<char *>(workspace);
     const int rc = hip_status(qmoe::launch_act_mx8(a.x, T, routed->H, reinterpret_cast<uint8_t *>(ws + p.xq_off),
                                                    reinterpret_cast<uint8_t *>(ws + p.xs_off), s),
@@ -742,20 +743,31 @@ int moe_layer_forward(const void *x_bf16, int T, const void *w_router_bf16, cons
   if (T == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
   qmoe::GateUpArgs a = gate_up_args(routed, shared, x_bf16, T, k, al, slice_lo, p, workspace);
-  if (!route1_path(a, p, T, al->block_m)) {  // exactly the two calls
-    rc = moe_route_align(x_bf16, T, H, w_router_bf16, E, bias, k, renormalize, logits, topk_ids, topk_w, al,
-                         route_workspace, route_workspace_bytes, stream);
+  // MXFP4: the split-K router GEMM, which reads x anyway, also writes its activation planes
+  char *ws = static_cast<char *>(workspace);
+  const qmoe::XPlanes planes{reinterpret_cast<uint8_t *>(ws + p.xq_off), reinterpret_cast<uint8_t *>(ws + p.xs_off)};
+  const bool mx_planes = routed->fmt == MOE_FMT_MXFP4_E8M0 && qmoe::router_writes_planes(T);
+  const qmoe::XPlanes *xp = mx_planes ? &planes : nullptr;
+  char *rws = static_cast<char *>(route_workspace);
+  float *part = reinterpret_cast<float *>(rws);
+  if (!route1_path(a, p, T, al->block_m)) {  // the kernels of the two calls
+    const size_t hist_off = (moe_route_workspace_bytes(T, H, E) + 255) / 256 * 256;
+    rc = hip_status(qmoe::launch_route_align(static_cast<const uint16_t *>(x_bf16), T, H,
+                                             static_cast<const uint16_t *>(w_router_bf16), E, bias, k, renormalize,
+                                             logits, topk_ids, topk_w, part, al->block_m, al->capacity,
+                                             al->sorted_ids, al->block_expert, al->counts, al->offsets,
+                                             al->total_padded, reinterpret_cast<int32_t *>(rws + hist_off), s, xp),
+                    "route_align launch");
     if (rc) return rc;
-    rc = launch_gate_up_args(routed, a, T, p, workspace, s);
+    rc = launch_gate_up_args(routed, a, T, p, workspace, s, mx_planes);
     if (rc) return rc;
     return run_down(routed, shared, T, k, topk_w, al, slice_lo, p, out, out_dtype, workspace, s);
   }
   // one token: the router GEMM, then gate_up ranks its logits in every routed workgroup and
   // writes the routing and the alignment, which down reads
   int ks = 1;
-  float *part = static_cast<float *>(route_workspace);
   rc = hip_status(qmoe::launch_router(static_cast<const uint16_t *>(x_bf16), T, H,
-                                      static_cast<const uint16_t *>(w_router_bf16), E, bias, logits, part, &ks, s),
+                                      static_cast<const uint16_t *>(w_router_bf16), E, bias, logits, part, &ks, xp, s),
                   "router launch");
   if (rc) return rc;
   a.route1 = 1;
@@ -771,7 +783,7 @@ int moe_layer_forward(const void *x_bf16, int T, const void *w_router_bf16, cons
   a.al_counts = al->counts;
   a.al_offsets = al->offsets;
   a.al_total = al->total_padded;
-  rc = launch_gate_up_args(routed, a, T, p, workspace, s);
+  rc = launch_gate_up_args(routed, a, T, p, workspace, s, mx_planes);
   if (rc) return rc;
   return run_down(routed, shared, T, k, topk_w, al, slice_lo, p, out, out_dtype, workspace, s);
 }

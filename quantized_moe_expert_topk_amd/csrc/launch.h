@@ -69,10 +69,16 @@ int forward_workspace_need(const moe_bank *routed, const moe_bank *shared, const
 
 int router_ksplit(int T, int E, int H);
 size_t router_workspace_bytes(int T, int E, int H);
+// MXFP4 activation planes of x (ActMX layout: q [2][T][H] e4m3, s [2][T][H/32] e8m0) for the
+// router GEMM to write alongside the logits, where router_writes_planes(T).
+struct XPlanes {
+  uint8_t *q, *s;
+};
+bool router_writes_planes(int T);
 // The router GEMM of launch_route alone: split-K partials into partial when it splits K
-// (*ks > 1), else the logits with the bias added into logits.
+// (*ks > 1), else the logits with the bias added into logits; xp: also the planes, or NULL.
 hipError_t launch_router(const uint16_t *x, int T, int H, const uint16_t *w, int E, const float *bias,
-                         float *logits, float *partial, int *ks, hipStream_t s);
+                         float *logits, float *partial, int *ks, const XPlanes *xp, hipStream_t s);
 hipError_t launch_route(const uint16_t *x, int T, int H, const uint16_t *w, int E, const float *bias, int k,
                         int renormalize, float *logits, int32_t *ids, float *wts, float *partial,
                         hipStream_t s);
@@ -89,7 +95,8 @@ bool route_align_fused(int T, int E, int k);
 hipError_t launch_route_align(const uint16_t *x, int T, int H, const uint16_t *w, int E, const float *bias, int k,
                               int renormalize, float *logits, int32_t *ids, float *wts, float *partial, int BM,
                               int cap, int32_t *sorted_ids, int32_t *block_expert, int32_t *counts,
-                              int32_t *offsets, int32_t *total_padded, int32_t *hist, hipStream_t s);
+                              int32_t *offsets, int32_t *total_padded, int32_t *hist, hipStream_t s,
+                              const XPlanes *xp = nullptr);
 hipError_t launch_gate_up(int fmt, const GateUpArgs &a, int n_shared_sub, hipStream_t s);
 hipError_t launch_down(int fmt, const DownArgs &a, int n_shared_sub, hipStream_t s);
 // One token: down and the combine in one launch (16 waves per 64 hidden columns, one per

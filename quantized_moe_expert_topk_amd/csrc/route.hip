@@ -25,17 +25,22 @@ namespace qmoe {
 // One workgroup = 4 waves = 16 tokens x 64 experts x one K split; wave w owns experts
 // [16w, 16w+16).  K advances 128 per step: lane group g = l/16 loads the contiguous
 // 32-element run [kc + 32g, kc + 32g + 32) of its row for both operands.
+// PLANES: wave 0 of the first expert group also writes the MXFP4 activation planes of its
+// tokens over its K range (router_wave_partial).
+template <bool PLANES>
 __global__ __launch_bounds__(256) void k_router_partial(const uint16_t *__restrict__ x, int T, int H,
                                                         const uint16_t *__restrict__ w, int E,
                                                         const float *__restrict__ bias, int kchunk,
-                                                        float *__restrict__ part) {
+                                                        float *__restrict__ part, uint8_t *__restrict__ pq,
+                                                        uint8_t *__restrict__ ps) {
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int t0 = blockIdx.y * 16, e0 = blockIdx.x * 64 + wave * 16;
   if (e0 >= E) return;
   const int ks = blockIdx.z;
   const int kbeg = ks * kchunk;
-  const f32x4_t acc = router_wave_partial(x, T, H, w, E, t0, e0, kbeg, kbeg + kchunk);
+  const f32x4_t acc = router_wave_partial<PLANES>(x, T, H, w, E, t0, e0, kbeg, kbeg + kchunk, pq, ps,
+                                                  PLANES && blockIdx.x == 0 && wave == 0);
   const int eb = e0 + r;
   if (eb < E) {
     const float bv = (bias && ks == 0 && gridDim.z == 1) ? bias[eb] : 0.f;
@@ -167,6 +172,7 @@ static hipError_t launch_topk_ns(const float *part, int KS, int T, int E, const 
 // fp32 partials that the top-k kernel reads back (E = 256: T = 8192 4 -> 2 splits, step
 // 646 -> 640 us; T = 4096 8 -> 4 splits, 269 -> 264 us).
 static bool router_tiled(int T) { return T >= 1024; }
+bool router_writes_planes(int T) { return !router_tiled(T); }
 
 int router_ksplit(int T, int E, int H) {
   if (router_tiled(T)) {  // K ranges stay whole 64-wide stages
@@ -189,17 +195,21 @@ size_t router_workspace_bytes(int T, int E, int H) {
 // The router GEMM into part: the K-split partials [ks][T][E] when ks > 1, else the logits
 // with the bias added.
 static hipError_t launch_router_gemm(const uint16_t *x, int T, int H, const uint16_t *w, int E, const float *bias,
-                                     int ks, float *part, hipStream_t s) {
+                                     int ks, float *part, const XPlanes *xp, hipStream_t s) {
   if (router_tiled(T)) return launch_router_tiled(x, T, H, w, E, bias, ks, part, s);
   dim3 grid((E + 63) / 64, (T + 15) / 16, ks);
-  hipLaunchKernelGGL(k_router_partial, grid, dim3(256), 0, s, x, T, H, w, E, bias, H / ks, part);
+  if (xp)
+    hipLaunchKernelGGL(k_router_partial<true>, grid, dim3(256), 0, s, x, T, H, w, E, bias, H / ks, part, xp->q, xp->s);
+  else
+    hipLaunchKernelGGL(k_router_partial<false>, grid, dim3(256), 0, s, x, T, H, w, E, bias, H / ks, part, nullptr,
+                       nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_router(const uint16_t *x, int T, int H, const uint16_t *w, int E, const float *bias,
-                         float *logits, float *partial, int *ks, hipStream_t s) {
+                         float *logits, float *partial, int *ks, const XPlanes *xp, hipStream_t s) {
   *ks = router_ksplit(T, E, H);
-  return launch_router_gemm(x, T, H, w, E, bias, *ks, *ks > 1 ? partial : logits, s);
+  return launch_router_gemm(x, T, H, w, E, bias, *ks, *ks > 1 ? partial : logits, xp, s);
 }
 
 hipError_t launch_route(const uint16_t *x, int T, int H, const uint16_t *w, int E, const float *bias, int k,
@@ -207,7 +217,7 @@ hipError_t launch_route(const uint16_t *x, int T, int H, const uint16_t *w, int 
                         hipStream_t s) {
   const int ks = router_ksplit(T, E, H);
   float *part = ks > 1 ? partial : logits;
-  const hipError_t e = launch_router_gemm(x, T, H, w, E, bias, ks, part, s);
+  const hipError_t e = launch_router_gemm(x, T, H, w, E, bias, ks, part, nullptr, s);
   if (e != hipSuccess) return e;
   // with one split the GEMM already added the bias and wrote the logits in place
   return launch_topk_ns(part, ks, T, E, ks > 1 ? bias : nullptr, k, renormalize, ks > 1 ? logits : nullptr, ids, wts,
@@ -241,15 +251,26 @@ static void launch_topk_align_ns(const float *part, int KS, int T, int E, const 
 hipError_t launch_route_align(const uint16_t *x, int T, int H, const uint16_t *w, int E, const float *bias, int k,
                               int renormalize, float *logits, int32_t *ids, float *wts, float *partial, int BM,
                               int cap, int32_t *sorted_ids, int32_t *block_expert, int32_t *counts,
-                              int32_t *offsets, int32_t *total_padded, int32_t *hist, hipStream_t s) {
+                              int32_t *offsets, int32_t *total_padded, int32_t *hist, hipStream_t s,
+                              const XPlanes *xp) {
   if (!route_align_fused(T, E, k)) {
-    hipError_t e = launch_route(x, T, H, w, E, bias, k, renormalize, logits, ids, wts, partial, s);
+    hipError_t e;
+    if (xp) {  // launch_route with the planes written by its router GEMM
+      const int ks = router_ksplit(T, E, H);
+      float *part = ks > 1 ? partial : logits;
+      e = launch_router_gemm(x, T, H, w, E, bias, ks, part, xp, s);
+      if (e == hipSuccess)
+        e = launch_topk_ns(part, ks, T, E, ks > 1 ? bias : nullptr, k, renormalize, ks > 1 ? logits : nullptr, ids,
+                           wts, s);
+    } else {
+      e = launch_route(x, T, H, w, E, bias, k, renormalize, logits, ids, wts, partial, s);
+    }
     if (e != hipSuccess) return e;
     return launch_align(ids, T, k, E, BM, cap, sorted_ids, block_expert, counts, offsets, total_padded, hist, s);
   }
   const int ks = router_ksplit(T, E, H);  // the router GEMM exactly as launch_route runs it
   float *part = ks > 1 ? partial : logits;
-  const hipError_t e = launch_router_gemm(x, T, H, w, E, bias, ks, part, s);
+  const hipError_t e = launch_router_gemm(x, T, H, w, E, bias, ks, part, xp, s);
   if (e != hipSuccess) return e;
   const float *b = ks > 1 ? bias : nullptr;
   float *lo = ks > 1 ? logits : nullptr;

@@ -11,10 +11,15 @@ namespace qmoe {
 // One wave's split-K router tile: 16 tokens [t0, t0+16) x 16 experts [e0, e0+16) over K
 // [kbeg, kend) of H.  K advances 128 per step: lane group g = l/16 loads the contiguous
 // 32-element run [kc + 32g, kc + 32g + 32) of its row for both operands.  Tokens past T
-// and experts past E read zeros.
+// and experts past E read zeros.  PLANES (with emit): the wave also writes the MXFP4
+// activation planes of its tokens over [kbeg, kend) from the x runs it loaded, each lane one
+// whole 32-element block: pq [2][T][H] e4m3 (hi, then lo) and ps [2][T][H/32] e8m0, the
+// split the activation kernel makes (the same mx8_split on the same block).
+template <bool PLANES = false>
 __device__ __forceinline__ f32x4_t router_wave_partial(const uint16_t *__restrict__ x, int T, int H,
                                                        const uint16_t *__restrict__ w, int E, int t0, int e0,
-                                                       int kbeg, int kend) {
+                                                       int kbeg, int kend, uint8_t *__restrict__ pq = nullptr,
+                                                       uint8_t *__restrict__ ps = nullptr, bool emit = false) {
   const int lane = lane_id(), r = lane & 15, g = lane >> 4;
   const int ta = t0 + r, eb = e0 + r;
   const bool va = ta < T, vb = eb < E;
@@ -38,6 +43,36 @@ __device__ __forceinline__ f32x4_t router_wave_partial(const uint16_t *__restric
       if (kc + 128 * st < kend)
 #pragma unroll
         for (int s = 0; s < 4; s++) acc = mfma_bf16(a[st][s], b[st][s], acc);
+    if constexpr (PLANES) {
+      if (emit && va) {
+#pragma unroll
+        for (int st = 0; st < 2; st++) {
+          if (kc + 128 * st >= kend) break;
+          float v[32];
+#pragma unroll
+          for (int s = 0; s < 4; s++)
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+              v[8 * s + 2 * j] = __uint_as_float(a[st][s].u[j] << 16);
+              v[8 * s + 2 * j + 1] = __uint_as_float(a[st][s].u[j] & 0xFFFF0000u);
+            }
+          uint32_t qh[16], ql[16], s1, s2;
+          mx8_split<32>(v, [](float m) { return m; }, qh, ql, s1, s2);
+          const size_t k0 = (size_t)kc + 128 * st + 32 * g, o = (size_t)ta * H + k0, plane = (size_t)T * H;
+#pragma unroll
+          for (int h = 0; h < 2; h++) {
+            *reinterpret_cast<uint4 *>(pq + o + 16 * h) =
+                make_uint4(qh[8 * h] | (qh[8 * h + 1] << 16), qh[8 * h + 2] | (qh[8 * h + 3] << 16),
+                           qh[8 * h + 4] | (qh[8 * h + 5] << 16), qh[8 * h + 6] | (qh[8 * h + 7] << 16));
+            *reinterpret_cast<uint4 *>(pq + plane + o + 16 * h) =
+                make_uint4(ql[8 * h] | (ql[8 * h + 1] << 16), ql[8 * h + 2] | (ql[8 * h + 3] << 16),
+                           ql[8 * h + 4] | (ql[8 * h + 5] << 16), ql[8 * h + 6] | (ql[8 * h + 7] << 16));
+          }
+          ps[(size_t)ta * (H / 32) + k0 / 32] = (uint8_t)s1;
+          ps[(size_t)T * (H / 32) + (size_t)ta * (H / 32) + k0 / 32] = (uint8_t)s2;
+        }
+      }
+    }
   }
   return acc;
 }

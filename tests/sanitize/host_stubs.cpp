@@ -72,8 +72,11 @@ size_t router_workspace_bytes(int T, int E, int H) {
   return (size_t)16 * T * E * sizeof(float);
 }
 
+bool router_writes_planes(int T) { return T < 1024; }
+
 hipError_t launch_router(const uint16_t *x, int T, int H, const uint16_t *w, int E, const float *, float *logits,
-                         float *partial, int *ks, hipStream_t) {
+                         float *partial, int *ks, const XPlanes *xp, hipStream_t) {
+  if (xp) expect_inside(g_ws_base, xp->q, (size_t)2 * T * H, "planes inside the workspace");
   expect(x && w && logits && T > 0 && H % 128 == 0 && E >= 1, "router args");
   *ks = 2;  // the one-token path with split-K partials
   expect(partial != nullptr, "router partials");
@@ -109,7 +112,9 @@ hipError_t launch_align(const int32_t *ids, int T, int k, int E, int BM, int cap
 hipError_t launch_route_align(const uint16_t *x, int T, int H, const uint16_t *w, int E, const float *bias, int k,
                               int renormalize, float *logits, int32_t *ids, float *wts, float *partial, int BM,
                               int cap, int32_t *sorted_ids, int32_t *block_expert, int32_t *counts,
-                              int32_t *offsets, int32_t *total_padded, int32_t *hist, hipStream_t s) {
+                              int32_t *offsets, int32_t *total_padded, int32_t *hist, hipStream_t s,
+                              const XPlanes *xp) {
+  if (xp) expect(T < 1024 && xp->q && xp->s, "planes only from the split-K router");
   const hipError_t e = launch_route(x, T, H, w, E, bias, k, renormalize, logits, ids, wts, partial, s);
   if (e != hipSuccess) return e;
   return launch_align(ids, T, k, E, BM, cap, sorted_ids, block_expert, counts, offsets, total_padded, hist, s);

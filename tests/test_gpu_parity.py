@@ -657,6 +657,10 @@ LAYER_CALL_CASES = [
     ("nvfp4", 8, 256, 128, 2, 1, (0, 128), False, False, True, None),
     ("nvfp4", 256, 2048, 512, 8, 5, (0, 256), True, True, True, None),
     ("mxfp4", 256, 4096, 2048, 8, 16, (0, 1024), True, False, True, None),
+    # MXFP4's activation planes written by the split-K router GEMM (T = 256), and by the
+    # activation kernel after the tiled router (T = 1024)
+    ("mxfp4", 256, 4096, 2048, 8, 256, (0, 1024), True, False, True, None),
+    ("mxfp4", 64, 512, 256, 4, 1024, (32, 256), True, True, True, None),
 ]
 
 
