@@ -657,6 +657,10 @@ LAYER_CALL_CASES = [
     ("nvfp4", 8, 256, 128, 2, 1, (0, 128), False, False, True, None),
     ("nvfp4", 256, 2048, 512, 8, 5, (0, 256), True, True, True, None),
     ("mxfp4", 256, 4096, 2048, 8, 16, (0, 1024), True, False, True, None),
+    # mid-size batches: 1024 pairs, a block size of 48, E = 1000
+    ("nvfp4", 256, 2048, 512, 8, 128, (0, 512), True, True, True, None),
+    ("nvfp4", 256, 2048, 512, 8, 40, (256, 512), False, True, False, 48),
+    ("nvfp4", 1000, 1024, 128, 10, 100, (0, 128), False, True, True, None),
     # MXFP4's activation planes written by the split-K router GEMM (T = 256), and by the
     # activation kernel after the tiled router (T = 1024)
     ("mxfp4", 256, 4096, 2048, 8, 256, (0, 1024), True, False, True, None),
