@@ -342,7 +342,8 @@ def time_point(args, qm, torch, cfg, inst, xs, T, lo, hi, R):
         ach = k_bytes / (k_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s", frac=ach / HBM_PEAK_GBS,
                     per_launch=k_bytes)
-    roof.update(kernel=f"{kname} (gate_up grouped GEMM + SwiGLU)", kernel_us=k_ms * 1e3,
+    # algorithmic bytes of the kernel either way (the counters' traffic is compared with them)
+    roof.update(kernel=f"{kname} (gate_up grouped GEMM + SwiGLU)", kernel_us=k_ms * 1e3, alg_bytes_per_launch=k_bytes,
                 traffic=load_traffic(kname, f"cfg{cfg.cid}_T{T}_slice{Il}"))
     pt = dict(config=cfg.cid, workload=workload, format=cfg.fmt, T=T, slice=[lo, hi], block_m=bm,
               dtype=DTYPES[(cfg.fmt, wide)], ms_per_step=ms, tokens_per_s=T / (ms * 1e-3),
