@@ -25,8 +25,9 @@ namespace qmoe {
 // One workgroup = 4 waves = 16 tokens x 64 experts x one K split; wave w owns experts
 // [16w, 16w+16).  K advances 128 per step: lane group g = l/16 loads the contiguous
 // 32-element run [kc + 32g, kc + 32g + 32) of its row for both operands.
-// PLANES: wave 0 of the first expert group also writes the MXFP4 activation planes of its
-// tokens over its K range (router_wave_partial).
+// PLANES: the 4 waves of the first expert group also write the MXFP4 activation planes of
+// their tokens over their K range, a quarter of the steps each (router_wave_partial; measured on
+// MI355X against wave 0 alone: DeepSeek-shaped layer T = 256, 373.3 -> 371.9 us per step).
 template <bool PLANES>
 __global__ __launch_bounds__(256) void k_router_partial(const uint16_t *__restrict__ x, int T, int H,
                                                         const uint16_t *__restrict__ w, int E,
@@ -40,7 +41,7 @@ __global__ __launch_bounds__(256) void k_router_partial(const uint16_t *__restri
   const int ks = blockIdx.z;
   const int kbeg = ks * kchunk;
   const f32x4_t acc = router_wave_partial<PLANES>(x, T, H, w, E, t0, e0, kbeg, kbeg + kchunk, pq, ps,
-                                                  PLANES && blockIdx.x == 0 && wave == 0);
+                                                  PLANES && blockIdx.x == 0 ? wave : -1);
   const int eb = e0 + r;
   if (eb < E) {
     const float bv = (bias && ks == 0 && gridDim.z == 1) ? bias[eb] : 0.f;

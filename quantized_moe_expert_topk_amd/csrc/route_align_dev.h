@@ -11,15 +11,16 @@ namespace qmoe {
 // One wave's split-K router tile: 16 tokens [t0, t0+16) x 16 experts [e0, e0+16) over K
 // [kbeg, kend) of H.  K advances 128 per step: lane group g = l/16 loads the contiguous
 // 32-element run [kc + 32g, kc + 32g + 32) of its row for both operands.  Tokens past T
-// and experts past E read zeros.  PLANES (with emit): the wave also writes the MXFP4
-// activation planes of its tokens over [kbeg, kend) from the x runs it loaded, each lane one
-// whole 32-element block: pq [2][T][H] e4m3 (hi, then lo) and ps [2][T][H/32] e8m0, the
-// split the activation kernel makes (the same mx8_split on the same block).
+// and experts past E read zeros.  PLANES: the wave also writes the MXFP4 activation planes of
+// its tokens for every 128-wide step s of [kbeg, kend) with s % 4 == plane_wave (the 4 waves of
+// a workgroup that load the same x rows share the work; -1: none), from the x runs it loaded,
+// each lane one whole 32-element block: pq [2][T][H] e4m3 (hi, then lo) and ps [2][T][H/32]
+// e8m0, the split the activation kernel makes (the same mx8_split on the same block).
 template <bool PLANES = false>
 __device__ __forceinline__ f32x4_t router_wave_partial(const uint16_t *__restrict__ x, int T, int H,
                                                        const uint16_t *__restrict__ w, int E, int t0, int e0,
                                                        int kbeg, int kend, uint8_t *__restrict__ pq = nullptr,
-                                                       uint8_t *__restrict__ ps = nullptr, bool emit = false) {
+                                                       uint8_t *__restrict__ ps = nullptr, int plane_wave = -1) {
   const int lane = lane_id(), r = lane & 15, g = lane >> 4;
   const int ta = t0 + r, eb = e0 + r;
   const bool va = ta < T, vb = eb < E;
@@ -44,10 +45,11 @@ __device__ __forceinline__ f32x4_t router_wave_partial(const uint16_t *__restric
 #pragma unroll
         for (int s = 0; s < 4; s++) acc = mfma_bf16(a[st][s], b[st][s], acc);
     if constexpr (PLANES) {
-      if (emit && va) {
+      if (plane_wave >= 0 && va) {
 #pragma unroll
         for (int st = 0; st < 2; st++) {
           if (kc + 128 * st >= kend) break;
+          if ((((kc - kbeg) >> 7) + st) % 4 != plane_wave) continue;
           float v[32];
 #pragma unroll
           for (int s = 0; s < 4; s++)
