@@ -38,7 +38,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0}
 RIDGE_FLOP_PER_BYTE = MFMA_PEAK_TFLOPS["bf16"] * 1e12 / (HBM_PEAK_GBS * 1e9)
 # the sources each gate_up kernel is built from (counter summaries are keyed on their hash)
-KERNEL_SOURCES = {"k_gate_up": ("expert_kernels.h", "expert_mxfp4.hip", "device_common.h"),
+KERNEL_SOURCES = {"k_gate_up": ("expert_kernels.h", "expert_mxfp4.hip", "device_common.h", "route_align_dev.h"),
                   "k_gate_up_wide": ("expert_wide.hip", "device_common.h")}
 WIDE_FORMATS = ("nvfp4", "fp8blk", "bf16")  # formats whose 128-row align blocks run the wide GEMMs
 

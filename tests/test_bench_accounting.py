@@ -45,6 +45,7 @@ def test_kernel_source_hash_ignores_comments_not_code(tmp_path, monkeypatch):
     (csrc / "device_common.h").write_text("#pragma once\nint helper(int x) { return x + 1; }\n")
     (csrc / "expert_kernels.h").write_text("// streaming\n__global__ void k(int *p) { p[0] = 1; }\n")
     (csrc / "expert_mxfp4.hip").write_text('#include "expert_kernels.h"\n')
+    (csrc / "route_align_dev.h").write_text("#pragma once\nint rank(int x) { return x; }\n")
     (csrc / "expert_wide.hip").write_text("/* wide */\n__global__ void w(int *p) { p[0] = 2; }\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     h0, w0 = bench.kernel_source_hash("k_gate_up"), bench.kernel_source_hash("k_gate_up_wide")
@@ -60,3 +61,6 @@ def test_kernel_source_hash_ignores_comments_not_code(tmp_path, monkeypatch):
     assert bench.kernel_source_hash("k_gate_up") != h1
     (csrc / "device_common.h").write_text("#pragma once\nint helper(int x) { return x + 2; }\n")
     assert bench.kernel_source_hash("k_gate_up_wide") != w0
+    h2 = bench.kernel_source_hash("k_gate_up")
+    (csrc / "route_align_dev.h").write_text("#pragma once\nint rank(int x) { return -x; }\n")
+    assert bench.kernel_source_hash("k_gate_up") != h2  # the routing helpers gate_up includes
