@@ -50,13 +50,15 @@ __global__ __launch_bounds__(1024) void k_align_scan(int32_t *__restrict__ hist,
   const int e = threadIdx.x;
   int run = 0;
   if (e < E) {
-    // exclusive prefix over chunks, 8 independent loads at a time
-    for (int c0 = 0; c0 < nchunk; c0 += 8) {
-      int v[8];
+    // exclusive prefix over chunks, 32 independent loads at a time: each batch is one round trip
+    // to the histograms the previous kernel wrote (T = 8192, k = 8: 64 chunks in 2 round trips;
+    // measured 7.2 -> 6.3 us against batches of 8)
+    for (int c0 = 0; c0 < nchunk; c0 += 32) {
+      int v[32];
 #pragma unroll
-      for (int u = 0; u < 8; u++) v[u] = c0 + u < nchunk ? hist[(size_t)(c0 + u) * E + e] : 0;
+      for (int u = 0; u < 32; u++) v[u] = c0 + u < nchunk ? hist[(size_t)(c0 + u) * E + e] : 0;
 #pragma unroll
-      for (int u = 0; u < 8; u++) {
+      for (int u = 0; u < 32; u++) {
         if (c0 + u < nchunk) hist[(size_t)(c0 + u) * E + e] = run;  // where chunk c's pairs of e start
         run += v[u];
       }
