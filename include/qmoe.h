@@ -340,7 +340,8 @@ int moe_expert_down(const moe_bank *routed, const moe_bank *shared, int T, int k
  * moe_route; *al receives the alignment), and the same outputs bit for bit: logits, topk_ids
  * and topk_w, every array of *al, and out.
  *   route_workspace >= moe_route_align_workspace_bytes(T, H, E, k) bytes;
- *   workspace       >= moe_workspace_bytes(routed, shared, T, k, al->block_m, lo, hi) bytes.
+ *   workspace       >= moe_workspace_bytes(routed, shared, T, k, al->block_m, lo, hi) bytes;
+ *   the two must not overlap (kernels of the call use both at once), else MOE_ERR_INVALID_ARG.
  * For one token (T = 1) on 16-row blocks, when the gate_up launch takes 8 waves per
  * workgroup, the top-k and the alignment run inside the gate_up kernel: each routed
  * workgroup sums the router's partial logits and ranks them itself, and the first writes the

@@ -738,6 +738,10 @@ int moe_layer_forward(const void *x_bf16, int T, const void *w_router_bf16, cons
   if (route_workspace_bytes < rneed)
     return fail(MOE_ERR_WORKSPACE, "moe_layer_forward: route workspace %zu < %zu", route_workspace_bytes, rneed);
   if (rneed && !route_workspace) return fail(MOE_ERR_INVALID_ARG, "moe_layer_forward: route workspace is NULL");
+  // gate_up reads the router's partials while it writes the expert workspace (one token), and the
+  // router writes MXFP4's planes into it beside its partials: the two must not share bytes
+  if (rneed && p.total && overlap(route_workspace, rneed, workspace, p.total))
+    return fail(MOE_ERR_INVALID_ARG, "moe_layer_forward: route workspace and workspace overlap");
   rc = check_device();
   if (rc) return rc;
   if (T == 0) return ok();

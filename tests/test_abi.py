@@ -123,13 +123,13 @@ def test_forward_rejects_bad_arguments_before_any_launch(kw, code):
 
 
 def _layer(bank=None, shared=None, T=16, k=2, lo=0, hi=128, al=None, ws=1 << 30, out_dtype=0, x=FAKE, wr=FAKE,
-           rws=1 << 30, routed_null=False):
+           rws=1 << 30, routed_null=False, ws_ptr=FAKE + (1 << 31)):
     lib = L.lib()
     bank = bank or _bank()
     al = al or _align(T=T, k=k, E=bank.E)
     rc = lib.moe_layer_forward(x, T, wr, None, k, 1, None if routed_null else ctypes.byref(bank),
                                ctypes.byref(shared) if shared else None, lo, hi, FAKE, FAKE, FAKE, ctypes.byref(al),
-                               FAKE, out_dtype, FAKE, rws, FAKE, ws, None)
+                               FAKE, out_dtype, FAKE, rws, ws_ptr, ws, None)
     return rc, lib.moe_last_error().decode()
 
 
@@ -139,6 +139,7 @@ def _layer(bank=None, shared=None, T=16, k=2, lo=0, hi=128, al=None, ws=1 << 30,
     (dict(routed_null=True), L.MOE_ERR_INVALID_ARG),
     (dict(bank=_bank(E=2048, I=128), k=2), L.MOE_ERR_UNSUPPORTED),  # the router needs E <= 1024
     (dict(bank=_bank(E=128), k=65), L.MOE_ERR_UNSUPPORTED),          # and k <= 64
+    (dict(ws_ptr=FAKE + 64), L.MOE_ERR_INVALID_ARG),                # the two workspaces overlap
 ])
 def test_layer_forward_rejects_bad_arguments_before_any_launch(kw, code):
     """moe_layer_forward runs the checks of moe_route_align and moe_expert_forward: the same
