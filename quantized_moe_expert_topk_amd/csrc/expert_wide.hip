@@ -117,6 +117,15 @@ struct NoEpi {
   __device__ void operator()(int) const {}
 };
 
+// Wave priority over a stage's MFMA block: with two workgroups on a CU, the wave that holds
+// its operands in registers issues its matrix ops ahead of the other workgroup's loads and
+// address math, so the matrix core idles less.  Measured on MI355X (gate_up / down, us):
+// fp8-block T = 4096, slice 256: 112.9 / 82.2 -> 103.5 / 81.6; bf16 T = 8192, full I:
+// 459 / 306 -> 453 / 289.  NVFP4 runs without it: its in-register decode of the weights is
+// vector work inside that block, and the raised priority slowed it (332 / 208 -> 337 / 214).
+template <int FMT>
+constexpr bool kWidePrio = FMT == MOE_FMT_FP8_BLOCK128 || FMT == MOE_FMT_BF16;
+
 template <int FMT, bool TAIL, bool AFFINE, bool WALK = false, class BOff = NoBOff, class Epi = NoEpi>
 __device__ __forceinline__ void wide_k_loop(WideLDS &lds, rsrc_t ra,
                                             const uint32_t (&a_off)[AStage<kWideK<FMT>>::NQ], uint32_t a_stride,
@@ -243,6 +252,7 @@ __device__ __forceinline__ void wide_k_loop(WideLDS &lds, rsrc_t ra,
           for (int j = 0; j < 16; j++) acc[mi][ct][j] *= r;
       }
     }
+    if constexpr (kWidePrio<FMT>) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int c = 0; c < WK / 16; c++) {
       frag8 af[4], bf[2];
@@ -253,6 +263,7 @@ __device__ __forceinline__ void wide_k_loop(WideLDS &lds, rsrc_t ra,
 #pragma unroll
         for (int ct = 0; ct < 2; ct++) acc[mi][ct] = mfma32_bf16(af[mi], bf[ct], acc[mi][ct]);
     }
+    if constexpr (kWidePrio<FMT>) __builtin_amdgcn_s_setprio(0);
   };
   fetch_a(0, at);
   fetch_b(0, bt[0]);
