@@ -150,6 +150,37 @@ __global__ __launch_bounds__(256, 2) void k_router_tiled(const uint16_t *__restr
   if (st < nK) stage(st, at[0], bt[0], at[1], bt[1]);  // odd stage count: the last one, peeled
   float *dst = part + (size_t)blockIdx.z * T * E;
   const bool add_bias = bias && gridDim.z == 1;
+  static_assert(sizeof(TileLDS) >= sizeof(float) * TM * TW, "the output tile fits the stage buffers");
+  if (E % 4 == 0 && (reinterpret_cast<uintptr_t>(part) & 15) == 0) {
+    // The tile leaves through LDS (the stage buffers, 64 KB = 128 x 128 fp32; the K loop ended
+    // with a barrier) as 16-byte pieces of whole rows, 32 lanes per row of 128 experts, instead of
+    // 64-byte pieces of four rows per store (the path below, for other E or an unaligned part).
+    // Measured on MI355X, E = 256, 16.8 MB of partials: T = 8192 27.0 -> 20.6 us, T = 4096
+    // 21.0 -> 14.5 us (a timing copy without any stores: 19.9 and 13.0 us).
+    float(*ot)[TW] = reinterpret_cast<float(*)[TW]>(&lds);
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) ot[64 * wm + 16 * i + 4 * g + jj][64 * wn + 16 * j + r] = acc[i][j][jj];
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < TM * TW / 4 / 256; q++) {
+      const int c = tid + 256 * q, row = c / (TW / 4), e = e0 + 4 * (c % (TW / 4)), t = t0 + row;
+      if (t < T && e < E) {
+        float4 v = *reinterpret_cast<const float4 *>(&ot[row][e - e0]);
+        if (add_bias) {
+          v.x += bias[e];
+          v.y += bias[e + 1];
+          v.z += bias[e + 2];
+          v.w += bias[e + 3];
+        }
+        *reinterpret_cast<float4 *>(&dst[(size_t)t * E + e]) = v;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const int e = e0 + 64 * wn + 16 * j + r;
