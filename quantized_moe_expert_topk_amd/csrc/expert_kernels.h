@@ -900,11 +900,23 @@ __device__ __forceinline__ bool down_wave(const DownArgs &a, int sb, int n0, uin
   return true;
 }
 
+// Row pitch (floats) of a wave's 16 x 64 output tile in LDS: 68 puts the four row groups a
+// result register spans (rows 4 apart) two by two in different bank halves, and keeps rows
+// 16-byte aligned.
+constexpr int kYPitch = 16 * DNT + 4;
+
+// The pair rows leave through LDS for MXFP4 only.  Measured on MI355X (whole step, same box):
+// DeepSeek-shaped layer T = 256 371.6 -> 369.7 us, T = 16 145.6 -> 144.7 us; NVFP4 T = 64
+// 62.2 -> 62.9 us (its 2-step instance crosses 128 registers), fp8-block and q4_0 unchanged.
+template <int FMT>
+constexpr bool kDownStagedY = FMT == MOE_FMT_MXFP4_E8M0;
+
 template <int FMT, int COUNT, bool NTW>
 __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lsc[4 * down_lsc_bytes<FMT, COUNT>()];
+  __shared__ __attribute__((aligned(16))) float ytile[kDownStagedY<FMT> ? 4 : 1][16][kYPitch];  // per wave: its rows
   const int lane = lane_id(), wave = threadIdx.x >> 6;
-  const int r = lane & 15;
+  const int r = lane & 15, g = lane >> 4;
   const int sb = a.cols_fastest ? blockIdx.y : blockIdx.x;
   const int n0 = (a.cols_fastest ? blockIdx.x : blockIdx.y) * 64 * DNT + wave * 16 * DNT;  // first output column
   if (n0 >= a.H) return;
@@ -914,14 +926,42 @@ __global__ __launch_bounds__(256, kMinWaves) void k_down(DownArgs a) {
   if (!down_wave<FMT, COUNT, NTW>(a, sb, n0, &lsc[wave * down_lsc_bytes<FMT, COUNT>()], acc, dst, dglob, ntile))
     return;
   const int H = a.H;
+  if constexpr (!kDownStagedY<FMT>) {
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
-    if (dst[j] < 0) continue;
+    for (int j = 0; j < 4; j++) {
+      if (dst[j] < 0) continue;
 #pragma unroll
-    for (int t = 0; t < DNT; t++) {
-      if (t >= ntile) break;
-      a.Y[(size_t)dst[j] * H + n0 + 16 * t + r] = acc[t][j] * dglob[t];
+      for (int t = 0; t < DNT; t++) {
+        if (t >= ntile) break;
+        a.Y[(size_t)dst[j] * H + n0 + 16 * t + r] = acc[t][j] * dglob[t];
+      }
     }
+    return;
+  }
+  // The pair rows through LDS: register j of lane (r, g) is row 4g + j, column 16t + r, so the
+  // direct stores above write 64-byte pieces of four rows; here each store writes 16 bytes a
+  // lane, 16 lanes per row, whole 256-byte row pieces of 4 rows.
+  float(*yt)[kYPitch] = ytile[wave];
+#pragma unroll
+  for (int t = 0; t < DNT; t++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) yt[4 * g + j][16 * t + r] = acc[t][j] * dglob[t];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int c4 = 4 * r;  // this lane's 4 columns of a row
+#pragma unroll
+  for (int u = 0; u < 4; u++) {
+    // row 4u + g: the lanes of row group u hold its destination as their dst[g]
+    int d = -1;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int v = __shfl(dst[j], 16 * u);
+      d = g == j ? v : d;
+    }
+    if (d >= 0 && c4 < 16 * ntile)
+      *reinterpret_cast<float4 *>(&a.Y[(size_t)d * H + n0 + c4]) =
+          *reinterpret_cast<const float4 *>(&yt[4 * u + g][c4]);
   }
 }
 
