@@ -37,7 +37,9 @@ __global__ __launch_bounds__(256) void k_router_partial(const uint16_t *__restri
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int t0 = blockIdx.y * 16, e0 = blockIdx.x * 64 + wave * 16;
-  if (e0 >= E) return;
+  // a wave past the last expert has no logits to compute, but in the first expert group it still
+  // writes its share of the activation planes (its weight loads read zeros)
+  if (e0 >= E && !(PLANES && blockIdx.x == 0)) return;
   const int ks = blockIdx.z;
   const int kbeg = ks * kchunk;
   const f32x4_t acc = router_wave_partial<PLANES>(x, T, H, w, E, t0, e0, kbeg, kbeg + kchunk, pq, ps,

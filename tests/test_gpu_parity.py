@@ -665,6 +665,13 @@ LAYER_CALL_CASES = [
     # activation kernel after the tiled router (T = 1024)
     ("mxfp4", 256, 4096, 2048, 8, 256, (0, 1024), True, False, True, None),
     ("mxfp4", 64, 512, 256, 4, 1024, (32, 256), True, True, True, None),
+    # MXFP4 with fewer than 64 experts: waves of the router's first expert group that have no
+    # experts still write their share of the activation planes (at H = 4096 the router splits K
+    # 16 ways, 256 each: waves 0 and 1 own a 128-wide step; E <= 16 leaves wave 1 without experts)
+    ("mxfp4", 16, 4096, 256, 4, 1, (0, 256), True, True, True, None),
+    ("mxfp4", 16, 4096, 256, 4, 5, (0, 256), True, False, True, None),
+    ("mxfp4", 8, 4096, 256, 2, 64, (32, 256), False, True, True, None),
+    ("mxfp4", 40, 4096, 256, 4, 64, (0, 256), False, False, True, None),
 ]
 
 
@@ -699,6 +706,8 @@ def test_layer_forward_equals_the_two_calls(case, ties):
     for buf in (layer.ids, layer.align.sorted_ids, layer.align.block_expert, layer.align.counts,
                 layer.align.offsets, layer.align.total_padded):
         buf.fill_(-7)
+    for buf in (layer.ws, layer.route_ws):  # no byte the call should write is left over (0xFF: e4m3 NaN)
+        buf.fill_(0xFF)
     out2 = layer(x)
     torch.cuda.synchronize()
     assert torch.equal(layer.logits, lg1) and torch.equal(layer.ids, ids1) and torch.equal(layer.w, w1)
