@@ -5,6 +5,7 @@ device tensors.  Argument marshalling only; every step runs in the gfx950 kernel
 from __future__ import annotations
 
 import ctypes
+import os
 from dataclasses import dataclass
 
 import torch
@@ -13,6 +14,16 @@ from . import _lib
 from ._lib import (MOE_FMT, MOE_LAYOUT_ROWS, MOE_LAYOUT_TILE16, MOE_OUT_BF16, MOE_OUT_F32, MoeAlignOutStruct,
                    MoeBankStruct, check, lib)
 
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    """A device workspace.  With QMOE_POISON_WORKSPACE set (the test session sets it) every byte
+    starts as 0xFF (e4m3 NaN, int32 -1), so that a kernel reading a byte nobody wrote shows up in
+    its results instead of passing on leftovers of an earlier call."""
+    ws = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    if os.environ.get("QMOE_POISON_WORKSPACE"):
+        ws.fill_(0xFF)
+    return ws
 
 def _ptr(t: torch.Tensor | None):
     if t is None:
@@ -126,7 +137,7 @@ def moe_route(x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor | None
     _need(topk_w, torch.float32, (T, k), "topk_w")
     need = moe_route_workspace_bytes(T, H, E)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = _workspace(need, dev)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     check("moe_route", lib().moe_route(_ptr(x), T, H, _ptr(w_router), E, _ptr(bias), k, int(renormalize),
                                        _ptr(logits), _ptr(topk_ids), _ptr(topk_w), _ptr(workspace), ws_bytes,
@@ -173,7 +184,7 @@ def moe_align(topk_ids: torch.Tensor, E: int, block_m: int, out: AlignOut | None
     out = alloc_align(T, k, E, block_m, topk_ids.device) if out is None else out
     need = moe_align_workspace_bytes(T, k, E)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=topk_ids.device)
+        workspace = _workspace(need, topk_ids.device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = out.struct()
     check("moe_align", lib().moe_align(_ptr(topk_ids), T, k, E, ctypes.byref(st), _ptr(workspace), ws_bytes,
@@ -206,7 +217,7 @@ def moe_route_align(x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor 
     out = alloc_align(T, k, E, block_m, dev) if out is None else out
     need = moe_route_align_workspace_bytes(T, H, E, k)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = _workspace(need, dev)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = out.struct()
     check("moe_route_align", lib().moe_route_align(_ptr(x), T, H, _ptr(w_router), E, _ptr(bias), k, int(renormalize),
@@ -228,7 +239,7 @@ def moe_workspace_bytes(routed: DeviceBank, shared: DeviceBank | None, T: int, k
 def _fwd_common(routed, shared, T, k, align, slice_lo, slice_hi, workspace, device):
     need = moe_workspace_bytes(routed, shared, T, k, align.block_m, slice_lo, slice_hi)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+        workspace = _workspace(need, device)
     rs, ss, al = routed.struct(), (shared.struct() if shared is not None else None), align.struct()
     return workspace, rs, ss, al
 
@@ -349,10 +360,8 @@ class MoeLayer:
         self.ids = torch.empty((T, k), dtype=torch.int32, device=dev)
         self.w = torch.empty((T, k), dtype=torch.float32, device=dev)
         self.align = alloc_align(T, k, E, self.block_m, dev)
-        self.route_ws = torch.empty(max(moe_route_align_workspace_bytes(T, routed.H, E, k), 1), dtype=torch.uint8,
-                                    device=dev)
-        self.ws = torch.empty(max(moe_workspace_bytes(routed, shared, T, k, self.block_m, slice_lo, slice_hi), 1),
-                              dtype=torch.uint8, device=dev)
+        self.route_ws = _workspace(moe_route_align_workspace_bytes(T, routed.H, E, k), dev)
+        self.ws = _workspace(moe_workspace_bytes(routed, shared, T, k, self.block_m, slice_lo, slice_hi), dev)
         self.out = torch.empty((T, routed.H), dtype=out_dtype, device=dev)
 
     def __call__(self, x: torch.Tensor, stream=None) -> torch.Tensor:
