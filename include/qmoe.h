@@ -225,7 +225,7 @@ int moe_align(const int32_t *topk_ids, int T, int k, int E, const moe_align_out 
 /* moe_route_align -- moe_route followed by moe_align on its topk_ids, in one call, for the
  * decode step: same arguments, outputs and requirements as the two calls (the route
  * arguments, then the align descriptor *out, whose every array is fully written), and
- * results identical to them bit for bit.  For 1 <= T <= 16, E <= 512 and T*k <= 1024 the
+ * results identical to them bit for bit.  For 1 <= T <= 8, E <= 512 and T*k <= 1024 the
  * top-k selection and the counting sort run in one workgroup with the picks kept on chip
  * (one kernel launch fewer than the two calls); otherwise it enqueues exactly what the two
  * calls enqueue.

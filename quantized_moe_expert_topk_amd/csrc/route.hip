@@ -12,7 +12,7 @@
 //   k_topk            sums the KS partials in a fixed order (plus bias), writes the
 //                     logits, then one wave per token selects k experts by k rounds of a
 //                     wave-wide (value, lower index) maximum built from DPP row steps.
-//   k_topk_align      for T <= 16: k_topk's work for every token in one workgroup of 1024
+//   k_topk_align      for T <= 8 (it handles up to 16): k_topk's work for every token in one workgroup of 1024
 //                     threads, then moe_align's single-workgroup counting sort on the picks,
 //                     which stay in LDS (moe_route_align; the same results as k_topk followed
 //                     by k_align_small, one launch and one global round trip fewer).
@@ -232,7 +232,11 @@ hipError_t launch_topk(const float *logits, int T, int E, const float *bias, int
   return launch_topk_ns(logits, 1, T, E, bias, k, renormalize, nullptr, ids, wts, s);
 }
 
-bool route_align_fused(int T, int E, int k) { return T >= 1 && T <= 16 && E <= 512 && T * k <= 1024; }
+// The one workgroup loads every token's split-K partials itself (T x E x splits), so past a few
+// tokens the parallel top-k workgroups and k_align_small win.  Measured on MI355X, E = 256, k = 8
+// (step, us): T = 8 fused 36.5 vs 37.0; T = 16 fused 45.2 vs 43.1 (NVFP4 decode layer) and 134.7 vs
+// 132.5 (DeepSeek-shaped MXFP4 layer).
+bool route_align_fused(int T, int E, int k) { return T >= 1 && T <= 8 && E <= 512 && T * k <= 1024; }
 
 template <int NS>
 static void launch_topk_align_ns(const float *part, int KS, int T, int E, const float *bias, int k, int renormalize,

@@ -189,7 +189,7 @@ def test_align_is_bit_exact(T, k, E, bm, kind):
     # block sizes that are not powers of two
     (3, 256, 8, 2048, True, True, 48), (40, 256, 8, 1024, False, True, 176)])
 def test_route_align_equals_route_then_align(T, E, k, H, with_bias, renorm, bm):
-    """moe_route_align (one top-k + align workgroup for T <= 16, E <= 512, T*k <= 1024) gives
+    """moe_route_align (one top-k + align workgroup for T <= 8, E <= 512, T*k <= 1024) gives
     exactly the outputs of moe_route followed by moe_align, on both sides of that boundary."""
     x, wr = bf16_dev(S.tokens(5, T, H)), bf16_dev(S.router_weight(5, E, H))
     bias = to_dev(S.zipf_bias(5, E, 1.1)) if with_bias else None
