@@ -115,7 +115,10 @@ def test_route_matches_oracle(cid, T):
 
 @pytest.mark.parametrize("T,E,H,k,with_bias", [(1500, 200, 1024, 6, True), (1024, 256, 4096, 8, False),
                                                (2077, 64, 384, 4, False), (1031, 100, 256, 64, True),
-                                               (1100, 300, 512, 8, True)])
+                                               (1100, 300, 512, 8, True),
+                                               # E % 4 != 0: the output tile's direct stores instead of
+                                               # the LDS-staged 16-byte ones
+                                               (1030, 61, 256, 3, True), (1040, 130, 512, 8, False)])
 def test_tiled_router_shapes_match_oracle(T, E, H, k, with_bias):
     """Batches of 1024 tokens and more run the router on the LDS-tiled GEMM (split over
     K): ragged token and expert tiles, k up to 64, more than 256 experts, with and without a
