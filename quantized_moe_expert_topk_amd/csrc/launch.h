@@ -55,7 +55,7 @@ struct DownArgs {
   const int32_t *sorted_ids, *block_expert, *total_padded;
   int block_m, cap, n_routed_sub;
   int lo, Il;
-  int cols_fastest;  // as in GateUpArgs
+  int cols_fastest;  // as in GateUpArgs; k_down then keeps the column groups of a sub-block on one XCD
   int nt_weights;    // as in GateUpArgs
   float *Y;  // [T * k + T_shared, H] unweighted pair rows: fp32 (streaming kernels) or bf16 (prefill GEMMs)
 };
