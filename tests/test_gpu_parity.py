@@ -567,6 +567,29 @@ def test_random_shapes_match_oracle(seed):
     check_close(f"random {fmt} E={E} H={H} I={I} [{lo},{hi}) k={k} T={T} bm={bm} shared={shared}", got, ref)
 
 
+@pytest.mark.parametrize("fmt,E,H,I,lo,hi,k,T,shared", [
+    ("mxfp4", 40, 1152, 640, 0, 640, 6, 100, True),     # 5 column groups, the last one half outside H
+    ("nvfp4", 24, 2304, 1024, 128, 768, 8, 70, False),  # 9 column groups, slice inside I
+    ("q4_0", 16, 1280, 512, 0, 512, 4, 130, True),      # 5 column groups
+])
+def test_down_column_groups_on_one_xcd(fmt, E, H, I, lo, hi, k, T, shared):
+    """Slices of at least 512 with at least 512 pairs launch the streaming kernels with the column
+    group as the fastest grid index, and down then maps its linear workgroup index so that the
+    column groups of a sub-block share one XCD.  Column-group and sub-block counts that are not
+    multiples of 8 exercise the remap and the plain order past the last whole group of 8."""
+    assert hi - lo >= 512 and T * k >= 512
+    seed = 71
+    b = S.routed_bank(seed, fmt, E, H, I)
+    sh = S.shared_bank(seed, fmt, H, I) if shared else None
+    x = S.tokens(seed, T, H)
+    _, ids, w, _ = O.route(x, S.router_weight(seed, E, H), None, k, True)
+    ref = O.expert_forward(b, sh, x, ids, w, lo, hi)
+    al = qm.moe_align(to_dev(ids.astype(np.int32).reshape(T, k)), E, 16)
+    got = qm.moe_expert_forward(device_bank(b), device_bank(sh) if sh is not None else None, bf16_dev(x),
+                                to_dev(w.astype(np.float32).reshape(T, k)), al, lo, hi).float().cpu().numpy()
+    check_close(f"down XCD order {fmt} E={E} H={H} [{lo},{hi}) k={k} T={T}", got, ref)
+
+
 @pytest.mark.parametrize("sl", [(0, 384), (128, 384)])
 def test_fp8_prefill_zero_block_scales(sl):
     """fp8-block scales of 0 (an all-zero weight block) with nonzero codes: the block adds
